@@ -1,0 +1,311 @@
+"""GrowPage's page-boundary pass, float64 / exact integer arithmetic.
+
+Steps, in the order GrowPage App. E.1 runs them at a capacity boundary:
+
+1. Calibration (Eq. 12): gamma^x = RMS(q_t) / RMS(qbar^x), qtilde^x = gamma^x qbar^x, then RoPE
+   at the current decoding position (Sec. 3.2, App. E.1). RoPE here is the rotate-half form
+   on pairs (i, i + d/2) with angle pos * theta^(-2i/d); theta <= 0 disables it.
+2. Candidate set C_t: every cached slot outside the most recent page (Sec. 3.2, App. E.1
+   "exclude the most recent physical KV block"). The slots of that last page are the
+   protected recent tokens R_t of Sec. 3.3.
+3. Scores: for each view x and KV head h, the softmax over C_t of qtilde^x_g . k / sqrt(d) for
+   each query head g mapped to h (native GQA mapping, App. E.1), averaged over those heads.
+4. Working set (Eq. 2 / Eq. 7): K^x_h = min{k : sum of the k largest weights >= p}, computed
+   exactly on the given weight values; if no k reaches p, K = |C_t|.
+5. Trend and decision (Eq. 8, Sec. 3.2): Delta = (1/H) sum_h (K^S_h - K^L_h) / |C_t|; Grow by
+   One Page iff Delta > tau, else Compress & Hold. Policies of App. H.1: always compress
+   (GrowPage-Fixed), always grow, and GrowPage-Inverse (grow iff Delta <= tau).
+6. Allocation (Sec. 4.2, App. E.2): Grow pops the top of the global free-page stack and appends
+   it to the block table; with no free page (or a full block table) it falls back to
+   compression. Compression that must write into pages shared with other requests
+   (refcount > 1) first pops one private target page per shared page, in ascending logical
+   order; the old references are released after every pop of the call, and a page whose
+   count reaches zero is pushed back on the stack. If too few pages are free, the request is
+   left untouched (NO_PAGES).
+7. Selection (Eq. 9, Eq. 10): s_i = max(a^S_i, a^L_i); K_t = (P - 1) b - |R_t|; S_loc is the
+   union over historical pages of their k_loc best tokens; the rest of the budget is filled
+   with the best tokens of C_t outside S_loc. Order: larger s first, lower token index first
+   on ties. If |S_loc| >= K_t, S is the K_t best tokens of C_t.
+8. Compaction (Sec. 3.3, App. E.2): the kept tokens in ascending order, then R_t, are written to
+   slots 0 .. K_t + |R_t| - 1 of the (new) block table; the cached length becomes K_t + |R_t|,
+   i.e. (P - 1) b, leaving one page of free slots.
+
+Pinned by: RMS of the calibrated summary equals RMS(q_t); RoPE keeps norms and its dot
+products depend only on relative position; full retention (p -> 1) gives K = |C|; uniform
+weights give K = ceil(p |C|); one dominant weight gives K = 1; brute force over all subsets of
+tiny candidate sets (GrowPage Thm. 3.1 / App. C: the top-k weights maximise retained mass);
+the tight worst-case construction of App. C; equal summaries give Delta = 0 -> compress and
+the inverse policy flips it; selection against brute-force enumeration; page conservation,
+refcount bookkeeping, shared pages untouched and kept K/V bit-identical after compaction.
+"""
+from fractions import Fraction
+
+import numpy as np
+
+COMPRESS, GROW, GROW_FALLBACK_COMPRESS, NO_PAGES = 0, 1, 2, 3
+POLICY_AUTO, POLICY_FORCE_COMPRESS, POLICY_FORCE_GROW, POLICY_INVERSE = 0, 1, 2, 3
+
+
+# ---------------------------------------------------------------------------- step 1
+def rms(x):
+    x = np.asarray(x, dtype=np.float64)
+    return np.sqrt(np.mean(x * x, axis=-1))
+
+
+def calibrate(q_t, qbar):
+    """Eq. 12 for one head: scale qbar so its RMS equals RMS(q_t). A zero summary stays zero."""
+    rq, rb = rms(q_t), rms(qbar)
+    if rb == 0.0:
+        return np.zeros_like(np.asarray(qbar, dtype=np.float64))
+    return (rq / rb) * np.asarray(qbar, dtype=np.float64)
+
+
+def rope(x, pos, theta):
+    """Rotate-half RoPE of vectors x [..., d] at integer position pos (theta <= 0: identity)."""
+    x = np.asarray(x, dtype=np.float64)
+    if theta <= 0:
+        return x.copy()
+    d = x.shape[-1]
+    half = d // 2
+    i = np.arange(half, dtype=np.float64)
+    ang = float(pos) * np.power(float(theta), -2.0 * i / d)
+    c, s = np.cos(ang), np.sin(ang)
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c - hi * s, lo * s + hi * c], axis=-1)
+
+
+# ---------------------------------------------------------------------------- step 2
+def candidate_count(ctx, page_size):
+    """|C_t|: slots outside the last (partially) filled page."""
+    ctx = int(ctx)
+    if ctx <= 0:
+        return 0
+    used = -(-ctx // page_size)
+    return (used - 1) * page_size
+
+
+# ---------------------------------------------------------------------------- step 3
+def score_request(q_t, qbar, pos, keys, theta, sm_scale, G):
+    """Averaged short/long attention over the candidate keys.
+
+    q_t [H_q, d], qbar [2, H_q, d], keys [H_kv, n_cand, d] -> a [2, H_kv, n_cand].
+    """
+    H_kv, n, _ = keys.shape
+    a = np.zeros((2, H_kv, n))
+    if n == 0:
+        return a
+    for x in range(2):
+        for h in range(H_kv):
+            acc = np.zeros(n)
+            for g in range(h * G, (h + 1) * G):
+                qt = rope(calibrate(q_t[g], qbar[x, g]), pos, theta)
+                z = keys[h] @ qt * sm_scale
+                w = np.exp(z - z.max())
+                acc += w / w.sum()
+            a[x, h] = acc / G
+    return a
+
+
+# ---------------------------------------------------------------------------- step 4
+def _exact_ints(values):
+    """Exact integer numerators of float values over a common power-of-two denominator."""
+    vals = np.asarray(values)
+    scale_exp = 149 if vals.dtype == np.float32 else 1074
+    out = []
+    for v in vals.tolist():
+        num, den = float(v).as_integer_ratio()
+        out.append(num * ((1 << scale_exp) // den))
+    return out, scale_exp
+
+
+def working_set_size(weights, p):
+    """Eq. 2 / Eq. 7 on the exact values of `weights` (float32 or float64 array)."""
+    w = np.asarray(weights)
+    n = w.shape[0]
+    if n == 0:
+        return 0
+    desc = np.sort(w)[::-1]
+    ints, e = _exact_ints(desc)
+    pf = Fraction(p)
+    target_num, target_den = pf.numerator << e, pf.denominator   # p * 2^e as a fraction
+    total = 0
+    for k, v in enumerate(ints, 1):
+        total += v
+        if total * target_den >= target_num:
+            return k
+    return n
+
+
+def score_and_working_set(q, qstate, slot_ids, req_idx, k_pool, block_tables, context_lens,
+                          positions, page_size, rope_theta, p, sm_scale, C_max=None):
+    """Steps 1-4 for the boundary requests req_idx.
+
+    Returns a_short, a_long [R, H_kv, C_max] (float64, zero beyond |C|), ws_counts
+    [R, H_kv, 2] (K^S, K^L computed on the float64 weights) and n_cand [R].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kp = np.asarray(k_pool)
+    H_kv = kp.shape[1]
+    H_q = q.shape[1]
+    G = H_q // H_kv
+    R = len(req_idx)
+    ncs = [candidate_count(context_lens[r], page_size) for r in req_idx]
+    if C_max is None:
+        C_max = max(ncs) if ncs else 0
+    a_s = np.zeros((R, H_kv, C_max))
+    a_l = np.zeros((R, H_kv, C_max))
+    ws = np.zeros((R, H_kv, 2), dtype=np.int64)
+    for i, r in enumerate(req_idx):
+        n = ncs[i]
+        slots = np.arange(n)
+        pages = np.asarray(block_tables[r])[slots // page_size]
+        keys = kp[pages, :, slots % page_size, :].astype(np.float64).transpose(1, 0, 2)
+        a = score_request(q[r], np.asarray(qstate[int(slot_ids[r])], dtype=np.float64),
+                          int(positions[r]), keys, rope_theta, sm_scale, G)
+        a_s[i, :, :n] = a[0]
+        a_l[i, :, :n] = a[1]
+        for h in range(H_kv):
+            ws[i, h, 0] = working_set_size(a[0, h], p)
+            ws[i, h, 1] = working_set_size(a[1, h], p)
+    return a_s, a_l, ws, np.array(ncs, dtype=np.int64)
+
+
+def working_set_counts(a_short, a_long, n_cand, p):
+    """Step 4 alone, on given weight arrays (the GPU's float32 scores in parity tests)."""
+    R, H, _ = a_short.shape
+    ws = np.zeros((R, H, 2), dtype=np.int64)
+    for i in range(R):
+        n = int(n_cand[i])
+        for h in range(H):
+            ws[i, h, 0] = working_set_size(a_short[i, h, :n], p)
+            ws[i, h, 1] = working_set_size(a_long[i, h, :n], p)
+    return ws
+
+
+# ---------------------------------------------------------------------------- step 5
+def wants_grow(ws_counts_r, n_cand_r, tau, policy):
+    """Primary decision of one request (before allocation): True = Grow by One Page."""
+    if policy == POLICY_FORCE_COMPRESS:
+        return False
+    if policy == POLICY_FORCE_GROW or n_cand_r == 0:
+        return True
+    ws = np.asarray(ws_counts_r, dtype=np.int64)
+    H = ws.shape[0]
+    delta = Fraction(int(ws[:, 0].sum() - ws[:, 1].sum()), H * int(n_cand_r))
+    grow = delta > Fraction(tau)
+    return (not grow) if policy == POLICY_INVERSE else grow
+
+
+# ---------------------------------------------------------------------------- step 7
+def select_kept(s, K_t, page_size, k_loc):
+    """Eq. 10 for one (layer, KV head): sorted indices of the K_t retained candidates."""
+    s = np.asarray(s, dtype=np.float64)
+    n = s.shape[0]
+    if K_t >= n:
+        return np.arange(n)
+    idx = np.arange(n)
+    local = []
+    for j in range(0, n, page_size):
+        blk = idx[j:j + page_size]
+        order = blk[np.lexsort((blk, -s[blk]))]
+        local.extend(order[:k_loc].tolist())
+    local = np.array(sorted(local), dtype=np.int64)
+    glob = idx[np.lexsort((idx, -s))]
+    if len(local) >= K_t:
+        chosen = glob[:K_t]
+    else:
+        mask = np.ones(n, dtype=bool)
+        mask[local] = False
+        rest = glob[mask[glob]][:K_t - len(local)]
+        chosen = np.concatenate([local, rest])
+    return np.sort(chosen)
+
+
+# ---------------------------------------------------------------------------- steps 5-8
+def compact_or_grow(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, policy,
+                    k_pool, v_pool, block_tables, n_pages, context_lens, refcount,
+                    free_stack, free_top, page_size, policies=None):
+    """Decision, allocation, selection and compaction for the boundary requests, in order.
+
+    State arrays (numpy) are updated in place: k_pool [N, H, b, d], v_pool [N, H, d, b],
+    block_tables [B, max_pages], n_pages, context_lens, refcount, free_stack, free_top [1].
+    `policies` optionally gives a per-request policy overriding `policy`.
+    Returns decision [R] and kept_idx [R, H_kv, C_max] (-1 where unused).
+    """
+    b = page_size
+    R = len(req_idx)
+    H = k_pool.shape[1]
+    C_max = a_short.shape[2]
+    max_pages = block_tables.shape[1]
+    decision = np.full(R, -1, dtype=np.int64)
+    kept_idx = np.full((R, H, C_max), -1, dtype=np.int64)
+    releases = []
+    for i, r in enumerate(req_idx):
+        pol = policy if policies is None else policies[i]
+        P = int(n_pages[r])
+        ctx = int(context_lens[r])
+        n = int(n_cand[i])
+        assert n == candidate_count(ctx, b)
+        R_n = ctx - n
+        K_t = min(n, max(0, (P - 1) * b - R_n))
+        E = n - K_t
+        if wants_grow(ws_counts[i], n, tau, pol):
+            if int(free_top[0]) > 0 and P < max_pages:
+                top = int(free_top[0]) - 1
+                page = int(free_stack[top])
+                free_stack[top] = -1
+                free_top[0] = top
+                block_tables[r, P] = page
+                n_pages[r] = P + 1
+                refcount[page] = 1
+                decision[i] = GROW
+                continue
+            if n == 0:
+                decision[i] = NO_PAGES
+                continue
+            code = GROW_FALLBACK_COMPRESS
+        else:
+            code = COMPRESS
+        if E == 0:
+            decision[i] = code
+            kept_idx[i, :, :n] = np.arange(n)
+            continue
+        ctx_new = K_t + R_n
+        n_dest = -(-ctx_new // b)
+        shared = [j for j in range(n_dest) if refcount[block_tables[r, j]] > 1]
+        if len(shared) > int(free_top[0]):
+            decision[i] = NO_PAGES
+            continue
+        old_bt = block_tables[r].copy()
+        for j in shared:
+            top = int(free_top[0]) - 1
+            page = int(free_stack[top])
+            free_stack[top] = -1
+            free_top[0] = top
+            block_tables[r, j] = page
+            refcount[page] = 1
+            releases.append(int(old_bt[j]))
+        # selection per KV head, then move the tokens (read everything first, then write)
+        src_slots = np.arange(ctx)
+        for h in range(H):
+            s = np.maximum(np.asarray(a_short[i, h, :n], dtype=np.float64),
+                           np.asarray(a_long[i, h, :n], dtype=np.float64))
+            kept = select_kept(s, K_t, b, k_loc)
+            kept_idx[i, h, :K_t] = kept
+            src = np.concatenate([kept, src_slots[n:ctx]])
+            sp, so = old_bt[src // b], src % b
+            kv_k = k_pool[sp, h, so, :].copy()
+            kv_v = v_pool[sp, h, :, so].copy()
+            dst = np.arange(ctx_new)
+            dp, do = block_tables[r][dst // b], dst % b
+            k_pool[dp, h, do, :] = kv_k
+            v_pool[dp, h, :, do] = kv_v
+        context_lens[r] = ctx_new
+        decision[i] = code
+    for page in releases:
+        refcount[page] -= 1
+        if refcount[page] == 0:
+            top = int(free_top[0])
+            free_stack[top] = page
+            free_top[0] = top + 1
+    return decision, kept_idx
