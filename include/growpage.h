@@ -1,0 +1,198 @@
+/*
+ * growpage.h - C ABI of the MI355X (gfx950) paged-KV decode and page-boundary budgeting library.
+ *
+ * Operations and the passages that define them:
+ *   gp_paged_decode_attn      PASK, Sec. 3.1 (o = V softmax(K^T q / sqrt(d_k))), App. B.2 and B.5
+ *                             (mixed-precision pages, GQA routes, split-KV merge); GrowPage Sec. 4.2
+ *                             (block tables, unchanged attention interface after a grown page).
+ *   gp_update_query_summaries GrowPage Sec. 3.2 Eq. 6 and App. E.1 (slot pool, first-step init).
+ *   gp_score_and_working_set  GrowPage App. E.1 Eq. 12 (RMS calibration + RoPE), Sec. 3.2
+ *                             (candidate set without the most recent block, short/long views),
+ *                             Eq. 2 / Eq. 7 (p-coverage working set).
+ *   gp_compact_or_grow        GrowPage Eq. 8 (trend, tau), Sec. 3.3 Eq. 9-10 (importance and
+ *                             block-local + global selection, Compress & Hold, Grow by One Page),
+ *                             Sec. 4.2 and App. E.2 (free-page pool, fallback, prefix sharing),
+ *                             App. H.1 (fixed / inverse policies).
+ *
+ * Conventions shared by every call
+ *   - All array arguments are DEVICE pointers owned by the caller; scalars are passed by value.
+ *     The library allocates no memory: scratch comes from a caller-provided workspace whose size
+ *     the matching *_workspace_size() call returns (NULL / 0 allowed when that size is 0).
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default stream) and never
+ *     synchronises with the host, so calls can be captured in a HIP graph.
+ *   - Return value: GP_OK or a negative gp_status. Arguments are validated on the host before
+ *     anything is launched; on error nothing is launched and no buffer is touched.
+ *     Values read from device arrays (block-table entries, lengths, slots, request indices)
+ *     are range-checked inside the kernels: an entry outside its range makes that request (or
+ *     page) count as empty rather than being dereferenced.
+ *   - Layouts (row-major, innermost last):
+ *       K pool  [num_pages, H_kv, page_size, head_dim]       (a page holds page_size key rows)
+ *       V pool  [num_pages, H_kv, head_dim, page_size]       (values transposed within a page)
+ *       block_tables [B, max_pages] int32, context_lens [B] int32 (cached tokens of a request;
+ *       token slot j lives at page block_tables[r][j / page_size], offset j % page_size).
+ *     The query head g uses KV head g / (H_q / H_kv).
+ *   - Re-entrant; the library keeps no mutable global state.
+ */
+#ifndef GROWPAGE_H
+#define GROWPAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GP_VERSION 1
+
+typedef enum {
+  GP_OK = 0,
+  GP_ERR_INVALID = -1,      /* a pointer, size or parameter is out of range            */
+  GP_ERR_UNSUPPORTED = -2,  /* a valid combination this build does not implement       */
+  GP_ERR_WORKSPACE = -3,    /* workspace missing or smaller than *_workspace_size()     */
+  GP_ERR_HIP = -4           /* a HIP launch failed                                      */
+} gp_status;
+
+typedef enum { GP_F32 = 0, GP_BF16 = 1 } gp_dtype;
+
+/* Page tags of mixed-precision caches (PASK App. B.2: released entries keep their positions). */
+enum { GP_TAG_RELEASE = 0, GP_TAG_FP8 = 1, GP_TAG_BF16 = 2 };
+
+/* Outcome per boundary request (GrowPage Sec. 4.2, App. H.2). */
+enum {
+  GP_DECISION_COMPRESS = 0,               /* Compress & Hold                                 */
+  GP_DECISION_GROW = 1,                   /* Grow by One Page                                */
+  GP_DECISION_GROW_FALLBACK_COMPRESS = 2, /* grow wanted, no page granted: compressed instead */
+  GP_DECISION_NO_PAGES = 3                /* neither possible: request left untouched        */
+};
+
+/* Capacity-control policies (GrowPage Sec. 3.2 and App. H.1). */
+enum {
+  GP_POLICY_AUTO = 0,           /* grow iff Delta > tau                        */
+  GP_POLICY_FORCE_COMPRESS = 1, /* GrowPage-Fixed: always Compress & Hold      */
+  GP_POLICY_FORCE_GROW = 2,     /* always try to grow                          */
+  GP_POLICY_INVERSE = 3         /* GrowPage-Inverse: grow iff Delta <= tau     */
+};
+
+/*
+ * One layer's paged KV cache.
+ *   k, v      pools in `dtype` (GP_F32 or GP_BF16), layouts above. Required.
+ *   page_tag  NULL for a uniform cache. Otherwise [num_pages] uint8 with GP_TAG_*: a mixed
+ *             cache (dtype must be GP_BF16). Released pages are skipped entirely; fp8 pages
+ *             read k8/v8 (OCP E4M3FN codes, same layouts as k/v) times the per-row scales
+ *             k_scale/v_scale [num_pages, H_kv, page_size] fp32; bf16 pages read k/v.
+ *   page_size a multiple of 16 (16 .. 256); head_dim 64 or 128.
+ */
+typedef struct {
+  void* k;
+  void* v;
+  void* k8;
+  void* v8;
+  float* k_scale;
+  float* v_scale;
+  const uint8_t* page_tag;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+} gp_kv_cache;
+
+int gp_version(void);
+const char* gp_status_string(int status);
+
+/*
+ * Decode attention for one new token per request (PASK Sec. 3.1, App. B.5).
+ *   q            [B, H_q, head_dim] in the cache dtype (bf16 for mixed caches); the query as
+ *                attention sees it (already rotated).
+ *   block_tables [B, max_pages]; context_lens [B] (0 .. max_context; 0 gives out = 0, lse = -inf).
+ *   max_context  host-side upper bound on every context_lens[r]; it sizes the split-K grid.
+ *   sm_scale     logit scale, normally 1/sqrt(head_dim).
+ *   out          [B, H_q, head_dim] in the q dtype.
+ *   lse          [B, H_q] fp32 natural-log log-sum-exp of the scaled logits, or NULL.
+ *   workspace    >= gp_paged_decode_attn_workspace_size(...) bytes (split partials).
+ * Long contexts are partitioned into splits whose partial (max, sum, output) are merged with
+ * PASK App. B.5's rule.
+ */
+size_t gp_paged_decode_attn_workspace_size(int B, int H_q, int H_kv, int head_dim, int page_size,
+                                           int max_context);
+int gp_paged_decode_attn(const void* q, int q_dtype, int B, int H_q, const gp_kv_cache* kv,
+                         const int32_t* block_tables, int max_pages, const int32_t* context_lens,
+                         int max_context, float sm_scale, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * Dual-timescale EMA of the pre-RoPE queries (GrowPage Eq. 6, App. E.1).
+ *   q        [B, H_q, head_dim] (GP_F32 or GP_BF16).
+ *   slot_ids [B] int32 in [0, num_slots); fresh [B] uint8 (1 = first step of this slot).
+ *   qstate   [num_slots, 2, H_q, head_dim] fp32, index 0 short and 1 long; updated in place:
+ *            fresh: both = q; else x <- beta_x * x + (1 - beta_x) * q.
+ * Two requests of one call must not share a slot.
+ */
+int gp_update_query_summaries(const void* q, int q_dtype, int B, int H_q, int head_dim,
+                              const int32_t* slot_ids, const uint8_t* fresh, float* qstate,
+                              int num_slots, float beta_s, float beta_l, void* stream);
+
+/*
+ * Scores and working sets of the boundary requests (GrowPage App. E.1, Sec. 3.2, Eq. 7, Eq. 12).
+ *   q [B, H_q, head_dim] current pre-RoPE queries; qstate / slot_ids as above.
+ *   req_idx [R] request indices in [0, B); positions [B] 0-based position of the current token.
+ *   For request r the candidate set C is every slot outside its last (partially) filled page:
+ *   |C| = (ceil(ctx/b) - 1) * b. Per query head and view x in {short, long} the summary is
+ *   RMS-calibrated to q (Eq. 12), rotated (rotate-half RoPE on pairs (i, i + d/2), angle
+ *   pos * rope_theta^(-2i/d); rope_theta <= 0 disables it), and softmax-ed over C with scale
+ *   sm_scale; the G query heads of a KV head are averaged.
+ *   a_short, a_long [R, H_kv, C_max] fp32 outputs; entries past |C| are not written.
+ *   ws_counts [R, H_kv, 2] int32: K^S, K^L = min{k : sum of the k largest weights >= p},
+ *   computed exactly on the fp32 weights written to a_short / a_long (|C| if never reached).
+ *   n_cand [R] int32 = |C|; a request whose index, slot or length is out of range, or whose
+ *   |C| exceeds C_max, gets n_cand = -1 and ws_counts = -1 and is otherwise skipped.
+ *   Limits: 2 * (H_q / H_kv) <= 16, C_max <= 32768 and a multiple of 4, 0 < p <= 1.
+ *   workspace >= gp_score_and_working_set_workspace_size(...) bytes.
+ * Uniform caches only (page_tag must be NULL).
+ */
+size_t gp_score_and_working_set_workspace_size(int R, int H_q, int H_kv, int head_dim,
+                                               int page_size, int C_max);
+int gp_score_and_working_set(const void* q, int q_dtype, int B, int H_q, const float* qstate,
+                             int num_slots, const int32_t* slot_ids, const int32_t* req_idx, int R,
+                             const gp_kv_cache* kv, const int32_t* block_tables, int max_pages,
+                             const int32_t* context_lens, const int32_t* positions,
+                             float rope_theta, double p, float sm_scale, float* a_short,
+                             float* a_long, int C_max, int32_t* ws_counts, int32_t* n_cand,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Compress-or-grow for the boundary requests, processed in req_idx order (GrowPage Sec. 3.2,
+ * Sec. 3.3, Sec. 4.2, App. E.2, App. H.1).
+ *   Decision: Delta = (1/H_kv) sum_h (K^S_h - K^L_h) / |C| compared exactly with tau under
+ *   `policy` (or policies[i] when `policies` is non-NULL); |C| = 0 always grows.
+ *   Grow: pop free_stack[*free_top - 1], append it to the block table, n_pages += 1, refcount
+ *   of the page = 1. No free page (or a full block table) falls back to compression.
+ *   Compress: with P = n_pages[r], R = tokens of the last page, K_t = min(|C|, (P-1)b - |R|).
+ *   If K_t < |C|, each page among the first ceil((K_t+|R|)/b) that is shared (refcount > 1)
+ *   is replaced by a popped page (ascending logical order; too few free pages -> NO_PAGES,
+ *   request untouched), then per KV head the kept set S (Eq. 9-10 with k_loc, ties to the lower
+ *   token index) in ascending order followed by the |R| recent tokens is written to slots
+ *   0 .. K_t+|R|-1 and context_lens[r] becomes K_t + |R|. Released references are
+ *   decremented after all pops of the call; pages reaching zero are pushed on the stack.
+ *   decision [R] int32 (GP_DECISION_*); kept_idx [R, H_kv, C_max] int32: the kept candidate
+ *   indices in ascending order (all of C when nothing is evicted), -1 elsewhere and for
+ *   requests that grew or got no pages.
+ *   a_short / a_long / ws_counts / n_cand as produced by gp_score_and_working_set.
+ *   kv, block_tables, n_pages, context_lens, refcount, free_stack, free_top are updated in place.
+ *   Uniform caches only (page_tag must be NULL). Requests of one call must be distinct.
+ */
+size_t gp_compact_or_grow_workspace_size(int R, int H_kv, int max_pages, int page_size, int C_max);
+int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const float* a_short,
+                       const float* a_long, int C_max, const int32_t* ws_counts,
+                       const int32_t* n_cand, double tau, int k_loc, int policy,
+                       const int32_t* policies, gp_kv_cache* kv, int32_t* block_tables,
+                       int32_t* n_pages, int max_pages, int32_t* context_lens, int32_t* refcount,
+                       int32_t* free_stack, int32_t* free_top, int32_t* decision,
+                       int32_t* kept_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GROWPAGE_H */

@@ -1,0 +1,630 @@
+// Page-boundary demand estimation for gfx950 (GrowPage App. E.1: Eq. 12 calibration and RoPE of
+// the short/long summaries, candidate set without the most recent block, per-view attention with
+// the native GQA mapping; Sec. 3.2 Eq. 7 p-coverage working sets).
+//
+// Four launches:
+//   1. prep:      per boundary request and query head, RMS-calibrate both summaries to q_t and
+//                 rotate them to the current position (float64 arithmetic, tiny).
+//   2. logits:    matrix-core contraction of every candidate key tile with the 2G calibrated
+//                 summaries of its KV head (keys as the 16-row operand, the 2G summaries as
+//                 columns; bf16 keys meet a hi+lo bf16 split of the fp32 summaries, fp32 keys
+//                 use the fp32 MFMA); logits go to the workspace with per-chunk (max, sum).
+//   3. normalize: softmax of every row and the mean over the G heads of each view.
+//   4. working set: per (request, KV head, view) the p-coverage size, exact on the fp32 weights:
+//                 a float64 binary search over the weight bit patterns finds the threshold
+//                 weight, which an exact 160-bit fixed-point sum then certifies (and corrects
+//                 if float64 rounding picked a neighbour).
+#include "common.h"
+
+namespace {
+
+constexpr int LG_WAVES = 4;
+constexpr int LG_THREADS = LG_WAVES * GP_WAVE;
+constexpr int CHUNK_TILES = 32;  // 512 candidate tokens per logits workgroup
+constexpr int WS_THREADS = 1024;
+constexpr int WS_VPT = 32;        // weights per thread held in registers (|C| <= 32768)
+constexpr int WS_MAX_C = WS_THREADS * WS_VPT;
+
+struct ScoreParams {
+  const void* q;
+  const float* qstate;
+  const int32_t* slot_ids;
+  const int32_t* req_idx;
+  const void* k;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* positions;
+  float* a_short;
+  float* a_long;
+  int32_t* ws_counts;
+  int32_t* n_cand;
+  float* qt;      // [R, 2, H_q, D]
+  float* logits;  // [R, 2, H_q, C_max]  (log2 domain)
+  float* stats;   // [R, 2, H_q, NCH, 2]
+  int B, R, H_q, H_kv, G, D, page_size, num_pages, max_pages, num_slots, C_max, nch;
+  int q_bf16;
+  float scale_log2;
+  double rope_theta;
+  uint32_t p_fixed[5];  // p in units of 2^-149, little-endian 32-bit digits (rounded up)
+};
+
+// |C| of request index i (or -1 for an invalid request / slot, or |C| > C_max)
+__device__ __forceinline__ int candidates(const ScoreParams& P, int i, int* r_out) {
+  const int r = P.req_idx[i];
+  *r_out = r;
+  if (r < 0 || r >= P.B) return -1;
+  const int slot = P.slot_ids[r];
+  if (slot < 0 || slot >= P.num_slots) return -1;
+  const int ctx = P.context_lens[r];
+  if (ctx < 0 || (long)ctx > (long)P.max_pages * P.page_size) return -1;
+  if (ctx == 0) return 0;
+  const int used = (ctx + P.page_size - 1) / P.page_size;
+  const int n = (used - 1) * P.page_size;
+  return n > P.C_max ? -1 : n;
+}
+
+// ------------------------------------------------------------------------------ 1. prep
+__global__ __launch_bounds__(256) void prep_kernel(ScoreParams P) {
+  const int i = blockIdx.x;
+  int r;
+  const int n = candidates(P, i, &r);
+  if (threadIdx.x == 0) P.n_cand[i] = n;
+  if (n < 0) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int D = P.D, half = D / 2;
+  const int slot = P.slot_ids[r];
+  const double pos = (double)P.positions[r];
+  for (int row = w; row < 2 * P.H_q; row += 4) {
+    const int x = row / P.H_q, g = row % P.H_q;
+    double qv[2], sv[2];
+    double sq = 0.0, ss = 0.0;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int d = lane + 64 * c;
+      qv[c] = sv[c] = 0.0;
+      if (d < D) {
+        const size_t qi = ((size_t)r * P.H_q + g) * D + d;
+        qv[c] = P.q_bf16 ? (double)gp::bf16_bits_to_f32(static_cast<const uint16_t*>(P.q)[qi])
+                         : (double)static_cast<const float*>(P.q)[qi];
+        sv[c] = (double)P.qstate[(((size_t)slot * 2 + x) * P.H_q + g) * D + d];
+      }
+      sq += qv[c] * qv[c];
+      ss += sv[c] * sv[c];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      sq += __shfl_xor(sq, o, GP_WAVE);
+      ss += __shfl_xor(ss, o, GP_WAVE);
+    }
+    const double gamma = ss > 0.0 ? sqrt(sq / ss) : 0.0;  // RMS ratio (the 1/D cancels)
+    // calibrated vector into LDS-free registers, then rotate pairs (d, d + D/2)
+    double cv[2] = {gamma * sv[0], gamma * sv[1]};
+    double part[2];
+    // the partner of element d is d +/- D/2: lane-local when D == 128 (c swaps), a shuffle when 64
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      if (D == 128) part[c] = cv[1 - c];
+      else part[c] = __shfl_xor(cv[0], 32, GP_WAVE);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int d = lane + 64 * c;
+      if (d >= D) continue;
+      const int j = d % half;
+      double out = cv[c];
+      if (P.rope_theta > 0.0) {
+        const double ang = pos * pow(P.rope_theta, -2.0 * j / D);
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        out = (d < half) ? cv[c] * cs - part[c] * sn : part[c] * sn + cv[c] * cs;
+      }
+      P.qt[(((size_t)i * 2 + x) * P.H_q + g) * D + d] = (float)out;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ 2. logits
+template <int D, bool BF16>
+__global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
+  const int chunk = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+  int r;
+  const int n = candidates(P, i, &r);
+  const int tile0 = chunk * CHUNK_TILES;
+  if (n <= 0 || tile0 * 16 >= n) return;
+  const int tile1 = min(n >> 4, tile0 + CHUNK_TILES);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const int G = P.G, b = P.page_size;
+  const bool col_ok = n16 < 2 * G;
+  const int x = n16 / G, g = n16 % G;
+  const int hq = h * G + g;
+  const float* qrow = P.qt + (((size_t)i * 2 + x) * P.H_q + hq) * D;
+
+  // summary operand: column n16 = (view x, head g)
+  u32x4_t qhi[BF16 ? D / 32 : D / 16], qlo[BF16 ? D / 32 : 1];
+  if constexpr (BF16) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v0 = 0.f, v1 = 0.f;
+        if (col_ok) {
+          v0 = qrow[32 * kk + 8 * g4 + 2 * e];
+          v1 = qrow[32 * kk + 8 * g4 + 2 * e + 1];
+        }
+        const uint32_t h0 = gp::f32_to_bf16_bits(v0), h1 = gp::f32_to_bf16_bits(v1);
+        hi[e] = h0 | (h1 << 16);
+        lo[e] = gp::pack_bf16x2(v0 - gp::bf16_bits_to_f32(h0), v1 - gp::bf16_bits_to_f32(h1));
+      }
+      qhi[kk] = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+      qlo[kk] = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+      if (col_ok) v = *reinterpret_cast<const f32x4_t*>(qrow + (D / 4) * g4 + 4 * c);
+      qhi[c] = __builtin_bit_cast(u32x4_t, v);
+    }
+    (void)qlo;
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float* lrow = P.logits + (((size_t)i * 2 + x) * P.H_q + hq) * P.C_max;
+  for (int t = tile0 + w; t < tile1; t += LG_WAVES) {
+    const int tok0 = t << 4;
+    int pg = P.block_tables[(size_t)r * P.max_pages + tok0 / b];
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+    const bool valid_page = pg >= 0 && pg < P.num_pages;
+    if (valid_page) {
+      const size_t base = ((size_t)pg * P.H_kv + h) * (size_t)b * D + (size_t)(tok0 % b + n16) * D;
+      if constexpr (BF16) {
+        const uint16_t* kr = static_cast<const uint16_t*>(P.k) + base + 8 * g4;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+          const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(kr + 32 * kk);
+          sacc = gp::mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, kw), __builtin_bit_cast(bf16x8_t, qhi[kk]), sacc);
+          sacc = gp::mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, kw), __builtin_bit_cast(bf16x8_t, qlo[kk]), sacc);
+        }
+      } else {
+        const float* kr = static_cast<const float*>(P.k) + base + (D / 4) * g4;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+          const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(kr + 4 * c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sacc = gp::mfma_f32_16x16x4(__uint_as_float(kw[e]), __uint_as_float(qhi[c][e]), sacc);
+        }
+      }
+    }
+    f32x4_t z;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = valid_page ? sacc[e] * P.scale_log2 : -INFINITY;
+    if (col_ok) *reinterpret_cast<f32x4_t*>(lrow + tok0 + 4 * g4) = z;
+    float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    const float m_new = fmaxf(m_run, mx);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += gp::safe_exp2_diff(z[e], m_new);
+    l_run = l_run * gp::safe_exp2_diff(m_run, m_new) + s;
+    m_run = m_new;
+  }
+  // merge the 4 lanes of each column, then the waves
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const float mo = __shfl_xor(m_run, o, GP_WAVE), lo_ = __shfl_xor(l_run, o, GP_WAVE);
+    const float mm = fmaxf(m_run, mo);
+    l_run = l_run * gp::safe_exp2_diff(m_run, mm) + lo_ * gp::safe_exp2_diff(mo, mm);
+    m_run = mm;
+  }
+  __shared__ float sm[LG_WAVES][16], sl[LG_WAVES][16];
+  if (lane < 16) {
+    sm[w][lane] = m_run;
+    sl[w][lane] = l_run;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2 * G) {
+    const int c = threadIdx.x;
+    float m = -INFINITY;
+    for (int ww = 0; ww < LG_WAVES; ++ww) m = fmaxf(m, sm[ww][c]);
+    float l = 0.f;
+    for (int ww = 0; ww < LG_WAVES; ++ww) l += sl[ww][c] * gp::safe_exp2_diff(sm[ww][c], m);
+    const int xx = c / G, gg = c % G;
+    float* st = P.stats + ((((size_t)i * 2 + xx) * P.H_q + h * G + gg) * P.nch + chunk) * 2;
+    st[0] = m;
+    st[1] = l;
+  }
+}
+
+// ------------------------------------------------------------------------------ 3. normalize
+__global__ __launch_bounds__(256) void normalize_kernel(ScoreParams P) {
+  const int blk = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+  int r;
+  const int n = candidates(P, i, &r);
+  if (n <= 0 || blk * 1024 >= n) return;
+  const int G = P.G;
+  __shared__ float sM[32], sInv[32];
+  const int nchunks = (n + CHUNK_TILES * 16 - 1) / (CHUNK_TILES * 16);
+  if (threadIdx.x < 2 * G) {
+    const int c = threadIdx.x, x = c / G, g = c % G;
+    const float* st = P.stats + (((size_t)i * 2 + x) * P.H_q + h * G + g) * P.nch * 2;
+    float m = -INFINITY;
+    for (int j = 0; j < nchunks; ++j) m = fmaxf(m, st[2 * j]);
+    float l = 0.f;
+    for (int j = 0; j < nchunks; ++j) l += st[2 * j + 1] * gp::safe_exp2_diff(st[2 * j], m);
+    sM[c] = m;
+    sInv[c] = l > 0.f ? 1.f / l : 0.f;
+  }
+  __syncthreads();
+  const int t = blk * 1024 + threadIdx.x * 4;
+  if (t >= n) return;
+  const float invG = 1.0f / (float)G;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < G; ++g) {
+      const int c = x * G + g;
+      const f32x4_t z = *reinterpret_cast<const f32x4_t*>(
+          P.logits + (((size_t)i * 2 + x) * P.H_q + h * G + g) * P.C_max + t);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += gp::safe_exp2_diff(z[e], sM[c]) * sInv[c];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] *= invG;
+    float* dst = (x == 0 ? P.a_short : P.a_long) + ((size_t)i * P.H_kv + h) * P.C_max + t;
+    *reinterpret_cast<f32x4_t*>(dst) = acc;
+  }
+}
+
+// ------------------------------------------------------------------------------ 4. working set
+// 160-bit fixed point in units of 2^-149, accumulated as five 32-bit digits held in 64-bit
+// counters (carries are resolved once, after the block reduction).
+struct Acc5 {
+  uint64_t d[6];
+};
+
+__device__ __forceinline__ void acc_add(Acc5& a, uint32_t bits) {
+  const uint32_t E = bits >> 23;
+  if (bits == 0u) return;
+  uint32_t M = bits & 0x7fffffu;
+  uint32_t sh = 0;
+  if (E) {
+    M |= 0x800000u;
+    sh = min(E, 129u) - 1u;
+  }
+  const uint64_t v = (uint64_t)M << (sh & 31u);
+  const uint32_t k0 = sh >> 5;
+  const uint64_t lo = v & 0xffffffffull, hi = v >> 32;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    a.d[k] += (k == (int)k0) ? lo : 0ull;
+    a.d[k] += (k == (int)k0 + 1) ? hi : 0ull;
+  }
+}
+
+// a += count * value(bits), exact (count * mantissa < 2^40)
+__device__ __forceinline__ void acc_add_mul(Acc5& a, uint32_t bits, uint32_t count) {
+  const uint32_t E = bits >> 23;
+  if (bits == 0u || count == 0u) return;
+  uint32_t M = bits & 0x7fffffu;
+  uint32_t sh = 0;
+  if (E) {
+    M |= 0x800000u;
+    sh = min(E, 129u) - 1u;
+  }
+  const unsigned __int128 v = (unsigned __int128)((uint64_t)M * count) << (sh & 31u);
+  const uint32_t k0 = sh >> 5;
+  const uint64_t d0 = (uint64_t)v & 0xffffffffull, d1 = (uint64_t)(v >> 32) & 0xffffffffull,
+                 d2 = (uint64_t)(v >> 64);
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    a.d[k] += (k == (int)k0) ? d0 : 0ull;
+    a.d[k] += (k == (int)k0 + 1) ? d1 : 0ull;
+    a.d[k] += (k == (int)k0 + 2) ? d2 : 0ull;
+  }
+}
+
+// normalise carries into 6 clean 32-bit digits
+__device__ __forceinline__ void acc_norm(const Acc5& a, uint32_t out[6]) {
+  uint64_t carry = 0;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const uint64_t t = a.d[k] + carry;
+    out[k] = (uint32_t)t;
+    carry = t >> 32;
+  }
+}
+
+// compare a (6 digits) with p (5 digits): returns -1, 0, 1
+__device__ __forceinline__ int cmp_p(const uint32_t a[6], const uint32_t p[5]) {
+  if (a[5]) return 1;
+  for (int k = 4; k >= 0; --k) {
+    if (a[k] != p[k]) return a[k] < p[k] ? -1 : 1;
+  }
+  return 0;
+}
+
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T* scratch) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, GP_WAVE);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  T s = 0;
+  for (int k = 0; k < WS_THREADS / GP_WAVE; ++k) s += scratch[k];
+  return s;
+}
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* scratch) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, GP_WAVE));
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  uint32_t s = 0;
+  for (int k = 0; k < WS_THREADS / GP_WAVE; ++k) s = max(s, scratch[k]);
+  return s;
+}
+
+__global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) {
+  const int row = blockIdx.x, i = blockIdx.y;
+  const int h = row >> 1, x = row & 1;
+  int r;
+  const int n = candidates(P, i, &r);
+  int32_t* out = P.ws_counts + ((size_t)i * P.H_kv + h) * 2 + x;
+  if (n <= 0) {
+    if (threadIdx.x == 0) *out = n < 0 ? -1 : 0;
+    return;
+  }
+  __shared__ double sd[WS_THREADS / GP_WAVE];
+  __shared__ uint64_t su[WS_THREADS / GP_WAVE];
+  __shared__ uint32_t sx[WS_THREADS / GP_WAVE];
+  const float* src = (x == 0 ? P.a_short : P.a_long) + ((size_t)i * P.H_kv + h) * P.C_max;
+  uint32_t u[WS_VPT];
+#pragma unroll
+  for (int j = 0; j < WS_VPT; ++j) {
+    const int t = threadIdx.x + j * WS_THREADS;
+    u[j] = t < n ? __float_as_uint(src[t]) & 0x7fffffffu : 0u;
+  }
+  const double p = 0.0;  // unused: the float64 search compares against p_f64 below
+  (void)p;
+  double p_f64 = 0.0;
+  for (int k = 4; k >= 0; --k) p_f64 = p_f64 * 4294967296.0 + (double)P.p_fixed[k];
+  p_f64 = ldexp(p_f64, -149);
+
+  // exact total mass: if it never reaches p, K = |C|
+  {
+    Acc5 a = {};
+#pragma unroll
+    for (int j = 0; j < WS_VPT; ++j) acc_add(a, u[j]);
+    Acc5 t;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) t.d[k] = block_sum<uint64_t>(a.d[k], su);
+    uint32_t tot[6];
+    acc_norm(t, tot);
+    if (cmp_p(tot, P.p_fixed) < 0) {
+      if (threadIdx.x == 0) *out = n;
+      return;
+    }
+  }
+  // float64 binary search for the largest bit pattern T with mass(weights >= T) >= p
+  uint32_t lo = 1u, hi = 0x7f800000u;  // mass(>= lo) >= p holds up to rounding; hi fails
+  while (hi - lo > 1u) {
+    const uint32_t mid = lo + (hi - lo) / 2;
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < WS_VPT; ++j) {
+      uint32_t uj = u[j];
+      asm volatile("" : "+v"(uj));  // keep the float64 conversion inside the loop (registers)
+      s += uj >= mid ? (double)__uint_as_float(uj) : 0.0;
+    }
+    s = block_sum<double>(s, sd);
+    if (s >= p_f64) lo = mid; else hi = mid;
+  }
+  // snap T to the largest present weight <= lo
+  uint32_t T;
+  {
+    uint32_t best = 0u;
+#pragma unroll
+    for (int j = 0; j < WS_VPT; ++j) if (u[j] <= lo) best = max(best, u[j]);
+    T = block_max_u32(best, sx);
+  }
+  // exact certificate: mass(> T) < p <= mass(>= T); move T to a neighbour value until it holds
+  for (int iter = 0; iter < 64; ++iter) {
+    Acc5 gt = {};
+    uint32_t cgt = 0, ceq = 0;
+#pragma unroll 4
+    for (int j = 0; j < WS_VPT; ++j) {
+      if (u[j] > T) {
+        acc_add(gt, u[j]);
+        ++cgt;
+      } else if (u[j] == T) {
+        ++ceq;
+      }
+    }
+    Acc5 sgt;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) sgt.d[k] = block_sum<uint64_t>(gt.d[k], su);
+    cgt = (uint32_t)block_sum<uint64_t>((uint64_t)cgt, su);
+    ceq = (uint32_t)block_sum<uint64_t>((uint64_t)ceq, su);
+    uint32_t mge[6], mgt[6];
+    acc_norm(sgt, mgt);
+    Acc5 sge = sgt;  // mass(>= T) = mass(> T) + #(== T) * T
+    acc_add_mul(sge, T, ceq);
+    acc_norm(sge, mge);
+    if (T != 0u && cmp_p(mge, P.p_fixed) < 0) {
+      // too high: next smaller present value
+      uint32_t best = 0u;
+#pragma unroll
+      for (int j = 0; j < WS_VPT; ++j) if (u[j] < T) best = max(best, u[j]);
+      T = block_max_u32(best, sx);
+      continue;
+    }
+    if (cmp_p(mgt, P.p_fixed) >= 0) {
+      // too low: next larger present value
+      uint32_t best = 0u;
+#pragma unroll
+      for (int j = 0; j < WS_VPT; ++j) if (u[j] > T) best = max(best, ~u[j]);
+      T = ~block_max_u32(best, sx);
+      continue;
+    }
+    // K = #(> T) + ceil((p - mass(> T)) / T), all exact
+    if (threadIdx.x == 0) {
+      // X = p - mass(> T), 160-bit
+      uint32_t X[5];
+      int64_t borrow = 0;
+      for (int k = 0; k < 5; ++k) {
+        int64_t t = (int64_t)P.p_fixed[k] - (int64_t)mgt[k] - borrow;
+        borrow = t < 0;
+        X[k] = (uint32_t)(t + (borrow ? 4294967296ll : 0ll));
+      }
+      const uint32_t E = T >> 23;
+      uint32_t M = T & 0x7fffffu, sh = 0;
+      if (E) {
+        M |= 0x800000u;
+        sh = E - 1u;
+      }
+      // Y = X >> sh (fits 64 bits), and whether any shifted-out bit was set
+      const uint32_t w0 = sh >> 5, o = sh & 31u;
+      uint64_t Y = 0;
+      bool rem = false;
+#pragma unroll
+      for (int k = 0; k < 5; ++k) {
+        const uint64_t xk = X[k];
+        if ((uint32_t)k < w0) rem |= xk != 0u;
+        if ((uint32_t)k == w0) rem |= (o ? (xk & ((1ull << o) - 1ull)) : 0ull) != 0ull;
+        const int rel = k - (int)w0;  // word k lands at bit 32*rel - o of Y
+        if (rel >= 0 && rel <= 2) {
+          const int at = 32 * rel - (int)o;
+          Y |= at >= 0 ? (xk << at) : (xk >> (-at));
+        }
+      }
+      uint64_t j = Y / M;
+      if (rem || (Y % M) != 0ull) ++j;
+      if (j == 0) j = 1;
+      *out = (int32_t)(cgt + j);
+    }
+    return;
+  }
+  if (threadIdx.x == 0) *out = -2;  // certificate did not converge (not expected)
+}
+
+}  // namespace
+
+// p as a 160-bit fixed-point number of 2^-149 units, rounded up (so "sum >= p" is exact)
+static void p_to_fixed(double p, uint32_t out[5]) {
+  for (int k = 0; k < 5; ++k) out[k] = 0;
+  int e;
+  const double m = frexp(p, &e);  // p = m * 2^e, m in [0.5, 1)
+  const uint64_t mant = (uint64_t)ldexp(m, 53);  // p = mant * 2^(e - 53)
+  const int shift = e - 53 + 149;
+  if (shift >= 0) {
+    for (int bit = 0; bit < 53; ++bit)
+      if ((mant >> bit) & 1ull) {
+        const int b = bit + shift;
+        if (b < 160) out[b >> 5] |= 1u << (b & 31);
+      }
+  } else {
+    const int s = -shift;
+    uint64_t q = s >= 64 ? 0 : (mant >> s);
+    const bool r = s >= 64 ? mant != 0 : (mant & ((1ull << s) - 1)) != 0;
+    if (r) ++q;
+    out[0] = (uint32_t)q;
+    out[1] = (uint32_t)(q >> 32);
+  }
+}
+
+extern "C" size_t gp_score_and_working_set_workspace_size(int R, int H_q, int H_kv, int head_dim,
+                                                          int page_size, int C_max) {
+  (void)H_kv;
+  (void)page_size;
+  if (R <= 0 || H_q <= 0 || head_dim <= 0 || C_max <= 0) return 0;
+  const size_t nch = (C_max + CHUNK_TILES * 16 - 1) / (CHUNK_TILES * 16);
+  const size_t c_pad = (size_t)((C_max + 3) / 4) * 4;
+  return ((size_t)R * 2 * H_q * head_dim + (size_t)R * 2 * H_q * c_pad + (size_t)R * 2 * H_q * nch * 2) *
+         sizeof(float);
+}
+
+extern "C" int gp_score_and_working_set(const void* q, int q_dtype, int B, int H_q, const float* qstate,
+                                        int num_slots, const int32_t* slot_ids, const int32_t* req_idx,
+                                        int R, const gp_kv_cache* kv, const int32_t* block_tables,
+                                        int max_pages, const int32_t* context_lens,
+                                        const int32_t* positions, float rope_theta, double p,
+                                        float sm_scale, float* a_short, float* a_long, int C_max,
+                                        int32_t* ws_counts, int32_t* n_cand, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (R < 0 || B < 0 || H_q <= 0 || num_slots <= 0 || !kv || max_pages <= 0 || C_max <= 0)
+    return GP_ERR_INVALID;
+  if (R == 0) return GP_OK;
+  if (!q || !qstate || !slot_ids || !req_idx || !block_tables || !context_lens || !positions ||
+      !a_short || !a_long || !ws_counts || !n_cand || !kv->k)
+    return GP_ERR_INVALID;
+  if (!(p > 0.0 && p <= 1.0)) return GP_ERR_INVALID;
+  const int H_kv = kv->num_kv_heads, D = kv->head_dim, b = kv->page_size;
+  if (H_kv <= 0 || H_q % H_kv != 0 || kv->num_pages <= 0) return GP_ERR_INVALID;
+  if (kv->page_tag) return GP_ERR_UNSUPPORTED;
+  if (q_dtype != kv->dtype || (q_dtype != GP_F32 && q_dtype != GP_BF16)) return GP_ERR_INVALID;
+  if (D != 64 && D != 128) return GP_ERR_UNSUPPORTED;
+  if (b < 16 || b > 256 || b % 16) return GP_ERR_UNSUPPORTED;
+  const int G = H_q / H_kv;
+  if (2 * G > 16) return GP_ERR_UNSUPPORTED;
+  if (C_max > WS_MAX_C || C_max % 4) return GP_ERR_UNSUPPORTED;
+  const size_t need = gp_score_and_working_set_workspace_size(R, H_q, H_kv, D, b, C_max);
+  if (!workspace || workspace_bytes < need) return GP_ERR_WORKSPACE;
+
+  ScoreParams P{};
+  P.q = q;
+  P.qstate = qstate;
+  P.slot_ids = slot_ids;
+  P.req_idx = req_idx;
+  P.k = kv->k;
+  P.block_tables = block_tables;
+  P.context_lens = context_lens;
+  P.positions = positions;
+  P.a_short = a_short;
+  P.a_long = a_long;
+  P.ws_counts = ws_counts;
+  P.n_cand = n_cand;
+  P.B = B;
+  P.R = R;
+  P.H_q = H_q;
+  P.H_kv = H_kv;
+  P.G = G;
+  P.D = D;
+  P.page_size = b;
+  P.num_pages = kv->num_pages;
+  P.max_pages = max_pages;
+  P.num_slots = num_slots;
+  P.C_max = C_max;
+  P.nch = (C_max + CHUNK_TILES * 16 - 1) / (CHUNK_TILES * 16);
+  P.q_bf16 = q_dtype == GP_BF16;
+  P.scale_log2 = sm_scale * GP_LOG2E;
+  P.rope_theta = rope_theta;
+  p_to_fixed(p, P.p_fixed);
+  float* ws = static_cast<float*>(workspace);
+  P.qt = ws;
+  P.logits = P.qt + (size_t)R * 2 * H_q * D;
+  P.stats = P.logits + (size_t)R * 2 * H_q * (size_t)((C_max + 3) / 4) * 4;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(prep_kernel, dim3(R), dim3(256), 0, s, P);
+  GP_CHECK_LAUNCH();
+  dim3 lg(P.nch, H_kv, R);
+  if (q_dtype == GP_BF16) {
+    if (D == 64) hipLaunchKernelGGL((logits_kernel<64, true>), lg, dim3(LG_THREADS), 0, s, P);
+    else hipLaunchKernelGGL((logits_kernel<128, true>), lg, dim3(LG_THREADS), 0, s, P);
+  } else {
+    if (D == 64) hipLaunchKernelGGL((logits_kernel<64, false>), lg, dim3(LG_THREADS), 0, s, P);
+    else hipLaunchKernelGGL((logits_kernel<128, false>), lg, dim3(LG_THREADS), 0, s, P);
+  }
+  GP_CHECK_LAUNCH();
+  hipLaunchKernelGGL(normalize_kernel, dim3((C_max + 1023) / 1024, H_kv, R), dim3(256), 0, s, P);
+  GP_CHECK_LAUNCH();
+  hipLaunchKernelGGL(working_set_kernel, dim3(2 * H_kv, R), dim3(WS_THREADS), 0, s, P);
+  GP_CHECK_LAUNCH();
+  return GP_OK;
+}

@@ -1,0 +1,223 @@
+"""Thin ctypes binding of ``libgrowpage.so`` (the C ABI in include/growpage.h).
+
+Argument marshalling only: torch tensors provide device memory and the current HIP stream;
+every step of the computation runs in the library's kernels. Importing this module does not
+touch the GPU; the first call loads the library and raises if it has not been built.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libgrowpage.so")
+
+GP_F32, GP_BF16 = 0, 1
+TAG_RELEASE, TAG_FP8, TAG_BF16 = 0, 1, 2
+COMPRESS, GROW, GROW_FALLBACK_COMPRESS, NO_PAGES = 0, 1, 2, 3
+POLICY_AUTO, POLICY_FORCE_COMPRESS, POLICY_FORCE_GROW, POLICY_INVERSE = 0, 1, 2, 3
+
+EXPORTED = (
+    "gp_version", "gp_status_string",
+    "gp_paged_decode_attn_workspace_size", "gp_paged_decode_attn",
+    "gp_update_query_summaries",
+    "gp_score_and_working_set_workspace_size", "gp_score_and_working_set",
+    "gp_compact_or_grow_workspace_size", "gp_compact_or_grow",
+)
+
+
+class GpKvCache(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("k8", ctypes.c_void_p), ("v8", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("page_tag", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_VP, _I, _SZ, _F, _D = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_double
+
+
+def lib():
+    """Load the HIP library once; raise if it is missing (there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run paged_kv_cache_472_amd/build.py or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        L.gp_version.restype = _I
+        L.gp_status_string.restype = ctypes.c_char_p
+        L.gp_status_string.argtypes = [_I]
+        L.gp_paged_decode_attn_workspace_size.restype = _SZ
+        L.gp_paged_decode_attn_workspace_size.argtypes = [_I] * 6
+        L.gp_paged_decode_attn.restype = _I
+        L.gp_paged_decode_attn.argtypes = [_VP, _I, _I, _I, ctypes.POINTER(GpKvCache), _VP, _I, _VP,
+                                           _I, _F, _VP, _VP, _VP, _SZ, _VP]
+        L.gp_update_query_summaries.restype = _I
+        L.gp_update_query_summaries.argtypes = [_VP, _I, _I, _I, _I, _VP, _VP, _VP, _I, _F, _F, _VP]
+        L.gp_score_and_working_set_workspace_size.restype = _SZ
+        L.gp_score_and_working_set_workspace_size.argtypes = [_I] * 6
+        L.gp_score_and_working_set.restype = _I
+        L.gp_score_and_working_set.argtypes = [_VP, _I, _I, _I, _VP, _I, _VP, _VP, _I,
+                                               ctypes.POINTER(GpKvCache), _VP, _I, _VP, _VP, _F, _D,
+                                               _F, _VP, _VP, _I, _VP, _VP, _VP, _SZ, _VP]
+        L.gp_compact_or_grow_workspace_size.restype = _SZ
+        L.gp_compact_or_grow_workspace_size.argtypes = [_I] * 5
+        L.gp_compact_or_grow.restype = _I
+        L.gp_compact_or_grow.argtypes = [_VP, _I, _I, _VP, _VP, _I, _VP, _VP, _D, _I, _I, _VP,
+                                         ctypes.POINTER(GpKvCache), _VP, _VP, _I, _VP, _VP, _VP, _VP,
+                                         _VP, _VP, _VP, _SZ, _VP]
+        _lib = L
+    return _lib
+
+
+def _check(status, what):
+    if status != 0:
+        msg = lib().gp_status_string(status).decode()
+        raise RuntimeError(f"{what} failed: {msg} ({status})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return GP_F32
+    if t.dtype == torch.bfloat16:
+        return GP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+class KVCache:
+    """Device tensors of one layer's paged cache (layouts in include/growpage.h)."""
+
+    def __init__(self, k, v, page_size, k8=None, v8=None, k_scale=None, v_scale=None, page_tag=None):
+        self.k, self.v, self.page_size = k, v, int(page_size)
+        self.k8, self.v8, self.k_scale, self.v_scale, self.page_tag = k8, v8, k_scale, v_scale, page_tag
+
+    @classmethod
+    def from_workload(cls, wl):
+        return cls(wl.k_pool, wl.v_pool, wl.page_size, wl.k8, wl.v8, wl.k_scale, wl.v_scale,
+                   wl.page_tag)
+
+    @property
+    def num_kv_heads(self):
+        return self.k.shape[1]
+
+    @property
+    def head_dim(self):
+        return self.k.shape[3]
+
+    def struct(self):
+        return GpKvCache(
+            _ptr(self.k), _ptr(self.v), _ptr(self.k8), _ptr(self.v8), _ptr(self.k_scale),
+            _ptr(self.v_scale), _ptr(self.page_tag), self.k.shape[0], self.page_size,
+            self.k.shape[1], self.k.shape[3], _dtype_code(self.k))
+
+
+def gp_paged_decode_attn_workspace_size(B, H_q, H_kv, head_dim, page_size, max_context):
+    return lib().gp_paged_decode_attn_workspace_size(B, H_q, H_kv, head_dim, page_size, max_context)
+
+
+def gp_paged_decode_attn(q, cache, block_tables, context_lens, max_context, sm_scale,
+                         out=None, lse=None, workspace=None):
+    """Decode attention; returns (out [B, H_q, d] in q's dtype, lse [B, H_q] fp32)."""
+    B, H_q, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    need = gp_paged_decode_attn_workspace_size(B, H_q, cache.num_kv_heads, d, cache.page_size,
+                                               max_context)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    kv = cache.struct()
+    st = lib().gp_paged_decode_attn(
+        _ptr(q), _dtype_code(q), B, H_q, ctypes.byref(kv), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), int(max_context), float(sm_scale), _ptr(out),
+        _ptr(lse), _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
+    _check(st, "gp_paged_decode_attn")
+    return out, lse
+
+
+def gp_update_query_summaries(q, slot_ids, fresh, qstate, beta_s, beta_l):
+    B, H_q, d = q.shape
+    st = lib().gp_update_query_summaries(_ptr(q), _dtype_code(q), B, H_q, d, _ptr(slot_ids),
+                                         _ptr(fresh), _ptr(qstate), qstate.shape[0],
+                                         float(beta_s), float(beta_l), _stream())
+    _check(st, "gp_update_query_summaries")
+    return qstate
+
+
+def gp_score_and_working_set_workspace_size(R, H_q, H_kv, head_dim, page_size, C_max):
+    return lib().gp_score_and_working_set_workspace_size(R, H_q, H_kv, head_dim, page_size, C_max)
+
+
+def gp_score_and_working_set(q, qstate, slot_ids, req_idx, cache, block_tables, context_lens,
+                             positions, rope_theta, p, sm_scale, C_max, a_short=None,
+                             a_long=None, ws_counts=None, n_cand=None, workspace=None):
+    """Returns (a_short, a_long [R, H_kv, C_max] fp32, ws_counts [R, H_kv, 2], n_cand [R])."""
+    B, H_q, d = q.shape
+    R = req_idx.numel()
+    H_kv = cache.num_kv_heads
+    dev = q.device
+    if a_short is None:
+        a_short = torch.empty((R, H_kv, C_max), dtype=torch.float32, device=dev)
+    if a_long is None:
+        a_long = torch.empty((R, H_kv, C_max), dtype=torch.float32, device=dev)
+    if ws_counts is None:
+        ws_counts = torch.empty((R, H_kv, 2), dtype=torch.int32, device=dev)
+    if n_cand is None:
+        n_cand = torch.empty((R,), dtype=torch.int32, device=dev)
+    need = gp_score_and_working_set_workspace_size(R, H_q, H_kv, d, cache.page_size, C_max)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    kv = cache.struct()
+    st = lib().gp_score_and_working_set(
+        _ptr(q), _dtype_code(q), B, H_q, _ptr(qstate), qstate.shape[0], _ptr(slot_ids),
+        _ptr(req_idx), R, ctypes.byref(kv), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), _ptr(positions), float(rope_theta), float(p), float(sm_scale),
+        _ptr(a_short), _ptr(a_long), int(C_max), _ptr(ws_counts), _ptr(n_cand), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream())
+    _check(st, "gp_score_and_working_set")
+    return a_short, a_long, ws_counts, n_cand
+
+
+def gp_compact_or_grow_workspace_size(R, H_kv, max_pages, page_size, C_max):
+    return lib().gp_compact_or_grow_workspace_size(R, H_kv, max_pages, page_size, C_max)
+
+
+def gp_compact_or_grow(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, policy, cache,
+                       block_tables, n_pages, context_lens, refcount, free_stack, free_top,
+                       policies=None, decision=None, kept_idx=None, workspace=None):
+    """Returns (decision [R] int32, kept_idx [R, H_kv, C_max] int32); state updated in place."""
+    R = req_idx.numel()
+    H_kv = cache.num_kv_heads
+    C_max = a_short.shape[2]
+    dev = a_short.device
+    if decision is None:
+        decision = torch.empty((R,), dtype=torch.int32, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty((R, H_kv, C_max), dtype=torch.int32, device=dev)
+    need = gp_compact_or_grow_workspace_size(R, H_kv, block_tables.shape[1], cache.page_size, C_max)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    kv = cache.struct()
+    st = lib().gp_compact_or_grow(
+        _ptr(req_idx), R, block_tables.shape[0], _ptr(a_short), _ptr(a_long), C_max,
+        _ptr(ws_counts), _ptr(n_cand), float(tau), int(k_loc), int(policy), _ptr(policies),
+        ctypes.byref(kv), _ptr(block_tables), _ptr(n_pages), block_tables.shape[1],
+        _ptr(context_lens), _ptr(refcount), _ptr(free_stack), _ptr(free_top), _ptr(decision),
+        _ptr(kept_idx), _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
+    _check(st, "gp_compact_or_grow")
+    return decision, kept_idx

@@ -1,0 +1,118 @@
+"""GPU parity: gp_paged_decode_attn (HIP, through the C ABI) vs the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_472_amd as gp
+from oracle import attention as oatt
+from gpu_common import (DEV, TOL, gather_pages_to_host, maxabs, sample_requests, say,
+                        workload_on_gpu)
+from util import f64, npy
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_gpu(wl, q=None, bt=None, ctx=None, max_context=None):
+    cache = gp.KVCache.from_workload(wl)
+    out, lse = gp.gp_paged_decode_attn(
+        wl.q if q is None else q, cache, wl.block_tables if bt is None else bt,
+        wl.context_lens if ctx is None else ctx,
+        wl.max_context if max_context is None else max_context, wl.sm_scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _mixed_np(sub_or_wl):
+    g = (lambda n: sub_or_wl[n]) if isinstance(sub_or_wl, dict) else (lambda n: getattr(sub_or_wl, n))
+    return dict(page_tag=npy(g("page_tag")), k8=npy(g("k8")), v8=npy(g("v8")),
+                k_scale=npy(g("k_scale")), v_scale=npy(g("v_scale")))
+
+
+@pytest.mark.parametrize("cfg", ["1", "2", "3a", "3b", "4", "5"])
+def test_decode_small_elementwise(cfg):
+    wl = workload_on_gpu(cfg, "small")
+    out, lse = _run_gpu(wl)
+    extra = _mixed_np(wl) if wl.mixed else {}
+    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
+                                          npy(wl.block_tables), npy(wl.context_lens),
+                                          wl.page_size, wl.sm_scale, **extra)
+    eo, nan_o = maxabs(f64(out), ref_o)
+    el, nan_l = maxabs(lse.cpu().numpy(), ref_l)
+    say(f"[decode small {cfg}] max|out-ref|={eo:.3e} max|lse-ref|={el:.3e}")
+    assert not nan_o and not nan_l
+    assert eo <= TOL[wl.dtype] and el <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("cfg", ["2", "3a", "3b", "4", "5"])
+def test_decode_full_size_sampled(cfg):
+    wl = workload_on_gpu(cfg, "full")
+    out, lse = _run_gpu(wl)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    reqs = sample_requests(wl, 3)
+    sub, bt = gather_pages_to_host(wl, reqs)
+    extra = _mixed_np(sub) if wl.mixed else {}
+    q = f64(wl.q[reqs])
+    ctx = npy(wl.context_lens[reqs])
+    ref_o, ref_l = oatt.paged_decode_attn(q, f64(sub["k_pool"]), f64(sub["v_pool"]), bt, ctx,
+                                          wl.page_size, wl.sm_scale, **extra)
+    eo, nan_o = maxabs(f64(out[reqs]), ref_o)
+    el, nan_l = maxabs(lse[reqs].cpu().numpy(), ref_l)
+    say(f"[decode full {cfg}] requests={reqs} max|out-ref|={eo:.3e} max|lse-ref|={el:.3e}")
+    assert not nan_o and not nan_l
+    assert eo <= TOL[wl.dtype] and el <= TOL[wl.dtype]
+
+
+def test_decode_deterministic_and_grow_bit_identical():
+    wl = workload_on_gpu("2", "small")
+    o1, l1 = _run_gpu(wl)
+    o2, l2 = _run_gpu(wl)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # append a free page to every block table without changing the context: output unchanged
+    bt = wl.block_tables.clone()
+    top = int(wl.free_top.item())
+    for r in range(wl.B):
+        bt[r, int(wl.n_pages[r])] = int(wl.free_stack[top - 1 - r])
+    o3, l3 = _run_gpu(wl, bt=bt)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_decode_edge_cases():
+    wl = workload_on_gpu("2", "small")
+    ctx = wl.context_lens.clone()
+    # empty, one token, exactly one page, a page plus one token; plus a huge max_context bound
+    ctx[0], ctx[1], ctx[2] = 0, 1, 16
+    out, lse = _run_gpu(wl, ctx=ctx, max_context=wl.max_pages * wl.page_size)
+    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
+                                          npy(wl.block_tables), npy(ctx), wl.page_size, wl.sm_scale)
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    eo, nan_o = maxabs(f64(out), ref_o)
+    el, _ = maxabs(lse.cpu().numpy(), ref_l)
+    say(f"[decode edge] max|out-ref|={eo:.3e} max|lse-ref|={el:.3e}")
+    assert not nan_o and eo <= TOL["bf16"] and el <= TOL["bf16"]
+    # invalid block-table entries are skipped, never dereferenced
+    bt = wl.block_tables.clone()
+    bt[1, 0] = -5
+    bt[2, 0] = wl.num_pages + 100
+    out2, _ = _run_gpu(wl, bt=bt, ctx=ctx)
+    assert torch.isfinite(out2.float()).all()
+    # a single request, and batch 0
+    o1, _ = gp.gp_paged_decode_attn(wl.q[:1].contiguous(), gp.KVCache.from_workload(wl),
+                                    wl.block_tables[:1].contiguous(), wl.context_lens[:1].contiguous(),
+                                    wl.max_context, wl.sm_scale)
+    torch.cuda.synchronize()
+    o_all, _ = _run_gpu(wl)
+    assert torch.equal(o1[0], o_all[0])
+
+
+def test_decode_lse_and_split_count_independence():
+    """The same request decoded with a different split plan (other batch size) agrees."""
+    wl = workload_on_gpu("3b", "small")
+    out, lse = _run_gpu(wl)
+    for r in range(wl.B):
+        o1, l1 = gp.gp_paged_decode_attn(wl.q[r:r + 1].contiguous(), gp.KVCache.from_workload(wl),
+                                         wl.block_tables[r:r + 1].contiguous(),
+                                         wl.context_lens[r:r + 1].contiguous(), wl.max_pages * wl.page_size,
+                                         wl.sm_scale)
+        torch.cuda.synchronize()
+        e, _ = maxabs(f64(o1[0]), f64(out[r]))
+        assert e <= 1e-2
