@@ -1,0 +1,415 @@
+"""Benchmark of the paged-KV hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of the Qwen3-8B-shaped decode layer
+(64 requests, contexts uniform in [4096, 16384], 32 query / 8 KV heads, head_dim 128, 16-token
+pages, bf16): the dual-timescale summary update of every request, paged decode attention of
+every request (split partials plus their merge), and the page-boundary pass of the requests that
+sit at a page boundary (scores, working sets, compress-or-grow with compaction). Compaction and
+page growth are destructive, so each step first restores the small integer page state (block
+tables, lengths, page counts, refcounts, free stack) with one device copy, inside the timed
+region; K/V pages are left as the previous step's compaction wrote them (still valid tokens, same
+amount of work).
+
+Prints one JSON line. `value` is the step's algorithmic HBM bytes divided by the step time;
+`roofline` is the decode call (its two kernels) against the 8 TB/s HBM peak, timed with HIP
+events on the stream the kernels are launched on; `cpu_baseline` is the float64 CPU oracle on
+a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "paged decode attention KV GB/s (% HBM peak) + boundary-pass latency/request"
+PMC_FILE = os.path.join(ROOT, "profiles", "decode_qwen3_8b_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_472_amd", "csrc", "decode.hip")
+
+WORKLOAD_NAMES = {
+    "1": "tiny decode step (B=2, ctx 200/333, Hq=8, Hkv=2, d=64, fp32)",
+    "2": "Qwen3-8B-shaped decode layer (B=64, ctx U[4096,16384], Hq=32, Hkv=8, d=128, b=16, bf16)",
+    "3a": "long-reasoning mix, 8/2 heads d=64 (B=256, lognormal ctx, bf16)",
+    "3b": "long-reasoning mix, 32/8 heads d=128 (B=256, lognormal ctx, bf16)",
+    "4": "prefix-shared batch (B=128, shared 2048 + U[1024,8192], Hq=40, Hkv=8, d=128, bf16)",
+    "5": "mixed-precision pages (B=128, ctx U[8192,24576], 30/40/30 release/fp8/bf16)",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the oracle's timed sample (0 disables the cpu_baseline leg)")
+    ap.add_argument("--copy-probe-gib", type=float, default=1.0,
+                    help="size of the plain device copy timed beside the path (HBM reference)")
+    return ap.parse_args()
+
+
+def file_sha(path):
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+class Path:
+    """Preallocated buffers and the per-step launch sequence of one workload."""
+
+    def __init__(self, wl, gp, torch):
+        self.wl, self.gp, self.torch = wl, gp, torch
+        dev = wl.q.device
+        i32 = torch.int32
+        # integer page state in one flat buffer so a step can restore it with one copy
+        names = ("block_tables", "n_pages", "context_lens", "refcount", "free_stack", "free_top")
+        sizes = [getattr(wl, n).numel() for n in names]
+        self.meta = torch.empty(sum(sizes), dtype=i32, device=dev)
+        off = 0
+        for n, sz in zip(names, sizes):
+            t = getattr(wl, n)
+            view = self.meta[off:off + sz].view(t.shape)
+            view.copy_(t)
+            setattr(wl, n, view)
+            off += sz
+        self.meta0 = self.meta.clone()
+        self.cache = gp.KVCache.from_workload(wl)
+        B, H_q, d = wl.q.shape
+        H_kv = wl.H_kv
+        self.out = torch.empty_like(wl.q)
+        self.lse = torch.empty((B, H_q), dtype=torch.float32, device=dev)
+        n = gp.gp_paged_decode_attn_workspace_size(B, H_q, H_kv, d, wl.page_size, wl.max_context)
+        self.dws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+        self.fresh0 = torch.zeros(B, dtype=torch.uint8, device=dev)
+        self.R = wl.req_idx.numel()
+        if self.R:
+            req = wl.req_idx.cpu().tolist()
+            ctx = wl.context_lens.cpu().tolist()
+            b = wl.page_size
+            cm = max(max(0, (math.ceil(ctx[r] / b) - 1) * b) for r in req)
+            self.C_max = max(16, -(-cm // 16) * 16)
+            R, C = self.R, self.C_max
+            self.a_s = torch.empty((R, H_kv, C), dtype=torch.float32, device=dev)
+            self.a_l = torch.empty_like(self.a_s)
+            self.wsc = torch.empty((R, H_kv, 2), dtype=i32, device=dev)
+            self.ncand = torch.empty((R,), dtype=i32, device=dev)
+            n = gp.gp_score_and_working_set_workspace_size(R, H_q, H_kv, d, b, C)
+            self.sws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+            self.dec = torch.empty((R,), dtype=i32, device=dev)
+            self.kept = torch.empty((R, H_kv, C), dtype=i32, device=dev)
+            n = gp.gp_compact_or_grow_workspace_size(R, H_kv, wl.max_pages, b, C)
+            self.cws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+            self.policies = torch.as_tensor(wl.req_policy, dtype=i32, device=dev)
+
+    def build_state(self):
+        """Summaries after the past queries (first one initialises the slot)."""
+        wl, gp, torch = self.wl, self.gp, self.torch
+        ones = torch.ones_like(self.fresh0)
+        for t in range(wl.q_hist.shape[0]):
+            gp.gp_update_query_summaries(wl.q_hist[t].contiguous(), wl.slot_ids,
+                                         ones if t == 0 else self.fresh0, wl.qstate,
+                                         wl.beta_s, wl.beta_l)
+
+    def step(self, ev=None):
+        wl, gp = self.wl, self.gp
+        rec = (lambda k: ev[k].record()) if ev is not None else (lambda k: None)
+        rec(0)
+        self.meta.copy_(self.meta0)
+        rec(1)
+        gp.gp_update_query_summaries(wl.q, wl.slot_ids, self.fresh0, wl.qstate, wl.beta_s,
+                                     wl.beta_l)
+        rec(2)
+        gp.gp_paged_decode_attn(wl.q, self.cache, wl.block_tables, wl.context_lens,
+                                wl.max_context, wl.sm_scale, out=self.out, lse=self.lse,
+                                workspace=self.dws)
+        rec(3)
+        if self.R:
+            gp.gp_score_and_working_set(wl.q, wl.qstate, wl.slot_ids, wl.req_idx, self.cache,
+                                        wl.block_tables, wl.context_lens, wl.positions,
+                                        wl.rope_theta, wl.p, wl.sm_scale, self.C_max,
+                                        a_short=self.a_s, a_long=self.a_l, ws_counts=self.wsc,
+                                        n_cand=self.ncand, workspace=self.sws)
+            rec(4)
+            gp.gp_compact_or_grow(wl.req_idx, self.a_s, self.a_l, self.wsc, self.ncand, wl.tau,
+                                  wl.k_loc, 0, self.cache, wl.block_tables, wl.n_pages,
+                                  wl.context_lens, wl.refcount, wl.free_stack, wl.free_top,
+                                  policies=self.policies, decision=self.dec,
+                                  kept_idx=self.kept, workspace=self.cws)
+        rec(5)
+
+
+def algorithmic_bytes(wl, path, np):
+    """Bytes each row must move at least once (HBM), per step."""
+    es = 4 if wl.dtype == "f32" else 2
+    B, H_q, d, H_kv, b = wl.B, wl.H_q, wl.d, wl.H_kv, wl.page_size
+    ctx = wl.context_lens.cpu().numpy().astype(np.int64)
+    if wl.mixed:
+        tags = wl.page_tag.cpu().numpy()
+        bt = wl.block_tables.cpu().numpy()
+        kv = 0
+        for r in range(B):
+            n = int(ctx[r])
+            pages = bt[r, np.arange(n) // b]
+            t = tags[pages]
+            kv += int((t == 2).sum()) * H_kv * d * 2 * 2            # bf16 K + V
+            kv += int((t == 1).sum()) * H_kv * (d * 2 + 2 * 4)     # fp8 K + V codes + 2 scales
+    else:
+        kv = int(ctx.sum()) * H_kv * d * es * 2
+    pages = int(sum(math.ceil(c / b) for c in ctx))
+    decode = kv + 2 * B * H_q * d * es + B * H_q * 4 + pages * 4 + B * 4
+    summaries = B * H_q * d * (es + 4 * 4) + B * 5
+    out = dict(decode=decode, decode_kv=kv, summaries=summaries, score=0, compact=0)
+    if path.R:
+        req = wl.req_idx.cpu().tolist()
+        for r in req:
+            c = max(0, (math.ceil(int(ctx[r]) / b) - 1) * b)
+            out["score"] += c * H_kv * d * es + 4 * H_kv * c * 4
+    return out
+
+
+def moved_bytes(wl, path, ctx_before, np):
+    """K/V bytes read and written by the last step's compaction (tokens that shifted)."""
+    if not path.R:
+        return 0
+    es = 4 if wl.dtype == "f32" else 2
+    kept = path.kept.cpu().numpy()
+    dec = path.dec.cpu().numpy()
+    nc = path.ncand.cpu().numpy()
+    ctx_after = wl.context_lens.cpu().numpy()
+    req = wl.req_idx.cpu().tolist()
+    tot = 0
+    for i, r in enumerate(req):
+        if dec[i] not in (0, 2) or ctx_after[r] == ctx_before[r]:
+            continue
+        for h in range(wl.H_kv):
+            row = kept[i, h, :nc[i]]
+            same = np.nonzero(row != np.arange(len(row)))[0]
+            first = int(same[0]) if len(same) else int(ctx_after[r])
+            tot += (int(ctx_after[r]) - first) * wl.d * es * 2 * 2   # K and V, read + write
+    return tot
+
+
+def cpu_baseline(wl, path, budget_s, np):
+    """The float64 oracle on a bounded sample: decode of whole requests, then the boundary pass
+    of boundary requests, until the time budget is used. Returns GB/s on the same byte model."""
+    import torch
+    from oracle import attention as oatt
+    from oracle import boundary as ob
+    from oracle import summaries as osum
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    b = wl.page_size
+    es = 4 if wl.dtype == "f32" else 2
+    ctx = wl.context_lens.cpu().numpy().astype(np.int64)
+    bt_all = wl.block_tables.cpu().numpy().astype(np.int64)
+
+    def host_pages(reqs):
+        rows = bt_all[reqs]
+        pages = np.unique(rows[rows >= 0])
+        idx = torch.as_tensor(pages, device=wl.k_pool.device, dtype=torch.long)
+        remap = np.full(wl.num_pages, -1, dtype=np.int64)
+        remap[pages] = np.arange(len(pages))
+        sub = {"k": wl.k_pool.index_select(0, idx).cpu().double().numpy(),
+               "v": wl.v_pool.index_select(0, idx).cpu().double().numpy()}
+        if wl.mixed:
+            for nm in ("k8", "v8", "k_scale", "v_scale", "page_tag"):
+                sub[nm] = getattr(wl, nm).index_select(0, idx).cpu().numpy()
+        bt = np.where(rows >= 0, remap[np.maximum(rows, 0)], -1)
+        return sub, bt
+
+    t_used, bytes_done, what = 0.0, 0, []
+    # summaries: one update of every request (small)
+    qst = wl.qstate.cpu().double().numpy()
+    q64 = wl.q.cpu().double().numpy()
+    t0 = time.perf_counter()
+    osum.update_query_summaries(q64, wl.slot_ids.cpu().numpy(), [False] * wl.B, qst,
+                                wl.beta_s, wl.beta_l)
+    t_used += time.perf_counter() - t0
+    bytes_done += wl.B * wl.H_q * wl.d * (es + 16)
+    what.append(f"summary update of all {wl.B} requests")
+    # decode, request by request
+    n_dec = 0
+    for r in range(wl.B):
+        if t_used > 0.6 * budget_s:
+            break
+        sub, bt = host_pages([r])
+        extra = {}
+        if wl.mixed:
+            extra = dict(page_tag=sub["page_tag"], k8=sub["k8"], v8=sub["v8"],
+                         k_scale=sub["k_scale"], v_scale=sub["v_scale"])
+        t0 = time.perf_counter()
+        oatt.paged_decode_attn(q64[r:r + 1], sub["k"], sub["v"], bt, ctx[r:r + 1], b,
+                               wl.sm_scale, **extra)
+        t_used += time.perf_counter() - t0
+        bytes_done += int(ctx[r]) * wl.H_kv * wl.d * es * 2
+        n_dec += 1
+    what.append(f"decode of {n_dec} of {wl.B} requests")
+    # boundary pass, request by request
+    n_bnd = 0
+    if path.R and not wl.mixed:
+        req = wl.req_idx.cpu().tolist()
+        pol = list(wl.req_policy)
+        for i, r in enumerate(req):
+            if t_used > budget_s:
+                break
+            sub, bt = host_pages([r])
+            t0 = time.perf_counter()
+            a_s, a_l, ws, nc = ob.score_and_working_set(
+                q64[r:r + 1], qst, wl.slot_ids[r:r + 1].cpu().numpy(), [0], sub["k"], bt,
+                ctx[r:r + 1], wl.positions[r:r + 1].cpu().numpy(), b, wl.rope_theta, wl.p,
+                wl.sm_scale)
+            st = dict(bt=bt.copy(), n_pages=wl.n_pages[r:r + 1].cpu().numpy().astype(np.int64),
+                      ctx=ctx[r:r + 1].copy(), rc=np.ones(sub["k"].shape[0], dtype=np.int64),
+                      fs=np.full(sub["k"].shape[0] + 1, -1, dtype=np.int64),
+                      top=np.zeros(1, dtype=np.int64))
+            ob.compact_or_grow([0], a_s, a_l, ws, nc, wl.tau, wl.k_loc, ob.POLICY_FORCE_COMPRESS,
+                               sub["k"], sub["v"], st["bt"], st["n_pages"], st["ctx"], st["rc"],
+                               st["fs"], st["top"], b, policies=[ob.POLICY_FORCE_COMPRESS])
+            t_used += time.perf_counter() - t0
+            c = int(nc[0])
+            bytes_done += c * wl.H_kv * wl.d * es + 4 * wl.H_kv * c * 4
+            n_bnd += 1
+        what.append(f"boundary pass (score, working set, forced compress) of {n_bnd} of "
+                    f"{len(req)} boundary requests")
+    gbps = bytes_done / t_used / 1e9 if t_used > 0 else None
+    return dict(value=gbps, unit="GB/s", cores=int(blas), kind="oracle",
+                sample="; ".join(what) + f"; {t_used:.1f} s of oracle time, bytes on the "
+                       "same algorithmic model as value (numpy float64; BLAS threads = cores, "
+                       "elementwise numpy single-threaded)",
+                seconds=round(t_used, 2))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import paged_kv_cache_472_amd as gp
+    from workloads import make_workload
+
+    gp.lib()  # raises if the HIP library is missing: there is no other path
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda:0"
+    print(f"[bench] building workload {args.config} on {dev}", file=sys.stderr, flush=True)
+    wl = make_workload(args.config, "full", device=dev)
+    path = Path(wl, gp, torch)
+    path.build_state()
+    torch.cuda.synchronize()
+    ctx_before = wl.context_lens.cpu().numpy().copy()
+
+    nev = 6
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        path.step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        path.step(events[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    def avg_ms(a, z):
+        return sum(events[k][a].elapsed_time(events[k][z]) for k in range(args.steps)) / args.steps
+
+    rows_ms = dict(restore=avg_ms(0, 1), update_query_summaries=avg_ms(1, 2),
+                   paged_decode_attn=avg_ms(2, 3))
+    if path.R:
+        rows_ms["score_and_working_set"] = avg_ms(3, 4)
+        rows_ms["compact_or_grow"] = avg_ms(4, 5)
+    event_step_ms = avg_ms(0, 5)
+
+    by = algorithmic_bytes(wl, path, np)
+    by["compact"] = moved_bytes(wl, path, ctx_before, np)
+    step_bytes = by["decode"] + by["summaries"] + by["score"] + by["compact"]
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    dec_ms = rows_ms["paged_decode_attn"]
+    achieved = by["decode"] / (dec_ms * 1e-3) / 1e9
+
+    # plain device copy of known size: the practical HBM ceiling on this machine
+    nbytes = int(args.copy_probe_gib * (1 << 30))
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    traffic = None
+    if os.path.exists(PMC_FILE):
+        with open(PMC_FILE) as fh:
+            pmc = json.load(fh)
+        if pmc.get("decode_src_sha") == file_sha(DECODE_SRC) and pmc.get("config") == args.config:
+            traffic = pmc.get("bytes_per_launch")
+
+    boundary = None
+    if path.R:
+        bnd_ms = rows_ms["score_and_working_set"] + rows_ms["compact_or_grow"]
+        boundary = dict(requests=path.R, us_per_request=bnd_ms * 1e3 / path.R,
+                        score_us=rows_ms["score_and_working_set"] * 1e3,
+                        compact_us=rows_ms["compact_or_grow"] * 1e3,
+                        decisions=path.dec.cpu().tolist())
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        print(f"[bench] cpu_baseline (oracle, ~{args.cpu_seconds:.0f} s)", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(wl, path, args.cpu_seconds, np)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "batch": wl.B,
+                   "mean_context": round(float(wl.context_lens.float().mean()), 1),
+                   "boundary_requests": path.R, "page_size": wl.page_size},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "paged_decode_attn (split + merge launches)",
+                     "bytes_per_launch": by["decode"], "avg_launch_ms": round(dec_ms, 4)},
+        "cpu_baseline": cpu,
+        "decode_kv_gbps": round(by["decode_kv"] / (dec_ms * 1e-3) / 1e9, 1),
+        "decode_frac_of_copy": round(achieved / copy_gbps, 4),
+        "copy_gbps": round(copy_gbps, 1),
+        "boundary": boundary,
+        "rows_ms": {k: round(v, 4) for k, v in rows_ms.items()},
+        "event_ms_per_step": round(event_step_ms, 4),
+        "bytes_per_step": by,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

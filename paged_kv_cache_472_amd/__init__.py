@@ -6,8 +6,11 @@ include/growpage.h); :mod:`.growpage` is its ctypes binding.
 from .growpage import (  # noqa: F401
     KVCache,
     gp_compact_or_grow,
+    gp_compact_or_grow_workspace_size,
     gp_paged_decode_attn,
+    gp_paged_decode_attn_workspace_size,
     gp_score_and_working_set,
+    gp_score_and_working_set_workspace_size,
     gp_update_query_summaries,
     lib,
 )

@@ -172,13 +172,15 @@ __global__ __launch_bounds__(64) void decide_alloc_kernel(CParams P) {
         int32_t* row = P.block_tables + (size_t)r * P.max_pages;
         int cnt = 0;
         bool bad = false;
-        for (int j0 = 0; j0 < n_dest; j0 += 64) {
+        // every page the compaction may read (all Pn) must be a valid id; the first n_dest
+        // are written, so the shared ones among them need a replacement
+        for (int j0 = 0; j0 < Pn; j0 += 64) {
           const int j = j0 + lane;
           bool sh = false;
-          if (j < n_dest) {
+          if (j < Pn) {
             const int pg = row[j];
             if (pg < 0 || pg >= P.num_pages) bad = true;
-            else sh = P.refcount[pg] > 1;
+            else sh = j < n_dest && P.refcount[pg] > 1;
           }
           cnt += __popcll(__ballot(sh));
         }

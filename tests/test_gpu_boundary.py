@@ -199,6 +199,5 @@ def test_compact_deterministic_and_prefix_untouched():
     assert torch.equal(d1, d2)
     for i, n in enumerate(nc.tolist()):   # entries past |C| are not written by contract
         assert torch.equal(k1[i, :, :n], k2[i, :, :n])
-    for k, v in wl.snapshot().items():
-        assert torch.equal(v.view(torch.int16) if v.dtype == torch.bfloat16 else v,
-                           s1[k].view(torch.int16) if v.dtype == torch.bfloat16 else s1[k]), k
+    for k, v in wl.snapshot().items():   # bit patterns: the state pool holds NaN poison
+        assert np.array_equal(bits(v), bits(s1[k])), k
