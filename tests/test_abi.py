@@ -1,0 +1,125 @@
+"""CPU checks of the C ABI: the HIP library loads, exports every function include/growpage.h
+declares, and rejects invalid arguments on the host before anything is launched (no GPU needed;
+every call below returns during argument validation)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "growpage.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from paged_kv_cache_472_amd import growpage
+    if not os.path.exists(growpage.LIB_PATH):
+        from paged_kv_cache_472_amd.build import build
+        build()
+    return growpage.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gp_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("gp_paged_decode_attn", "gp_update_query_summaries", "gp_score_and_working_set",
+              "gp_compact_or_grow"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from paged_kv_cache_472_amd import growpage
+    names = declared_functions()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(growpage.EXPORTED) == names
+    dyn = subprocess.run(["nm", "-D", "--defined-only", growpage.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in dyn.splitlines() if ln.strip()}
+    assert set(names) <= exported
+
+
+def test_version_and_status_strings(lib):
+    m = re.search(r"#define\s+GP_VERSION\s+(\d+)", open(HEADER).read())
+    assert lib.gp_version() == int(m.group(1))
+    assert lib.gp_status_string(0) == b"ok"
+    for code in (-1, -2, -3, -4):
+        assert lib.gp_status_string(code) not in (b"ok", b"unknown status")
+    assert lib.gp_status_string(7) == b"unknown status"
+
+
+def test_workspace_sizes(lib):
+    # one 16-token tile fits one split: no workspace; long contexts need split partials
+    assert lib.gp_paged_decode_attn_workspace_size(2, 8, 2, 64, 16, 16) == 0
+    big = lib.gp_paged_decode_attn_workspace_size(64, 32, 8, 128, 16, 16384)
+    assert big > 0 and big % (4 * 130) == 0
+    assert lib.gp_paged_decode_attn_workspace_size(-1, 32, 8, 128, 16, 16384) == 0
+    s1 = lib.gp_score_and_working_set_workspace_size(4, 32, 8, 128, 16, 8192)
+    s2 = lib.gp_score_and_working_set_workspace_size(8, 32, 8, 128, 16, 8192)
+    assert 0 < s1 < s2
+    c1 = lib.gp_compact_or_grow_workspace_size(4, 8, 1028, 16, 16384)
+    assert c1 > 0 and lib.gp_compact_or_grow_workspace_size(0, 8, 1028, 16, 16384) == 0
+
+
+def _kv(growpage, D=128, b=16, fake=True, dtype=1):
+    p = ctypes.c_void_p(0x1000) if fake else None
+    return growpage.GpKvCache(p, p, None, None, None, None, None, 100, b, 8, D, dtype)
+
+
+def test_invalid_arguments_rejected_on_host(lib):
+    from paged_kv_cache_472_amd import growpage
+    fake = ctypes.c_void_p(0x1000)
+    kv = _kv(growpage)
+    # negative batch, null pointers, head_dim 96, page size 24, dtype mismatch, missing workspace
+    assert lib.gp_paged_decode_attn(fake, 1, -1, 32, ctypes.byref(kv), fake, 8, fake, 128, 0.1,
+                                    fake, None, None, 0, None) == -1
+    assert lib.gp_paged_decode_attn(None, 1, 4, 32, ctypes.byref(kv), fake, 8, fake, 128, 0.1,
+                                    fake, None, None, 0, None) == -1
+    kv96 = _kv(growpage, D=96)
+    assert lib.gp_paged_decode_attn(fake, 1, 4, 32, ctypes.byref(kv96), fake, 8, fake, 128, 0.1,
+                                    fake, None, None, 0, None) == -2
+    kvb = _kv(growpage, b=24)
+    assert lib.gp_paged_decode_attn(fake, 1, 4, 32, ctypes.byref(kvb), fake, 8, fake, 128, 0.1,
+                                    fake, None, None, 0, None) == -2
+    assert lib.gp_paged_decode_attn(fake, 0, 4, 32, ctypes.byref(kv), fake, 8, fake, 128, 0.1,
+                                    fake, None, None, 0, None) == -1
+    assert lib.gp_paged_decode_attn(fake, 1, 64, 32, ctypes.byref(kv), fake, 1024, fake, 16384,
+                                    0.1, fake, None, None, 0, None) == -3
+    # max_context beyond the block table's reach
+    assert lib.gp_paged_decode_attn(fake, 1, 4, 32, ctypes.byref(kv), fake, 8, fake, 1000, 0.1,
+                                    fake, None, None, 0, None) == -1
+    # summaries: bad dtype, H_q * d not a multiple of 4
+    assert lib.gp_update_query_summaries(fake, 7, 4, 32, 128, fake, fake, fake, 16, 0.9,
+                                         0.999, None) == -1
+    assert lib.gp_update_query_summaries(fake, 0, 4, 1, 3, fake, fake, fake, 16, 0.9,
+                                         0.999, None) == -2
+    # score: p outside (0, 1], C_max not a multiple of 4, missing workspace
+    args = lambda p, cmax, ws, wsb: (fake, 1, 4, 32, fake, 16, fake, fake, 2, ctypes.byref(kv),  # noqa: E731
+                                     fake, 8, fake, fake, 10000.0, p, 0.1, fake, fake, cmax, fake,
+                                     fake, ws, wsb, None)
+    assert lib.gp_score_and_working_set(*args(0.0, 128, fake, 1 << 30)) == -1
+    assert lib.gp_score_and_working_set(*args(1.5, 128, fake, 1 << 30)) == -1
+    assert lib.gp_score_and_working_set(*args(0.99, 126, fake, 1 << 30)) == -2
+    assert lib.gp_score_and_working_set(*args(0.99, 128, None, 0)) == -3
+    # compact: bad policy, NaN tau, unsupported page size, missing workspace
+    cargs = lambda tau, pol, kvx, ws, wsb: (fake, 2, 4, fake, fake, 128, fake, fake, tau, 4, pol,  # noqa: E731
+                                            None, ctypes.byref(kvx), fake, fake, 8, fake, fake,
+                                            fake, fake, fake, fake, ws, wsb, None)
+    assert lib.gp_compact_or_grow(*cargs(0.0, 9, kv, fake, 1 << 30)) == -1
+    assert lib.gp_compact_or_grow(*cargs(float("nan"), 0, kv, fake, 1 << 30)) == -1
+    kv64 = _kv(growpage, b=64)
+    assert lib.gp_compact_or_grow(*cargs(0.0, 0, kv64, fake, 1 << 30)) == -2
+    assert lib.gp_compact_or_grow(*cargs(0.0, 0, kv, None, 0)) == -3
+    # R = 0 and B = 0 are no-ops that succeed without touching anything
+    assert lib.gp_compact_or_grow(None, 0, 4, None, None, 128, None, None, 0.0, 4, 0, None,
+                                  ctypes.byref(kv), None, None, 8, None, None, None, None, None,
+                                  None, None, 0, None) == 0
+    assert lib.gp_paged_decode_attn(None, 1, 0, 32, ctypes.byref(kv), None, 8, None, 128, 0.1,
+                                    None, None, None, 0, None) == 0
