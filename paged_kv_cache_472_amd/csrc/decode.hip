@@ -1,26 +1,38 @@
 // Paged decode attention for gfx950 (PASK Sec. 3.1 attention definition, App. B.5 split-KV
 // merge and mixed-precision page reads; GrowPage Sec. 4.2 block tables).
 //
-// Work decomposition: one workgroup (4 wave64s) per (split of a request's tokens, KV head,
-// request). A split is a run of 16-token tiles; wave w takes tiles w, w+4, ... of the split.
-// Per tile the G query heads of the KV head are contracted against the key tile on the
-// matrix cores (keys as the 16-row operand, heads as the 16-column operand, so the result
-// lands with one head per lane column), an online softmax runs on the 4 logits each lane holds,
-// and the probability tile - already in the operand layout of the next product - is multiplied
-// with the value tile (values are stored token-contiguous inside a page, so each lane reads 4
-// consecutive tokens of one value row). The four waves merge their (max, sum, output) in LDS;
-// with more than one split per request a second kernel merges split partials with the rule of
-// PASK App. B.5.
+// Work decomposition (stream-K over a variable-length batch): the (request, 16-token tile) units
+// of the whole batch are laid end to end and cut into equal contiguous ranges, one per resident
+// workgroup, so every compute unit streams the same number of bytes whatever the length mix.
+// A workgroup holds one wave64 per KV head (up to 8); all its waves walk the same tiles, so
+// together they read each page's whole K block and V block (the heads of a page are adjacent
+// in HBM). A range that covers a whole request writes its output directly; otherwise each
+// request segment leaves a partial (max, sum, unnormalised output) that a second kernel merges
+// with the rule of PASK App. B.5.
+//
+// Per tile the G query heads of the wave's KV head are contracted against the key tile on the
+// matrix cores (keys as the 16-row operand, heads as the 16-column operand, so the result lands
+// with one head per lane column), an online softmax runs on the 4 logits each lane holds, and the
+// probability tile - already in the operand layout of the next product - is multiplied with the
+// value tile (values are stored token-contiguous inside a page, so each lane reads 4 consecutive
+// tokens of one value row). Tiles are prefetched into a register ring whose slots rotate by
+// unrolling, so no register copy waits on an in-flight load; page ids are fetched 64 tiles at a
+// time, one per lane, a chunk ahead of use.
 #include "common.h"
+
+#include <algorithm>
+#include <atomic>
 
 namespace {
 
 constexpr int KIND_F32 = 0;
 constexpr int KIND_BF16 = 1;
 constexpr int KIND_MIXED = 2;
-constexpr int WAVES = 4;
-constexpr int THREADS = WAVES * GP_WAVE;
-constexpr int MAX_SPLIT_TILES = 256;
+constexpr int MAX_HEADS_PER_WG = 8;
+constexpr int MAX_THREADS = MAX_HEADS_PER_WG * GP_WAVE;
+constexpr int RING = 2;           // tiles in flight per wave
+constexpr int MAX_BATCH = 8191;   // prefix of tile counts kept in LDS (32 KB)
+constexpr int J_CAP = 16;         // bound on the workgroups one request is spread over
 
 struct DecodeParams {
   const void* q;
@@ -35,10 +47,14 @@ struct DecodeParams {
   const int32_t* context_lens;
   void* out;
   float* lse;
-  float* ws_o;   // [B, H_q, num_splits, D]
-  float* ws_ml;  // [B, H_q, num_splits, 2]
+  float* ws_o;       // [B, H_q, J_max, D] partial outputs
+  float* ws_ml;      // [B, H_q, J_max, 2] partial (max, sum)
+  int32_t* ws_pref;  // [B + 1] prefix of tile counts, written by workgroup 0
   int B, H_q, H_kv, G, page_size, num_pages, max_pages, max_context;
-  int split_tiles, num_splits;
+  int heads_per_wg;
+  int num_wg;  // workgroups per head group (the stream-K width)
+  int r_min;   // minimum tiles per range
+  int j_max;   // partial slots per output row
   float scale_log2;
 };
 
@@ -72,6 +88,7 @@ __device__ __forceinline__ int sanitize_ctx(const DecodeParams& p, int r) {
   return ctx;
 }
 
+// Load tile `tok0` (a multiple of 16) of KV head h from the page encoded in `code`.
 template <int D, int KIND>
 __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int tok0, int h,
                                           int lane, TileRaw<D, KIND>& t) {
@@ -85,7 +102,7 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
       const uint8_t* kr = p.k8 + kv_base + (size_t)(off + n16) * D + 8 * g4;
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
-        u32x2_t c = *reinterpret_cast<const u32x2_t*>(kr + 32 * kk);
+        const u32x2_t c = *reinterpret_cast<const u32x2_t*>(kr + 32 * kk);
         t.k[kk] = u32x4_t{c.x, c.y, 0u, 0u};
       }
       const uint8_t* vr = p.v8 + kv_base + (size_t)n16 * b + off + 4 * g4;
@@ -106,8 +123,7 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
     t.ks = f32x4_t{1.f, 1.f, 1.f, 1.f};
     t.vs = t.ks;
   } else {
-    const int pg = code;
-    const size_t kv_base = ((size_t)pg * p.H_kv + h) * (size_t)b * D;
+    const size_t kv_base = ((size_t)code * p.H_kv + h) * (size_t)b * D;
     if constexpr (KIND == KIND_BF16) {
       const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.k) + kv_base + (size_t)(off + n16) * D + 8 * g4;
 #pragma unroll
@@ -126,278 +142,388 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
   }
 }
 
-template <int D, int KIND>
-__global__ __launch_bounds__(THREADS) void decode_split_kernel(DecodeParams p) {
-  const int s = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int n16 = lane & 15, g4 = lane >> 4;
-  const int G = p.G;
-  const int ctx = sanitize_ctx(p, r);
-  const int ntiles = (ctx + 15) >> 4;
-  const int t0 = s * p.split_tiles;
-  if (s > 0 && t0 >= ntiles) return;
-  const int t1 = min(ntiles, t0 + p.split_tiles);
-
-  __shared__ int s_code[MAX_SPLIT_TILES];
-  extern __shared__ float s_dyn[];  // m [WAVES][16], l [WAVES][16], o [WAVES][G][D]
-  for (int i = threadIdx.x; i < t1 - t0; i += THREADS) {
-    const int tok = (t0 + i) << 4;
-    int pg = p.block_tables[(size_t)r * p.max_pages + tok / p.page_size];
-    int code = (pg >= 0 && pg < p.num_pages) ? pg : -1;
-    if constexpr (KIND == KIND_MIXED) {
-      if (code >= 0) {
-        const int tag = p.page_tag[pg];
-        code = (tag == GP_TAG_FP8 || tag == GP_TAG_BF16) ? ((pg << 2) | tag) : -1;
-      }
-    }
-    s_code[i] = code;
-  }
-  __syncthreads();
-
-  // query operand: head (lane % 16) of this KV head's group, zero rows past G
-  const int hq0 = h * G;
-  constexpr int NQ = (KIND == KIND_F32) ? D / 4 : D / 32;
-  u32x4_t qf[KIND == KIND_F32 ? D / 16 : D / 32];
-  if constexpr (KIND == KIND_F32) {
-    const float* qr = reinterpret_cast<const float*>(p.q) + ((size_t)r * p.H_q + hq0 + n16) * D + (D / 4) * g4;
-#pragma unroll
-    for (int i = 0; i < D / 16; ++i)
-      qf[i] = (n16 < G) ? *reinterpret_cast<const u32x4_t*>(qr + 4 * i) : u32x4_t{0u, 0u, 0u, 0u};
-  } else {
-    const uint16_t* qr = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)r * p.H_q + hq0 + n16) * D + 8 * g4;
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-      qf[kk] = (n16 < G) ? *reinterpret_cast<const u32x4_t*>(qr + 32 * kk) : u32x4_t{0u, 0u, 0u, 0u};
-  }
-  (void)NQ;
-
+// Running softmax state of one wave: output rows of the G heads (acc, head 4*g4 + i in
+// component i, dim 16*nb + n16), running max (log2 domain) of head n16, this lane's share of the
+// running sum of head n16.
+template <int D>
+struct WaveState {
   f32x4_t acc[D / 16];
-#pragma unroll
-  for (int nb = 0; nb < D / 16; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // running max (log2 domain) of head n16
-  float l_run = 0.f;        // this lane's share of the running sum of head n16
+  float m_run, l_run;
+};
 
-  TileRaw<D, KIND> cur, nxt;
-  int ti = t0 + w;
-  int code_cur = (ti < t1) ? s_code[ti - t0] : -1;
-  if (code_cur >= 0) load_tile<D, KIND>(p, code_cur, ti << 4, h, lane, cur);
-
-  for (; ti < t1; ti += WAVES) {
-    const int tn = ti + WAVES;
-    const int code_nxt = (tn < t1) ? s_code[tn - t0] : -1;
-    if (code_nxt >= 0) load_tile<D, KIND>(p, code_nxt, tn << 4, h, lane, nxt);
-
-    if (code_cur >= 0) {
-      const int tok0 = ti << 4;
-      const bool tail = tok0 + 16 > ctx;
-      // ---- logits: S[token 4*g4 + i][head n16]
-      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-      bool fp8 = false;
-      if constexpr (KIND == KIND_MIXED) fp8 = (code_cur & 3) == GP_TAG_FP8;
-      if constexpr (KIND == KIND_F32) {
+template <int D, int KIND>
+__device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRaw<D, KIND>& cur,
+                                             int code, int tok0, int ctx, int lane,
+                                             const u32x4_t* qf, WaveState<D>& st) {
+  const int g4 = lane >> 4;
+  const bool tail = tok0 + 16 > ctx;
+  // ---- logits: S[token 4*g4 + i][head n16]
+  f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+  bool fp8 = false;
+  if constexpr (KIND == KIND_MIXED) fp8 = (code & 3) == GP_TAG_FP8;
+  if constexpr (KIND == KIND_F32) {
 #pragma unroll
-        for (int i = 0; i < D / 16; ++i) {
+    for (int i = 0; i < D / 16; ++i) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            sacc = gp::mfma_f32_16x16x4(__uint_as_float(cur.k[i][c]), __uint_as_float(qf[i][c]), sacc);
-        }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-          u32x4_t kw = cur.k[kk];
-          if constexpr (KIND == KIND_MIXED) {
-            if (fp8) {
-              u32x2_t lo = gp::fp8x4_to_bf16x4(kw.x), hi = gp::fp8x4_to_bf16x4(kw.y);
-              kw = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-            }
-          }
-          sacc = gp::mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, kw),
-                                        __builtin_bit_cast(bf16x8_t, qf[kk]), sacc);
-        }
-      }
-      float sv[4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float z = sacc[i];
-        if constexpr (KIND == KIND_MIXED) z *= cur.ks[i];
-        const bool ok = tok0 + 4 * g4 + i < ctx;
-        sv[i] = ok ? z * p.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, sv[i]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, GP_WAVE));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, GP_WAVE));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = gp::safe_exp2_diff(m_run, m_new);
-      float pv[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = gp::safe_exp2_diff(sv[i], m_new);
-        psum += pv[i];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      // rescale the output rows: this lane holds heads 4*g4 + i
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g4 + i, GP_WAVE);
-#pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[nb][i] *= al[i];
-      // token validity of the 4 tokens this lane feeds into the value product
-      if constexpr (KIND == KIND_F32) {
-#pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb) {
-          u32x4_t vw = cur.v[nb];
-          if (tail) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (tok0 + 4 * g4 + i >= ctx) vw[i] = 0u;
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[nb] = gp::mfma_f32_16x16x4(pv[i], __uint_as_float(vw[i]), acc[nb]);
-        }
-      } else {
-        float pw[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pw[i] = pv[i];
-          if constexpr (KIND == KIND_MIXED) pw[i] *= cur.vs[i];
-        }
-        if constexpr (KIND == KIND_MIXED) {
-          // released or poisoned scales only occur on masked tokens; keep them out of the product
-#pragma unroll
-          for (int i = 0; i < 4; ++i) if (pv[i] == 0.f) pw[i] = 0.f;
-        }
-        const u32x2_t pp = u32x2_t{gp::pack_bf16x2(pw[0], pw[1]), gp::pack_bf16x2(pw[2], pw[3])};
-        uint32_t mlo = 0xffffffffu, mhi = 0xffffffffu;
-        if (tail) {
-          const int base = tok0 + 4 * g4;
-          mlo = (base + 0 < ctx ? 0x0000ffffu : 0u) | (base + 1 < ctx ? 0xffff0000u : 0u);
-          mhi = (base + 2 < ctx ? 0x0000ffffu : 0u) | (base + 3 < ctx ? 0xffff0000u : 0u);
-        }
-#pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb) {
-          u32x2_t vw = cur.v[nb];
-          if constexpr (KIND == KIND_MIXED) {
-            if (fp8) vw = gp::fp8x4_to_bf16x4(vw.x);
-          }
-          vw.x &= mlo;
-          vw.y &= mhi;
-          acc[nb] = gp::mfma_bf16_16x16x16(__builtin_bit_cast(i16x4_t, pp),
-                                           __builtin_bit_cast(i16x4_t, vw), acc[nb]);
-        }
-      }
+      for (int c = 0; c < 4; ++c)
+        sacc = gp::mfma_f32_16x16x4(__uint_as_float(cur.k[i][c]), __uint_as_float(qf[i][c]), sacc);
     }
-    cur = nxt;
-    code_cur = code_nxt;
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      u32x4_t kw = cur.k[kk];
+      if constexpr (KIND == KIND_MIXED) {
+        if (fp8) {
+          const u32x2_t lo = gp::fp8x4_to_bf16x4(kw.x), hi = gp::fp8x4_to_bf16x4(kw.y);
+          kw = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        }
+      }
+      sacc = gp::mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, kw),
+                                    __builtin_bit_cast(bf16x8_t, qf[kk]), sacc);
+    }
   }
-
-  // ---- merge the 4 waves
-  float l_tot = l_run + __shfl_xor(l_run, 16, GP_WAVE);
-  l_tot += __shfl_xor(l_tot, 32, GP_WAVE);
-  float* s_m = s_dyn;
-  float* s_l = s_dyn + WAVES * 16;
-  float* s_o = s_dyn + 2 * WAVES * 16;
-  if (lane < 16) {
-    s_m[w * 16 + lane] = m_run;
-    s_l[w * 16 + lane] = l_tot;
+  float sv[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float z = sacc[i];
+    if constexpr (KIND == KIND_MIXED) z *= cur.ks[i];
+    const bool ok = tok0 + 4 * g4 + i < ctx;
+    sv[i] = ok ? z * p.scale_log2 : -INFINITY;
+    mx = fmaxf(mx, sv[i]);
   }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, GP_WAVE));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, GP_WAVE));
+  const float m_new = fmaxf(st.m_run, mx);
+  const float alpha = gp::safe_exp2_diff(st.m_run, m_new);
+  float pv[4];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pv[i] = gp::safe_exp2_diff(sv[i], m_new);
+    psum += pv[i];
+  }
+  st.l_run = st.l_run * alpha + psum;
+  st.m_run = m_new;
+  // rescale the output rows: this lane holds heads 4*g4 + i
+  float al[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g4 + i, GP_WAVE);
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb)
 #pragma unroll
+    for (int i = 0; i < 4; ++i) st.acc[nb][i] *= al[i];
+  if constexpr (KIND == KIND_F32) {
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) {
+      u32x4_t vw = cur.v[nb];
+      if (tail) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tok0 + 4 * g4 + i >= ctx) vw[i] = 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.acc[nb] = gp::mfma_f32_16x16x4(pv[i], __uint_as_float(vw[i]), st.acc[nb]);
+    }
+  } else {
+    float pw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pw[i] = pv[i];
+      if constexpr (KIND == KIND_MIXED) pw[i] *= cur.vs[i];
+    }
+    if constexpr (KIND == KIND_MIXED) {
+      // scales of masked tokens may be poison; keep them out of the product
+#pragma unroll
+      for (int i = 0; i < 4; ++i) if (pv[i] == 0.f) pw[i] = 0.f;
+    }
+    const u32x2_t pp = u32x2_t{gp::pack_bf16x2(pw[0], pw[1]), gp::pack_bf16x2(pw[2], pw[3])};
+    // values of tokens past the context (the tail of the last page) are masked to zero bits
+    uint32_t mlo = 0xffffffffu, mhi = 0xffffffffu;
+    if (tail) {
+      const int base = tok0 + 4 * g4;
+      mlo = (base + 0 < ctx ? 0x0000ffffu : 0u) | (base + 1 < ctx ? 0xffff0000u : 0u);
+      mhi = (base + 2 < ctx ? 0x0000ffffu : 0u) | (base + 3 < ctx ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) {
+      u32x2_t vw = cur.v[nb];
+      if constexpr (KIND == KIND_MIXED) {
+        if (fp8) vw = gp::fp8x4_to_bf16x4(vw.x);
+      }
+      vw.x &= mlo;
+      vw.y &= mhi;
+      st.acc[nb] = gp::mfma_bf16_16x16x16(__builtin_bit_cast(i16x4_t, pp),
+                                          __builtin_bit_cast(i16x4_t, vw), st.acc[nb]);
+    }
+  }
+}
+
+
+// Tiles per workgroup range: equal shares of the batch's U units, at least r_min.
+__device__ __forceinline__ int range_len(const DecodeParams& p, int U) {
+  return max((U + p.num_wg - 1) / p.num_wg, p.r_min);
+}
+
+template <int D, int KIND>
+__global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParams p) {
+  extern __shared__ int s_pref[];  // [B + 1]
+  __shared__ int s_wsum[MAX_HEADS_PER_WG];
+  const int wg = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int h = blockIdx.y * p.heads_per_wg + w;
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const int G = p.G;
+
+  // ---- inclusive prefix of tile counts over the batch (block-wide scan in chunks)
+  int carry = 0;
+  if (threadIdx.x == 0) s_pref[0] = 0;
+  for (int base = 0; base < p.B; base += blockDim.x) {
+    const int r = base + threadIdx.x;
+    int v = r < p.B ? (sanitize_ctx(p, r) + 15) >> 4 : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(v, o, GP_WAVE);
+      if (lane >= o) v += t;
+    }
+    if (lane == 63) s_wsum[w] = v;
+    __syncthreads();
+    int off = carry;
+    for (int k = 0; k < w; ++k) off += s_wsum[k];
+    int tot = 0;
+    for (int k = 0; k < nw; ++k) tot += s_wsum[k];
+    if (r < p.B) s_pref[r + 1] = off + v;
+    carry += tot;
+    __syncthreads();
+  }
+  const int U = s_pref[p.B];
+  if (wg == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i <= p.B; i += blockDim.x) p.ws_pref[i] = s_pref[i];
+  if (h >= p.H_kv) return;
+  const int R = range_len(p, U);
+  const long u0l = (long)wg * R;
+  if (u0l >= U) return;
+  const int u0 = (int)u0l, u1 = min(U, u0 + R);
+  const int b = p.page_size;
+
+  int u = u0;
+  while (u < u1) {
+    // request of unit u: the last r with s_pref[r] <= u (never an empty request)
+    int lo = 0, hi = p.B;  // invariant: s_pref[lo] <= u < s_pref[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] <= u) lo = mid; else hi = mid;
+    }
+    const int r = lo;
+    const int seg_end = min(u1, s_pref[r + 1]);
+    const int ta = u - s_pref[r], tb = ta + (seg_end - u);
+    const int ntiles = s_pref[r + 1] - s_pref[r];
+    const int ctx = sanitize_ctx(p, r);
+    u = seg_end;
+
+    // page codes of tiles [c0, c0 + 64) of this segment, one per lane (-1: skipped)
+    const int32_t* bt = p.block_tables + (size_t)r * p.max_pages;
+    auto load_codes = [&](int c0) -> int {
+      const int t = c0 + lane;
+      int code = -1;
+      if (t < tb) {
+        const int pg = bt[(t << 4) / b];
+        code = (pg >= 0 && pg < p.num_pages) ? pg : -1;
+        if constexpr (KIND == KIND_MIXED) {
+          if (code >= 0) {
+            const int tag = p.page_tag[pg];
+            code = (tag == GP_TAG_FP8 || tag == GP_TAG_BF16) ? ((pg << 2) | tag) : -1;
+          }
+        }
+      }
+      return code;
+    };
+    int ca = ta;
+    int ids_a = load_codes(ca);
+    int ids_b = load_codes(ca + 64);
+    // code of tile x; x only grows, and the chunk window slides when x leaves it
+    auto code_of = [&](int x) -> int {
+      if (x - ca >= 64) {
+        ids_a = ids_b;
+        ca += 64;
+        ids_b = load_codes(ca + 64);
+      }
+      const int i = x - ca;
+      return i < 64 ? __builtin_amdgcn_readlane(ids_a, i) : __builtin_amdgcn_readlane(ids_b, i - 64);
+    };
+
+    // query operand: head (lane % 16) of this KV head's group, zero rows past G
+    const int hq0 = h * G;
+    u32x4_t qf[KIND == KIND_F32 ? D / 16 : D / 32];
+    if constexpr (KIND == KIND_F32) {
+      const float* qr = reinterpret_cast<const float*>(p.q) + ((size_t)r * p.H_q + hq0 + n16) * D + (D / 4) * g4;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i)
+        qf[i] = (n16 < G) ? *reinterpret_cast<const u32x4_t*>(qr + 4 * i) : u32x4_t{0u, 0u, 0u, 0u};
+    } else {
+      const uint16_t* qr = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)r * p.H_q + hq0 + n16) * D + 8 * g4;
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk)
+        qf[kk] = (n16 < G) ? *reinterpret_cast<const u32x4_t*>(qr + 32 * kk) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+
+    WaveState<D> st;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) st.acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+
+    TileRaw<D, KIND> ring[RING];
+    int codes[RING];
+#pragma unroll
+    for (int q = 0; q < RING; ++q) {
+      const int x = ta + q;
+      codes[q] = x < tb ? code_of(x) : -1;
+      if (codes[q] >= 0) load_tile<D, KIND>(p, codes[q], x << 4, h, lane, ring[q]);
+    }
+    for (int base = ta; base < tb; base += RING) {
+#pragma unroll
+      for (int q = 0; q < RING; ++q) {
+        const int t = base + q;
+        if (t < tb) {
+          if (codes[q] >= 0) process_tile<D, KIND>(p, ring[q], codes[q], t << 4, ctx, lane, qf, st);
+          const int x = t + RING;
+          codes[q] = x < tb ? code_of(x) : -1;
+          if (codes[q] >= 0) load_tile<D, KIND>(p, codes[q], x << 4, h, lane, ring[q]);
+        }
+      }
+    }
+
+    // ---- segment epilogue: final output rows, or a partial in slot j of this request
+    float l_tot = st.l_run + __shfl_xor(st.l_run, 16, GP_WAVE);
+    l_tot += __shfl_xor(l_tot, 32, GP_WAVE);
+    float l_i[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l_i[i] = __shfl(l_tot, 4 * g4 + i, GP_WAVE);
+    const bool whole = ta == 0 && tb == ntiles;
+    const int j = wg - s_pref[r] / R;
+#pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int head = 4 * g4 + i;
-      if (head < G) s_o[((size_t)w * G + head) * D + 16 * nb + n16] = acc[nb][i];
-    }
-  __syncthreads();
-
-  const bool final_out = p.num_splits == 1;
-  for (int idx = threadIdx.x; idx < G * D; idx += THREADS) {
-    const int head = idx / D, dd = idx % D;
-    float m = -INFINITY;
+      if (head >= G) continue;
+      const size_t row = (size_t)r * p.H_q + hq0 + head;
+      if (whole) {
+        const float inv = l_i[i] > 0.f ? 1.f / l_i[i] : 0.f;
 #pragma unroll
-    for (int ww = 0; ww < WAVES; ++ww) m = fmaxf(m, s_m[ww * 16 + head]);
-    float num = 0.f, den = 0.f;
+        for (int nb = 0; nb < D / 16; ++nb) {
+          const float o = st.acc[nb][i] * inv;
+          if constexpr (KIND == KIND_F32)
+            reinterpret_cast<float*>(p.out)[row * D + 16 * nb + n16] = o;
+          else
+            reinterpret_cast<uint16_t*>(p.out)[row * D + 16 * nb + n16] = (uint16_t)gp::f32_to_bf16_bits(o);
+        }
+      } else {
+        float* wo = p.ws_o + (row * p.j_max + j) * D;
 #pragma unroll
-    for (int ww = 0; ww < WAVES; ++ww) {
-      const float e = gp::safe_exp2_diff(s_m[ww * 16 + head], m);
-      num += e * s_o[((size_t)ww * G + head) * D + dd];
-      den += e * s_l[ww * 16 + head];
+        for (int nb = 0; nb < D / 16; ++nb) wo[16 * nb + n16] = st.acc[nb][i];
+      }
     }
-    const size_t row = (size_t)r * p.H_q + hq0 + head;
-    if (final_out) {
-      const float o = den > 0.f ? num / den : 0.f;
-      if constexpr (KIND == KIND_F32)
-        reinterpret_cast<float*>(p.out)[row * D + dd] = o;
-      else
-        reinterpret_cast<uint16_t*>(p.out)[row * D + dd] = (uint16_t)gp::f32_to_bf16_bits(o);
-      if (dd == 0 && p.lse) p.lse[row] = den > 0.f ? (m + __log2f(den)) * GP_LN2 : -INFINITY;
-    } else {
-      p.ws_o[(row * p.num_splits + s) * D + dd] = num;
-      if (dd == 0) {
-        p.ws_ml[(row * p.num_splits + s) * 2 + 0] = m;
-        p.ws_ml[(row * p.num_splits + s) * 2 + 1] = den;
+    if (g4 == 0 && n16 < G) {
+      const size_t row = (size_t)r * p.H_q + hq0 + n16;
+      if (whole) {
+        if (p.lse) p.lse[row] = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * GP_LN2 : -INFINITY;
+      } else {
+        p.ws_ml[(row * p.j_max + j) * 2 + 0] = st.m_run;
+        p.ws_ml[(row * p.j_max + j) * 2 + 1] = l_tot;
       }
     }
   }
 }
 
-// Merge of split partials (PASK App. B.5): o = sum_j e^{m_j - m} u_j / sum_j e^{m_j - m} l_j.
+// Merge of a request's partials (PASK App. B.5): o = sum_j e^{m_j - m} u_j / sum_j e^{m_j - m} l_j.
+// One wave per output row. Rows of requests that one workgroup finished are left as written;
+// rows of empty requests get o = 0 and lse = -inf.
 template <int D, int KIND>
-__global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams p) {
-  const int hq = blockIdx.x, r = blockIdx.y;
-  const int ctx = sanitize_ctx(p, r);
-  const int ntiles = (ctx + 15) >> 4;
-  int ns = (ntiles + p.split_tiles - 1) / p.split_tiles;
-  ns = max(1, min(ns, p.num_splits));
-  const size_t row = (size_t)r * p.H_q + hq;
-  const float* ml = p.ws_ml + row * p.num_splits * 2;
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (long)p.B * p.H_q) return;
+  const int r = (int)(row / p.H_q);
+  const int U = p.ws_pref[p.B];
+  const int pa = p.ws_pref[r], pb = p.ws_pref[r + 1];
+  int J = 0;
+  if (pb > pa) {
+    const int R = range_len(p, U);
+    J = (pb - 1) / R - pa / R + 1;
+  }
+  if (J == 1) return;
+  const float* ml = p.ws_ml + row * p.j_max * 2;
   float m = -INFINITY;
-  for (int j = 0; j < ns; ++j) m = fmaxf(m, ml[2 * j]);
+  for (int j = 0; j < J; ++j) m = fmaxf(m, ml[2 * j]);
   float den = 0.f;
-  for (int j = 0; j < ns; ++j) den += gp::safe_exp2_diff(ml[2 * j], m) * ml[2 * j + 1];
+  for (int j = 0; j < J; ++j) den += gp::safe_exp2_diff(ml[2 * j], m) * ml[2 * j + 1];
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  for (int dd = threadIdx.x; dd < D; dd += 64) {
+  for (int dd = lane; dd < D; dd += 64) {
     float num = 0.f;
-    for (int j = 0; j < ns; ++j)
-      num += gp::safe_exp2_diff(ml[2 * j], m) * p.ws_o[(row * p.num_splits + j) * D + dd];
+    for (int j = 0; j < J; ++j)
+      num += gp::safe_exp2_diff(ml[2 * j], m) * p.ws_o[(row * p.j_max + j) * D + dd];
     const float o = num * inv;
     if constexpr (KIND == KIND_F32)
       reinterpret_cast<float*>(p.out)[row * D + dd] = o;
     else
       reinterpret_cast<uint16_t*>(p.out)[row * D + dd] = (uint16_t)gp::f32_to_bf16_bits(o);
   }
-  if (threadIdx.x == 0 && p.lse) p.lse[row] = den > 0.f ? (m + __log2f(den)) * GP_LN2 : -INFINITY;
+  if (lane == 0 && p.lse) p.lse[row] = den > 0.f ? (m + __log2f(den)) * GP_LN2 : -INFINITY;
 }
 
-struct SplitPlan {
-  int split_tiles;
-  int num_splits;
+struct Plan {
+  int r_min, j_max;
 };
 
-SplitPlan plan_splits(int B, int H_kv, int max_context) {
-  const long max_tiles = (max_context + 15) / 16;
-  int st = 64;
-  while (st > 4 && (long)B * H_kv * ((max_tiles + st - 1) / st) < 4096) st >>= 1;
-  SplitPlan sp;
-  sp.split_tiles = st;
-  sp.num_splits = (int)std::max<long>(1, (max_tiles + st - 1) / st);
-  return sp;
+// Ranges hold at least r_min tiles, so one request is spread over at most j_max workgroups.
+Plan plan_for(int max_context) {
+  const int max_tiles = (max_context + 15) / 16;
+  Plan pl;
+  pl.r_min = std::max(8, (max_tiles + J_CAP - 1) / J_CAP);
+  pl.j_max = (max_tiles + pl.r_min - 1) / pl.r_min + 1;
+  return pl;
+}
+
+// Workgroups of the streaming kernel that fit on the device at once (memoised per device
+// and instantiation; only host-side device properties are cached).
+template <int D, int KIND>
+int resident_workgroups(int threads, size_t lds) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const int slot = dev & 63;
+  const int key = threads * 65536 + (int)std::min<size_t>(lds, 65535);
+  static std::atomic<int> cache_key[64];
+  if (cache_key[slot].load() == key) {
+    const int v = cache[slot].load();
+    if (v > 0) return v;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_streamk_kernel<D, KIND>, threads,
+                                                   lds) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  const int v = cus * per_cu;
+  cache[slot].store(v);
+  cache_key[slot].store(key);
+  return v;
 }
 
 template <int D, int KIND>
-int launch_decode(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.num_splits, p.H_kv, p.B);
-  const size_t lds = (size_t)(2 * WAVES * 16 + WAVES * p.G * D) * sizeof(float);
-  hipLaunchKernelGGL((decode_split_kernel<D, KIND>), grid, dim3(THREADS), lds, stream, p);
+int launch_decode(DecodeParams p, hipStream_t stream) {
+  const int hg = (p.H_kv + p.heads_per_wg - 1) / p.heads_per_wg;
+  const int threads = p.heads_per_wg * GP_WAVE;
+  const size_t lds = (size_t)(p.B + 1) * sizeof(int);
+  p.num_wg = std::max(1, resident_workgroups<D, KIND>(threads, lds) / hg);
+  hipLaunchKernelGGL((decode_streamk_kernel<D, KIND>), dim3(p.num_wg, hg), dim3(threads), lds,
+                     stream, p);
   GP_CHECK_LAUNCH();
-  if (p.num_splits > 1) {
-    hipLaunchKernelGGL((decode_combine_kernel<D, KIND>), dim3(p.H_q, p.B), dim3(64), 0, stream, p);
-    GP_CHECK_LAUNCH();
-  }
+  const long rows = (long)p.B * p.H_q;
+  hipLaunchKernelGGL((decode_merge_kernel<D, KIND>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                     stream, p);
+  GP_CHECK_LAUNCH();
   return GP_OK;
 }
 
@@ -406,10 +532,12 @@ int launch_decode(const DecodeParams& p, hipStream_t stream) {
 extern "C" size_t gp_paged_decode_attn_workspace_size(int B, int H_q, int H_kv, int head_dim,
                                                       int page_size, int max_context) {
   (void)page_size;
-  if (B <= 0 || H_q <= 0 || H_kv <= 0 || head_dim <= 0 || max_context < 0) return 0;
-  const SplitPlan sp = plan_splits(B, H_kv, max_context);
-  if (sp.num_splits <= 1) return 0;
-  return (size_t)B * H_q * sp.num_splits * (head_dim + 2) * sizeof(float);
+  (void)H_kv;
+  if (B <= 0 || H_q <= 0 || head_dim <= 0 || max_context < 0) return 0;
+  const Plan pl = plan_for(max_context);
+  const size_t partials = (size_t)B * H_q * pl.j_max * (head_dim + 2) * sizeof(float);
+  const size_t pref = ((size_t)(B + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
+  return pref + partials;
 }
 
 extern "C" int gp_paged_decode_attn(const void* q, int q_dtype, int B, int H_q,
@@ -426,17 +554,19 @@ extern "C" int gp_paged_decode_attn(const void* q, int q_dtype, int B, int H_q,
   if (D != 64 && D != 128) return GP_ERR_UNSUPPORTED;
   const int G = H_q / H_kv;
   if (G > 16) return GP_ERR_UNSUPPORTED;
+  if (B > MAX_BATCH) return GP_ERR_UNSUPPORTED;
   if (q_dtype != kv->dtype || (q_dtype != GP_F32 && q_dtype != GP_BF16)) return GP_ERR_INVALID;
   const bool mixed = kv->page_tag != nullptr;
   if (mixed && (q_dtype != GP_BF16 || !kv->k8 || !kv->v8 || !kv->k_scale || !kv->v_scale))
     return GP_ERR_INVALID;
   if ((long)max_context > (long)max_pages * b) return GP_ERR_INVALID;
   if ((long)kv->num_pages * H_kv * b > (1L << 40)) return GP_ERR_INVALID;
+  if ((long)kv->num_pages * 4 > (long)INT32_MAX) return GP_ERR_UNSUPPORTED;  // tag packing
+  if ((long)B * ((max_context + 15) / 16) > (long)INT32_MAX / 2) return GP_ERR_UNSUPPORTED;
 
-  const SplitPlan sp = plan_splits(B, H_kv, max_context);
   const size_t need = gp_paged_decode_attn_workspace_size(B, H_q, H_kv, D, b, max_context);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return GP_ERR_WORKSPACE;
-  if (sp.split_tiles > MAX_SPLIT_TILES) return GP_ERR_INVALID;
+  if (!workspace || workspace_bytes < need) return GP_ERR_WORKSPACE;
+  const Plan pl = plan_for(max_context);
 
   DecodeParams p{};
   p.q = q;
@@ -459,13 +589,14 @@ extern "C" int gp_paged_decode_attn(const void* q, int q_dtype, int B, int H_q,
   p.num_pages = kv->num_pages;
   p.max_pages = max_pages;
   p.max_context = max_context;
-  p.split_tiles = sp.split_tiles;
-  p.num_splits = sp.num_splits;
+  p.heads_per_wg = std::min(H_kv, MAX_HEADS_PER_WG);
+  p.r_min = pl.r_min;
+  p.j_max = pl.j_max;
   p.scale_log2 = sm_scale * GP_LOG2E;
-  if (sp.num_splits > 1) {
-    p.ws_o = static_cast<float*>(workspace);
-    p.ws_ml = p.ws_o + (size_t)B * H_q * sp.num_splits * D;
-  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  p.ws_pref = reinterpret_cast<int32_t*>(ws);
+  p.ws_o = reinterpret_cast<float*>(ws + (((size_t)(B + 1) * sizeof(int32_t) + 255) & ~(size_t)255));
+  p.ws_ml = p.ws_o + (size_t)B * H_q * pl.j_max * D;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (mixed) return D == 64 ? launch_decode<64, KIND_MIXED>(p, s) : launch_decode<128, KIND_MIXED>(p, s);
   if (q_dtype == GP_BF16) return D == 64 ? launch_decode<64, KIND_BF16>(p, s) : launch_decode<128, KIND_BF16>(p, s);

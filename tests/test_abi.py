@@ -56,10 +56,13 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    # one 16-token tile fits one split: no workspace; long contexts need split partials
-    assert lib.gp_paged_decode_attn_workspace_size(2, 8, 2, 64, 16, 16) == 0
+    # a prefix of tile counts (B + 1 ints, 256-byte aligned) plus split partials that grow
+    # with the longest context
+    small = lib.gp_paged_decode_attn_workspace_size(2, 8, 2, 64, 16, 16)
     big = lib.gp_paged_decode_attn_workspace_size(64, 32, 8, 128, 16, 16384)
-    assert big > 0 and big % (4 * 130) == 0
+    assert small >= 3 * 4 and big > small
+    header = ((64 + 1) * 4 + 255) // 256 * 256
+    assert (big - header) % (64 * 32 * 130 * 4) == 0
     assert lib.gp_paged_decode_attn_workspace_size(-1, 32, 8, 128, 16, 16384) == 0
     s1 = lib.gp_score_and_working_set_workspace_size(4, 32, 8, 128, 16, 8192)
     s2 = lib.gp_score_and_working_set_workspace_size(8, 32, 8, 128, 16, 8192)
@@ -92,6 +95,8 @@ def test_invalid_arguments_rejected_on_host(lib):
                                     fake, None, None, 0, None) == -1
     assert lib.gp_paged_decode_attn(fake, 1, 64, 32, ctypes.byref(kv), fake, 1024, fake, 16384,
                                     0.1, fake, None, None, 0, None) == -3
+    assert lib.gp_paged_decode_attn(fake, 1, 9000, 32, ctypes.byref(kv), fake, 1024, fake, 16384,
+                                    0.1, fake, None, fake, 1 << 40, None) == -2
     # max_context beyond the block table's reach
     assert lib.gp_paged_decode_attn(fake, 1, 4, 32, ctypes.byref(kv), fake, 8, fake, 1000, 0.1,
                                     fake, None, None, 0, None) == -1

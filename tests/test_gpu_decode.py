@@ -101,7 +101,8 @@ def test_decode_edge_cases():
                                     wl.max_context, wl.sm_scale)
     torch.cuda.synchronize()
     o_all, _ = _run_gpu(wl)
-    assert torch.equal(o1[0], o_all[0])
+    e1, _ = maxabs(f64(o1[0]), f64(o_all[0]))   # other batch: other split ranges, same result
+    assert e1 <= TOL["bf16"]
 
 
 def test_decode_lse_and_split_count_independence():
