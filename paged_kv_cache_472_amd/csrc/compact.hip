@@ -7,26 +7,32 @@
 //      sum_h (K^S_h - K^L_h) / (H |C|) with tau; Grow pops the LIFO free stack; compression pops
 //      one private page per shared page it must write (wave-parallel ballot ranks, ascending
 //      logical order); released references are applied after every pop of the call.
-//   2. select (per request x KV head, 1024 threads): s = max(a^S, a^L) held in registers, 32
-//      consecutive candidates per thread so each thread ranks whole pages for the k_loc quota;
-//      the E <= page_size evicted tokens are found by E rounds of a block-wide minimum over the
-//      unique keys (s, ~index), which realises the (s desc, index asc) order exactly.
+//   2. select (three launches): s = max(a^S, a^L); the E <= page_size evicted tokens are the E
+//      smallest of the unique keys (s, ~index) outside each page's k_loc quota, which realises
+//      the (s desc, index asc) order exactly: chunk-local E smallest, their merge per request
+//      and KV head, then kept_idx written in parallel.
 //   3. snapshot: compaction is a left shift by at most E slots, so a chunk of destination pages
 //      only reads its own pages plus the first page of the next chunk; that page is saved first.
-//   4. compact (per chunk x KV head x request): read all sources (keys row-wise from HBM, values
-//      through LDS), barrier, write the chunk's destination pages.
+//   4. compact (per chunk x KV head x request): tabulate the source slot of every destination
+//      slot, read all sources (keys row-wise from HBM, values through LDS), barrier, write the
+//      chunk's destination pages.
 #include "common.h"
+
+#include <climits>
 
 namespace {
 
 constexpr int MODE_NONE = 0;      // grow / no pages: kept_idx = -1 over |C|
 constexpr int MODE_IDENTITY = 1;  // compress with nothing to evict: kept_idx = 0..|C|-1
 constexpr int MODE_COMPACT = 2;
-constexpr int SEL_THREADS = 1024;
-constexpr int SEL_VPT = 32;
+constexpr int SEL_T = 256;           // threads (candidate pages) per selection chunk
+constexpr int MAX_CAND = 32768;      // largest candidate set
+constexpr int SEL_MAX_CHUNKS = MAX_CAND / (SEL_T * 16);
 constexpr int MAX_EVICT = 32;
+constexpr int CHUNK_PAGES = 16;           // destination pages per compaction workgroup
+constexpr int MAX_WINDOW_SLOTS = 8 * 32;  // LDS window pages (<= 8) x page size (<= 32)
 constexpr int CP_THREADS = 256;
-constexpr int CP_LDS_BYTES = 48 * 1024;
+constexpr int CP_LDS_BYTES = 56 * 1024;  // K and V source pages of one window
 
 struct Info {
   int r, mode, P, ctx_old, n, K_t, R_n, E, ctx_new, n_dest, first_repl, pad;
@@ -54,9 +60,11 @@ struct CParams {
   int32_t* rel;       // [R * max_pages]
   int32_t* ev;        // [R, H_kv, MAX_EVICT]
   int32_t* dp0;       // [R, H_kv]
+  unsigned long long* cand;  // [R, H_kv, SEL_MAX_CHUNKS, MAX_EVICT] chunk survivors
   uint8_t* snap;      // [R, H_kv, max_chunks, 2, page bytes]
   int R, B, H_kv, D, page_size, num_pages, max_pages, C_max, k_loc, policy, es;
-  int chunk_pages, max_chunks;
+  int chunk_pages, max_chunks, window_pages;
+  int log_b, log_kq, log_vq, log_qpp;  // log2 of page size, 16-byte pieces per key row / value row / page
   double tau;
 };
 
@@ -240,110 +248,170 @@ __global__ __launch_bounds__(64) void decide_alloc_kernel(CParams P) {
   }
 }
 
-__device__ __forceinline__ unsigned long long block_min_u64(unsigned long long v, unsigned long long* scratch) {
+__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const unsigned long long t = __shfl_xor(v, o, GP_WAVE);
     v = t < v ? t : v;
   }
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) scratch[w] = v;
-  __syncthreads();
-  unsigned long long m = ~0ull;
-  for (int k = 0; k < SEL_THREADS / GP_WAVE; ++k) m = scratch[k] < m ? scratch[k] : m;
-  return m;
+  return v;
 }
 
+// Selection (Eq. 9-10) in three short launches over chunks of SEL_T pages (one page per
+// thread, so the k_loc quota of a page is ranked in registers).
+//   select_local: per chunk, the E smallest eviction keys (s, ~index) of the chunk: each wave
+//                 finds its own E smallest with shuffles, then one wave picks the E smallest of
+//                 the 4 * E survivors.
+//   select_merge: per (request, KV head), the E smallest of all chunk survivors: the evicted
+//                 tokens, sorted by token index, and the first destination page that changes.
+//   select_write: per chunk, kept_idx: kept token t goes to position t - #(evicted < t).
+// Keys are unique, so the result is exactly the (s desc, index asc) order whatever the split.
 template <int PB>
-__global__ __launch_bounds__(SEL_THREADS) void select_kernel(CParams P) {
-  const int h = blockIdx.x, i = blockIdx.y;
+__global__ __launch_bounds__(SEL_T) void select_local_kernel(CParams P) {
+  constexpr int b = PB;
+  const int c = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
   const Info inf = P.info[i];
   const int n = inf.n;
-  int32_t* out = P.kept_idx + ((size_t)i * P.H_kv + h) * P.C_max;
-  if (inf.mode != MODE_COMPACT) {
-    for (int t = threadIdx.x; t < n; t += SEL_THREADS) out[t] = inf.mode == MODE_IDENTITY ? t : -1;
-    return;
-  }
-  constexpr int b = PB;
+  if (inf.mode != MODE_COMPACT || c * SEL_T * b >= n) return;
   const int K_t = inf.K_t, E = inf.E;
-  const int t0 = threadIdx.x * SEL_VPT;
+  const int t0 = (c * SEL_T + threadIdx.x) * b;  // first candidate of this thread's page
   const float* as = P.a_short + ((size_t)i * P.H_kv + h) * P.C_max;
   const float* al = P.a_long + ((size_t)i * P.H_kv + h) * P.C_max;
-  uint32_t s[SEL_VPT];
+  uint32_t sv[b];
 #pragma unroll
-  for (int j = 0; j < SEL_VPT; j += 4) {
-    if (t0 + j < n) {
+  for (int j = 0; j < b; j += 4) {
+    if (t0 < n) {  // pages are whole: t0 < n covers all b candidates
       const f32x4_t x = *reinterpret_cast<const f32x4_t*>(as + t0 + j);
       const f32x4_t y = *reinterpret_cast<const f32x4_t*>(al + t0 + j);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[j + e] = max(__float_as_uint(x[e]) & 0x7fffffffu, __float_as_uint(y[e]) & 0x7fffffffu);
+      for (int e = 0; e < 4; ++e)
+        sv[j + e] = max(__float_as_uint(x[e]) & 0x7fffffffu, __float_as_uint(y[e]) & 0x7fffffffu);
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[j + e] = 0u;
+      for (int e = 0; e < 4; ++e) sv[j + e] = 0u;
     }
   }
   const int kloc = min(P.k_loc, b);
   const long n_loc = (long)(n / b) * kloc;
-  const bool pool_all = n_loc >= K_t;
-  unsigned long long key[SEL_VPT];
+  const bool pool_all = n_loc >= K_t;  // |S_loc| >= K_t: S is the K_t best of all of C
+  unsigned long long key[b];
 #pragma unroll
-  for (int j = 0; j < SEL_VPT; ++j) {
-    const int t = t0 + j;
-    bool cand = t < n;
+  for (int j = 0; j < b; ++j) {
+    bool cand = t0 < n;
     if (cand && !pool_all) {
-      // rank of t inside its page under (s desc, index asc); pages never straddle threads
-      const int pbase = (j / b) * b;
+      // rank of candidate j inside its page under (s desc, index asc): the k_loc best stay
       int rank = 0;
 #pragma unroll
-      for (int u = 0; u < b; ++u) {
-        const int ju = pbase + u;
-        const bool better = s[ju] > s[j] || (s[ju] == s[j] && ju < j);
-        rank += better ? 1 : 0;
-      }
+      for (int u = 0; u < b; ++u) rank += (sv[u] > sv[j] || (sv[u] == sv[j] && u < j)) ? 1 : 0;
       cand = rank >= kloc;
     }
-    key[j] = cand ? (((unsigned long long)s[j] << 32) | (0xffffffffu - (uint32_t)t)) : ~0ull;
+    key[j] = cand ? (((unsigned long long)sv[j] << 32) | (0xffffffffu - (uint32_t)(t0 + j))) : ~0ull;
   }
-  __shared__ unsigned long long scratch[SEL_THREADS / GP_WAVE];
-  __shared__ int s_ev[MAX_EVICT], s_sorted[MAX_EVICT];
+  constexpr int NW = SEL_T / GP_WAVE;
+  __shared__ unsigned long long s_cand[NW * MAX_EVICT];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   unsigned long long prev = 0;
   for (int e = 0; e < E; ++e) {
     unsigned long long m = ~0ull;
 #pragma unroll
-    for (int j = 0; j < SEL_VPT; ++j) {
-      const bool ok = (e == 0) || key[j] > prev;
-      if (ok && key[j] < m) m = key[j];
-    }
-    m = block_min_u64(m, scratch);
+    for (int j = 0; j < b; ++j)
+      if ((e == 0 || key[j] > prev) && key[j] < m) m = key[j];
+    m = wave_min_u64(m);
     prev = m;
-    if (threadIdx.x == 0) s_ev[e] = (int)(0xffffffffu - (uint32_t)(m & 0xffffffffu));
+    if (lane == 0) s_cand[wv * MAX_EVICT + e] = m;
   }
   __syncthreads();
-  if (threadIdx.x < E) {
-    const int v = s_ev[threadIdx.x];
-    int rank = 0;
-    for (int e = 0; e < E; ++e) rank += s_ev[e] < v ? 1 : 0;
-    s_sorted[rank] = v;
-  }
-  __syncthreads();
-  if (threadIdx.x < E) {
-    P.ev[((size_t)i * P.H_kv + h) * MAX_EVICT + threadIdx.x] = s_sorted[threadIdx.x];
-    out[K_t + threadIdx.x] = -1;
-  }
-  if (threadIdx.x == 0) P.dp0[(size_t)i * P.H_kv + h] = min(s_sorted[0] / b, inf.first_repl);
-  // kept tokens in ascending order: token t goes to t - #(evicted < t)
+  if (wv == 0) {
+    constexpr int PER = NW * MAX_EVICT / GP_WAVE;
+    unsigned long long cv[PER];
 #pragma unroll
-  for (int j = 0; j < SEL_VPT; ++j) {
-    const int t = t0 + j;
-    if (t >= n) continue;
-    int before = 0;
-    bool evicted = false;
-    for (int e = 0; e < E; ++e) {
-      before += s_sorted[e] < t ? 1 : 0;
-      evicted |= s_sorted[e] == t;
+    for (int k = 0; k < PER; ++k) {
+      const int idx = lane + GP_WAVE * k;
+      cv[k] = (idx % MAX_EVICT) < E ? s_cand[idx] : ~0ull;
     }
-    if (!evicted) out[t - before] = t;
+    unsigned long long* dst = P.cand + (((size_t)i * P.H_kv + h) * SEL_MAX_CHUNKS + c) * MAX_EVICT;
+    unsigned long long pv = 0;
+    for (int e = 0; e < E; ++e) {
+      unsigned long long m = ~0ull;
+#pragma unroll
+      for (int k = 0; k < PER; ++k)
+        if ((e == 0 || cv[k] > pv) && cv[k] < m) m = cv[k];
+      m = wave_min_u64(m);
+      pv = m;
+      if (lane == 0) dst[e] = m;
+    }
+  }
+}
+
+__global__ __launch_bounds__(GP_WAVE) void select_merge_kernel(CParams P) {
+  const int h = blockIdx.x, i = blockIdx.y;
+  const Info inf = P.info[i];
+  if (inf.mode != MODE_COMPACT) return;
+  const int b = P.page_size, E = inf.E, lane = threadIdx.x;
+  const int nch = (inf.n + SEL_T * b - 1) / (SEL_T * b);
+  const unsigned long long* src = P.cand + ((size_t)i * P.H_kv + h) * SEL_MAX_CHUNKS * MAX_EVICT;
+  constexpr int PER = SEL_MAX_CHUNKS * MAX_EVICT / GP_WAVE;
+  unsigned long long cv[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = lane + GP_WAVE * k;  // chunk idx / MAX_EVICT, rank idx % MAX_EVICT
+    cv[k] = (idx / MAX_EVICT < nch && (idx % MAX_EVICT) < E) ? src[idx] : ~0ull;
+  }
+  int tok = INT_MAX;  // lane e < E: the e-th evicted token (by key)
+  unsigned long long pv = 0;
+  for (int e = 0; e < E; ++e) {
+    unsigned long long m = ~0ull;
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+      if ((e == 0 || cv[k] > pv) && cv[k] < m) m = cv[k];
+    m = wave_min_u64(m);
+    pv = m;
+    if (lane == e) tok = (int)(0xffffffffu - (uint32_t)(m & 0xffffffffu));
+  }
+  // sort the evicted tokens by index: rank of lane e's token among the E
+  int rank = 0;
+  for (int e = 0; e < E; ++e) {
+    const int o = __shfl(tok, e, GP_WAVE);
+    rank += o < tok ? 1 : 0;
+  }
+  __shared__ int s_sorted[MAX_EVICT];
+  if (lane < E) s_sorted[rank] = tok;
+  __syncthreads();
+  if (lane < E) P.ev[((size_t)i * P.H_kv + h) * MAX_EVICT + lane] = s_sorted[lane];
+  if (lane == 0) P.dp0[(size_t)i * P.H_kv + h] = min(s_sorted[0] / b, inf.first_repl);
+}
+
+template <int PB>
+__global__ __launch_bounds__(SEL_T) void select_write_kernel(CParams P) {
+  constexpr int b = PB;
+  const int c = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+  const Info inf = P.info[i];
+  const int n = inf.n;
+  if (c * SEL_T * b >= n) return;
+  int32_t* out = P.kept_idx + ((size_t)i * P.H_kv + h) * P.C_max;
+  const int t0 = (c * SEL_T + threadIdx.x) * b;
+  if (inf.mode != MODE_COMPACT) {
+    if (t0 < n)
+      for (int j = 0; j < b; ++j) out[t0 + j] = inf.mode == MODE_IDENTITY ? t0 + j : -1;
+    return;
+  }
+  const int E = inf.E;
+  __shared__ int s_ev[MAX_EVICT];
+  if (threadIdx.x < MAX_EVICT)
+    s_ev[threadIdx.x] = threadIdx.x < E ? P.ev[((size_t)i * P.H_kv + h) * MAX_EVICT + threadIdx.x] : INT_MAX;
+  __syncthreads();
+  if (c == 0 && threadIdx.x < E) out[inf.K_t + threadIdx.x] = -1;
+  if (t0 >= n) return;
+  int before = 0;  // evicted tokens below t0
+#pragma unroll
+  for (int e = 0; e < MAX_EVICT; ++e) before += s_ev[e] < t0 ? 1 : 0;
+  for (int j = 0; j < b; ++j) {
+    const int t = t0 + j;
+    if (before < E && s_ev[before] == t) {
+      ++before;
+    } else {
+      out[t - before] = t;
+    }
   }
 }
 
@@ -379,106 +447,112 @@ __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
   }
 }
 
-// source position of destination slot j: the j-th kept token, then the recent tokens
-__device__ __forceinline__ int src_of(int j, const int* ev, int E) {
-  int k = 0;
-  while (k < E && ev[k] <= j + k) ++k;
-  return j + k;
-}
-
-template <int ITEMS>
+// Destination slot j of a compacted head takes source slot j + #{k : ev[k] - k <= j} (ev the
+// ascending evicted candidates): the j-th kept candidate, then the recent tokens. A workgroup
+// owns a chunk of destination pages and walks it left to right in windows: it stages the source
+// pages of the window (plus the next page) in LDS with coalesced 16-byte loads, tabulates the
+// source slot of every destination slot, then writes the window's destination pages from LDS.
+// Inside a chunk the extra page is not yet rewritten when it is read; the first page of the next
+// chunk, which another workgroup rewrites, comes from the snapshot.
 __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   const int c = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
   const Info inf = P.info[i];
   if (inf.mode != MODE_COMPACT) return;
-  const int L = P.chunk_pages, b = P.page_size, D = P.D, es = P.es;
+  const int L = P.chunk_pages, W = P.window_pages, D = P.D, es = P.es;
+  const int lb = P.log_b, b = 1 << lb;
   const int dp0 = P.dp0[(size_t)i * P.H_kv + h];
   const int dp_lo = max(dp0, c * L), dp_hi = min((c + 1) * L, inf.n_dest);
   if (dp_lo >= dp_hi) return;
-  __shared__ int s_ev[MAX_EVICT];
-  extern __shared__ __align__(16) uint8_t s_v[];  // value pages [dp_lo .. dp_hi] of this head
+  __shared__ int s_thr[MAX_EVICT];
+  __shared__ int s_src[MAX_WINDOW_SLOTS];
+  extern __shared__ __align__(16) uint8_t s_kv[];  // key pages, then value pages of the window
   const int E = inf.E;
-  if (threadIdx.x < E) s_ev[threadIdx.x] = P.ev[((size_t)i * P.H_kv + h) * MAX_EVICT + threadIdx.x];
+  if (threadIdx.x < MAX_EVICT)
+    s_thr[threadIdx.x] = threadIdx.x < E
+                             ? P.ev[((size_t)i * P.H_kv + h) * MAX_EVICT + threadIdx.x] - (int)threadIdx.x
+                             : INT_MAX;
   const int32_t* obt = P.old_bt + (size_t)i * P.max_pages;
   const int32_t* nbt = P.block_tables + (size_t)inf.r * P.max_pages;
   const size_t pb = page_bytes(P);
-  const int q_per_page = (int)(pb / 16);
-  // stage the source value pages through LDS (coalesced 16-byte loads)
-  const int nsrc = dp_hi - dp_lo + 1;
-  for (int q = threadIdx.x; q < nsrc * q_per_page; q += CP_THREADS) {
-    const int sp = q / q_per_page, qq = q % q_per_page;
-    const int lp = dp_lo + sp;
-    u32x4_t val = u32x4_t{0u, 0u, 0u, 0u};
-    if (lp < inf.P) {
-      const uint8_t* src = from_snapshot(P, lp, dp0, inf.n_dest) ? snap_ptr(P, i, h, lp / L, 1)
-                                                                  : P.v + pool_off(P, obt[lp], h);
-      val = reinterpret_cast<const u32x4_t*>(src)[qq];
+  const int lqpp = P.log_qpp, qpp = 1 << lqpp;  // 16-byte pieces per page
+  const int lkq = P.log_kq, lvq = P.log_vq;
+  const int per = 16 / es;                      // elements per 16-byte piece
+  for (int w0 = dp_lo; w0 < dp_hi; w0 += W) {
+    const int w1 = min(w0 + W, dp_hi);          // destination pages [w0, w1)
+    const int nsrc = w1 - w0 + 1;               // source pages [w0, w1]
+    uint8_t* s_k = s_kv;
+    uint8_t* s_v = s_kv + (size_t)nsrc * pb;
+    __syncthreads();  // the previous window's readers are done with LDS
+    for (int q = threadIdx.x; q < (nsrc << lqpp); q += CP_THREADS) {
+      const int sp = q >> lqpp, qq = q & (qpp - 1);
+      const int lp = w0 + sp;
+      u32x4_t kv = u32x4_t{0u, 0u, 0u, 0u}, vv = kv;
+      if (lp < inf.P) {
+        const bool snap = from_snapshot(P, lp, dp0, inf.n_dest);
+        const uint8_t* ks = snap ? snap_ptr(P, i, h, lp / L, 0) : P.k + pool_off(P, obt[lp], h);
+        const uint8_t* vs = snap ? snap_ptr(P, i, h, lp / L, 1) : P.v + pool_off(P, obt[lp], h);
+        kv = reinterpret_cast<const u32x4_t*>(ks)[qq];
+        vv = reinterpret_cast<const u32x4_t*>(vs)[qq];
+      }
+      reinterpret_cast<u32x4_t*>(s_k)[q] = kv;
+      reinterpret_cast<u32x4_t*>(s_v)[q] = vv;
     }
-    reinterpret_cast<u32x4_t*>(s_v)[q] = val;
-  }
-  __syncthreads();
-  // read phase: keys (16-byte pieces of rows) and value pieces (16 bytes of a value row)
-  const int kq_row = D * es / 16;           // 16-byte pieces per key row
-  const int n_items_k = (dp_hi - dp_lo) * b * kq_row;
-  const int vq_row = b * es / 16;           // 16-byte pieces per value row of a page
-  const int n_items_v = (dp_hi - dp_lo) * D * vq_row;
-  u32x4_t kreg[ITEMS], vreg[ITEMS];
+    const int nslots = (w1 - w0) << lb;
+    for (int q = threadIdx.x; q < nslots; q += CP_THREADS) {
+      const int j = (w0 << lb) + q;
+      int cnt = 0;
 #pragma unroll
-  for (int it = 0; it < ITEMS; ++it) {
-    const int q = threadIdx.x + it * CP_THREADS;
-    if (q < n_items_k) {
-      const int slot_g = q / kq_row, piece = q % kq_row;
-      const int j = dp_lo * b + slot_g;
-      const int sidx = src_of(j, s_ev, E);
-      const int lp = sidx / b, so = sidx % b;
-      const uint8_t* base = from_snapshot(P, lp, dp0, inf.n_dest) ? snap_ptr(P, i, h, lp / L, 0)
-                                                                   : P.k + pool_off(P, obt[lp], h);
-      kreg[it] = reinterpret_cast<const u32x4_t*>(base + (size_t)so * D * es)[piece];
+      for (int k = 0; k < MAX_EVICT; ++k) cnt += s_thr[k] <= j ? 1 : 0;
+      s_src[q] = q + cnt;  // source slot relative to the window
     }
-    if (q < n_items_v) {
-      const int dpl = q / (D * vq_row), rem = q % (D * vq_row);
-      const int dd = rem / vq_row, piece = rem % vq_row;
-      const int per = 16 / es;
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
+    __syncthreads();
+    // keys: 16-byte pieces of destination rows
+    const int krow = D * es;
+    for (int q = threadIdx.x; q < (nslots << lkq); q += CP_THREADS) {
+      const int slot = q >> lkq, piece = q & ((1 << lkq) - 1);
+      const int rs = s_src[slot];
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(s_k + (size_t)(rs >> lb) * pb +
+                                                            (size_t)(rs & (b - 1)) * krow + 16 * piece);
+      const int dp = w0 + (slot >> lb);
+      reinterpret_cast<u32x4_t*>(P.k + pool_off(P, nbt[dp], h) + (size_t)(slot & (b - 1)) * krow)[piece] = val;
+    }
+    // values: 16-byte pieces of destination value rows (token-contiguous inside a page)
+    const int lrow_pieces = lvq;  // pieces per value row
+    const int npieces = (w1 - w0) * D << lrow_pieces;
+    for (int q = threadIdx.x; q < npieces; q += CP_THREADS) {
+      const int piece = q & ((1 << lrow_pieces) - 1);
+      const int rowi = q >> lrow_pieces;  // (page, dd)
+      const int dpl = rowi / D, dd = rowi - dpl * D;
+      uint32_t wv[4] = {0u, 0u, 0u, 0u};
       for (int e = 0; e < per; ++e) {
-        const int slot = piece * per + e;
-        const int j = (dp_lo + dpl) * b + slot;
-        const int sidx = src_of(j, s_ev, E);
-        const int sp = sidx / b - dp_lo, so = sidx % b;
-        const uint8_t* src = s_v + (size_t)sp * pb + ((size_t)dd * b + so) * es;
+        const int rs = s_src[(dpl << lb) + piece * per + e];
+        const uint8_t* src = s_v + (size_t)(rs >> lb) * pb + ((size_t)dd * b + (rs & (b - 1))) * es;
         if (es == 2) {
           const uint32_t x = *reinterpret_cast<const uint16_t*>(src);
-          w[e >> 1] |= x << (16 * (e & 1));
+          wv[e >> 1] |= x << (16 * (e & 1));
         } else {
-          w[e] = *reinterpret_cast<const uint32_t*>(src);
+          wv[e] = *reinterpret_cast<const uint32_t*>(src);
         }
       }
-      vreg[it] = u32x4_t{w[0], w[1], w[2], w[3]};
-    }
-  }
-  __syncthreads();
-  // write phase
-#pragma unroll
-  for (int it = 0; it < ITEMS; ++it) {
-    const int q = threadIdx.x + it * CP_THREADS;
-    if (q < n_items_k) {
-      const int slot_g = q / kq_row, piece = q % kq_row;
-      const int dp = dp_lo + slot_g / b, so = slot_g % b;
-      reinterpret_cast<u32x4_t*>(P.k + pool_off(P, nbt[dp], h) + (size_t)so * D * es)[piece] = kreg[it];
-    }
-    if (q < n_items_v) {
-      const int dpl = q / (D * vq_row), rem = q % (D * vq_row);
-      const int dd = rem / vq_row, piece = rem % vq_row;
-      reinterpret_cast<u32x4_t*>(P.v + pool_off(P, nbt[dp_lo + dpl], h) + (size_t)dd * b * es)[piece] = vreg[it];
+      reinterpret_cast<u32x4_t*>(P.v + pool_off(P, nbt[w0 + dpl], h) + (size_t)dd * b * es)[piece] =
+          u32x4_t{wv[0], wv[1], wv[2], wv[3]};
     }
   }
 }
 
-int chunk_pages_for(int page_size, int D, int es) {
+// LDS window: the K and V source pages of W destination pages plus one
+int window_pages_for(int page_size, int D, int es) {
   const long pv = (long)page_size * D * es;
-  int L = (int)(CP_LDS_BYTES / pv) - 1;
-  return std::max(1, std::min(8, L));
+  const int W = (int)(CP_LDS_BYTES / (2 * pv)) - 1;
+  return std::max(1, std::min(8, W));
 }
+
+int ilog2(int v) {
+  int l = 0;
+  while ((1 << (l + 1)) <= v) ++l;
+  return l;
+}
+
 
 }  // namespace
 
@@ -486,16 +560,16 @@ extern "C" size_t gp_compact_or_grow_workspace_size(int R, int H_kv, int max_pag
                                                    int C_max) {
   (void)C_max;
   if (R <= 0 || H_kv <= 0 || max_pages <= 0 || page_size <= 0) return 0;
-  // sized for the widest supported element (fp32) and head_dim 128
+  // snapshots sized for the widest supported element (fp32) and head_dim 128
   const int es = 4, D = 128;
-  const int L = chunk_pages_for(page_size, D, es);
-  const size_t max_chunks = (size_t)(max_pages + L - 1) / L;
+  const size_t max_chunks = (size_t)(max_pages + CHUNK_PAGES - 1) / CHUNK_PAGES;
   size_t bytes = 0;
   bytes += (size_t)R * sizeof(Info);
   bytes += (size_t)R * max_pages * 4 * 2;               // old_bt, rel
   bytes += (size_t)R * H_kv * MAX_EVICT * 4;
   bytes += (size_t)R * H_kv * 4;
   bytes = (bytes + 255) & ~(size_t)255;
+  bytes += (size_t)R * H_kv * SEL_MAX_CHUNKS * MAX_EVICT * 8;
   bytes += (size_t)R * H_kv * max_chunks * 2 * (size_t)page_size * D * es;
   return bytes;
 }
@@ -522,7 +596,12 @@ extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const fl
   if (kv->dtype != GP_F32 && kv->dtype != GP_BF16) return GP_ERR_INVALID;
   if (D != 64 && D != 128) return GP_ERR_UNSUPPORTED;
   if (b != 16 && b != 32) return GP_ERR_UNSUPPORTED;
-  if (C_max % 4 || C_max > SEL_THREADS * SEL_VPT) return GP_ERR_UNSUPPORTED;
+  {
+    const int es = kv->dtype == GP_F32 ? 4 : 2;
+    const size_t lds = (size_t)2 * (window_pages_for(b, D, es) + 1) * b * D * es;
+    if (lds + sizeof(int) * (MAX_EVICT + MAX_WINDOW_SLOTS) > 64 * 1024) return GP_ERR_UNSUPPORTED;
+  }
+  if (C_max % 4 || C_max > MAX_CAND) return GP_ERR_UNSUPPORTED;
   const size_t need = gp_compact_or_grow_workspace_size(R, H_kv, max_pages, b, C_max);
   if (!workspace || workspace_bytes < need) return GP_ERR_WORKSPACE;
 
@@ -555,8 +634,13 @@ extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const fl
   P.policy = policy;
   P.es = kv->dtype == GP_F32 ? 4 : 2;
   P.tau = tau;
-  P.chunk_pages = chunk_pages_for(b, D, P.es);
-  P.max_chunks = (max_pages + P.chunk_pages - 1) / P.chunk_pages;
+  P.chunk_pages = CHUNK_PAGES;
+  P.max_chunks = (max_pages + CHUNK_PAGES - 1) / CHUNK_PAGES;
+  P.window_pages = window_pages_for(b, D, P.es);
+  P.log_b = ilog2(b);
+  P.log_kq = ilog2(D * P.es / 16);
+  P.log_vq = ilog2(b * P.es / 16);
+  P.log_qpp = ilog2(b * D * P.es / 16);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   size_t off = 0;
   P.info = reinterpret_cast<Info*>(ws + off);
@@ -570,24 +654,29 @@ extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const fl
   P.dp0 = reinterpret_cast<int32_t*>(ws + off);
   off += (size_t)R * H_kv * 4;
   off = (off + 255) & ~(size_t)255;
+  P.cand = reinterpret_cast<unsigned long long*>(ws + off);
+  off += (size_t)R * H_kv * SEL_MAX_CHUNKS * MAX_EVICT * 8;
   P.snap = ws + off;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(decide_alloc_kernel, dim3(1), dim3(64), 0, s, P);
   GP_CHECK_LAUNCH();
-  if (b == 16) hipLaunchKernelGGL(select_kernel<16>, dim3(H_kv, R), dim3(SEL_THREADS), 0, s, P);
-  else hipLaunchKernelGGL(select_kernel<32>, dim3(H_kv, R), dim3(SEL_THREADS), 0, s, P);
-  GP_CHECK_LAUNCH();
+  {
+    const int nch = (C_max + SEL_T * b - 1) / (SEL_T * b);
+    const dim3 g(nch, H_kv, R);
+    if (b == 16) hipLaunchKernelGGL(select_local_kernel<16>, g, dim3(SEL_T), 0, s, P);
+    else hipLaunchKernelGGL(select_local_kernel<32>, g, dim3(SEL_T), 0, s, P);
+    GP_CHECK_LAUNCH();
+    hipLaunchKernelGGL(select_merge_kernel, dim3(H_kv, R), dim3(GP_WAVE), 0, s, P);
+    GP_CHECK_LAUNCH();
+    if (b == 16) hipLaunchKernelGGL(select_write_kernel<16>, g, dim3(SEL_T), 0, s, P);
+    else hipLaunchKernelGGL(select_write_kernel<32>, g, dim3(SEL_T), 0, s, P);
+    GP_CHECK_LAUNCH();
+  }
   hipLaunchKernelGGL(snapshot_kernel, dim3(P.max_chunks, H_kv, R), dim3(CP_THREADS), 0, s, P);
   GP_CHECK_LAUNCH();
-  // items per thread: a chunk holds L pages of b key rows (D * es / 16 pieces each)
-  const long items = ((long)P.chunk_pages * b * D * P.es / 16 + CP_THREADS - 1) / CP_THREADS;
-  const size_t lds = (size_t)(P.chunk_pages + 1) * b * D * P.es;
-  dim3 grid(P.max_chunks, H_kv, R);
-  if (items <= 4) hipLaunchKernelGGL(compact_kernel<4>, grid, dim3(CP_THREADS), lds, s, P);
-  else if (items <= 8) hipLaunchKernelGGL(compact_kernel<8>, grid, dim3(CP_THREADS), lds, s, P);
-  else if (items <= 16) hipLaunchKernelGGL(compact_kernel<16>, grid, dim3(CP_THREADS), lds, s, P);
-  else return GP_ERR_UNSUPPORTED;
+  const size_t lds = (size_t)2 * (P.window_pages + 1) * b * D * P.es;
+  hipLaunchKernelGGL(compact_kernel, dim3(P.max_chunks, H_kv, R), dim3(CP_THREADS), lds, s, P);
   GP_CHECK_LAUNCH();
   return GP_OK;
 }

@@ -437,8 +437,10 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
 }
 
 // Merge of a request's partials (PASK App. B.5): o = sum_j e^{m_j - m} u_j / sum_j e^{m_j - m} l_j.
-// One wave per output row. Rows of requests that one workgroup finished are left as written;
-// rows of empty requests get o = 0 and lse = -inf.
+// One wave per output row; lane j holds partial j's (m_j, l_j), so the maximum, the denominator
+// and the weights come from wave reductions and the partial outputs are fetched in one pass.
+// Rows of requests that one workgroup finished are left as written; rows of empty requests get
+// o = 0 and lse = -inf.
 template <int D, int KIND>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
@@ -453,21 +455,32 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     J = (pb - 1) / R - pa / R + 1;
   }
   if (J == 1) return;
+  // J <= j_max <= J_CAP + 1 < 64
   const float* ml = p.ws_ml + row * p.j_max * 2;
-  float m = -INFINITY;
-  for (int j = 0; j < J; ++j) m = fmaxf(m, ml[2 * j]);
-  float den = 0.f;
-  for (int j = 0; j < J; ++j) den += gp::safe_exp2_diff(ml[2 * j], m) * ml[2 * j + 1];
+  const float mj = lane < J ? ml[2 * lane] : -INFINITY;
+  const float lj = lane < J ? ml[2 * lane + 1] : 0.f;
+  const float m = gp::wave_max(mj);
+  const float wj = gp::safe_exp2_diff(mj, m);
+  const float den = gp::wave_sum(wj * lj);
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  for (int dd = lane; dd < D; dd += 64) {
-    float num = 0.f;
-    for (int j = 0; j < J; ++j)
-      num += gp::safe_exp2_diff(ml[2 * j], m) * p.ws_o[(row * p.j_max + j) * D + dd];
-    const float o = num * inv;
+  const float* wo = p.ws_o + row * p.j_max * D;
+  constexpr int PER = D / 64;
+  float num[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) num[e] = 0.f;
+  for (int j = 0; j < J; ++j) {
+    const float wt = __shfl(wj, j, GP_WAVE);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) num[e] += wt * wo[(size_t)j * D + lane + 64 * e];
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const float o = num[e] * inv;
+    const size_t at = row * D + lane + 64 * e;
     if constexpr (KIND == KIND_F32)
-      reinterpret_cast<float*>(p.out)[row * D + dd] = o;
+      reinterpret_cast<float*>(p.out)[at] = o;
     else
-      reinterpret_cast<uint16_t*>(p.out)[row * D + dd] = (uint16_t)gp::f32_to_bf16_bits(o);
+      reinterpret_cast<uint16_t*>(p.out)[at] = (uint16_t)gp::f32_to_bf16_bits(o);
   }
   if (lane == 0 && p.lse) p.lse[row] = den > 0.f ? (m + __log2f(den)) * GP_LN2 : -INFINITY;
 }

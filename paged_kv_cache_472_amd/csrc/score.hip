@@ -3,8 +3,8 @@
 // the native GQA mapping; Sec. 3.2 Eq. 7 p-coverage working sets).
 //
 // Four launches:
-//   1. prep:      per boundary request and query head, RMS-calibrate both summaries to q_t and
-//                 rotate them to the current position (float64 arithmetic, tiny).
+//   1. prep:      one wave per boundary request, view and query head: RMS-calibrate the summary
+//                 to q_t and rotate it to the current position (float64 arithmetic, tiny).
 //   2. logits:    matrix-core contraction of every candidate key tile with the 2G calibrated
 //                 summaries of its KV head (keys as the 16-row operand, the 2G summaries as
 //                 columns; bf16 keys meet a hi+lo bf16 split of the fp32 summaries, fp32 keys
@@ -64,17 +64,19 @@ __device__ __forceinline__ int candidates(const ScoreParams& P, int i, int* r_ou
 }
 
 // ------------------------------------------------------------------------------ 1. prep
+// one wave per (boundary request, view, query head) row
 __global__ __launch_bounds__(256) void prep_kernel(ScoreParams P) {
   const int i = blockIdx.x;
   int r;
   const int n = candidates(P, i, &r);
-  if (threadIdx.x == 0) P.n_cand[i] = n;
+  if (blockIdx.y == 0 && threadIdx.x == 0) P.n_cand[i] = n;
   if (n < 0) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int D = P.D, half = D / 2;
   const int slot = P.slot_ids[r];
   const double pos = (double)P.positions[r];
-  for (int row = w; row < 2 * P.H_q; row += 4) {
+  const int row = blockIdx.y * 4 + w;
+  if (row < 2 * P.H_q) {
     const int x = row / P.H_q, g = row % P.H_q;
     double qv[2], sv[2];
     double sq = 0.0, ss = 0.0;
@@ -345,30 +347,7 @@ __device__ __forceinline__ int cmp_p(const uint32_t a[6], const uint32_t p[5]) {
   return 0;
 }
 
-template <typename T>
-__device__ __forceinline__ T block_sum(T v, T* scratch) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, GP_WAVE);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) scratch[w] = v;
-  __syncthreads();
-  T s = 0;
-  for (int k = 0; k < WS_THREADS / GP_WAVE; ++k) s += scratch[k];
-  return s;
-}
-
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* scratch) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, GP_WAVE));
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) scratch[w] = v;
-  __syncthreads();
-  uint32_t s = 0;
-  for (int k = 0; k < WS_THREADS / GP_WAVE; ++k) s = max(s, scratch[k]);
-  return s;
-}
+constexpr int WS_WAVES = WS_THREADS / GP_WAVE;
 
 __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) {
   const int row = blockIdx.x, i = blockIdx.y;
@@ -380,9 +359,53 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     if (threadIdx.x == 0) *out = n < 0 ? -1 : 0;
     return;
   }
-  __shared__ double sd[WS_THREADS / GP_WAVE];
-  __shared__ uint64_t su[WS_THREADS / GP_WAVE];
-  __shared__ uint32_t sx[WS_THREADS / GP_WAVE];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // Block reductions with one barrier each: wave partials alternate between two scratch
+  // buffers, so a buffer is rewritten only after every thread has passed another barrier.
+  __shared__ double s_d[2][WS_WAVES];
+  __shared__ uint64_t s_u[2][8][WS_WAVES];
+  __shared__ uint32_t s_x[2][WS_WAVES];
+  int ph = 0;
+  auto sum_d = [&](double v) -> double {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, GP_WAVE);
+    if (lane == 0) s_d[ph][w] = v;
+    __syncthreads();
+    double t = 0.0;
+#pragma unroll
+    for (int k = 0; k < WS_WAVES; ++k) t += s_d[ph][k];
+    ph ^= 1;
+    return t;
+  };
+  auto sum_u8 = [&](uint64_t (&v)[8]) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v[c] += __shfl_xor(v[c], o, GP_WAVE);
+      if (lane == 0) s_u[ph][c][w] = v[c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint64_t t = 0;
+#pragma unroll
+      for (int k = 0; k < WS_WAVES; ++k) t += s_u[ph][c][k];
+      v[c] = t;
+    }
+    ph ^= 1;
+  };
+  auto max_x = [&](uint32_t v) -> uint32_t {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, GP_WAVE));
+    if (lane == 0) s_x[ph][w] = v;
+    __syncthreads();
+    uint32_t t = 0;
+#pragma unroll
+    for (int k = 0; k < WS_WAVES; ++k) t = max(t, s_x[ph][k]);
+    ph ^= 1;
+    return t;
+  };
+
   const float* src = (x == 0 ? P.a_short : P.a_long) + ((size_t)i * P.H_kv + h) * P.C_max;
   uint32_t u[WS_VPT];
 #pragma unroll
@@ -390,39 +413,41 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     const int t = threadIdx.x + j * WS_THREADS;
     u[j] = t < n ? __float_as_uint(src[t]) & 0x7fffffffu : 0u;
   }
-  const double p = 0.0;  // unused: the float64 search compares against p_f64 below
-  (void)p;
   double p_f64 = 0.0;
   for (int k = 4; k >= 0; --k) p_f64 = p_f64 * 4294967296.0 + (double)P.p_fixed[k];
   p_f64 = ldexp(p_f64, -149);
 
-  // exact total mass: if it never reaches p, K = |C|
+  // exact total mass: if it never reaches p, K = |C|; also the largest weight
+  uint32_t vmax;
   {
     Acc5 a = {};
+    uint32_t m = 0u;
 #pragma unroll
-    for (int j = 0; j < WS_VPT; ++j) acc_add(a, u[j]);
-    Acc5 t;
+    for (int j = 0; j < WS_VPT; ++j) {
+      acc_add(a, u[j]);
+      m = max(m, u[j]);
+    }
+    uint64_t t[8] = {a.d[0], a.d[1], a.d[2], a.d[3], a.d[4], a.d[5], 0ull, 0ull};
+    sum_u8(t);
+    Acc5 tt;
 #pragma unroll
-    for (int k = 0; k < 6; ++k) t.d[k] = block_sum<uint64_t>(a.d[k], su);
+    for (int k = 0; k < 6; ++k) tt.d[k] = t[k];
     uint32_t tot[6];
-    acc_norm(t, tot);
+    acc_norm(tt, tot);
     if (cmp_p(tot, P.p_fixed) < 0) {
       if (threadIdx.x == 0) *out = n;
       return;
     }
+    vmax = max_x(m);
   }
-  // float64 binary search for the largest bit pattern T with mass(weights >= T) >= p
-  uint32_t lo = 1u, hi = 0x7f800000u;  // mass(>= lo) >= p holds up to rounding; hi fails
+  // float64 bisection for the largest bit pattern T with mass(weights >= T) >= p
+  uint32_t lo = 1u, hi = vmax + 1u;  // mass(>= lo) >= p holds up to rounding; hi fails
   while (hi - lo > 1u) {
     const uint32_t mid = lo + (hi - lo) / 2;
-    double s = 0.0;
+    double s4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int j = 0; j < WS_VPT; ++j) {
-      uint32_t uj = u[j];
-      asm volatile("" : "+v"(uj));  // keep the float64 conversion inside the loop (registers)
-      s += uj >= mid ? (double)__uint_as_float(uj) : 0.0;
-    }
-    s = block_sum<double>(s, sd);
+    for (int j = 0; j < WS_VPT; ++j) s4[j & 3] += u[j] >= mid ? (double)__uint_as_float(u[j]) : 0.0;
+    const double s = sum_d((s4[0] + s4[1]) + (s4[2] + s4[3]));
     if (s >= p_f64) lo = mid; else hi = mid;
   }
   // snap T to the largest present weight <= lo
@@ -431,7 +456,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     uint32_t best = 0u;
 #pragma unroll
     for (int j = 0; j < WS_VPT; ++j) if (u[j] <= lo) best = max(best, u[j]);
-    T = block_max_u32(best, sx);
+    T = max_x(best);
   }
   // exact certificate: mass(> T) < p <= mass(>= T); move T to a neighbour value until it holds
   for (int iter = 0; iter < 64; ++iter) {
@@ -446,11 +471,13 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
         ++ceq;
       }
     }
+    uint64_t t[8] = {gt.d[0], gt.d[1], gt.d[2], gt.d[3], gt.d[4], gt.d[5], (uint64_t)cgt, (uint64_t)ceq};
+    sum_u8(t);
     Acc5 sgt;
 #pragma unroll
-    for (int k = 0; k < 6; ++k) sgt.d[k] = block_sum<uint64_t>(gt.d[k], su);
-    cgt = (uint32_t)block_sum<uint64_t>((uint64_t)cgt, su);
-    ceq = (uint32_t)block_sum<uint64_t>((uint64_t)ceq, su);
+    for (int k = 0; k < 6; ++k) sgt.d[k] = t[k];
+    cgt = (uint32_t)t[6];
+    ceq = (uint32_t)t[7];
     uint32_t mge[6], mgt[6];
     acc_norm(sgt, mgt);
     Acc5 sge = sgt;  // mass(>= T) = mass(> T) + #(== T) * T
@@ -461,7 +488,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
       uint32_t best = 0u;
 #pragma unroll
       for (int j = 0; j < WS_VPT; ++j) if (u[j] < T) best = max(best, u[j]);
-      T = block_max_u32(best, sx);
+      T = max_x(best);
       continue;
     }
     if (cmp_p(mgt, P.p_fixed) >= 0) {
@@ -469,7 +496,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
       uint32_t best = 0u;
 #pragma unroll
       for (int j = 0; j < WS_VPT; ++j) if (u[j] > T) best = max(best, ~u[j]);
-      T = ~block_max_u32(best, sx);
+      T = ~max_x(best);
       continue;
     }
     // K = #(> T) + ceil((p - mass(> T)) / T), all exact
@@ -478,9 +505,9 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
       uint32_t X[5];
       int64_t borrow = 0;
       for (int k = 0; k < 5; ++k) {
-        int64_t t = (int64_t)P.p_fixed[k] - (int64_t)mgt[k] - borrow;
-        borrow = t < 0;
-        X[k] = (uint32_t)(t + (borrow ? 4294967296ll : 0ll));
+        int64_t tk = (int64_t)P.p_fixed[k] - (int64_t)mgt[k] - borrow;
+        borrow = tk < 0;
+        X[k] = (uint32_t)(tk + (borrow ? 4294967296ll : 0ll));
       }
       const uint32_t E = T >> 23;
       uint32_t M = T & 0x7fffffu, sh = 0;
@@ -611,7 +638,7 @@ extern "C" int gp_score_and_working_set(const void* q, int q_dtype, int B, int H
   P.stats = P.logits + (size_t)R * 2 * H_q * (size_t)((C_max + 3) / 4) * 4;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(prep_kernel, dim3(R), dim3(256), 0, s, P);
+  hipLaunchKernelGGL(prep_kernel, dim3(R, (2 * H_q + 3) / 4), dim3(256), 0, s, P);
   GP_CHECK_LAUNCH();
   dim3 lg(P.nch, H_kv, R);
   if (q_dtype == GP_BF16) {
