@@ -76,3 +76,68 @@ __device__ __forceinline__ f32x4_t mfma_f32_16x16x4(float a, float b, f32x4_t c)
   do {                                                    \
     if (hipGetLastError() != hipSuccess) return GP_ERR_HIP; \
   } while (0)
+
+// Wave64 reductions on the data-parallel-primitive (DPP) path: lane permutations inside rows
+// of 16 (quad swaps, half-row and row mirrors), then the row broadcasts of lanes 15 and 31,
+// leave the full reduction in lane 63, which is read back as a wave-uniform value. Unlike
+// __shfl_xor these never go through the LDS permute unit.
+namespace gp {
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)v);
+  const uint32_t hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane63_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// DPP controls: quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror, row_bcast:15,
+// row_bcast:31 (the broadcasts only update rows 1,3 and 2,3 respectively).
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+  v += dpp_u64<0xb1>(v);
+  v += dpp_u64<0x4e>(v);
+  v += dpp_u64<0x141>(v);
+  v += dpp_u64<0x140>(v);
+  v += dpp_u64<0x142, 0xa>(v);
+  v += dpp_u64<0x143, 0xc>(v);
+  return readlane63_u64(v);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+  uint64_t v = __builtin_bit_cast(uint64_t, x);
+  x += __builtin_bit_cast(double, dpp_u64<0xb1>(v));
+  v = __builtin_bit_cast(uint64_t, x);
+  x += __builtin_bit_cast(double, dpp_u64<0x4e>(v));
+  v = __builtin_bit_cast(uint64_t, x);
+  x += __builtin_bit_cast(double, dpp_u64<0x141>(v));
+  v = __builtin_bit_cast(uint64_t, x);
+  x += __builtin_bit_cast(double, dpp_u64<0x140>(v));
+  v = __builtin_bit_cast(uint64_t, x);
+  x += __builtin_bit_cast(double, dpp_u64<0x142, 0xa>(v));
+  v = __builtin_bit_cast(uint64_t, x);
+  x += __builtin_bit_cast(double, dpp_u64<0x143, 0xc>(v));
+  return __builtin_bit_cast(double, readlane63_u64(__builtin_bit_cast(uint64_t, x)));
+}
+
+// maximum of unsigned values (lanes outside a broadcast's row mask see 0, the identity)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xb1>(v));
+  v = max(v, dpp_u32<0x4e>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  v = max(v, dpp_u32<0x142, 0xa>(v));
+  v = max(v, dpp_u32<0x143, 0xc>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+}  // namespace gp

@@ -11,9 +11,9 @@
 //                 use the fp32 MFMA); logits go to the workspace with per-chunk (max, sum).
 //   3. normalize: softmax of every row and the mean over the G heads of each view.
 //   4. working set: per (request, KV head, view) the p-coverage size, exact on the fp32 weights:
-//                 a float64 binary search over the weight bit patterns finds the threshold
-//                 weight, which an exact 160-bit fixed-point sum then certifies (and corrects
-//                 if float64 rounding picked a neighbour).
+//                 a binary search over the weight bit patterns (float32 sums per thread,
+//                 float64 across threads) finds the threshold weight, which an exact 160-bit
+//                 fixed-point sum then certifies (and corrects if rounding picked a neighbour).
 #include "common.h"
 
 namespace {
@@ -128,7 +128,9 @@ __global__ __launch_bounds__(256) void prep_kernel(ScoreParams P) {
 // ------------------------------------------------------------------------------ 2. logits
 template <int D, bool BF16>
 __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
-  const int chunk = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+  // heads vary fastest over the grid, so the KV heads of a page (adjacent in HBM) are read by
+  // neighbouring workgroups at the same time
+  const int h = blockIdx.x, chunk = blockIdx.y, i = blockIdx.z;
   int r;
   const int n = candidates(P, i, &r);
   const int tile0 = chunk * CHUNK_TILES;
@@ -246,17 +248,21 @@ __global__ __launch_bounds__(256) void normalize_kernel(ScoreParams P) {
   const int n = candidates(P, i, &r);
   if (n <= 0 || blk * 1024 >= n) return;
   const int G = P.G;
-  __shared__ float sM[32], sInv[32];
-  const int nchunks = (n + CHUNK_TILES * 16 - 1) / (CHUNK_TILES * 16);
-  if (threadIdx.x < 2 * G) {
-    const int c = threadIdx.x, x = c / G, g = c % G;
+  __shared__ float sM[16], sInv[16];
+  const int nchunks = (n + CHUNK_TILES * 16 - 1) / (CHUNK_TILES * 16);  // <= 64
+  // one wave per (view, head) column: lane j holds chunk j's (max, sum)
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int col = w; col < 2 * G; col += 4) {
+    const int x = col / G, g = col % G;
     const float* st = P.stats + (((size_t)i * 2 + x) * P.H_q + h * G + g) * P.nch * 2;
-    float m = -INFINITY;
-    for (int j = 0; j < nchunks; ++j) m = fmaxf(m, st[2 * j]);
-    float l = 0.f;
-    for (int j = 0; j < nchunks; ++j) l += st[2 * j + 1] * gp::safe_exp2_diff(st[2 * j], m);
-    sM[c] = m;
-    sInv[c] = l > 0.f ? 1.f / l : 0.f;
+    const float mj = lane < nchunks ? st[2 * lane] : -INFINITY;
+    const float lj = lane < nchunks ? st[2 * lane + 1] : 0.f;
+    const float m = gp::wave_max(mj);
+    const float l = gp::wave_sum(lj * gp::safe_exp2_diff(mj, m));
+    if (lane == 0) {
+      sM[col] = m;
+      sInv[col] = l > 0.f ? 1.f / l : 0.f;
+    }
   }
   __syncthreads();
   const int t = blk * 1024 + threadIdx.x * 4;
@@ -367,8 +373,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   __shared__ uint32_t s_x[2][WS_WAVES];
   int ph = 0;
   auto sum_d = [&](double v) -> double {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, GP_WAVE);
+    v = gp::wave_sum_f64(v);
     if (lane == 0) s_d[ph][w] = v;
     __syncthreads();
     double t = 0.0;
@@ -380,8 +385,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   auto sum_u8 = [&](uint64_t (&v)[8]) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) v[c] += __shfl_xor(v[c], o, GP_WAVE);
+      v[c] = gp::wave_sum_u64(v[c]);
       if (lane == 0) s_u[ph][c][w] = v[c];
     }
     __syncthreads();
@@ -395,8 +399,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     ph ^= 1;
   };
   auto max_x = [&](uint32_t v) -> uint32_t {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, GP_WAVE));
+    v = gp::wave_max_u32(v);
     if (lane == 0) s_x[ph][w] = v;
     __syncthreads();
     uint32_t t = 0;
@@ -440,14 +443,16 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     }
     vmax = max_x(m);
   }
-  // float64 bisection for the largest bit pattern T with mass(weights >= T) >= p
+  // bisection for the largest bit pattern T with mass(weights >= T) >= p
   uint32_t lo = 1u, hi = vmax + 1u;  // mass(>= lo) >= p holds up to rounding; hi fails
   while (hi - lo > 1u) {
     const uint32_t mid = lo + (hi - lo) / 2;
-    double s4[4] = {0.0, 0.0, 0.0, 0.0};
+    // a thread's 32 weights are summed in float32 (the search only has to land on or next to
+    // the threshold; the certificate below decides exactly), threads in float64
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < WS_VPT; ++j) s4[j & 3] += u[j] >= mid ? (double)__uint_as_float(u[j]) : 0.0;
-    const double s = sum_d((s4[0] + s4[1]) + (s4[2] + s4[3]));
+    for (int j = 0; j < WS_VPT; ++j) s4[j & 3] += u[j] >= mid ? __uint_as_float(u[j]) : 0.f;
+    const double s = sum_d((double)(s4[0] + s4[1]) + (double)(s4[2] + s4[3]));
     if (s >= p_f64) lo = mid; else hi = mid;
   }
   // snap T to the largest present weight <= lo
@@ -640,7 +645,7 @@ extern "C" int gp_score_and_working_set(const void* q, int q_dtype, int B, int H
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(prep_kernel, dim3(R, (2 * H_q + 3) / 4), dim3(256), 0, s, P);
   GP_CHECK_LAUNCH();
-  dim3 lg(P.nch, H_kv, R);
+  dim3 lg(H_kv, P.nch, R);
   if (q_dtype == GP_BF16) {
     if (D == 64) hipLaunchKernelGGL((logits_kernel<64, true>), lg, dim3(LG_THREADS), 0, s, P);
     else hipLaunchKernelGGL((logits_kernel<128, true>), lg, dim3(LG_THREADS), 0, s, P);
