@@ -181,6 +181,8 @@ int gp_score_and_working_set(const void* q, int q_dtype, int B, int H_q, const f
  *   a_short / a_long / ws_counts / n_cand as produced by gp_score_and_working_set.
  *   kv, block_tables, n_pages, context_lens, refcount, free_stack, free_top are updated in place.
  *   Uniform caches only (page_tag must be NULL). Requests of one call must be distinct.
+ *   Limits: R <= 1024, page_size 16 or 32 (32-token fp32 pages need head_dim 64),
+ *   C_max <= 32768 and a multiple of 4.
  */
 size_t gp_compact_or_grow_workspace_size(int R, int H_kv, int max_pages, int page_size, int C_max);
 int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const float* a_short,

@@ -3,19 +3,20 @@
 // fallback and prefix-safe compaction, App. H.1 policies).
 //
 // Launches:
-//   1. decide_alloc (one wave): requests in req_idx order. Decision from the exact comparison of
-//      sum_h (K^S_h - K^L_h) / (H |C|) with tau; Grow pops the LIFO free stack; compression pops
-//      one private page per shared page it must write (wave-parallel ballot ranks, ascending
-//      logical order); released references are applied after every pop of the call.
+//   1. decide_alloc (one workgroup): requests in req_idx order. Decision from the exact comparison
+//      of sum_h (K^S_h - K^L_h) / (H |C|) with tau; Grow pops the LIFO free stack; compression
+//      pops one private page per shared page it must write (ascending logical order); released
+//      references are applied after every pop of the call. Per-request work and the page checks
+//      run in parallel; only the pop order is a serial scan.
 //   2. select (three launches): s = max(a^S, a^L); the E <= page_size evicted tokens are the E
 //      smallest of the unique keys (s, ~index) outside each page's k_loc quota, which realises
 //      the (s desc, index asc) order exactly: chunk-local E smallest, their merge per request
 //      and KV head, then kept_idx written in parallel.
 //   3. snapshot: compaction is a left shift by at most E slots, so a chunk of destination pages
 //      only reads its own pages plus the first page of the next chunk; that page is saved first.
-//   4. compact (per chunk x KV head x request): tabulate the source slot of every destination
-//      slot, read all sources (keys row-wise from HBM, values through LDS), barrier, write the
-//      chunk's destination pages.
+//   4. compact (per chunk x KV head x request), window by window: tabulate the source slot of
+//      every destination slot, read all sources (key rows into registers, value pages into
+//      LDS), barrier, write the window's destination pages.
 #include "common.h"
 
 #include <climits>
@@ -32,7 +33,8 @@ constexpr int MAX_EVICT = 32;
 constexpr int CHUNK_PAGES = 16;           // destination pages per compaction workgroup
 constexpr int MAX_WINDOW_SLOTS = 8 * 32;  // LDS window pages (<= 8) x page size (<= 32)
 constexpr int CP_THREADS = 256;
-constexpr int CP_LDS_BYTES = 56 * 1024;  // K and V source pages of one window
+constexpr int CP_LDS_BYTES = 40 * 1024;  // source value pages of one window
+constexpr int K_PIECES = 8;               // key pieces per thread and window
 
 struct Info {
   int r, mode, P, ctx_old, n, K_t, R_n, E, ctx_new, n_dest, first_repl, pad;
@@ -83,18 +85,51 @@ __device__ bool trend_exceeds(long long Dsum, long long HN, double tau) {
   return (__int128)Dsum > fl;                              // integer D > x  <=>  D > floor(x)
 }
 
-__global__ __launch_bounds__(64) void decide_alloc_kernel(CParams P) {
-  const int lane = threadIdx.x;
-  const int b = P.page_size;
-  int top = *P.free_top;
-  if (top < 0 || top > P.num_pages) top = 0;
-  int nrel = 0;
-  for (int i = 0; i < P.R; ++i) {
+// Decision and page allocation for all boundary requests in one workgroup. The refcount of a
+// page that sits in a block table does not change until the releases at the end of the call
+// (pops only touch free pages), so everything except the order of the pops is computed for all
+// requests at once; only a short register scan over the requests runs serially.
+constexpr int DA_THREADS = 1024;
+constexpr int DA_MAX_R = 1024;
+enum : int {
+  F_VALID = 1, F_GROW = 2, F_SLOT = 4, F_EMPTY = 8, F_CHECK = 16, F_BAD = 32
+};
+enum : int { O_NONE = 0, O_GROW = 1, O_IDENTITY = 2, O_COMPACT = 3 };
+
+__device__ __forceinline__ int block_excl_scan(int v, int* s_w, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(x, o, GP_WAVE);
+    if (lane >= o) x += t;
+  }
+  if (lane == 63) s_w[w] = x;
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int k = 0; k < nw; ++k) {
+    off += k < w ? s_w[k] : 0;
+    tot += s_w[k];
+  }
+  __syncthreads();
+  *total = tot;
+  return off + x - v;
+}
+
+__global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
+  const int tid = threadIdx.x;
+  const int b = P.page_size, R = P.R;
+  __shared__ int s_flags[DA_MAX_R], s_cnt[DA_MAX_R], s_pn[DA_MAX_R], s_ndest[DA_MAX_R];
+  __shared__ int s_r[DA_MAX_R], s_top[DA_MAX_R], s_relbase[DA_MAX_R], s_pref[DA_MAX_R + 1];
+  __shared__ int s_w[DA_THREADS / GP_WAVE];
+  __shared__ int s_any_repl, s_top_end, s_nrel;
+
+  // ---- A: per request (one thread each): validity, primary decision, compaction geometry
+  for (int i = tid; i < R; i += DA_THREADS) {
     Info inf = {};
     inf.mode = MODE_NONE;
     const int nc = P.n_cand[i];
     inf.n = (nc > 0 && nc <= P.C_max) ? nc : 0;
-    int dec = GP_DECISION_NO_PAGES;
     const int r = P.req_idx[i];
     inf.r = r;
     bool ok = r >= 0 && r < P.B && nc >= 0 && nc <= P.C_max;
@@ -109,58 +144,31 @@ __global__ __launch_bounds__(64) void decide_alloc_kernel(CParams P) {
       n = ctx == 0 ? 0 : ((ctx + b - 1) / b - 1) * b;
       ok = n == nc;
     }
-    // sum over KV heads of K^S - K^L
-    long long dsum = 0;
-    bool bad_ws = false;
+    long long dsum = 0;  // sum over KV heads of K^S - K^L
     if (ok) {
-      for (int h = lane; h < P.H_kv; h += 64) {
+      bool bad_ws = false;
+      for (int h = 0; h < P.H_kv; ++h) {
         const int ks = P.ws_counts[((size_t)i * P.H_kv + h) * 2 + 0];
         const int kl = P.ws_counts[((size_t)i * P.H_kv + h) * 2 + 1];
         if (ks < 0 || kl < 0) bad_ws = true;
         dsum += (long long)ks - kl;
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) dsum += __shfl_xor(dsum, o, GP_WAVE);
-      bad_ws = __any(bad_ws);
       if (n > 0 && bad_ws) ok = false;
     }
-    if (!ok) {
-      if (lane == 0) {
-        P.decision[i] = GP_DECISION_NO_PAGES;
-        P.info[i] = inf;
+    int flags = 0, ndest = 0;
+    if (ok) {
+      flags |= F_VALID;
+      const int pol = P.policies ? P.policies[i] : P.policy;
+      bool want_grow;
+      if (pol == GP_POLICY_FORCE_COMPRESS) want_grow = false;
+      else if (pol == GP_POLICY_FORCE_GROW || n == 0) want_grow = true;
+      else {
+        const bool g = trend_exceeds(dsum, (long long)P.H_kv * n, P.tau);
+        want_grow = (pol == GP_POLICY_INVERSE) ? !g : g;
       }
-      continue;
-    }
-    const int pol = P.policies ? P.policies[i] : P.policy;
-    bool want_grow;
-    if (pol == GP_POLICY_FORCE_COMPRESS) want_grow = false;
-    else if (pol == GP_POLICY_FORCE_GROW || n == 0) want_grow = true;
-    else {
-      const bool g = trend_exceeds(dsum, (long long)P.H_kv * n, P.tau);
-      want_grow = (pol == GP_POLICY_INVERSE) ? !g : g;
-    }
-    int code = GP_DECISION_COMPRESS;
-    bool done = false;
-    if (want_grow) {
-      if (top > 0 && Pn < P.max_pages) {
-        if (lane == 0) {
-          const int pg = P.free_stack[top - 1];
-          P.free_stack[top - 1] = -1;
-          P.block_tables[(size_t)r * P.max_pages + Pn] = pg;
-          P.n_pages[r] = Pn + 1;
-          if (pg >= 0 && pg < P.num_pages) P.refcount[pg] = 1;
-        }
-        --top;
-        dec = GP_DECISION_GROW;
-        done = true;
-      } else if (n == 0) {
-        dec = GP_DECISION_NO_PAGES;
-        done = true;
-      } else {
-        code = GP_DECISION_GROW_FALLBACK_COMPRESS;
-      }
-    }
-    if (!done) {
+      if (want_grow) flags |= F_GROW;
+      if (Pn < P.max_pages) flags |= F_SLOT;
+      if (n == 0) flags |= F_EMPTY;
       const int R_n = ctx - n;
       const int K_t = min(n, max(0, (Pn - 1) * b - R_n));
       const int E = n - K_t;
@@ -169,76 +177,172 @@ __global__ __launch_bounds__(64) void decide_alloc_kernel(CParams P) {
       inf.K_t = K_t;
       inf.R_n = R_n;
       inf.E = E;
-      if (E == 0) {
-        inf.mode = MODE_IDENTITY;
-        dec = code;
-      } else if (E > MAX_EVICT) {
-        dec = GP_DECISION_NO_PAGES;  // unreachable for page sizes <= 32 (E <= page_size)
-      } else {
-        const int ctx_new = K_t + R_n;
-        const int n_dest = (ctx_new + b - 1) / b;
-        int32_t* row = P.block_tables + (size_t)r * P.max_pages;
-        int cnt = 0;
-        bool bad = false;
-        // every page the compaction may read (all Pn) must be a valid id; the first n_dest
-        // are written, so the shared ones among them need a replacement
-        for (int j0 = 0; j0 < Pn; j0 += 64) {
-          const int j = j0 + lane;
-          bool sh = false;
-          if (j < Pn) {
-            const int pg = row[j];
-            if (pg < 0 || pg >= P.num_pages) bad = true;
-            else sh = j < n_dest && P.refcount[pg] > 1;
+      inf.ctx_new = K_t + R_n;
+      ndest = (inf.ctx_new + b - 1) / b;
+      inf.n_dest = ndest;
+      if (E > 0 && E <= MAX_EVICT) flags |= F_CHECK;  // may compact: check its pages
+      flags |= min(E, 255) << 8;
+    }
+    if (i < DA_MAX_R) {
+      s_flags[i] = flags;
+      s_cnt[i] = 0;
+      s_pn[i] = (flags & F_CHECK) ? Pn : 0;
+      s_ndest[i] = ndest;
+      s_r[i] = r;
+    }
+    P.info[i] = inf;
+  }
+  __syncthreads();
+
+  // ---- B: every (request, page) pair of a request that may compact: all page ids valid,
+  // count the shared ones among the pages it writes, keep a copy of the old block table row
+  if (tid == 0) {
+    int acc = 0;
+    for (int i = 0; i < R; ++i) {
+      s_pref[i] = acc;
+      acc += s_pn[i];
+    }
+    s_pref[R] = acc;
+  }
+  __syncthreads();
+  const int npairs = s_pref[R];
+  for (int f = tid; f < npairs; f += DA_THREADS) {
+    int lo = 0, hi = R;  // last i with s_pref[i] <= f
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] <= f) lo = mid; else hi = mid;
+    }
+    const int i = lo, j = f - s_pref[i];
+    const int pg = P.block_tables[(size_t)s_r[i] * P.max_pages + j];
+    P.old_bt[(size_t)i * P.max_pages + j] = pg;
+    if (pg < 0 || pg >= P.num_pages) atomicOr(&s_flags[i], F_BAD);
+    else if (j < s_ndest[i] && P.refcount[pg] > 1) atomicAdd(&s_cnt[i], 1);
+  }
+  __syncthreads();
+
+  // ---- C: allocation order (registers only): outcome, stack top before the pops, release base
+  if (tid == 0) {
+    int top = *P.free_top;
+    if (top < 0 || top > P.num_pages) top = 0;
+    int nrel = 0, any = 0;
+    for (int i = 0; i < R; ++i) {
+      const int fl = s_flags[i];
+      int out = O_NONE, dec = GP_DECISION_NO_PAGES;
+      s_top[i] = top;
+      s_relbase[i] = nrel;
+      if (fl & F_VALID) {
+        bool compress = true;
+        int code = GP_DECISION_COMPRESS;
+        if (fl & F_GROW) {
+          if (top > 0 && (fl & F_SLOT)) {
+            --top;
+            out = O_GROW;
+            dec = GP_DECISION_GROW;
+            compress = false;
+          } else if (fl & F_EMPTY) {
+            compress = false;  // nothing to compress: NO_PAGES
+          } else {
+            code = GP_DECISION_GROW_FALLBACK_COMPRESS;
           }
-          cnt += __popcll(__ballot(sh));
         }
-        bad = __any(bad);
-        if (bad || cnt > top) {
-          dec = GP_DECISION_NO_PAGES;
-        } else {
-          for (int j = lane; j < Pn; j += 64) P.old_bt[(size_t)i * P.max_pages + j] = row[j];
-          int base = 0;
-          int first = n_dest;
-          for (int j0 = 0; j0 < n_dest; j0 += 64) {
-            const int j = j0 + lane;
-            bool sh = false;
-            int pg = -1;
-            if (j < n_dest) {
-              pg = row[j];
-              sh = P.refcount[pg] > 1;
-            }
-            const unsigned long long m = __ballot(sh);
-            if (m && first == n_dest) first = j0 + __ffsll((long long)m) - 1;
-            const int rank = base + __popcll(m & ((1ull << lane) - 1ull));
-            if (sh) {
-              const int np = P.free_stack[top - 1 - rank];
-              P.free_stack[top - 1 - rank] = -1;
-              P.rel[nrel + rank] = pg;
-              row[j] = np;
-              if (np >= 0 && np < P.num_pages) P.refcount[np] = 1;
-            }
-            base += __popcll(m);
+        if (compress) {
+          const int E = fl >> 8;
+          if (E == 0) {
+            out = O_IDENTITY;
+            dec = code;
+          } else if (E > MAX_EVICT) {
+            dec = GP_DECISION_NO_PAGES;  // unreachable for page sizes <= 32 (E <= page_size)
+          } else if ((fl & F_BAD) || s_cnt[i] > top) {
+            dec = GP_DECISION_NO_PAGES;
+          } else {
+            out = O_COMPACT;
+            dec = code;
+            top -= s_cnt[i];
+            nrel += s_cnt[i];
+            any |= s_cnt[i] > 0;
           }
-          top -= cnt;
-          nrel += cnt;
-          if (lane == 0) P.context_lens[r] = ctx_new;
-          inf.mode = MODE_COMPACT;
-          inf.ctx_new = ctx_new;
-          inf.n_dest = n_dest;
-          inf.first_repl = first;
-          dec = code;
         }
       }
+      s_flags[i] = (out << 4) | dec;  // outcome for phase D
     }
-    if (lane == 0) {
-      P.decision[i] = dec;
-      P.info[i] = inf;
+    s_top_end = top;
+    s_nrel = nrel;
+    s_any_repl = any;
+  }
+  __syncthreads();
+
+  // ---- D: apply outcomes (one thread per request)
+  for (int i = tid; i < R; i += DA_THREADS) {
+    const int out = s_flags[i] >> 4, dec = s_flags[i] & 15;
+    P.decision[i] = dec;
+    const int r = s_r[i];
+    if (out == O_GROW) {
+      const int top = s_top[i];
+      const int Pn = P.info[i].P;
+      const int pg = P.free_stack[top - 1];
+      P.free_stack[top - 1] = -1;
+      P.block_tables[(size_t)r * P.max_pages + Pn] = pg;
+      P.n_pages[r] = Pn + 1;
+      if (pg >= 0 && pg < P.num_pages) P.refcount[pg] = 1;
+      P.info[i].mode = MODE_NONE;
+    } else if (out == O_IDENTITY) {
+      P.info[i].mode = MODE_IDENTITY;
+    } else if (out == O_COMPACT) {
+      P.context_lens[r] = P.info[i].ctx_new;
+      P.info[i].mode = MODE_COMPACT;
+      P.info[i].first_repl = s_ndest[i];
+    } else {
+      P.info[i].mode = MODE_NONE;
+    }
+  }
+  // shared pages of compacting requests get private replacements, popped in ascending logical
+  // order (an ordered scan over the pairs gives each its rank within its request)
+  if (s_any_repl) {
+    __syncthreads();
+    int carry = 0;
+    for (int f0 = 0; f0 < npairs; f0 += DA_THREADS) {
+      const int f = f0 + tid;
+      int i = 0, j = 0, pg = -1;
+      bool sh = false;
+      if (f < npairs) {
+        int lo = 0, hi = R;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_pref[mid] <= f) lo = mid; else hi = mid;
+        }
+        i = lo;
+        j = f - s_pref[i];
+        if ((s_flags[i] >> 4) == O_COMPACT && j < s_ndest[i]) {
+          pg = P.old_bt[(size_t)i * P.max_pages + j];
+          sh = P.refcount[pg] > 1;
+        }
+      }
+      int total;
+      const int ex = carry + block_excl_scan(sh ? 1 : 0, s_w, &total);
+      if (sh) {
+        // shared pairs of earlier requests precede request i's in the scan
+        int before = 0;
+        for (int k = 0; k < i; ++k)
+          if ((s_flags[k] >> 4) == O_COMPACT) before += s_cnt[k];
+        const int rank = ex - before;
+        const int top = s_top[i];
+        const int np = P.free_stack[top - 1 - rank];
+        P.free_stack[top - 1 - rank] = -1;
+        P.rel[s_relbase[i] + rank] = pg;
+        P.block_tables[(size_t)s_r[i] * P.max_pages + j] = np;
+        if (np >= 0 && np < P.num_pages) P.refcount[np] = 1;
+        atomicMin(&P.info[i].first_repl, j);
+      }
+      carry += total;
     }
   }
   __threadfence();
   __syncthreads();
-  if (lane == 0) {
-    for (int k = 0; k < nrel; ++k) {
+
+  // ---- E: release the replaced references (after every pop); pages reaching zero go back
+  if (tid == 0) {
+    int top = s_top_end;
+    for (int k = 0; k < s_nrel; ++k) {
       const int pg = P.rel[k];
       const int rc = P.refcount[pg] - 1;
       P.refcount[pg] = rc;
@@ -248,13 +352,24 @@ __global__ __launch_bounds__(64) void decide_alloc_kernel(CParams P) {
   }
 }
 
+// minimum over the wave on the DPP path (lanes outside a broadcast's row mask see all-ones,
+// the identity of the minimum)
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ unsigned long long dpp_min_step(unsigned long long v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)v, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xf, false);
+  const unsigned long long t = ((unsigned long long)hi << 32) | lo;
+  return t < v ? t : v;
+}
+
 __device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long t = __shfl_xor(v, o, GP_WAVE);
-    v = t < v ? t : v;
-  }
-  return v;
+  v = dpp_min_step<0xb1>(v);
+  v = dpp_min_step<0x4e>(v);
+  v = dpp_min_step<0x141>(v);
+  v = dpp_min_step<0x140>(v);
+  v = dpp_min_step<0x142, 0xa>(v);
+  v = dpp_min_step<0x143, 0xc>(v);
+  return gp::readlane63_u64(v);
 }
 
 // Selection (Eq. 9-10) in three short launches over chunks of SEL_T pages (one page per
@@ -449,11 +564,13 @@ __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
 
 // Destination slot j of a compacted head takes source slot j + #{k : ev[k] - k <= j} (ev the
 // ascending evicted candidates): the j-th kept candidate, then the recent tokens. A workgroup
-// owns a chunk of destination pages and walks it left to right in windows: it stages the source
-// pages of the window (plus the next page) in LDS with coalesced 16-byte loads, tabulates the
-// source slot of every destination slot, then writes the window's destination pages from LDS.
-// Inside a chunk the extra page is not yet rewritten when it is read; the first page of the next
-// chunk, which another workgroup rewrites, comes from the snapshot.
+// owns a chunk of destination pages and walks it left to right in windows. Per window it
+// tabulates the source slot of every destination slot, reads the key rows it will write into
+// registers (rows are contiguous, 16 bytes per lane), stages the source value pages (token-
+// contiguous inside a page, so a gather needs them whole) in LDS, and only then writes the
+// window's destination pages. Inside a chunk the page after a window is not yet rewritten when
+// it is read; the first page of the next chunk, which another workgroup rewrites, comes from the
+// snapshot.
 __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   const int c = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
   const Info inf = P.info[i];
@@ -465,7 +582,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   if (dp_lo >= dp_hi) return;
   __shared__ int s_thr[MAX_EVICT];
   __shared__ int s_src[MAX_WINDOW_SLOTS];
-  extern __shared__ __align__(16) uint8_t s_kv[];  // key pages, then value pages of the window
+  extern __shared__ __align__(16) uint8_t s_v[];  // value pages of the window
   const int E = inf.E;
   if (threadIdx.x < MAX_EVICT)
     s_thr[threadIdx.x] = threadIdx.x < E
@@ -476,28 +593,13 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   const size_t pb = page_bytes(P);
   const int lqpp = P.log_qpp, qpp = 1 << lqpp;  // 16-byte pieces per page
   const int lkq = P.log_kq, lvq = P.log_vq;
+  const int krow = D * es;
   const int per = 16 / es;                      // elements per 16-byte piece
   for (int w0 = dp_lo; w0 < dp_hi; w0 += W) {
     const int w1 = min(w0 + W, dp_hi);          // destination pages [w0, w1)
     const int nsrc = w1 - w0 + 1;               // source pages [w0, w1]
-    uint8_t* s_k = s_kv;
-    uint8_t* s_v = s_kv + (size_t)nsrc * pb;
-    __syncthreads();  // the previous window's readers are done with LDS
-    for (int q = threadIdx.x; q < (nsrc << lqpp); q += CP_THREADS) {
-      const int sp = q >> lqpp, qq = q & (qpp - 1);
-      const int lp = w0 + sp;
-      u32x4_t kv = u32x4_t{0u, 0u, 0u, 0u}, vv = kv;
-      if (lp < inf.P) {
-        const bool snap = from_snapshot(P, lp, dp0, inf.n_dest);
-        const uint8_t* ks = snap ? snap_ptr(P, i, h, lp / L, 0) : P.k + pool_off(P, obt[lp], h);
-        const uint8_t* vs = snap ? snap_ptr(P, i, h, lp / L, 1) : P.v + pool_off(P, obt[lp], h);
-        kv = reinterpret_cast<const u32x4_t*>(ks)[qq];
-        vv = reinterpret_cast<const u32x4_t*>(vs)[qq];
-      }
-      reinterpret_cast<u32x4_t*>(s_k)[q] = kv;
-      reinterpret_cast<u32x4_t*>(s_v)[q] = vv;
-    }
     const int nslots = (w1 - w0) << lb;
+    __syncthreads();  // s_thr is set; the previous window is done with LDS
     for (int q = threadIdx.x; q < nslots; q += CP_THREADS) {
       const int j = (w0 << lb) + q;
       int cnt = 0;
@@ -506,22 +608,48 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
       s_src[q] = q + cnt;  // source slot relative to the window
     }
     __syncthreads();
-    // keys: 16-byte pieces of destination rows
-    const int krow = D * es;
-    for (int q = threadIdx.x; q < (nslots << lkq); q += CP_THREADS) {
-      const int slot = q >> lkq, piece = q & ((1 << lkq) - 1);
-      const int rs = s_src[slot];
-      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(s_k + (size_t)(rs >> lb) * pb +
-                                                            (size_t)(rs & (b - 1)) * krow + 16 * piece);
-      const int dp = w0 + (slot >> lb);
-      reinterpret_cast<u32x4_t*>(P.k + pool_off(P, nbt[dp], h) + (size_t)(slot & (b - 1)) * krow)[piece] = val;
+    // keys: the 16-byte pieces of the destination rows this thread writes, read first; value
+    // pages staged in LDS alongside, so both wait on one round trip
+    const int nk = nslots << lkq;
+    u32x4_t kreg[K_PIECES];
+#pragma unroll
+    for (int it = 0; it < K_PIECES; ++it) {
+      const int q = threadIdx.x + it * CP_THREADS;
+      if (q < nk) {
+        const int slot = q >> lkq, piece = q & ((1 << lkq) - 1);
+        const int src = (w0 << lb) + s_src[slot];
+        const int lp = src >> lb;
+        const uint8_t* ks = from_snapshot(P, lp, dp0, inf.n_dest) ? snap_ptr(P, i, h, lp / L, 0)
+                                                                   : P.k + pool_off(P, obt[lp], h);
+        kreg[it] = reinterpret_cast<const u32x4_t*>(ks + (size_t)(src & (b - 1)) * krow)[piece];
+      }
     }
-    // values: 16-byte pieces of destination value rows (token-contiguous inside a page)
-    const int lrow_pieces = lvq;  // pieces per value row
-    const int npieces = (w1 - w0) * D << lrow_pieces;
+    for (int q = threadIdx.x; q < (nsrc << lqpp); q += CP_THREADS) {
+      const int sp = q >> lqpp, qq = q & (qpp - 1);
+      const int lp = w0 + sp;
+      u32x4_t vv = u32x4_t{0u, 0u, 0u, 0u};
+      if (lp < inf.P) {
+        const uint8_t* vs = from_snapshot(P, lp, dp0, inf.n_dest) ? snap_ptr(P, i, h, lp / L, 1)
+                                                                   : P.v + pool_off(P, obt[lp], h);
+        vv = reinterpret_cast<const u32x4_t*>(vs)[qq];
+      }
+      reinterpret_cast<u32x4_t*>(s_v)[q] = vv;
+    }
+    __syncthreads();  // every read of this window's sources precedes any write
+#pragma unroll
+    for (int it = 0; it < K_PIECES; ++it) {
+      const int q = threadIdx.x + it * CP_THREADS;
+      if (q < nk) {
+        const int slot = q >> lkq, piece = q & ((1 << lkq) - 1);
+        const int dp = w0 + (slot >> lb);
+        reinterpret_cast<u32x4_t*>(P.k + pool_off(P, nbt[dp], h) + (size_t)(slot & (b - 1)) * krow)[piece] = kreg[it];
+      }
+    }
+    // values: 16-byte pieces of destination value rows gathered from LDS
+    const int npieces = (w1 - w0) * D << lvq;
     for (int q = threadIdx.x; q < npieces; q += CP_THREADS) {
-      const int piece = q & ((1 << lrow_pieces) - 1);
-      const int rowi = q >> lrow_pieces;  // (page, dd)
+      const int piece = q & ((1 << lvq) - 1);
+      const int rowi = q >> lvq;  // (page, dd)
       const int dpl = rowi / D, dd = rowi - dpl * D;
       uint32_t wv[4] = {0u, 0u, 0u, 0u};
       for (int e = 0; e < per; ++e) {
@@ -540,11 +668,14 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   }
 }
 
-// LDS window: the K and V source pages of W destination pages plus one
+// Window of W destination pages: LDS holds the W + 1 source value pages, and the W * b key rows
+// must fit K_PIECES 16-byte pieces per thread.
 int window_pages_for(int page_size, int D, int es) {
   const long pv = (long)page_size * D * es;
-  const int W = (int)(CP_LDS_BYTES / (2 * pv)) - 1;
-  return std::max(1, std::min(8, W));
+  int W = (int)(CP_LDS_BYTES / pv) - 1;
+  W = std::max(1, std::min(8, W));
+  while (W > 1 && (long)W * page_size * D * es > (long)K_PIECES * CP_THREADS * 16) --W;
+  return W;
 }
 
 int ilog2(int v) {
@@ -584,6 +715,7 @@ extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const fl
                                   size_t workspace_bytes, void* stream) {
   if (R < 0 || B < 0 || C_max <= 0 || !kv || max_pages <= 0 || k_loc < 0) return GP_ERR_INVALID;
   if (R == 0) return GP_OK;
+  if (R > DA_MAX_R) return GP_ERR_UNSUPPORTED;
   if (!req_idx || !a_short || !a_long || !ws_counts || !n_cand || !block_tables || !n_pages ||
       !context_lens || !refcount || !free_stack || !free_top || !decision || !kept_idx || !kv->k ||
       !kv->v)
@@ -598,8 +730,10 @@ extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const fl
   if (b != 16 && b != 32) return GP_ERR_UNSUPPORTED;
   {
     const int es = kv->dtype == GP_F32 ? 4 : 2;
-    const size_t lds = (size_t)2 * (window_pages_for(b, D, es) + 1) * b * D * es;
+    const int W = window_pages_for(b, D, es);
+    const size_t lds = (size_t)(W + 1) * b * D * es;
     if (lds + sizeof(int) * (MAX_EVICT + MAX_WINDOW_SLOTS) > 64 * 1024) return GP_ERR_UNSUPPORTED;
+    if ((long)W * b * D * es > (long)K_PIECES * CP_THREADS * 16) return GP_ERR_UNSUPPORTED;
   }
   if (C_max % 4 || C_max > MAX_CAND) return GP_ERR_UNSUPPORTED;
   const size_t need = gp_compact_or_grow_workspace_size(R, H_kv, max_pages, b, C_max);
@@ -659,7 +793,7 @@ extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const fl
   P.snap = ws + off;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(decide_alloc_kernel, dim3(1), dim3(64), 0, s, P);
+  hipLaunchKernelGGL(decide_alloc_kernel, dim3(1), dim3(DA_THREADS), 0, s, P);
   GP_CHECK_LAUNCH();
   {
     const int nch = (C_max + SEL_T * b - 1) / (SEL_T * b);
@@ -675,7 +809,7 @@ extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const fl
   }
   hipLaunchKernelGGL(snapshot_kernel, dim3(P.max_chunks, H_kv, R), dim3(CP_THREADS), 0, s, P);
   GP_CHECK_LAUNCH();
-  const size_t lds = (size_t)2 * (P.window_pages + 1) * b * D * P.es;
+  const size_t lds = (size_t)(P.window_pages + 1) * b * D * P.es;
   hipLaunchKernelGGL(compact_kernel, dim3(P.max_chunks, H_kv, R), dim3(CP_THREADS), lds, s, P);
   GP_CHECK_LAUNCH();
   return GP_OK;

@@ -16,6 +16,8 @@
 //                 fixed-point sum then certifies (and corrects if rounding picked a neighbour).
 #include "common.h"
 
+#include <cmath>
+
 namespace {
 
 constexpr int LG_WAVES = 4;
@@ -45,6 +47,7 @@ struct ScoreParams {
   int q_bf16;
   float scale_log2;
   double rope_theta;
+  double inv_freq[64];  // rope_theta^(-2j/D), j < D/2 (float64, from the host)
   uint32_t p_fixed[5];  // p in units of 2^-149, little-endian 32-bit digits (rounded up)
 };
 
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ScoreParams P) {
       const int j = d % half;
       double out = cv[c];
       if (P.rope_theta > 0.0) {
-        const double ang = pos * pow(P.rope_theta, -2.0 * j / D);
+        const double ang = pos * P.inv_freq[j];
         double sn, cs;
         sincos(ang, &sn, &cs);
         out = (d < half) ? cv[c] * cs - part[c] * sn : part[c] * sn + cv[c] * cs;
@@ -636,6 +639,8 @@ extern "C" int gp_score_and_working_set(const void* q, int q_dtype, int B, int H
   P.q_bf16 = q_dtype == GP_BF16;
   P.scale_log2 = sm_scale * GP_LOG2E;
   P.rope_theta = rope_theta;
+  for (int j = 0; j < 64; ++j)
+    P.inv_freq[j] = (rope_theta > 0.f && j < D / 2) ? std::pow((double)rope_theta, -2.0 * j / D) : 0.0;
   p_to_fixed(p, P.p_fixed);
   float* ws = static_cast<float*>(workspace);
   P.qt = ws;
