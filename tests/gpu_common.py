@@ -15,13 +15,13 @@ def say(*a):
     sys.stdout.flush()
 
 
-def workload_on_gpu(cfg, scale):
+def workload_on_gpu(cfg, scale, page_size=16):
     """Small workloads are drawn on the CPU and copied (identical values on both sides);
     full-size ones are drawn directly on the GPU."""
-    say(f"[workload] config={cfg} scale={scale}")
+    say(f"[workload] config={cfg} scale={scale} page_size={page_size}")
     if scale == "small":
-        return make_workload(cfg, "small", device="cpu").to(DEV)
-    return make_workload(cfg, "full", device=DEV)
+        return make_workload(cfg, "small", device="cpu", page_size=page_size).to(DEV)
+    return make_workload(cfg, "full", device=DEV, page_size=page_size)
 
 
 def maxabs(a, b):

@@ -124,12 +124,13 @@ def compare_state(wl, st, dec, kept, dec_ref, kept_ref, nc):
         assert np.array_equal(after[name], st[name]), name
 
 
-@pytest.mark.parametrize("cfg", ["1", "2", "3a", "3b", "4"])
-def test_score_small(cfg):
-    wl = workload_on_gpu(cfg, "small")
+@pytest.mark.parametrize("cfg,page_size", [("1", 16), ("2", 16), ("3a", 16), ("3b", 16), ("4", 16),
+                                            ("1", 32), ("3a", 32), ("4", 32)])
+def test_score_small(cfg, page_size):
+    wl = workload_on_gpu(cfg, "small", page_size)
     build_state(wl)
     a_s, a_l, ws, nc = run_score(wl)
-    check_score(wl, a_s, a_l, ws, nc, label=f"small {cfg}")
+    check_score(wl, a_s, a_l, ws, nc, label=f"small {cfg} b={page_size}")
 
 
 @pytest.mark.parametrize("cfg", ["2", "3a", "3b", "4"])
@@ -141,11 +142,12 @@ def test_score_full_size(cfg):
     check_score(wl, a_s, a_l, ws, nc, reqs_checked=pick, label=f"full {cfg}")
 
 
-@pytest.mark.parametrize("cfg,policy_mode", [("1", "auto"), ("2", "auto"), ("3a", "auto"),
-                                             ("3b", "auto"), ("4", "config"), ("4", "auto"),
-                                             ("1", "inverse"), ("3a", "compress")])
-def test_compact_or_grow_small(cfg, policy_mode):
-    wl = workload_on_gpu(cfg, "small")
+@pytest.mark.parametrize("cfg,policy_mode,page_size", [
+    ("1", "auto", 16), ("2", "auto", 16), ("3a", "auto", 16), ("3b", "auto", 16),
+    ("4", "config", 16), ("4", "auto", 16), ("1", "inverse", 16), ("3a", "compress", 16),
+    ("1", "compress", 32), ("3a", "compress", 32), ("3b", "compress", 32), ("4", "config", 32)])
+def test_compact_or_grow_small(cfg, policy_mode, page_size):
+    wl = workload_on_gpu(cfg, "small", page_size)
     build_state(wl)
     a_s, a_l, ws, nc = run_score(wl)
     policies = wl.req_policy if policy_mode == "config" else None
@@ -154,7 +156,7 @@ def test_compact_or_grow_small(cfg, policy_mode):
     st = host_state(wl)
     dec, kept = run_compact(wl, a_s, a_l, ws, nc, policy=policy, policies=policies)
     dec_ref, kept_ref = oracle_compact(wl, st, a_s, a_l, ws, nc, policy=policy, policies=policies)
-    say(f"[compact small {cfg} {policy_mode}] decisions={npy(dec).tolist()}")
+    say(f"[compact small {cfg} {policy_mode} b={page_size}] decisions={npy(dec).tolist()}")
     compare_state(wl, st, dec, kept, dec_ref, kept_ref, nc)
 
 

@@ -28,9 +28,11 @@ def _mixed_np(sub_or_wl):
                 k_scale=npy(g("k_scale")), v_scale=npy(g("v_scale")))
 
 
-@pytest.mark.parametrize("cfg", ["1", "2", "3a", "3b", "4", "5"])
-def test_decode_small_elementwise(cfg):
-    wl = workload_on_gpu(cfg, "small")
+@pytest.mark.parametrize("cfg,page_size", [("1", 16), ("2", 16), ("3a", 16), ("3b", 16), ("4", 16),
+                                            ("5", 16), ("1", 32), ("3a", 32), ("4", 32), ("5", 32),
+                                            ("2", 64)])
+def test_decode_small_elementwise(cfg, page_size):
+    wl = workload_on_gpu(cfg, "small", page_size)
     out, lse = _run_gpu(wl)
     extra = _mixed_np(wl) if wl.mixed else {}
     ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
@@ -38,7 +40,7 @@ def test_decode_small_elementwise(cfg):
                                           wl.page_size, wl.sm_scale, **extra)
     eo, nan_o = maxabs(f64(out), ref_o)
     el, nan_l = maxabs(lse.cpu().numpy(), ref_l)
-    say(f"[decode small {cfg}] max|out-ref|={eo:.3e} max|lse-ref|={el:.3e}")
+    say(f"[decode small {cfg} b={page_size}] max|out-ref|={eo:.3e} max|lse-ref|={el:.3e}")
     assert not nan_o and not nan_l
     assert eo <= TOL[wl.dtype] and el <= TOL[wl.dtype]
 
