@@ -12,13 +12,15 @@
 //      smallest of the unique keys (s, ~index) outside each page's k_loc quota, which realises
 //      the (s desc, index asc) order exactly: chunk-local E smallest, their merge per request
 //      and KV head, then kept_idx written in parallel.
-//   3. snapshot: compaction is a left shift by at most E slots, so a chunk of destination pages
-//      only reads its own pages plus the first page of the next chunk; that page is saved first.
-//   4. compact (per chunk x KV head x request), window by window: tabulate the source slot of
+//   3. chunk list + snapshot: the (request, head, chunk) items to rewrite are listed on the device;
+//      compaction is a left shift by at most E slots, so a chunk of destination pages only reads
+//      its own pages plus the first page of the next chunk, which is saved first.
+//   4. compact (resident workgroups striding over the list), window by window: tabulate the source slot of
 //      every destination slot, read all sources (key rows into registers, value pages into
 //      LDS), barrier, write the window's destination pages.
 #include "common.h"
 
+#include <atomic>
 #include <climits>
 
 namespace {
@@ -35,6 +37,7 @@ constexpr int MAX_WINDOW_SLOTS = 8 * 32;  // LDS window pages (<= 8) x page size
 constexpr int CP_THREADS = 256;
 constexpr int CP_LDS_BYTES = 40 * 1024;  // source value pages of one window
 constexpr int K_PIECES = 8;               // key pieces per thread and window
+constexpr int V_PIECES = 12;              // staged value pieces per thread and window
 
 struct Info {
   int r, mode, P, ctx_old, n, K_t, R_n, E, ctx_new, n_dest, first_repl, pad;
@@ -63,6 +66,8 @@ struct CParams {
   int32_t* ev;        // [R, H_kv, MAX_EVICT]
   int32_t* dp0;       // [R, H_kv]
   unsigned long long* cand;  // [R, H_kv, SEL_MAX_CHUNKS, MAX_EVICT] chunk survivors
+  int2* items;               // [R * H_kv * max_chunks] (request * H_kv + head, chunk) to compact
+  int32_t* n_items;          // [1]
   uint8_t* snap;      // [R, H_kv, max_chunks, 2, page bytes]
   int R, B, H_kv, D, page_size, num_pages, max_pages, C_max, k_loc, policy, es;
   int chunk_pages, max_chunks, window_pages;
@@ -339,17 +344,37 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
   __threadfence();
   __syncthreads();
 
-  // ---- E: release the replaced references (after every pop); pages reaching zero go back
-  if (tid == 0) {
-    int top = s_top_end;
-    for (int k = 0; k < s_nrel; ++k) {
-      const int pg = P.rel[k];
-      const int rc = P.refcount[pg] - 1;
-      P.refcount[pg] = rc;
-      if (rc == 0 && top < P.num_pages) P.free_stack[top++] = pg;
+  // ---- E: release the replaced references after every pop, in release order, in chunks of
+  // DA_THREADS: each release decrements its page; a page that reaches zero had all its remaining
+  // references released by now, the last of them in this chunk, and is pushed at the position of
+  // that last release among this chunk's zero-reaching releases
+  __shared__ int s_rel[DA_THREADS], s_last[DA_THREADS];
+  int top = s_top_end;
+  const int nrel = s_nrel;
+  for (int k0 = 0; k0 < nrel; k0 += DA_THREADS) {
+    const int k = k0 + tid, cnt = min(DA_THREADS, nrel - k0);
+    int pg = -1;
+    if (tid < cnt) pg = P.rel[k];
+    s_rel[tid] = pg;
+    s_last[tid] = 0;
+    __syncthreads();
+    if (tid < cnt && pg >= 0 && pg < P.num_pages) {
+      const int old = atomicSub(&P.refcount[pg], 1);
+      if (old == 1) {
+        int last = tid;
+        for (int q = tid + 1; q < cnt; ++q)
+          if (s_rel[q] == pg) last = q;
+        s_last[last] = 1;
+      }
     }
-    *P.free_top = top;
+    __syncthreads();
+    int total;
+    const int pos = block_excl_scan(s_last[tid], s_w, &total);
+    if (s_last[tid] && top + pos < P.num_pages) P.free_stack[top + pos] = s_rel[tid];
+    top = min(P.num_pages, top + total);
+    __syncthreads();
   }
+  if (tid == 0) *P.free_top = top;
 }
 
 // minimum over the wave on the DPP path (lanes outside a broadcast's row mask see all-ones,
@@ -543,22 +568,54 @@ __device__ __forceinline__ bool from_snapshot(const CParams& P, int lp, int dp0,
   return (lp % P.chunk_pages) == 0 && lp > dp0 && lp < n_dest;
 }
 
+// List of the (request, head, chunk) items that compaction rewrites: for a compacting head the
+// chunks from the one holding its first changed page to the one holding its last destination page.
+__global__ __launch_bounds__(DA_THREADS) void chunk_list_kernel(CParams P) {
+  __shared__ int s_w[DA_THREADS / GP_WAVE];
+  const int L = P.chunk_pages, n = P.R * P.H_kv;
+  int carry = 0;
+  for (int base = 0; base < n; base += DA_THREADS) {
+    const int ih = base + threadIdx.x;
+    int c0 = 0, cnt = 0;
+    if (ih < n) {
+      const Info inf = P.info[ih / P.H_kv];
+      if (inf.mode == MODE_COMPACT) {
+        const int dp0 = P.dp0[ih];
+        if (dp0 < inf.n_dest) {
+          c0 = dp0 / L;
+          cnt = (inf.n_dest + L - 1) / L - c0;
+        }
+      }
+    }
+    int total;
+    const int off = carry + block_excl_scan(cnt, s_w, &total);
+    for (int k = 0; k < cnt; ++k) P.items[off + k] = make_int2(ih, c0 + k);
+    carry += total;
+  }
+  if (threadIdx.x == 0) *P.n_items = carry;
+}
+
+// The first page of the next chunk, saved before any chunk is rewritten (it is that chunk's to
+// rewrite, and this chunk's last source page). Workgroups stride over the work list.
 __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
-  const int c = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
-  const Info inf = P.info[i];
-  if (inf.mode != MODE_COMPACT || c == 0) return;
-  const int lp = c * P.chunk_pages;
-  const int dp0 = P.dp0[(size_t)i * P.H_kv + h];
-  if (!from_snapshot(P, lp, dp0, inf.n_dest)) return;
-  const int pg = P.old_bt[(size_t)i * P.max_pages + lp];
-  const size_t nb = page_bytes(P);
-  const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(P.k + pool_off(P, pg, h));
-  const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(P.v + pool_off(P, pg, h));
-  u32x4_t* kd = reinterpret_cast<u32x4_t*>(snap_ptr(P, i, h, c, 0));
-  u32x4_t* vd = reinterpret_cast<u32x4_t*>(snap_ptr(P, i, h, c, 1));
-  for (size_t q = threadIdx.x; q < nb / 16; q += CP_THREADS) {
-    kd[q] = ks[q];
-    vd[q] = vs[q];
+  const int n_items = *P.n_items;
+  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int2 item = P.items[it];
+    const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y + 1;
+    const Info inf = P.info[i];
+    const int lp = c * P.chunk_pages;
+    const int dp0 = P.dp0[item.x];
+    if (!from_snapshot(P, lp, dp0, inf.n_dest)) continue;  // uniform over the workgroup
+    const int pg = P.old_bt[(size_t)i * P.max_pages + lp];
+    const size_t nb = page_bytes(P);
+    const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(P.k + pool_off(P, pg, h));
+    const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(P.v + pool_off(P, pg, h));
+    u32x4_t* kd = reinterpret_cast<u32x4_t*>(snap_ptr(P, i, h, c, 0));
+    u32x4_t* vd = reinterpret_cast<u32x4_t*>(snap_ptr(P, i, h, c, 1));
+    for (size_t q = threadIdx.x; q < nb / 16; q += CP_THREADS) {
+      kd[q] = ks[q];
+      vd[q] = vs[q];
+    }
   }
 }
 
@@ -572,34 +629,47 @@ __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
 // it is read; the first page of the next chunk, which another workgroup rewrites, comes from the
 // snapshot.
 __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
-  const int c = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
+  const int n_items = *P.n_items;
+  for (int item_k = blockIdx.x; item_k < n_items; item_k += gridDim.x) {
+  __syncthreads();  // the previous item is done with the tables and LDS
+  const int2 item = P.items[item_k];
+  const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y;
   const Info inf = P.info[i];
-  if (inf.mode != MODE_COMPACT) return;
   const int L = P.chunk_pages, W = P.window_pages, D = P.D, es = P.es;
   const int lb = P.log_b, b = 1 << lb;
-  const int dp0 = P.dp0[(size_t)i * P.H_kv + h];
+  const int dp0 = P.dp0[item.x];
   const int dp_lo = max(dp0, c * L), dp_hi = min((c + 1) * L, inf.n_dest);
-  if (dp_lo >= dp_hi) return;
   __shared__ int s_thr[MAX_EVICT];
   __shared__ int s_src[MAX_WINDOW_SLOTS];
+  // source pages dp_lo .. dp_hi: byte offset of (page, head) in the pool, or -1 for the snapshot,
+  // or -2 past the old pages; destination pages dp_lo .. dp_hi - 1: byte offset in the pool
+  __shared__ long long s_soff[CHUNK_PAGES + 1], s_doff[CHUNK_PAGES];
   extern __shared__ __align__(16) uint8_t s_v[];  // value pages of the window
   const int E = inf.E;
+  const size_t pb = page_bytes(P);
   if (threadIdx.x < MAX_EVICT)
     s_thr[threadIdx.x] = threadIdx.x < E
                              ? P.ev[((size_t)i * P.H_kv + h) * MAX_EVICT + threadIdx.x] - (int)threadIdx.x
                              : INT_MAX;
-  const int32_t* obt = P.old_bt + (size_t)i * P.max_pages;
-  const int32_t* nbt = P.block_tables + (size_t)inf.r * P.max_pages;
-  const size_t pb = page_bytes(P);
+  if (threadIdx.x <= dp_hi - dp_lo) {
+    const int lp = dp_lo + threadIdx.x;
+    long long so = -2;
+    if (lp < inf.P)
+      so = from_snapshot(P, lp, dp0, inf.n_dest) ? -1
+                                                 : (long long)pool_off(P, P.old_bt[(size_t)i * P.max_pages + lp], h);
+    s_soff[threadIdx.x] = so;
+    if (lp < dp_hi) s_doff[threadIdx.x] = (long long)pool_off(P, P.block_tables[(size_t)inf.r * P.max_pages + lp], h);
+  }
   const int lqpp = P.log_qpp, qpp = 1 << lqpp;  // 16-byte pieces per page
   const int lkq = P.log_kq, lvq = P.log_vq;
   const int krow = D * es;
   const int per = 16 / es;                      // elements per 16-byte piece
+  const uint8_t* snapk = snap_ptr(P, i, h, 0, 0);
   for (int w0 = dp_lo; w0 < dp_hi; w0 += W) {
     const int w1 = min(w0 + W, dp_hi);          // destination pages [w0, w1)
     const int nsrc = w1 - w0 + 1;               // source pages [w0, w1]
     const int nslots = (w1 - w0) << lb;
-    __syncthreads();  // s_thr is set; the previous window is done with LDS
+    __syncthreads();  // tables are set; the previous window is done with LDS
     for (int q = threadIdx.x; q < nslots; q += CP_THREADS) {
       const int j = (w0 << lb) + q;
       int cnt = 0;
@@ -608,8 +678,24 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
       s_src[q] = q + cnt;  // source slot relative to the window
     }
     __syncthreads();
-    // keys: the 16-byte pieces of the destination rows this thread writes, read first; value
-    // pages staged in LDS alongside, so both wait on one round trip
+    // issue every read of the window before using any: value pieces, then key pieces
+    auto src_page = [&](int lp, int which) -> const uint8_t* {
+      const long long so = s_soff[lp - dp_lo];
+      if (so == -1) return snapk + (((size_t)(lp / L) * 2 + which) * pb);
+      return (which ? P.v : P.k) + so;
+    };
+    const int nv = nsrc << lqpp;
+    u32x4_t vreg[V_PIECES];
+#pragma unroll
+    for (int it = 0; it < V_PIECES; ++it) {
+      const int q = threadIdx.x + it * CP_THREADS;
+      vreg[it] = u32x4_t{0u, 0u, 0u, 0u};
+      if (q < nv) {
+        const int lp = w0 + (q >> lqpp);
+        if (s_soff[lp - dp_lo] != -2)
+          vreg[it] = reinterpret_cast<const u32x4_t*>(src_page(lp, 1))[q & (qpp - 1)];
+      }
+    }
     const int nk = nslots << lkq;
     u32x4_t kreg[K_PIECES];
 #pragma unroll
@@ -618,22 +704,13 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
       if (q < nk) {
         const int slot = q >> lkq, piece = q & ((1 << lkq) - 1);
         const int src = (w0 << lb) + s_src[slot];
-        const int lp = src >> lb;
-        const uint8_t* ks = from_snapshot(P, lp, dp0, inf.n_dest) ? snap_ptr(P, i, h, lp / L, 0)
-                                                                   : P.k + pool_off(P, obt[lp], h);
-        kreg[it] = reinterpret_cast<const u32x4_t*>(ks + (size_t)(src & (b - 1)) * krow)[piece];
+        kreg[it] = reinterpret_cast<const u32x4_t*>(src_page(src >> lb, 0) + (size_t)(src & (b - 1)) * krow)[piece];
       }
     }
-    for (int q = threadIdx.x; q < (nsrc << lqpp); q += CP_THREADS) {
-      const int sp = q >> lqpp, qq = q & (qpp - 1);
-      const int lp = w0 + sp;
-      u32x4_t vv = u32x4_t{0u, 0u, 0u, 0u};
-      if (lp < inf.P) {
-        const uint8_t* vs = from_snapshot(P, lp, dp0, inf.n_dest) ? snap_ptr(P, i, h, lp / L, 1)
-                                                                   : P.v + pool_off(P, obt[lp], h);
-        vv = reinterpret_cast<const u32x4_t*>(vs)[qq];
-      }
-      reinterpret_cast<u32x4_t*>(s_v)[q] = vv;
+#pragma unroll
+    for (int it = 0; it < V_PIECES; ++it) {
+      const int q = threadIdx.x + it * CP_THREADS;
+      if (q < nv) reinterpret_cast<u32x4_t*>(s_v)[q] = vreg[it];
     }
     __syncthreads();  // every read of this window's sources precedes any write
 #pragma unroll
@@ -642,7 +719,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
       if (q < nk) {
         const int slot = q >> lkq, piece = q & ((1 << lkq) - 1);
         const int dp = w0 + (slot >> lb);
-        reinterpret_cast<u32x4_t*>(P.k + pool_off(P, nbt[dp], h) + (size_t)(slot & (b - 1)) * krow)[piece] = kreg[it];
+        reinterpret_cast<u32x4_t*>(P.k + s_doff[dp - dp_lo] + (size_t)(slot & (b - 1)) * krow)[piece] = kreg[it];
       }
     }
     // values: 16-byte pieces of destination value rows gathered from LDS
@@ -662,9 +739,10 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
           wv[e] = *reinterpret_cast<const uint32_t*>(src);
         }
       }
-      reinterpret_cast<u32x4_t*>(P.v + pool_off(P, nbt[w0 + dpl], h) + (size_t)dd * b * es)[piece] =
+      reinterpret_cast<u32x4_t*>(P.v + s_doff[w0 + dpl - dp_lo] + (size_t)dd * b * es)[piece] =
           u32x4_t{wv[0], wv[1], wv[2], wv[3]};
     }
+  }
   }
 }
 
@@ -674,8 +752,23 @@ int window_pages_for(int page_size, int D, int es) {
   const long pv = (long)page_size * D * es;
   int W = (int)(CP_LDS_BYTES / pv) - 1;
   W = std::max(1, std::min(8, W));
-  while (W > 1 && (long)W * page_size * D * es > (long)K_PIECES * CP_THREADS * 16) --W;
+  while (W > 1 && ((long)W * page_size * D * es > (long)K_PIECES * CP_THREADS * 16 ||
+                   (long)(W + 1) * page_size * D * es > (long)V_PIECES * CP_THREADS * 16))
+    --W;
   return W;
+}
+
+// compute units of the current device (memoised per device; host-side property only)
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const int v = cache[dev & 63].load();
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  cache[dev & 63].store(cus);
+  return cus;
 }
 
 int ilog2(int v) {
@@ -701,6 +794,7 @@ extern "C" size_t gp_compact_or_grow_workspace_size(int R, int H_kv, int max_pag
   bytes += (size_t)R * H_kv * 4;
   bytes = (bytes + 255) & ~(size_t)255;
   bytes += (size_t)R * H_kv * SEL_MAX_CHUNKS * MAX_EVICT * 8;
+  bytes += (size_t)R * H_kv * max_chunks * sizeof(int2) + 256;
   bytes += (size_t)R * H_kv * max_chunks * 2 * (size_t)page_size * D * es;
   return bytes;
 }
@@ -734,6 +828,7 @@ extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const fl
     const size_t lds = (size_t)(W + 1) * b * D * es;
     if (lds + sizeof(int) * (MAX_EVICT + MAX_WINDOW_SLOTS) > 64 * 1024) return GP_ERR_UNSUPPORTED;
     if ((long)W * b * D * es > (long)K_PIECES * CP_THREADS * 16) return GP_ERR_UNSUPPORTED;
+    if ((long)(W + 1) * b * D * es > (long)V_PIECES * CP_THREADS * 16) return GP_ERR_UNSUPPORTED;
   }
   if (C_max % 4 || C_max > MAX_CAND) return GP_ERR_UNSUPPORTED;
   const size_t need = gp_compact_or_grow_workspace_size(R, H_kv, max_pages, b, C_max);
@@ -790,6 +885,10 @@ extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const fl
   off = (off + 255) & ~(size_t)255;
   P.cand = reinterpret_cast<unsigned long long*>(ws + off);
   off += (size_t)R * H_kv * SEL_MAX_CHUNKS * MAX_EVICT * 8;
+  P.items = reinterpret_cast<int2*>(ws + off);
+  off += (size_t)R * H_kv * P.max_chunks * sizeof(int2);
+  P.n_items = reinterpret_cast<int32_t*>(ws + off);
+  off += 256;
   P.snap = ws + off;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -807,10 +906,15 @@ extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const fl
     else hipLaunchKernelGGL(select_write_kernel<32>, g, dim3(SEL_T), 0, s, P);
     GP_CHECK_LAUNCH();
   }
-  hipLaunchKernelGGL(snapshot_kernel, dim3(P.max_chunks, H_kv, R), dim3(CP_THREADS), 0, s, P);
+  hipLaunchKernelGGL(chunk_list_kernel, dim3(1), dim3(DA_THREADS), 0, s, P);
+  GP_CHECK_LAUNCH();
+  const int cus = device_cus();
+  hipLaunchKernelGGL(snapshot_kernel, dim3(std::max(1, std::min(4 * cus, R * H_kv * P.max_chunks))),
+                     dim3(CP_THREADS), 0, s, P);
   GP_CHECK_LAUNCH();
   const size_t lds = (size_t)(P.window_pages + 1) * b * D * P.es;
-  hipLaunchKernelGGL(compact_kernel, dim3(P.max_chunks, H_kv, R), dim3(CP_THREADS), lds, s, P);
+  hipLaunchKernelGGL(compact_kernel, dim3(std::max(1, std::min(2 * cus, R * H_kv * P.max_chunks))),
+                     dim3(CP_THREADS), lds, s, P);
   GP_CHECK_LAUNCH();
   return GP_OK;
 }
