@@ -10,10 +10,18 @@ tables, lengths, page counts, refcounts, free stack) with one device copy, insid
 region; K/V pages are left as the previous step's compaction wrote them (still valid tokens, same
 amount of work).
 
+With --overlap 1 the step runs as GrowPage overlaps compaction with decoding: after
+the summary update, the boundary requests are decoded and then scored and compressed-or-grown on a
+second stream while the main stream decodes the other requests (their lengths masked to zero for
+it, so no page the boundary pass rewrites is read); the main stream waits for the second before
+the step ends. Every request still sees update -> decode -> boundary pass in that order. It is
+not the default: the decode sizes its grid to occupy every compute unit, so kernels on the second
+stream wait for it and the overlapped step is slower than the single-stream one.
+
 Prints one JSON line. `value` is the step's algorithmic HBM bytes divided by the step time;
-`roofline` is the decode call (its two kernels) against the 8 TB/s HBM peak, timed with HIP
-events on the stream the kernels are launched on; `cpu_baseline` is the float64 CPU oracle on
-a bounded sample of the same workload.
+`roofline` is the main decode call (its two kernels) against the 8 TB/s HBM peak, timed with HIP
+events on the stream it is launched on; `cpu_baseline` is the float64 CPU oracle on a bounded
+sample of the same workload.
 """
 import argparse
 import hashlib
@@ -50,6 +58,9 @@ def parse():
     ap.add_argument("--config", default="2", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's timed sample (0 disables the cpu_baseline leg)")
+    ap.add_argument("--overlap", type=int, default=0,
+                    help="1: the boundary requests' decode and boundary pass run on a second stream "
+                         "beside the decode of the other requests; 0: everything on one stream")
     ap.add_argument("--copy-probe-gib", type=float, default=1.0,
                     help="size of the plain device copy timed beside the path (HBM reference)")
     return ap.parse_args()
@@ -63,14 +74,17 @@ def file_sha(path):
 class Path:
     """Preallocated buffers and the per-step launch sequence of one workload."""
 
-    def __init__(self, wl, gp, torch):
+    def __init__(self, wl, gp, torch, overlap=False):
         self.wl, self.gp, self.torch = wl, gp, torch
         dev = wl.q.device
         i32 = torch.int32
-        # integer page state in one flat buffer so a step can restore it with one copy
+        self.R = wl.req_idx.numel()
+        self.overlap = bool(overlap) and self.R > 0
+        # integer page state in one flat buffer so a step can restore it with one copy; with
+        # overlap it also holds the lengths the main decode sees (boundary requests masked to 0)
         names = ("block_tables", "n_pages", "context_lens", "refcount", "free_stack", "free_top")
         sizes = [getattr(wl, n).numel() for n in names]
-        self.meta = torch.empty(sum(sizes), dtype=i32, device=dev)
+        self.meta = torch.empty(sum(sizes) + wl.B, dtype=i32, device=dev)
         off = 0
         for n, sz in zip(names, sizes):
             t = getattr(wl, n)
@@ -78,6 +92,10 @@ class Path:
             view.copy_(t)
             setattr(wl, n, view)
             off += sz
+        self.ctx_main = self.meta[off:off + wl.B]
+        self.ctx_main.copy_(wl.context_lens)
+        if self.R:
+            self.ctx_main.index_fill_(0, wl.req_idx.long(), 0)
         self.meta0 = self.meta.clone()
         self.cache = gp.KVCache.from_workload(wl)
         B, H_q, d = wl.q.shape
@@ -87,7 +105,6 @@ class Path:
         n = gp.gp_paged_decode_attn_workspace_size(B, H_q, H_kv, d, wl.page_size, wl.max_context)
         self.dws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
         self.fresh0 = torch.zeros(B, dtype=torch.uint8, device=dev)
-        self.R = wl.req_idx.numel()
         if self.R:
             req = wl.req_idx.cpu().tolist()
             ctx = wl.context_lens.cpu().tolist()
@@ -106,6 +123,19 @@ class Path:
             n = gp.gp_compact_or_grow_workspace_size(R, H_kv, wl.max_pages, b, C)
             self.cws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
             self.policies = torch.as_tensor(wl.req_policy, dtype=i32, device=dev)
+        if self.overlap:
+            R = self.R
+            self.stream_b = torch.cuda.Stream(device=dev)  # default priority
+            self.req_l = wl.req_idx.long()
+            self.q_b = torch.empty((R, H_q, d), dtype=wl.q.dtype, device=dev)
+            self.bt_b = torch.empty((R, wl.max_pages), dtype=i32, device=dev)
+            self.ctx_b = torch.empty((R,), dtype=i32, device=dev)
+            self.out_b = torch.empty((R, H_q, d), dtype=wl.q.dtype, device=dev)
+            self.lse_b = torch.empty((R, H_q), dtype=torch.float32, device=dev)
+            n = gp.gp_paged_decode_attn_workspace_size(R, H_q, H_kv, d, wl.page_size, wl.max_context)
+            self.dws_b = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+            self.ev_a = torch.cuda.Event()
+            self.ev_b = torch.cuda.Event()
 
     def build_state(self):
         """Summaries after the past queries (first one initialises the slot)."""
@@ -143,33 +173,83 @@ class Path:
                                   kept_idx=self.kept, workspace=self.cws)
         rec(5)
 
+    # events of an overlapped step: main stream 0 start, 1 restored, 2 summaries, 3 main decode,
+    # 8 joined; second stream 4 start, 5 boundary decode, 6 score, 7 compress-or-grow
+    NEV_OVERLAP = 9
+
+    def step_overlap(self, ev=None):
+        wl, gp, torch = self.wl, self.gp, self.torch
+        main = torch.cuda.current_stream()
+        sb = self.stream_b
+        rec = (lambda k, st: ev[k].record(st)) if ev is not None else (lambda k, st: None)
+        rec(0, main)
+        self.meta.copy_(self.meta0)
+        rec(1, main)
+        gp.gp_update_query_summaries(wl.q, wl.slot_ids, self.fresh0, wl.qstate, wl.beta_s,
+                                     wl.beta_l)
+        rec(2, main)
+        self.ev_a.record(main)
+        with torch.cuda.stream(sb):
+            sb.wait_event(self.ev_a)
+            rec(4, sb)
+            torch.index_select(wl.q, 0, self.req_l, out=self.q_b)
+            torch.index_select(wl.block_tables, 0, self.req_l, out=self.bt_b)
+            torch.index_select(wl.context_lens, 0, self.req_l, out=self.ctx_b)
+            gp.gp_paged_decode_attn(self.q_b, self.cache, self.bt_b, self.ctx_b, wl.max_context,
+                                    wl.sm_scale, out=self.out_b, lse=self.lse_b,
+                                    workspace=self.dws_b)
+            rec(5, sb)
+            gp.gp_score_and_working_set(wl.q, wl.qstate, wl.slot_ids, wl.req_idx, self.cache,
+                                        wl.block_tables, wl.context_lens, wl.positions,
+                                        wl.rope_theta, wl.p, wl.sm_scale, self.C_max,
+                                        a_short=self.a_s, a_long=self.a_l, ws_counts=self.wsc,
+                                        n_cand=self.ncand, workspace=self.sws)
+            rec(6, sb)
+            gp.gp_compact_or_grow(wl.req_idx, self.a_s, self.a_l, self.wsc, self.ncand, wl.tau,
+                                  wl.k_loc, 0, self.cache, wl.block_tables, wl.n_pages,
+                                  wl.context_lens, wl.refcount, wl.free_stack, wl.free_top,
+                                  policies=self.policies, decision=self.dec,
+                                  kept_idx=self.kept, workspace=self.cws)
+            rec(7, sb)
+            self.ev_b.record(sb)
+        # the other requests (boundary requests masked to length 0: none of their pages is read)
+        gp.gp_paged_decode_attn(wl.q, self.cache, wl.block_tables, self.ctx_main,
+                                wl.max_context, wl.sm_scale, out=self.out, lse=self.lse,
+                                workspace=self.dws)
+        rec(3, main)
+        main.wait_event(self.ev_b)
+        self.out.index_copy_(0, self.req_l, self.out_b)
+        self.lse.index_copy_(0, self.req_l, self.lse_b)
+        rec(8, main)
+
 
 def algorithmic_bytes(wl, path, np):
-    """Bytes each row must move at least once (HBM), per step."""
+    """Bytes each row must move at least once (HBM), per step. decode_main counts the decode
+    call that excludes the boundary requests when the step overlaps them on a second stream."""
     es = 4 if wl.dtype == "f32" else 2
     B, H_q, d, H_kv, b = wl.B, wl.H_q, wl.d, wl.H_kv, wl.page_size
     ctx = wl.context_lens.cpu().numpy().astype(np.int64)
+    req = set(wl.req_idx.cpu().tolist()) if path.R else set()
+    kv_r = np.zeros(B, dtype=np.int64)
     if wl.mixed:
         tags = wl.page_tag.cpu().numpy()
         bt = wl.block_tables.cpu().numpy()
-        kv = 0
         for r in range(B):
             n = int(ctx[r])
-            pages = bt[r, np.arange(n) // b]
-            t = tags[pages]
-            kv += int((t == 2).sum()) * H_kv * d * 2 * 2            # bf16 K + V
-            kv += int((t == 1).sum()) * H_kv * (d * 2 + 2 * 4)     # fp8 K + V codes + 2 scales
+            t = tags[bt[r, np.arange(n) // b]]
+            kv_r[r] = (int((t == 2).sum()) * H_kv * d * 2 * 2             # bf16 K + V
+                       + int((t == 1).sum()) * H_kv * (d * 2 + 2 * 4))    # fp8 K + V codes + 2 scales
     else:
-        kv = int(ctx.sum()) * H_kv * d * es * 2
-    pages = int(sum(math.ceil(c / b) for c in ctx))
-    decode = kv + 2 * B * H_q * d * es + B * H_q * 4 + pages * 4 + B * 4
-    summaries = B * H_q * d * (es + 4 * 4) + B * 5
-    out = dict(decode=decode, decode_kv=kv, summaries=summaries, score=0, compact=0)
-    if path.R:
-        req = wl.req_idx.cpu().tolist()
-        for r in req:
-            c = max(0, (math.ceil(int(ctx[r]) / b) - 1) * b)
-            out["score"] += c * H_kv * d * es + 4 * H_kv * c * 4
+        kv_r[:] = ctx * H_kv * d * es * 2
+    pages_r = np.array([math.ceil(c / b) for c in ctx], dtype=np.int64)
+    per_req = kv_r + 2 * H_q * d * es + H_q * 4 + pages_r * 4 + 4
+    main = [r for r in range(B) if r not in req] if path.overlap else list(range(B))
+    out = dict(decode=int(per_req.sum()), decode_kv=int(kv_r.sum()),
+               decode_main=int(per_req[main].sum()), decode_main_kv=int(kv_r[main].sum()),
+               summaries=B * H_q * d * (es + 4 * 4) + B * 5, score=0, compact=0)
+    for r in req:
+        c = max(0, (math.ceil(int(ctx[r]) / b) - 1) * b)
+        out["score"] += c * H_kv * d * es + 4 * H_kv * c * 4
     return out
 
 
@@ -306,22 +386,23 @@ def main():
     dev = "cuda:0"
     print(f"[bench] building workload {args.config} on {dev}", file=sys.stderr, flush=True)
     wl = make_workload(args.config, "full", device=dev)
-    path = Path(wl, gp, torch)
+    path = Path(wl, gp, torch, overlap=args.overlap)
     path.build_state()
     torch.cuda.synchronize()
     ctx_before = wl.context_lens.cpu().numpy().copy()
 
-    nev = 6
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    step = path.step_overlap if path.overlap else path.step
+    nev = Path.NEV_OVERLAP if path.overlap else 6
+    print(f"[bench] warmup {args.warmup} (overlap {int(path.overlap)})", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        path.step()
+        step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        path.step(events[k])
+        step(events[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
@@ -331,17 +412,23 @@ def main():
 
     rows_ms = dict(restore=avg_ms(0, 1), update_query_summaries=avg_ms(1, 2),
                    paged_decode_attn=avg_ms(2, 3))
-    if path.R:
-        rows_ms["score_and_working_set"] = avg_ms(3, 4)
-        rows_ms["compact_or_grow"] = avg_ms(4, 5)
-    event_step_ms = avg_ms(0, 5)
+    if path.overlap:
+        rows_ms["boundary_requests_decode"] = avg_ms(4, 5)
+        rows_ms["score_and_working_set"] = avg_ms(5, 6)
+        rows_ms["compact_or_grow"] = avg_ms(6, 7)
+        event_step_ms = avg_ms(0, 8)
+    else:
+        if path.R:
+            rows_ms["score_and_working_set"] = avg_ms(3, 4)
+            rows_ms["compact_or_grow"] = avg_ms(4, 5)
+        event_step_ms = avg_ms(0, 5)
 
     by = algorithmic_bytes(wl, path, np)
     by["compact"] = moved_bytes(wl, path, ctx_before, np)
     step_bytes = by["decode"] + by["summaries"] + by["score"] + by["compact"]
     value = step_bytes / (ms_step * 1e-3) / 1e9
     dec_ms = rows_ms["paged_decode_attn"]
-    achieved = by["decode"] / (dec_ms * 1e-3) / 1e9
+    achieved = by["decode_main"] / (dec_ms * 1e-3) / 1e9
 
     # plain device copy of known size: the practical HBM ceiling on this machine
     nbytes = int(args.copy_probe_gib * (1 << 30))
@@ -362,7 +449,8 @@ def main():
     if os.path.exists(PMC_FILE):
         with open(PMC_FILE) as fh:
             pmc = json.load(fh)
-        if pmc.get("decode_src_sha") == file_sha(DECODE_SRC) and pmc.get("config") == args.config:
+        if (pmc.get("decode_src_sha") == file_sha(DECODE_SRC) and pmc.get("config") == args.config
+                and pmc.get("overlap", 0) == int(path.overlap)):
             traffic = pmc.get("bytes_per_launch")
 
     boundary = None
@@ -397,10 +485,14 @@ def main():
                    "boundary_requests": path.R, "page_size": wl.page_size},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "paged_decode_attn (split + merge launches)",
-                     "bytes_per_launch": by["decode"], "avg_launch_ms": round(dec_ms, 4)},
+                     "traffic": traffic,
+                     "kernel": "paged_decode_attn (stream-K + merge launches)" + (
+                         " of the requests not at a page boundary, beside the boundary pass on a "
+                         "second stream" if path.overlap else ""),
+                     "bytes_per_launch": by["decode_main"], "avg_launch_ms": round(dec_ms, 4)},
         "cpu_baseline": cpu,
-        "decode_kv_gbps": round(by["decode_kv"] / (dec_ms * 1e-3) / 1e9, 1),
+        "decode_kv_gbps": round(by["decode_main_kv"] / (dec_ms * 1e-3) / 1e9, 1),
+        "overlap": int(path.overlap),
         "decode_frac_of_copy": round(achieved / copy_gbps, 4),
         "copy_gbps": round(copy_gbps, 1),
         "boundary": boundary,
