@@ -106,13 +106,17 @@ const char* gp_status_string(int status);
  *   q            [B, H_q, head_dim] in the cache dtype (bf16 for mixed caches); the query as
  *                attention sees it (already rotated).
  *   block_tables [B, max_pages]; context_lens [B] (0 .. max_context; 0 gives out = 0, lse = -inf).
- *   max_context  host-side upper bound on every context_lens[r]; it sizes the split-K grid.
+ *   max_context  host-side upper bound on every context_lens[r]; it sizes the workspace.
  *   sm_scale     logit scale, normally 1/sqrt(head_dim).
  *   out          [B, H_q, head_dim] in the q dtype.
  *   lse          [B, H_q] fp32 natural-log log-sum-exp of the scaled logits, or NULL.
- *   workspace    >= gp_paged_decode_attn_workspace_size(...) bytes (split partials).
- * Long contexts are partitioned into splits whose partial (max, sum, output) are merged with
- * PASK App. B.5's rule.
+ *   workspace    >= gp_paged_decode_attn_workspace_size(...) bytes: a prefix of the per-request
+ *                tile counts and the partial (max, sum, output) of every request segment. Its
+ *                contents need no initialisation and are meaningless after the call.
+ * The 16-token tiles of the whole batch are divided evenly over the resident workgroups; a
+ * request spread over several of them is merged from its partials with PASK App. B.5's rule.
+ * Limits: B <= 8191, 1 <= H_q / H_kv <= 16, head_dim 64 or 128, page_size a multiple of 16 up to
+ * 256. Any H_kv (workgroups take up to 8 KV heads each).
  */
 size_t gp_paged_decode_attn_workspace_size(int B, int H_q, int H_kv, int head_dim, int page_size,
                                            int max_context);

@@ -1,0 +1,115 @@
+"""GPU parity on shapes the named workloads do not reach: more than 8 KV heads (several head
+groups per workgroup), one and sixteen query heads per KV head, thousands of tiny or empty
+requests, one very long request spread over many workgroups; plus the boundary pass with one
+query head per KV head. All against the float64 oracle, element by element."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_472_amd as gp
+from oracle import attention as oatt
+from oracle import boundary as ob
+from gpu_common import DEV, TOL, maxabs, say
+from util import f64, npy
+from workloads.configs import make_decode_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _lens(kind, B, rng):
+    if kind == "mixed":
+        return rng.integers(0, 700, size=B)
+    if kind == "tiny":
+        return rng.integers(0, 41, size=B)
+    raise ValueError(kind)
+
+
+CASES = [
+    # B, H_q, H_kv, d, b, lengths, dtype
+    (5, 16, 16, 64, 16, "mixed", "bf16"),     # G = 1, two head groups
+    (3, 32, 2, 64, 16, "mixed", "f32"),       # G = 16
+    (7, 40, 8, 128, 16, "mixed", "bf16"),     # G = 5
+    (2000, 8, 8, 64, 16, "tiny", "bf16"),     # many short and empty requests per workgroup
+    (1, 8, 2, 128, 32, [32768], "bf16"),      # one long request over many workgroups
+    (4, 24, 12, 128, 16, "mixed", "f32"),     # 12 KV heads: a full and a partial head group
+]
+
+
+@pytest.mark.parametrize("B,H_q,H_kv,d,b,lens,dtype", CASES)
+def test_decode_shapes(B, H_q, H_kv, d, b, lens, dtype):
+    rng = np.random.default_rng(B * 131 + H_q)
+    L = lens if isinstance(lens, list) else _lens(lens, B, rng)
+    wl = make_decode_case(B, H_q, H_kv, d, b, L, dtype=dtype, seed=B + H_q).to(DEV)
+    out, lse = gp.gp_paged_decode_attn(wl.q, gp.KVCache.from_workload(wl), wl.block_tables,
+                                       wl.context_lens, wl.max_context, wl.sm_scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
+                                          npy(wl.block_tables), npy(wl.context_lens), b, wl.sm_scale)
+    eo, nan_o = maxabs(f64(out), ref_o)
+    el, nan_l = maxabs(lse.cpu().numpy(), ref_l)
+    empty = npy(wl.context_lens) == 0
+    say(f"[shapes {B}x{H_q}/{H_kv}x{d} b={b} {dtype}] empty={int(empty.sum())} "
+        f"max|out-ref|={eo:.3e} max|lse-ref|={el:.3e}")
+    assert not nan_o and not nan_l
+    assert eo <= TOL[dtype] and el <= TOL[dtype]
+    if empty.any():
+        assert torch.all(out[torch.as_tensor(empty, device=DEV)] == 0)
+        assert torch.all(torch.isneginf(lse[torch.as_tensor(empty, device=DEV)]))
+
+
+def test_decode_rejects_too_many_heads_per_kv_head():
+    wl = make_decode_case(2, 34, 2, 64, 16, [40, 50], dtype="bf16").to(DEV)   # G = 17
+    with pytest.raises(RuntimeError, match="unsupported"):
+        gp.gp_paged_decode_attn(wl.q, gp.KVCache.from_workload(wl), wl.block_tables,
+                                wl.context_lens, wl.max_context, wl.sm_scale)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_boundary_pass_one_query_head_per_kv_head(dtype):
+    """Scores, working sets, decisions, selection and compaction with G = 1 and 12 KV heads."""
+    B = 4
+    lens = [200, 333, 512, 97]
+    wl = make_decode_case(B, 12, 12, 64, 16, lens, dtype=dtype, seed=11, boundary=[0, 1, 2]).to(DEV)
+    ones = torch.ones(B, dtype=torch.uint8, device=DEV)
+    for t in range(wl.q_hist.shape[0] + 1):
+        q = wl.q_hist[t].contiguous() if t < wl.q_hist.shape[0] else wl.q
+        gp.gp_update_query_summaries(q, wl.slot_ids, ones if t == 0 else ones * 0, wl.qstate,
+                                     wl.beta_s, wl.beta_l)
+    C_max = 512
+    cache = gp.KVCache.from_workload(wl)
+    a_s, a_l, ws, nc = gp.gp_score_and_working_set(wl.q, wl.qstate, wl.slot_ids, wl.req_idx, cache,
+                                                   wl.block_tables, wl.context_lens, wl.positions,
+                                                   wl.rope_theta, wl.p, wl.sm_scale, C_max)
+    torch.cuda.synchronize()
+    req = npy(wl.req_idx).tolist()
+    ra_s, ra_l, _, rnc = ob.score_and_working_set(
+        f64(wl.q), f64(wl.qstate), npy(wl.slot_ids), req, f64(wl.k_pool), npy(wl.block_tables),
+        npy(wl.context_lens), npy(wl.positions), wl.page_size, wl.rope_theta, wl.p, wl.sm_scale,
+        C_max=C_max)
+    assert npy(nc).tolist() == rnc.tolist()
+    for i, n in enumerate(rnc.tolist()):
+        e, bad = maxabs(npy(a_s)[i, :, :n], ra_s[i, :, :n])
+        assert not bad and e <= TOL[dtype]
+    ws_ref = ob.working_set_counts(npy(a_s), npy(a_l), rnc, wl.p)
+    assert np.array_equal(npy(ws).astype(np.int64), ws_ref)
+    k_bits = lambda t: t.detach().cpu().view(torch.int16 if t.element_size() == 2 else torch.int32).numpy().copy()  # noqa: E731
+    st = dict(k=k_bits(wl.k_pool), v=k_bits(wl.v_pool), bt=npy(wl.block_tables).astype(np.int64),
+              np_=npy(wl.n_pages).astype(np.int64), ctx=npy(wl.context_lens).astype(np.int64),
+              rc=npy(wl.refcount).astype(np.int64), fs=npy(wl.free_stack).astype(np.int64),
+              top=npy(wl.free_top).astype(np.int64))
+    pol = torch.full((len(req),), ob.POLICY_FORCE_COMPRESS, dtype=torch.int32, device=DEV)
+    dec, kept = gp.gp_compact_or_grow(wl.req_idx, a_s, a_l, ws, nc, wl.tau, wl.k_loc, 0, cache,
+                                      wl.block_tables, wl.n_pages, wl.context_lens, wl.refcount,
+                                      wl.free_stack, wl.free_top, policies=pol)
+    torch.cuda.synchronize()
+    dec_ref, kept_ref = ob.compact_or_grow(req, npy(a_s).astype(np.float64),
+                                           npy(a_l).astype(np.float64), ws_ref, rnc, wl.tau,
+                                           wl.k_loc, ob.POLICY_AUTO, st["k"], st["v"], st["bt"],
+                                           st["np_"], st["ctx"], st["rc"], st["fs"], st["top"],
+                                           wl.page_size, policies=[ob.POLICY_FORCE_COMPRESS] * len(req))
+    assert npy(dec).tolist() == dec_ref.tolist()
+    for i, n in enumerate(rnc.tolist()):
+        assert np.array_equal(npy(kept)[i, :, :n], kept_ref[i, :, :n])
+    assert np.array_equal(k_bits(wl.k_pool), st["k"]) and np.array_equal(k_bits(wl.v_pool), st["v"])
+    assert np.array_equal(npy(wl.context_lens).astype(np.int64), st["ctx"])
+    say(f"[boundary G=1 {dtype}] decisions={npy(dec).tolist()} ws={npy(ws).reshape(-1).tolist()[:6]}")

@@ -362,3 +362,63 @@ def make_workload(name: str, scale: str = "full", device="cpu", seed_offset: int
                   unique_tokens=shared_tokens + int(ctx.sum())),
     )
     return wl
+
+
+def make_decode_case(B: int, H_q: int, H_kv: int, d: int, page_size: int, lens, dtype: str = DTYPE_BF16,
+                     seed: int = 7, device="cpu", boundary=()) -> Workload:
+    """A decode batch of arbitrary shape for edge-case tests: the given context lengths, block
+    tables drawn as a seeded permutation of a pool 1.25x the pages needed (plus 8 spare), N(0,1)
+    q/K/V rounded to `dtype`, NaN in every slot that holds no live token. `boundary` lists request
+    indices to mark as boundary requests (summaries initialised from 4 past queries)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    b = page_size
+    tdt = torch.float32 if dtype == DTYPE_F32 else torch.bfloat16
+    ctx = np.asarray(lens, dtype=np.int64)
+    n_pages = np.maximum(1, -(-ctx // b))
+    used = int(n_pages.sum())
+    num_pages = used + max(8, int(0.25 * used))
+    perm = rng.permutation(num_pages).astype(np.int64)
+    max_pages = int(n_pages.max()) + 2
+    bt = np.full((B, max_pages), -1, dtype=np.int64)
+    cur = 0
+    for r in range(B):
+        k = int(n_pages[r])
+        bt[r, :k] = perm[cur:cur + k]
+        cur += k
+    free_ids = perm[cur:]
+    refcount = np.zeros(num_pages, dtype=np.int64)
+    refcount[perm[:cur]] = 1
+    free_stack = np.full(num_pages, -1, dtype=np.int64)
+    free_stack[:len(free_ids)] = free_ids
+    q = _randn(gen, (B, H_q, d), device).to(tdt)
+    q_hist = _randn(gen, (4, B, H_q, d), device).to(tdt)
+    k_pool = _randn(gen, (num_pages, H_kv, b, d), device).to(tdt)
+    v_pool = _randn(gen, (num_pages, H_kv, b, d), device).to(tdt).transpose(2, 3).contiguous()
+    _nan_fill_pages(k_pool, free_ids)
+    _nan_fill_pages(v_pool, free_ids)
+    for r in range(B):
+        n = int(ctx[r])
+        if n % b or n == 0:
+            last = int(bt[r, max(0, (n - 1) // b)])
+            k_pool[last, :, n % b:, :] = float("nan")
+            v_pool[last, :, :, n % b:] = float("nan")
+    slot_ids = rng.permutation(max(NUM_SLOTS, B))[:B].astype(np.int64)
+
+    def i32(a):
+        return torch.as_tensor(np.asarray(a), dtype=torch.int32, device=device)
+
+    req = sorted(int(r) for r in boundary)
+    return Workload(
+        name="custom", scale="small", B=B, H_q=H_q, H_kv=H_kv, d=d, page_size=b, dtype=dtype,
+        mixed=False, num_pages=num_pages, max_pages=max_pages, q=q, q_hist=q_hist,
+        k_pool=k_pool, v_pool=v_pool, block_tables=i32(bt), n_pages=i32(n_pages),
+        context_lens=i32(ctx), positions=i32(np.maximum(ctx - 1, 0)), slot_ids=i32(slot_ids),
+        refcount=i32(refcount), free_stack=i32(free_stack), free_top=i32([len(free_ids)]),
+        qstate=torch.full((max(NUM_SLOTS, B), 2, H_q, d), float("nan"), dtype=torch.float32,
+                          device=device),
+        req_idx=i32(req), req_policy=[0] * len(req), k_loc=max(1, b // 4),
+        info=dict(max_context=int(ctx.max()) if B else 0, total_tokens=int(ctx.sum()), seed=seed,
+                  unique_tokens=int(ctx.sum())),
+    )
