@@ -10,10 +10,10 @@ the HIP library and is written from the definitions on the pages:
   (importance and block-local + global selection), Eq. 12 (RMS calibration), Sec. 3.3 and
   Sec. 4.2 (Compress & Hold / Grow by One Page), App. E.1 and E.2 (slot pool, prefix sharing).
 * PASK: Parser-Aware Structural KV Persistence: Sec. 3.1 (attention definition) and App. B.5
-  (packed attention inputs, split-KV merge).
+  (packed attention inputs, symmetric per-row INT4 quantisation, split-KV merge).
 
 Parity status per function is listed in each module header; every function here is pinned by
 a CPU test against closed forms, invariants, hand-derived fixtures, library special cases or
 brute force.
 """
-from . import fp8, attention, summaries, boundary  # noqa: F401
+from . import fp8, int4, attention, summaries, boundary  # noqa: F401

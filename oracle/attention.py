@@ -5,8 +5,9 @@ KV head, o = V softmax(K^T q / sqrt(d_k)). Keys and values are found through the
 block table: token slot j lives in physical page bt[j // b] at offset j % b (GrowPage Sec. 4.2:
 a page appended to the block table leaves the attention interface unchanged). GQA maps query
 head g to KV head g // G (PASK App. B.5). With mixed-precision pages (PASK App. B.2 and B.5)
-a released page contributes no tokens, an fp8 page's element is code value * row scale, and
-absolute token positions survive the gaps.
+a released page contributes no tokens, an fp8 page's element is code value * row scale, an
+INT4 page's element is its signed nibble times the row's half-precision scale (App. B.5, the
+packing described in oracle.int4), and absolute token positions survive the gaps.
 
 Split-KV merge (PASK App. B.5): partial results (v_j, l_j, u_j) = (max logit, sum of
 exponentials, unnormalised output) of disjoint token sets combine as
@@ -15,20 +16,25 @@ o = sum_j e^{v_j - v} u_j / sum_j e^{v_j - v} l_j with v = max_j v_j.
 Pinned by: softmax weights sum to one; a contiguous layout equals any block-table permutation;
 equality with torch.nn.functional.scaled_dot_product_attention in float64 on the gathered
 tokens; random split partitions merged equal the single pass; a released page equals deleting
-its tokens; a hand-computed two-token example (tests/golden/decode_tiny.txt).
+its tokens; an INT4 page equals a float page holding its dequantised values; a hand-computed
+two-token example (tests/golden/decode_tiny.txt).
 """
 import numpy as np
 
 from .fp8 import e4m3_decode
+from .int4 import unpack_pairs
 
-TAG_RELEASE, TAG_FP8, TAG_BF16 = 0, 1, 2
+TAG_RELEASE, TAG_FP8, TAG_BF16, TAG_INT4 = 0, 1, 2, 3
 
 
 def gather_request_kv(r, k_pool, v_pool, block_tables, context_lens, page_size,
-                      page_tag=None, k8=None, v8=None, k_scale=None, v_scale=None):
+                      page_tag=None, k8=None, v8=None, k_scale=None, v_scale=None,
+                      k4=None, v4=None, k4_scale=None, v4_scale=None):
     """Visible keys and values of request r as float64 arrays [H_kv, n_vis, d].
 
     k_pool is [num_pages, H_kv, b, d]; v_pool is [num_pages, H_kv, d, b] (token axis last).
+    INT4 pools: k4 [num_pages, H_kv, b, d/2] (packed along d), v4 [num_pages, H_kv, d, b/2]
+    (packed along tokens), k4_scale / v4_scale [num_pages, H_kv, b] half values.
     Also returns the absolute slot index of every visible token.
     """
     n = int(context_lens[r])
@@ -51,6 +57,16 @@ def gather_request_kv(r, k_pool, v_pool, block_tables, context_lens, page_size,
             vs = np.asarray(v_scale)[pages[f8], :, offs[f8]].astype(np.float64)
             k[f8] = kc * ks[..., None]
             v[f8] = vc * vs[..., None]
+        i4 = tags == TAG_INT4
+        if i4.any():
+            pg, of = pages[i4], offs[i4]
+            kc = unpack_pairs(np.asarray(k4)[pg, :, of, :], axis=-1)              # [m, H, d]
+            vfull = unpack_pairs(np.asarray(v4)[pg], axis=-1)                     # [m, H, d, b]
+            vc = vfull[np.arange(len(pg)), :, :, of]                              # [m, H, d]
+            ks = np.asarray(k4_scale)[pg, :, of].astype(np.float64)
+            vs = np.asarray(v4_scale)[pg, :, of].astype(np.float64)
+            k[i4] = kc.astype(np.float64) * ks[..., None]
+            v[i4] = vc.astype(np.float64) * vs[..., None]
     return k.transpose(1, 0, 2), v.transpose(1, 0, 2), slots
 
 
@@ -73,7 +89,7 @@ def attend(q, k, v, sm_scale):
 
 def paged_decode_attn(q, k_pool, v_pool, block_tables, context_lens, page_size, sm_scale,
                       page_tag=None, k8=None, v8=None, k_scale=None, v_scale=None,
-                      requests=None):
+                      k4=None, v4=None, k4_scale=None, v4_scale=None, requests=None):
     """Decode attention for every request (or the listed ones).
 
     q: [B, H_q, d]. Returns out [B, H_q, d] and lse [B, H_q] in float64; rows of requests not
@@ -87,7 +103,8 @@ def paged_decode_attn(q, k_pool, v_pool, block_tables, context_lens, page_size, 
     lse = np.full((B, H_q), np.nan)
     for r in (range(B) if requests is None else requests):
         k, v, _ = gather_request_kv(r, k_pool, v_pool, block_tables, context_lens, page_size,
-                                    page_tag, k8, v8, k_scale, v_scale)
+                                    page_tag, k8, v8, k_scale, v_scale, k4, v4, k4_scale,
+                                    v4_scale)
         for h in range(H_kv):
             o, l_ = attend(q[r, h * G:(h + 1) * G], k[h], v[h], sm_scale)
             out[r, h * G:(h + 1) * G] = o

@@ -118,12 +118,26 @@ def test_split_merge_equals_single_pass():
         assert np.allclose(o, o2, rtol=0, atol=1e-12) and np.allclose(lse, lse2, atol=1e-12)
 
 
-def test_released_page_equals_deleting_its_tokens():
-    wl = make_workload("5", "small")
+def _mixed(wl):
+    return dict(page_tag=npy(wl.page_tag), k8=npy(wl.k8), v8=npy(wl.v8),
+                k_scale=npy(wl.k_scale), v_scale=npy(wl.v_scale), k4=npy(wl.k4), v4=npy(wl.v4),
+                k4_scale=npy(wl.k4_scale), v4_scale=npy(wl.v4_scale))
+
+
+def _nibble(byte_array, high):
+    """Signed nibble by arithmetic shifts of int8 (an independent route to the code)."""
+    b = np.asarray(byte_array, dtype=np.uint8)
+    if not high:
+        b = (b << 4).astype(np.uint8)
+    return (b.view(np.int8) >> 4).astype(np.float64)
+
+
+@pytest.mark.parametrize("int4_frac", [0.0, 0.5])
+def test_released_page_equals_deleting_its_tokens(int4_frac):
+    wl = make_workload("5", "small", int4_frac=int4_frac)
     args = (f64(wl.k_pool), f64(wl.v_pool), npy(wl.block_tables), npy(wl.context_lens),
             wl.page_size)
-    mixed = dict(page_tag=npy(wl.page_tag), k8=npy(wl.k8), v8=npy(wl.v8),
-                 k_scale=npy(wl.k_scale), v_scale=npy(wl.v_scale))
+    mixed = _mixed(wl)
     out, lse = oatt.paged_decode_attn(f64(wl.q), *args[:4], wl.page_size, wl.sm_scale, **mixed)
     assert np.isfinite(out).all()
     tags = npy(wl.page_tag)
@@ -139,14 +153,48 @@ def test_released_page_equals_deleting_its_tokens():
             if tags[pg] == 2:
                 ks.append(f64(wl.k_pool)[pg, :, off, :])
                 vs.append(f64(wl.v_pool)[pg, :, :, off])
+            elif tags[pg] == 3:
+                kb = npy(wl.k4)[pg, :, off, :]                       # [H, d/2]
+                kc = np.stack([_nibble(kb, False), _nibble(kb, True)], -1).reshape(wl.H_kv, wl.d)
+                vc = _nibble(npy(wl.v4)[pg, :, :, off // 2], off % 2 == 1)   # [H, d]
+                ks.append(kc * npy(wl.k4_scale)[pg, :, off, None].astype(np.float64))
+                vs.append(vc * npy(wl.v4_scale)[pg, :, off, None].astype(np.float64))
             else:
                 ks.append(e4m3_decode(npy(wl.k8)[pg, :, off, :]) * npy(wl.k_scale)[pg, :, off, None])
                 vs.append(e4m3_decode(npy(wl.v8)[pg, :, :, off]) * npy(wl.v_scale)[pg, :, off, None])
+        if int4_frac:
+            assert (tags[npy(wl.block_tables)[r, :(n + wl.page_size - 1) // wl.page_size]] == 3).any()
         K, V = np.stack(ks, 1), np.stack(vs, 1)
         for h in range(wl.H_kv):
             o, l_ = oatt.attend(f64(wl.q)[r, h * wl.G:(h + 1) * wl.G], K[h], V[h], wl.sm_scale)
             assert np.allclose(out[r, h * wl.G:(h + 1) * wl.G], o, rtol=0, atol=1e-12)
             assert np.allclose(lse[r, h * wl.G:(h + 1) * wl.G], l_, atol=1e-12)
+
+
+def test_int4_page_equals_float_page_of_its_values():
+    """Dequantised through the oracle's own unpacking, an INT4 page must give the same output
+    as a float page holding code * scale; the values come from arithmetic shifts here."""
+    wl = make_workload("5", "small", int4_frac=1.0)
+    tags = npy(wl.page_tag)
+    assert (tags == 3).any()
+    kp, vp = f64(wl.k_pool), f64(wl.v_pool)
+    for pg in np.nonzero(tags == 3)[0]:
+        kb = npy(wl.k4)[pg]                                            # [H, b, d/2]
+        kc = np.stack([_nibble(kb, False), _nibble(kb, True)], -1).reshape(kp.shape[1:])
+        vb = npy(wl.v4)[pg]                                            # [H, d, b/2]
+        vc = np.stack([_nibble(vb, False), _nibble(vb, True)], -1).reshape(vp.shape[1:])
+        kp[pg] = kc * npy(wl.k4_scale)[pg][..., None].astype(np.float64)
+        vp[pg] = vc * npy(wl.v4_scale)[pg][:, None, :].astype(np.float64)
+    float_tags = np.where(tags == 3, 2, tags).astype(np.uint8)
+    mixed = _mixed(wl)
+    o1, l1 = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
+                                    npy(wl.block_tables), npy(wl.context_lens), wl.page_size,
+                                    wl.sm_scale, **mixed)
+    mixed["page_tag"] = float_tags
+    o2, l2 = oatt.paged_decode_attn(f64(wl.q), kp, vp, npy(wl.block_tables),
+                                    npy(wl.context_lens), wl.page_size, wl.sm_scale, **mixed)
+    assert np.isfinite(o1).all()
+    assert np.allclose(o1, o2, rtol=0, atol=1e-12) and np.allclose(l1, l2, rtol=0, atol=1e-12)
 
 
 def test_all_pages_released_gives_zero():

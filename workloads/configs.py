@@ -8,14 +8,21 @@ Storage layout produced here (the layout the library consumes):
 * mixed-precision pages (GrowPage's companion page on packed KV, PASK B.5, and the fp8 tag of
   the mixed config): ``k8 [num_pages, H_kv, b, d]`` and ``v8 [num_pages, H_kv, d, b]`` hold
   OCP E4M3FN codes, ``k_scale / v_scale [num_pages, H_kv, b]`` one fp32 scale per token row
-  and KV head, and ``page_tag [num_pages]`` (0 released, 1 fp8, 2 bf16).
+  and KV head, and ``page_tag [num_pages]`` (0 released, 1 fp8, 2 bf16, 3 int4).
+* INT4 pages (PASK B.5, present in every mixed workload): ``k4 [num_pages, H_kv, b, d/2]``
+  (two signed nibbles per byte along d, even index low), ``v4 [num_pages, H_kv, d, b/2]``
+  (packed along the token axis), ``k4_scale / v4_scale [num_pages, H_kv, b]`` float16. With
+  ``int4_frac > 0`` that share of the bf16 pages becomes INT4 pages holding random codes in
+  [-7, 7] and random half scales in [0.25, 0.6); otherwise the INT4 pools are poison only.
 * ``block_tables [B, max_pages]`` int32 (unused entries -1), ``n_pages [B]`` allocated pages,
   ``context_lens [B]`` cached tokens, ``positions [B]`` 0-based position of the current token.
 * page pool: ``refcount [num_pages]`` and a LIFO ``free_stack [num_pages]`` with ``free_top [1]``.
 * query-state pool ``[M, 2, H_q, d]`` fp32 (GrowPage App. E.1, Eq. 11, one layer).
 
 Draw order (fixed): metadata from ``numpy.random.Generator(PCG64(1000 + c))``; bulk tensors
-from ``torch.Generator(device).manual_seed(1000 + c)`` in the order q, q_hist, K, V, K8, V8.
+from ``torch.Generator(device).manual_seed(1000 + c)`` in the order q, q_hist, K, V, K8, V8 and,
+with ``int4_frac > 0``, K4, V4, K4 scales, V4 scales; the INT4 page choice comes from its own
+``numpy.random.Generator(PCG64(1000 + c + 7919))`` so that the other draws do not move.
 Slots that hold no live token (free pages, the unused tail of a last page, released pages,
 the inactive precision of a mixed page) are filled with NaN so that any stray read shows up.
 """
@@ -31,7 +38,7 @@ import torch
 DTYPE_F32 = "f32"
 DTYPE_BF16 = "bf16"
 
-TAG_RELEASE, TAG_FP8, TAG_BF16 = 0, 1, 2
+TAG_RELEASE, TAG_FP8, TAG_BF16, TAG_INT4 = 0, 1, 2, 3
 
 CONFIG_NAMES = ("1", "2", "3a", "3b", "4", "5")
 SEED_BASE = 1000
@@ -75,6 +82,10 @@ class Workload:
     k_scale: Optional[torch.Tensor] = None
     v_scale: Optional[torch.Tensor] = None
     page_tag: Optional[torch.Tensor] = None
+    k4: Optional[torch.Tensor] = None
+    v4: Optional[torch.Tensor] = None
+    k4_scale: Optional[torch.Tensor] = None
+    v4_scale: Optional[torch.Tensor] = None
     # method parameters for this config
     beta_s: float = 0.9
     beta_l: float = 0.999
@@ -167,8 +178,11 @@ def _nan_fill_pages(pool: torch.Tensor, pages: np.ndarray) -> None:
 
 
 def make_workload(name: str, scale: str = "full", device="cpu", seed_offset: int = 0,
-                  page_size: int = 16) -> Workload:
-    """Build config ``name`` ("1", "2", "3a", "3b", "4", "5") at ``scale`` ("full"/"small")."""
+                  page_size: int = 16, int4_frac: float = 0.0) -> Workload:
+    """Build config ``name`` ("1", "2", "3a", "3b", "4", "5") at ``scale`` ("full"/"small").
+
+    ``int4_frac`` (mixed configs only): share of the bf16 pages turned into INT4 pages.
+    """
     if name not in CONFIG_NAMES:
         raise ValueError(f"unknown config {name!r}")
     sp = _spec(name, scale)
@@ -324,6 +338,40 @@ def make_workload(name: str, scale: str = "full", device="cpu", seed_offset: int
             k_scale.index_fill_(0, idx, float("nan"))
             v_scale.index_fill_(0, idx, float("nan"))
 
+    k4 = v4 = k4_scale = v4_scale = None
+    if mixed:
+        # INT4 pools: poison (code -8 in both nibbles, NaN scales) except on INT4 pages
+        k4 = torch.full((num_pages, H_kv, b, d // 2), 0x88, dtype=torch.uint8, device=device)
+        v4 = torch.full((num_pages, H_kv, d, b // 2), 0x88, dtype=torch.uint8, device=device)
+        k4_scale = torch.full((num_pages, H_kv, b), float("nan"), dtype=torch.float16, device=device)
+        v4_scale = torch.full_like(k4_scale, float("nan"))
+        if int4_frac > 0:
+            rng4 = np.random.Generator(np.random.PCG64(seed + 7919))
+            bf = np.nonzero(page_tag == TAG_BF16)[0]
+            pick = np.sort(rng4.permutation(bf)[:int(round(int4_frac * len(bf)))])
+
+            def codes(shape):  # random bytes; a nibble 8 (code -8, outside the range) -> 0
+                x = torch.randint(0, 256, shape, generator=gen, device=device, dtype=torch.int32)
+                lo, hi = x & 0xF, x >> 4
+                lo = torch.where(lo == 8, 0, lo)
+                hi = torch.where(hi == 8, 0, hi)
+                return (lo | (hi << 4)).to(torch.uint8)
+
+            def scales(shape):
+                u = torch.rand(shape, generator=gen, device=device, dtype=torch.float32)
+                return (0.25 + 0.35 * u).to(torch.float16)
+
+            n4 = len(pick)
+            idx = torch.as_tensor(pick, dtype=torch.long, device=device)
+            k4[idx] = codes((n4, H_kv, b, d // 2))
+            v4[idx] = codes((n4, H_kv, d, b // 2))
+            k4_scale[idx] = scales((n4, H_kv, b))
+            v4_scale[idx] = scales((n4, H_kv, b))
+            page_tag[pick] = TAG_INT4
+            tag_t = torch.as_tensor(page_tag, device=device)
+            _nan_fill_pages(k_pool, pick)
+            _nan_fill_pages(v_pool, pick)
+
     # poison: free pages and the unused tail of every request's last page
     _nan_fill_pages(k_pool, free_ids)
     _nan_fill_pages(v_pool, free_ids)
@@ -340,6 +388,13 @@ def make_workload(name: str, scale: str = "full", device="cpu", seed_offset: int
             if mixed:
                 k8[last, :, n % b:, :] = 0x7F
                 v8[last, :, :, n % b:] = 0x7F
+                t0 = n % b
+                k4[last, :, t0:, :] = 0x88
+                k4_scale[last, :, t0:] = float("nan")
+                v4_scale[last, :, t0:] = float("nan")
+                if t0 % 2:  # the byte shared with the last live token: poison its high nibble
+                    v4[last, :, :, t0 // 2] = (v4[last, :, :, t0 // 2] & 0x0F) | 0x80
+                v4[last, :, :, (t0 + 1) // 2:] = 0x88
 
     qstate = torch.full((NUM_SLOTS, 2, H_q, d), float("nan"), dtype=torch.float32, device=device)
 
@@ -355,6 +410,7 @@ def make_workload(name: str, scale: str = "full", device="cpu", seed_offset: int
         free_stack=i32(free_stack), free_top=i32(free_top), qstate=qstate,
         req_idx=i32(req), req_policy=policy,
         k8=k8, v8=v8, k_scale=k_scale, v_scale=v_scale, page_tag=tag_t,
+        k4=k4, v4=v4, k4_scale=k4_scale, v4_scale=v4_scale,
         beta_s=sp.get("beta_s", 0.9), beta_l=sp.get("beta_l", 0.999), p=sp.get("p", 0.99),
         tau=0.0, k_loc=max(1, b // 4), rope_theta=10000.0, shared_pages=shared_pages,
         info=dict(max_context=int(context_lens.max()) if B else 0,
