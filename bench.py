@@ -36,6 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MIXED_POOLS = ("k8", "v8", "k_scale", "v_scale", "page_tag", "k4", "v4", "k4_scale", "v4_scale")
 METRIC = "paged decode attention KV GB/s (% HBM peak) + boundary-pass latency/request"
 PMC_FILE = os.path.join(ROOT, "profiles", "decode_qwen3_8b_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_472_amd", "csrc", "decode.hip")
@@ -238,7 +239,8 @@ def algorithmic_bytes(wl, path, np):
             n = int(ctx[r])
             t = tags[bt[r, np.arange(n) // b]]
             kv_r[r] = (int((t == 2).sum()) * H_kv * d * 2 * 2             # bf16 K + V
-                       + int((t == 1).sum()) * H_kv * (d * 2 + 2 * 4))    # fp8 K + V codes + 2 scales
+                       + int((t == 1).sum()) * H_kv * (d * 2 + 2 * 4)     # fp8 K + V codes + 2 scales
+                       + int((t == 3).sum()) * H_kv * (d + 2 * 2))        # INT4 K + V codes + 2 scales
     else:
         kv_r[:] = ctx * H_kv * d * es * 2
     pages_r = np.array([math.ceil(c / b) for c in ctx], dtype=np.int64)
@@ -301,7 +303,7 @@ def cpu_baseline(wl, path, budget_s, np):
         sub = {"k": wl.k_pool.index_select(0, idx).cpu().double().numpy(),
                "v": wl.v_pool.index_select(0, idx).cpu().double().numpy()}
         if wl.mixed:
-            for nm in ("k8", "v8", "k_scale", "v_scale", "page_tag"):
+            for nm in MIXED_POOLS:
                 sub[nm] = getattr(wl, nm).index_select(0, idx).cpu().numpy()
         bt = np.where(rows >= 0, remap[np.maximum(rows, 0)], -1)
         return sub, bt
@@ -324,8 +326,7 @@ def cpu_baseline(wl, path, budget_s, np):
         sub, bt = host_pages([r])
         extra = {}
         if wl.mixed:
-            extra = dict(page_tag=sub["page_tag"], k8=sub["k8"], v8=sub["v8"],
-                         k_scale=sub["k_scale"], v_scale=sub["v_scale"])
+            extra = {nm: sub[nm] for nm in MIXED_POOLS}
         t0 = time.perf_counter()
         oatt.paged_decode_attn(q64[r:r + 1], sub["k"], sub["v"], bt, ctx[r:r + 1], b,
                                wl.sm_scale, **extra)

@@ -5,6 +5,8 @@
  *   gp_paged_decode_attn      PASK, Sec. 3.1 (o = V softmax(K^T q / sqrt(d_k))), App. B.2 and B.5
  *                             (mixed-precision pages, GQA routes, split-KV merge); GrowPage Sec. 4.2
  *                             (block tables, unchanged attention interface after a grown page).
+ *   gp_quantize_pages_int4    PASK App. B.5 (symmetric per-row INT4 codes with half scales, two
+ *                             signed nibbles per byte).
  *   gp_update_query_summaries GrowPage Sec. 3.2 Eq. 6 and App. E.1 (slot pool, first-step init).
  *   gp_score_and_working_set  GrowPage App. E.1 Eq. 12 (RMS calibration + RoPE), Sec. 3.2
  *                             (candidate set without the most recent block, short/long views),
@@ -56,7 +58,7 @@ typedef enum {
 typedef enum { GP_F32 = 0, GP_BF16 = 1 } gp_dtype;
 
 /* Page tags of mixed-precision caches (PASK App. B.2: released entries keep their positions). */
-enum { GP_TAG_RELEASE = 0, GP_TAG_FP8 = 1, GP_TAG_BF16 = 2 };
+enum { GP_TAG_RELEASE = 0, GP_TAG_FP8 = 1, GP_TAG_BF16 = 2, GP_TAG_INT4 = 3 };
 
 /* Outcome per boundary request (GrowPage Sec. 4.2, App. H.2). */
 enum {
@@ -78,9 +80,19 @@ enum {
  * One layer's paged KV cache.
  *   k, v      pools in `dtype` (GP_F32 or GP_BF16), layouts above. Required.
  *   page_tag  NULL for a uniform cache. Otherwise [num_pages] uint8 with GP_TAG_*: a mixed
- *             cache (dtype must be GP_BF16). Released pages are skipped entirely; fp8 pages
- *             read k8/v8 (OCP E4M3FN codes, same layouts as k/v) times the per-row scales
- *             k_scale/v_scale [num_pages, H_kv, page_size] fp32; bf16 pages read k/v.
+ *             cache (dtype must be GP_BF16) whose fp8 and INT4 pools must all be given.
+ *             Released pages are skipped entirely; bf16 pages read k/v; fp8 pages read k8/v8
+ *             (OCP E4M3FN codes, same layouts as k/v) times the per-row scales
+ *             k_scale/v_scale [num_pages, H_kv, page_size] fp32; INT4 pages (PASK App. B.5)
+ *             read signed 4-bit codes (two's complement nibbles, the even index of a pair in
+ *             the low nibble) times per-row IEEE half scales:
+ *               k4       [num_pages, H_kv, page_size, head_dim / 2]  key rows packed along d
+ *               v4       [num_pages, H_kv, head_dim, page_size / 2]  value rows of one
+ *                        dimension packed along the token axis (values stay token-contiguous)
+ *               k4_scale, v4_scale [num_pages, H_kv, page_size]      half bits, one per token
+ *                        row and KV head.
+ *             A byte value in an INT4 pool always decodes to finite codes (-8 .. 7), so only
+ *             the scales of live tokens need to be meaningful.
  *   page_size a multiple of 16 (16 .. 256); head_dim 64 or 128.
  */
 typedef struct {
@@ -90,12 +102,16 @@ typedef struct {
   void* v8;
   float* k_scale;
   float* v_scale;
-  const uint8_t* page_tag;
+  uint8_t* page_tag; /* written only by gp_quantize_pages_int4 */
   int32_t num_pages;
   int32_t page_size;
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t dtype;
+  void* k4;
+  void* v4;
+  uint16_t* k4_scale;
+  uint16_t* v4_scale;
 } gp_kv_cache;
 
 int gp_version(void);
@@ -117,6 +133,9 @@ const char* gp_status_string(int status);
  * request spread over several of them is merged from its partials with PASK App. B.5's rule.
  * Limits: B <= 8191, 1 <= H_q / H_kv <= 16, head_dim 64 or 128, page_size a multiple of 16 up to
  * 256. Any H_kv (workgroups take up to 8 KV heads each).
+ * INT4 pages are contracted exactly in half precision: the query elements are rounded to half
+ * (exact for bf16 values of magnitude 2^-14 .. 65504; larger ones overflow) and the probability
+ * weights times the value scales are rounded to half toward zero before the value product.
  */
 size_t gp_paged_decode_attn_workspace_size(int B, int H_q, int H_kv, int head_dim, int page_size,
                                            int max_context);
@@ -124,6 +143,21 @@ int gp_paged_decode_attn(const void* q, int q_dtype, int B, int H_q, const gp_kv
                          const int32_t* block_tables, int max_pages, const int32_t* context_lens,
                          int max_context, float sm_scale, void* out, float* lse, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * Demote bf16 pages of a mixed cache to INT4 pages (PASK App. B.5).
+ *   page_ids [num_ids] int32 device array. For every listed page whose tag is GP_TAG_BF16, each
+ *   K row and each V row (one token of one KV head, head_dim elements read from k / v) gets the
+ *   scale s = half(amax / 7) (nearest, ties to even; at least 2^-24; 1 for an all-zero row)
+ *   written to k4_scale / v4_scale, and the codes clip(round_half_even(x / s), -7, 7) written
+ *   to k4 / v4 in the layouts of gp_kv_cache; then the tag becomes GP_TAG_INT4. All page_size
+ *   rows of the page are converted. Ids outside [0, num_pages) and pages with another tag are
+ *   left alone; a repeated id is converted once. The bf16 pool of the page is not modified.
+ *   Rows holding NaN or Inf get unspecified codes and scales.
+ *   kv must be a mixed cache (page_tag, k4, v4, k4_scale, v4_scale given, dtype GP_BF16).
+ */
+int gp_quantize_pages_int4(const gp_kv_cache* kv, const int32_t* page_ids, int num_ids,
+                           void* stream);
 
 /*
  * Dual-timescale EMA of the pre-RoPE queries (GrowPage Eq. 6, App. E.1).

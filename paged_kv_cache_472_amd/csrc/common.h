@@ -12,6 +12,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 #define GP_WAVE 64
 #define GP_LOG2E 1.4426950408889634f
@@ -44,6 +47,40 @@ __device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t codes) {
   return r;
 }
 
+// Signed 4-bit codes (two's complement nibbles) -> exact half values. A code c becomes the
+// biased nibble u = c + 8 (= nibble ^ 8); placed in the low mantissa bits of 1024.0 (0x6400,
+// whose half spacing is 1) it reads as 1024 + u, and subtracting 1032 leaves c exactly. A
+// nibble in bits 4..7 of a half reads as 1024 + 16u; times 1/16 minus 72 it is c again.
+__device__ __forceinline__ f16x2_t int4_lo_pair(uint32_t x) {  // nibbles at bits 0..3, 16..19
+  return __builtin_bit_cast(f16x2_t, (x & 0x000F000Fu) ^ 0x64086408u) - f16x2_t{1032, 1032};
+}
+__device__ __forceinline__ f16x2_t int4_hi_pair(uint32_t x) {  // nibbles at bits 4..7, 20..23
+  return __builtin_bit_cast(f16x2_t, (x & 0x00F000F0u) ^ 0x64806480u) * f16x2_t{0.0625, 0.0625} -
+         f16x2_t{72, 72};
+}
+
+// Eight codes of one dword (nibble j = element j) -> halves in the element order
+// (0, 4, 1, 5, 2, 6, 3, 7).
+__device__ __forceinline__ f16x8_t int4x8_to_f16x8(uint32_t w) {
+  const f16x2_t a = int4_lo_pair(w), b = int4_hi_pair(w);
+  const f16x2_t c = int4_lo_pair(w >> 8), d = int4_hi_pair(w >> 8);
+  return f16x8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
+
+// Four codes in the low 16 bits (nibble j = element j) -> halves in the order (0, 2, 1, 3).
+__device__ __forceinline__ f16x4_t int4x4_to_f16x4(uint32_t w) {
+  const uint32_t x = (w & 0xffu) | ((w & 0xff00u) << 8);  // byte 1 moves to byte 2
+  const f16x2_t a = int4_lo_pair(x), b = int4_hi_pair(x);
+  return f16x4_t{a.x, a.y, b.x, b.y};
+}
+
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, GP_WAVE));
@@ -65,6 +102,12 @@ __device__ __forceinline__ f32x4_t mfma_bf16_16x16x32(bf16x8_t a, bf16x8_t b, f3
 }
 __device__ __forceinline__ f32x4_t mfma_bf16_16x16x16(i16x4_t a, i16x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f16_16x16x32(f16x8_t a, f16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f16_16x16x16(f16x4_t a, f16x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4_t mfma_f32_16x16x4(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

@@ -18,6 +18,13 @@
 // tokens of one value row). Tiles are prefetched into a register ring whose slots rotate by
 // unrolling, so no register copy waits on an in-flight load; page ids are fetched 64 tiles at a
 // time, one per lane, a chunk ahead of use.
+//
+// Mixed-precision caches choose the page kind per tile (a uniform branch): released pages are
+// skipped, fp8 codes are widened exactly to bf16 and their row scales applied to the logits and
+// the probability weights, and INT4 pages (PASK App. B.5) are contracted in half precision:
+// their nibbles become exact half values through the mantissa of 1024.0, the key product uses a
+// half copy of the query laid out in the order the nibbles unpack in, and the value product
+// takes each lane's four tokens in the order (0, 2, 1, 3) on both operands.
 #include "common.h"
 
 #include <algorithm>
@@ -42,6 +49,10 @@ struct DecodeParams {
   const uint8_t* v8;
   const float* k_scale;
   const float* v_scale;
+  const uint8_t* k4;
+  const uint8_t* v4;
+  const uint16_t* k4_scale;
+  const uint16_t* v4_scale;
   const uint8_t* page_tag;
   const int32_t* block_tables;
   const int32_t* context_lens;
@@ -76,9 +87,10 @@ struct TileRaw<D, KIND_BF16> {
 
 template <int D>
 struct TileRaw<D, KIND_MIXED> {
-  u32x4_t k[D / 32];  // bf16: 8 elements; fp8: 8 codes in .xy
-  u32x2_t v[D / 16];  // bf16: 4 elements; fp8: 4 codes in .x
-  f32x4_t ks, vs;     // per-token scales of the 4 tokens this lane owns (fp8 pages)
+  u32x4_t k[D / 32];  // bf16: 8 elements; fp8: 8 codes in .xy; INT4: 8 codes in .x
+  u32x2_t v[D / 16];  // bf16: 4 elements; fp8: 4 codes in .x; INT4: 4 codes in .x (low half)
+  f32x4_t ks, vs;     // per-token scales of the 4 tokens this lane owns (fp8: fp32 values;
+                      // INT4: four half bit patterns in components 0 and 1)
 };
 
 __device__ __forceinline__ int sanitize_ctx(const DecodeParams& p, int r) {
@@ -98,6 +110,24 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
   if constexpr (KIND == KIND_MIXED) {
     const int pg = code >> 2, tag = code & 3;
     const size_t kv_base = ((size_t)pg * p.H_kv + h) * (size_t)b * D;
+    const size_t sb = ((size_t)pg * p.H_kv + h) * b + off + 4 * g4;
+    if (tag == GP_TAG_INT4) {
+      // key row (off + n16) packed along d: the 8 codes of step kk are 4 bytes
+      const uint8_t* kr = p.k4 + kv_base / 2 + (size_t)(off + n16) * (D / 2) + 4 * g4;
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk)
+        t.k[kk] = u32x4_t{*reinterpret_cast<const uint32_t*>(kr + 16 * kk), 0u, 0u, 0u};
+      // value row n16 (+16 nb) packed along tokens: this lane's 4 tokens are 2 bytes
+      const uint8_t* vr = p.v4 + kv_base / 2 + (size_t)n16 * (b / 2) + (off + 4 * g4) / 2;
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb)
+        t.v[nb] = u32x2_t{(uint32_t)*reinterpret_cast<const uint16_t*>(vr + (size_t)8 * nb * b), 0u};
+      const u32x2_t ksr = *reinterpret_cast<const u32x2_t*>(p.k4_scale + sb);
+      const u32x2_t vsr = *reinterpret_cast<const u32x2_t*>(p.v4_scale + sb);
+      t.ks = f32x4_t{__uint_as_float(ksr.x), __uint_as_float(ksr.y), 0.f, 0.f};
+      t.vs = f32x4_t{__uint_as_float(vsr.x), __uint_as_float(vsr.y), 0.f, 0.f};
+      return;
+    }
     if (tag == GP_TAG_FP8) {
       const uint8_t* kr = p.k8 + kv_base + (size_t)(off + n16) * D + 8 * g4;
 #pragma unroll
@@ -109,7 +139,6 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb)
         t.v[nb] = u32x2_t{*reinterpret_cast<const uint32_t*>(vr + (size_t)16 * nb * b), 0u};
-      const size_t sb = ((size_t)pg * p.H_kv + h) * b + off + 4 * g4;
       t.ks = *reinterpret_cast<const f32x4_t*>(p.k_scale + sb);
       t.vs = *reinterpret_cast<const f32x4_t*>(p.v_scale + sb);
       return;
@@ -154,13 +183,27 @@ struct WaveState {
 template <int D, int KIND>
 __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRaw<D, KIND>& cur,
                                              int code, int tok0, int ctx, int lane,
-                                             const u32x4_t* qf, WaveState<D>& st) {
+                                             const u32x4_t* qf, const f16x8_t* qh,
+                                             WaveState<D>& st) {
   const int g4 = lane >> 4;
   const bool tail = tok0 + 16 > ctx;
   // ---- logits: S[token 4*g4 + i][head n16]
   f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-  bool fp8 = false;
-  if constexpr (KIND == KIND_MIXED) fp8 = (code & 3) == GP_TAG_FP8;
+  bool fp8 = false, int4 = false;
+  float ks[4], vs[4];
+  if constexpr (KIND == KIND_MIXED) {
+    fp8 = (code & 3) == GP_TAG_FP8;
+    int4 = (code & 3) == GP_TAG_INT4;
+    if (int4) {
+      const uint32_t k01 = __float_as_uint(cur.ks[0]), k23 = __float_as_uint(cur.ks[1]);
+      const uint32_t v01 = __float_as_uint(cur.vs[0]), v23 = __float_as_uint(cur.vs[1]);
+      ks[0] = gp::half_lo(k01); ks[1] = gp::half_hi(k01); ks[2] = gp::half_lo(k23); ks[3] = gp::half_hi(k23);
+      vs[0] = gp::half_lo(v01); vs[1] = gp::half_hi(v01); vs[2] = gp::half_lo(v23); vs[3] = gp::half_hi(v23);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { ks[i] = cur.ks[i]; vs[i] = cur.vs[i]; }
+    }
+  }
   if constexpr (KIND == KIND_F32) {
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
@@ -168,6 +211,10 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
       for (int c = 0; c < 4; ++c)
         sacc = gp::mfma_f32_16x16x4(__uint_as_float(cur.k[i][c]), __uint_as_float(qf[i][c]), sacc);
     }
+  } else if (int4) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      sacc = gp::mfma_f16_16x16x32(gp::int4x8_to_f16x8(cur.k[kk].x), qh[kk], sacc);
   } else {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
@@ -187,7 +234,7 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float z = sacc[i];
-    if constexpr (KIND == KIND_MIXED) z *= cur.ks[i];
+    if constexpr (KIND == KIND_MIXED) z *= ks[i];
     const bool ok = tok0 + 4 * g4 + i < ctx;
     sv[i] = ok ? z * p.scale_log2 : -INFINITY;
     mx = fmaxf(mx, sv[i]);
@@ -230,12 +277,22 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       pw[i] = pv[i];
-      if constexpr (KIND == KIND_MIXED) pw[i] *= cur.vs[i];
+      if constexpr (KIND == KIND_MIXED) pw[i] *= vs[i];
     }
     if constexpr (KIND == KIND_MIXED) {
       // scales of masked tokens may be poison; keep them out of the product
 #pragma unroll
       for (int i = 0; i < 4; ++i) if (pv[i] == 0.f) pw[i] = 0.f;
+      if (int4) {
+        // every INT4 byte decodes to a finite code, so no value masking is needed
+        const f16x2_t p02 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(pw[0], pw[2]));
+        const f16x2_t p13 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(pw[1], pw[3]));
+        const f16x4_t ph = f16x4_t{p02.x, p02.y, p13.x, p13.y};
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb)
+          st.acc[nb] = gp::mfma_f16_16x16x16(ph, gp::int4x4_to_f16x4(cur.v[nb].x), st.acc[nb]);
+        return;
+      }
     }
     const u32x2_t pp = u32x2_t{gp::pack_bf16x2(pw[0], pw[1]), gp::pack_bf16x2(pw[2], pw[3])};
     // values of tokens past the context (the tail of the last page) are masked to zero bits
@@ -333,7 +390,8 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
         if constexpr (KIND == KIND_MIXED) {
           if (code >= 0) {
             const int tag = p.page_tag[pg];
-            code = (tag == GP_TAG_FP8 || tag == GP_TAG_BF16) ? ((pg << 2) | tag) : -1;
+            code = (tag == GP_TAG_FP8 || tag == GP_TAG_BF16 || tag == GP_TAG_INT4)
+                       ? ((pg << 2) | tag) : -1;
           }
         }
       }
@@ -367,6 +425,20 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
       for (int kk = 0; kk < D / 32; ++kk)
         qf[kk] = (n16 < G) ? *reinterpret_cast<const u32x4_t*>(qr + 32 * kk) : u32x4_t{0u, 0u, 0u, 0u};
     }
+    // half copy of the query for INT4 pages, in the element order their codes unpack in
+    f16x8_t qh[KIND == KIND_MIXED ? D / 32 : 1];
+    if constexpr (KIND == KIND_MIXED) {
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const u32x4_t a = qf[kk];
+        const float e0 = __uint_as_float(a.x << 16), e1 = __uint_as_float(a.x & 0xffff0000u);
+        const float e2 = __uint_as_float(a.y << 16), e3 = __uint_as_float(a.y & 0xffff0000u);
+        const float e4 = __uint_as_float(a.z << 16), e5 = __uint_as_float(a.z & 0xffff0000u);
+        const float e6 = __uint_as_float(a.w << 16), e7 = __uint_as_float(a.w & 0xffff0000u);
+        qh[kk] = f16x8_t{(_Float16)e0, (_Float16)e4, (_Float16)e1, (_Float16)e5,
+                         (_Float16)e2, (_Float16)e6, (_Float16)e3, (_Float16)e7};
+      }
+    }
 
     WaveState<D> st;
 #pragma unroll
@@ -387,7 +459,7 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
       for (int q = 0; q < RING; ++q) {
         const int t = base + q;
         if (t < tb) {
-          if (codes[q] >= 0) process_tile<D, KIND>(p, ring[q], codes[q], t << 4, ctx, lane, qf, st);
+          if (codes[q] >= 0) process_tile<D, KIND>(p, ring[q], codes[q], t << 4, ctx, lane, qf, qh, st);
           const int x = t + RING;
           codes[q] = x < tb ? code_of(x) : -1;
           if (codes[q] >= 0) load_tile<D, KIND>(p, codes[q], x << 4, h, lane, ring[q]);
@@ -570,7 +642,8 @@ extern "C" int gp_paged_decode_attn(const void* q, int q_dtype, int B, int H_q,
   if (B > MAX_BATCH) return GP_ERR_UNSUPPORTED;
   if (q_dtype != kv->dtype || (q_dtype != GP_F32 && q_dtype != GP_BF16)) return GP_ERR_INVALID;
   const bool mixed = kv->page_tag != nullptr;
-  if (mixed && (q_dtype != GP_BF16 || !kv->k8 || !kv->v8 || !kv->k_scale || !kv->v_scale))
+  if (mixed && (q_dtype != GP_BF16 || !kv->k8 || !kv->v8 || !kv->k_scale || !kv->v_scale ||
+                !kv->k4 || !kv->v4 || !kv->k4_scale || !kv->v4_scale))
     return GP_ERR_INVALID;
   if ((long)max_context > (long)max_pages * b) return GP_ERR_INVALID;
   if ((long)kv->num_pages * H_kv * b > (1L << 40)) return GP_ERR_INVALID;
@@ -589,6 +662,10 @@ extern "C" int gp_paged_decode_attn(const void* q, int q_dtype, int B, int H_q,
   p.v8 = static_cast<const uint8_t*>(kv->v8);
   p.k_scale = kv->k_scale;
   p.v_scale = kv->v_scale;
+  p.k4 = static_cast<const uint8_t*>(kv->k4);
+  p.v4 = static_cast<const uint8_t*>(kv->v4);
+  p.k4_scale = kv->k4_scale;
+  p.v4_scale = kv->v4_scale;
   p.page_tag = kv->page_tag;
   p.block_tables = block_tables;
   p.context_lens = context_lens;

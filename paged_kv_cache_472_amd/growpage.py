@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libgrowpage.so")
 
 GP_F32, GP_BF16 = 0, 1
-TAG_RELEASE, TAG_FP8, TAG_BF16 = 0, 1, 2
+TAG_RELEASE, TAG_FP8, TAG_BF16, TAG_INT4 = 0, 1, 2, 3
 COMPRESS, GROW, GROW_FALLBACK_COMPRESS, NO_PAGES = 0, 1, 2, 3
 POLICY_AUTO, POLICY_FORCE_COMPRESS, POLICY_FORCE_GROW, POLICY_INVERSE = 0, 1, 2, 3
 
@@ -23,6 +23,7 @@ EXPORTED = (
     "gp_update_query_summaries",
     "gp_score_and_working_set_workspace_size", "gp_score_and_working_set",
     "gp_compact_or_grow_workspace_size", "gp_compact_or_grow",
+    "gp_quantize_pages_int4",
 )
 
 
@@ -35,6 +36,8 @@ class GpKvCache(ctypes.Structure):
         ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
         ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("k4", ctypes.c_void_p), ("v4", ctypes.c_void_p),
+        ("k4_scale", ctypes.c_void_p), ("v4_scale", ctypes.c_void_p),
     ]
 
 
@@ -72,6 +75,8 @@ def lib():
         L.gp_compact_or_grow.argtypes = [_VP, _I, _I, _VP, _VP, _I, _VP, _VP, _D, _I, _I, _VP,
                                          ctypes.POINTER(GpKvCache), _VP, _VP, _I, _VP, _VP, _VP, _VP,
                                          _VP, _VP, _VP, _SZ, _VP]
+        L.gp_quantize_pages_int4.restype = _I
+        L.gp_quantize_pages_int4.argtypes = [ctypes.POINTER(GpKvCache), _VP, _I, _VP]
         _lib = L
     return _lib
 
@@ -101,14 +106,16 @@ def _dtype_code(t):
 class KVCache:
     """Device tensors of one layer's paged cache (layouts in include/growpage.h)."""
 
-    def __init__(self, k, v, page_size, k8=None, v8=None, k_scale=None, v_scale=None, page_tag=None):
+    def __init__(self, k, v, page_size, k8=None, v8=None, k_scale=None, v_scale=None, page_tag=None,
+                 k4=None, v4=None, k4_scale=None, v4_scale=None):
         self.k, self.v, self.page_size = k, v, int(page_size)
         self.k8, self.v8, self.k_scale, self.v_scale, self.page_tag = k8, v8, k_scale, v_scale, page_tag
+        self.k4, self.v4, self.k4_scale, self.v4_scale = k4, v4, k4_scale, v4_scale
 
     @classmethod
     def from_workload(cls, wl):
         return cls(wl.k_pool, wl.v_pool, wl.page_size, wl.k8, wl.v8, wl.k_scale, wl.v_scale,
-                   wl.page_tag)
+                   wl.page_tag, wl.k4, wl.v4, wl.k4_scale, wl.v4_scale)
 
     @property
     def num_kv_heads(self):
@@ -122,7 +129,8 @@ class KVCache:
         return GpKvCache(
             _ptr(self.k), _ptr(self.v), _ptr(self.k8), _ptr(self.v8), _ptr(self.k_scale),
             _ptr(self.v_scale), _ptr(self.page_tag), self.k.shape[0], self.page_size,
-            self.k.shape[1], self.k.shape[3], _dtype_code(self.k))
+            self.k.shape[1], self.k.shape[3], _dtype_code(self.k), _ptr(self.k4), _ptr(self.v4),
+            _ptr(self.k4_scale), _ptr(self.v4_scale))
 
 
 def gp_paged_decode_attn_workspace_size(B, H_q, H_kv, head_dim, page_size, max_context):
@@ -221,3 +229,10 @@ def gp_compact_or_grow(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, 
         _ptr(kept_idx), _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
     _check(st, "gp_compact_or_grow")
     return decision, kept_idx
+
+
+def gp_quantize_pages_int4(cache, page_ids):
+    """Demote the listed bf16 pages of a mixed cache to INT4 pages (in place)."""
+    kv = cache.struct()
+    st = lib().gp_quantize_pages_int4(ctypes.byref(kv), _ptr(page_ids), page_ids.numel(), _stream())
+    _check(st, "gp_quantize_pages_int4")

@@ -15,13 +15,24 @@ def say(*a):
     sys.stdout.flush()
 
 
-def workload_on_gpu(cfg, scale, page_size=16):
+MIXED_POOLS = ("k8", "v8", "k_scale", "v_scale", "page_tag", "k4", "v4", "k4_scale", "v4_scale")
+
+
+def workload_on_gpu(cfg, scale, page_size=16, int4_frac=0.0):
     """Small workloads are drawn on the CPU and copied (identical values on both sides);
     full-size ones are drawn directly on the GPU."""
-    say(f"[workload] config={cfg} scale={scale} page_size={page_size}")
+    say(f"[workload] config={cfg} scale={scale} page_size={page_size} int4_frac={int4_frac}")
     if scale == "small":
-        return make_workload(cfg, "small", device="cpu", page_size=page_size).to(DEV)
-    return make_workload(cfg, "full", device=DEV, page_size=page_size)
+        return make_workload(cfg, "small", device="cpu", page_size=page_size,
+                             int4_frac=int4_frac).to(DEV)
+    return make_workload(cfg, "full", device=DEV, page_size=page_size, int4_frac=int4_frac)
+
+
+def mixed_np(sub_or_wl):
+    """The mixed-precision pools of a workload (or of gather_pages_to_host's dict) as numpy."""
+    from util import npy
+    g = (lambda n: sub_or_wl[n]) if isinstance(sub_or_wl, dict) else (lambda n: getattr(sub_or_wl, n))
+    return {n: npy(g(n)) for n in MIXED_POOLS}
 
 
 def maxabs(a, b):
@@ -46,7 +57,7 @@ def gather_pages_to_host(wl, requests):
     remap[pages] = np.arange(len(pages))
     sub = dict(k_pool=wl.k_pool.index_select(0, idx).cpu(), v_pool=wl.v_pool.index_select(0, idx).cpu())
     if wl.mixed:
-        for name in ("k8", "v8", "k_scale", "v_scale", "page_tag"):
+        for name in MIXED_POOLS:
             sub[name] = getattr(wl, name).index_select(0, idx).cpu()
     bt_full = wl.block_tables.cpu().numpy()
     bt_sub = np.full((len(requests), bt_full.shape[1]), -1, dtype=np.int64)
