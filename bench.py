@@ -21,7 +21,9 @@ stream wait for it and the overlapped step is slower than the single-stream one.
 Prints one JSON line. `value` is the step's algorithmic HBM bytes divided by the step time;
 `roofline` is the main decode call (its two kernels) against the 8 TB/s HBM peak, timed with HIP
 events on the stream it is launched on; `cpu_baseline` is the float64 CPU oracle on a bounded
-sample of the same workload.
+sample of the same workload. `int4_decode` (bf16 workloads, --int4 1) times decode of the same
+batch after every used page has been demoted to INT4 pages by the page quantiser (PASK App. B.5):
+the quantiser call itself, the decode time per launch and its bytes against the same peak.
 """
 import argparse
 import hashlib
@@ -62,6 +64,9 @@ def parse():
     ap.add_argument("--overlap", type=int, default=0,
                     help="1: the boundary requests' decode and boundary pass run on a second stream "
                          "beside the decode of the other requests; 0: everything on one stream")
+    ap.add_argument("--int4", type=int, default=1,
+                    help="also time decode with every page of the batch demoted to INT4 "
+                         "(PASK App. B.5) by the page quantiser (bf16 workloads)")
     ap.add_argument("--copy-probe-gib", type=float, default=1.0,
                     help="size of the plain device copy timed beside the path (HBM reference)")
     return ap.parse_args()
@@ -277,6 +282,53 @@ def moved_bytes(wl, path, ctx_before, np):
     return tot
 
 
+def int4_leg(wl, gp, torch, np, steps):
+    """Decode of the same batch with every used page demoted to INT4 (one quantiser call over
+    all of them, timed once), on a mixed cache sharing the bf16 pools. Returns a dict with the
+    decode time per launch and its algorithmic bytes: codes d/2 bytes per K and per V row plus
+    two half scales per token and KV head."""
+    dev = wl.k_pool.device
+    P, H, b, d = wl.k_pool.shape
+    tiny = torch.zeros(64, dtype=torch.uint8, device=dev)  # fp8 pools: no page carries that tag
+    cache = gp.KVCache(wl.k_pool, wl.v_pool, b, k8=tiny, v8=tiny, k_scale=tiny.view(torch.float32),
+                       v_scale=tiny.view(torch.float32),
+                       page_tag=torch.full((P,), 2, dtype=torch.uint8, device=dev),
+                       k4=torch.empty((P, H, b, d // 2), dtype=torch.uint8, device=dev),
+                       v4=torch.empty((P, H, b // 4, d, 2), dtype=torch.uint8, device=dev),
+                       k4_scale=torch.empty((P, H, b), dtype=torch.float16, device=dev),
+                       v4_scale=torch.empty((P, H, b), dtype=torch.float16, device=dev))
+    bt = wl.block_tables.cpu().numpy()
+    used = torch.as_tensor(np.unique(bt[bt >= 0]), dtype=torch.int32, device=dev)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record()
+    gp.gp_quantize_pages_int4(cache, used)
+    e[1].record()
+    need = gp.gp_paged_decode_attn_workspace_size(wl.B, wl.H_q, H, d, b, wl.max_context)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(wl.q)
+    lse = torch.empty((wl.B, wl.H_q), dtype=torch.float32, device=dev)
+
+    def run():
+        gp.gp_paged_decode_attn(wl.q, cache, wl.block_tables, wl.context_lens, wl.max_context,
+                                wl.sm_scale, out=out, lse=lse, workspace=ws)
+    for _ in range(3):
+        run()
+    e[2].record()
+    for _ in range(steps):
+        run()
+    e[3].record()
+    torch.cuda.synchronize()
+    ms = e[2].elapsed_time(e[3]) / steps
+    ctx = wl.context_lens.cpu().numpy().astype(np.int64)
+    pages = np.array([math.ceil(c / b) for c in ctx], dtype=np.int64)
+    kv = int(ctx.sum()) * H * (d + 2 * 2)
+    total = kv + int((2 * wl.H_q * d * 2 + wl.H_q * 4 + pages * 4 + 4).sum())
+    return dict(pages=int(used.numel()), quantize_ms=round(e[0].elapsed_time(e[1]), 4),
+                decode_ms=round(ms, 4), bytes_per_launch=total,
+                achieved_gbps=round(total / (ms * 1e-3) / 1e9, 1),
+                frac=round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
+
+
 def cpu_baseline(wl, path, budget_s, np):
     """The float64 oracle on a bounded sample: decode of whole requests, then the boundary pass
     of boundary requests, until the time budget is used. Returns GB/s on the same byte model."""
@@ -454,6 +506,12 @@ def main():
                 and pmc.get("overlap", 0) == int(path.overlap)):
             traffic = pmc.get("bytes_per_launch")
 
+    int4 = None
+    if args.int4 and not wl.mixed and wl.dtype == "bf16":
+        print("[bench] INT4 leg: demote every used page, time decode", file=sys.stderr, flush=True)
+        int4 = int4_leg(wl, gp, torch, np, args.steps)
+        int4["speedup_vs_bf16_decode"] = round(dec_ms / int4["decode_ms"], 3)
+
     boundary = None
     if path.R:
         bnd_ms = rows_ms["score_and_working_set"] + rows_ms["compact_or_grow"]
@@ -497,6 +555,7 @@ def main():
         "decode_frac_of_copy": round(achieved / copy_gbps, 4),
         "copy_gbps": round(copy_gbps, 1),
         "boundary": boundary,
+        "int4_decode": int4,
         "rows_ms": {k: round(v, 4) for k, v in rows_ms.items()},
         "event_ms_per_step": round(event_step_ms, 4),
         "bytes_per_step": by,

@@ -87,8 +87,11 @@ enum {
  *             read signed 4-bit codes (two's complement nibbles, the even index of a pair in
  *             the low nibble) times per-row IEEE half scales:
  *               k4       [num_pages, H_kv, page_size, head_dim / 2]  key rows packed along d
- *               v4       [num_pages, H_kv, head_dim, page_size / 2]  value rows of one
- *                        dimension packed along the token axis (values stay token-contiguous)
+ *               v4       [num_pages, H_kv, page_size / 4, head_dim, 2]  values packed along
+ *                        the token axis in blocks of 4 tokens: byte 0 of a dimension holds
+ *                        tokens 4Q, 4Q+1, byte 1 tokens 4Q+2, 4Q+3; within a block dimension
+ *                        j sits at position (j % 16) * (head_dim / 16) + j / 16, so that the
+ *                        head_dim / 16 dimensions one lane accumulates are adjacent
  *               k4_scale, v4_scale [num_pages, H_kv, page_size]      half bits, one per token
  *                        row and KV head.
  *             A byte value in an INT4 pool always decodes to finite codes (-8 .. 7), so only

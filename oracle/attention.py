@@ -22,7 +22,7 @@ two-token example (tests/golden/decode_tiny.txt).
 import numpy as np
 
 from .fp8 import e4m3_decode
-from .int4 import unpack_pairs
+from .int4 import unpack_pairs, unpack_values
 
 TAG_RELEASE, TAG_FP8, TAG_BF16, TAG_INT4 = 0, 1, 2, 3
 
@@ -33,8 +33,9 @@ def gather_request_kv(r, k_pool, v_pool, block_tables, context_lens, page_size,
     """Visible keys and values of request r as float64 arrays [H_kv, n_vis, d].
 
     k_pool is [num_pages, H_kv, b, d]; v_pool is [num_pages, H_kv, d, b] (token axis last).
-    INT4 pools: k4 [num_pages, H_kv, b, d/2] (packed along d), v4 [num_pages, H_kv, d, b/2]
-    (packed along tokens), k4_scale / v4_scale [num_pages, H_kv, b] half values.
+    INT4 pools: k4 [num_pages, H_kv, b, d/2] (packed along d), v4 [num_pages, H_kv, b/4, d, 2]
+    (four-token blocks packed along tokens, dimensions interleaved as in oracle.int4),
+    k4_scale / v4_scale [num_pages, H_kv, b] half values.
     Also returns the absolute slot index of every visible token.
     """
     n = int(context_lens[r])
@@ -61,7 +62,7 @@ def gather_request_kv(r, k_pool, v_pool, block_tables, context_lens, page_size,
         if i4.any():
             pg, of = pages[i4], offs[i4]
             kc = unpack_pairs(np.asarray(k4)[pg, :, of, :], axis=-1)              # [m, H, d]
-            vfull = unpack_pairs(np.asarray(v4)[pg], axis=-1)                     # [m, H, d, b]
+            vfull = unpack_values(np.asarray(v4)[pg])                             # [m, H, d, b]
             vc = vfull[np.arange(len(pg)), :, :, of]                              # [m, H, d]
             ks = np.asarray(k4_scale)[pg, :, of].astype(np.float64)
             vs = np.asarray(v4_scale)[pg, :, of].astype(np.float64)

@@ -11,10 +11,14 @@ less. The code of element x is round(x / s) (nearest integer, ties to even) clip
 Two signed 4-bit codes (two's complement nibbles) share one byte: the element with the even
 index along the packing axis sits in the low nibble, the next one in the high nibble.
 
-Packing axis of this library's layout: keys pack along the head dimension (a key row of d
-elements is d/2 bytes), values pack along the token axis, because values are stored with the
-token index contiguous inside a page (a value row of one dimension over b tokens is b/2 bytes).
-The scale belongs to the (token, KV head) row in both cases.
+Storage layout of this library (the scale belongs to the (token, KV head) row in both pools):
+* keys pack along the head dimension: a key row of d elements is d/2 bytes, in page order;
+* values pack along the token axis in blocks of four tokens: for tokens 4Q .. 4Q+3 and one
+  dimension j, byte 0 holds tokens 4Q and 4Q+1 and byte 1 tokens 4Q+2 and 4Q+3, and the d
+  two-byte groups of the block are stored in the interleaved dimension order
+  slot(j) = (j mod 16) * (d / 16) + floor(j / 16), so that the d/16 dimensions j = 16 i + c
+  (i = 0 .. d/16 - 1) of one residue c sit next to each other. A page of one KV head is the
+  array [b/4, d, 2] of bytes.
 
 Pinned by: hand-derived rows with their scales, codes and bytes (tests/golden/int4_rows.txt),
 including ties in the scale rounding, ties in the code rounding, a subnormal scale, a
@@ -22,7 +26,8 @@ subnormal scale that rounds down far enough to clip, the 2^-24 floor and a zero 
 rounding checked against torch's float64 -> float16 conversion on random magnitudes;
 invariants (|code| <= 7, a nonzero row reaches 7, with a normal scale every element within
 s/2 of code * s, elements beyond 7.5 s clipped to +-7); all 256 byte values unpacked against
-arithmetic shifts of int8 and packed back; a page packed along the right axes by brute force.
+arithmetic shifts of int8 and packed back; a page packed into the key rows and the value blocks
+by brute force, byte by byte.
 """
 import numpy as np
 
@@ -77,12 +82,40 @@ def unpack_pairs(packed, axis=-1) -> np.ndarray:
     return np.moveaxis(out.astype(np.int8), -1, axis)
 
 
+def value_slot(d):
+    """Storage slot of each dimension inside a four-token value block."""
+    j = np.arange(d)
+    return (j % 16) * (d // 16) + j // 16
+
+
+def pack_values(codes):
+    """Value codes [..., d, b] (dimension rows over b tokens) -> bytes [..., b/4, d, 2]."""
+    c = np.asarray(codes, dtype=np.int64)
+    d, b = c.shape[-2], c.shape[-1]
+    pairs = pack_pairs(c, axis=-1)                              # [..., d, b/2], tokens (2i, 2i+1)
+    blocks = pairs.reshape(c.shape[:-2] + (d, b // 4, 2))       # [..., d, Q, k]
+    blocks = np.moveaxis(blocks, -3, -2)                        # [..., Q, d, k]
+    out = np.empty_like(blocks)
+    out[..., value_slot(d), :] = blocks
+    return out
+
+
+def unpack_values(packed):
+    """Inverse of pack_values: bytes [..., b/4, d, 2] -> signed codes [..., d, b]."""
+    p = np.asarray(packed, dtype=np.uint8)
+    d = p.shape[-2]
+    blocks = p[..., value_slot(d), :]                           # [..., Q, d, k] natural order
+    blocks = np.moveaxis(blocks, -2, -3)                        # [..., d, Q, k]
+    pairs = blocks.reshape(blocks.shape[:-2] + (blocks.shape[-2] * 2,))
+    return unpack_pairs(pairs, axis=-1)
+
+
 def quantize_page_kv(k_page, v_page):
     """Quantise one page of keys [H, b, d] and values [H, d, b] (values token-contiguous).
 
-    Returns (k4 [H, b, d/2] uint8, v4 [H, d, b/2] uint8, k_scale [H, b], v_scale [H, b]):
+    Returns (k4 [H, b, d/2] uint8, v4 [H, b/4, d, 2] uint8, k_scale [H, b], v_scale [H, b]):
     the row of a value is one token over all d dimensions, so its scale runs over axis 1.
     """
     kc, ks = quantize_rows(k_page)                                # rows along d
     vc, vs = quantize_rows(np.swapaxes(np.asarray(v_page), 1, 2))  # [H, b, d] rows along d
-    return pack_pairs(kc, axis=-1), pack_pairs(np.swapaxes(vc, 1, 2), axis=-1), ks, vs
+    return pack_pairs(kc, axis=-1), pack_values(np.swapaxes(vc, 1, 2)), ks, vs

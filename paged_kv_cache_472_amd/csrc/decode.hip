@@ -22,9 +22,12 @@
 // Mixed-precision caches choose the page kind per tile (a uniform branch): released pages are
 // skipped, fp8 codes are widened exactly to bf16 and their row scales applied to the logits and
 // the probability weights, and INT4 pages (PASK App. B.5) are contracted in half precision:
-// their nibbles become exact half values through the mantissa of 1024.0, the key product uses a
-// half copy of the query laid out in the order the nibbles unpack in, and the value product
-// takes each lane's four tokens in the order (0, 2, 1, 3) on both operands.
+// their nibbles become exact half values through the mantissa of 1024.0. An INT4 tile is five
+// loads per lane: the lane's quarter of a key row (the key product pairs it with a half copy of
+// the query holding the same dimensions, in the order the nibbles unpack in), the lane's
+// head_dim/16 value dimensions of its four tokens (adjacent in the stored value block), and
+// the 16-byte chunks of key and value scales around its tokens. The value product takes the
+// four tokens in the order (0, 2, 1, 3) on both operands.
 #include "common.h"
 
 #include <algorithm>
@@ -87,10 +90,11 @@ struct TileRaw<D, KIND_BF16> {
 
 template <int D>
 struct TileRaw<D, KIND_MIXED> {
-  u32x4_t k[D / 32];  // bf16: 8 elements; fp8: 8 codes in .xy; INT4: 8 codes in .x
-  u32x2_t v[D / 16];  // bf16: 4 elements; fp8: 4 codes in .x; INT4: 4 codes in .x (low half)
+  u32x4_t k[D / 32];  // bf16: 8 elements; fp8: 8 codes in .xy; INT4: k[0] holds D/4 codes
+  u32x2_t v[D / 16];  // bf16: 4 elements; fp8: 4 codes in .x; INT4: v[0..D/64) hold 2 bytes
+                      // (4 tokens) for each of D/16 dimensions
   f32x4_t ks, vs;     // per-token scales of the 4 tokens this lane owns (fp8: fp32 values;
-                      // INT4: four half bit patterns in components 0 and 1)
+                      // INT4: the 8 half scales of the aligned 8-token group around them)
 };
 
 __device__ __forceinline__ int sanitize_ctx(const DecodeParams& p, int r) {
@@ -112,20 +116,20 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
     const size_t kv_base = ((size_t)pg * p.H_kv + h) * (size_t)b * D;
     const size_t sb = ((size_t)pg * p.H_kv + h) * b + off + 4 * g4;
     if (tag == GP_TAG_INT4) {
-      // key row (off + n16) packed along d: the 8 codes of step kk are 4 bytes
-      const uint8_t* kr = p.k4 + kv_base / 2 + (size_t)(off + n16) * (D / 2) + 4 * g4;
+      // key row (off + n16): this lane's dimensions [g4 D/4, (g4 + 1) D/4) are D/8 bytes
+      const uint8_t* kr = p.k4 + kv_base / 2 + (size_t)(off + n16) * (D / 2) + g4 * (D / 8);
+      if constexpr (D == 128)
+        t.k[0] = *reinterpret_cast<const u32x4_t*>(kr);
+      else
+        *reinterpret_cast<u32x2_t*>(&t.k[0]) = *reinterpret_cast<const u32x2_t*>(kr);
+      // value block of tokens off + 4 g4 .. + 3: dimensions 16 i + n16 are D/8 adjacent bytes
+      const uint8_t* vr = p.v4 + kv_base / 2 + (size_t)((off >> 2) + g4) * (2 * D) + n16 * (D / 8);
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk)
-        t.k[kk] = u32x4_t{*reinterpret_cast<const uint32_t*>(kr + 16 * kk), 0u, 0u, 0u};
-      // value row n16 (+16 nb) packed along tokens: this lane's 4 tokens are 2 bytes
-      const uint8_t* vr = p.v4 + kv_base / 2 + (size_t)n16 * (b / 2) + (off + 4 * g4) / 2;
-#pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb)
-        t.v[nb] = u32x2_t{(uint32_t)*reinterpret_cast<const uint16_t*>(vr + (size_t)8 * nb * b), 0u};
-      const u32x2_t ksr = *reinterpret_cast<const u32x2_t*>(p.k4_scale + sb);
-      const u32x2_t vsr = *reinterpret_cast<const u32x2_t*>(p.v4_scale + sb);
-      t.ks = f32x4_t{__uint_as_float(ksr.x), __uint_as_float(ksr.y), 0.f, 0.f};
-      t.vs = f32x4_t{__uint_as_float(vsr.x), __uint_as_float(vsr.y), 0.f, 0.f};
+      for (int i = 0; i < D / 64; ++i) t.v[i] = *reinterpret_cast<const u32x2_t*>(vr + 8 * i);
+      // the 16-byte aligned group of 8 scales holding this lane's 4 tokens
+      const size_t sc = ((size_t)pg * p.H_kv + h) * b + ((off + 4 * g4) & ~7);
+      t.ks = *reinterpret_cast<const f32x4_t*>(p.k4_scale + sc);
+      t.vs = *reinterpret_cast<const f32x4_t*>(p.v4_scale + sc);
       return;
     }
     if (tag == GP_TAG_FP8) {
@@ -195,8 +199,11 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
     fp8 = (code & 3) == GP_TAG_FP8;
     int4 = (code & 3) == GP_TAG_INT4;
     if (int4) {
-      const uint32_t k01 = __float_as_uint(cur.ks[0]), k23 = __float_as_uint(cur.ks[1]);
-      const uint32_t v01 = __float_as_uint(cur.vs[0]), v23 = __float_as_uint(cur.vs[1]);
+      const bool up = g4 & 1;  // this lane's tokens are the upper half of the 8-scale group
+      const uint32_t k01 = __float_as_uint(up ? cur.ks[2] : cur.ks[0]);
+      const uint32_t k23 = __float_as_uint(up ? cur.ks[3] : cur.ks[1]);
+      const uint32_t v01 = __float_as_uint(up ? cur.vs[2] : cur.vs[0]);
+      const uint32_t v23 = __float_as_uint(up ? cur.vs[3] : cur.vs[1]);
       ks[0] = gp::half_lo(k01); ks[1] = gp::half_hi(k01); ks[2] = gp::half_lo(k23); ks[3] = gp::half_hi(k23);
       vs[0] = gp::half_lo(v01); vs[1] = gp::half_hi(v01); vs[2] = gp::half_lo(v23); vs[3] = gp::half_hi(v23);
     } else {
@@ -214,7 +221,7 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
   } else if (int4) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
-      sacc = gp::mfma_f16_16x16x32(gp::int4x8_to_f16x8(cur.k[kk].x), qh[kk], sacc);
+      sacc = gp::mfma_f16_16x16x32(gp::int4x8_to_f16x8(cur.k[0][kk]), qh[kk], sacc);
   } else {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
@@ -289,8 +296,11 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
         const f16x2_t p13 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(pw[1], pw[3]));
         const f16x4_t ph = f16x4_t{p02.x, p02.y, p13.x, p13.y};
 #pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb)
-          st.acc[nb] = gp::mfma_f16_16x16x16(ph, gp::int4x4_to_f16x4(cur.v[nb].x), st.acc[nb]);
+        for (int nb = 0; nb < D / 16; ++nb) {
+          const uint32_t word = cur.v[nb / 4][(nb / 2) % 2];  // dimension 16 nb + n16: 2 bytes
+          const uint32_t grp = (nb % 2) ? (word >> 16) : word;
+          st.acc[nb] = gp::mfma_f16_16x16x16(ph, gp::int4x4_to_f16x4(grp), st.acc[nb]);
+        }
         return;
       }
     }
@@ -425,12 +435,14 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
       for (int kk = 0; kk < D / 32; ++kk)
         qf[kk] = (n16 < G) ? *reinterpret_cast<const u32x4_t*>(qr + 32 * kk) : u32x4_t{0u, 0u, 0u, 0u};
     }
-    // half copy of the query for INT4 pages, in the element order their codes unpack in
+    // half copy of the query for INT4 pages: step kk of lane (n16, g4) holds dimensions
+    // g4 D/4 + 8 kk + (0, 4, 1, 5, 2, 6, 3, 7), the order the lane's key codes unpack in
     f16x8_t qh[KIND == KIND_MIXED ? D / 32 : 1];
     if constexpr (KIND == KIND_MIXED) {
+      const uint16_t* qr = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)r * p.H_q + hq0 + n16) * D + (D / 4) * g4;
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
-        const u32x4_t a = qf[kk];
+        const u32x4_t a = (n16 < G) ? *reinterpret_cast<const u32x4_t*>(qr + 8 * kk) : u32x4_t{0u, 0u, 0u, 0u};
         const float e0 = __uint_as_float(a.x << 16), e1 = __uint_as_float(a.x & 0xffff0000u);
         const float e2 = __uint_as_float(a.y << 16), e3 = __uint_as_float(a.y & 0xffff0000u);
         const float e4 = __uint_as_float(a.z << 16), e5 = __uint_as_float(a.z & 0xffff0000u);

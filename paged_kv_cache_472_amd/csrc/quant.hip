@@ -4,8 +4,10 @@
 // row's head_dim elements (a contiguous key row, and the value row gathered from the
 // token-contiguous value block: consecutive threads read consecutive tokens), takes the largest
 // magnitude, derives the half scale and writes the codes. Key codes pack along d (4 bytes per
-// 8 elements); value codes pack along the token axis, so the even-token thread of each pair
-// gathers its neighbour's codes with a lane shuffle and writes the shared bytes. The page tag
+// 8 elements); value codes pack along the token axis in four-token blocks with the dimensions
+// interleaved (the layout the decode kernel reads with one 16-byte load per lane), so the
+// even-token thread of each pair gathers its neighbour's codes with a lane shuffle and writes
+// the shared bytes. The page tag
 // changes last, after a barrier, so a reader of the tag never sees a half-written page.
 //
 // Exactness of the scale and codes against a float64 evaluation: the inputs are bf16 (8
@@ -95,12 +97,15 @@ __global__ __launch_bounds__(QT_THREADS) void quantize_pages_kernel(QuantParams 
     const _Float16 sh = row_scale(amax);
     const float s = (float)sh;
     if (live) p.v4_scale[head * b + t] = __builtin_bit_cast(uint16_t, sh);
-    // rows are b-aligned and b is even, so a token pair never straddles a head or a pass
-    uint8_t* v4h = p.v4 + head * (size_t)D * (b / 2) + t / 2;
+    // rows are b-aligned and b is even, so a token pair never straddles a head or a pass.
+    // Block of tokens 4Q .. 4Q+3: dimension j's two bytes sit at slot (j % 16) * (D / 16) + j / 16,
+    // byte (t % 4) / 2 of the slot holds tokens t & ~1 (low nibble) and t | 1 (high nibble).
+    uint8_t* v4h = p.v4 + head * (size_t)D * (b / 2) + (size_t)(t / 4) * (2 * D) + (t % 4) / 2;
     for (int d = 0; d < D; ++d) {
       const uint32_t c = live ? code_of(gp::bf16_bits_to_f32(vr[(size_t)d * b]), s) : 0u;
       const uint32_t other = __shfl_xor(c, 1, GP_WAVE);
-      if (live && (t & 1) == 0) v4h[(size_t)d * (b / 2)] = (uint8_t)(c | (other << 4));
+      const int slot = (d % 16) * (D / 16) + d / 16;
+      if (live && (t & 1) == 0) v4h[2 * slot] = (uint8_t)(c | (other << 4));
     }
   }
   __syncthreads();

@@ -31,7 +31,7 @@ def _attach_mixed_pools(k, v, b, tags):
         v_scale=torch.ones((P, H, b), dtype=torch.float32, device=DEV),
         page_tag=torch.as_tensor(tags, dtype=torch.uint8, device=DEV),
         k4=torch.full((P, H, b, D // 2), K_SENTINEL, dtype=torch.uint8, device=DEV),
-        v4=torch.full((P, H, D, b // 2), V_SENTINEL, dtype=torch.uint8, device=DEV),
+        v4=torch.full((P, H, b // 4, D, 2), V_SENTINEL, dtype=torch.uint8, device=DEV),
         k4_scale=torch.full((P, H, b), S_SENTINEL, dtype=torch.int16, device=DEV).view(torch.float16),
         v4_scale=torch.full((P, H, b), S_SENTINEL, dtype=torch.int16, device=DEV).view(torch.float16))
 

@@ -156,7 +156,9 @@ def test_released_page_equals_deleting_its_tokens(int4_frac):
             elif tags[pg] == 3:
                 kb = npy(wl.k4)[pg, :, off, :]                       # [H, d/2]
                 kc = np.stack([_nibble(kb, False), _nibble(kb, True)], -1).reshape(wl.H_kv, wl.d)
-                vc = _nibble(npy(wl.v4)[pg, :, :, off // 2], off % 2 == 1)   # [H, d]
+                slot = (np.arange(wl.d) % 16) * (wl.d // 16) + np.arange(wl.d) // 16
+                vb = npy(wl.v4)[pg, :, off // 4][:, slot, (off % 4) // 2]      # [H, d]
+                vc = _nibble(vb, off % 2 == 1)
                 ks.append(kc * npy(wl.k4_scale)[pg, :, off, None].astype(np.float64))
                 vs.append(vc * npy(wl.v4_scale)[pg, :, off, None].astype(np.float64))
             else:
@@ -181,8 +183,10 @@ def test_int4_page_equals_float_page_of_its_values():
     for pg in np.nonzero(tags == 3)[0]:
         kb = npy(wl.k4)[pg]                                            # [H, b, d/2]
         kc = np.stack([_nibble(kb, False), _nibble(kb, True)], -1).reshape(kp.shape[1:])
-        vb = npy(wl.v4)[pg]                                            # [H, d, b/2]
-        vc = np.stack([_nibble(vb, False), _nibble(vb, True)], -1).reshape(vp.shape[1:])
+        slot = (np.arange(wl.d) % 16) * (wl.d // 16) + np.arange(wl.d) // 16
+        vb = npy(wl.v4)[pg][:, :, slot, :]                             # [H, b/4, d, 2]
+        vc = np.stack([_nibble(vb, False), _nibble(vb, True)], -1)     # [H, Q, d, k, 2]
+        vc = vc.transpose(0, 2, 1, 3, 4).reshape(vp.shape[1:])         # [H, d, b]
         kp[pg] = kc * npy(wl.k4_scale)[pg][..., None].astype(np.float64)
         vp[pg] = vc * npy(wl.v4_scale)[pg][:, None, :].astype(np.float64)
     float_tags = np.where(tags == 3, 2, tags).astype(np.uint8)

@@ -81,19 +81,33 @@ def test_every_byte_unpacks_like_arithmetic_shifts():
     assert np.array_equal(int4.pack_pairs(got, axis=-1)[:, 0], b)
 
 
+def test_value_slots_hand_derived():
+    """Interleaved dimension order of a value block: dims 16 i + c of one residue c adjacent."""
+    slot = int4.value_slot(32)
+    assert [slot[j] for j in (0, 16, 1, 17, 2, 15, 31)] == [0, 1, 2, 3, 4, 30, 31]
+    slot = int4.value_slot(64)
+    assert [slot[j] for j in (0, 16, 32, 48, 1, 63)] == [0, 1, 2, 3, 4, 63]
+    assert sorted(int4.value_slot(128).tolist()) == list(range(128))
+
+
 def test_page_layout_by_brute_force():
-    """Keys pack along d, values along tokens; every (token, head) row owns one scale."""
+    """Keys pack along d, values in four-token blocks; every (token, head) row owns one scale."""
     rng = np.random.default_rng(7)
-    H, b, d = 2, 4, 6
+    H, b, d = 2, 8, 32
     k = rng.standard_normal((H, b, d))
     v = rng.standard_normal((H, d, b)) * 3
     k4, v4, ks, vs = int4.quantize_page_kv(k, v)
-    assert k4.shape == (H, b, d // 2) and v4.shape == (H, d, b // 2)
+    assert k4.shape == (H, b, d // 2) and v4.shape == (H, b // 4, d, 2)
+    slot = {j: (j % 16) * (d // 16) + j // 16 for j in range(d)}
     for h in range(H):
         for t in range(b):
             krow, vrow = k[h, t, :], v[h, :, t]
-            for row, sc, get in ((krow, ks[h, t], lambda j: (k4[h, t, j // 2] >> 4 * (j % 2)) & 15),
-                                 (vrow, vs[h, t], lambda j: (v4[h, j, t // 2] >> 4 * (t % 2)) & 15)):
+            getters = (
+                (krow, ks[h, t], lambda j: (k4[h, t, j // 2] >> 4 * (j % 2)) & 15),
+                (vrow, vs[h, t],
+                 lambda j: (v4[h, t // 4, slot[j], (t % 4) // 2] >> 4 * (t % 2)) & 15),
+            )
+            for row, sc, get in getters:
                 a = max(abs(x) for x in row)
                 s_ref = float(np.float16(a / 7))
                 assert sc == s_ref
@@ -101,3 +115,6 @@ def test_page_layout_by_brute_force():
                     code = int(round(row[j] / s_ref))         # no exact ties in random data
                     code = max(-7, min(7, code))
                     assert int(get(j)) == code & 15
+    back = int4.unpack_values(v4)
+    assert back.shape == (H, d, b)
+    assert np.array_equal(int4.pack_values(back), v4)

@@ -10,8 +10,9 @@ Storage layout produced here (the layout the library consumes):
   OCP E4M3FN codes, ``k_scale / v_scale [num_pages, H_kv, b]`` one fp32 scale per token row
   and KV head, and ``page_tag [num_pages]`` (0 released, 1 fp8, 2 bf16, 3 int4).
 * INT4 pages (PASK B.5, present in every mixed workload): ``k4 [num_pages, H_kv, b, d/2]``
-  (two signed nibbles per byte along d, even index low), ``v4 [num_pages, H_kv, d, b/2]``
-  (packed along the token axis), ``k4_scale / v4_scale [num_pages, H_kv, b]`` float16. With
+  (two signed nibbles per byte along d, even index low), ``v4 [num_pages, H_kv, b/4, d, 2]``
+  (four-token blocks packed along the token axis, dimensions in the interleaved order
+  (j mod 16) * (d/16) + j // 16), ``k4_scale / v4_scale [num_pages, H_kv, b]`` float16. With
   ``int4_frac > 0`` that share of the bf16 pages becomes INT4 pages holding random codes in
   [-7, 7] and random half scales in [0.25, 0.6); otherwise the INT4 pools are poison only.
 * ``block_tables [B, max_pages]`` int32 (unused entries -1), ``n_pages [B]`` allocated pages,
@@ -342,7 +343,7 @@ def make_workload(name: str, scale: str = "full", device="cpu", seed_offset: int
     if mixed:
         # INT4 pools: poison (code -8 in both nibbles, NaN scales) except on INT4 pages
         k4 = torch.full((num_pages, H_kv, b, d // 2), 0x88, dtype=torch.uint8, device=device)
-        v4 = torch.full((num_pages, H_kv, d, b // 2), 0x88, dtype=torch.uint8, device=device)
+        v4 = torch.full((num_pages, H_kv, b // 4, d, 2), 0x88, dtype=torch.uint8, device=device)
         k4_scale = torch.full((num_pages, H_kv, b), float("nan"), dtype=torch.float16, device=device)
         v4_scale = torch.full_like(k4_scale, float("nan"))
         if int4_frac > 0:
@@ -364,7 +365,7 @@ def make_workload(name: str, scale: str = "full", device="cpu", seed_offset: int
             n4 = len(pick)
             idx = torch.as_tensor(pick, dtype=torch.long, device=device)
             k4[idx] = codes((n4, H_kv, b, d // 2))
-            v4[idx] = codes((n4, H_kv, d, b // 2))
+            v4[idx] = codes((n4, H_kv, b // 4, d, 2))
             k4_scale[idx] = scales((n4, H_kv, b))
             v4_scale[idx] = scales((n4, H_kv, b))
             page_tag[pick] = TAG_INT4
@@ -392,9 +393,12 @@ def make_workload(name: str, scale: str = "full", device="cpu", seed_offset: int
                 k4[last, :, t0:, :] = 0x88
                 k4_scale[last, :, t0:] = float("nan")
                 v4_scale[last, :, t0:] = float("nan")
-                if t0 % 2:  # the byte shared with the last live token: poison its high nibble
-                    v4[last, :, :, t0 // 2] = (v4[last, :, :, t0 // 2] & 0x0F) | 0x80
-                v4[last, :, :, (t0 + 1) // 2:] = 0x88
+                for t in range(t0, b):  # nibble of token t in its four-token block
+                    blk = v4[last, :, t // 4, :, (t % 4) // 2]
+                    if t % 2:
+                        v4[last, :, t // 4, :, (t % 4) // 2] = (blk & 0x0F) | 0x80
+                    else:
+                        v4[last, :, t // 4, :, (t % 4) // 2] = (blk & 0xF0) | 0x08
 
     qstate = torch.full((NUM_SLOTS, 2, H_q, d), float("nan"), dtype=torch.float32, device=device)
 
