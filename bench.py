@@ -10,13 +10,16 @@ tables, lengths, page counts, refcounts, free stack) with one device copy, insid
 region; K/V pages are left as the previous step's compaction wrote them (still valid tokens, same
 amount of work).
 
-With --overlap 1 the step runs as GrowPage overlaps compaction with decoding: after
-the summary update, the boundary requests are decoded and then scored and compressed-or-grown on a
-second stream while the main stream decodes the other requests (their lengths masked to zero for
-it, so no page the boundary pass rewrites is read); the main stream waits for the second before
-the step ends. Every request still sees update -> decode -> boundary pass in that order. It is
-not the default: the decode sizes its grid to occupy every compute unit, so kernels on the second
-stream wait for it and the overlapped step is slower than the single-stream one.
+By default (--overlap 1) the step overlaps the boundary pass with decoding, as GrowPage does
+(App. E.3). On the main stream the boundary requests are decoded first (a small call on copies of
+their block-table rows and lengths), then the other requests (their lengths masked to zero, so
+none of the pages the boundary pass rewrites is read; their summary update fused into the call,
+whose grid leaves --reserve-cus compute units free). A second stream meanwhile updates the
+boundary requests' summaries, scores them and plans their compress-or-grow (decisions, page
+allocation, kept tokens: bookkeeping only); the planned K/V movement runs on the main stream
+after the decode, with the whole GPU. The boundary requests' outputs stay in their own buffers.
+Every request still sees update -> decode -> boundary pass in that order. --overlap 0 runs the
+same rows one after another on one stream.
 
 Prints one JSON line. `value` is the step's algorithmic HBM bytes divided by the step time;
 `roofline` is the main decode call (its two kernels) against the 8 TB/s HBM peak, timed with HIP
@@ -61,7 +64,10 @@ def parse():
     ap.add_argument("--config", default="2", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's timed sample (0 disables the cpu_baseline leg)")
-    ap.add_argument("--overlap", type=int, default=0,
+    ap.add_argument("--reserve-cus", type=int, default=32,
+                    help="with --overlap 1: compute units the main decode leaves free for the "
+                         "boundary pass on the second stream (its workgroup cap)")
+    ap.add_argument("--overlap", type=int, default=1,
                     help="1: the boundary requests' decode and boundary pass run on a second stream "
                          "beside the decode of the other requests; 0: everything on one stream")
     ap.add_argument("--int4", type=int, default=1,
@@ -80,7 +86,7 @@ def file_sha(path):
 class Path:
     """Preallocated buffers and the per-step launch sequence of one workload."""
 
-    def __init__(self, wl, gp, torch, overlap=False):
+    def __init__(self, wl, gp, torch, overlap=False, reserve_cus=0):
         self.wl, self.gp, self.torch = wl, gp, torch
         dev = wl.q.device
         i32 = torch.int32
@@ -111,6 +117,9 @@ class Path:
         n = gp.gp_paged_decode_attn_workspace_size(B, H_q, H_kv, d, wl.page_size, wl.max_context)
         self.dws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
         self.fresh0 = torch.zeros(B, dtype=torch.uint8, device=dev)
+        self.upd = dict(q_pre=wl.q, slot_ids=wl.slot_ids, fresh=self.fresh0, qstate=wl.qstate,
+                        beta_s=wl.beta_s, beta_l=wl.beta_l)
+        self.max_wg = 0
         if self.R:
             req = wl.req_idx.cpu().tolist()
             ctx = wl.context_lens.cpu().tolist()
@@ -140,6 +149,19 @@ class Path:
             self.lse_b = torch.empty((R, H_q), dtype=torch.float32, device=dev)
             n = gp.gp_paged_decode_attn_workspace_size(R, H_q, H_kv, d, wl.page_size, wl.max_context)
             self.dws_b = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+            # the main decode updates the summaries of the other requests; the boundary requests'
+            # own decode (second stream) updates theirs before their scores read them
+            slot_main = wl.slot_ids.clone()
+            slot_main.index_fill_(0, self.req_l, -1)
+            self.upd_main = dict(self.upd, slot_ids=slot_main)
+            # the second stream updates the boundary requests' summaries (slots of the others
+            # masked) before scoring them
+            slot_b = torch.full_like(wl.slot_ids, -1)
+            slot_b[self.req_l] = wl.slot_ids[self.req_l]
+            self.upd_b = dict(slot_ids_full=slot_b)
+            self.ev_dec_b = torch.cuda.Event()
+            cus = torch.cuda.get_device_properties(dev).multi_processor_count
+            self.max_wg = max(1, cus - reserve_cus) if reserve_cus > 0 else 0
             self.ev_a = torch.cuda.Event()
             self.ev_b = torch.cuda.Event()
 
@@ -158,12 +180,10 @@ class Path:
         rec(0)
         self.meta.copy_(self.meta0)
         rec(1)
-        gp.gp_update_query_summaries(wl.q, wl.slot_ids, self.fresh0, wl.qstate, wl.beta_s,
-                                     wl.beta_l)
         rec(2)
-        gp.gp_paged_decode_attn(wl.q, self.cache, wl.block_tables, wl.context_lens,
-                                wl.max_context, wl.sm_scale, out=self.out, lse=self.lse,
-                                workspace=self.dws)
+        gp.gp_paged_decode_attn_ex(wl.q, self.cache, wl.block_tables, wl.context_lens,
+                                   wl.max_context, wl.sm_scale, summaries=self.upd, out=self.out,
+                                   lse=self.lse, workspace=self.dws)
         rec(3)
         if self.R:
             gp.gp_score_and_working_set(wl.q, wl.qstate, wl.slot_ids, wl.req_idx, self.cache,
@@ -179,11 +199,18 @@ class Path:
                                   kept_idx=self.kept, workspace=self.cws)
         rec(5)
 
-    # events of an overlapped step: main stream 0 start, 1 restored, 2 summaries, 3 main decode,
-    # 8 joined; second stream 4 start, 5 boundary decode, 6 score, 7 compress-or-grow
+    # events of an overlapped step: main stream 0 start, 1 restored, 2 boundary requests decoded,
+    # 3 other requests decoded, 8 compaction moved (end); second stream 4 start, 5 summaries of
+    # the boundary requests, 6 scored, 7 compress-or-grow planned
     NEV_OVERLAP = 9
 
     def step_overlap(self, ev=None):
+        """GrowPage's overlap of the boundary pass with decoding. The boundary requests are
+        decoded first on the main stream (a small call, from copies of their block-table rows
+        and lengths); the second stream meanwhile updates their summaries, scores them and plans
+        their compress-or-grow (decisions, pages, kept tokens: bookkeeping only), while the main
+        stream decodes the other requests. The planned K/V movement then runs on the main stream
+        once the other requests are decoded, with the whole GPU to itself."""
         wl, gp, torch = self.wl, self.gp, self.torch
         main = torch.cuda.current_stream()
         sb = self.stream_b
@@ -191,19 +218,27 @@ class Path:
         rec(0, main)
         self.meta.copy_(self.meta0)
         rec(1, main)
-        gp.gp_update_query_summaries(wl.q, wl.slot_ids, self.fresh0, wl.qstate, wl.beta_s,
-                                     wl.beta_l)
-        rec(2, main)
+        torch.index_select(wl.q, 0, self.req_l, out=self.q_b)
+        torch.index_select(wl.block_tables, 0, self.req_l, out=self.bt_b)
+        torch.index_select(wl.context_lens, 0, self.req_l, out=self.ctx_b)
         self.ev_a.record(main)
+        gp.gp_paged_decode_attn_ex(self.q_b, self.cache, self.bt_b, self.ctx_b, wl.max_context,
+                                   wl.sm_scale, out=self.out_b, lse=self.lse_b,
+                                   workspace=self.dws_b)
+        rec(2, main)
+        # the other requests (boundary requests masked to length 0: none of their pages or
+        # block-table rows is read); enqueued before the second stream's work so that its launch
+        # does not wait on the host
+        gp.gp_paged_decode_attn_ex(wl.q, self.cache, wl.block_tables, self.ctx_main,
+                                   wl.max_context, wl.sm_scale, summaries=self.upd_main,
+                                   max_workgroups=self.max_wg, out=self.out, lse=self.lse,
+                                   workspace=self.dws)
+        rec(3, main)
         with torch.cuda.stream(sb):
             sb.wait_event(self.ev_a)
             rec(4, sb)
-            torch.index_select(wl.q, 0, self.req_l, out=self.q_b)
-            torch.index_select(wl.block_tables, 0, self.req_l, out=self.bt_b)
-            torch.index_select(wl.context_lens, 0, self.req_l, out=self.ctx_b)
-            gp.gp_paged_decode_attn(self.q_b, self.cache, self.bt_b, self.ctx_b, wl.max_context,
-                                    wl.sm_scale, out=self.out_b, lse=self.lse_b,
-                                    workspace=self.dws_b)
+            gp.gp_update_query_summaries(wl.q, self.upd_b["slot_ids_full"], self.fresh0,
+                                         wl.qstate, wl.beta_s, wl.beta_l)
             rec(5, sb)
             gp.gp_score_and_working_set(wl.q, wl.qstate, wl.slot_ids, wl.req_idx, self.cache,
                                         wl.block_tables, wl.context_lens, wl.positions,
@@ -211,22 +246,20 @@ class Path:
                                         a_short=self.a_s, a_long=self.a_l, ws_counts=self.wsc,
                                         n_cand=self.ncand, workspace=self.sws)
             rec(6, sb)
-            gp.gp_compact_or_grow(wl.req_idx, self.a_s, self.a_l, self.wsc, self.ncand, wl.tau,
-                                  wl.k_loc, 0, self.cache, wl.block_tables, wl.n_pages,
-                                  wl.context_lens, wl.refcount, wl.free_stack, wl.free_top,
-                                  policies=self.policies, decision=self.dec,
-                                  kept_idx=self.kept, workspace=self.cws)
+            self._compact(gp.growpage.PHASE_PLAN)
             rec(7, sb)
             self.ev_b.record(sb)
-        # the other requests (boundary requests masked to length 0: none of their pages is read)
-        gp.gp_paged_decode_attn(wl.q, self.cache, wl.block_tables, self.ctx_main,
-                                wl.max_context, wl.sm_scale, out=self.out, lse=self.lse,
-                                workspace=self.dws)
-        rec(3, main)
         main.wait_event(self.ev_b)
-        self.out.index_copy_(0, self.req_l, self.out_b)
-        self.lse.index_copy_(0, self.req_l, self.lse_b)
+        self._compact(gp.growpage.PHASE_MOVE)
         rec(8, main)
+
+    def _compact(self, phases):
+        wl, gp = self.wl, self.gp
+        gp.gp_compact_or_grow(wl.req_idx, self.a_s, self.a_l, self.wsc, self.ncand, wl.tau,
+                              wl.k_loc, 0, self.cache, wl.block_tables, wl.n_pages,
+                              wl.context_lens, wl.refcount, wl.free_stack, wl.free_top,
+                              policies=self.policies, decision=self.dec, kept_idx=self.kept,
+                              workspace=self.cws, phases=phases)
 
 
 def algorithmic_bytes(wl, path, np):
@@ -251,9 +284,10 @@ def algorithmic_bytes(wl, path, np):
     pages_r = np.array([math.ceil(c / b) for c in ctx], dtype=np.int64)
     per_req = kv_r + 2 * H_q * d * es + H_q * 4 + pages_r * 4 + 4
     main = [r for r in range(B) if r not in req] if path.overlap else list(range(B))
+    summ_r = H_q * d * (es + 4 * 4) + 5   # q_pre read, both fp32 summaries read and written
     out = dict(decode=int(per_req.sum()), decode_kv=int(kv_r.sum()),
                decode_main=int(per_req[main].sum()), decode_main_kv=int(kv_r[main].sum()),
-               summaries=B * H_q * d * (es + 4 * 4) + B * 5, score=0, compact=0)
+               summaries=B * summ_r, summaries_main=len(main) * summ_r, score=0, compact=0)
     for r in req:
         c = max(0, (math.ceil(int(ctx[r]) / b) - 1) * b)
         out["score"] += c * H_kv * d * es + 4 * H_kv * c * 4
@@ -439,7 +473,7 @@ def main():
     dev = "cuda:0"
     print(f"[bench] building workload {args.config} on {dev}", file=sys.stderr, flush=True)
     wl = make_workload(args.config, "full", device=dev)
-    path = Path(wl, gp, torch, overlap=args.overlap)
+    path = Path(wl, gp, torch, overlap=args.overlap, reserve_cus=args.reserve_cus)
     path.build_state()
     torch.cuda.synchronize()
     ctx_before = wl.context_lens.cpu().numpy().copy()
@@ -463,12 +497,13 @@ def main():
     def avg_ms(a, z):
         return sum(events[k][a].elapsed_time(events[k][z]) for k in range(args.steps)) / args.steps
 
-    rows_ms = dict(restore=avg_ms(0, 1), update_query_summaries=avg_ms(1, 2),
-                   paged_decode_attn=avg_ms(2, 3))
+    # the summary update runs inside the decode call (events 1 and 2 are adjacent)
+    rows_ms = dict(restore=avg_ms(0, 1), paged_decode_attn_with_summaries=avg_ms(2, 3))
     if path.overlap:
-        rows_ms["boundary_requests_decode"] = avg_ms(4, 5)
-        rows_ms["score_and_working_set"] = avg_ms(5, 6)
-        rows_ms["compact_or_grow"] = avg_ms(6, 7)
+        rows_ms = dict(restore=avg_ms(0, 1), boundary_requests_decode=avg_ms(1, 2),
+                       paged_decode_attn_with_summaries=avg_ms(2, 3),
+                       boundary_summaries=avg_ms(4, 5), score_and_working_set=avg_ms(5, 6),
+                       compact_or_grow_plan=avg_ms(6, 7), compact_or_grow_move_incl_wait=avg_ms(3, 8))
         event_step_ms = avg_ms(0, 8)
     else:
         if path.R:
@@ -476,12 +511,32 @@ def main():
             rows_ms["compact_or_grow"] = avg_ms(4, 5)
         event_step_ms = avg_ms(0, 5)
 
+    single = None
+    if path.overlap:
+        # the same rows one after another on one stream, for reference
+        print(f"[bench] single-stream reference, {args.steps} steps", file=sys.stderr, flush=True)
+        ev1 = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+        for _ in range(2):
+            path.step()
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        for k in range(args.steps):
+            path.step(ev1[k])
+        torch.cuda.synchronize()
+        ms1 = (time.perf_counter() - s0) * 1e3 / args.steps
+        a1 = lambda i, j: sum(ev1[k][i].elapsed_time(ev1[k][j]) for k in range(args.steps)) / args.steps  # noqa: E731
+        single = dict(ms_per_step=round(ms1, 4), decode_ms=round(a1(2, 3), 4),
+                      score_us=round(a1(3, 4) * 1e3, 1), compact_us=round(a1(4, 5) * 1e3, 1),
+                      boundary_us_per_request=round((a1(3, 5)) * 1e3 / path.R, 1))
+
     by = algorithmic_bytes(wl, path, np)
     by["compact"] = moved_bytes(wl, path, ctx_before, np)
     step_bytes = by["decode"] + by["summaries"] + by["score"] + by["compact"]
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    dec_ms = rows_ms["paged_decode_attn"]
-    achieved = by["decode_main"] / (dec_ms * 1e-3) / 1e9
+    if single is not None:
+        single["value"] = round(step_bytes / (single["ms_per_step"] * 1e-3) / 1e9, 2)
+    dec_ms = rows_ms["paged_decode_attn_with_summaries"]
+    achieved = (by["decode_main"] + by["summaries_main"]) / (dec_ms * 1e-3) / 1e9
 
     # plain device copy of known size: the practical HBM ceiling on this machine
     nbytes = int(args.copy_probe_gib * (1 << 30))
@@ -503,7 +558,8 @@ def main():
         with open(PMC_FILE) as fh:
             pmc = json.load(fh)
         if (pmc.get("decode_src_sha") == file_sha(DECODE_SRC) and pmc.get("config") == args.config
-                and pmc.get("overlap", 0) == int(path.overlap)):
+                and pmc.get("overlap", 0) == int(path.overlap)
+                and pmc.get("reserve_cus", 0) == (args.reserve_cus if path.overlap else 0)):
             traffic = pmc.get("bytes_per_launch")
 
     int4 = None
@@ -514,11 +570,13 @@ def main():
 
     boundary = None
     if path.R:
-        bnd_ms = rows_ms["score_and_working_set"] + rows_ms["compact_or_grow"]
+        cmp_ms = rows_ms.get("compact_or_grow")
+        if cmp_ms is None:
+            cmp_ms = rows_ms["compact_or_grow_plan"] + rows_ms["compact_or_grow_move_incl_wait"]
+        bnd_ms = rows_ms["score_and_working_set"] + cmp_ms
         boundary = dict(requests=path.R, us_per_request=bnd_ms * 1e3 / path.R,
                         score_us=rows_ms["score_and_working_set"] * 1e3,
-                        compact_us=rows_ms["compact_or_grow"] * 1e3,
-                        decisions=path.dec.cpu().tolist())
+                        compact_us=cmp_ms * 1e3, decisions=path.dec.cpu().tolist())
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -545,10 +603,12 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "paged_decode_attn (stream-K + merge launches)" + (
+                     "kernel": "paged_decode_attn_ex (stream-K decode with the fused summary "
+                               "update + merge launches)" + (
                          " of the requests not at a page boundary, beside the boundary pass on a "
                          "second stream" if path.overlap else ""),
-                     "bytes_per_launch": by["decode_main"], "avg_launch_ms": round(dec_ms, 4)},
+                     "bytes_per_launch": by["decode_main"] + by["summaries_main"],
+                     "avg_launch_ms": round(dec_ms, 4)},
         "cpu_baseline": cpu,
         "decode_kv_gbps": round(by["decode_main_kv"] / (dec_ms * 1e-3) / 1e9, 1),
         "overlap": int(path.overlap),
@@ -556,6 +616,7 @@ def main():
         "copy_gbps": round(copy_gbps, 1),
         "boundary": boundary,
         "int4_decode": int4,
+        "single_stream": single,
         "rows_ms": {k: round(v, 4) for k, v in rows_ms.items()},
         "event_ms_per_step": round(event_step_ms, 4),
         "bytes_per_step": by,

@@ -163,6 +163,33 @@ int gp_quantize_pages_int4(const gp_kv_cache* kv, const int32_t* page_ids, int n
                            void* stream);
 
 /*
+ * Decode attention with the summary update fused in (GrowPage Sec. 4.1: the attention kernel also
+ * updates both EMA summaries from the pre-RoPE query), and an optional cap on its grid.
+ *   Arguments as gp_paged_decode_attn (same workspace size), plus
+ *   summaries       NULL, or the update of gp_update_query_summaries applied to every request
+ *                   of this call (the same arithmetic, so the same bits); it is finished when
+ *                   the call's work on the stream is.
+ *   max_workgroups  0, or an upper bound on the workgroups of the streaming kernel (at least one
+ *                   per group of 8 KV heads is kept), so that kernels on another stream find
+ *                   free compute units while this call runs.
+ */
+typedef struct {
+  const void* q_pre;       /* [B, H_q, head_dim] pre-RoPE queries, in q_dtype                 */
+  const int32_t* slot_ids; /* [B] slot of each request in [0, num_slots); others are skipped  */
+  const uint8_t* fresh;    /* [B] 1 = first step of the slot: both summaries = q_pre          */
+  float* qstate;           /* [num_slots, 2, H_q, head_dim] fp32, updated in place            */
+  int num_slots;
+  float beta_s, beta_l;
+} gp_summary_update;
+
+int gp_paged_decode_attn_ex(const void* q, int q_dtype, int B, int H_q, const gp_kv_cache* kv,
+                            const int32_t* block_tables, int max_pages,
+                            const int32_t* context_lens, int max_context, float sm_scale,
+                            void* out, float* lse, const gp_summary_update* summaries,
+                            int max_workgroups, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * Dual-timescale EMA of the pre-RoPE queries (GrowPage Eq. 6, App. E.1).
  *   q        [B, H_q, head_dim] (GP_F32 or GP_BF16).
  *   slot_ids [B] int32 in [0, num_slots); fresh [B] uint8 (1 = first step of this slot).
@@ -216,9 +243,10 @@ int gp_score_and_working_set(const void* q, int q_dtype, int B, int H_q, const f
  *   token index) in ascending order followed by the |R| recent tokens is written to slots
  *   0 .. K_t+|R|-1 and context_lens[r] becomes K_t + |R|. Released references are
  *   decremented after all pops of the call; pages reaching zero are pushed on the stack.
- *   decision [R] int32 (GP_DECISION_*); kept_idx [R, H_kv, C_max] int32: the kept candidate
- *   indices in ascending order (all of C when nothing is evicted), -1 elsewhere and for
- *   requests that grew or got no pages.
+ *   decision [R] int32 (GP_DECISION_*); kept_idx [R, H_kv, C_max] int32: within the first |C|
+ *   entries of a row, the kept candidate indices in ascending order (all of C when nothing is
+ *   evicted) and -1 after them, or -1 throughout for requests that grew or got no pages;
+ *   entries past |C| are not written.
  *   a_short / a_long / ws_counts / n_cand as produced by gp_score_and_working_set.
  *   kv, block_tables, n_pages, context_lens, refcount, free_stack, free_top are updated in place.
  *   Uniform caches only (page_tag must be NULL). Requests of one call must be distinct.
@@ -226,6 +254,27 @@ int gp_score_and_working_set(const void* q, int q_dtype, int B, int H_q, const f
  *   C_max <= 32768 and a multiple of 4.
  */
 size_t gp_compact_or_grow_workspace_size(int R, int H_kv, int max_pages, int page_size, int C_max);
+
+/*
+ * gp_compact_or_grow in two phases, so that the data movement can be scheduled apart from the
+ * bookkeeping (GrowPage App. E.3 overlaps compaction with decoding):
+ *   GP_PHASE_PLAN  decisions, page allocation and release, kept_idx, and the list of page chunks
+ *                  to move: every update of block_tables, n_pages, context_lens, refcount,
+ *                  free_stack, free_top and decision. K/V pages are not touched.
+ *   GP_PHASE_MOVE  the K/V movement planned by the PLAN call that used this workspace; it must
+ *                  come after that call (same arguments and workspace, none of them changed in
+ *                  between) and after every read of the boundary requests' old pages.
+ * phases = GP_PHASE_PLAN | GP_PHASE_MOVE is gp_compact_or_grow itself.
+ */
+enum { GP_PHASE_PLAN = 1, GP_PHASE_MOVE = 2 };
+int gp_compact_or_grow_phase(const int32_t* req_idx, int R, int B, const float* a_short,
+                             const float* a_long, int C_max, const int32_t* ws_counts,
+                             const int32_t* n_cand, double tau, int k_loc, int policy,
+                             const int32_t* policies, gp_kv_cache* kv, int32_t* block_tables,
+                             int32_t* n_pages, int max_pages, int32_t* context_lens,
+                             int32_t* refcount, int32_t* free_stack, int32_t* free_top,
+                             int32_t* decision, int32_t* kept_idx, void* workspace,
+                             size_t workspace_bytes, int phases, void* stream);
 int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const float* a_short,
                        const float* a_long, int C_max, const int32_t* ws_counts,
                        const int32_t* n_cand, double tau, int k_loc, int policy,

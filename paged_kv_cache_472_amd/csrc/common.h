@@ -81,6 +81,45 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
+// Dual-timescale EMA step (GrowPage Sec. 3.2 Eq. 6) on four consecutive elements of one slot's
+// short and long summaries: x <- beta_x * x + (1 - beta_x) * q, or x = q on the slot's first step.
+// Shared by the standalone update and the one fused into decode attention, so both give the
+// same bits.
+__device__ __forceinline__ void ema_update4(float* short_row, float* long_row, const float q[4],
+                                            bool fresh, float beta_s, float beta_l) {
+  f32x4_t* s = reinterpret_cast<f32x4_t*>(short_row);
+  f32x4_t* l = reinterpret_cast<f32x4_t*>(long_row);
+  if (fresh) {
+    const f32x4_t v = {q[0], q[1], q[2], q[3]};
+    *s = v;
+    *l = v;
+  } else {
+    f32x4_t vs = *s, vl = *l;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      vs[c] = beta_s * vs[c] + (1.0f - beta_s) * q[c];
+      vl[c] = beta_l * vl[c] + (1.0f - beta_l) * q[c];
+    }
+    *s = vs;
+    *l = vl;
+  }
+}
+
+// Four consecutive query elements as fp32 (bf16 or fp32 storage).
+template <bool BF16>
+__device__ __forceinline__ void load_q4(const void* q, size_t idx, float x[4]) {
+  if constexpr (BF16) {
+    const u32x2_t w = *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(q) + idx);
+    x[0] = __uint_as_float(w.x << 16);
+    x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = __uint_as_float(w.y << 16);
+    x[3] = __uint_as_float(w.y & 0xffff0000u);
+  } else {
+    const f32x4_t w = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(q) + idx);
+    x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+  }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, GP_WAVE));

@@ -799,15 +799,17 @@ extern "C" size_t gp_compact_or_grow_workspace_size(int R, int H_kv, int max_pag
   return bytes;
 }
 
-extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const float* a_short,
-                                  const float* a_long, int C_max, const int32_t* ws_counts,
-                                  const int32_t* n_cand, double tau, int k_loc, int policy,
-                                  const int32_t* policies, gp_kv_cache* kv, int32_t* block_tables,
-                                  int32_t* n_pages, int max_pages, int32_t* context_lens,
-                                  int32_t* refcount, int32_t* free_stack, int32_t* free_top,
-                                  int32_t* decision, int32_t* kept_idx, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+extern "C" int gp_compact_or_grow_phase(const int32_t* req_idx, int R, int B,
+                                        const float* a_short, const float* a_long, int C_max,
+                                        const int32_t* ws_counts, const int32_t* n_cand, double tau,
+                                        int k_loc, int policy, const int32_t* policies,
+                                        gp_kv_cache* kv, int32_t* block_tables, int32_t* n_pages,
+                                        int max_pages, int32_t* context_lens, int32_t* refcount,
+                                        int32_t* free_stack, int32_t* free_top, int32_t* decision,
+                                        int32_t* kept_idx, void* workspace,
+                                        size_t workspace_bytes, int phases, void* stream) {
   if (R < 0 || B < 0 || C_max <= 0 || !kv || max_pages <= 0 || k_loc < 0) return GP_ERR_INVALID;
+  if (phases < 1 || phases > (GP_PHASE_PLAN | GP_PHASE_MOVE)) return GP_ERR_INVALID;
   if (R == 0) return GP_OK;
   if (R > DA_MAX_R) return GP_ERR_UNSUPPORTED;
   if (!req_idx || !a_short || !a_long || !ws_counts || !n_cand || !block_tables || !n_pages ||
@@ -892,9 +894,9 @@ extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const fl
   P.snap = ws + off;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(decide_alloc_kernel, dim3(1), dim3(DA_THREADS), 0, s, P);
-  GP_CHECK_LAUNCH();
-  {
+  if (phases & GP_PHASE_PLAN) {
+    hipLaunchKernelGGL(decide_alloc_kernel, dim3(1), dim3(DA_THREADS), 0, s, P);
+    GP_CHECK_LAUNCH();
     const int nch = (C_max + SEL_T * b - 1) / (SEL_T * b);
     const dim3 g(nch, H_kv, R);
     if (b == 16) hipLaunchKernelGGL(select_local_kernel<16>, g, dim3(SEL_T), 0, s, P);
@@ -905,9 +907,10 @@ extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const fl
     if (b == 16) hipLaunchKernelGGL(select_write_kernel<16>, g, dim3(SEL_T), 0, s, P);
     else hipLaunchKernelGGL(select_write_kernel<32>, g, dim3(SEL_T), 0, s, P);
     GP_CHECK_LAUNCH();
+    hipLaunchKernelGGL(chunk_list_kernel, dim3(1), dim3(DA_THREADS), 0, s, P);
+    GP_CHECK_LAUNCH();
   }
-  hipLaunchKernelGGL(chunk_list_kernel, dim3(1), dim3(DA_THREADS), 0, s, P);
-  GP_CHECK_LAUNCH();
+  if (!(phases & GP_PHASE_MOVE)) return GP_OK;
   const int cus = device_cus();
   hipLaunchKernelGGL(snapshot_kernel, dim3(std::max(1, std::min(4 * cus, R * H_kv * P.max_chunks))),
                      dim3(CP_THREADS), 0, s, P);
@@ -917,4 +920,19 @@ extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const fl
                      dim3(CP_THREADS), lds, s, P);
   GP_CHECK_LAUNCH();
   return GP_OK;
+}
+
+extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const float* a_short,
+                                  const float* a_long, int C_max, const int32_t* ws_counts,
+                                  const int32_t* n_cand, double tau, int k_loc, int policy,
+                                  const int32_t* policies, gp_kv_cache* kv, int32_t* block_tables,
+                                  int32_t* n_pages, int max_pages, int32_t* context_lens,
+                                  int32_t* refcount, int32_t* free_stack, int32_t* free_top,
+                                  int32_t* decision, int32_t* kept_idx, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return gp_compact_or_grow_phase(req_idx, R, B, a_short, a_long, C_max, ws_counts, n_cand, tau,
+                                  k_loc, policy, policies, kv, block_tables, n_pages, max_pages,
+                                  context_lens, refcount, free_stack, free_top, decision, kept_idx,
+                                  workspace, workspace_bytes, GP_PHASE_PLAN | GP_PHASE_MOVE,
+                                  stream);
 }

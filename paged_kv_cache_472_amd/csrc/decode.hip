@@ -42,7 +42,7 @@ constexpr int MAX_HEADS_PER_WG = 8;
 constexpr int MAX_THREADS = MAX_HEADS_PER_WG * GP_WAVE;
 constexpr int RING = 2;           // tiles in flight per wave
 constexpr int MAX_BATCH = 8191;   // prefix of tile counts kept in LDS (32 KB)
-constexpr int J_CAP = 16;         // bound on the workgroups one request is spread over
+constexpr int J_CAP_MAX = 127;    // partials one output row can have (the merge holds two per lane)
 
 struct DecodeParams {
   const void* q;
@@ -64,6 +64,13 @@ struct DecodeParams {
   float* ws_o;       // [B, H_q, J_max, D] partial outputs
   float* ws_ml;      // [B, H_q, J_max, 2] partial (max, sum)
   int32_t* ws_pref;  // [B + 1] prefix of tile counts, written by workgroup 0
+  // fused summary update (NULL q_pre: none)
+  const void* q_pre;
+  const int32_t* slot_ids;
+  const uint8_t* fresh;
+  float* qstate;
+  int num_slots;
+  float beta_s, beta_l;
   int B, H_q, H_kv, G, page_size, num_pages, max_pages, max_context;
   int heads_per_wg;
   int num_wg;  // workgroups per head group (the stream-K width)
@@ -368,6 +375,26 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
   if (wg == 0 && blockIdx.y == 0)
     for (int i = threadIdx.x; i <= p.B; i += blockDim.x) p.ws_pref[i] = s_pref[i];
   if (h >= p.H_kv) return;
+
+  // ---- fused summary update (GrowPage Eq. 6 on the pre-RoPE queries): requests wg, wg + num_wg,
+  // ... for this wave's KV head, independent of the tile ranges (empty requests included)
+  if (p.q_pre) {
+    const int GD = G * D;
+    for (int r = wg; r < p.B; r += p.num_wg) {
+      const int slot = p.slot_ids[r];
+      if (slot < 0 || slot >= p.num_slots) continue;
+      const bool fr = p.fresh[r] != 0;
+      const size_t qb = ((size_t)r * p.H_q + (size_t)h * G) * D;
+      const size_t sb = (size_t)slot * 2 * p.H_q * D + (size_t)h * G * D;
+      for (int i = lane * 4; i < GD; i += 4 * GP_WAVE) {
+        float x[4];
+        gp::load_q4<KIND != KIND_F32>(p.q_pre, qb + i, x);
+        gp::ema_update4(p.qstate + sb + i, p.qstate + sb + (size_t)p.H_q * D + i, x, fr, p.beta_s,
+                        p.beta_l);
+      }
+    }
+  }
+
   const int R = range_len(p, U);
   const long u0l = (long)wg * R;
   if (u0l >= U) return;
@@ -539,23 +566,36 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     J = (pb - 1) / R - pa / R + 1;
   }
   if (J == 1) return;
-  // J <= j_max <= J_CAP + 1 < 64
+  // J <= j_max <= J_CAP_MAX + 1 = 128: lane l holds partials l and l + 64
   const float* ml = p.ws_ml + row * p.j_max * 2;
-  const float mj = lane < J ? ml[2 * lane] : -INFINITY;
-  const float lj = lane < J ? ml[2 * lane + 1] : 0.f;
-  const float m = gp::wave_max(mj);
-  const float wj = gp::safe_exp2_diff(mj, m);
-  const float den = gp::wave_sum(wj * lj);
+  const float m0 = lane < J ? ml[2 * lane] : -INFINITY;
+  const float l0 = lane < J ? ml[2 * lane + 1] : 0.f;
+  const float m1 = lane + 64 < J ? ml[2 * (lane + 64)] : -INFINITY;
+  const float l1 = lane + 64 < J ? ml[2 * (lane + 64) + 1] : 0.f;
+  const float m = gp::wave_max(fmaxf(m0, m1));
+  const float w0 = gp::safe_exp2_diff(m0, m), w1 = gp::safe_exp2_diff(m1, m);
+  const float den = gp::wave_sum(w0 * l0 + w1 * l1);
   const float inv = den > 0.f ? 1.f / den : 0.f;
   const float* wo = p.ws_o + row * p.j_max * D;
   constexpr int PER = D / 64;
+  constexpr int BATCH = 8;  // partial rows fetched before any is used
   float num[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) num[e] = 0.f;
-  for (int j = 0; j < J; ++j) {
-    const float wt = __shfl(wj, j, GP_WAVE);
+  for (int j0 = 0; j0 < J; j0 += BATCH) {
+    float x[BATCH][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] += wt * wo[(size_t)j * D + lane + 64 * e];
+    for (int u = 0; u < BATCH; ++u)
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        x[u][e] = j0 + u < J ? wo[(size_t)(j0 + u) * D + lane + 64 * e] : 0.f;
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int j = j0 + u;
+      const float wt = j < J ? __shfl(j < 64 ? w0 : w1, j & 63, GP_WAVE) : 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) num[e] += wt * x[u][e];
+    }
   }
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -574,10 +614,13 @@ struct Plan {
 };
 
 // Ranges hold at least r_min tiles, so one request is spread over at most j_max workgroups.
-Plan plan_for(int max_context) {
+Plan plan_for(int B, int max_context) {
   const int max_tiles = (max_context + 15) / 16;
+  // a batch of many requests fills the device with few splits each; a small batch of long
+  // requests needs more of them (the workspace grows with B * j_max either way)
+  const int j_cap = std::min(J_CAP_MAX, std::max(16, 1024 / std::max(B, 1)));
   Plan pl;
-  pl.r_min = std::max(8, (max_tiles + J_CAP - 1) / J_CAP);
+  pl.r_min = std::max(8, (max_tiles + j_cap - 1) / j_cap);
   pl.j_max = (max_tiles + pl.r_min - 1) / pl.r_min + 1;
   return pl;
 }
@@ -609,11 +652,13 @@ int resident_workgroups(int threads, size_t lds) {
 }
 
 template <int D, int KIND>
-int launch_decode(DecodeParams p, hipStream_t stream) {
+int launch_decode(DecodeParams p, int max_workgroups, hipStream_t stream) {
   const int hg = (p.H_kv + p.heads_per_wg - 1) / p.heads_per_wg;
   const int threads = p.heads_per_wg * GP_WAVE;
   const size_t lds = (size_t)(p.B + 1) * sizeof(int);
-  p.num_wg = std::max(1, resident_workgroups<D, KIND>(threads, lds) / hg);
+  int total = resident_workgroups<D, KIND>(threads, lds);
+  if (max_workgroups > 0) total = std::min(total, max_workgroups);
+  p.num_wg = std::max(1, total / hg);
   hipLaunchKernelGGL((decode_streamk_kernel<D, KIND>), dim3(p.num_wg, hg), dim3(threads), lds,
                      stream, p);
   GP_CHECK_LAUNCH();
@@ -631,18 +676,23 @@ extern "C" size_t gp_paged_decode_attn_workspace_size(int B, int H_q, int H_kv, 
   (void)page_size;
   (void)H_kv;
   if (B <= 0 || H_q <= 0 || head_dim <= 0 || max_context < 0) return 0;
-  const Plan pl = plan_for(max_context);
+  const Plan pl = plan_for(B, max_context);
   const size_t partials = (size_t)B * H_q * pl.j_max * (head_dim + 2) * sizeof(float);
   const size_t pref = ((size_t)(B + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
   return pref + partials;
 }
 
-extern "C" int gp_paged_decode_attn(const void* q, int q_dtype, int B, int H_q,
-                                    const gp_kv_cache* kv, const int32_t* block_tables,
-                                    int max_pages, const int32_t* context_lens, int max_context,
-                                    float sm_scale, void* out, float* lse, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+namespace {
+
+int decode_impl(const void* q, int q_dtype, int B, int H_q, const gp_kv_cache* kv,
+                const int32_t* block_tables, int max_pages, const int32_t* context_lens,
+                int max_context, float sm_scale, void* out, float* lse,
+                const gp_summary_update* upd, int max_workgroups, void* workspace,
+                size_t workspace_bytes, void* stream) {
   if (B < 0 || H_q <= 0 || !kv || max_pages <= 0 || max_context < 0) return GP_ERR_INVALID;
+  if (max_workgroups < 0) return GP_ERR_INVALID;
+  if (upd && (!upd->q_pre || !upd->slot_ids || !upd->fresh || !upd->qstate || upd->num_slots <= 0))
+    return GP_ERR_INVALID;
   if (B == 0) return GP_OK;
   if (!q || !out || !block_tables || !context_lens || !kv->k || !kv->v) return GP_ERR_INVALID;
   const int H_kv = kv->num_kv_heads, D = kv->head_dim, b = kv->page_size;
@@ -664,7 +714,7 @@ extern "C" int gp_paged_decode_attn(const void* q, int q_dtype, int B, int H_q,
 
   const size_t need = gp_paged_decode_attn_workspace_size(B, H_q, H_kv, D, b, max_context);
   if (!workspace || workspace_bytes < need) return GP_ERR_WORKSPACE;
-  const Plan pl = plan_for(max_context);
+  const Plan pl = plan_for(B, max_context);
 
   DecodeParams p{};
   p.q = q;
@@ -699,8 +749,40 @@ extern "C" int gp_paged_decode_attn(const void* q, int q_dtype, int B, int H_q,
   p.ws_pref = reinterpret_cast<int32_t*>(ws);
   p.ws_o = reinterpret_cast<float*>(ws + (((size_t)(B + 1) * sizeof(int32_t) + 255) & ~(size_t)255));
   p.ws_ml = p.ws_o + (size_t)B * H_q * pl.j_max * D;
+  if (upd) {
+    p.q_pre = upd->q_pre;
+    p.slot_ids = upd->slot_ids;
+    p.fresh = upd->fresh;
+    p.qstate = upd->qstate;
+    p.num_slots = upd->num_slots;
+    p.beta_s = upd->beta_s;
+    p.beta_l = upd->beta_l;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (mixed) return D == 64 ? launch_decode<64, KIND_MIXED>(p, s) : launch_decode<128, KIND_MIXED>(p, s);
-  if (q_dtype == GP_BF16) return D == 64 ? launch_decode<64, KIND_BF16>(p, s) : launch_decode<128, KIND_BF16>(p, s);
-  return D == 64 ? launch_decode<64, KIND_F32>(p, s) : launch_decode<128, KIND_F32>(p, s);
+  const int mw = max_workgroups;
+  if (mixed) return D == 64 ? launch_decode<64, KIND_MIXED>(p, mw, s) : launch_decode<128, KIND_MIXED>(p, mw, s);
+  if (q_dtype == GP_BF16) return D == 64 ? launch_decode<64, KIND_BF16>(p, mw, s) : launch_decode<128, KIND_BF16>(p, mw, s);
+  return D == 64 ? launch_decode<64, KIND_F32>(p, mw, s) : launch_decode<128, KIND_F32>(p, mw, s);
+}
+
+}  // namespace
+
+extern "C" int gp_paged_decode_attn(const void* q, int q_dtype, int B, int H_q,
+                                    const gp_kv_cache* kv, const int32_t* block_tables,
+                                    int max_pages, const int32_t* context_lens, int max_context,
+                                    float sm_scale, void* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return decode_impl(q, q_dtype, B, H_q, kv, block_tables, max_pages, context_lens, max_context,
+                     sm_scale, out, lse, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+extern "C" int gp_paged_decode_attn_ex(const void* q, int q_dtype, int B, int H_q,
+                                       const gp_kv_cache* kv, const int32_t* block_tables,
+                                       int max_pages, const int32_t* context_lens,
+                                       int max_context, float sm_scale, void* out, float* lse,
+                                       const gp_summary_update* summaries, int max_workgroups,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, q_dtype, B, H_q, kv, block_tables, max_pages, context_lens, max_context,
+                     sm_scale, out, lse, summaries, max_workgroups, workspace, workspace_bytes,
+                     stream);
 }

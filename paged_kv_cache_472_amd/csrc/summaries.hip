@@ -16,32 +16,9 @@ __global__ __launch_bounds__(256) void ema_kernel(const void* __restrict__ q, in
   const int slot = slot_ids[r];
   if (slot < 0 || slot >= num_slots) return;
   float x[4];
-  if constexpr (BF16) {
-    const u32x2_t w = *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(q) + (size_t)r * HD + i);
-    x[0] = gp::bf16_bits_to_f32(w.x & 0xffffu);
-    x[1] = gp::bf16_bits_to_f32(w.x >> 16);
-    x[2] = gp::bf16_bits_to_f32(w.y & 0xffffu);
-    x[3] = gp::bf16_bits_to_f32(w.y >> 16);
-  } else {
-    const f32x4_t w = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(q) + (size_t)r * HD + i);
-    x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
-  }
-  f32x4_t* s = reinterpret_cast<f32x4_t*>(qstate + ((size_t)slot * 2 + 0) * HD + i);
-  f32x4_t* l = reinterpret_cast<f32x4_t*>(qstate + ((size_t)slot * 2 + 1) * HD + i);
-  if (fresh[r]) {
-    const f32x4_t v = {x[0], x[1], x[2], x[3]};
-    *s = v;
-    *l = v;
-  } else {
-    f32x4_t vs = *s, vl = *l;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      vs[c] = beta_s * vs[c] + (1.0f - beta_s) * x[c];
-      vl[c] = beta_l * vl[c] + (1.0f - beta_l) * x[c];
-    }
-    *s = vs;
-    *l = vl;
-  }
+  gp::load_q4<BF16>(q, (size_t)r * HD + i, x);
+  gp::ema_update4(qstate + ((size_t)slot * 2 + 0) * HD + i, qstate + ((size_t)slot * 2 + 1) * HD + i,
+                  x, fresh[r] != 0, beta_s, beta_l);
 }
 
 }  // namespace

@@ -16,13 +16,14 @@ GP_F32, GP_BF16 = 0, 1
 TAG_RELEASE, TAG_FP8, TAG_BF16, TAG_INT4 = 0, 1, 2, 3
 COMPRESS, GROW, GROW_FALLBACK_COMPRESS, NO_PAGES = 0, 1, 2, 3
 POLICY_AUTO, POLICY_FORCE_COMPRESS, POLICY_FORCE_GROW, POLICY_INVERSE = 0, 1, 2, 3
+PHASE_PLAN, PHASE_MOVE = 1, 2
 
 EXPORTED = (
     "gp_version", "gp_status_string",
-    "gp_paged_decode_attn_workspace_size", "gp_paged_decode_attn",
+    "gp_paged_decode_attn_workspace_size", "gp_paged_decode_attn", "gp_paged_decode_attn_ex",
     "gp_update_query_summaries",
     "gp_score_and_working_set_workspace_size", "gp_score_and_working_set",
-    "gp_compact_or_grow_workspace_size", "gp_compact_or_grow",
+    "gp_compact_or_grow_workspace_size", "gp_compact_or_grow", "gp_compact_or_grow_phase",
     "gp_quantize_pages_int4",
 )
 
@@ -38,6 +39,14 @@ class GpKvCache(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("k4", ctypes.c_void_p), ("v4", ctypes.c_void_p),
         ("k4_scale", ctypes.c_void_p), ("v4_scale", ctypes.c_void_p),
+    ]
+
+
+class GpSummaryUpdate(ctypes.Structure):
+    _fields_ = [
+        ("q_pre", ctypes.c_void_p), ("slot_ids", ctypes.c_void_p), ("fresh", ctypes.c_void_p),
+        ("qstate", ctypes.c_void_p), ("num_slots", ctypes.c_int32),
+        ("beta_s", ctypes.c_float), ("beta_l", ctypes.c_float),
     ]
 
 
@@ -61,6 +70,10 @@ def lib():
         L.gp_paged_decode_attn.restype = _I
         L.gp_paged_decode_attn.argtypes = [_VP, _I, _I, _I, ctypes.POINTER(GpKvCache), _VP, _I, _VP,
                                            _I, _F, _VP, _VP, _VP, _SZ, _VP]
+        L.gp_paged_decode_attn_ex.restype = _I
+        L.gp_paged_decode_attn_ex.argtypes = [_VP, _I, _I, _I, ctypes.POINTER(GpKvCache), _VP, _I,
+                                              _VP, _I, _F, _VP, _VP,
+                                              ctypes.POINTER(GpSummaryUpdate), _I, _VP, _SZ, _VP]
         L.gp_update_query_summaries.restype = _I
         L.gp_update_query_summaries.argtypes = [_VP, _I, _I, _I, _I, _VP, _VP, _VP, _I, _F, _F, _VP]
         L.gp_score_and_working_set_workspace_size.restype = _SZ
@@ -75,6 +88,8 @@ def lib():
         L.gp_compact_or_grow.argtypes = [_VP, _I, _I, _VP, _VP, _I, _VP, _VP, _D, _I, _I, _VP,
                                          ctypes.POINTER(GpKvCache), _VP, _VP, _I, _VP, _VP, _VP, _VP,
                                          _VP, _VP, _VP, _SZ, _VP]
+        L.gp_compact_or_grow_phase.restype = _I
+        L.gp_compact_or_grow_phase.argtypes = L.gp_compact_or_grow.argtypes[:-1] + [_I, _VP]
         L.gp_quantize_pages_int4.restype = _I
         L.gp_quantize_pages_int4.argtypes = [ctypes.POINTER(GpKvCache), _VP, _I, _VP]
         _lib = L
@@ -158,6 +173,36 @@ def gp_paged_decode_attn(q, cache, block_tables, context_lens, max_context, sm_s
     return out, lse
 
 
+def gp_paged_decode_attn_ex(q, cache, block_tables, context_lens, max_context, sm_scale,
+                            summaries=None, max_workgroups=0, out=None, lse=None, workspace=None):
+    """Decode attention with the summary update fused in (``summaries``: a dict with q_pre,
+    slot_ids, fresh, qstate, beta_s, beta_l, or None) and an optional cap on the decode grid.
+    Returns (out, lse)."""
+    B, H_q, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    need = gp_paged_decode_attn_workspace_size(B, H_q, cache.num_kv_heads, d, cache.page_size,
+                                               max_context)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    upd = None
+    if summaries is not None:
+        u = summaries
+        upd = GpSummaryUpdate(_ptr(u["q_pre"]), _ptr(u["slot_ids"]), _ptr(u["fresh"]),
+                              _ptr(u["qstate"]), u["qstate"].shape[0], float(u["beta_s"]),
+                              float(u["beta_l"]))
+    kv = cache.struct()
+    st = lib().gp_paged_decode_attn_ex(
+        _ptr(q), _dtype_code(q), B, H_q, ctypes.byref(kv), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), int(max_context), float(sm_scale), _ptr(out),
+        _ptr(lse), None if upd is None else ctypes.byref(upd), int(max_workgroups),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
+    _check(st, "gp_paged_decode_attn_ex")
+    return out, lse
+
+
 def gp_update_query_summaries(q, slot_ids, fresh, qstate, beta_s, beta_l):
     B, H_q, d = q.shape
     st = lib().gp_update_query_summaries(_ptr(q), _dtype_code(q), B, H_q, d, _ptr(slot_ids),
@@ -207,8 +252,11 @@ def gp_compact_or_grow_workspace_size(R, H_kv, max_pages, page_size, C_max):
 
 def gp_compact_or_grow(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, policy, cache,
                        block_tables, n_pages, context_lens, refcount, free_stack, free_top,
-                       policies=None, decision=None, kept_idx=None, workspace=None):
-    """Returns (decision [R] int32, kept_idx [R, H_kv, C_max] int32); state updated in place."""
+                       policies=None, decision=None, kept_idx=None, workspace=None,
+                       phases=PHASE_PLAN | PHASE_MOVE):
+    """Returns (decision [R] int32, kept_idx [R, H_kv, C_max] int32); state updated in place.
+    ``phases`` selects the planning and/or the data movement (gp_compact_or_grow_phase); a
+    MOVE-only call must reuse the workspace of its PLAN call."""
     R = req_idx.numel()
     H_kv = cache.num_kv_heads
     C_max = a_short.shape[2]
@@ -221,12 +269,15 @@ def gp_compact_or_grow(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, 
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     kv = cache.struct()
-    st = lib().gp_compact_or_grow(
-        _ptr(req_idx), R, block_tables.shape[0], _ptr(a_short), _ptr(a_long), C_max,
-        _ptr(ws_counts), _ptr(n_cand), float(tau), int(k_loc), int(policy), _ptr(policies),
-        ctypes.byref(kv), _ptr(block_tables), _ptr(n_pages), block_tables.shape[1],
-        _ptr(context_lens), _ptr(refcount), _ptr(free_stack), _ptr(free_top), _ptr(decision),
-        _ptr(kept_idx), _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
+    args = (_ptr(req_idx), R, block_tables.shape[0], _ptr(a_short), _ptr(a_long), C_max,
+            _ptr(ws_counts), _ptr(n_cand), float(tau), int(k_loc), int(policy), _ptr(policies),
+            ctypes.byref(kv), _ptr(block_tables), _ptr(n_pages), block_tables.shape[1],
+            _ptr(context_lens), _ptr(refcount), _ptr(free_stack), _ptr(free_top), _ptr(decision),
+            _ptr(kept_idx), _ptr(workspace), 0 if workspace is None else workspace.numel())
+    if phases == PHASE_PLAN | PHASE_MOVE:
+        st = lib().gp_compact_or_grow(*args, _stream())
+    else:
+        st = lib().gp_compact_or_grow_phase(*args, int(phases), _stream())
     _check(st, "gp_compact_or_grow")
     return decision, kept_idx
 

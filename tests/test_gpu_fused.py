@@ -1,0 +1,142 @@
+"""GPU parity of the calls that let a step overlap its rows (GrowPage §4.1 and App. E.3):
+gp_paged_decode_attn_ex, decode attention with the dual-timescale summary update fused in and a
+capped grid (the fused update must give the bits of gp_update_query_summaries, the decode those
+of gp_paged_decode_attn at the same grid, and both must match the float64 oracle at any grid
+cap), and gp_compact_or_grow_phase, whose PLAN and MOVE phases must together leave the exact
+state of one gp_compact_or_grow call."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_472_amd as gp
+from oracle import attention as oatt
+from oracle.summaries import update_query_summaries
+from gpu_common import DEV, TOL, maxabs, mixed_np, say, workload_on_gpu
+from util import f64, npy
+from workloads.configs import make_decode_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _slots_and_fresh(wl, seed):
+    rng = np.random.default_rng(seed)
+    slots = npy(wl.slot_ids).astype(np.int64).copy()
+    fresh = (rng.random(wl.B) < 0.3).astype(np.uint8)
+    if wl.B > 2:
+        slots[1] = -1                      # an unbound request: no update
+    return slots, fresh
+
+
+def _prime(wl):
+    """Summaries after two past queries, so that non-fresh updates read real state."""
+    one = torch.ones(wl.B, dtype=torch.uint8, device=DEV)
+    gp.gp_update_query_summaries(wl.q_hist[0].contiguous(), wl.slot_ids, one, wl.qstate,
+                                 wl.beta_s, wl.beta_l)
+    gp.gp_update_query_summaries(wl.q_hist[1].contiguous(), wl.slot_ids, one * 0, wl.qstate,
+                                 wl.beta_s, wl.beta_l)
+
+
+@pytest.mark.parametrize("cfg", ["1", "2", "4", "5"])
+def test_fused_equals_separate_bitwise(cfg):
+    wl = workload_on_gpu(cfg, "small", int4_frac=0.5 if cfg == "5" else 0.0)
+    _prime(wl)
+    slots, fresh = _slots_and_fresh(wl, 3)
+    slot_t = torch.as_tensor(slots, dtype=torch.int32, device=DEV)
+    fresh_t = torch.as_tensor(fresh, device=DEV)
+    q_pre = wl.q_hist[2].contiguous()
+    cache = gp.KVCache.from_workload(wl)
+    st0 = wl.qstate.clone()
+    # separate calls
+    gp.gp_update_query_summaries(q_pre, slot_t, fresh_t, wl.qstate, wl.beta_s, wl.beta_l)
+    o1, l1 = gp.gp_paged_decode_attn(wl.q, cache, wl.block_tables, wl.context_lens,
+                                     wl.max_context, wl.sm_scale)
+    torch.cuda.synchronize()
+    st_sep = wl.qstate.clone()
+    # fused call from the same starting state
+    wl.qstate.copy_(st0)
+    o2, l2 = gp.gp_paged_decode_attn_ex(
+        wl.q, cache, wl.block_tables, wl.context_lens, wl.max_context, wl.sm_scale,
+        summaries=dict(q_pre=q_pre, slot_ids=slot_t, fresh=fresh_t, qstate=wl.qstate,
+                       beta_s=wl.beta_s, beta_l=wl.beta_l))
+    torch.cuda.synchronize()
+    say(f"[fused {cfg}] state equal={torch.equal(torch.nan_to_num(st_sep, 7.0), torch.nan_to_num(wl.qstate, 7.0))}")
+    assert torch.equal(st_sep.view(torch.int32), wl.qstate.view(torch.int32))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("max_wg", [1, 3, 37, 100000])
+def test_fused_capped_grid_matches_oracle(max_wg):
+    lens = [0, 5, 700, 16, 3000, 1, 0, 257, 1200, 64]
+    wl = make_decode_case(len(lens), 16, 4, 128, 16, lens, dtype="bf16", seed=max_wg % 97).to(DEV)
+    B = wl.B
+    state_ref = np.random.default_rng(1).standard_normal((8, 2, wl.H_q, wl.d))
+    qstate = torch.as_tensor(state_ref, dtype=torch.float32, device=DEV)
+    state_ref = f64(qstate)
+    slots = np.arange(B) % 8
+    slots[:B // 2] = np.arange(B // 2)                # distinct slots for the first half
+    slots[B // 2:] = -1                              # the rest unbound
+    fresh = np.zeros(B, dtype=np.uint8)
+    fresh[2] = 1
+    q_pre = (wl.q.float() * 0.5 + 0.25).to(torch.bfloat16)
+    out, lse = gp.gp_paged_decode_attn_ex(
+        wl.q, gp.KVCache.from_workload(wl), wl.block_tables, wl.context_lens, wl.max_context,
+        wl.sm_scale, summaries=dict(q_pre=q_pre, slot_ids=torch.as_tensor(slots, dtype=torch.int32, device=DEV),
+                                    fresh=torch.as_tensor(fresh, device=DEV), qstate=qstate,
+                                    beta_s=0.9, beta_l=0.999),
+        max_workgroups=max_wg)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
+                                          npy(wl.block_tables), npy(wl.context_lens), 16,
+                                          wl.sm_scale)
+    bound = slots >= 0
+    update_query_summaries(f64(q_pre)[bound], slots[bound], fresh[bound], state_ref, 0.9, 0.999)
+    eo, nan_o = maxabs(f64(out), ref_o)
+    el, nan_l = maxabs(lse.cpu().numpy(), ref_l)
+    es, nan_s = maxabs(qstate.cpu().numpy(), state_ref)
+    say(f"[fused cap={max_wg}] max|out-ref|={eo:.3e} max|lse-ref|={el:.3e} max|state-ref|={es:.3e}")
+    assert not (nan_o or nan_l or nan_s)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"] and es <= TOL["f32"]
+    # the empty requests still had their summaries updated (request 0 is bound and empty)
+    assert lens[0] == 0 and bound[0]
+
+
+@pytest.mark.parametrize("cfg", ["1", "3b", "4"])
+def test_compact_or_grow_phases_equal_one_call(cfg):
+    """PLAN then MOVE (gp_compact_or_grow_phase) leaves exactly the state of one
+    gp_compact_or_grow call: pools, block tables, page pool, decisions and kept indices."""
+    from test_gpu_boundary import bits, build_state, c_max_of, host_state, run_score
+    wl = workload_on_gpu(cfg, "small")
+    build_state(wl)
+    C_max = c_max_of(wl)
+    a_s, a_l, ws, nc = run_score(wl, C_max=C_max)
+    pol = torch.as_tensor(wl.req_policy, dtype=torch.int32, device=DEV)
+    snap = wl.snapshot()
+    results = []
+    for split in (False, True):
+        wl.restore(snap)
+        cache = gp.KVCache.from_workload(wl)
+        args = (wl.req_idx, a_s, a_l, ws, nc, wl.tau, wl.k_loc, 0, cache, wl.block_tables,
+                wl.n_pages, wl.context_lens, wl.refcount, wl.free_stack, wl.free_top)
+        need = gp.gp_compact_or_grow_workspace_size(wl.req_idx.numel(), wl.H_kv,
+                                                    wl.block_tables.shape[1], wl.page_size, C_max)
+        wsp = torch.empty(need, dtype=torch.uint8, device=DEV)
+        if split:
+            dec, kept = gp.gp_compact_or_grow(*args, policies=pol, workspace=wsp, phases=1)
+            torch.cuda.synchronize()
+            pools_after_plan = (bits(wl.k_pool), bits(wl.v_pool))
+            gp.gp_compact_or_grow(*args, policies=pol, decision=dec, kept_idx=kept,
+                                  workspace=wsp, phases=2)
+        else:
+            dec, kept = gp.gp_compact_or_grow(*args, policies=pol, workspace=wsp)
+        torch.cuda.synchronize()
+        results.append((host_state(wl), npy(dec), npy(kept)))
+    (s1, d1, k1), (s2, d2, k2) = results
+    say(f"[phases {cfg}] decisions={d1.tolist()}")
+    # the plan alone moved no K/V byte
+    assert np.array_equal(pools_after_plan[0], bits(snap["k_pool"]))
+    assert np.array_equal(pools_after_plan[1], bits(snap["v_pool"]))
+    assert np.array_equal(d1, d2)
+    for i, n in enumerate(npy(nc).tolist()):     # kept_idx is defined on the first |C| entries
+        assert np.array_equal(k1[i, :, :max(n, 0)], k2[i, :, :max(n, 0)])
+    for name in s1:
+        assert np.array_equal(s1[name], s2[name]), name
