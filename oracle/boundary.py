@@ -12,9 +12,14 @@ Steps, in the order GrowPage App. E.1 runs them at a capacity boundary:
    each query head g mapped to h (native GQA mapping, App. E.1), averaged over those heads.
 4. Working set (Eq. 2 / Eq. 7): K^x_h = min{k : sum of the k largest weights >= p}, computed
    exactly on the given weight values; if no k reaches p, K = |C_t|.
-5. Trend and decision (Eq. 8, Sec. 3.2): Delta = (1/H) sum_h (K^S_h - K^L_h) / |C_t|; Grow by
-   One Page iff Delta > tau, else Compress & Hold. Policies of App. H.1: always compress
-   (GrowPage-Fixed), always grow, and GrowPage-Inverse (grow iff Delta <= tau).
+5. Trend and decision (Eq. 8, Sec. 3.2): Delta = (1/(L H)) sum over layers and KV heads of
+   (K^S - K^L) / |C_t| (one decision per request for all layers); Grow by One Page iff
+   Delta > tau, else Compress & Hold. Policies of App. H.1: always compress (GrowPage-Fixed),
+   always grow, GrowPage-Inverse (grow iff Delta <= tau) and GrowPage-Shrink (Eq. 13): Shrink
+   iff Delta < -0.005, grow iff Delta > tau, else Compress & Hold. Shrink evicts two pages'
+   worth of history, returns the last page to the pool and leaves one page of free slots; it
+   is taken only while the capacity stays at least 1024 tokens afterwards (else Compress &
+   Hold).
 6. Allocation (Sec. 4.2, App. E.2): Grow pops the top of the global free-page stack and appends
    it to the block table; with no free page (or a full block table) it falls back to
    compression. Compression that must write into pages shared with other requests
@@ -28,7 +33,9 @@ Steps, in the order GrowPage App. E.1 runs them at a capacity boundary:
    on ties. If |S_loc| >= K_t, S is the K_t best tokens of C_t.
 8. Compaction (Sec. 3.3, App. E.2): the kept tokens in ascending order, then R_t, are written to
    slots 0 .. K_t + |R_t| - 1 of the (new) block table; the cached length becomes K_t + |R_t|,
-   i.e. (P - 1) b, leaving one page of free slots.
+   i.e. (P - 1) b, leaving one page of free slots. Selection and compaction run per layer and
+   KV head on the shared block table. Shrink uses K_t = (P - 2) b - |R_t|, then drops the last
+   page from the block table and releases it with the other references of the call.
 
 Pinned by: RMS of the calibrated summary equals RMS(q_t); RoPE keeps norms and its dot
 products depend only on relative position; full retention (p -> 1) gives K = |C|; uniform
@@ -36,14 +43,20 @@ weights give K = ceil(p |C|); one dominant weight gives K = 1; brute force over 
 tiny candidate sets (GrowPage Thm. 3.1 / App. C: the top-k weights maximise retained mass);
 the tight worst-case construction of App. C; equal summaries give Delta = 0 -> compress and
 the inverse policy flips it; selection against brute-force enumeration; page conservation,
-refcount bookkeeping, shared pages untouched and kept K/V bit-identical after compaction.
+refcount bookkeeping, shared pages untouched and kept K/V bit-identical after compaction;
+hand-worked GrowPage-Shrink decisions over several layers (tests/golden/shrink_cases.txt); a
+shrink's geometry, capacity floor, released page and moved K/V; a call over two layers whose
+mean decides, with each layer's moved K/V bit-identical to its own kept set, and one layer
+through the layered call equal to the single-layer call.
 """
 from fractions import Fraction
 
 import numpy as np
 
-COMPRESS, GROW, GROW_FALLBACK_COMPRESS, NO_PAGES = 0, 1, 2, 3
-POLICY_AUTO, POLICY_FORCE_COMPRESS, POLICY_FORCE_GROW, POLICY_INVERSE = 0, 1, 2, 3
+COMPRESS, GROW, GROW_FALLBACK_COMPRESS, NO_PAGES, SHRINK = 0, 1, 2, 3, 4
+POLICY_AUTO, POLICY_FORCE_COMPRESS, POLICY_FORCE_GROW, POLICY_INVERSE, POLICY_SHRINK = 0, 1, 2, 3, 4
+SHRINK_BELOW = Fraction(-5, 1000)   # GrowPage Eq. 13
+MIN_CAPACITY = 1024                 # tokens a shrink must leave (GrowPage App. H.1)
 
 
 # ---------------------------------------------------------------------------- step 1
@@ -183,17 +196,33 @@ def working_set_counts(a_short, a_long, n_cand, p):
 
 
 # ---------------------------------------------------------------------------- step 5
+def trend(ws_counts_r, n_cand_r):
+    """Eq. 8 as an exact fraction: the mean over every (layer, KV head) row of
+    (K^S - K^L) / |C|. ws_counts_r holds rows of (K^S, K^L), layers and heads in any order."""
+    ws = np.asarray(ws_counts_r, dtype=np.int64).reshape(-1, 2)
+    return Fraction(int(ws[:, 0].sum() - ws[:, 1].sum()), ws.shape[0] * int(n_cand_r))
+
+
+def primary_action(ws_counts_r, n_cand_r, tau, policy):
+    """Primary decision of one request before allocation: "grow", "compress" or "shrink"."""
+    if policy == POLICY_FORCE_COMPRESS:
+        return "compress"
+    if policy == POLICY_FORCE_GROW or n_cand_r == 0:
+        return "grow"
+    delta = trend(ws_counts_r, n_cand_r)
+    grow = delta > Fraction(tau)
+    if policy == POLICY_INVERSE:
+        grow = not grow
+    if grow:
+        return "grow"
+    if policy == POLICY_SHRINK and delta < SHRINK_BELOW:
+        return "shrink"
+    return "compress"
+
+
 def wants_grow(ws_counts_r, n_cand_r, tau, policy):
     """Primary decision of one request (before allocation): True = Grow by One Page."""
-    if policy == POLICY_FORCE_COMPRESS:
-        return False
-    if policy == POLICY_FORCE_GROW or n_cand_r == 0:
-        return True
-    ws = np.asarray(ws_counts_r, dtype=np.int64)
-    H = ws.shape[0]
-    delta = Fraction(int(ws[:, 0].sum() - ws[:, 1].sum()), H * int(n_cand_r))
-    grow = delta > Fraction(tau)
-    return (not grow) if policy == POLICY_INVERSE else grow
+    return primary_action(ws_counts_r, n_cand_r, tau, policy) == "grow"
 
 
 # ---------------------------------------------------------------------------- step 7
@@ -225,20 +254,43 @@ def select_kept(s, K_t, page_size, k_loc):
 def compact_or_grow(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, policy,
                     k_pool, v_pool, block_tables, n_pages, context_lens, refcount,
                     free_stack, free_top, page_size, policies=None):
-    """Decision, allocation, selection and compaction for the boundary requests, in order.
+    """Decision, allocation, selection and compaction for the boundary requests of one layer.
 
     State arrays (numpy) are updated in place: k_pool [N, H, b, d], v_pool [N, H, d, b],
     block_tables [B, max_pages], n_pages, context_lens, refcount, free_stack, free_top [1].
     `policies` optionally gives a per-request policy overriding `policy`.
     Returns decision [R] and kept_idx [R, H_kv, C_max] (-1 where unused).
     """
+    dec, kept = compact_or_grow_layers(req_idx, [a_short], [a_long], [ws_counts], n_cand, tau,
+                                       k_loc, policy, [k_pool], [v_pool], block_tables, n_pages,
+                                       context_lens, refcount, free_stack, free_top, page_size,
+                                       policies)
+    return dec, kept[0]
+
+
+def _pop(free_stack, free_top):
+    top = int(free_top[0]) - 1
+    page = int(free_stack[top])
+    free_stack[top] = -1
+    free_top[0] = top
+    return page
+
+
+def compact_or_grow_layers(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, policy,
+                           k_pools, v_pools, block_tables, n_pages, context_lens, refcount,
+                           free_stack, free_top, page_size, policies=None):
+    """As compact_or_grow for L layers that share block tables and the page pool: a_short,
+    a_long, ws_counts, k_pools, v_pools are lists with one entry per layer. One decision per
+    request from the mean over all layers and KV heads (Eq. 8); selection and compaction per
+    layer. Returns decision [R] and a list of kept_idx [R, H_kv, C_max], one per layer."""
     b = page_size
+    L = len(k_pools)
     R = len(req_idx)
-    H = k_pool.shape[1]
-    C_max = a_short.shape[2]
+    H = k_pools[0].shape[1]
+    C_max = a_short[0].shape[2]
     max_pages = block_tables.shape[1]
     decision = np.full(R, -1, dtype=np.int64)
-    kept_idx = np.full((R, H, C_max), -1, dtype=np.int64)
+    kept_idx = [np.full((R, H, C_max), -1, dtype=np.int64) for _ in range(L)]
     releases = []
     for i, r in enumerate(req_idx):
         pol = policy if policies is None else policies[i]
@@ -247,14 +299,12 @@ def compact_or_grow(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, pol
         n = int(n_cand[i])
         assert n == candidate_count(ctx, b)
         R_n = ctx - n
-        K_t = min(n, max(0, (P - 1) * b - R_n))
-        E = n - K_t
-        if wants_grow(ws_counts[i], n, tau, pol):
+        ws_r = np.concatenate([np.asarray(ws_counts[l][i]).reshape(-1, 2) for l in range(L)])
+        action = primary_action(ws_r, n, tau, pol)
+        code = COMPRESS
+        if action == "grow":
             if int(free_top[0]) > 0 and P < max_pages:
-                top = int(free_top[0]) - 1
-                page = int(free_stack[top])
-                free_stack[top] = -1
-                free_top[0] = top
+                page = _pop(free_stack, free_top)
                 block_tables[r, P] = page
                 n_pages[r] = P + 1
                 refcount[page] = 1
@@ -264,11 +314,21 @@ def compact_or_grow(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, pol
                 decision[i] = NO_PAGES
                 continue
             code = GROW_FALLBACK_COMPRESS
-        else:
-            code = COMPRESS
+        shrink = action == "shrink" and P >= 2 and (P - 1) * b >= MIN_CAPACITY
+        if shrink:
+            code = SHRINK
+        keep_pages = P - 2 if shrink else P - 1
+        K_t = min(n, max(0, keep_pages * b - R_n))
+        E = n - K_t
         if E == 0:
+            # nothing to evict: no token moves (a shrink still hands back the empty last page)
+            for l in range(L):
+                kept_idx[l][i, :, :n] = np.arange(n)
+            if shrink:
+                releases.append(int(block_tables[r, P - 1]))
+                block_tables[r, P - 1] = -1
+                n_pages[r] = P - 1
             decision[i] = code
-            kept_idx[i, :, :n] = np.arange(n)
             continue
         ctx_new = K_t + R_n
         n_dest = -(-ctx_new // b)
@@ -278,28 +338,30 @@ def compact_or_grow(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, pol
             continue
         old_bt = block_tables[r].copy()
         for j in shared:
-            top = int(free_top[0]) - 1
-            page = int(free_stack[top])
-            free_stack[top] = -1
-            free_top[0] = top
+            page = _pop(free_stack, free_top)
             block_tables[r, j] = page
             refcount[page] = 1
             releases.append(int(old_bt[j]))
-        # selection per KV head, then move the tokens (read everything first, then write)
+        # selection per layer and KV head, then move the tokens (read everything first)
         src_slots = np.arange(ctx)
-        for h in range(H):
-            s = np.maximum(np.asarray(a_short[i, h, :n], dtype=np.float64),
-                           np.asarray(a_long[i, h, :n], dtype=np.float64))
-            kept = select_kept(s, K_t, b, k_loc)
-            kept_idx[i, h, :K_t] = kept
-            src = np.concatenate([kept, src_slots[n:ctx]])
-            sp, so = old_bt[src // b], src % b
-            kv_k = k_pool[sp, h, so, :].copy()
-            kv_v = v_pool[sp, h, :, so].copy()
-            dst = np.arange(ctx_new)
-            dp, do = block_tables[r][dst // b], dst % b
-            k_pool[dp, h, do, :] = kv_k
-            v_pool[dp, h, :, do] = kv_v
+        for l in range(L):
+            for h in range(H):
+                s = np.maximum(np.asarray(a_short[l][i, h, :n], dtype=np.float64),
+                               np.asarray(a_long[l][i, h, :n], dtype=np.float64))
+                kept = select_kept(s, K_t, b, k_loc)
+                kept_idx[l][i, h, :K_t] = kept
+                src = np.concatenate([kept, src_slots[n:ctx]])
+                sp, so = old_bt[src // b], src % b
+                kv_k = k_pools[l][sp, h, so, :].copy()
+                kv_v = v_pools[l][sp, h, :, so].copy()
+                dst = np.arange(ctx_new)
+                dp, do = block_tables[r][dst // b], dst % b
+                k_pools[l][dp, h, do, :] = kv_k
+                v_pools[l][dp, h, :, do] = kv_v
+        if shrink:
+            releases.append(int(old_bt[P - 1]))
+            block_tables[r, P - 1] = -1
+            n_pages[r] = P - 1
         context_lens[r] = ctx_new
         decision[i] = code
     for page in releases:
