@@ -14,7 +14,9 @@
  *   gp_compact_or_grow        GrowPage Eq. 8 (trend, tau), Sec. 3.3 Eq. 9-10 (importance and
  *                             block-local + global selection, Compress & Hold, Grow by One Page),
  *                             Sec. 4.2 and App. E.2 (free-page pool, fallback, prefix sharing),
- *                             App. H.1 (fixed / inverse policies).
+ *                             App. H.1 (fixed / inverse / shrink policies, Eq. 13); the _phase
+ *                             and _layers forms split it for overlap (App. E.3) and aggregate
+ *                             Eq. 8 over layers.
  *
  * Conventions shared by every call
  *   - All array arguments are DEVICE pointers owned by the caller; scalars are passed by value.
@@ -65,7 +67,9 @@ enum {
   GP_DECISION_COMPRESS = 0,               /* Compress & Hold                                 */
   GP_DECISION_GROW = 1,                   /* Grow by One Page                                */
   GP_DECISION_GROW_FALLBACK_COMPRESS = 2, /* grow wanted, no page granted: compressed instead */
-  GP_DECISION_NO_PAGES = 3                /* neither possible: request left untouched        */
+  GP_DECISION_NO_PAGES = 3,               /* neither possible: request left untouched        */
+  GP_DECISION_SHRINK = 4                  /* GrowPage-Shrink: two pages' worth evicted, the
+                                             last page returned to the pool (App. H.1)       */
 };
 
 /* Capacity-control policies (GrowPage Sec. 3.2 and App. H.1). */
@@ -73,7 +77,9 @@ enum {
   GP_POLICY_AUTO = 0,           /* grow iff Delta > tau                        */
   GP_POLICY_FORCE_COMPRESS = 1, /* GrowPage-Fixed: always Compress & Hold      */
   GP_POLICY_FORCE_GROW = 2,     /* always try to grow                          */
-  GP_POLICY_INVERSE = 3         /* GrowPage-Inverse: grow iff Delta <= tau     */
+  GP_POLICY_INVERSE = 3,        /* GrowPage-Inverse: grow iff Delta <= tau     */
+  GP_POLICY_SHRINK = 4          /* GrowPage-Shrink (Eq. 13): shrink iff Delta < -0.005, grow iff
+                                   Delta > tau, else Compress & Hold                        */
 };
 
 /*
@@ -233,7 +239,11 @@ int gp_score_and_working_set(const void* q, int q_dtype, int B, int H_q, const f
  * Compress-or-grow for the boundary requests, processed in req_idx order (GrowPage Sec. 3.2,
  * Sec. 3.3, Sec. 4.2, App. E.2, App. H.1).
  *   Decision: Delta = (1/H_kv) sum_h (K^S_h - K^L_h) / |C| compared exactly with tau under
- *   `policy` (or policies[i] when `policies` is non-NULL); |C| = 0 always grows.
+ *   `policy` (or policies[i] when `policies` is non-NULL); |C| = 0 always grows. Under
+ *   GP_POLICY_SHRINK a request with Delta < -0.005 (exact) shrinks instead of compressing when
+ *   its capacity stays >= 1024 tokens afterwards ((n_pages - 1) * page_size >= 1024): as
+ *   Compress below with K_t = min(|C|, (P-2)b - |R|), then the last page leaves the block table
+ *   (n_pages - 1) and its reference is released after the request's replaced pages.
  *   Grow: pop free_stack[*free_top - 1], append it to the block table, n_pages += 1, refcount
  *   of the page = 1. No free page (or a full block table) falls back to compression.
  *   Compress: with P = n_pages[r], R = tokens of the last page, K_t = min(|C|, (P-1)b - |R|).
@@ -251,7 +261,8 @@ int gp_score_and_working_set(const void* q, int q_dtype, int B, int H_q, const f
  *   kv, block_tables, n_pages, context_lens, refcount, free_stack, free_top are updated in place.
  *   Uniform caches only (page_tag must be NULL). Requests of one call must be distinct.
  *   Limits: R <= 1024, page_size 16 or 32 (32-token fp32 pages need head_dim 64),
- *   C_max <= 32768 and a multiple of 4.
+ *   C_max <= 32768 and a multiple of 4. GP_POLICY_SHRINK needs page_size 16 (a shrink evicts up
+ *   to 2 * page_size tokens); with 32-token pages a per-request Shrink is answered NO_PAGES.
  */
 size_t gp_compact_or_grow_workspace_size(int R, int H_kv, int max_pages, int page_size, int C_max);
 
@@ -267,6 +278,29 @@ size_t gp_compact_or_grow_workspace_size(int R, int H_kv, int max_pages, int pag
  * phases = GP_PHASE_PLAN | GP_PHASE_MOVE is gp_compact_or_grow itself.
  */
 enum { GP_PHASE_PLAN = 1, GP_PHASE_MOVE = 2 };
+
+/*
+ * Compress-or-grow for L layers that share block tables and the page pool (GrowPage Eq. 8:
+ * one decision per request from the mean of (K^S - K^L)/|C| over every layer and KV head;
+ * Eq. 9-10: selection and compaction per layer and KV head).
+ *   a_short, a_long, kept_idx  [num_layers, R, H_kv, C_max] (layer l's scores at offset l);
+ *   ws_counts                  [num_layers, R, H_kv, 2];
+ *   kv_layers                  HOST array of num_layers caches with the same geometry and dtype;
+ *   n_cand [R] (the candidate count does not depend on the layer); other arguments, phases and
+ *   outcomes as gp_compact_or_grow_phase. num_layers = 1 is gp_compact_or_grow_phase itself.
+ *   workspace >= gp_compact_or_grow_layers_workspace_size(num_layers, ...) bytes.
+ */
+size_t gp_compact_or_grow_layers_workspace_size(int num_layers, int R, int H_kv, int max_pages,
+                                                int page_size, int C_max);
+int gp_compact_or_grow_layers(const int32_t* req_idx, int R, int B, int num_layers,
+                              const float* a_short, const float* a_long, int C_max,
+                              const int32_t* ws_counts, const int32_t* n_cand, double tau,
+                              int k_loc, int policy, const int32_t* policies,
+                              gp_kv_cache* const* kv_layers, int32_t* block_tables,
+                              int32_t* n_pages, int max_pages, int32_t* context_lens,
+                              int32_t* refcount, int32_t* free_stack, int32_t* free_top,
+                              int32_t* decision, int32_t* kept_idx, void* workspace,
+                              size_t workspace_bytes, int phases, void* stream);
 int gp_compact_or_grow_phase(const int32_t* req_idx, int R, int B, const float* a_short,
                              const float* a_long, int C_max, const int32_t* ws_counts,
                              const int32_t* n_cand, double tau, int k_loc, int policy,

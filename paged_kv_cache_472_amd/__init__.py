@@ -6,6 +6,8 @@ include/growpage.h); :mod:`.growpage` is its ctypes binding.
 from .growpage import (  # noqa: F401
     KVCache,
     gp_compact_or_grow,
+    gp_compact_or_grow_layers,
+    gp_compact_or_grow_layers_workspace_size,
     gp_compact_or_grow_workspace_size,
     gp_paged_decode_attn,
     gp_paged_decode_attn_ex,

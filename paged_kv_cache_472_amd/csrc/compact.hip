@@ -32,6 +32,8 @@ constexpr int SEL_T = 256;           // threads (candidate pages) per selection 
 constexpr int MAX_CAND = 32768;      // largest candidate set
 constexpr int SEL_MAX_CHUNKS = MAX_CAND / (SEL_T * 16);
 constexpr int MAX_EVICT = 32;
+constexpr int MAX_SPAN = 2;               // pages a compaction shifts by at most (Shrink: 2)
+constexpr int SHRINK_MIN_CAPACITY = 1024; // tokens a Shrink must leave (GrowPage App. H.1)
 constexpr int CHUNK_PAGES = 16;           // destination pages per compaction workgroup
 constexpr int MAX_WINDOW_SLOTS = 8 * 32;  // LDS window pages (<= 8) x page size (<= 32)
 constexpr int CP_THREADS = 256;
@@ -68,8 +70,10 @@ struct CParams {
   unsigned long long* cand;  // [R, H_kv, SEL_MAX_CHUNKS, MAX_EVICT] chunk survivors
   int2* items;               // [R * H_kv * max_chunks] (request * H_kv + head, chunk) to compact
   int32_t* n_items;          // [1]
-  uint8_t* snap;      // [R, H_kv, max_chunks, 2, page bytes]
+  uint8_t* snap;      // [R, H_kv, max_chunks, MAX_SPAN, 2, page bytes]
   int R, B, H_kv, D, page_size, num_pages, max_pages, C_max, k_loc, policy, es;
+  int L;              // layers whose working sets enter the decision (ws_counts [L, R, H_kv, 2])
+  int span;           // pages a compaction of this call may shift by (1, or 2 when Shrink can occur)
   int chunk_pages, max_chunks, window_pages;
   int log_b, log_kq, log_vq, log_qpp;  // log2 of page size, 16-byte pieces per key row / value row / page
   double tau;
@@ -97,7 +101,7 @@ __device__ bool trend_exceeds(long long Dsum, long long HN, double tau) {
 constexpr int DA_THREADS = 1024;
 constexpr int DA_MAX_R = 1024;
 enum : int {
-  F_VALID = 1, F_GROW = 2, F_SLOT = 4, F_EMPTY = 8, F_CHECK = 16, F_BAD = 32
+  F_VALID = 1, F_GROW = 2, F_SLOT = 4, F_EMPTY = 8, F_CHECK = 16, F_BAD = 32, F_SHRINK = 64
 };
 enum : int { O_NONE = 0, O_GROW = 1, O_IDENTITY = 2, O_COMPACT = 3 };
 
@@ -125,6 +129,7 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
   const int tid = threadIdx.x;
   const int b = P.page_size, R = P.R;
   __shared__ int s_flags[DA_MAX_R], s_cnt[DA_MAX_R], s_pn[DA_MAX_R], s_ndest[DA_MAX_R];
+  __shared__ unsigned char s_shr[DA_MAX_R];
   __shared__ int s_r[DA_MAX_R], s_top[DA_MAX_R], s_relbase[DA_MAX_R], s_pref[DA_MAX_R + 1];
   __shared__ int s_w[DA_THREADS / GP_WAVE];
   __shared__ int s_any_repl, s_top_end, s_nrel;
@@ -149,33 +154,41 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
       n = ctx == 0 ? 0 : ((ctx + b - 1) / b - 1) * b;
       ok = n == nc;
     }
-    long long dsum = 0;  // sum over KV heads of K^S - K^L
+    long long dsum = 0;  // sum over layers and KV heads of K^S - K^L
     if (ok) {
       bool bad_ws = false;
-      for (int h = 0; h < P.H_kv; ++h) {
-        const int ks = P.ws_counts[((size_t)i * P.H_kv + h) * 2 + 0];
-        const int kl = P.ws_counts[((size_t)i * P.H_kv + h) * 2 + 1];
-        if (ks < 0 || kl < 0) bad_ws = true;
-        dsum += (long long)ks - kl;
-      }
+      for (int l = 0; l < P.L; ++l)
+        for (int h = 0; h < P.H_kv; ++h) {
+          const int32_t* w = P.ws_counts + (((size_t)l * P.R + i) * P.H_kv + h) * 2;
+          const int ks = w[0], kl = w[1];
+          if (ks < 0 || kl < 0) bad_ws = true;
+          dsum += (long long)ks - kl;
+        }
       if (n > 0 && bad_ws) ok = false;
     }
     int flags = 0, ndest = 0;
     if (ok) {
       flags |= F_VALID;
       const int pol = P.policies ? P.policies[i] : P.policy;
-      bool want_grow;
+      const long long HN = (long long)P.L * P.H_kv * n;  // Delta = dsum / HN
+      bool want_grow, want_shrink = false;
       if (pol == GP_POLICY_FORCE_COMPRESS) want_grow = false;
       else if (pol == GP_POLICY_FORCE_GROW || n == 0) want_grow = true;
       else {
-        const bool g = trend_exceeds(dsum, (long long)P.H_kv * n, P.tau);
+        const bool g = trend_exceeds(dsum, HN, P.tau);
         want_grow = (pol == GP_POLICY_INVERSE) ? !g : g;
+        // GrowPage-Shrink (Eq. 13): Delta < -0.005 = -1/200, decided exactly
+        if (!want_grow && pol == GP_POLICY_SHRINK) want_shrink = dsum * 200 < -HN;
       }
+      // a Shrink must leave a capacity of at least SHRINK_MIN_CAPACITY tokens
+      const bool shrink = want_shrink && Pn >= 2 && (long)(Pn - 1) * b >= SHRINK_MIN_CAPACITY;
       if (want_grow) flags |= F_GROW;
+      if (shrink) flags |= F_SHRINK;
       if (Pn < P.max_pages) flags |= F_SLOT;
       if (n == 0) flags |= F_EMPTY;
       const int R_n = ctx - n;
-      const int K_t = min(n, max(0, (Pn - 1) * b - R_n));
+      const int keep = shrink ? Pn - 2 : Pn - 1;  // pages of history plus recent tokens kept
+      const int K_t = min(n, max(0, keep * b - R_n));
       const int E = n - K_t;
       inf.P = Pn;
       inf.ctx_old = ctx;
@@ -235,9 +248,10 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
       int out = O_NONE, dec = GP_DECISION_NO_PAGES;
       s_top[i] = top;
       s_relbase[i] = nrel;
+      bool shr = false;
       if (fl & F_VALID) {
         bool compress = true;
-        int code = GP_DECISION_COMPRESS;
+        int code = (fl & F_SHRINK) ? GP_DECISION_SHRINK : GP_DECISION_COMPRESS;
         if (fl & F_GROW) {
           if (top > 0 && (fl & F_SLOT)) {
             --top;
@@ -252,23 +266,29 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
         }
         if (compress) {
           const int E = fl >> 8;
+          shr = (fl & F_SHRINK) != 0;
           if (E == 0) {
-            out = O_IDENTITY;
+            out = O_IDENTITY;  // nothing moves; a Shrink still hands back its last page
             dec = code;
+            nrel += shr ? 1 : 0;
           } else if (E > MAX_EVICT) {
-            dec = GP_DECISION_NO_PAGES;  // unreachable for page sizes <= 32 (E <= page_size)
+            // unreachable for Compress & Hold (E <= page_size); a Shrink of 32-token pages
+            dec = GP_DECISION_NO_PAGES;
+            shr = false;
           } else if ((fl & F_BAD) || s_cnt[i] > top) {
             dec = GP_DECISION_NO_PAGES;
+            shr = false;
           } else {
             out = O_COMPACT;
             dec = code;
             top -= s_cnt[i];
-            nrel += s_cnt[i];
+            nrel += s_cnt[i] + (shr ? 1 : 0);  // the Shrink's last page follows its replacements
             any |= s_cnt[i] > 0;
           }
         }
       }
       s_flags[i] = (out << 4) | dec;  // outcome for phase D
+      s_shr[i] = shr ? 1 : 0;
     }
     s_top_end = top;
     s_nrel = nrel;
@@ -298,6 +318,15 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
       P.info[i].first_repl = s_ndest[i];
     } else {
       P.info[i].mode = MODE_NONE;
+    }
+    if (s_shr[i]) {
+      // Shrink: the last page leaves the block table (no destination page is that high) and is
+      // released after this request's replaced pages
+      const int Pn = P.info[i].P;
+      const size_t e = (size_t)r * P.max_pages + Pn - 1;
+      P.rel[s_relbase[i] + (out == O_COMPACT ? s_cnt[i] : 0)] = P.block_tables[e];
+      P.block_tables[e] = -1;
+      P.n_pages[r] = Pn - 1;
     }
   }
   // shared pages of compacting requests get private replacements, popped in ascending logical
@@ -560,12 +589,19 @@ __device__ __forceinline__ size_t page_bytes(const CParams& P) { return (size_t)
 __device__ __forceinline__ size_t pool_off(const CParams& P, int pg, int h) {
   return ((size_t)pg * P.H_kv + h) * page_bytes(P);
 }
-__device__ __forceinline__ uint8_t* snap_ptr(const CParams& P, int i, int h, int c, int which) {
-  return P.snap + ((((size_t)i * P.H_kv + h) * P.max_chunks + c) * 2 + which) * page_bytes(P);
+// saved page lp of a head: chunk lp / chunk_pages, slot lp % chunk_pages (< MAX_SPAN)
+__device__ __forceinline__ uint8_t* snap_ptr(const CParams& P, int i, int h, int lp, int which) {
+  const int c = lp / P.chunk_pages, s = lp % P.chunk_pages;
+  return P.snap + (((((size_t)i * P.H_kv + h) * P.max_chunks + c) * MAX_SPAN + s) * 2 + which) *
+                      page_bytes(P);
 }
-// does the chunk that ends at logical page lp read lp from the snapshot?
-__device__ __forceinline__ bool from_snapshot(const CParams& P, int lp, int dp0, int n_dest) {
-  return (lp % P.chunk_pages) == 0 && lp > dp0 && lp < n_dest;
+// does chunk c read logical page lp from the snapshot? Only the first `span` pages of the next
+// chunk, and only those that chunk rewrites (pages below n_dest): the workgroup of chunk c + 1
+// may have rewritten them by the time chunk c reads them. Pages of chunk c itself are read before
+// the same workgroup writes them.
+__device__ __forceinline__ bool from_snapshot(const CParams& P, int lp, int c, int n_dest) {
+  const int first = (c + 1) * P.chunk_pages;
+  return lp >= first && lp < first + P.span && lp < n_dest;
 }
 
 // List of the (request, head, chunk) items that compaction rewrites: for a compacting head the
@@ -595,26 +631,27 @@ __global__ __launch_bounds__(DA_THREADS) void chunk_list_kernel(CParams P) {
   if (threadIdx.x == 0) *P.n_items = carry;
 }
 
-// The first page of the next chunk, saved before any chunk is rewritten (it is that chunk's to
-// rewrite, and this chunk's last source page). Workgroups stride over the work list.
+// The first `span` pages of the next chunk, saved before any chunk is rewritten (they are that
+// chunk's to rewrite, and this chunk's last source pages). Workgroups stride over the work list.
 __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
   const int n_items = *P.n_items;
   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
     const int2 item = P.items[it];
-    const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y + 1;
+    const int i = item.x / P.H_kv, h = item.x % P.H_kv;
     const Info inf = P.info[i];
-    const int lp = c * P.chunk_pages;
-    const int dp0 = P.dp0[item.x];
-    if (!from_snapshot(P, lp, dp0, inf.n_dest)) continue;  // uniform over the workgroup
-    const int pg = P.old_bt[(size_t)i * P.max_pages + lp];
-    const size_t nb = page_bytes(P);
-    const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(P.k + pool_off(P, pg, h));
-    const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(P.v + pool_off(P, pg, h));
-    u32x4_t* kd = reinterpret_cast<u32x4_t*>(snap_ptr(P, i, h, c, 0));
-    u32x4_t* vd = reinterpret_cast<u32x4_t*>(snap_ptr(P, i, h, c, 1));
-    for (size_t q = threadIdx.x; q < nb / 16; q += CP_THREADS) {
-      kd[q] = ks[q];
-      vd[q] = vs[q];
+    for (int s = 0; s < P.span; ++s) {
+      const int lp = (item.y + 1) * P.chunk_pages + s;
+      if (!from_snapshot(P, lp, item.y, inf.n_dest)) continue;  // uniform over the workgroup
+      const int pg = P.old_bt[(size_t)i * P.max_pages + lp];
+      const size_t nb = page_bytes(P);
+      const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(P.k + pool_off(P, pg, h));
+      const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(P.v + pool_off(P, pg, h));
+      u32x4_t* kd = reinterpret_cast<u32x4_t*>(snap_ptr(P, i, h, lp, 0));
+      u32x4_t* vd = reinterpret_cast<u32x4_t*>(snap_ptr(P, i, h, lp, 1));
+      for (size_t q = threadIdx.x; q < nb / 16; q += CP_THREADS) {
+        kd[q] = ks[q];
+        vd[q] = vs[q];
+      }
     }
   }
 }
@@ -625,9 +662,10 @@ __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
 // tabulates the source slot of every destination slot, reads the key rows it will write into
 // registers (rows are contiguous, 16 bytes per lane), stages the source value pages (token-
 // contiguous inside a page, so a gather needs them whole) in LDS, and only then writes the
-// window's destination pages. Inside a chunk the page after a window is not yet rewritten when
-// it is read; the first page of the next chunk, which another workgroup rewrites, comes from the
-// snapshot.
+// window's destination pages. A shift of at most `span` pages means a window of destination
+// pages [w0, w1) reads source pages [w0, w1 + span - 1]; inside a chunk those are not yet
+// rewritten when read, and the first `span` pages of the next chunk, which another workgroup
+// rewrites, come from the snapshot.
 __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   const int n_items = *P.n_items;
   for (int item_k = blockIdx.x; item_k < n_items; item_k += gridDim.x) {
@@ -641,9 +679,9 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   const int dp_lo = max(dp0, c * L), dp_hi = min((c + 1) * L, inf.n_dest);
   __shared__ int s_thr[MAX_EVICT];
   __shared__ int s_src[MAX_WINDOW_SLOTS];
-  // source pages dp_lo .. dp_hi: byte offset of (page, head) in the pool, or -1 for the snapshot,
-  // or -2 past the old pages; destination pages dp_lo .. dp_hi - 1: byte offset in the pool
-  __shared__ long long s_soff[CHUNK_PAGES + 1], s_doff[CHUNK_PAGES];
+  // source pages dp_lo .. dp_hi + span - 1: byte offset of (page, head) in the pool, or -1 for the
+  // snapshot, or -2 past the old pages; destination pages dp_lo .. dp_hi - 1: pool byte offset
+  __shared__ long long s_soff[CHUNK_PAGES + MAX_SPAN], s_doff[CHUNK_PAGES];
   extern __shared__ __align__(16) uint8_t s_v[];  // value pages of the window
   const int E = inf.E;
   const size_t pb = page_bytes(P);
@@ -651,11 +689,11 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
     s_thr[threadIdx.x] = threadIdx.x < E
                              ? P.ev[((size_t)i * P.H_kv + h) * MAX_EVICT + threadIdx.x] - (int)threadIdx.x
                              : INT_MAX;
-  if (threadIdx.x <= dp_hi - dp_lo) {
+  if (threadIdx.x < dp_hi - dp_lo + P.span) {
     const int lp = dp_lo + threadIdx.x;
     long long so = -2;
     if (lp < inf.P)
-      so = from_snapshot(P, lp, dp0, inf.n_dest) ? -1
+      so = from_snapshot(P, lp, c, inf.n_dest) ? -1
                                                  : (long long)pool_off(P, P.old_bt[(size_t)i * P.max_pages + lp], h);
     s_soff[threadIdx.x] = so;
     if (lp < dp_hi) s_doff[threadIdx.x] = (long long)pool_off(P, P.block_tables[(size_t)inf.r * P.max_pages + lp], h);
@@ -664,10 +702,9 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   const int lkq = P.log_kq, lvq = P.log_vq;
   const int krow = D * es;
   const int per = 16 / es;                      // elements per 16-byte piece
-  const uint8_t* snapk = snap_ptr(P, i, h, 0, 0);
   for (int w0 = dp_lo; w0 < dp_hi; w0 += W) {
     const int w1 = min(w0 + W, dp_hi);          // destination pages [w0, w1)
-    const int nsrc = w1 - w0 + 1;               // source pages [w0, w1]
+    const int nsrc = w1 - w0 + P.span;          // source pages [w0, w1 + span - 1]
     const int nslots = (w1 - w0) << lb;
     __syncthreads();  // tables are set; the previous window is done with LDS
     for (int q = threadIdx.x; q < nslots; q += CP_THREADS) {
@@ -681,7 +718,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
     // issue every read of the window before using any: value pieces, then key pieces
     auto src_page = [&](int lp, int which) -> const uint8_t* {
       const long long so = s_soff[lp - dp_lo];
-      if (so == -1) return snapk + (((size_t)(lp / L) * 2 + which) * pb);
+      if (so == -1) return snap_ptr(P, i, h, lp, which);
       return (which ? P.v : P.k) + so;
     };
     const int nv = nsrc << lqpp;
@@ -746,14 +783,14 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   }
 }
 
-// Window of W destination pages: LDS holds the W + 1 source value pages, and the W * b key rows
-// must fit K_PIECES 16-byte pieces per thread.
-int window_pages_for(int page_size, int D, int es) {
+// Window of W destination pages: LDS holds the W + span source value pages, and the W * b key
+// rows must fit K_PIECES 16-byte pieces per thread.
+int window_pages_for(int page_size, int D, int es, int span) {
   const long pv = (long)page_size * D * es;
-  int W = (int)(CP_LDS_BYTES / pv) - 1;
+  int W = (int)(CP_LDS_BYTES / pv) - span;
   W = std::max(1, std::min(8, W));
   while (W > 1 && ((long)W * page_size * D * es > (long)K_PIECES * CP_THREADS * 16 ||
-                   (long)(W + 1) * page_size * D * es > (long)V_PIECES * CP_THREADS * 16))
+                   (long)(W + span) * page_size * D * es > (long)V_PIECES * CP_THREADS * 16))
     --W;
   return W;
 }
@@ -780,23 +817,216 @@ int ilog2(int v) {
 
 }  // namespace
 
-extern "C" size_t gp_compact_or_grow_workspace_size(int R, int H_kv, int max_pages, int page_size,
-                                                   int C_max) {
-  (void)C_max;
-  if (R <= 0 || H_kv <= 0 || max_pages <= 0 || page_size <= 0) return 0;
+namespace {
+
+// Workspace: per call the request records, old block-table rows and release list; per layer the
+// evicted lists, first changed pages and chunk work list; shared by the layers (used one layer
+// at a time, in stream order) the selection survivors and the chunk snapshots.
+struct WsLayout {
+  size_t info, old_bt, rel, layer0, layer_bytes, ev, dp0, items, n_items, cand, snap, total;
+};
+
+WsLayout ws_layout(int L, int R, int H_kv, int max_pages, int page_size) {
   // snapshots sized for the widest supported element (fp32) and head_dim 128
   const int es = 4, D = 128;
   const size_t max_chunks = (size_t)(max_pages + CHUNK_PAGES - 1) / CHUNK_PAGES;
-  size_t bytes = 0;
-  bytes += (size_t)R * sizeof(Info);
-  bytes += (size_t)R * max_pages * 4 * 2;               // old_bt, rel
-  bytes += (size_t)R * H_kv * MAX_EVICT * 4;
-  bytes += (size_t)R * H_kv * 4;
-  bytes = (bytes + 255) & ~(size_t)255;
-  bytes += (size_t)R * H_kv * SEL_MAX_CHUNKS * MAX_EVICT * 8;
-  bytes += (size_t)R * H_kv * max_chunks * sizeof(int2) + 256;
-  bytes += (size_t)R * H_kv * max_chunks * 2 * (size_t)page_size * D * es;
-  return bytes;
+  WsLayout w{};
+  size_t off = 0;
+  w.info = off;
+  off += (size_t)R * sizeof(Info);
+  w.old_bt = off;
+  off += (size_t)R * max_pages * 4;
+  w.rel = off;
+  off += (size_t)R * max_pages * 4;
+  off = (off + 255) & ~(size_t)255;
+  w.layer0 = off;
+  w.ev = 0;
+  size_t lo = (size_t)R * H_kv * MAX_EVICT * 4;
+  w.dp0 = lo;
+  lo += (size_t)R * H_kv * 4;
+  lo = (lo + 15) & ~(size_t)15;
+  w.items = lo;
+  lo += (size_t)R * H_kv * max_chunks * sizeof(int2);
+  w.n_items = lo;
+  lo += 256;
+  w.layer_bytes = (lo + 255) & ~(size_t)255;
+  off += (size_t)L * w.layer_bytes;
+  w.cand = off;
+  off += (size_t)R * H_kv * SEL_MAX_CHUNKS * MAX_EVICT * 8;
+  w.snap = off;
+  off += (size_t)R * H_kv * max_chunks * MAX_SPAN * 2 * (size_t)page_size * D * es;
+  w.total = off;
+  return w;
+}
+
+int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_short,
+                 const float* a_long, int C_max, const int32_t* ws_counts, const int32_t* n_cand,
+                 double tau, int k_loc, int policy, const int32_t* policies,
+                 gp_kv_cache* const* kv_layers, int32_t* block_tables, int32_t* n_pages,
+                 int max_pages, int32_t* context_lens, int32_t* refcount, int32_t* free_stack,
+                 int32_t* free_top, int32_t* decision, int32_t* kept_idx, void* workspace,
+                 size_t workspace_bytes, int phases, void* stream) {
+  if (R < 0 || B < 0 || L <= 0 || C_max <= 0 || !kv_layers || max_pages <= 0 || k_loc < 0)
+    return GP_ERR_INVALID;
+  if (phases < 1 || phases > (GP_PHASE_PLAN | GP_PHASE_MOVE)) return GP_ERR_INVALID;
+  if (R == 0) return GP_OK;
+  if (R > DA_MAX_R) return GP_ERR_UNSUPPORTED;
+  if (!req_idx || !a_short || !a_long || !ws_counts || !n_cand || !block_tables || !n_pages ||
+      !context_lens || !refcount || !free_stack || !free_top || !decision || !kept_idx)
+    return GP_ERR_INVALID;
+  if (policy < GP_POLICY_AUTO || policy > GP_POLICY_SHRINK) return GP_ERR_INVALID;
+  if (!(tau == tau)) return GP_ERR_INVALID;
+  const gp_kv_cache* kv = kv_layers[0];
+  if (!kv) return GP_ERR_INVALID;
+  const int H_kv = kv->num_kv_heads, D = kv->head_dim, b = kv->page_size;
+  for (int l = 0; l < L; ++l) {
+    const gp_kv_cache* c = kv_layers[l];
+    if (!c || !c->k || !c->v) return GP_ERR_INVALID;
+    if (c->page_tag) return GP_ERR_UNSUPPORTED;
+    if (c->num_kv_heads != H_kv || c->head_dim != D || c->page_size != b ||
+        c->num_pages != kv->num_pages || c->dtype != kv->dtype)
+      return GP_ERR_INVALID;  // the layers share block tables and the page pool
+  }
+  if (H_kv <= 0 || kv->num_pages <= 0) return GP_ERR_INVALID;
+  if (kv->dtype != GP_F32 && kv->dtype != GP_BF16) return GP_ERR_INVALID;
+  if (D != 64 && D != 128) return GP_ERR_UNSUPPORTED;
+  if (b != 16 && b != 32) return GP_ERR_UNSUPPORTED;
+  if (policy == GP_POLICY_SHRINK && b != 16) return GP_ERR_UNSUPPORTED;  // E <= 2b <= MAX_EVICT
+  // a Shrink moves tokens by up to two pages; only calls where one can occur pay for that
+  const int span = (policy == GP_POLICY_SHRINK || policies) ? MAX_SPAN : 1;
+  const int es = kv->dtype == GP_F32 ? 4 : 2;
+  const int W = window_pages_for(b, D, es, span);
+  {
+    const size_t lds = (size_t)(W + span) * b * D * es;
+    if (lds + sizeof(int) * (MAX_EVICT + MAX_WINDOW_SLOTS) > 64 * 1024) return GP_ERR_UNSUPPORTED;
+    if ((long)W * b * D * es > (long)K_PIECES * CP_THREADS * 16) return GP_ERR_UNSUPPORTED;
+    if ((long)(W + span) * b * D * es > (long)V_PIECES * CP_THREADS * 16) return GP_ERR_UNSUPPORTED;
+  }
+  if (C_max % 4 || C_max > MAX_CAND) return GP_ERR_UNSUPPORTED;
+  const WsLayout wl = ws_layout(L, R, H_kv, max_pages, b);
+  if (!workspace || workspace_bytes < wl.total) return GP_ERR_WORKSPACE;
+
+  CParams P{};
+  P.req_idx = req_idx;
+  P.ws_counts = ws_counts;
+  P.n_cand = n_cand;
+  P.policies = policies;
+  P.block_tables = block_tables;
+  P.n_pages = n_pages;
+  P.context_lens = context_lens;
+  P.refcount = refcount;
+  P.free_stack = free_stack;
+  P.free_top = free_top;
+  P.decision = decision;
+  P.R = R;
+  P.B = B;
+  P.L = L;
+  P.span = span;
+  P.H_kv = H_kv;
+  P.D = D;
+  P.page_size = b;
+  P.num_pages = kv->num_pages;
+  P.max_pages = max_pages;
+  P.C_max = C_max;
+  P.k_loc = k_loc;
+  P.policy = policy;
+  P.es = es;
+  P.tau = tau;
+  P.chunk_pages = CHUNK_PAGES;
+  P.max_chunks = (max_pages + CHUNK_PAGES - 1) / CHUNK_PAGES;
+  P.window_pages = W;
+  P.log_b = ilog2(b);
+  P.log_kq = ilog2(D * es / 16);
+  P.log_vq = ilog2(b * es / 16);
+  P.log_qpp = ilog2(b * D * es / 16);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  P.info = reinterpret_cast<Info*>(ws + wl.info);
+  P.old_bt = reinterpret_cast<int32_t*>(ws + wl.old_bt);
+  P.rel = reinterpret_cast<int32_t*>(ws + wl.rel);
+  P.cand = reinterpret_cast<unsigned long long*>(ws + wl.cand);
+  P.snap = ws + wl.snap;
+  // the parameters of layer l: its scores, kept indices, pools and per-layer workspace
+  const size_t plane = (size_t)R * H_kv * C_max;
+  auto layer = [&](int l) {
+    CParams Q = P;
+    Q.a_short = a_short + (size_t)l * plane;
+    Q.a_long = a_long + (size_t)l * plane;
+    Q.kept_idx = kept_idx + (size_t)l * plane;
+    Q.k = static_cast<uint8_t*>(kv_layers[l]->k);
+    Q.v = static_cast<uint8_t*>(kv_layers[l]->v);
+    uint8_t* lw = ws + wl.layer0 + (size_t)l * wl.layer_bytes;
+    Q.ev = reinterpret_cast<int32_t*>(lw + wl.ev);
+    Q.dp0 = reinterpret_cast<int32_t*>(lw + wl.dp0);
+    Q.items = reinterpret_cast<int2*>(lw + wl.items);
+    Q.n_items = reinterpret_cast<int32_t*>(lw + wl.n_items);
+    return Q;
+  };
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (phases & GP_PHASE_PLAN) {
+    // one decision and allocation per request for all layers (Eq. 8 over layers and KV heads)
+    hipLaunchKernelGGL(decide_alloc_kernel, dim3(1), dim3(DA_THREADS), 0, s, layer(0));
+    GP_CHECK_LAUNCH();
+    const int nch = (C_max + SEL_T * b - 1) / (SEL_T * b);
+    const dim3 g(nch, H_kv, R);
+    for (int l = 0; l < L; ++l) {  // selection per layer and KV head (Eq. 9-10)
+      const CParams Q = layer(l);
+      if (b == 16) hipLaunchKernelGGL(select_local_kernel<16>, g, dim3(SEL_T), 0, s, Q);
+      else hipLaunchKernelGGL(select_local_kernel<32>, g, dim3(SEL_T), 0, s, Q);
+      GP_CHECK_LAUNCH();
+      hipLaunchKernelGGL(select_merge_kernel, dim3(H_kv, R), dim3(GP_WAVE), 0, s, Q);
+      GP_CHECK_LAUNCH();
+      if (b == 16) hipLaunchKernelGGL(select_write_kernel<16>, g, dim3(SEL_T), 0, s, Q);
+      else hipLaunchKernelGGL(select_write_kernel<32>, g, dim3(SEL_T), 0, s, Q);
+      GP_CHECK_LAUNCH();
+      hipLaunchKernelGGL(chunk_list_kernel, dim3(1), dim3(DA_THREADS), 0, s, Q);
+      GP_CHECK_LAUNCH();
+    }
+  }
+  if (!(phases & GP_PHASE_MOVE)) return GP_OK;
+  const int cus = device_cus();
+  const size_t lds = (size_t)(W + span) * b * D * es;
+  for (int l = 0; l < L; ++l) {
+    const CParams Q = layer(l);
+    hipLaunchKernelGGL(snapshot_kernel, dim3(std::max(1, std::min(4 * cus, R * H_kv * P.max_chunks))),
+                       dim3(CP_THREADS), 0, s, Q);
+    GP_CHECK_LAUNCH();
+    hipLaunchKernelGGL(compact_kernel, dim3(std::max(1, std::min(2 * cus, R * H_kv * P.max_chunks))),
+                       dim3(CP_THREADS), lds, s, Q);
+    GP_CHECK_LAUNCH();
+  }
+  return GP_OK;
+}
+
+}  // namespace
+
+extern "C" size_t gp_compact_or_grow_layers_workspace_size(int num_layers, int R, int H_kv,
+                                                          int max_pages, int page_size,
+                                                          int C_max) {
+  (void)C_max;
+  if (num_layers <= 0 || R <= 0 || H_kv <= 0 || max_pages <= 0 || page_size <= 0) return 0;
+  return ws_layout(num_layers, R, H_kv, max_pages, page_size).total;
+}
+
+extern "C" size_t gp_compact_or_grow_workspace_size(int R, int H_kv, int max_pages, int page_size,
+                                                   int C_max) {
+  return gp_compact_or_grow_layers_workspace_size(1, R, H_kv, max_pages, page_size, C_max);
+}
+
+extern "C" int gp_compact_or_grow_layers(const int32_t* req_idx, int R, int B, int num_layers,
+                                         const float* a_short, const float* a_long, int C_max,
+                                         const int32_t* ws_counts, const int32_t* n_cand,
+                                         double tau, int k_loc, int policy,
+                                         const int32_t* policies, gp_kv_cache* const* kv_layers,
+                                         int32_t* block_tables, int32_t* n_pages, int max_pages,
+                                         int32_t* context_lens, int32_t* refcount,
+                                         int32_t* free_stack, int32_t* free_top,
+                                         int32_t* decision, int32_t* kept_idx, void* workspace,
+                                         size_t workspace_bytes, int phases, void* stream) {
+  return compact_impl(req_idx, R, B, num_layers, a_short, a_long, C_max, ws_counts, n_cand, tau,
+                      k_loc, policy, policies, kv_layers, block_tables, n_pages, max_pages,
+                      context_lens, refcount, free_stack, free_top, decision, kept_idx, workspace,
+                      workspace_bytes, phases, stream);
 }
 
 extern "C" int gp_compact_or_grow_phase(const int32_t* req_idx, int R, int B,
@@ -808,118 +1038,11 @@ extern "C" int gp_compact_or_grow_phase(const int32_t* req_idx, int R, int B,
                                         int32_t* free_stack, int32_t* free_top, int32_t* decision,
                                         int32_t* kept_idx, void* workspace,
                                         size_t workspace_bytes, int phases, void* stream) {
-  if (R < 0 || B < 0 || C_max <= 0 || !kv || max_pages <= 0 || k_loc < 0) return GP_ERR_INVALID;
-  if (phases < 1 || phases > (GP_PHASE_PLAN | GP_PHASE_MOVE)) return GP_ERR_INVALID;
-  if (R == 0) return GP_OK;
-  if (R > DA_MAX_R) return GP_ERR_UNSUPPORTED;
-  if (!req_idx || !a_short || !a_long || !ws_counts || !n_cand || !block_tables || !n_pages ||
-      !context_lens || !refcount || !free_stack || !free_top || !decision || !kept_idx || !kv->k ||
-      !kv->v)
-    return GP_ERR_INVALID;
-  if (policy < GP_POLICY_AUTO || policy > GP_POLICY_INVERSE) return GP_ERR_INVALID;
-  if (!(tau == tau)) return GP_ERR_INVALID;
-  if (kv->page_tag) return GP_ERR_UNSUPPORTED;
-  const int H_kv = kv->num_kv_heads, D = kv->head_dim, b = kv->page_size;
-  if (H_kv <= 0 || kv->num_pages <= 0) return GP_ERR_INVALID;
-  if (kv->dtype != GP_F32 && kv->dtype != GP_BF16) return GP_ERR_INVALID;
-  if (D != 64 && D != 128) return GP_ERR_UNSUPPORTED;
-  if (b != 16 && b != 32) return GP_ERR_UNSUPPORTED;
-  {
-    const int es = kv->dtype == GP_F32 ? 4 : 2;
-    const int W = window_pages_for(b, D, es);
-    const size_t lds = (size_t)(W + 1) * b * D * es;
-    if (lds + sizeof(int) * (MAX_EVICT + MAX_WINDOW_SLOTS) > 64 * 1024) return GP_ERR_UNSUPPORTED;
-    if ((long)W * b * D * es > (long)K_PIECES * CP_THREADS * 16) return GP_ERR_UNSUPPORTED;
-    if ((long)(W + 1) * b * D * es > (long)V_PIECES * CP_THREADS * 16) return GP_ERR_UNSUPPORTED;
-  }
-  if (C_max % 4 || C_max > MAX_CAND) return GP_ERR_UNSUPPORTED;
-  const size_t need = gp_compact_or_grow_workspace_size(R, H_kv, max_pages, b, C_max);
-  if (!workspace || workspace_bytes < need) return GP_ERR_WORKSPACE;
-
-  CParams P{};
-  P.req_idx = req_idx;
-  P.a_short = a_short;
-  P.a_long = a_long;
-  P.ws_counts = ws_counts;
-  P.n_cand = n_cand;
-  P.policies = policies;
-  P.k = static_cast<uint8_t*>(kv->k);
-  P.v = static_cast<uint8_t*>(kv->v);
-  P.block_tables = block_tables;
-  P.n_pages = n_pages;
-  P.context_lens = context_lens;
-  P.refcount = refcount;
-  P.free_stack = free_stack;
-  P.free_top = free_top;
-  P.decision = decision;
-  P.kept_idx = kept_idx;
-  P.R = R;
-  P.B = B;
-  P.H_kv = H_kv;
-  P.D = D;
-  P.page_size = b;
-  P.num_pages = kv->num_pages;
-  P.max_pages = max_pages;
-  P.C_max = C_max;
-  P.k_loc = k_loc;
-  P.policy = policy;
-  P.es = kv->dtype == GP_F32 ? 4 : 2;
-  P.tau = tau;
-  P.chunk_pages = CHUNK_PAGES;
-  P.max_chunks = (max_pages + CHUNK_PAGES - 1) / CHUNK_PAGES;
-  P.window_pages = window_pages_for(b, D, P.es);
-  P.log_b = ilog2(b);
-  P.log_kq = ilog2(D * P.es / 16);
-  P.log_vq = ilog2(b * P.es / 16);
-  P.log_qpp = ilog2(b * D * P.es / 16);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  size_t off = 0;
-  P.info = reinterpret_cast<Info*>(ws + off);
-  off += (size_t)R * sizeof(Info);
-  P.old_bt = reinterpret_cast<int32_t*>(ws + off);
-  off += (size_t)R * max_pages * 4;
-  P.rel = reinterpret_cast<int32_t*>(ws + off);
-  off += (size_t)R * max_pages * 4;
-  P.ev = reinterpret_cast<int32_t*>(ws + off);
-  off += (size_t)R * H_kv * MAX_EVICT * 4;
-  P.dp0 = reinterpret_cast<int32_t*>(ws + off);
-  off += (size_t)R * H_kv * 4;
-  off = (off + 255) & ~(size_t)255;
-  P.cand = reinterpret_cast<unsigned long long*>(ws + off);
-  off += (size_t)R * H_kv * SEL_MAX_CHUNKS * MAX_EVICT * 8;
-  P.items = reinterpret_cast<int2*>(ws + off);
-  off += (size_t)R * H_kv * P.max_chunks * sizeof(int2);
-  P.n_items = reinterpret_cast<int32_t*>(ws + off);
-  off += 256;
-  P.snap = ws + off;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (phases & GP_PHASE_PLAN) {
-    hipLaunchKernelGGL(decide_alloc_kernel, dim3(1), dim3(DA_THREADS), 0, s, P);
-    GP_CHECK_LAUNCH();
-    const int nch = (C_max + SEL_T * b - 1) / (SEL_T * b);
-    const dim3 g(nch, H_kv, R);
-    if (b == 16) hipLaunchKernelGGL(select_local_kernel<16>, g, dim3(SEL_T), 0, s, P);
-    else hipLaunchKernelGGL(select_local_kernel<32>, g, dim3(SEL_T), 0, s, P);
-    GP_CHECK_LAUNCH();
-    hipLaunchKernelGGL(select_merge_kernel, dim3(H_kv, R), dim3(GP_WAVE), 0, s, P);
-    GP_CHECK_LAUNCH();
-    if (b == 16) hipLaunchKernelGGL(select_write_kernel<16>, g, dim3(SEL_T), 0, s, P);
-    else hipLaunchKernelGGL(select_write_kernel<32>, g, dim3(SEL_T), 0, s, P);
-    GP_CHECK_LAUNCH();
-    hipLaunchKernelGGL(chunk_list_kernel, dim3(1), dim3(DA_THREADS), 0, s, P);
-    GP_CHECK_LAUNCH();
-  }
-  if (!(phases & GP_PHASE_MOVE)) return GP_OK;
-  const int cus = device_cus();
-  hipLaunchKernelGGL(snapshot_kernel, dim3(std::max(1, std::min(4 * cus, R * H_kv * P.max_chunks))),
-                     dim3(CP_THREADS), 0, s, P);
-  GP_CHECK_LAUNCH();
-  const size_t lds = (size_t)(P.window_pages + 1) * b * D * P.es;
-  hipLaunchKernelGGL(compact_kernel, dim3(std::max(1, std::min(2 * cus, R * H_kv * P.max_chunks))),
-                     dim3(CP_THREADS), lds, s, P);
-  GP_CHECK_LAUNCH();
-  return GP_OK;
+  gp_kv_cache* one[1] = {kv};
+  return compact_impl(req_idx, R, B, 1, a_short, a_long, C_max, ws_counts, n_cand, tau, k_loc,
+                      policy, policies, kv ? one : nullptr, block_tables, n_pages, max_pages,
+                      context_lens, refcount, free_stack, free_top, decision, kept_idx, workspace,
+                      workspace_bytes, phases, stream);
 }
 
 extern "C" int gp_compact_or_grow(const int32_t* req_idx, int R, int B, const float* a_short,

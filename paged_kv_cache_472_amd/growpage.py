@@ -14,8 +14,8 @@ LIB_PATH = os.path.join(_HERE, "_lib", "libgrowpage.so")
 
 GP_F32, GP_BF16 = 0, 1
 TAG_RELEASE, TAG_FP8, TAG_BF16, TAG_INT4 = 0, 1, 2, 3
-COMPRESS, GROW, GROW_FALLBACK_COMPRESS, NO_PAGES = 0, 1, 2, 3
-POLICY_AUTO, POLICY_FORCE_COMPRESS, POLICY_FORCE_GROW, POLICY_INVERSE = 0, 1, 2, 3
+COMPRESS, GROW, GROW_FALLBACK_COMPRESS, NO_PAGES, SHRINK = 0, 1, 2, 3, 4
+POLICY_AUTO, POLICY_FORCE_COMPRESS, POLICY_FORCE_GROW, POLICY_INVERSE, POLICY_SHRINK = 0, 1, 2, 3, 4
 PHASE_PLAN, PHASE_MOVE = 1, 2
 
 EXPORTED = (
@@ -24,6 +24,7 @@ EXPORTED = (
     "gp_update_query_summaries",
     "gp_score_and_working_set_workspace_size", "gp_score_and_working_set",
     "gp_compact_or_grow_workspace_size", "gp_compact_or_grow", "gp_compact_or_grow_phase",
+    "gp_compact_or_grow_layers_workspace_size", "gp_compact_or_grow_layers",
     "gp_quantize_pages_int4",
 )
 
@@ -90,6 +91,12 @@ def lib():
                                          _VP, _VP, _VP, _SZ, _VP]
         L.gp_compact_or_grow_phase.restype = _I
         L.gp_compact_or_grow_phase.argtypes = L.gp_compact_or_grow.argtypes[:-1] + [_I, _VP]
+        L.gp_compact_or_grow_layers_workspace_size.restype = _SZ
+        L.gp_compact_or_grow_layers_workspace_size.argtypes = [_I] * 6
+        L.gp_compact_or_grow_layers.restype = _I
+        L.gp_compact_or_grow_layers.argtypes = ([_VP, _I, _I, _I, _VP, _VP, _I, _VP, _VP, _D, _I, _I,
+                                                 _VP, ctypes.POINTER(ctypes.POINTER(GpKvCache))]
+                                                + [_VP, _VP, _I] + [_VP] * 6 + [_VP, _SZ, _I, _VP])
         L.gp_quantize_pages_int4.restype = _I
         L.gp_quantize_pages_int4.argtypes = [ctypes.POINTER(GpKvCache), _VP, _I, _VP]
         _lib = L
@@ -279,6 +286,39 @@ def gp_compact_or_grow(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, 
     else:
         st = lib().gp_compact_or_grow_phase(*args, int(phases), _stream())
     _check(st, "gp_compact_or_grow")
+    return decision, kept_idx
+
+
+def gp_compact_or_grow_layers_workspace_size(L, R, H_kv, max_pages, page_size, C_max):
+    return lib().gp_compact_or_grow_layers_workspace_size(L, R, H_kv, max_pages, page_size, C_max)
+
+
+def gp_compact_or_grow_layers(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, policy,
+                              caches, block_tables, n_pages, context_lens, refcount, free_stack,
+                              free_top, policies=None, decision=None, kept_idx=None,
+                              workspace=None, phases=PHASE_PLAN | PHASE_MOVE):
+    """Compress-or-grow for L layers sharing block tables: a_short / a_long [L, R, H_kv, C_max],
+    ws_counts [L, R, H_kv, 2], caches a list of L KVCache. Returns (decision [R],
+    kept_idx [L, R, H_kv, C_max])."""
+    L, R, H_kv, C_max = a_short.shape
+    dev = a_short.device
+    if decision is None:
+        decision = torch.empty((R,), dtype=torch.int32, device=dev)
+    if kept_idx is None:
+        kept_idx = torch.empty((L, R, H_kv, C_max), dtype=torch.int32, device=dev)
+    need = gp_compact_or_grow_layers_workspace_size(L, R, H_kv, block_tables.shape[1],
+                                                    caches[0].page_size, C_max)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    structs = [c.struct() for c in caches]
+    arr = (ctypes.POINTER(GpKvCache) * L)(*[ctypes.pointer(x) for x in structs])
+    st = lib().gp_compact_or_grow_layers(
+        _ptr(req_idx), R, block_tables.shape[0], L, _ptr(a_short), _ptr(a_long), C_max,
+        _ptr(ws_counts), _ptr(n_cand), float(tau), int(k_loc), int(policy), _ptr(policies), arr,
+        _ptr(block_tables), _ptr(n_pages), block_tables.shape[1], _ptr(context_lens),
+        _ptr(refcount), _ptr(free_stack), _ptr(free_top), _ptr(decision), _ptr(kept_idx),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), int(phases), _stream())
+    _check(st, "gp_compact_or_grow_layers")
     return decision, kept_idx
 
 
