@@ -11,15 +11,14 @@ region; K/V pages are left as the previous step's compaction wrote them (still v
 amount of work).
 
 By default (--overlap 1) the step overlaps the boundary pass with decoding, as GrowPage does
-(App. E.3). On the main stream the boundary requests are decoded first (a small call on copies of
-their block-table rows and lengths), then the other requests (their lengths masked to zero, so
-none of the pages the boundary pass rewrites is read; their summary update fused into the call,
-whose grid leaves --reserve-cus compute units free). A second stream meanwhile updates the
-boundary requests' summaries, scores them and plans their compress-or-grow (decisions, page
-allocation, kept tokens: bookkeeping only); the planned K/V movement runs on the main stream
-after the decode, with the whole GPU. The boundary requests' outputs stay in their own buffers.
-Every request still sees update -> decode -> boundary pass in that order. --overlap 0 runs the
-same rows one after another on one stream.
+(App. E.3). The main stream decodes every request from a copy of the block tables and lengths
+taken by the restore, with the summary update of the requests that are not at a boundary fused
+into the call and a grid that leaves --reserve-cus compute units free. A second stream meanwhile
+updates the boundary requests' summaries, scores them and plans their compress-or-grow
+(decisions, page allocation, kept tokens: bookkeeping on the live tables only); the planned K/V
+movement runs on the main stream after the decode, with the whole GPU. Every request still sees
+update -> decode -> boundary pass in that order. --overlap 0 runs the same rows one after another
+on one stream.
 
 Prints one JSON line. `value` is the step's algorithmic HBM bytes divided by the step time;
 `roofline` is the main decode call (its two kernels) against the 8 TB/s HBM peak, timed with HIP
@@ -68,8 +67,8 @@ def parse():
                     help="with --overlap 1: compute units the main decode leaves free for the "
                          "boundary pass on the second stream (its workgroup cap)")
     ap.add_argument("--overlap", type=int, default=1,
-                    help="1: the boundary requests' decode and boundary pass run on a second stream "
-                         "beside the decode of the other requests; 0: everything on one stream")
+                    help="1: the boundary pass runs on a second stream beside the decode (its K/V "
+                         "movement after it); 0: everything on one stream")
     ap.add_argument("--int4", type=int, default=1,
                     help="also time decode with every page of the batch demoted to INT4 "
                          "(PASK App. B.5) by the page quantiser (bf16 workloads)")
@@ -93,10 +92,12 @@ class Path:
         self.R = wl.req_idx.numel()
         self.overlap = bool(overlap) and self.R > 0
         # integer page state in one flat buffer so a step can restore it with one copy; with
-        # overlap it also holds the lengths the main decode sees (boundary requests masked to 0)
+        # overlap it also holds a second copy of the block tables and lengths that the decode
+        # reads, so that the boundary pass may rewrite the live ones while the decode runs
         names = ("block_tables", "n_pages", "context_lens", "refcount", "free_stack", "free_top")
         sizes = [getattr(wl, n).numel() for n in names]
-        self.meta = torch.empty(sum(sizes) + wl.B, dtype=i32, device=dev)
+        extra = wl.block_tables.numel() + wl.B
+        self.meta = torch.empty(sum(sizes) + extra, dtype=i32, device=dev)
         off = 0
         for n, sz in zip(names, sizes):
             t = getattr(wl, n)
@@ -104,10 +105,11 @@ class Path:
             view.copy_(t)
             setattr(wl, n, view)
             off += sz
-        self.ctx_main = self.meta[off:off + wl.B]
-        self.ctx_main.copy_(wl.context_lens)
-        if self.R:
-            self.ctx_main.index_fill_(0, wl.req_idx.long(), 0)
+        self.bt_dec = self.meta[off:off + wl.block_tables.numel()].view(wl.block_tables.shape)
+        self.bt_dec.copy_(wl.block_tables)
+        off += wl.block_tables.numel()
+        self.ctx_dec = self.meta[off:off + wl.B]
+        self.ctx_dec.copy_(wl.context_lens)
         self.meta0 = self.meta.clone()
         self.cache = gp.KVCache.from_workload(wl)
         B, H_q, d = wl.q.shape
@@ -139,27 +141,15 @@ class Path:
             self.cws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
             self.policies = torch.as_tensor(wl.req_policy, dtype=i32, device=dev)
         if self.overlap:
-            R = self.R
             self.stream_b = torch.cuda.Stream(device=dev)  # default priority
             self.req_l = wl.req_idx.long()
-            self.q_b = torch.empty((R, H_q, d), dtype=wl.q.dtype, device=dev)
-            self.bt_b = torch.empty((R, wl.max_pages), dtype=i32, device=dev)
-            self.ctx_b = torch.empty((R,), dtype=i32, device=dev)
-            self.out_b = torch.empty((R, H_q, d), dtype=wl.q.dtype, device=dev)
-            self.lse_b = torch.empty((R, H_q), dtype=torch.float32, device=dev)
-            n = gp.gp_paged_decode_attn_workspace_size(R, H_q, H_kv, d, wl.page_size, wl.max_context)
-            self.dws_b = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
-            # the main decode updates the summaries of the other requests; the boundary requests'
-            # own decode (second stream) updates theirs before their scores read them
+            # the decode updates the summaries of the other requests; the second stream updates
+            # the boundary requests' own before their scores read them
             slot_main = wl.slot_ids.clone()
             slot_main.index_fill_(0, self.req_l, -1)
             self.upd_main = dict(self.upd, slot_ids=slot_main)
-            # the second stream updates the boundary requests' summaries (slots of the others
-            # masked) before scoring them
-            slot_b = torch.full_like(wl.slot_ids, -1)
-            slot_b[self.req_l] = wl.slot_ids[self.req_l]
-            self.upd_b = dict(slot_ids_full=slot_b)
-            self.ev_dec_b = torch.cuda.Event()
+            self.slot_b = torch.full_like(wl.slot_ids, -1)
+            self.slot_b[self.req_l] = wl.slot_ids[self.req_l]
             cus = torch.cuda.get_device_properties(dev).multi_processor_count
             self.max_wg = max(1, cus - reserve_cus) if reserve_cus > 0 else 0
             self.ev_a = torch.cuda.Event()
@@ -199,18 +189,19 @@ class Path:
                                   kept_idx=self.kept, workspace=self.cws)
         rec(5)
 
-    # events of an overlapped step: main stream 0 start, 1 restored, 2 boundary requests decoded,
-    # 3 other requests decoded, 8 compaction moved (end); second stream 4 start, 5 summaries of
-    # the boundary requests, 6 scored, 7 compress-or-grow planned
+    # events of an overlapped step: main stream 0 start, 1 restored, 3 decoded, 8 compaction
+    # moved (end); second stream 4 start, 5 summaries of the boundary requests, 6 scored,
+    # 7 compress-or-grow planned
     NEV_OVERLAP = 9
 
     def step_overlap(self, ev=None):
-        """GrowPage's overlap of the boundary pass with decoding. The boundary requests are
-        decoded first on the main stream (a small call, from copies of their block-table rows
-        and lengths); the second stream meanwhile updates their summaries, scores them and plans
-        their compress-or-grow (decisions, pages, kept tokens: bookkeeping only), while the main
-        stream decodes the other requests. The planned K/V movement then runs on the main stream
-        once the other requests are decoded, with the whole GPU to itself."""
+        """GrowPage's overlap of the boundary pass with decoding. The main stream decodes every
+        request from a copy of the block tables and lengths, with the summary update of the
+        requests that are not at a boundary fused in and a grid that leaves compute units free;
+        the second stream meanwhile updates the boundary requests' summaries, scores them and
+        plans their compress-or-grow (decisions, pages, kept tokens: bookkeeping on the live
+        tables only). The planned K/V movement runs on the main stream after the decode has read
+        every page, with the whole GPU."""
         wl, gp, torch = self.wl, self.gp, self.torch
         main = torch.cuda.current_stream()
         sb = self.stream_b
@@ -218,27 +209,17 @@ class Path:
         rec(0, main)
         self.meta.copy_(self.meta0)
         rec(1, main)
-        torch.index_select(wl.q, 0, self.req_l, out=self.q_b)
-        torch.index_select(wl.block_tables, 0, self.req_l, out=self.bt_b)
-        torch.index_select(wl.context_lens, 0, self.req_l, out=self.ctx_b)
         self.ev_a.record(main)
-        gp.gp_paged_decode_attn_ex(self.q_b, self.cache, self.bt_b, self.ctx_b, wl.max_context,
-                                   wl.sm_scale, out=self.out_b, lse=self.lse_b,
-                                   workspace=self.dws_b)
-        rec(2, main)
-        # the other requests (boundary requests masked to length 0: none of their pages or
-        # block-table rows is read); enqueued before the second stream's work so that its launch
-        # does not wait on the host
-        gp.gp_paged_decode_attn_ex(wl.q, self.cache, wl.block_tables, self.ctx_main,
-                                   wl.max_context, wl.sm_scale, summaries=self.upd_main,
+        gp.gp_paged_decode_attn_ex(wl.q, self.cache, self.bt_dec, self.ctx_dec, wl.max_context,
+                                   wl.sm_scale, summaries=self.upd_main,
                                    max_workgroups=self.max_wg, out=self.out, lse=self.lse,
                                    workspace=self.dws)
         rec(3, main)
         with torch.cuda.stream(sb):
             sb.wait_event(self.ev_a)
             rec(4, sb)
-            gp.gp_update_query_summaries(wl.q, self.upd_b["slot_ids_full"], self.fresh0,
-                                         wl.qstate, wl.beta_s, wl.beta_l)
+            gp.gp_update_query_summaries(wl.q, self.slot_b, self.fresh0, wl.qstate, wl.beta_s,
+                                         wl.beta_l)
             rec(5, sb)
             gp.gp_score_and_working_set(wl.q, wl.qstate, wl.slot_ids, wl.req_idx, self.cache,
                                         wl.block_tables, wl.context_lens, wl.positions,
@@ -263,8 +244,9 @@ class Path:
 
 
 def algorithmic_bytes(wl, path, np):
-    """Bytes each row must move at least once (HBM), per step. decode_main counts the decode
-    call that excludes the boundary requests when the step overlaps them on a second stream."""
+    """Bytes each row must move at least once (HBM), per step. decode_main is the decode call
+    (all requests); summaries_main the summary updates fused into it (in the overlapped step, the
+    requests that are not at a boundary)."""
     es = 4 if wl.dtype == "f32" else 2
     B, H_q, d, H_kv, b = wl.B, wl.H_q, wl.d, wl.H_kv, wl.page_size
     ctx = wl.context_lens.cpu().numpy().astype(np.int64)
@@ -283,11 +265,11 @@ def algorithmic_bytes(wl, path, np):
         kv_r[:] = ctx * H_kv * d * es * 2
     pages_r = np.array([math.ceil(c / b) for c in ctx], dtype=np.int64)
     per_req = kv_r + 2 * H_q * d * es + H_q * 4 + pages_r * 4 + 4
-    main = [r for r in range(B) if r not in req] if path.overlap else list(range(B))
     summ_r = H_q * d * (es + 4 * 4) + 5   # q_pre read, both fp32 summaries read and written
+    n_summ = B - len(req) if path.overlap else B   # the decode call's fused updates
     out = dict(decode=int(per_req.sum()), decode_kv=int(kv_r.sum()),
-               decode_main=int(per_req[main].sum()), decode_main_kv=int(kv_r[main].sum()),
-               summaries=B * summ_r, summaries_main=len(main) * summ_r, score=0, compact=0)
+               decode_main=int(per_req.sum()), decode_main_kv=int(kv_r.sum()),
+               summaries=B * summ_r, summaries_main=n_summ * summ_r, score=0, compact=0)
     for r in req:
         c = max(0, (math.ceil(int(ctx[r]) / b) - 1) * b)
         out["score"] += c * H_kv * d * es + 4 * H_kv * c * 4
@@ -498,14 +480,13 @@ def main():
         return sum(events[k][a].elapsed_time(events[k][z]) for k in range(args.steps)) / args.steps
 
     # the summary update runs inside the decode call (events 1 and 2 are adjacent)
-    rows_ms = dict(restore=avg_ms(0, 1), paged_decode_attn_with_summaries=avg_ms(2, 3))
     if path.overlap:
-        rows_ms = dict(restore=avg_ms(0, 1), boundary_requests_decode=avg_ms(1, 2),
-                       paged_decode_attn_with_summaries=avg_ms(2, 3),
+        rows_ms = dict(restore=avg_ms(0, 1), paged_decode_attn_with_summaries=avg_ms(1, 3),
                        boundary_summaries=avg_ms(4, 5), score_and_working_set=avg_ms(5, 6),
                        compact_or_grow_plan=avg_ms(6, 7), compact_or_grow_move_incl_wait=avg_ms(3, 8))
         event_step_ms = avg_ms(0, 8)
     else:
+        rows_ms = dict(restore=avg_ms(0, 1), paged_decode_attn_with_summaries=avg_ms(2, 3))
         if path.R:
             rows_ms["score_and_working_set"] = avg_ms(3, 4)
             rows_ms["compact_or_grow"] = avg_ms(4, 5)
@@ -535,6 +516,7 @@ def main():
     value = step_bytes / (ms_step * 1e-3) / 1e9
     if single is not None:
         single["value"] = round(step_bytes / (single["ms_per_step"] * 1e-3) / 1e9, 2)
+
     dec_ms = rows_ms["paged_decode_attn_with_summaries"]
     achieved = (by["decode_main"] + by["summaries_main"]) / (dec_ms * 1e-3) / 1e9
 
@@ -559,14 +541,17 @@ def main():
             pmc = json.load(fh)
         if (pmc.get("decode_src_sha") == file_sha(DECODE_SRC) and pmc.get("config") == args.config
                 and pmc.get("overlap", 0) == int(path.overlap)
-                and pmc.get("reserve_cus", 0) == (args.reserve_cus if path.overlap else 0)):
+                and pmc.get("reserve_cus", 0) == (args.reserve_cus if path.overlap else 0)
+                and pmc.get("decode_call") == "every request, fused summary update"):
             traffic = pmc.get("bytes_per_launch")
 
     int4 = None
     if args.int4 and not wl.mixed and wl.dtype == "bf16":
         print("[bench] INT4 leg: demote every used page, time decode", file=sys.stderr, flush=True)
         int4 = int4_leg(wl, gp, torch, np, args.steps)
-        int4["speedup_vs_bf16_decode"] = round(dec_ms / int4["decode_ms"], 3)
+        # against the same batch in bf16 decoded with the full grid
+        ref_ms = single["decode_ms"] if single is not None else dec_ms
+        int4["speedup_vs_bf16_decode"] = round(ref_ms / int4["decode_ms"], 3)
 
     boundary = None
     if path.R:
@@ -603,10 +588,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "paged_decode_attn_ex (stream-K decode with the fused summary "
-                               "update + merge launches)" + (
-                         " of the requests not at a page boundary, beside the boundary pass on a "
-                         "second stream" if path.overlap else ""),
+                     "kernel": "paged_decode_attn_ex (stream-K decode of every request with the "
+                               "fused summary update + merge launches)" + (
+                         ", grid capped, beside the boundary pass on a second stream"
+                         if path.overlap else ""),
                      "bytes_per_launch": by["decode_main"] + by["summaries_main"],
                      "avg_launch_ms": round(dec_ms, 4)},
         "cpu_baseline": cpu,
