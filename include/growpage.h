@@ -260,9 +260,11 @@ int gp_score_and_working_set(const void* q, int q_dtype, int B, int H_q, const f
  *   a_short / a_long / ws_counts / n_cand as produced by gp_score_and_working_set.
  *   kv, block_tables, n_pages, context_lens, refcount, free_stack, free_top are updated in place.
  *   Uniform caches only (page_tag must be NULL). Requests of one call must be distinct.
- *   Limits: R <= 1024, page_size 16 or 32 (32-token fp32 pages need head_dim 64),
- *   C_max <= 32768 and a multiple of 4. GP_POLICY_SHRINK needs page_size 16 (a shrink evicts up
- *   to 2 * page_size tokens); with 32-token pages a per-request Shrink is answered NO_PAGES.
+ *   Limits: R <= 1024, page_size 16, 32, 64, 128 or 256 (32-token fp32 pages need head_dim
+ *   64), C_max <= 32768 and a multiple of 4. A Shrink evicts up to 2 * page_size tokens: with
+ *   32-token pages GP_POLICY_SHRINK is rejected and a per-request Shrink is answered NO_PAGES.
+ *   With pages of 64 tokens or more (GrowPage's own runs use 256-token blocks and k_loc = 64)
+ *   the candidate set still excludes the whole last page, so all of its tokens are kept.
  */
 size_t gp_compact_or_grow_workspace_size(int R, int H_kv, int max_pages, int page_size, int C_max);
 

@@ -8,16 +8,20 @@
 //      pops one private page per shared page it must write (ascending logical order); released
 //      references are applied after every pop of the call. Per-request work and the page checks
 //      run in parallel; only the pop order is a serial scan.
-//   2. select (three launches): s = max(a^S, a^L); the E <= page_size evicted tokens are the E
-//      smallest of the unique keys (s, ~index) outside each page's k_loc quota, which realises
-//      the (s desc, index asc) order exactly: chunk-local E smallest, their merge per request
-//      and KV head, then kept_idx written in parallel.
+//   2. select: s = max(a^S, a^L); the E evicted tokens (E <= page_size, 2 page_size for a
+//      Shrink) are the E smallest of the unique keys (s, ~index) outside each page's k_loc
+//      quota, which realises the (s desc, index asc) order exactly. Pages of 16 or 32 tokens:
+//      three launches (chunk-local E smallest, their merge per request and KV head, kept_idx
+//      written in parallel). Pages of 64..256 tokens: one workgroup per request and KV head,
+//      radix selects for the page quotas and for the E-th smallest key.
 //   3. chunk list + snapshot: the (request, head, chunk) items to rewrite are listed on the device;
 //      compaction is a left shift by at most E slots, so a chunk of destination pages only reads
-//      its own pages plus the first page of the next chunk, which is saved first.
-//   4. compact (resident workgroups striding over the list), window by window: tabulate the source slot of
-//      every destination slot, read all sources (key rows into registers, value pages into
-//      LDS), barrier, write the window's destination pages.
+//      its own pages plus the first pages of the next chunk, which are saved first.
+//   4. compact (resident workgroups striding over the list). Pages of 16 or 32 tokens, window by
+//      window: tabulate the source slot of every destination slot, read all sources (key rows
+//      into registers, value pages into LDS), barrier, write the window's destination pages.
+//      Pages of 64..256 tokens: items also split the head dimension into 64-byte parts, and
+//      each destination page is rewritten from an LDS ring of its source pages' value rows.
 #include "common.h"
 
 #include <atomic>
@@ -40,6 +44,13 @@ constexpr int CP_THREADS = 256;
 constexpr int CP_LDS_BYTES = 40 * 1024;  // source value pages of one window
 constexpr int K_PIECES = 8;               // key pieces per thread and window
 constexpr int V_PIECES = 12;              // staged value pieces per thread and window
+constexpr int WIDE_MIN_PAGE = 64;         // page sizes from here on take the wide path
+constexpr int WIDE_MAX_EVICT = 512;       // 2 pages of 256 tokens (Shrink)
+constexpr int WIDE_T = 1024;              // threads of a wide selection workgroup
+constexpr int WIDE_VPT = 32;              // candidates per thread (|C| <= 32768)
+constexpr int WIDE_PART = 64;             // bytes of each key row one wide compaction item owns
+constexpr int WIDE_MAX_PARTS = 128 * 4 / WIDE_PART;
+constexpr int KEY_BITS = 46;              // 31 score bits above a 15-bit complemented index
 
 struct Info {
   int r, mode, P, ctx_old, n, K_t, R_n, E, ctx_new, n_dest, first_repl, pad;
@@ -65,17 +76,20 @@ struct CParams {
   Info* info;         // [R]
   int32_t* old_bt;    // [R, max_pages]
   int32_t* rel;       // [R * max_pages]
-  int32_t* ev;        // [R, H_kv, MAX_EVICT]
+  int32_t* ev;        // [R, H_kv, max_evict]
   int32_t* dp0;       // [R, H_kv]
   unsigned long long* cand;  // [R, H_kv, SEL_MAX_CHUNKS, MAX_EVICT] chunk survivors
-  int2* items;               // [R * H_kv * max_chunks] (request * H_kv + head, chunk) to compact
+  int2* items;               // [R * H_kv * max_chunks * npart] (request * H_kv + head, chunk * npart + part)
   int32_t* n_items;          // [1]
   uint8_t* snap;      // [R, H_kv, max_chunks, MAX_SPAN, 2, page bytes]
   int R, B, H_kv, D, page_size, num_pages, max_pages, C_max, k_loc, policy, es;
   int L;              // layers whose working sets enter the decision (ws_counts [L, R, H_kv, 2])
   int span;           // pages a compaction of this call may shift by (1, or 2 when Shrink can occur)
   int chunk_pages, max_chunks, window_pages;
+  int max_evict;      // evicted tokens per head the selection can hold (MAX_EVICT or 2 page_size)
+  int npart;          // parts of the head dimension compacted apart (1 below WIDE_MIN_PAGE)
   int log_b, log_kq, log_vq, log_qpp;  // log2 of page size, 16-byte pieces per key row / value row / page
+  int log_kpq;        // log2 of the 16-byte pieces of a key row one part owns
   double tau;
 };
 
@@ -198,8 +212,8 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
       inf.ctx_new = K_t + R_n;
       ndest = (inf.ctx_new + b - 1) / b;
       inf.n_dest = ndest;
-      if (E > 0 && E <= MAX_EVICT) flags |= F_CHECK;  // may compact: check its pages
-      flags |= min(E, 255) << 8;
+      if (E > 0 && E <= P.max_evict) flags |= F_CHECK;  // may compact: check its pages
+      flags |= min(E, 65535) << 8;
     }
     if (i < DA_MAX_R) {
       s_flags[i] = flags;
@@ -271,7 +285,7 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
             out = O_IDENTITY;  // nothing moves; a Shrink still hands back its last page
             dec = code;
             nrel += shr ? 1 : 0;
-          } else if (E > MAX_EVICT) {
+          } else if (E > P.max_evict) {
             // unreachable for Compress & Hold (E <= page_size); a Shrink of 32-token pages
             dec = GP_DECISION_NO_PAGES;
             shr = false;
@@ -546,7 +560,7 @@ __global__ __launch_bounds__(GP_WAVE) void select_merge_kernel(CParams P) {
   __shared__ int s_sorted[MAX_EVICT];
   if (lane < E) s_sorted[rank] = tok;
   __syncthreads();
-  if (lane < E) P.ev[((size_t)i * P.H_kv + h) * MAX_EVICT + lane] = s_sorted[lane];
+  if (lane < E) P.ev[((size_t)i * P.H_kv + h) * P.max_evict + lane] = s_sorted[lane];
   if (lane == 0) P.dp0[(size_t)i * P.H_kv + h] = min(s_sorted[0] / b, inf.first_repl);
 }
 
@@ -567,7 +581,7 @@ __global__ __launch_bounds__(SEL_T) void select_write_kernel(CParams P) {
   const int E = inf.E;
   __shared__ int s_ev[MAX_EVICT];
   if (threadIdx.x < MAX_EVICT)
-    s_ev[threadIdx.x] = threadIdx.x < E ? P.ev[((size_t)i * P.H_kv + h) * MAX_EVICT + threadIdx.x] : INT_MAX;
+    s_ev[threadIdx.x] = threadIdx.x < E ? P.ev[((size_t)i * P.H_kv + h) * P.max_evict + threadIdx.x] : INT_MAX;
   __syncthreads();
   if (c == 0 && threadIdx.x < E) out[inf.K_t + threadIdx.x] = -1;
   if (t0 >= n) return;
@@ -582,6 +596,108 @@ __global__ __launch_bounds__(SEL_T) void select_write_kernel(CParams P) {
       out[t - before] = t;
     }
   }
+}
+
+// Selection for pages of 64..256 tokens (up to 2 page_size evictions): one workgroup per
+// (request, KV head), WIDE_VPT consecutive candidates per thread. A key holds the score bits
+// above the complemented token index, so a larger key is a better token under (s desc,
+// index asc) and all keys differ. The k_loc quota of a page is every key at or above the
+// page's k_loc-th largest, found by a bitwise radix select over the LPP lanes that hold the
+// page; the evicted tokens are the keys outside the quotas up to the E-th smallest of them,
+// found by a bitwise radix select over the workgroup. Writes the ascending evicted list, the
+// first changed destination page and kept_idx.
+template <int LPP>  // lanes per page: page_size / WIDE_VPT
+__global__ __launch_bounds__(WIDE_T) void select_wide_kernel(CParams P) {
+  const int h = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
+  const Info inf = P.info[i];
+  const int n = inf.n;
+  int32_t* out = P.kept_idx + ((size_t)i * P.H_kv + h) * P.C_max;
+  if (inf.mode != MODE_COMPACT) {
+    for (int t = tid; t < n; t += WIDE_T) out[t] = inf.mode == MODE_IDENTITY ? t : -1;
+    return;
+  }
+  const int K_t = inf.K_t, E = inf.E, b = P.page_size;
+  const int t0 = tid * WIDE_VPT;
+  const bool live = t0 < n;  // |C| is a multiple of the page size, so of WIDE_VPT
+  const float* as = P.a_short + ((size_t)i * P.H_kv + h) * P.C_max;
+  const float* al = P.a_long + ((size_t)i * P.H_kv + h) * P.C_max;
+  unsigned long long key[WIDE_VPT];
+#pragma unroll
+  for (int j = 0; j < WIDE_VPT; j += 4) {
+    f32x4_t x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+    if (live) {
+      x = *reinterpret_cast<const f32x4_t*>(as + t0 + j);
+      y = *reinterpret_cast<const f32x4_t*>(al + t0 + j);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t sv = max(__float_as_uint(x[e]) & 0x7fffffffu, __float_as_uint(y[e]) & 0x7fffffffu);
+      key[j + e] = ((unsigned long long)sv << 15) | (uint32_t)(0x7fff - ((t0 + j + e) & 0x7fff));
+    }
+  }
+  const int kloc = min(P.k_loc, b);
+  const long n_loc = (long)(n / b) * kloc;
+  if (n_loc < K_t && kloc > 0) {
+    // the page's kloc-th largest key: the largest x with #{keys >= x} >= kloc
+    unsigned long long x = 0;
+    for (int bit = KEY_BITS - 1; bit >= 0; --bit) {
+      const unsigned long long c = x | (1ull << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < WIDE_VPT; ++j) cnt += key[j] >= c ? 1 : 0;
+#pragma unroll
+      for (int o = 1; o < LPP; o <<= 1) cnt += __shfl_xor(cnt, o, GP_WAVE);
+      if (cnt >= kloc) x = c;
+    }
+#pragma unroll
+    for (int j = 0; j < WIDE_VPT; ++j)
+      if (key[j] >= x) key[j] = ~0ull;  // in the quota: never evicted
+  }
+  // otherwise |S_loc| >= K_t and S is the K_t best of all of C: every candidate may go
+  if (!live) {
+#pragma unroll
+    for (int j = 0; j < WIDE_VPT; ++j) key[j] = ~0ull;
+  }
+  // the E-th smallest remaining key: the largest x with #{keys < x} < E
+  constexpr int NW = WIDE_T / GP_WAVE;
+  __shared__ int s_part[2][NW];
+  __shared__ int s_w[NW];
+  const int lane = tid & 63, wv = tid >> 6;
+  unsigned long long x = 0;
+  for (int bit = KEY_BITS - 1, it = 0; bit >= 0; --bit, ++it) {
+    const unsigned long long c = x | (1ull << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < WIDE_VPT; ++j) cnt += key[j] < c ? 1 : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, GP_WAVE);
+    if (lane == 0) s_part[it & 1][wv] = cnt;
+    __syncthreads();  // one barrier per step: the two buffers alternate
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += s_part[it & 1][w];
+    if (tot < E) x = c;
+  }
+  uint32_t evm = 0;  // bit j: candidate t0 + j is evicted
+#pragma unroll
+  for (int j = 0; j < WIDE_VPT; ++j) evm |= (key[j] <= x ? 1u : 0u) << j;
+  int total;
+  const int ex = block_excl_scan(__popc(evm), s_w, &total);  // total == E
+  int32_t* ev = P.ev + ((size_t)i * P.H_kv + h) * P.max_evict;
+  if (evm) {
+    int k = ex;
+    for (int j = 0; j < WIDE_VPT; ++j)
+      if ((evm >> j) & 1u) ev[k++] = t0 + j;
+    if (ex == 0) P.dp0[(size_t)i * P.H_kv + h] = min((t0 + __ffs(evm) - 1) / b, inf.first_repl);
+  }
+  if (live) {
+    int before = ex;  // evicted tokens below t0 + j
+    for (int j = 0; j < WIDE_VPT; ++j) {
+      if ((evm >> j) & 1u) ++before;
+      else out[t0 + j - before] = t0 + j;
+    }
+  }
+  if (tid < E) out[K_t + tid] = -1;
 }
 
 // page bytes of one KV head: keys [b][D], values [D][b]
@@ -604,8 +720,9 @@ __device__ __forceinline__ bool from_snapshot(const CParams& P, int lp, int c, i
   return lp >= first && lp < first + P.span && lp < n_dest;
 }
 
-// List of the (request, head, chunk) items that compaction rewrites: for a compacting head the
-// chunks from the one holding its first changed page to the one holding its last destination page.
+// List of the (request, head, chunk, part) items that compaction rewrites: for a compacting head
+// the chunks from the one holding its first changed page to the one holding its last destination
+// page, each with every part of the head dimension (one part below WIDE_MIN_PAGE).
 __global__ __launch_bounds__(DA_THREADS) void chunk_list_kernel(CParams P) {
   __shared__ int s_w[DA_THREADS / GP_WAVE];
   const int L = P.chunk_pages, n = P.R * P.H_kv;
@@ -618,40 +735,46 @@ __global__ __launch_bounds__(DA_THREADS) void chunk_list_kernel(CParams P) {
       if (inf.mode == MODE_COMPACT) {
         const int dp0 = P.dp0[ih];
         if (dp0 < inf.n_dest) {
-          c0 = dp0 / L;
-          cnt = (inf.n_dest + L - 1) / L - c0;
+          c0 = dp0 / L * P.npart;
+          cnt = ((inf.n_dest + L - 1) / L - dp0 / L) * P.npart;
         }
       }
     }
     int total;
     const int off = carry + block_excl_scan(cnt, s_w, &total);
-    for (int k = 0; k < cnt; ++k) P.items[off + k] = make_int2(ih, c0 + k);
+    for (int k = 0; k < cnt; ++k) P.items[off + k] = make_int2(ih, c0 + k);  // chunk * npart + part
     carry += total;
   }
   if (threadIdx.x == 0) *P.n_items = carry;
 }
 
 // The first `span` pages of the next chunk, saved before any chunk is rewritten (they are that
-// chunk's to rewrite, and this chunk's last source pages). Workgroups stride over the work list.
+// chunk's to rewrite, and this chunk's last source pages): the bytes of the item's part, i.e.
+// its slice of every key row and its value rows. Workgroups stride over the work list.
 __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
   const int n_items = *P.n_items;
+  const int krow = P.D * P.es, kb = krow / P.npart;   // key row bytes, of them the part's
+  const size_t vb = page_bytes(P) / P.npart;           // value bytes of the part (contiguous rows)
+  const int lkpq = P.log_kpq, nkq = P.page_size << lkpq;
   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
     const int2 item = P.items[it];
     const int i = item.x / P.H_kv, h = item.x % P.H_kv;
+    const int c = item.y / P.npart, part = item.y % P.npart;
     const Info inf = P.info[i];
     for (int s = 0; s < P.span; ++s) {
-      const int lp = (item.y + 1) * P.chunk_pages + s;
-      if (!from_snapshot(P, lp, item.y, inf.n_dest)) continue;  // uniform over the workgroup
+      const int lp = (c + 1) * P.chunk_pages + s;
+      if (!from_snapshot(P, lp, c, inf.n_dest)) continue;  // uniform over the workgroup
       const int pg = P.old_bt[(size_t)i * P.max_pages + lp];
-      const size_t nb = page_bytes(P);
-      const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(P.k + pool_off(P, pg, h));
-      const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(P.v + pool_off(P, pg, h));
-      u32x4_t* kd = reinterpret_cast<u32x4_t*>(snap_ptr(P, i, h, lp, 0));
-      u32x4_t* vd = reinterpret_cast<u32x4_t*>(snap_ptr(P, i, h, lp, 1));
-      for (size_t q = threadIdx.x; q < nb / 16; q += CP_THREADS) {
-        kd[q] = ks[q];
-        vd[q] = vs[q];
+      const uint8_t* ks = P.k + pool_off(P, pg, h) + (size_t)part * kb;
+      const uint8_t* vs = P.v + pool_off(P, pg, h) + (size_t)part * vb;
+      uint8_t* kd = snap_ptr(P, i, h, lp, 0) + (size_t)part * kb;
+      uint8_t* vd = snap_ptr(P, i, h, lp, 1) + (size_t)part * vb;
+      for (int q = threadIdx.x; q < nkq; q += CP_THREADS) {
+        const size_t o = (size_t)(q >> lkpq) * krow + (size_t)(q & ((1 << lkpq) - 1)) * 16;
+        *reinterpret_cast<u32x4_t*>(kd + o) = *reinterpret_cast<const u32x4_t*>(ks + o);
       }
+      for (size_t q = threadIdx.x; q < vb / 16; q += CP_THREADS)
+        reinterpret_cast<u32x4_t*>(vd)[q] = reinterpret_cast<const u32x4_t*>(vs)[q];
     }
   }
 }
@@ -687,7 +810,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   const size_t pb = page_bytes(P);
   if (threadIdx.x < MAX_EVICT)
     s_thr[threadIdx.x] = threadIdx.x < E
-                             ? P.ev[((size_t)i * P.H_kv + h) * MAX_EVICT + threadIdx.x] - (int)threadIdx.x
+                             ? P.ev[((size_t)i * P.H_kv + h) * P.max_evict + threadIdx.x] - (int)threadIdx.x
                              : INT_MAX;
   if (threadIdx.x < dp_hi - dp_lo + P.span) {
     const int lp = dp_lo + threadIdx.x;
@@ -783,6 +906,125 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   }
 }
 
+// Compaction for pages of 64..256 tokens. An item is (request, head, chunk, part); part p owns
+// bytes [64p, 64p + 64) of every key row and the value rows [p Dp, (p + 1) Dp) (Dp = 64 bytes of
+// elements), so items of different parts never touch the same bytes. The item rewrites its
+// chunk's destination pages one at a time, left to right: destination page dp reads source
+// pages dp .. dp + span, whose value rows of the part stay in an LDS ring of span + 1 slices
+// (each source slice is fetched once), and key pieces go through registers. A destination page
+// overwrites only its own source page, which no later page of the item reads; the first `span`
+// pages of the next chunk come from the snapshot.
+constexpr int WIDE_KQ = 4;  // key pieces per thread and page: 256 slots x 4 pieces / CP_THREADS
+constexpr int WIDE_VQ = 4;  // value pieces per thread and page slice
+__global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
+  const int n_items = *P.n_items;
+  const int L = P.chunk_pages, span = P.span, ring = span + 1, es = P.es;
+  const int lb = P.log_b, b = 1 << lb;
+  const int krow = P.D * es;
+  const int vslice = WIDE_PART * b;         // bytes of one page's value rows of a part
+  const int per = 16 / es;                  // elements per 16-byte piece
+  __shared__ int s_thr[WIDE_MAX_EVICT];
+  __shared__ int s_src[256];                // source slot of each destination slot of the page
+  __shared__ long long s_soff[CHUNK_PAGES + MAX_SPAN], s_doff[CHUNK_PAGES];
+  extern __shared__ __align__(16) uint8_t s_ring[];  // ring x vslice bytes
+  for (int item_k = blockIdx.x; item_k < n_items; item_k += gridDim.x) {
+    __syncthreads();  // the previous item is done with the tables and the ring
+    const int2 item = P.items[item_k];
+    const int i = item.x / P.H_kv, h = item.x % P.H_kv;
+    const int c = item.y / P.npart, part = item.y % P.npart;
+    const Info inf = P.info[i];
+    const int E = inf.E;
+    const int dp0 = P.dp0[item.x];
+    const int dp_lo = max(dp0, c * L), dp_hi = min((c + 1) * L, inf.n_dest);
+    for (int k = threadIdx.x; k < WIDE_MAX_EVICT; k += CP_THREADS)
+      s_thr[k] = k < E ? P.ev[((size_t)i * P.H_kv + h) * P.max_evict + k] - k : INT_MAX;
+    if (threadIdx.x < dp_hi - dp_lo + span) {
+      const int lp = dp_lo + threadIdx.x;
+      long long so = -2;
+      if (lp < inf.P)
+        so = from_snapshot(P, lp, c, inf.n_dest) ? -1
+                                                   : (long long)pool_off(P, P.old_bt[(size_t)i * P.max_pages + lp], h);
+      s_soff[threadIdx.x] = so;
+      if (lp < dp_hi) s_doff[threadIdx.x] = (long long)pool_off(P, P.block_tables[(size_t)inf.r * P.max_pages + lp], h);
+    }
+    __syncthreads();
+    const size_t koff = (size_t)part * WIDE_PART;  // the part's bytes inside a key row
+    const size_t voff = (size_t)part * vslice;     // the part's value rows inside a page
+    auto src_page = [&](int lp, int which) -> const uint8_t* {
+      const long long so = s_soff[lp - dp_lo];
+      if (so == -1) return snap_ptr(P, i, h, lp, which);
+      return (which ? P.v : P.k) + so;
+    };
+    // value rows of source page lp into its ring slot (zeros past the old pages: never read)
+    auto load_slice = [&](int lp) {
+      u32x4_t r[WIDE_VQ];
+      const bool have = s_soff[lp - dp_lo] != -2;
+      const u32x4_t* src = have ? reinterpret_cast<const u32x4_t*>(src_page(lp, 1) + voff) : nullptr;
+#pragma unroll
+      for (int it = 0; it < WIDE_VQ; ++it) {
+        const int q = threadIdx.x + it * CP_THREADS;
+        r[it] = u32x4_t{0u, 0u, 0u, 0u};
+        if (have && q < vslice / 16) r[it] = src[q];
+      }
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(s_ring + (size_t)(lp % ring) * vslice);
+#pragma unroll
+      for (int it = 0; it < WIDE_VQ; ++it) {
+        const int q = threadIdx.x + it * CP_THREADS;
+        if (q < vslice / 16) dst[q] = r[it];
+      }
+    };
+    for (int lp = dp_lo; lp < dp_lo + span; ++lp) load_slice(lp);
+    for (int dp = dp_lo; dp < dp_hi; ++dp) {
+      if (dp > dp_lo) __syncthreads();  // the previous page is done with s_src and its ring slot
+      load_slice(dp + span);
+      for (int q = threadIdx.x; q < b; q += CP_THREADS) {
+        const int j = (dp << lb) + q;
+        int lo = 0, hi = E;  // #{k : thr[k] <= j}; thr is nondecreasing
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s_thr[mid] <= j) lo = mid + 1;
+          else hi = mid;
+        }
+        s_src[q] = j + lo;
+      }
+      __syncthreads();  // ring slices and the source table are complete
+      const int nk = b * (WIDE_PART / 16);
+      u32x4_t kreg[WIDE_KQ];
+#pragma unroll
+      for (int it = 0; it < WIDE_KQ; ++it) {
+        const int q = threadIdx.x + it * CP_THREADS;
+        if (q < nk) {
+          const int src = s_src[q >> 2];
+          kreg[it] = *reinterpret_cast<const u32x4_t*>(src_page(src >> lb, 0) + (size_t)(src & (b - 1)) * krow +
+                                                       koff + (q & 3) * 16);
+        }
+      }
+      __syncthreads();  // every read of the page's own source bytes precedes its writes
+      uint8_t* kd = P.k + s_doff[dp - dp_lo] + koff;
+#pragma unroll
+      for (int it = 0; it < WIDE_KQ; ++it) {
+        const int q = threadIdx.x + it * CP_THREADS;
+        if (q < nk) *reinterpret_cast<u32x4_t*>(kd + (size_t)(q >> 2) * krow + (q & 3) * 16) = kreg[it];
+      }
+      // value rows: 16-byte pieces of destination rows gathered from the ring
+      uint8_t* vd = P.v + s_doff[dp - dp_lo] + voff;
+      const int row_pieces = b * es / 16, nvp = vslice / 16;
+      for (int q = threadIdx.x; q < nvp; q += CP_THREADS) {
+        const int dl = q / row_pieces, piece = q - dl * row_pieces;
+        uint32_t wv[4] = {0u, 0u, 0u, 0u};
+        for (int e = 0; e < per; ++e) {
+          const int rs = s_src[piece * per + e];
+          const uint8_t* sp = s_ring + (size_t)((rs >> lb) % ring) * vslice +
+                              ((size_t)dl * b + (rs & (b - 1))) * es;
+          if (es == 2) wv[e >> 1] |= (uint32_t)(*reinterpret_cast<const uint16_t*>(sp)) << (16 * (e & 1));
+          else wv[e] = *reinterpret_cast<const uint32_t*>(sp);
+        }
+        *reinterpret_cast<u32x4_t*>(vd + (size_t)q * 16) = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
+      }
+    }
+  }
+}
+
 // Window of W destination pages: LDS holds the W + span source value pages, and the W * b key
 // rows must fit K_PIECES 16-byte pieces per thread.
 int window_pages_for(int page_size, int D, int es, int span) {
@@ -829,6 +1071,9 @@ struct WsLayout {
 WsLayout ws_layout(int L, int R, int H_kv, int max_pages, int page_size) {
   // snapshots sized for the widest supported element (fp32) and head_dim 128
   const int es = 4, D = 128;
+  const bool wide = page_size >= WIDE_MIN_PAGE;
+  const size_t max_evict = wide ? 2 * (size_t)page_size : MAX_EVICT;
+  const size_t parts = wide ? WIDE_MAX_PARTS : 1;
   const size_t max_chunks = (size_t)(max_pages + CHUNK_PAGES - 1) / CHUNK_PAGES;
   WsLayout w{};
   size_t off = 0;
@@ -841,12 +1086,12 @@ WsLayout ws_layout(int L, int R, int H_kv, int max_pages, int page_size) {
   off = (off + 255) & ~(size_t)255;
   w.layer0 = off;
   w.ev = 0;
-  size_t lo = (size_t)R * H_kv * MAX_EVICT * 4;
+  size_t lo = (size_t)R * H_kv * max_evict * 4;
   w.dp0 = lo;
   lo += (size_t)R * H_kv * 4;
   lo = (lo + 15) & ~(size_t)15;
   w.items = lo;
-  lo += (size_t)R * H_kv * max_chunks * sizeof(int2);
+  lo += (size_t)R * H_kv * max_chunks * parts * sizeof(int2);
   w.n_items = lo;
   lo += 256;
   w.layer_bytes = (lo + 255) & ~(size_t)255;
@@ -890,14 +1135,21 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
   if (H_kv <= 0 || kv->num_pages <= 0) return GP_ERR_INVALID;
   if (kv->dtype != GP_F32 && kv->dtype != GP_BF16) return GP_ERR_INVALID;
   if (D != 64 && D != 128) return GP_ERR_UNSUPPORTED;
-  if (b != 16 && b != 32) return GP_ERR_UNSUPPORTED;
-  if (policy == GP_POLICY_SHRINK && b != 16) return GP_ERR_UNSUPPORTED;  // E <= 2b <= MAX_EVICT
+  if (b != 16 && b != 32 && b != 64 && b != 128 && b != 256) return GP_ERR_UNSUPPORTED;
+  // a Shrink evicts up to 2b tokens: beyond the 32 evictions of the 32-token path
+  if (policy == GP_POLICY_SHRINK && b == 32) return GP_ERR_UNSUPPORTED;
+  const bool wide = b >= WIDE_MIN_PAGE;
   // a Shrink moves tokens by up to two pages; only calls where one can occur pay for that
   const int span = (policy == GP_POLICY_SHRINK || policies) ? MAX_SPAN : 1;
   const int es = kv->dtype == GP_F32 ? 4 : 2;
-  const int W = window_pages_for(b, D, es, span);
-  {
-    const size_t lds = (size_t)(W + span) * b * D * es;
+  const int W = wide ? 1 : window_pages_for(b, D, es, span);
+  size_t lds;
+  if (wide) {
+    lds = (size_t)(span + 1) * WIDE_PART * b;
+    if (lds + sizeof(int) * (WIDE_MAX_EVICT + 256) + 16 * (2 * CHUNK_PAGES + MAX_SPAN) > 64 * 1024)
+      return GP_ERR_UNSUPPORTED;
+  } else {
+    lds = (size_t)(W + span) * b * D * es;
     if (lds + sizeof(int) * (MAX_EVICT + MAX_WINDOW_SLOTS) > 64 * 1024) return GP_ERR_UNSUPPORTED;
     if ((long)W * b * D * es > (long)K_PIECES * CP_THREADS * 16) return GP_ERR_UNSUPPORTED;
     if ((long)(W + span) * b * D * es > (long)V_PIECES * CP_THREADS * 16) return GP_ERR_UNSUPPORTED;
@@ -935,6 +1187,9 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
   P.chunk_pages = CHUNK_PAGES;
   P.max_chunks = (max_pages + CHUNK_PAGES - 1) / CHUNK_PAGES;
   P.window_pages = W;
+  P.max_evict = wide ? 2 * b : MAX_EVICT;
+  P.npart = wide ? D * es / WIDE_PART : 1;
+  P.log_kpq = ilog2(D * es / P.npart / 16);
   P.log_b = ilog2(b);
   P.log_kq = ilog2(D * es / 16);
   P.log_vq = ilog2(b * es / 16);
@@ -971,28 +1226,40 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
     const dim3 g(nch, H_kv, R);
     for (int l = 0; l < L; ++l) {  // selection per layer and KV head (Eq. 9-10)
       const CParams Q = layer(l);
-      if (b == 16) hipLaunchKernelGGL(select_local_kernel<16>, g, dim3(SEL_T), 0, s, Q);
-      else hipLaunchKernelGGL(select_local_kernel<32>, g, dim3(SEL_T), 0, s, Q);
-      GP_CHECK_LAUNCH();
-      hipLaunchKernelGGL(select_merge_kernel, dim3(H_kv, R), dim3(GP_WAVE), 0, s, Q);
-      GP_CHECK_LAUNCH();
-      if (b == 16) hipLaunchKernelGGL(select_write_kernel<16>, g, dim3(SEL_T), 0, s, Q);
-      else hipLaunchKernelGGL(select_write_kernel<32>, g, dim3(SEL_T), 0, s, Q);
-      GP_CHECK_LAUNCH();
+      if (wide) {
+        const dim3 gw(H_kv, R);
+        if (b == 64) hipLaunchKernelGGL(select_wide_kernel<2>, gw, dim3(WIDE_T), 0, s, Q);
+        else if (b == 128) hipLaunchKernelGGL(select_wide_kernel<4>, gw, dim3(WIDE_T), 0, s, Q);
+        else hipLaunchKernelGGL(select_wide_kernel<8>, gw, dim3(WIDE_T), 0, s, Q);
+        GP_CHECK_LAUNCH();
+      } else {
+        if (b == 16) hipLaunchKernelGGL(select_local_kernel<16>, g, dim3(SEL_T), 0, s, Q);
+        else hipLaunchKernelGGL(select_local_kernel<32>, g, dim3(SEL_T), 0, s, Q);
+        GP_CHECK_LAUNCH();
+        hipLaunchKernelGGL(select_merge_kernel, dim3(H_kv, R), dim3(GP_WAVE), 0, s, Q);
+        GP_CHECK_LAUNCH();
+        if (b == 16) hipLaunchKernelGGL(select_write_kernel<16>, g, dim3(SEL_T), 0, s, Q);
+        else hipLaunchKernelGGL(select_write_kernel<32>, g, dim3(SEL_T), 0, s, Q);
+        GP_CHECK_LAUNCH();
+      }
       hipLaunchKernelGGL(chunk_list_kernel, dim3(1), dim3(DA_THREADS), 0, s, Q);
       GP_CHECK_LAUNCH();
     }
   }
   if (!(phases & GP_PHASE_MOVE)) return GP_OK;
   const int cus = device_cus();
-  const size_t lds = (size_t)(W + span) * b * D * es;
+  const int max_items = R * H_kv * P.max_chunks * P.npart;
   for (int l = 0; l < L; ++l) {
     const CParams Q = layer(l);
-    hipLaunchKernelGGL(snapshot_kernel, dim3(std::max(1, std::min(4 * cus, R * H_kv * P.max_chunks))),
+    hipLaunchKernelGGL(snapshot_kernel, dim3(std::max(1, std::min(4 * cus, max_items))),
                        dim3(CP_THREADS), 0, s, Q);
     GP_CHECK_LAUNCH();
-    hipLaunchKernelGGL(compact_kernel, dim3(std::max(1, std::min(2 * cus, R * H_kv * P.max_chunks))),
-                       dim3(CP_THREADS), lds, s, Q);
+    if (wide)
+      hipLaunchKernelGGL(compact_wide_kernel, dim3(std::max(1, std::min(4 * cus, max_items))),
+                         dim3(CP_THREADS), lds, s, Q);
+    else
+      hipLaunchKernelGGL(compact_kernel, dim3(std::max(1, std::min(2 * cus, max_items))),
+                         dim3(CP_THREADS), lds, s, Q);
     GP_CHECK_LAUNCH();
   }
   return GP_OK;

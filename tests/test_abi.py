@@ -119,8 +119,10 @@ def test_invalid_arguments_rejected_on_host(lib):
                                             fake, fake, fake, fake, ws, wsb, None)
     assert lib.gp_compact_or_grow(*cargs(0.0, 9, kv, fake, 1 << 30)) == -1
     assert lib.gp_compact_or_grow(*cargs(float("nan"), 0, kv, fake, 1 << 30)) == -1
-    kv64 = _kv(growpage, b=64)
-    assert lib.gp_compact_or_grow(*cargs(0.0, 0, kv64, fake, 1 << 30)) == -2
+    for b in (48, 512):   # page sizes 16, 32, 64, 128 and 256 only
+        assert lib.gp_compact_or_grow(*cargs(0.0, 0, _kv(growpage, b=b), fake, 1 << 30)) == -2
+    # GrowPage-Shrink evicts up to two pages: not with 32-token pages
+    assert lib.gp_compact_or_grow(*cargs(0.0, 4, _kv(growpage, b=32), fake, 1 << 30)) == -2
     assert lib.gp_compact_or_grow(*cargs(0.0, 0, kv, None, 0)) == -3
     # phased form: only PLAN (1), MOVE (2) or both (3)
     for bad in (0, 4, -1):
