@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--int4", type=int, default=1,
                     help="also time decode with every page of the batch demoted to INT4 "
                          "(PASK App. B.5) by the page quantiser (bf16 workloads)")
+    ap.add_argument("--boundary-pass", type=int, default=1,
+                    help="also time the boundary pass alone on the long-reasoning, prefix-shared "
+                         "and tiny workloads (16- and 256-token pages)")
     ap.add_argument("--copy-probe-gib", type=float, default=1.0,
                     help="size of the plain device copy timed beside the path (HBM reference)")
     return ap.parse_args()
@@ -345,6 +348,87 @@ def int4_leg(wl, gp, torch, np, steps):
                 frac=round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
 
 
+BOUNDARY_CASES = (("3b", 16), ("3b", 256), ("3a", 256), ("4", 16), ("1", 16))
+
+
+def boundary_leg(name, b, gp, torch, np, reps, make_workload):
+    """Boundary-pass latency per request (score + working set, then compress-or-grow with every
+    boundary request forced to compress, so each one moves its tokens) on workload `name` with
+    `b`-token pages. The integer page state and the boundary requests' K/V pages are restored
+    before every repetition, outside the timed region; the median of `reps` after 3 warmups.
+    Also the same pass for the first boundary request alone (R = 1). Bytes per request: keys
+    of C read, both score planes written and read back, and the K/V of the tokens that shift,
+    read and written."""
+    dev = "cuda:0"
+    wl = make_workload(name, "full", device=dev, page_size=b)
+    path = Path(wl, gp, torch)
+    path.build_state()
+    es = 4 if wl.dtype == "f32" else 2
+    names = ("block_tables", "n_pages", "context_lens", "refcount", "free_stack", "free_top")
+    ints = {n: getattr(wl, n).clone() for n in names}
+    req_all = wl.req_idx.clone()
+    bt = wl.block_tables.cpu().numpy()
+    pages = np.unique(bt[req_all.cpu().numpy()][bt[req_all.cpu().numpy()] >= 0])
+    pidx = torch.as_tensor(pages, dtype=torch.long, device=dev)
+    k0, v0 = wl.k_pool.index_select(0, pidx), wl.v_pool.index_select(0, pidx)
+    out = {}
+    for label, req in (("all", req_all), ("one", req_all[:1].clone())):
+        R = req.numel()
+        pol = torch.full((R,), 1, dtype=torch.int32, device=dev)   # forced compress
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        t_s, t_c = [], []
+        for it in range(reps + 3):
+            for n in names:
+                getattr(wl, n).copy_(ints[n])
+            wl.k_pool.index_copy_(0, pidx, k0)
+            wl.v_pool.index_copy_(0, pidx, v0)
+            ev[0].record()
+            gp.gp_score_and_working_set(wl.q, wl.qstate, wl.slot_ids, req, path.cache,
+                                        wl.block_tables, wl.context_lens, wl.positions,
+                                        wl.rope_theta, wl.p, wl.sm_scale, path.C_max,
+                                        a_short=path.a_s[:R], a_long=path.a_l[:R],
+                                        ws_counts=path.wsc[:R], n_cand=path.ncand[:R],
+                                        workspace=path.sws)
+            ev[1].record()
+            gp.gp_compact_or_grow(req, path.a_s[:R], path.a_l[:R], path.wsc[:R], path.ncand[:R],
+                                  wl.tau, wl.k_loc, 0, path.cache, wl.block_tables, wl.n_pages,
+                                  wl.context_lens, wl.refcount, wl.free_stack, wl.free_top,
+                                  policies=pol, decision=path.dec[:R], kept_idx=path.kept[:R],
+                                  workspace=path.cws)
+            ev[2].record()
+            torch.cuda.synchronize()
+            if it >= 3:
+                t_s.append(ev[0].elapsed_time(ev[1]))
+                t_c.append(ev[1].elapsed_time(ev[2]))
+        dec = path.dec[:R].cpu().numpy()
+        nc = path.ncand[:R].cpu().numpy().astype(np.int64)
+        kept = path.kept[:R].cpu().numpy()
+        ctx0 = ints["context_lens"].cpu().numpy()
+        ctx1 = wl.context_lens.cpu().numpy()
+        moved = 0
+        for i, r in enumerate(req.cpu().tolist()):
+            if dec[i] not in (0, 2, 4) or ctx1[r] == ctx0[r]:
+                continue
+            for h in range(wl.H_kv):
+                row = kept[i, h, :nc[i]]
+                diff = np.nonzero(row != np.arange(len(row)))[0]
+                first = int(diff[0]) if len(diff) else int(ctx1[r])
+                moved += (int(ctx1[r]) - first) * wl.d * es * 2 * 2
+        byts = int(sum(int(c) * wl.H_kv * wl.d * es + 4 * wl.H_kv * int(c) * 4 for c in nc)) + moved
+        ms_s, ms_c = float(np.median(t_s)), float(np.median(t_c))
+        ms = ms_s + ms_c
+        out[label] = dict(requests=int(R), us_per_request=round(ms * 1e3 / R, 1),
+                          score_us=round(ms_s * 1e3, 1), compact_us=round(ms_c * 1e3, 1),
+                          bytes=byts, gbps=round(byts / (ms * 1e-3) / 1e9, 1),
+                          mean_candidates=round(float(nc.mean()), 1),
+                          decisions=sorted(set(int(x) for x in dec)))
+    res = dict(workload=WORKLOAD_NAMES[name], page_size=b, k_loc=int(wl.k_loc), **out["all"],
+               single_request=out["one"])
+    del wl, path, k0, v0
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, path, budget_s, np):
     """The float64 oracle on a bounded sample: decode of whole requests, then the boundary pass
     of boundary requests, until the time budget is used. Returns GB/s on the same byte model."""
@@ -563,6 +647,14 @@ def main():
                         score_us=rows_ms["score_and_working_set"] * 1e3,
                         compact_us=cmp_ms * 1e3, decisions=path.dec.cpu().tolist())
 
+    bpass = None
+    if args.boundary_pass:
+        bpass = []
+        for name, b in BOUNDARY_CASES:
+            print(f"[bench] boundary pass on workload {name}, {b}-token pages", file=sys.stderr,
+                  flush=True)
+            bpass.append(boundary_leg(name, b, gp, torch, np, 20, make_workload))
+
     cpu = None
     if args.cpu_seconds > 0:
         print(f"[bench] cpu_baseline (oracle, ~{args.cpu_seconds:.0f} s)", file=sys.stderr,
@@ -600,6 +692,7 @@ def main():
         "decode_frac_of_copy": round(achieved / copy_gbps, 4),
         "copy_gbps": round(copy_gbps, 1),
         "boundary": boundary,
+        "boundary_pass": bpass,
         "int4_decode": int4,
         "single_stream": single,
         "rows_ms": {k: round(v, 4) for k, v in rows_ms.items()},

@@ -7,7 +7,9 @@ Steps, in the order GrowPage App. E.1 runs them at a capacity boundary:
    on pairs (i, i + d/2) with angle pos * theta^(-2i/d); theta <= 0 disables it.
 2. Candidate set C_t: every cached slot outside the most recent page (Sec. 3.2, App. E.1
    "exclude the most recent physical KV block"). The slots of that last page are the
-   protected recent tokens R_t of Sec. 3.3.
+   protected recent tokens R_t of Sec. 3.3. With pages longer than the 16-token recent
+   window of Sec. 4.1 (its runs use 256-token blocks) the window lies inside that page, and
+   Eq. 10 selects only from C_t, so every token of the last page is kept.
 3. Scores: for each view x and KV head h, the softmax over C_t of qtilde^x_g . k / sqrt(d) for
    each query head g mapped to h (native GQA mapping, App. E.1), averaged over those heads.
 4. Working set (Eq. 2 / Eq. 7): K^x_h = min{k : sum of the k largest weights >= p}, computed
@@ -42,7 +44,8 @@ products depend only on relative position; full retention (p -> 1) gives K = |C|
 weights give K = ceil(p |C|); one dominant weight gives K = 1; brute force over all subsets of
 tiny candidate sets (GrowPage Thm. 3.1 / App. C: the top-k weights maximise retained mass);
 the tight worst-case construction of App. C; equal summaries give Delta = 0 -> compress and
-the inverse policy flips it; selection against brute-force enumeration; page conservation,
+the inverse policy flips it; selection against brute-force enumeration, and in closed form for
+256-token pages with a 64-token quota under monotone scores; page conservation,
 refcount bookkeeping, shared pages untouched and kept K/V bit-identical after compaction;
 hand-worked GrowPage-Shrink decisions over several layers (tests/golden/shrink_cases.txt); a
 shrink's geometry, capacity floor, released page and moved K/V; a call over two layers whose
@@ -52,6 +55,11 @@ through the layered call equal to the single-layer call.
 from fractions import Fraction
 
 import numpy as np
+
+from .fp8 import e4m3_decode
+from .int4 import pack_pairs, pack_values, unpack_pairs, unpack_values
+
+TAG_RELEASE, TAG_FP8, TAG_BF16, TAG_INT4 = 0, 1, 2, 3
 
 COMPRESS, GROW, GROW_FALLBACK_COMPRESS, NO_PAGES, SHRINK = 0, 1, 2, 3, 4
 POLICY_AUTO, POLICY_FORCE_COMPRESS, POLICY_FORCE_GROW, POLICY_INVERSE, POLICY_SHRINK = 0, 1, 2, 3, 4
@@ -98,25 +106,57 @@ def candidate_count(ctx, page_size):
 
 
 # ---------------------------------------------------------------------------- step 3
-def score_request(q_t, qbar, pos, keys, theta, sm_scale, G):
+def score_request(q_t, qbar, pos, keys, theta, sm_scale, G, visible=None):
     """Averaged short/long attention over the candidate keys.
 
-    q_t [H_q, d], qbar [2, H_q, d], keys [H_kv, n_cand, d] -> a [2, H_kv, n_cand].
+    q_t [H_q, d], qbar [2, H_q, d], keys [H_kv, n_cand, d] -> a [2, H_kv, n_cand]. Candidates
+    with visible = False (tokens of released pages) take no part in the softmax: weight 0.
     """
     H_kv, n, _ = keys.shape
     a = np.zeros((2, H_kv, n))
-    if n == 0:
+    vis = np.ones(n, dtype=bool) if visible is None else np.asarray(visible, dtype=bool)
+    if n == 0 or not vis.any():
         return a
     for x in range(2):
         for h in range(H_kv):
             acc = np.zeros(n)
             for g in range(h * G, (h + 1) * G):
                 qt = rope(calibrate(q_t[g], qbar[x, g]), pos, theta)
-                z = keys[h] @ qt * sm_scale
+                z = keys[h][vis] @ qt * sm_scale
                 w = np.exp(z - z.max())
-                acc += w / w.sum()
+                acc[vis] += w / w.sum()
             a[x, h] = acc / G
     return a
+
+
+def candidate_keys(r, n, k_pool, block_tables, page_size, mixed=None):
+    """Keys of request r's first n slots as float64 [H_kv, n, d] and their visibility.
+
+    With mixed-precision pages (`mixed`: page_tag, k8, k_scale, k4, k4_scale) an fp8 key is its
+    E4M3 code value times the row scale, an INT4 key its signed nibbles times the row's half
+    scale (PASK App. B.5), and the tokens of released pages are not visible.
+    """
+    b = page_size
+    slots = np.arange(n)
+    pages = np.asarray(block_tables[r])[slots // b].astype(np.int64)
+    offs = slots % b
+    keys = np.asarray(k_pool)[pages, :, offs, :].astype(np.float64)          # [n, H, d]
+    vis = np.ones(n, dtype=bool)
+    if mixed is not None and n:
+        tags = np.asarray(mixed["page_tag"])[pages]
+        vis = tags != TAG_RELEASE
+        f8 = tags == TAG_FP8
+        if f8.any():
+            kc = e4m3_decode(np.asarray(mixed["k8"])[pages[f8], :, offs[f8], :])
+            ks = np.asarray(mixed["k_scale"])[pages[f8], :, offs[f8]].astype(np.float64)
+            keys[f8] = kc * ks[..., None]
+        i4 = tags == TAG_INT4
+        if i4.any():
+            kc = unpack_pairs(np.asarray(mixed["k4"])[pages[i4], :, offs[i4], :], axis=-1)
+            ks = np.asarray(mixed["k4_scale"])[pages[i4], :, offs[i4]].astype(np.float64)
+            keys[i4] = kc.astype(np.float64) * ks[..., None]
+        keys[~vis] = 0.0
+    return keys.transpose(1, 0, 2), vis
 
 
 # ---------------------------------------------------------------------------- step 4
@@ -150,8 +190,8 @@ def working_set_size(weights, p):
 
 
 def score_and_working_set(q, qstate, slot_ids, req_idx, k_pool, block_tables, context_lens,
-                          positions, page_size, rope_theta, p, sm_scale, C_max=None):
-    """Steps 1-4 for the boundary requests req_idx.
+                          positions, page_size, rope_theta, p, sm_scale, C_max=None, mixed=None):
+    """Steps 1-4 for the boundary requests req_idx (`mixed`: see candidate_keys).
 
     Returns a_short, a_long [R, H_kv, C_max] (float64, zero beyond |C|), ws_counts
     [R, H_kv, 2] (K^S, K^L computed on the float64 weights) and n_cand [R].
@@ -170,11 +210,9 @@ def score_and_working_set(q, qstate, slot_ids, req_idx, k_pool, block_tables, co
     ws = np.zeros((R, H_kv, 2), dtype=np.int64)
     for i, r in enumerate(req_idx):
         n = ncs[i]
-        slots = np.arange(n)
-        pages = np.asarray(block_tables[r])[slots // page_size]
-        keys = kp[pages, :, slots % page_size, :].astype(np.float64).transpose(1, 0, 2)
+        keys, vis = candidate_keys(r, n, kp, block_tables, page_size, mixed)
         a = score_request(q[r], np.asarray(qstate[int(slot_ids[r])], dtype=np.float64),
-                          int(positions[r]), keys, rope_theta, sm_scale, G)
+                          int(positions[r]), keys, rope_theta, sm_scale, G, vis)
         a_s[i, :, :n] = a[0]
         a_l[i, :, :n] = a[1]
         for h in range(H_kv):
@@ -250,21 +288,102 @@ def select_kept(s, K_t, page_size, k_loc):
     return np.sort(chosen)
 
 
+# ---------------------------------------------------------------------------- mixed pages
+def bf16_bits(x):
+    """bfloat16 bit patterns (uint16) of float64 values rounded to nearest, ties to even: 8
+    significant bits, the subnormal spacing 2^-133 below 2^-126."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                           # |x| = m 2^e with 0.5 <= m < 1
+    ulp = np.maximum(e - 8, -133)
+    y = np.ldexp(np.rint(np.ldexp(x, -ulp)), ulp)   # exact scalings around one rounding
+    return (y.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _move_mixed(kp, vp, mx, old_bt, new_bt, srcs, first_repl, ctx_new, b, P):
+    """Compaction of one layer of a mixed-precision cache for one request.
+
+    srcs[h][j] is the source slot of destination slot j of KV head h. Pages from the first one
+    that changes for any head (an evicted token or a replaced page) to the last destination
+    page are rewritten for every head. A destination page keeps a precision when every page
+    that supplies it a token (any head) has that tag, and the tokens move with their codes and
+    row scales bit for bit; otherwise it becomes a bf16 page and each token it receives is
+    stored as its dequantised value rounded to bf16 once. kp / vp are the bf16 pools as 16-bit
+    patterns; the pools in `mx` and its page_tag are updated in place.
+    """
+    n_dest = ctx_new // b
+    dpm = first_repl
+    for src in srcs:
+        moved = np.nonzero(src[:ctx_new] != np.arange(ctx_new))[0]
+        if len(moved):
+            dpm = min(dpm, int(moved[0]) // b)
+    tags = mx["page_tag"]
+    old_tag = np.asarray(tags)[old_bt[:P]].copy()
+    new_tag = {}
+    for dp in range(dpm, n_dest):
+        lo = min(int(src[dp * b]) for src in srcs) // b
+        hi = max(int(src[dp * b + b - 1]) for src in srcs) // b
+        ts = set(old_tag[lo:hi + 1].tolist())
+        new_tag[dp] = ts.pop() if len(ts) == 1 else TAG_BF16
+    kb, vb = kp.view(np.uint16), vp.view(np.uint16)
+    old = {name: np.asarray(mx[name]).copy() for name in
+           ("k8", "v8", "k_scale", "v_scale", "k4", "v4", "k4_scale", "v4_scale")}
+    kb0, vb0 = kb.copy(), vb.copy()
+    vwork = {}
+    for h, src in enumerate(srcs):
+        for j in range(dpm * b, ctx_new):
+            sl = int(src[j])
+            sp, so, ts = int(old_bt[sl // b]), sl % b, int(old_tag[sl // b])
+            dp, do = j // b, j % b
+            pd, td = int(new_bt[dp]), new_tag[dp]
+            if td == ts == TAG_BF16:
+                kb[pd, h, do, :] = kb0[sp, h, so, :]
+                vb[pd, h, :, do] = vb0[sp, h, :, so]
+            elif td == ts == TAG_FP8:
+                mx["k8"][pd, h, do, :] = old["k8"][sp, h, so, :]
+                mx["v8"][pd, h, :, do] = old["v8"][sp, h, :, so]
+                mx["k_scale"][pd, h, do] = old["k_scale"][sp, h, so]
+                mx["v_scale"][pd, h, do] = old["v_scale"][sp, h, so]
+            elif td == ts == TAG_INT4:
+                mx["k4"][pd, h, do, :] = old["k4"][sp, h, so, :]
+                w = vwork.setdefault((pd, h), np.zeros((kp.shape[3], b), dtype=np.int8))
+                w[:, do] = unpack_values(old["v4"][sp, h])[:, so]
+                mx["k4_scale"][pd, h, do] = old["k4_scale"][sp, h, so]
+                mx["v4_scale"][pd, h, do] = old["v4_scale"][sp, h, so]
+            else:
+                assert td == TAG_BF16 and ts in (TAG_FP8, TAG_INT4)
+                if ts == TAG_FP8:
+                    kv = e4m3_decode(old["k8"][sp, h, so, :]) * float(old["k_scale"][sp, h, so])
+                    vv = e4m3_decode(old["v8"][sp, h, :, so]) * float(old["v_scale"][sp, h, so])
+                else:
+                    kc = unpack_pairs(old["k4"][sp, h, so, :], axis=-1).astype(np.float64)
+                    vc = unpack_values(old["v4"][sp, h])[:, so].astype(np.float64)
+                    kv = kc * float(old["k4_scale"][sp, h, so])
+                    vv = vc * float(old["v4_scale"][sp, h, so])
+                kb[pd, h, do, :] = bf16_bits(kv)
+                vb[pd, h, :, do] = bf16_bits(vv)
+    for (pd, h), w in vwork.items():
+        mx["v4"][pd, h] = pack_values(w)
+    for dp, t in new_tag.items():
+        tags[int(new_bt[dp])] = t
+
+
 # ---------------------------------------------------------------------------- steps 5-8
 def compact_or_grow(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, policy,
                     k_pool, v_pool, block_tables, n_pages, context_lens, refcount,
-                    free_stack, free_top, page_size, policies=None):
+                    free_stack, free_top, page_size, policies=None, mixed=None):
     """Decision, allocation, selection and compaction for the boundary requests of one layer.
 
     State arrays (numpy) are updated in place: k_pool [N, H, b, d], v_pool [N, H, d, b],
     block_tables [B, max_pages], n_pages, context_lens, refcount, free_stack, free_top [1].
-    `policies` optionally gives a per-request policy overriding `policy`.
+    `policies` optionally gives a per-request policy overriding `policy`. `mixed` (page_tag
+    and the fp8 / INT4 pools of a mixed-precision cache, bf16 pools given as bit patterns)
+    selects the mixed-precision compaction of _move_mixed.
     Returns decision [R] and kept_idx [R, H_kv, C_max] (-1 where unused).
     """
     dec, kept = compact_or_grow_layers(req_idx, [a_short], [a_long], [ws_counts], n_cand, tau,
                                        k_loc, policy, [k_pool], [v_pool], block_tables, n_pages,
                                        context_lens, refcount, free_stack, free_top, page_size,
-                                       policies)
+                                       policies, None if mixed is None else [mixed])
     return dec, kept[0]
 
 
@@ -278,11 +397,14 @@ def _pop(free_stack, free_top):
 
 def compact_or_grow_layers(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_loc, policy,
                            k_pools, v_pools, block_tables, n_pages, context_lens, refcount,
-                           free_stack, free_top, page_size, policies=None):
+                           free_stack, free_top, page_size, policies=None, mixed_layers=None):
     """As compact_or_grow for L layers that share block tables and the page pool: a_short,
-    a_long, ws_counts, k_pools, v_pools are lists with one entry per layer. One decision per
-    request from the mean over all layers and KV heads (Eq. 8); selection and compaction per
-    layer. Returns decision [R] and a list of kept_idx [R, H_kv, C_max], one per layer."""
+    a_long, ws_counts, k_pools, v_pools (and mixed_layers) are lists with one entry per layer.
+    One decision per request from the mean over all layers and KV heads (Eq. 8); selection and
+    compaction per layer. In a mixed-precision cache a request that must move tokens while one
+    of its pages is released (in any layer) is left untouched (NO_PAGES): a page's precision
+    is one tag for all its slots, so a released token could not stay masked among live ones.
+    Returns decision [R] and a list of kept_idx [R, H_kv, C_max], one per layer."""
     b = page_size
     L = len(k_pools)
     R = len(req_idx)
@@ -332,6 +454,11 @@ def compact_or_grow_layers(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_l
             continue
         ctx_new = K_t + R_n
         n_dest = -(-ctx_new // b)
+        if mixed_layers is not None and any(
+                (np.asarray(m["page_tag"])[block_tables[r, :P]] == TAG_RELEASE).any()
+                for m in mixed_layers):
+            decision[i] = NO_PAGES
+            continue
         shared = [j for j in range(n_dest) if refcount[block_tables[r, j]] > 1]
         if len(shared) > int(free_top[0]):
             decision[i] = NO_PAGES
@@ -345,12 +472,16 @@ def compact_or_grow_layers(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_l
         # selection per layer and KV head, then move the tokens (read everything first)
         src_slots = np.arange(ctx)
         for l in range(L):
+            srcs = []
             for h in range(H):
                 s = np.maximum(np.asarray(a_short[l][i, h, :n], dtype=np.float64),
                                np.asarray(a_long[l][i, h, :n], dtype=np.float64))
                 kept = select_kept(s, K_t, b, k_loc)
                 kept_idx[l][i, h, :K_t] = kept
                 src = np.concatenate([kept, src_slots[n:ctx]])
+                srcs.append(src)
+                if mixed_layers is not None:
+                    continue
                 sp, so = old_bt[src // b], src % b
                 kv_k = k_pools[l][sp, h, so, :].copy()
                 kv_v = v_pools[l][sp, h, :, so].copy()
@@ -358,6 +489,9 @@ def compact_or_grow_layers(req_idx, a_short, a_long, ws_counts, n_cand, tau, k_l
                 dp, do = block_tables[r][dst // b], dst % b
                 k_pools[l][dp, h, do, :] = kv_k
                 v_pools[l][dp, h, :, do] = kv_v
+            if mixed_layers is not None:
+                _move_mixed(k_pools[l], v_pools[l], mixed_layers[l], old_bt, block_tables[r],
+                            srcs, min(shared) if shared else n_dest, ctx_new, b, P)
         if shrink:
             releases.append(int(old_bt[P - 1]))
             block_tables[r, P - 1] = -1

@@ -209,6 +209,23 @@ def test_selection_brute_force(seed):
         assert got == sorted(best)
 
 
+def test_selection_paper_scale_closed_form():
+    """256-token pages with a 64-token local quota (GrowPage's default runs, App. D.2). With scores
+    strictly decreasing in the token index, each page's quota is its first 64 tokens and the
+    global fill takes the lowest remaining indices; strictly increasing scores mirror it."""
+    b, kloc, n = 256, 64, 4 * 256
+    K = 3 * 256                                   # P = 5 full pages: (P - 1) b - |R| = 768
+    dec = ob.select_kept(np.arange(n, 0, -1, dtype=np.float64), K, b, kloc)
+    # non-quota tokens: 192 per page; the 256 worst are page 3's 192 and page 2's last 64
+    assert dec.tolist() == list(range(0, 704)) + list(range(768, 832))
+    inc = ob.select_kept(np.arange(1, n + 1, dtype=np.float64), K, b, kloc)
+    # mirrored: page 0's 192 non-quota tokens and page 1's first 64 go
+    assert inc.tolist() == list(range(192, 256)) + list(range(320, 1024))
+    # every page keeps at least its quota
+    for kept in (dec, inc):
+        assert all(np.sum((kept >= j) & (kept < j + b)) >= kloc for j in range(0, n, b))
+
+
 # ------------------------------------------------------------------ allocation + compaction
 def _run_boundary(wl, policies=None, free_top=None):
     st = oracle_state(wl)
@@ -248,9 +265,10 @@ def _check_pool_invariants(wl, st, check_free=True):
         assert st["refcount"][pg] == held.get(pg, 0)                 # refcounts = references
 
 
-@pytest.mark.parametrize("cfg", ["1", "3a", "4"])
-def test_compaction_invariants(cfg):
-    wl = make_workload(cfg, "small")
+@pytest.mark.parametrize("cfg,page_size", [("1", 16), ("3a", 16), ("4", 16), ("3a", 256),
+                                            ("4", 64), ("1", 128)])
+def test_compaction_invariants(cfg, page_size):
+    wl = make_workload(cfg, "small", page_size=page_size)
     pol = wl.req_policy if cfg == "4" else None
     before, st, dec, kept, req, (a_s, a_l, ws, nc) = _run_boundary(wl, policies=pol)
     _check_pool_invariants(wl, before)
@@ -271,6 +289,9 @@ def test_compaction_invariants(cfg):
         assert dec[i] in (ob.COMPRESS, ob.GROW_FALLBACK_COMPRESS)
         n = int(nc[i])
         R_n = ctx0 - n
+        # the protected tokens are the whole last page, also where it is longer than the
+        # 16-token recent window (b = 256): none of them is a candidate
+        assert R_n == ctx0 - (-(-ctx0 // b) - 1) * b and 0 < R_n <= b
         K_t = min(n, (P0 - 1) * b - R_n)
         assert st["context_lens"][r] == K_t + R_n == (P0 - 1) * b
         assert st["n_pages"][r] == P0
