@@ -223,7 +223,10 @@ int gp_update_query_summaries(const void* q, int q_dtype, int B, int H_q, int he
  *   |C| exceeds C_max, gets n_cand = -1 and ws_counts = -1 and is otherwise skipped.
  *   Limits: 2 * (H_q / H_kv) <= 16, C_max <= 32768 and a multiple of 4, 0 < p <= 1.
  *   workspace >= gp_score_and_working_set_workspace_size(...) bytes.
- * Uniform caches only (page_tag must be NULL).
+ *   Mixed-precision caches (page_tag given; GP_BF16 with the fp8 and INT4 key pools): an fp8
+ *   key is its E4M3 code value times the row scale, an INT4 key its signed nibbles times the
+ *   row's half scale (PASK App. B.5), and the tokens of released pages take no part in the
+ *   softmax (weight 0; |C| still counts their slots).
  */
 size_t gp_score_and_working_set_workspace_size(int R, int H_q, int H_kv, int head_dim,
                                                int page_size, int C_max);
@@ -259,7 +262,16 @@ int gp_score_and_working_set(const void* q, int q_dtype, int B, int H_q, const f
  *   entries past |C| are not written.
  *   a_short / a_long / ws_counts / n_cand as produced by gp_score_and_working_set.
  *   kv, block_tables, n_pages, context_lens, refcount, free_stack, free_top are updated in place.
- *   Uniform caches only (page_tag must be NULL). Requests of one call must be distinct.
+ *   Requests of one call must be distinct.
+ *   Mixed-precision caches (page_tag given; GP_BF16 with every fp8 and INT4 pool; pages of 16
+ *   or 32 tokens; one layer): a request that must move tokens while one of its pages is
+ *   released is answered NO_PAGES and left untouched (one tag per page cannot keep a released
+ *   token masked among live ones). Otherwise every KV head rewrites the pages from the first
+ *   one that changes for any head; a destination page keeps a precision when all the pages
+ *   that supply its tokens (any head) carry it, and the tokens move with their codes and row
+ *   scales bit for bit (INT4 value nibbles regrouped into four-token blocks); else it becomes a
+ *   bf16 page holding each token's code * scale rounded once to bf16 (nearest, ties to even).
+ *   page_tag of the rewritten pages is updated at the end of the move.
  *   Limits: R <= 1024, page_size 16, 32, 64, 128 or 256 (32-token fp32 pages need head_dim
  *   64), C_max <= 32768 and a multiple of 4. A Shrink evicts up to 2 * page_size tokens: with
  *   32-token pages GP_POLICY_SHRINK is rejected and a per-request Shrink is answered NO_PAGES.

@@ -65,6 +65,17 @@ struct CParams {
   const int32_t* policies;
   uint8_t* k;
   uint8_t* v;
+  // mixed-precision cache (page_tag non-null): the fp8 and INT4 pools of the bf16 cache
+  uint8_t* page_tag;
+  uint8_t* k8;
+  uint8_t* v8;
+  float* k_scale;
+  float* v_scale;
+  uint8_t* k4;
+  uint8_t* v4;
+  uint16_t* k4_scale;
+  uint16_t* v4_scale;
+  int32_t* new_tag;   // [R, max_pages] tag of each rewritten destination page (mixed caches)
   int32_t* block_tables;
   int32_t* n_pages;
   int32_t* context_lens;
@@ -248,6 +259,9 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
     const int pg = P.block_tables[(size_t)s_r[i] * P.max_pages + j];
     P.old_bt[(size_t)i * P.max_pages + j] = pg;
     if (pg < 0 || pg >= P.num_pages) atomicOr(&s_flags[i], F_BAD);
+    // mixed caches: a request that must move tokens keeps its pages when one is released
+    // (one tag per page cannot keep a released token masked among live ones)
+    else if (P.page_tag && P.page_tag[pg] == GP_TAG_RELEASE) atomicOr(&s_flags[i], F_BAD);
     else if (j < s_ndest[i] && P.refcount[pg] > 1) atomicAdd(&s_cnt[i], 1);
   }
   __syncthreads();
@@ -1025,6 +1039,334 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
   }
 }
 
+// ------------------------------------------------------------------ mixed-precision pages
+// bf16 bits of a double, to nearest with ties to even: round to float with round-to-odd (the
+// float keeps 16 more bits than bf16, also among subnormals), then float to bf16 to nearest even
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
+  const float f = (float)x;
+  uint32_t u = __float_as_uint(f);
+  const double back = (double)f;
+  if (back != x) {
+    if (fabs(back) > fabs(x)) u -= 1u;  // the float rounded away from zero: step back
+    u |= 1u;                            // inexact: odd
+  }
+  return gp::f32_to_bf16_bits(__uint_as_float(u));
+}
+
+// Destination tags of a compacting request (one workgroup per request): every head rewrites
+// from the first destination page that changes for any head; a destination page keeps the
+// precision of the pages that supply its tokens (any head) when they share one tag, else it
+// becomes a bf16 page.
+__global__ __launch_bounds__(256) void mixed_plan_kernel(CParams P) {
+  const int i = blockIdx.x;
+  const Info inf = P.info[i];
+  if (inf.mode != MODE_COMPACT) return;
+  const int b = P.page_size, H = P.H_kv;
+  __shared__ int s_dpm;
+  if (threadIdx.x == 0) {
+    int m = INT_MAX;
+    for (int h = 0; h < H; ++h) m = min(m, P.dp0[(size_t)i * H + h]);
+    s_dpm = m;
+  }
+  __syncthreads();
+  const int dpm = s_dpm;
+  for (int h = threadIdx.x; h < H; h += blockDim.x) P.dp0[(size_t)i * H + h] = dpm;
+  for (int dp = dpm + (int)threadIdx.x; dp < inf.n_dest; dp += blockDim.x) {
+    int lo = INT_MAX, hi = 0;
+    for (int h = 0; h < H; ++h) {
+      const int32_t* ev = P.ev + ((size_t)i * H + h) * P.max_evict;
+      auto src = [&](int j) {  // j + #{k : ev[k] - k <= j}
+        int c = 0;
+        for (int k = 0; k < inf.E; ++k) c += (ev[k] - k <= j) ? 1 : 0;
+        return j + c;
+      };
+      lo = min(lo, src(dp * b) / b);
+      hi = max(hi, src(dp * b + b - 1) / b);
+    }
+    int tag = P.page_tag[P.old_bt[(size_t)i * P.max_pages + lo]];
+    for (int lp = lo + 1; lp <= hi; ++lp)
+      if (P.page_tag[P.old_bt[(size_t)i * P.max_pages + lp]] != tag) tag = GP_TAG_BF16;
+    P.new_tag[(size_t)i * P.max_pages + dp] = tag;
+  }
+}
+
+// The destination tags, written once every page of the call has moved.
+__global__ __launch_bounds__(256) void mixed_tags_kernel(CParams P) {
+  const int i = blockIdx.x;
+  const Info inf = P.info[i];
+  if (inf.mode != MODE_COMPACT) return;
+  const int dpm = P.dp0[(size_t)i * P.H_kv];
+  for (int dp = dpm + (int)threadIdx.x; dp < inf.n_dest; dp += blockDim.x)
+    P.page_tag[P.block_tables[(size_t)inf.r * P.max_pages + dp]] =
+        (uint8_t)P.new_tag[(size_t)i * P.max_pages + dp];
+}
+
+// Bytes of one (page, KV head) in a format: key part and value part (codes, then the row
+// scales); the snapshot and the LDS staging hold a page in its own format this way.
+struct MixedBytes {
+  int kc, vc, sc;  // key code bytes, value code bytes, scale bytes per part
+};
+__device__ __forceinline__ MixedBytes mixed_bytes(int tag, int b, int D) {
+  if (tag == GP_TAG_FP8) return MixedBytes{b * D, b * D, 4 * b};
+  if (tag == GP_TAG_INT4) return MixedBytes{b * D / 2, b * D / 2, 2 * b};
+  return MixedBytes{2 * b * D, 2 * b * D, 0};
+}
+// (page, head) sources of each part in the pools
+__device__ __forceinline__ void mixed_src(const CParams& P, int tag, int pg, int h, const uint8_t** kc,
+                                          const uint8_t** vc, const uint8_t** ks, const uint8_t** vs) {
+  const size_t ph = (size_t)pg * P.H_kv + h, b = P.page_size, D = P.D;
+  if (tag == GP_TAG_FP8) {
+    *kc = P.k8 + ph * b * D;
+    *vc = P.v8 + ph * b * D;
+    *ks = reinterpret_cast<const uint8_t*>(P.k_scale + ph * b);
+    *vs = reinterpret_cast<const uint8_t*>(P.v_scale + ph * b);
+  } else if (tag == GP_TAG_INT4) {
+    *kc = P.k4 + ph * b * D / 2;
+    *vc = P.v4 + ph * b * D / 2;
+    *ks = reinterpret_cast<const uint8_t*>(P.k4_scale + ph * b);
+    *vs = reinterpret_cast<const uint8_t*>(P.v4_scale + ph * b);
+  } else {
+    *kc = P.k + ph * b * D * 2;
+    *vc = P.v + ph * b * D * 2;
+    *ks = *vs = nullptr;
+  }
+}
+
+__device__ __forceinline__ void copy_bytes(uint8_t* dst, const uint8_t* src, int n) {
+  // n is a multiple of 16 for codes and of 4 for scales
+  if ((n & 15) == 0) {
+    for (int q = threadIdx.x; q < n / 16; q += CP_THREADS)
+      reinterpret_cast<u32x4_t*>(dst)[q] = reinterpret_cast<const u32x4_t*>(src)[q];
+  } else {
+    for (int q = threadIdx.x; q < n / 4; q += CP_THREADS)
+      reinterpret_cast<uint32_t*>(dst)[q] = reinterpret_cast<const uint32_t*>(src)[q];
+  }
+}
+
+// The snapshot of a mixed cache holds the saved page in its own format.
+__global__ __launch_bounds__(CP_THREADS) void snapshot_mixed_kernel(CParams P) {
+  const int n_items = *P.n_items;
+  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int2 item = P.items[it];
+    const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y;
+    const Info inf = P.info[i];
+    for (int s = 0; s < P.span; ++s) {
+      const int lp = (c + 1) * P.chunk_pages + s;
+      if (!from_snapshot(P, lp, c, inf.n_dest)) continue;
+      const int pg = P.old_bt[(size_t)i * P.max_pages + lp];
+      const int tag = P.page_tag[pg];
+      const MixedBytes mb = mixed_bytes(tag, P.page_size, P.D);
+      const uint8_t *kc, *vc, *ks, *vs;
+      mixed_src(P, tag, pg, h, &kc, &vc, &ks, &vs);
+      uint8_t* kd = snap_ptr(P, i, h, lp, 0);
+      uint8_t* vd = snap_ptr(P, i, h, lp, 1);
+      copy_bytes(kd, kc, mb.kc);
+      copy_bytes(vd, vc, mb.vc);
+      if (mb.sc) {
+        copy_bytes(kd + mb.kc, ks, mb.sc);
+        copy_bytes(vd + mb.vc, vs, mb.sc);
+      }
+    }
+  }
+}
+
+// signed nibble n (0..7 from the low end) of a 32-bit word
+__device__ __forceinline__ int nib(uint32_t w, int n) { return (int32_t)(w << (28 - 4 * n)) >> 28; }
+
+// Compaction of a mixed-precision cache (pages of 16 or 32 tokens). Per item, destination pages
+// one at a time: the source pages dp .. dp + span are staged in LDS in their own formats (an LDS
+// ring, one new page per destination page); the destination page is then written in its new
+// format: the same format as every source (codes and row scales copied; INT4 value nibbles
+// regrouped into four-token blocks) or bf16 (each element's exact code * scale rounded once).
+constexpr int MX_SLOT = 2 * (2 * 32 * 128) + 2 * 4 * 32;  // bf16 K + V of a 32-token page + scales
+__global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
+  const int n_items = *P.n_items;
+  const int L = P.chunk_pages, span = P.span, ring = span + 1;
+  const int lb = P.log_b, b = 1 << lb, D = P.D;
+  extern __shared__ __align__(16) uint8_t s_mx[];  // ring x MX_SLOT bytes
+  __shared__ int s_thr[MAX_EVICT];
+  __shared__ int s_src[32];
+  __shared__ int s_tag[MAX_SPAN + 1];
+  __shared__ long long s_soff[CHUNK_PAGES + MAX_SPAN];
+  __shared__ int s_spg[CHUNK_PAGES + MAX_SPAN], s_dpg[CHUNK_PAGES];
+  const int vslot = D / 16;  // INT4 value dimension slot stride: slot(j) = (j % 16) * (D/16) + j / 16
+  for (int item_k = blockIdx.x; item_k < n_items; item_k += gridDim.x) {
+    __syncthreads();
+    const int2 item = P.items[item_k];
+    const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y;
+    const Info inf = P.info[i];
+    const int E = inf.E;
+    const int dp0 = P.dp0[item.x];
+    const int dp_lo = max(dp0, c * L), dp_hi = min((c + 1) * L, inf.n_dest);
+    if (threadIdx.x < MAX_EVICT)
+      s_thr[threadIdx.x] = (int)threadIdx.x < E
+                               ? P.ev[((size_t)i * P.H_kv + h) * P.max_evict + threadIdx.x] - (int)threadIdx.x
+                               : INT_MAX;
+    if (threadIdx.x < dp_hi - dp_lo + span) {
+      const int lp = dp_lo + threadIdx.x;
+      long long so = -2;  // -2 past the old pages, -1 snapshot, else 0
+      int pg = -1;
+      if (lp < inf.P) {
+        pg = P.old_bt[(size_t)i * P.max_pages + lp];
+        so = from_snapshot(P, lp, c, inf.n_dest) ? -1 : 0;
+      }
+      s_soff[threadIdx.x] = so;
+      s_spg[threadIdx.x] = pg;
+      if (lp < dp_hi) s_dpg[threadIdx.x] = P.block_tables[(size_t)inf.r * P.max_pages + lp];
+    }
+    __syncthreads();
+    // stage source page lp (its own format) into ring slot lp % ring
+    auto stage = [&](int lp) {
+      const int t = lp - dp_lo;
+      uint8_t* dst = s_mx + (size_t)(lp % ring) * MX_SLOT;
+      if (s_soff[t] == -2) {
+        if (threadIdx.x == 0) s_tag[lp % ring] = -1;
+        return;
+      }
+      const int pg = s_spg[t];
+      const int tag = P.page_tag[pg];
+      if (threadIdx.x == 0) s_tag[lp % ring] = tag;
+      const MixedBytes mb = mixed_bytes(tag, b, D);
+      const uint8_t *kc, *vc, *ks, *vs;
+      if (s_soff[t] == -1) {
+        kc = snap_ptr(P, i, h, lp, 0);
+        vc = snap_ptr(P, i, h, lp, 1);
+        ks = kc + mb.kc;
+        vs = vc + mb.vc;
+      } else {
+        mixed_src(P, tag, pg, h, &kc, &vc, &ks, &vs);
+      }
+      // layout in the slot: key codes | value codes | key scales | value scales
+      copy_bytes(dst, kc, mb.kc);
+      copy_bytes(dst + mb.kc, vc, mb.vc);
+      if (mb.sc) {
+        copy_bytes(dst + mb.kc + mb.vc, ks, mb.sc);
+        copy_bytes(dst + mb.kc + mb.vc + mb.sc, vs, mb.sc);
+      }
+    };
+    for (int lp = dp_lo; lp < dp_lo + span; ++lp) stage(lp);
+    for (int dp = dp_lo; dp < dp_hi; ++dp) {
+      __syncthreads();  // the previous page is done with the ring slot and s_src
+      stage(dp + span);
+      if (threadIdx.x < b) {
+        const int j = (dp << lb) + threadIdx.x;
+        int cnt = 0;
+#pragma unroll
+        for (int k = 0; k < MAX_EVICT; ++k) cnt += s_thr[k] <= j ? 1 : 0;
+        s_src[threadIdx.x] = j + cnt;
+      }
+      __syncthreads();  // sources staged, source table complete
+      const int td = P.new_tag[(size_t)i * P.max_pages + dp];
+      const size_t ph = (size_t)s_dpg[dp - dp_lo] * P.H_kv + h;
+      // element e of token q's key / value in its source format, as float (exact) or double
+      auto src_of = [&](int q, int* slot, int* tag, int* so) {
+        const int sl = s_src[q];
+        *slot = (sl >> lb) % ring;
+        *tag = s_tag[*slot];
+        *so = sl & (b - 1);
+      };
+      if (td == GP_TAG_BF16) {
+        uint16_t* kd = reinterpret_cast<uint16_t*>(P.k) + ph * b * D;
+        uint16_t* vd = reinterpret_cast<uint16_t*>(P.v) + ph * b * D;
+        for (int q2 = threadIdx.x; q2 < b * D; q2 += CP_THREADS) {
+          // key element (token q, dim e) and value element (dim e2, token q3)
+          const int q = q2 / D, e = q2 % D;
+          int sl, tg, so;
+          src_of(q, &sl, &tg, &so);
+          const uint8_t* base = s_mx + (size_t)sl * MX_SLOT;
+          const MixedBytes mb = mixed_bytes(tg, b, D);
+          uint32_t kbits;
+          if (tg == GP_TAG_BF16) {
+            kbits = reinterpret_cast<const uint16_t*>(base)[so * D + e];
+          } else if (tg == GP_TAG_FP8) {
+            const uint32_t code = base[so * D + e];
+            const float f = __builtin_amdgcn_cvt_pk_f32_fp8(code, false)[0];
+            const float sc = reinterpret_cast<const float*>(base + mb.kc + mb.vc)[so];
+            kbits = f64_to_bf16_bits((double)f * (double)sc);
+          } else {
+            const uint32_t byte = base[so * (D / 2) + e / 2];
+            const int cde = nib(byte, e & 1);
+            const uint16_t hs = reinterpret_cast<const uint16_t*>(base + mb.kc + mb.vc)[so];
+            kbits = gp::f32_to_bf16_bits((float)cde * (float)__builtin_bit_cast(_Float16, hs));
+          }
+          kd[q * D + e] = (uint16_t)kbits;
+          // value element: dim e2, token q3 of the destination page ([D][b] layout)
+          const int e2 = q2 / b, q3 = q2 % b;
+          src_of(q3, &sl, &tg, &so);
+          const uint8_t* vb = s_mx + (size_t)sl * MX_SLOT;
+          const MixedBytes mv = mixed_bytes(tg, b, D);
+          uint32_t vbits;
+          if (tg == GP_TAG_BF16) {
+            vbits = reinterpret_cast<const uint16_t*>(vb + mv.kc)[e2 * b + so];
+          } else if (tg == GP_TAG_FP8) {
+            const uint32_t code = vb[mv.kc + e2 * b + so];
+            const float f = __builtin_amdgcn_cvt_pk_f32_fp8(code, false)[0];
+            const float sc = reinterpret_cast<const float*>(vb + mv.kc + mv.vc + mv.sc)[so];
+            vbits = f64_to_bf16_bits((double)f * (double)sc);
+          } else {
+            // four-token block so / 4, dimension slot of e2, byte (so % 4) / 2, nibble so % 2
+            const int slot = (e2 % 16) * vslot + e2 / 16;
+            const uint32_t byte = vb[mv.kc + ((so >> 2) * D + slot) * 2 + ((so & 3) >> 1)];
+            const int cde = nib(byte, so & 1);
+            const uint16_t hs = reinterpret_cast<const uint16_t*>(vb + mv.kc + mv.vc + mv.sc)[so];
+            vbits = gp::f32_to_bf16_bits((float)cde * (float)__builtin_bit_cast(_Float16, hs));
+          }
+          vd[e2 * b + q3] = (uint16_t)vbits;
+        }
+      } else if (td == GP_TAG_FP8) {
+        // every source is fp8: codes and row scales move as they are
+        uint8_t* kd = P.k8 + ph * b * D;
+        uint8_t* vd = P.v8 + ph * b * D;
+        for (int q2 = threadIdx.x; q2 < b * D; q2 += CP_THREADS) {
+          const int q = q2 / D, e = q2 % D;
+          int sl, tg, so;
+          src_of(q, &sl, &tg, &so);
+          kd[q * D + e] = s_mx[(size_t)sl * MX_SLOT + so * D + e];
+          const int e2 = q2 / b, q3 = q2 % b;
+          src_of(q3, &sl, &tg, &so);
+          vd[e2 * b + q3] = s_mx[(size_t)sl * MX_SLOT + b * D + e2 * b + so];
+        }
+        if (threadIdx.x < b) {
+          const int q = threadIdx.x;
+          int sl, tg, so;
+          src_of(q, &sl, &tg, &so);
+          const float* sc = reinterpret_cast<const float*>(s_mx + (size_t)sl * MX_SLOT + 2 * b * D);
+          P.k_scale[ph * b + q] = sc[so];
+          P.v_scale[ph * b + q] = sc[b + so];
+        }
+      } else {
+        // every source is INT4: key rows and scales copied, value nibbles regrouped
+        uint8_t* kd = P.k4 + ph * b * D / 2;
+        uint8_t* vd = P.v4 + ph * b * D / 2;
+        for (int q2 = threadIdx.x; q2 < b * D / 2; q2 += CP_THREADS) {
+          const int q = q2 / (D / 2), e = q2 % (D / 2);
+          int sl, tg, so;
+          src_of(q, &sl, &tg, &so);
+          kd[q * (D / 2) + e] = s_mx[(size_t)sl * MX_SLOT + so * (D / 2) + e];
+          // destination value byte q2: block Q, dimension slot ds, byte k (tokens 4Q+2k, 4Q+2k+1)
+          const int k = q2 & 1, ds = (q2 >> 1) % D, Q = (q2 >> 1) / D;
+          uint32_t out = 0;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            src_of(4 * Q + 2 * k + t, &sl, &tg, &so);
+            const uint32_t byte = s_mx[(size_t)sl * MX_SLOT + b * D / 2 + ((so >> 2) * D + ds) * 2 + ((so & 3) >> 1)];
+            out |= ((byte >> (4 * (so & 1))) & 0xFu) << (4 * t);
+          }
+          vd[q2] = (uint8_t)out;
+        }
+        if (threadIdx.x < b) {
+          const int q = threadIdx.x;
+          int sl, tg, so;
+          src_of(q, &sl, &tg, &so);
+          const uint16_t* sc = reinterpret_cast<const uint16_t*>(s_mx + (size_t)sl * MX_SLOT + b * D);
+          P.k4_scale[ph * b + q] = sc[so];
+          P.v4_scale[ph * b + q] = sc[b + so];
+        }
+      }
+    }
+  }
+}
+
 // Window of W destination pages: LDS holds the W + span source value pages, and the W * b key
 // rows must fit K_PIECES 16-byte pieces per thread.
 int window_pages_for(int page_size, int D, int es, int span) {
@@ -1065,7 +1407,7 @@ namespace {
 // evicted lists, first changed pages and chunk work list; shared by the layers (used one layer
 // at a time, in stream order) the selection survivors and the chunk snapshots.
 struct WsLayout {
-  size_t info, old_bt, rel, layer0, layer_bytes, ev, dp0, items, n_items, cand, snap, total;
+  size_t info, old_bt, rel, new_tag, layer0, layer_bytes, ev, dp0, items, n_items, cand, snap, total;
 };
 
 WsLayout ws_layout(int L, int R, int H_kv, int max_pages, int page_size) {
@@ -1082,6 +1424,8 @@ WsLayout ws_layout(int L, int R, int H_kv, int max_pages, int page_size) {
   w.old_bt = off;
   off += (size_t)R * max_pages * 4;
   w.rel = off;
+  off += (size_t)R * max_pages * 4;
+  w.new_tag = off;
   off += (size_t)R * max_pages * 4;
   off = (off + 255) & ~(size_t)255;
   w.layer0 = off;
@@ -1127,7 +1471,7 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
   for (int l = 0; l < L; ++l) {
     const gp_kv_cache* c = kv_layers[l];
     if (!c || !c->k || !c->v) return GP_ERR_INVALID;
-    if (c->page_tag) return GP_ERR_UNSUPPORTED;
+    if ((c->page_tag != nullptr) != (kv_layers[0]->page_tag != nullptr)) return GP_ERR_INVALID;
     if (c->num_kv_heads != H_kv || c->head_dim != D || c->page_size != b ||
         c->num_pages != kv->num_pages || c->dtype != kv->dtype)
       return GP_ERR_INVALID;  // the layers share block tables and the page pool
@@ -1155,6 +1499,14 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
     if ((long)(W + span) * b * D * es > (long)V_PIECES * CP_THREADS * 16) return GP_ERR_UNSUPPORTED;
   }
   if (C_max % 4 || C_max > MAX_CAND) return GP_ERR_UNSUPPORTED;
+  // mixed-precision caches: one layer, bf16 with its fp8 and INT4 pools, 16- or 32-token pages
+  const bool mixed = kv->page_tag != nullptr;
+  if (mixed) {
+    if (L != 1 || kv->dtype != GP_BF16 || wide) return GP_ERR_UNSUPPORTED;
+    if (!kv->k8 || !kv->v8 || !kv->k_scale || !kv->v_scale || !kv->k4 || !kv->v4 ||
+        !kv->k4_scale || !kv->v4_scale)
+      return GP_ERR_INVALID;
+  }
   const WsLayout wl = ws_layout(L, R, H_kv, max_pages, b);
   if (!workspace || workspace_bytes < wl.total) return GP_ERR_WORKSPACE;
 
@@ -1198,6 +1550,18 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
   P.info = reinterpret_cast<Info*>(ws + wl.info);
   P.old_bt = reinterpret_cast<int32_t*>(ws + wl.old_bt);
   P.rel = reinterpret_cast<int32_t*>(ws + wl.rel);
+  P.new_tag = reinterpret_cast<int32_t*>(ws + wl.new_tag);
+  if (mixed) {
+    P.page_tag = kv->page_tag;
+    P.k8 = static_cast<uint8_t*>(kv->k8);
+    P.v8 = static_cast<uint8_t*>(kv->v8);
+    P.k_scale = kv->k_scale;
+    P.v_scale = kv->v_scale;
+    P.k4 = static_cast<uint8_t*>(kv->k4);
+    P.v4 = static_cast<uint8_t*>(kv->v4);
+    P.k4_scale = kv->k4_scale;
+    P.v4_scale = kv->v4_scale;
+  }
   P.cand = reinterpret_cast<unsigned long long*>(ws + wl.cand);
   P.snap = ws + wl.snap;
   // the parameters of layer l: its scores, kept indices, pools and per-layer workspace
@@ -1242,6 +1606,10 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
         else hipLaunchKernelGGL(select_write_kernel<32>, g, dim3(SEL_T), 0, s, Q);
         GP_CHECK_LAUNCH();
       }
+      if (mixed) {  // destination tags; every head rewrites from the first changed page
+        hipLaunchKernelGGL(mixed_plan_kernel, dim3(R), dim3(256), 0, s, Q);
+        GP_CHECK_LAUNCH();
+      }
       hipLaunchKernelGGL(chunk_list_kernel, dim3(1), dim3(DA_THREADS), 0, s, Q);
       GP_CHECK_LAUNCH();
     }
@@ -1251,6 +1619,17 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
   const int max_items = R * H_kv * P.max_chunks * P.npart;
   for (int l = 0; l < L; ++l) {
     const CParams Q = layer(l);
+    if (mixed) {
+      hipLaunchKernelGGL(snapshot_mixed_kernel, dim3(std::max(1, std::min(4 * cus, max_items))),
+                         dim3(CP_THREADS), 0, s, Q);
+      GP_CHECK_LAUNCH();
+      hipLaunchKernelGGL(compact_mixed_kernel, dim3(std::max(1, std::min(4 * cus, max_items))),
+                         dim3(CP_THREADS), (size_t)(span + 1) * MX_SLOT, s, Q);
+      GP_CHECK_LAUNCH();
+      hipLaunchKernelGGL(mixed_tags_kernel, dim3(R), dim3(256), 0, s, Q);
+      GP_CHECK_LAUNCH();
+      continue;
+    }
     hipLaunchKernelGGL(snapshot_kernel, dim3(std::max(1, std::min(4 * cus, max_items))),
                        dim3(CP_THREADS), 0, s, Q);
     GP_CHECK_LAUNCH();

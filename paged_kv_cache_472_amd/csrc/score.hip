@@ -1,6 +1,8 @@
 // Page-boundary demand estimation for gfx950 (GrowPage App. E.1: Eq. 12 calibration and RoPE of
 // the short/long summaries, candidate set without the most recent block, per-view attention with
-// the native GQA mapping; Sec. 3.2 Eq. 7 p-coverage working sets).
+// the native GQA mapping; Sec. 3.2 Eq. 7 p-coverage working sets). Mixed-precision caches
+// (PASK App. B.2 / B.5 pages): fp8 and INT4 keys enter as their exact code values with the row
+// scale applied to the dot product, and released tokens are left out of every softmax.
 //
 // Four launches:
 //   1. prep:      one wave per boundary request, view and query head: RMS-calibrate the summary
@@ -33,6 +35,11 @@ struct ScoreParams {
   const int32_t* slot_ids;
   const int32_t* req_idx;
   const void* k;
+  const uint8_t* page_tag;  // mixed-precision cache: per-page tag, else null
+  const uint8_t* k8;        // fp8 key codes [pages, H_kv, b, D]
+  const float* k_scale;     // fp8 row scales [pages, H_kv, b]
+  const uint8_t* k4;        // INT4 key codes [pages, H_kv, b, D/2]
+  const uint16_t* k4_scale; // INT4 row scales, half bits [pages, H_kv, b]
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* positions;
@@ -183,8 +190,52 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
     const int tok0 = t << 4;
     int pg = P.block_tables[(size_t)r * P.max_pages + tok0 / b];
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-    const bool valid_page = pg >= 0 && pg < P.num_pages;
-    if (valid_page) {
+    bool valid_page = pg >= 0 && pg < P.num_pages;
+    int tag = GP_TAG_BF16;
+    if (valid_page && P.page_tag) {
+      tag = P.page_tag[pg];
+      valid_page = tag != GP_TAG_RELEASE;  // released tokens take no part in the softmax
+    }
+    if (valid_page && tag != GP_TAG_BF16) {
+      if constexpr (BF16) {
+        // fp8 / INT4 keys: the codes are exact bf16 values; the row scale multiplies the
+        // finished dot products (rows 4 g4 + e of the tile)
+        const size_t row0 = ((size_t)pg * P.H_kv + h) * (size_t)b + tok0 % b;
+        f32x4_t sc;
+        if (tag == GP_TAG_FP8) {
+          const uint8_t* kr = P.k8 + (row0 + n16) * D + 8 * g4;
+#pragma unroll
+          for (int kk = 0; kk < D / 32; ++kk) {
+            const u32x2_t c = *reinterpret_cast<const u32x2_t*>(kr + 32 * kk);
+            const u32x2_t lo = gp::fp8x4_to_bf16x4(c.x), hi = gp::fp8x4_to_bf16x4(c.y);
+            const bf16x8_t kw = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+            sacc = gp::mfma_bf16_16x16x32(kw, __builtin_bit_cast(bf16x8_t, qhi[kk]), sacc);
+            sacc = gp::mfma_bf16_16x16x32(kw, __builtin_bit_cast(bf16x8_t, qlo[kk]), sacc);
+          }
+          sc = *reinterpret_cast<const f32x4_t*>(P.k_scale + row0 + 4 * g4);
+        } else {
+          const uint8_t* kr = P.k4 + (row0 + n16) * (D / 2) + 4 * g4;
+#pragma unroll
+          for (int kk = 0; kk < D / 32; ++kk) {
+            const uint32_t w4 = *reinterpret_cast<const uint32_t*>(kr + 16 * kk);
+            uint32_t e2[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int c0 = (int32_t)(w4 << (28 - 8 * e)) >> 28;  // nibble 2e
+              const int c1 = (int32_t)(w4 << (24 - 8 * e)) >> 28;  // nibble 2e + 1
+              e2[e] = (__float_as_uint((float)c0) >> 16) | (__float_as_uint((float)c1) & 0xffff0000u);
+            }
+            const bf16x8_t kw = __builtin_bit_cast(bf16x8_t, u32x4_t{e2[0], e2[1], e2[2], e2[3]});
+            sacc = gp::mfma_bf16_16x16x32(kw, __builtin_bit_cast(bf16x8_t, qhi[kk]), sacc);
+            sacc = gp::mfma_bf16_16x16x32(kw, __builtin_bit_cast(bf16x8_t, qlo[kk]), sacc);
+          }
+          const u32x2_t hs = *reinterpret_cast<const u32x2_t*>(P.k4_scale + row0 + 4 * g4);
+          sc = f32x4_t{gp::half_lo(hs.x), gp::half_hi(hs.x), gp::half_lo(hs.y), gp::half_hi(hs.y)};
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc[e] *= sc[e];
+      }
+    } else if (valid_page) {
       const size_t base = ((size_t)pg * P.H_kv + h) * (size_t)b * D + (size_t)(tok0 % b + n16) * D;
       if constexpr (BF16) {
         const uint16_t* kr = static_cast<const uint16_t*>(P.k) + base + 8 * g4;
@@ -601,8 +652,12 @@ extern "C" int gp_score_and_working_set(const void* q, int q_dtype, int B, int H
   if (!(p > 0.0 && p <= 1.0)) return GP_ERR_INVALID;
   const int H_kv = kv->num_kv_heads, D = kv->head_dim, b = kv->page_size;
   if (H_kv <= 0 || H_q % H_kv != 0 || kv->num_pages <= 0) return GP_ERR_INVALID;
-  if (kv->page_tag) return GP_ERR_UNSUPPORTED;
   if (q_dtype != kv->dtype || (q_dtype != GP_F32 && q_dtype != GP_BF16)) return GP_ERR_INVALID;
+  if (kv->page_tag) {
+    // mixed-precision pages: bf16 caches with the fp8 and INT4 key pools
+    if (kv->dtype != GP_BF16) return GP_ERR_UNSUPPORTED;
+    if (!kv->k8 || !kv->k_scale || !kv->k4 || !kv->k4_scale) return GP_ERR_INVALID;
+  }
   if (D != 64 && D != 128) return GP_ERR_UNSUPPORTED;
   if (b < 16 || b > 256 || b % 16) return GP_ERR_UNSUPPORTED;
   const int G = H_q / H_kv;
@@ -617,6 +672,11 @@ extern "C" int gp_score_and_working_set(const void* q, int q_dtype, int B, int H
   P.slot_ids = slot_ids;
   P.req_idx = req_idx;
   P.k = kv->k;
+  P.page_tag = kv->page_tag;
+  P.k8 = static_cast<const uint8_t*>(kv->k8);
+  P.k_scale = kv->k_scale;
+  P.k4 = static_cast<const uint8_t*>(kv->k4);
+  P.k4_scale = kv->k4_scale;
   P.block_tables = block_tables;
   P.context_lens = context_lens;
   P.positions = positions;

@@ -123,6 +123,13 @@ def test_invalid_arguments_rejected_on_host(lib):
         assert lib.gp_compact_or_grow(*cargs(0.0, 0, _kv(growpage, b=b), fake, 1 << 30)) == -2
     # GrowPage-Shrink evicts up to two pages: not with 32-token pages
     assert lib.gp_compact_or_grow(*cargs(0.0, 4, _kv(growpage, b=32), fake, 1 << 30)) == -2
+    # mixed-precision caches: bf16 with every pool, pages of 16 or 32 tokens
+    assert lib.gp_compact_or_grow(*cargs(0.0, 0, _mixed_kv(growpage, int4=False), fake,
+                                         1 << 30)) == -1
+    assert lib.gp_compact_or_grow(*cargs(0.0, 0, _mixed_kv(growpage, dtype=0), fake,
+                                         1 << 30)) == -2
+    assert lib.gp_compact_or_grow(*cargs(0.0, 0, _mixed_kv(growpage, b=64), fake,
+                                         1 << 30)) == -2
     assert lib.gp_compact_or_grow(*cargs(0.0, 0, kv, None, 0)) == -3
     # phased form: only PLAN (1), MOVE (2) or both (3)
     for bad in (0, 4, -1):

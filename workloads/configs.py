@@ -482,3 +482,58 @@ def make_decode_case(B: int, H_q: int, H_kv: int, d: int, page_size: int, lens, 
         info=dict(max_context=int(ctx.max()) if B else 0, total_tokens=int(ctx.sum()), seed=seed,
                   unique_tokens=int(ctx.sum())),
     )
+
+
+def attach_mixed_pools(wl: Workload, page_tag, seed: int = 0) -> Workload:
+    """Turn a bf16 workload into a mixed-precision cache with the given per-page tags: fp8 pages
+    get random E4M3 codes of magnitude below 8 and fp32 row scales in [0.01, 0.5), INT4
+    pages random code bytes (no nibble 8) and half row scales in [0.01, 0.5); the pools of the
+    formats a page does not use, and every pool of a released page, hold poison (NaN bf16,
+    NaN fp8 codes, NaN scales, nibble 8)."""
+    dev = wl.k_pool.device
+    P, H, b, d = wl.k_pool.shape
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(SEED_BASE + 97 * seed + 5)
+    tags = np.asarray(page_tag, dtype=np.uint8)
+
+    def rnd(shape):
+        return torch.randint(0, 256, shape, generator=gen, device=dev, dtype=torch.int32)
+
+    def codes8(shape):  # sign, exponent field 0..9 (|value| < 8), mantissa: activation-sized
+        x = rnd(shape)
+        return ((x & 0x87) | ((x >> 3) % 10 << 3)).to(torch.uint8)
+
+    k8, v8 = codes8((P, H, b, d)), codes8((P, H, d, b))
+
+    def scale(shape, dt):
+        u = torch.rand(shape, generator=gen, device=dev, dtype=torch.float32)
+        return (0.01 + 0.49 * u).to(dt)
+
+    k_scale, v_scale = scale((P, H, b), torch.float32), scale((P, H, b), torch.float32)
+
+    def codes4(shape):
+        x = rnd(shape)
+        lo, hi = x & 0xF, x >> 4
+        lo = torch.where(lo == 8, 0, lo)
+        hi = torch.where(hi == 8, 0, hi)
+        return (lo | (hi << 4)).to(torch.uint8)
+
+    k4, v4 = codes4((P, H, b, d // 2)), codes4((P, H, b // 4, d, 2))
+    k4_scale, v4_scale = scale((P, H, b), torch.float16), scale((P, H, b), torch.float16)
+
+    def poison(pages, *pools_vals):
+        if len(pages):
+            idx = torch.as_tensor(pages, dtype=torch.long, device=dev)
+            for pool, val in pools_vals:
+                pool.index_fill_(0, idx, val)
+
+    poison(np.nonzero(tags != TAG_BF16)[0], (wl.k_pool, float("nan")), (wl.v_pool, float("nan")))
+    poison(np.nonzero(tags != TAG_FP8)[0], (k8, 0x7F), (v8, 0x7F), (k_scale, float("nan")),
+           (v_scale, float("nan")))
+    poison(np.nonzero(tags != TAG_INT4)[0], (k4, 0x88), (v4, 0x88), (k4_scale, float("nan")),
+           (v4_scale, float("nan")))
+    wl.mixed = True
+    wl.page_tag = torch.as_tensor(tags, device=dev)
+    wl.k8, wl.v8, wl.k_scale, wl.v_scale = k8, v8, k_scale, v_scale
+    wl.k4, wl.v4, wl.k4_scale, wl.v4_scale = k4, v4, k4_scale, v4_scale
+    return wl
