@@ -348,7 +348,10 @@ def int4_leg(wl, gp, torch, np, steps):
                 frac=round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
 
 
-BOUNDARY_CASES = (("3b", 16), ("3b", 256), ("3a", 256), ("4", 16), ("1", 16))
+BOUNDARY_CASES = (("3b", 16), ("3b", 256), ("3a", 256), ("4", 16), ("1", 16), ("5", 16))
+MIXED_BOUNDARY = ("mixed-precision pages, 40/30/30 fp8/bf16/INT4 with none released (B=128, ctx "
+                  "U[8192,24576], Hq=32, Hkv=8, d=128, b=16), 16 seeded requests forced to compress")
+MIXED_NAMES = ("k8", "v8", "k_scale", "v_scale", "k4", "v4", "k4_scale", "v4_scale")
 
 
 def boundary_leg(name, b, gp, torch, np, reps, make_workload):
@@ -361,6 +364,15 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
     read and written."""
     dev = "cuda:0"
     wl = make_workload(name, "full", device=dev, page_size=b)
+    if wl.mixed:
+        # the mixed-precision batch with its pages re-tagged fp8 / bf16 / INT4 (a request
+        # holding a released page is not compacted) and 16 seeded requests, forced to compress
+        from workloads.configs import attach_mixed_pools
+        rng = np.random.Generator(np.random.PCG64(2024))
+        tags = rng.choice([1, 2, 3], size=wl.num_pages, p=[0.4, 0.3, 0.3]).astype(np.uint8)
+        attach_mixed_pools(wl, tags, seed=5)
+        wl.req_idx = torch.as_tensor(np.sort(rng.choice(wl.B, size=16, replace=False)),
+                                     dtype=torch.int32, device=dev)
     path = Path(wl, gp, torch)
     path.build_state()
     es = 4 if wl.dtype == "f32" else 2
@@ -370,7 +382,9 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
     bt = wl.block_tables.cpu().numpy()
     pages = np.unique(bt[req_all.cpu().numpy()][bt[req_all.cpu().numpy()] >= 0])
     pidx = torch.as_tensor(pages, dtype=torch.long, device=dev)
-    k0, v0 = wl.k_pool.index_select(0, pidx), wl.v_pool.index_select(0, pidx)
+    pools = ("k_pool", "v_pool") + (MIXED_NAMES if wl.mixed else ())
+    saved = {n: getattr(wl, n).index_select(0, pidx) for n in pools}
+    tag0 = wl.page_tag.clone() if wl.mixed else None
     out = {}
     for label, req in (("all", req_all), ("one", req_all[:1].clone())):
         R = req.numel()
@@ -380,8 +394,10 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
         for it in range(reps + 3):
             for n in names:
                 getattr(wl, n).copy_(ints[n])
-            wl.k_pool.index_copy_(0, pidx, k0)
-            wl.v_pool.index_copy_(0, pidx, v0)
+            for n in pools:
+                getattr(wl, n).index_copy_(0, pidx, saved[n])
+            if tag0 is not None:
+                wl.page_tag.copy_(tag0)
             ev[0].record()
             gp.gp_score_and_working_set(wl.q, wl.qstate, wl.slot_ids, req, path.cache,
                                         wl.block_tables, wl.context_lens, wl.positions,
@@ -406,15 +422,40 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
         ctx0 = ints["context_lens"].cpu().numpy()
         ctx1 = wl.context_lens.cpu().numpy()
         moved = 0
+        # bytes of one token row of K or V by page tag (mixed pages: codes plus row scale)
+        row_bytes = {1: wl.d + 4, 2: wl.d * 2, 3: wl.d // 2 + 2}
+        bt0 = ints["block_tables"].cpu().numpy()
+        bt1 = wl.block_tables.cpu().numpy()
+        t0 = tag0.cpu().numpy() if tag0 is not None else None
+        t1 = wl.page_tag.cpu().numpy() if tag0 is not None else None
         for i, r in enumerate(req.cpu().tolist()):
             if dec[i] not in (0, 2, 4) or ctx1[r] == ctx0[r]:
                 continue
+            firsts = []
             for h in range(wl.H_kv):
                 row = kept[i, h, :nc[i]]
                 diff = np.nonzero(row != np.arange(len(row)))[0]
-                first = int(diff[0]) if len(diff) else int(ctx1[r])
-                moved += (int(ctx1[r]) - first) * wl.d * es * 2 * 2
-        byts = int(sum(int(c) * wl.H_kv * wl.d * es + 4 * wl.H_kv * int(c) * 4 for c in nc)) + moved
+                firsts.append(int(diff[0]) if len(diff) else int(ctx1[r]))
+            if t0 is None:
+                moved += sum(int(ctx1[r]) - f for f in firsts) * wl.d * es * 2 * 2
+                continue
+            # mixed pages: every head rewrites from the first changed page (read in the
+            # source page's format, written in the destination page's)
+            j0 = min(firsts) // b * b
+            for j in range(j0, int(ctx1[r])):
+                rd = row_bytes[int(t0[bt0[r, j // b]])]
+                wr = row_bytes[int(t1[bt1[r, j // b]])]
+                moved += (rd + wr) * 2 * wl.H_kv
+        score_bytes = 0
+        for i, r in enumerate(req.cpu().tolist()):
+            c = int(nc[i])
+            if t0 is None:
+                score_bytes += c * wl.H_kv * wl.d * es
+            else:   # keys of C in their pages' formats (released pages are not read)
+                tg = t0[bt0[r, np.arange(c) // b]] if c else np.zeros(0, np.uint8)
+                score_bytes += int(sum(row_bytes.get(int(t), 0) for t in tg)) * wl.H_kv
+            score_bytes += 4 * wl.H_kv * c * 4          # both score planes written and read
+        byts = score_bytes + moved
         ms_s, ms_c = float(np.median(t_s)), float(np.median(t_c))
         ms = ms_s + ms_c
         out[label] = dict(requests=int(R), us_per_request=round(ms * 1e3 / R, 1),
@@ -422,9 +463,9 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
                           bytes=byts, gbps=round(byts / (ms * 1e-3) / 1e9, 1),
                           mean_candidates=round(float(nc.mean()), 1),
                           decisions=sorted(set(int(x) for x in dec)))
-    res = dict(workload=WORKLOAD_NAMES[name], page_size=b, k_loc=int(wl.k_loc), **out["all"],
-               single_request=out["one"])
-    del wl, path, k0, v0
+    res = dict(workload=MIXED_BOUNDARY if wl.mixed else WORKLOAD_NAMES[name], page_size=b,
+               k_loc=int(wl.k_loc), **out["all"], single_request=out["one"])
+    del wl, path, saved
     torch.cuda.empty_cache()
     return res
 
