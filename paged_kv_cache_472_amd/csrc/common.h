@@ -131,9 +131,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// exp2 that maps -inf to 0 without producing NaN for (-inf) - (-inf)
+// exp2 that maps -inf to 0 without producing NaN for (-inf) - (-inf). The hardware exp2
+// (v_exp_f32, about 1 ulp; results below 2^-126 flush to zero, which a softmax weight can
+// afford) instead of the library's denormal-preserving expansion.
 __device__ __forceinline__ float safe_exp2_diff(float a, float m) {
-  return (a == -INFINITY) ? 0.0f : exp2f(a - m);
+  return (a == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(a - m);
 }
 
 __device__ __forceinline__ f32x4_t mfma_bf16_16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {

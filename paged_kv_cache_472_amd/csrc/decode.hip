@@ -19,15 +19,18 @@
 // unrolling, so no register copy waits on an in-flight load; page ids are fetched 64 tiles at a
 // time, one per lane, a chunk ahead of use.
 //
-// Mixed-precision caches choose the page kind per tile (a uniform branch): released pages are
-// skipped, fp8 codes are widened exactly to bf16 and their row scales applied to the logits and
-// the probability weights, and INT4 pages (PASK App. B.5) are contracted in half precision:
+// Mixed-precision caches decode in two passes over the same ranges, each leaving partials that
+// the merge combines: the first takes the bf16 and fp8 tiles, the second (an INT4-only kernel
+// with 16 registers per tile) the INT4 tiles. Released pages are skipped, fp8 codes are widened
+// exactly to bf16 and their row scales applied to the logits and the probability weights, and
+// INT4 pages (PASK App. B.5) are contracted in half precision:
 // their nibbles become exact half values through the mantissa of 1024.0. An INT4 tile is five
 // loads per lane: the lane's quarter of a key row (the key product pairs it with a half copy of
 // the query holding the same dimensions, in the order the nibbles unpack in), the lane's
 // head_dim/16 value dimensions of its four tokens (adjacent in the stored value block), and
-// the 16-byte chunks of key and value scales around its tokens. The value product takes the
-// four tokens in the order (0, 2, 1, 3) on both operands.
+// the four key and value half scales of its tokens. The value product takes the four tokens in
+// the order (0, 2, 1, 3) on both operands. The online softmax rescales lazily: the running
+// maximum moves only when a logit exceeds it by more than 2^8, so most tiles skip the rescale.
 #include "common.h"
 
 #include <algorithm>
@@ -37,10 +40,13 @@ namespace {
 
 constexpr int KIND_F32 = 0;
 constexpr int KIND_BF16 = 1;
-constexpr int KIND_MIXED = 2;
+constexpr int KIND_MIXED = 2;  // a mixed cache's bf16 and fp8 tiles (and INT4 ones in one pass)
+constexpr int KIND_INT4 = 3;   // a mixed cache's INT4 tiles only (the second pass)
 constexpr int MAX_HEADS_PER_WG = 8;
 constexpr int MAX_THREADS = MAX_HEADS_PER_WG * GP_WAVE;
-constexpr int RING = 2;           // tiles in flight per wave
+// tiles in flight per wave: an INT4 tile is 16 registers, so its pass keeps six of them in flight
+template <int KIND>
+constexpr int ring_depth() { return KIND == KIND_INT4 ? 6 : 2; }
 constexpr int MAX_BATCH = 8191;   // prefix of tile counts kept in LDS (32 KB)
 constexpr int J_CAP_MAX = 127;    // partials one output row can have (the merge holds two per lane)
 
@@ -61,8 +67,8 @@ struct DecodeParams {
   const int32_t* context_lens;
   void* out;
   float* lse;
-  float* ws_o;       // [B, H_q, J_max, D] partial outputs
-  float* ws_ml;      // [B, H_q, J_max, 2] partial (max, sum)
+  float* ws_o;       // [B, H_q, passes * J_max, D] partial outputs
+  float* ws_ml;      // [B, H_q, passes * J_max, 2] partial (max, sum)
   int32_t* ws_pref;  // [B + 1] prefix of tile counts, written by workgroup 0
   // fused summary update (NULL q_pre: none)
   const void* q_pre;
@@ -73,6 +79,8 @@ struct DecodeParams {
   float beta_s, beta_l;
   int B, H_q, H_kv, G, page_size, num_pages, max_pages, max_context;
   int heads_per_wg;
+  int passes;  // 2 for a mixed cache: the bf16 / fp8 tiles, then the INT4 tiles
+  int pass;    // this launch's pass; its partials sit in slots pass * j_max + j
   int num_wg;  // workgroups per head group (the stream-K width)
   int r_min;   // minimum tiles per range
   int j_max;   // partial slots per output row
@@ -101,7 +109,14 @@ struct TileRaw<D, KIND_MIXED> {
   u32x2_t v[D / 16];  // bf16: 4 elements; fp8: 4 codes in .x; INT4: v[0..D/64) hold 2 bytes
                       // (4 tokens) for each of D/16 dimensions
   f32x4_t ks, vs;     // per-token scales of the 4 tokens this lane owns (fp8: fp32 values;
-                      // INT4: the 8 half scales of the aligned 8-token group around them)
+                      // INT4: their 4 half scales in .xy)
+};
+
+template <int D>
+struct TileRaw<D, KIND_INT4> {
+  u32x4_t k;             // the lane's D/4 key codes (D = 64: in .xy)
+  u32x2_t v[D / 64];     // 2 bytes (4 tokens) for each of D/16 value dimensions
+  f32x4_t ks, vs;        // the 4 half scales of the lane's tokens, in .xy
 };
 
 __device__ __forceinline__ int sanitize_ctx(const DecodeParams& p, int r) {
@@ -118,7 +133,21 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
   const int n16 = lane & 15, g4 = lane >> 4;
   const int b = p.page_size;
   const int off = tok0 % b;
-  if constexpr (KIND == KIND_MIXED) {
+  if constexpr (KIND == KIND_INT4) {
+    const int pg = code >> 2;
+    const size_t kv_base = ((size_t)pg * p.H_kv + h) * (size_t)b * D;
+    const uint8_t* kr = p.k4 + kv_base / 2 + (size_t)(off + n16) * (D / 2) + g4 * (D / 8);
+    if constexpr (D == 128)
+      t.k = *reinterpret_cast<const u32x4_t*>(kr);
+    else
+      *reinterpret_cast<u32x2_t*>(&t.k) = *reinterpret_cast<const u32x2_t*>(kr);
+    const uint8_t* vr = p.v4 + kv_base / 2 + (size_t)((off >> 2) + g4) * (2 * D) + n16 * (D / 8);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) t.v[i] = *reinterpret_cast<const u32x2_t*>(vr + 8 * i);
+    const size_t sc = ((size_t)pg * p.H_kv + h) * b + off + 4 * g4;
+    *reinterpret_cast<u32x2_t*>(&t.ks) = *reinterpret_cast<const u32x2_t*>(p.k4_scale + sc);
+    *reinterpret_cast<u32x2_t*>(&t.vs) = *reinterpret_cast<const u32x2_t*>(p.v4_scale + sc);
+  } else if constexpr (KIND == KIND_MIXED) {
     const int pg = code >> 2, tag = code & 3;
     const size_t kv_base = ((size_t)pg * p.H_kv + h) * (size_t)b * D;
     const size_t sb = ((size_t)pg * p.H_kv + h) * b + off + 4 * g4;
@@ -133,10 +162,9 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
       const uint8_t* vr = p.v4 + kv_base / 2 + (size_t)((off >> 2) + g4) * (2 * D) + n16 * (D / 8);
 #pragma unroll
       for (int i = 0; i < D / 64; ++i) t.v[i] = *reinterpret_cast<const u32x2_t*>(vr + 8 * i);
-      // the 16-byte aligned group of 8 scales holding this lane's 4 tokens
-      const size_t sc = ((size_t)pg * p.H_kv + h) * b + ((off + 4 * g4) & ~7);
-      t.ks = *reinterpret_cast<const f32x4_t*>(p.k4_scale + sc);
-      t.vs = *reinterpret_cast<const f32x4_t*>(p.v4_scale + sc);
+      // the 4 half scales of this lane's tokens (8 bytes, in .xy)
+      *reinterpret_cast<u32x2_t*>(&t.ks) = *reinterpret_cast<const u32x2_t*>(p.k4_scale + sb);
+      *reinterpret_cast<u32x2_t*>(&t.vs) = *reinterpret_cast<const u32x2_t*>(p.v4_scale + sb);
       return;
     }
     if (tag == GP_TAG_FP8) {
@@ -200,17 +228,16 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
   const bool tail = tok0 + 16 > ctx;
   // ---- logits: S[token 4*g4 + i][head n16]
   f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-  bool fp8 = false, int4 = false;
+  bool fp8 = false, int4 = KIND == KIND_INT4;
   float ks[4], vs[4];
-  if constexpr (KIND == KIND_MIXED) {
-    fp8 = (code & 3) == GP_TAG_FP8;
-    int4 = (code & 3) == GP_TAG_INT4;
+  if constexpr (KIND == KIND_MIXED || KIND == KIND_INT4) {
+    if constexpr (KIND == KIND_MIXED) {
+      fp8 = (code & 3) == GP_TAG_FP8;
+      int4 = (code & 3) == GP_TAG_INT4;
+    }
     if (int4) {
-      const bool up = g4 & 1;  // this lane's tokens are the upper half of the 8-scale group
-      const uint32_t k01 = __float_as_uint(up ? cur.ks[2] : cur.ks[0]);
-      const uint32_t k23 = __float_as_uint(up ? cur.ks[3] : cur.ks[1]);
-      const uint32_t v01 = __float_as_uint(up ? cur.vs[2] : cur.vs[0]);
-      const uint32_t v23 = __float_as_uint(up ? cur.vs[3] : cur.vs[1]);
+      const uint32_t k01 = __float_as_uint(cur.ks[0]), k23 = __float_as_uint(cur.ks[1]);
+      const uint32_t v01 = __float_as_uint(cur.vs[0]), v23 = __float_as_uint(cur.vs[1]);
       ks[0] = gp::half_lo(k01); ks[1] = gp::half_hi(k01); ks[2] = gp::half_lo(k23); ks[3] = gp::half_hi(k23);
       vs[0] = gp::half_lo(v01); vs[1] = gp::half_hi(v01); vs[2] = gp::half_lo(v23); vs[3] = gp::half_hi(v23);
     } else {
@@ -218,7 +245,11 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
       for (int i = 0; i < 4; ++i) { ks[i] = cur.ks[i]; vs[i] = cur.vs[i]; }
     }
   }
-  if constexpr (KIND == KIND_F32) {
+  if constexpr (KIND == KIND_INT4) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+      sacc = gp::mfma_f16_16x16x32(gp::int4x8_to_f16x8(cur.k[kk]), qh[kk], sacc);
+  } else if constexpr (KIND == KIND_F32) {
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) {
 #pragma unroll
@@ -248,15 +279,18 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float z = sacc[i];
-    if constexpr (KIND == KIND_MIXED) z *= ks[i];
+    if constexpr (KIND == KIND_MIXED || KIND == KIND_INT4) z *= ks[i];
     const bool ok = tok0 + 4 * g4 + i < ctx;
     sv[i] = ok ? z * p.scale_log2 : -INFINITY;
     mx = fmaxf(mx, sv[i]);
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16, GP_WAVE));
   mx = fmaxf(mx, __shfl_xor(mx, 32, GP_WAVE));
-  const float m_new = fmaxf(st.m_run, mx);
-  const float alpha = gp::safe_exp2_diff(st.m_run, m_new);
+  // lazy rescaling: the running maximum moves only when a logit exceeds it by more than 2^8
+  // (log2 domain 8), so the weights stay below 256 and most tiles skip the rescale of the rows
+  const bool move = mx > st.m_run + 8.0f;
+  const float m_new = move ? mx : st.m_run;
+  const float alpha = move ? gp::safe_exp2_diff(st.m_run, m_new) : 1.0f;
   float pv[4];
   float psum = 0.f;
 #pragma unroll
@@ -266,14 +300,16 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
   }
   st.l_run = st.l_run * alpha + psum;
   st.m_run = m_new;
-  // rescale the output rows: this lane holds heads 4*g4 + i
-  float al[4];
+  if (__builtin_amdgcn_ballot_w64(move) != 0) {
+    // rescale the output rows: this lane holds heads 4*g4 + i
+    float al[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g4 + i, GP_WAVE);
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g4 + i, GP_WAVE);
 #pragma unroll
-  for (int nb = 0; nb < D / 16; ++nb)
+    for (int nb = 0; nb < D / 16; ++nb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.acc[nb][i] *= al[i];
+      for (int i = 0; i < 4; ++i) st.acc[nb][i] *= al[i];
+  }
   if constexpr (KIND == KIND_F32) {
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) {
@@ -291,9 +327,9 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       pw[i] = pv[i];
-      if constexpr (KIND == KIND_MIXED) pw[i] *= vs[i];
+      if constexpr (KIND == KIND_MIXED || KIND == KIND_INT4) pw[i] *= vs[i];
     }
-    if constexpr (KIND == KIND_MIXED) {
+    if constexpr (KIND == KIND_MIXED || KIND == KIND_INT4) {
       // scales of masked tokens may be poison; keep them out of the product
 #pragma unroll
       for (int i = 0; i < 4; ++i) if (pv[i] == 0.f) pw[i] = 0.f;
@@ -311,24 +347,26 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
         return;
       }
     }
-    const u32x2_t pp = u32x2_t{gp::pack_bf16x2(pw[0], pw[1]), gp::pack_bf16x2(pw[2], pw[3])};
-    // values of tokens past the context (the tail of the last page) are masked to zero bits
-    uint32_t mlo = 0xffffffffu, mhi = 0xffffffffu;
-    if (tail) {
-      const int base = tok0 + 4 * g4;
-      mlo = (base + 0 < ctx ? 0x0000ffffu : 0u) | (base + 1 < ctx ? 0xffff0000u : 0u);
-      mhi = (base + 2 < ctx ? 0x0000ffffu : 0u) | (base + 3 < ctx ? 0xffff0000u : 0u);
-    }
-#pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) {
-      u32x2_t vw = cur.v[nb];
-      if constexpr (KIND == KIND_MIXED) {
-        if (fp8) vw = gp::fp8x4_to_bf16x4(vw.x);
+    if constexpr (KIND != KIND_INT4) {
+      const u32x2_t pp = u32x2_t{gp::pack_bf16x2(pw[0], pw[1]), gp::pack_bf16x2(pw[2], pw[3])};
+      // values of tokens past the context (the tail of the last page) are masked to zero bits
+      uint32_t mlo = 0xffffffffu, mhi = 0xffffffffu;
+      if (tail) {
+        const int base = tok0 + 4 * g4;
+        mlo = (base + 0 < ctx ? 0x0000ffffu : 0u) | (base + 1 < ctx ? 0xffff0000u : 0u);
+        mhi = (base + 2 < ctx ? 0x0000ffffu : 0u) | (base + 3 < ctx ? 0xffff0000u : 0u);
       }
-      vw.x &= mlo;
-      vw.y &= mhi;
-      st.acc[nb] = gp::mfma_bf16_16x16x16(__builtin_bit_cast(i16x4_t, pp),
-                                          __builtin_bit_cast(i16x4_t, vw), st.acc[nb]);
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) {
+        u32x2_t vw = cur.v[nb];
+        if constexpr (KIND == KIND_MIXED) {
+          if (fp8) vw = gp::fp8x4_to_bf16x4(vw.x);
+        }
+        vw.x &= mlo;
+        vw.y &= mhi;
+        st.acc[nb] = gp::mfma_bf16_16x16x16(__builtin_bit_cast(i16x4_t, pp),
+                                            __builtin_bit_cast(i16x4_t, vw), st.acc[nb]);
+      }
     }
   }
 }
@@ -425,11 +463,14 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
         const int pg = bt[(t << 4) / b];
         code = (pg >= 0 && pg < p.num_pages) ? pg : -1;
         if constexpr (KIND == KIND_MIXED) {
+          // with two passes the INT4 tiles belong to the second one
           if (code >= 0) {
             const int tag = p.page_tag[pg];
-            code = (tag == GP_TAG_FP8 || tag == GP_TAG_BF16 || tag == GP_TAG_INT4)
+            code = (tag == GP_TAG_FP8 || tag == GP_TAG_BF16 || (tag == GP_TAG_INT4 && p.passes == 1))
                        ? ((pg << 2) | tag) : -1;
           }
+        } else if constexpr (KIND == KIND_INT4) {
+          if (code >= 0) code = p.page_tag[pg] == GP_TAG_INT4 ? ((pg << 2) | GP_TAG_INT4) : -1;
         }
       }
       return code;
@@ -464,8 +505,8 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
     }
     // half copy of the query for INT4 pages: step kk of lane (n16, g4) holds dimensions
     // g4 D/4 + 8 kk + (0, 4, 1, 5, 2, 6, 3, 7), the order the lane's key codes unpack in
-    f16x8_t qh[KIND == KIND_MIXED ? D / 32 : 1];
-    if constexpr (KIND == KIND_MIXED) {
+    f16x8_t qh[KIND == KIND_MIXED || KIND == KIND_INT4 ? D / 32 : 1];
+    if constexpr (KIND == KIND_MIXED || KIND == KIND_INT4) {
       const uint16_t* qr = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)r * p.H_q + hq0 + n16) * D + (D / 4) * g4;
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
@@ -485,6 +526,7 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
     st.m_run = -INFINITY;
     st.l_run = 0.f;
 
+    constexpr int RING = ring_depth<KIND>();
     TileRaw<D, KIND> ring[RING];
     int codes[RING];
 #pragma unroll
@@ -512,8 +554,9 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
     float l_i[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) l_i[i] = __shfl(l_tot, 4 * g4 + i, GP_WAVE);
-    const bool whole = ta == 0 && tb == ntiles;
-    const int j = wg - s_pref[r] / R;
+    // with two passes every segment leaves a partial, and the merge combines both passes
+    const bool whole = ta == 0 && tb == ntiles && p.passes == 1;
+    const int j = wg - s_pref[r] / R + p.pass * p.j_max;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int head = 4 * g4 + i;
@@ -530,7 +573,7 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
             reinterpret_cast<uint16_t*>(p.out)[row * D + 16 * nb + n16] = (uint16_t)gp::f32_to_bf16_bits(o);
         }
       } else {
-        float* wo = p.ws_o + (row * p.j_max + j) * D;
+        float* wo = p.ws_o + (row * p.passes * p.j_max + j) * D;
 #pragma unroll
         for (int nb = 0; nb < D / 16; ++nb) wo[16 * nb + n16] = st.acc[nb][i];
       }
@@ -540,18 +583,18 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
       if (whole) {
         if (p.lse) p.lse[row] = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * GP_LN2 : -INFINITY;
       } else {
-        p.ws_ml[(row * p.j_max + j) * 2 + 0] = st.m_run;
-        p.ws_ml[(row * p.j_max + j) * 2 + 1] = l_tot;
+        p.ws_ml[(row * p.passes * p.j_max + j) * 2 + 0] = st.m_run;
+        p.ws_ml[(row * p.passes * p.j_max + j) * 2 + 1] = l_tot;
       }
     }
   }
 }
 
 // Merge of a request's partials (PASK App. B.5): o = sum_j e^{m_j - m} u_j / sum_j e^{m_j - m} l_j.
-// One wave per output row; lane j holds partial j's (m_j, l_j), so the maximum, the denominator
-// and the weights come from wave reductions and the partial outputs are fetched in one pass.
-// Rows of requests that one workgroup finished are left as written; rows of empty requests get
-// o = 0 and lse = -inf.
+// One wave per output row; lane l holds partials l, l + 64, ... (J per pass, in slots
+// pass * j_max + j), so the maximum, the denominator and the weights come from wave reductions
+// and the partial outputs are fetched in one pass. With one pass, rows of requests that one
+// workgroup finished are left as written; rows of empty requests get o = 0 and lse = -inf.
 template <int D, int KIND>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
@@ -565,36 +608,54 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
     const int R = range_len(p, U);
     J = (pb - 1) / R - pa / R + 1;
   }
-  if (J == 1) return;
-  // J <= j_max <= J_CAP_MAX + 1 = 128: lane l holds partials l and l + 64
-  const float* ml = p.ws_ml + row * p.j_max * 2;
-  const float m0 = lane < J ? ml[2 * lane] : -INFINITY;
-  const float l0 = lane < J ? ml[2 * lane + 1] : 0.f;
-  const float m1 = lane + 64 < J ? ml[2 * (lane + 64)] : -INFINITY;
-  const float l1 = lane + 64 < J ? ml[2 * (lane + 64) + 1] : 0.f;
-  const float m = gp::wave_max(fmaxf(m0, m1));
-  const float w0 = gp::safe_exp2_diff(m0, m), w1 = gp::safe_exp2_diff(m1, m);
-  const float den = gp::wave_sum(w0 * l0 + w1 * l1);
+  if (J == 1 && p.passes == 1) return;
+  // J <= j_max <= J_CAP_MAX + 1 = 128 per pass: at most 4 partials per lane
+  const int NP = J * p.passes;
+  const int SL = p.passes * p.j_max;  // slots per row
+  auto slot = [&](int k) { return (k / J) * p.j_max + k % J; };  // k < NP
+  const float* ml = p.ws_ml + row * SL * 2;
+  float mk[4], lk[4];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int k = lane + 64 * q;
+    mk[q] = k < NP ? ml[2 * slot(k)] : -INFINITY;
+    lk[q] = k < NP ? ml[2 * slot(k) + 1] : 0.f;
+    mloc = fmaxf(mloc, mk[q]);
+  }
+  const float m = gp::wave_max(mloc);
+  float wk[4], dsum = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    wk[q] = gp::safe_exp2_diff(mk[q], m);
+    dsum += wk[q] * lk[q];
+  }
+  const float den = gp::wave_sum(dsum);
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  const float* wo = p.ws_o + row * p.j_max * D;
+  const float* wo = p.ws_o + row * SL * D;
   constexpr int PER = D / 64;
   constexpr int BATCH = 8;  // partial rows fetched before any is used
   float num[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) num[e] = 0.f;
-  for (int j0 = 0; j0 < J; j0 += BATCH) {
+  for (int k0 = 0; k0 < NP; k0 += BATCH) {
     float x[BATCH][PER];
 #pragma unroll
     for (int u = 0; u < BATCH; ++u)
 #pragma unroll
       for (int e = 0; e < PER; ++e)
-        x[u][e] = j0 + u < J ? wo[(size_t)(j0 + u) * D + lane + 64 * e] : 0.f;
+        x[u][e] = k0 + u < NP ? wo[(size_t)slot(k0 + u) * D + lane + 64 * e] : 0.f;
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
-      const int j = j0 + u;
-      const float wt = j < J ? __shfl(j < 64 ? w0 : w1, j & 63, GP_WAVE) : 0.f;
+      const int k = k0 + u;
+      float wt = 0.f;
+      if (k < NP) {
+        const int q = k >> 6;
+        const float wq = q == 0 ? wk[0] : q == 1 ? wk[1] : q == 2 ? wk[2] : wk[3];
+        wt = __shfl(wq, k & 63, GP_WAVE);
+      }
 #pragma unroll
-      for (int e = 0; e < PER; ++e) num[e] += wt * x[u][e];
+      for (int e = 0; e < PER; ++e) num[e] += wt > 0.f ? wt * x[u][e] : 0.f;
     }
   }
 #pragma unroll
@@ -657,11 +718,24 @@ int launch_decode(DecodeParams p, int max_workgroups, hipStream_t stream) {
   const int threads = p.heads_per_wg * GP_WAVE;
   const size_t lds = (size_t)(p.B + 1) * sizeof(int);
   int total = resident_workgroups<D, KIND>(threads, lds);
+  // a mixed cache decodes in two passes over the same ranges (the bf16 / fp8 tiles, then the
+  // INT4 tiles with a deeper ring); both must cut the batch identically
+  p.passes = KIND == KIND_MIXED ? 2 : 1;
+  if (p.passes == 2) total = std::min(total, resident_workgroups<D, KIND_INT4>(threads, lds));
   if (max_workgroups > 0) total = std::min(total, max_workgroups);
   p.num_wg = std::max(1, total / hg);
+  p.pass = 0;
   hipLaunchKernelGGL((decode_streamk_kernel<D, KIND>), dim3(p.num_wg, hg), dim3(threads), lds,
                      stream, p);
   GP_CHECK_LAUNCH();
+  if (p.passes == 2) {
+    DecodeParams p1 = p;
+    p1.pass = 1;
+    p1.q_pre = nullptr;  // the summary update ran in the first pass
+    hipLaunchKernelGGL((decode_streamk_kernel<D, KIND_INT4>), dim3(p.num_wg, hg), dim3(threads),
+                       lds, stream, p1);
+    GP_CHECK_LAUNCH();
+  }
   const long rows = (long)p.B * p.H_q;
   hipLaunchKernelGGL((decode_merge_kernel<D, KIND>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
                      stream, p);
@@ -677,7 +751,8 @@ extern "C" size_t gp_paged_decode_attn_workspace_size(int B, int H_q, int H_kv, 
   (void)H_kv;
   if (B <= 0 || H_q <= 0 || head_dim <= 0 || max_context < 0) return 0;
   const Plan pl = plan_for(B, max_context);
-  const size_t partials = (size_t)B * H_q * pl.j_max * (head_dim + 2) * sizeof(float);
+  // two passes' partials (a mixed cache decodes its INT4 tiles in a pass of their own)
+  const size_t partials = (size_t)B * H_q * 2 * pl.j_max * (head_dim + 2) * sizeof(float);
   const size_t pref = ((size_t)(B + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
   return pref + partials;
 }
@@ -748,7 +823,7 @@ int decode_impl(const void* q, int q_dtype, int B, int H_q, const gp_kv_cache* k
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   p.ws_pref = reinterpret_cast<int32_t*>(ws);
   p.ws_o = reinterpret_cast<float*>(ws + (((size_t)(B + 1) * sizeof(int32_t) + 255) & ~(size_t)255));
-  p.ws_ml = p.ws_o + (size_t)B * H_q * pl.j_max * D;
+  p.ws_ml = p.ws_o + (size_t)B * H_q * 2 * pl.j_max * D;
   if (upd) {
     p.q_pre = upd->q_pre;
     p.slot_ids = upd->slot_ids;
