@@ -19,17 +19,17 @@
 // unrolling, so no register copy waits on an in-flight load; page ids are fetched 64 tiles at a
 // time, one per lane, a chunk ahead of use.
 //
-// Mixed-precision caches decode in two passes over the same ranges, each leaving partials that
-// the merge combines: the first takes the bf16 and fp8 tiles, the second (an INT4-only kernel
-// with 16 registers per tile) the INT4 tiles. Released pages are skipped, fp8 codes are widened
-// exactly to bf16 and their row scales applied to the logits and the probability weights, and
-// INT4 pages (PASK App. B.5) are contracted in half precision:
-// their nibbles become exact half values through the mantissa of 1024.0. An INT4 tile is five
-// loads per lane: the lane's quarter of a key row (the key product pairs it with a half copy of
-// the query holding the same dimensions, in the order the nibbles unpack in), the lane's
-// head_dim/16 value dimensions of its four tokens (adjacent in the stored value block), and
-// the four key and value half scales of its tokens. The value product takes the four tokens in
-// the order (0, 2, 1, 3) on both operands. The online softmax rescales lazily: the running
+// Mixed-precision caches decode in two passes over the same batch, each leaving partials that
+// the merge combines: the first takes the bf16 and fp8 tiles, the second the INT4 tiles with an
+// INT4-only kernel (16 registers per tile, four waves per SIMD, its own stream-K width). Released
+// pages are skipped, fp8 codes are widened exactly to bf16 and their row scales applied to the
+// logits and the probability weights, and INT4 pages (PASK App. B.5) are contracted in half
+// precision: their nibbles become exact half values through the mantissa of 1024.0. An INT4
+// tile is five loads per lane: the lane's quarter of a key row (the key product pairs it with a
+// half copy of the query holding the same dimensions, in the order the nibbles unpack in), the
+// lane's head_dim/16 value dimensions of its four tokens (adjacent in the stored value block),
+// and the four key and value half scales of its tokens. The value product takes the four tokens
+// in the order (0, 2, 1, 3) on both operands. The online softmax rescales lazily: the running
 // maximum moves only when a logit exceeds it by more than 2^8, so most tiles skip the rescale.
 #include "common.h"
 
@@ -44,9 +44,10 @@ constexpr int KIND_MIXED = 2;  // a mixed cache's bf16 and fp8 tiles (and INT4 o
 constexpr int KIND_INT4 = 3;   // a mixed cache's INT4 tiles only (the second pass)
 constexpr int MAX_HEADS_PER_WG = 8;
 constexpr int MAX_THREADS = MAX_HEADS_PER_WG * GP_WAVE;
-// tiles in flight per wave: an INT4 tile is 16 registers, so its pass keeps six of them in flight
-template <int KIND>
-constexpr int ring_depth() { return KIND == KIND_INT4 ? 6 : 2; }
+constexpr int RING = 2;  // tiles in flight per wave
+// The INT4 pass is bound by instruction latency, not bytes: its kernel (126 registers) runs four
+// waves per SIMD, in workgroups of four heads so that four of them fit a compute unit.
+constexpr int INT4_HEADS_PER_WG = 4;
 constexpr int MAX_BATCH = 8191;   // prefix of tile counts kept in LDS (32 KB)
 constexpr int J_CAP_MAX = 127;    // partials one output row can have (the merge holds two per lane)
 
@@ -81,7 +82,8 @@ struct DecodeParams {
   int heads_per_wg;
   int passes;  // 2 for a mixed cache: the bf16 / fp8 tiles, then the INT4 tiles
   int pass;    // this launch's pass; its partials sit in slots pass * j_max + j
-  int num_wg;  // workgroups per head group (the stream-K width)
+  int num_wg;  // workgroups per head group (the stream-K width) of this launch
+  int num_wg_pass[2];  // the stream-K width of each pass (the merge needs both)
   int r_min;   // minimum tiles per range
   int j_max;   // partial slots per output row
   float scale_log2;
@@ -373,8 +375,11 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
 
 
 // Tiles per workgroup range: equal shares of the batch's U units, at least r_min.
+__device__ __forceinline__ int range_len(int num_wg, int r_min, int U) {
+  return max((U + num_wg - 1) / num_wg, r_min);
+}
 __device__ __forceinline__ int range_len(const DecodeParams& p, int U) {
-  return max((U + p.num_wg - 1) / p.num_wg, p.r_min);
+  return range_len(p.num_wg, p.r_min, U);
 }
 
 template <int D, int KIND>
@@ -382,7 +387,9 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
   extern __shared__ int s_pref[];  // [B + 1]
   __shared__ int s_wsum[MAX_HEADS_PER_WG];
   const int wg = blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // the wave index is uniform over the wave: say so, so that page addresses stay scalar
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
   const int h = blockIdx.y * p.heads_per_wg + w;
   const int n16 = lane & 15, g4 = lane >> 4;
@@ -526,7 +533,6 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
     st.m_run = -INFINITY;
     st.l_run = 0.f;
 
-    constexpr int RING = ring_depth<KIND>();
     TileRaw<D, KIND> ring[RING];
     int codes[RING];
 #pragma unroll
@@ -603,16 +609,19 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int r = (int)(row / p.H_q);
   const int U = p.ws_pref[p.B];
   const int pa = p.ws_pref[r], pb = p.ws_pref[r + 1];
-  int J = 0;
+  // partials of each pass: the ranges of its stream-K width that overlap the request
+  int Jp[2] = {0, 0};
   if (pb > pa) {
-    const int R = range_len(p, U);
-    J = (pb - 1) / R - pa / R + 1;
+    for (int q = 0; q < p.passes; ++q) {
+      const int R = range_len(p.num_wg_pass[q], p.r_min, U);
+      Jp[q] = (pb - 1) / R - pa / R + 1;
+    }
   }
-  if (J == 1 && p.passes == 1) return;
+  if (Jp[0] == 1 && p.passes == 1) return;
   // J <= j_max <= J_CAP_MAX + 1 = 128 per pass: at most 4 partials per lane
-  const int NP = J * p.passes;
+  const int J0 = Jp[0], NP = Jp[0] + Jp[1];
   const int SL = p.passes * p.j_max;  // slots per row
-  auto slot = [&](int k) { return (k / J) * p.j_max + k % J; };  // k < NP
+  auto slot = [&](int k) { return k < J0 ? k : p.j_max + (k - J0); };  // k < NP
   const float* ml = p.ws_ml + row * SL * 2;
   float mk[4], lk[4];
   float mloc = -INFINITY;
@@ -721,10 +730,19 @@ int launch_decode(DecodeParams p, int max_workgroups, hipStream_t stream) {
   // a mixed cache decodes in two passes over the same ranges (the bf16 / fp8 tiles, then the
   // INT4 tiles with a deeper ring); both must cut the batch identically
   p.passes = KIND == KIND_MIXED ? 2 : 1;
-  if (p.passes == 2) total = std::min(total, resident_workgroups<D, KIND_INT4>(threads, lds));
   if (max_workgroups > 0) total = std::min(total, max_workgroups);
   p.num_wg = std::max(1, total / hg);
   p.pass = 0;
+  // the INT4 pass has its own geometry: smaller workgroups, so that more waves hide latency
+  const int hpw1 = std::min(p.H_kv, INT4_HEADS_PER_WG);
+  const int hg1 = (p.H_kv + hpw1 - 1) / hpw1;
+  int total1 = 0;
+  if (p.passes == 2) {
+    total1 = resident_workgroups<D, KIND_INT4>(hpw1 * GP_WAVE, lds);
+    if (max_workgroups > 0) total1 = std::min(total1, max_workgroups * (p.heads_per_wg / hpw1));
+  }
+  p.num_wg_pass[0] = p.num_wg;
+  p.num_wg_pass[1] = std::max(1, total1 / hg1);
   hipLaunchKernelGGL((decode_streamk_kernel<D, KIND>), dim3(p.num_wg, hg), dim3(threads), lds,
                      stream, p);
   GP_CHECK_LAUNCH();
@@ -732,8 +750,10 @@ int launch_decode(DecodeParams p, int max_workgroups, hipStream_t stream) {
     DecodeParams p1 = p;
     p1.pass = 1;
     p1.q_pre = nullptr;  // the summary update ran in the first pass
-    hipLaunchKernelGGL((decode_streamk_kernel<D, KIND_INT4>), dim3(p.num_wg, hg), dim3(threads),
-                       lds, stream, p1);
+    p1.heads_per_wg = hpw1;
+    p1.num_wg = p.num_wg_pass[1];
+    hipLaunchKernelGGL((decode_streamk_kernel<D, KIND_INT4>), dim3(p1.num_wg, hg1),
+                       dim3(hpw1 * GP_WAVE), lds, stream, p1);
     GP_CHECK_LAUNCH();
   }
   const long rows = (long)p.B * p.H_q;
