@@ -38,7 +38,8 @@ constexpr int SEL_MAX_CHUNKS = MAX_CAND / (SEL_T * 16);
 constexpr int MAX_EVICT = 32;
 constexpr int MAX_SPAN = 2;               // pages a compaction shifts by at most (Shrink: 2)
 constexpr int SHRINK_MIN_CAPACITY = 1024; // tokens a Shrink must leave (GrowPage App. H.1)
-constexpr int CHUNK_PAGES = 16;           // destination pages per compaction workgroup
+constexpr int CHUNK_PAGES = 16;           // destination pages per compaction item (pages <= 32 tokens)
+constexpr int WIDE_CHUNK_PAGES = 8;       // the same for larger pages: more, shorter items
 constexpr int MAX_WINDOW_SLOTS = 8 * 32;  // LDS window pages (<= 8) x page size (<= 32)
 constexpr int CP_THREADS = 256;
 constexpr int CP_LDS_BYTES = 40 * 1024;  // source value pages of one window
@@ -651,8 +652,9 @@ __global__ __launch_bounds__(WIDE_T) void select_wide_kernel(CParams P) {
   }
   const int kloc = min(P.k_loc, b);
   const long n_loc = (long)(n / b) * kloc;
-  if (n_loc < K_t && kloc > 0) {
-    // the page's kloc-th largest key: the largest x with #{keys >= x} >= kloc
+  if (n_loc < K_t && kloc > 0 && live) {
+    // the page's kloc-th largest key: the largest x with #{keys >= x} >= kloc (the lanes of a
+    // page are live together, and waves past |C| skip the search)
     unsigned long long x = 0;
     for (int bit = KEY_BITS - 1; bit >= 0; --bit) {
       const unsigned long long c = x | (1ull << bit);
@@ -681,8 +683,10 @@ __global__ __launch_bounds__(WIDE_T) void select_wide_kernel(CParams P) {
   for (int bit = KEY_BITS - 1, it = 0; bit >= 0; --bit, ++it) {
     const unsigned long long c = x | (1ull << bit);
     int cnt = 0;
+    if (live) {  // waves past |C| only take part in the reduction
 #pragma unroll
-    for (int j = 0; j < WIDE_VPT; ++j) cnt += key[j] < c ? 1 : 0;
+      for (int j = 0; j < WIDE_VPT; ++j) cnt += key[j] < c ? 1 : 0;
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, GP_WAVE);
     if (lane == 0) s_part[it & 1][wv] = cnt;
@@ -1416,7 +1420,8 @@ WsLayout ws_layout(int L, int R, int H_kv, int max_pages, int page_size) {
   const bool wide = page_size >= WIDE_MIN_PAGE;
   const size_t max_evict = wide ? 2 * (size_t)page_size : MAX_EVICT;
   const size_t parts = wide ? WIDE_MAX_PARTS : 1;
-  const size_t max_chunks = (size_t)(max_pages + CHUNK_PAGES - 1) / CHUNK_PAGES;
+  const size_t cp = wide ? WIDE_CHUNK_PAGES : CHUNK_PAGES;
+  const size_t max_chunks = (size_t)(max_pages + cp - 1) / cp;
   WsLayout w{};
   size_t off = 0;
   w.info = off;
@@ -1536,8 +1541,8 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
   P.policy = policy;
   P.es = es;
   P.tau = tau;
-  P.chunk_pages = CHUNK_PAGES;
-  P.max_chunks = (max_pages + CHUNK_PAGES - 1) / CHUNK_PAGES;
+  P.chunk_pages = wide ? WIDE_CHUNK_PAGES : CHUNK_PAGES;
+  P.max_chunks = (max_pages + P.chunk_pages - 1) / P.chunk_pages;
   P.window_pages = W;
   P.max_evict = wide ? 2 * b : MAX_EVICT;
   P.npart = wide ? D * es / WIDE_PART : 1;
