@@ -285,7 +285,9 @@ size_t gp_compact_or_grow_workspace_size(int R, int H_kv, int max_pages, int pag
  * bookkeeping (GrowPage App. E.3 overlaps compaction with decoding):
  *   GP_PHASE_PLAN  decisions, page allocation and release, kept_idx, and the list of page chunks
  *                  to move: every update of block_tables, n_pages, context_lens, refcount,
- *                  free_stack, free_top and decision. K/V pages are not touched.
+ *                  free_stack, free_top and decision. K/V pages are not written (with one
+ *                  layer the plan also copies the few pages the move will need into the
+ *                  workspace: reads only).
  *   GP_PHASE_MOVE  the K/V movement planned by the PLAN call that used this workspace; it must
  *                  come after that call (same arguments and workspace, none of them changed in
  *                  between) and after every read of the boundary requests' old pages.

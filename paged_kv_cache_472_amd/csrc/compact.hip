@@ -50,6 +50,7 @@ constexpr int WIDE_MAX_EVICT = 512;       // 2 pages of 256 tokens (Shrink)
 constexpr int WIDE_T = 1024;              // threads of a wide selection workgroup
 constexpr int WIDE_VPT = 32;              // candidates per thread (|C| <= 32768)
 constexpr int WIDE_PART = 64;             // bytes of each key row one wide compaction item owns
+constexpr int NUM_XCD = 8;                // accelerator dies of the chip, each with its own L2
 constexpr int WIDE_MAX_PARTS = 128 * 4 / WIDE_PART;
 constexpr int KEY_BITS = 46;              // 31 score bits above a 15-bit complemented index
 
@@ -929,9 +930,9 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
 // elements), so items of different parts never touch the same bytes. The item rewrites its
 // chunk's destination pages one at a time, left to right: destination page dp reads source
 // pages dp .. dp + span, whose value rows of the part stay in an LDS ring of span + 1 slices
-// (each source slice is fetched once), and key pieces go through registers. A destination page
-// overwrites only its own source page, which no later page of the item reads; the first `span`
-// pages of the next chunk come from the snapshot.
+// (each source slice is fetched once), and key pieces go through registers, fetched one page
+// ahead. A destination page overwrites only its own source page, which no later page of the
+// item reads; the first `span` pages of the next chunk come from the snapshot.
 constexpr int WIDE_KQ = 4;  // key pieces per thread and page: 256 slots x 4 pieces / CP_THREADS
 constexpr int WIDE_VQ = 4;  // value pieces per thread and page slice
 __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
@@ -942,10 +943,19 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
   const int vslice = WIDE_PART * b;         // bytes of one page's value rows of a part
   const int per = 16 / es;                  // elements per 16-byte piece
   __shared__ int s_thr[WIDE_MAX_EVICT];
-  __shared__ int s_src[256];                // source slot of each destination slot of the page
+  __shared__ int s_src[2 * 256];            // source slots of two destination pages' slots
   __shared__ long long s_soff[CHUNK_PAGES + MAX_SPAN], s_doff[CHUNK_PAGES];
   extern __shared__ __align__(16) uint8_t s_ring[];  // ring x vslice bytes
-  for (int item_k = blockIdx.x; item_k < n_items; item_k += gridDim.x) {
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, and the parts of one
+  // (request, head, chunk) read the two halves of the same 128-byte key lines, so all parts of a
+  // chunk go to workgroups of one XCD (its L2 then serves the second half). Workgroup b of XCD
+  // b % 8 takes the m-th part-item of the chunks g = b % 8 (mod 8), m = b / 8, b / 8 + S, ...
+  const int n_groups = n_items / P.npart;
+  const int xcd = blockIdx.x % NUM_XCD, S = gridDim.x / NUM_XCD;
+  for (int m = blockIdx.x / NUM_XCD;; m += S) {
+    const int g = xcd + NUM_XCD * (m / P.npart);
+    if (g >= n_groups) break;
+    const int item_k = g * P.npart + m % P.npart;
     __syncthreads();  // the previous item is done with the tables and the ring
     const int2 item = P.items[item_k];
     const int i = item.x / P.H_kv, h = item.x % P.H_kv;
@@ -973,9 +983,9 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
       if (so == -1) return snap_ptr(P, i, h, lp, which);
       return (which ? P.v : P.k) + so;
     };
-    // value rows of source page lp into its ring slot (zeros past the old pages: never read)
-    auto load_slice = [&](int lp) {
-      u32x4_t r[WIDE_VQ];
+    const int nk = b * (WIDE_PART / 16);
+    // value rows of source page lp into registers (zeros past the old pages: never read)
+    auto load_slice = [&](int lp, u32x4_t (&r)[WIDE_VQ]) {
       const bool have = s_soff[lp - dp_lo] != -2;
       const u32x4_t* src = have ? reinterpret_cast<const u32x4_t*>(src_page(lp, 1) + voff) : nullptr;
 #pragma unroll
@@ -984,6 +994,8 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
         r[it] = u32x4_t{0u, 0u, 0u, 0u};
         if (have && q < vslice / 16) r[it] = src[q];
       }
+    };
+    auto store_slice = [&](int lp, const u32x4_t (&r)[WIDE_VQ]) {
       u32x4_t* dst = reinterpret_cast<u32x4_t*>(s_ring + (size_t)(lp % ring) * vslice);
 #pragma unroll
       for (int it = 0; it < WIDE_VQ; ++it) {
@@ -991,38 +1003,63 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
         if (q < vslice / 16) dst[q] = r[it];
       }
     };
-    for (int lp = dp_lo; lp < dp_lo + span; ++lp) load_slice(lp);
-    for (int dp = dp_lo; dp < dp_hi; ++dp) {
-      if (dp > dp_lo) __syncthreads();  // the previous page is done with s_src and its ring slot
-      load_slice(dp + span);
+    // source slot of every destination slot of page dp, into table t: j + #{k : thr[k] <= j}
+    // (thr is nondecreasing: a binary search)
+    auto make_src = [&](int dp, int t) {
       for (int q = threadIdx.x; q < b; q += CP_THREADS) {
         const int j = (dp << lb) + q;
-        int lo = 0, hi = E;  // #{k : thr[k] <= j}; thr is nondecreasing
+        int lo = 0, hi = E;
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
           if (s_thr[mid] <= j) lo = mid + 1;
           else hi = mid;
         }
-        s_src[q] = j + lo;
+        s_src[t * 256 + q] = j + lo;
       }
-      __syncthreads();  // ring slices and the source table are complete
-      const int nk = b * (WIDE_PART / 16);
-      u32x4_t kreg[WIDE_KQ];
+    };
+    auto load_keys = [&](int t, u32x4_t (&kr)[WIDE_KQ]) {
 #pragma unroll
       for (int it = 0; it < WIDE_KQ; ++it) {
         const int q = threadIdx.x + it * CP_THREADS;
         if (q < nk) {
-          const int src = s_src[q >> 2];
-          kreg[it] = *reinterpret_cast<const u32x4_t*>(src_page(src >> lb, 0) + (size_t)(src & (b - 1)) * krow +
-                                                       koff + (q & 3) * 16);
+          const int src = s_src[t * 256 + (q >> 2)];
+          kr[it] = *reinterpret_cast<const u32x4_t*>(src_page(src >> lb, 0) + (size_t)(src & (b - 1)) * krow +
+                                                     koff + (q & 3) * 16);
         }
       }
-      __syncthreads();  // every read of the page's own source bytes precedes its writes
+    };
+    // Software pipeline: while destination page dp is written, the key pieces of page dp + 1
+    // and the value slice of page dp + 1 + span are already in flight. Those loads read pages
+    // above dp only, which this item has not written yet.
+    {
+      u32x4_t r0[WIDE_VQ];
+      for (int lp = dp_lo; lp < dp_lo + span; ++lp) {
+        load_slice(lp, r0);
+        store_slice(lp, r0);
+      }
+    }
+    make_src(dp_lo, 0);
+    __syncthreads();
+    u32x4_t kA[WIDE_KQ], vA[WIDE_VQ];
+    load_keys(0, kA);
+    load_slice(dp_lo + span, vA);
+    for (int dp = dp_lo; dp < dp_hi; ++dp) {
+      const int t = (dp - dp_lo) & 1;
+      // kA: key pieces of page dp; vA: value slice of source page dp + span
+      store_slice(dp + span, vA);  // its ring slot held page dp - 1, which is finished
+      const bool next = dp + 1 < dp_hi;
+      if (next) make_src(dp + 1, t ^ 1);
+      __syncthreads();  // slice dp + span and the next source table are visible
+      u32x4_t kB[WIDE_KQ] = {}, vB[WIDE_VQ] = {};
+      if (next) {
+        load_keys(t ^ 1, kB);
+        load_slice(dp + 1 + span, vB);
+      }
       uint8_t* kd = P.k + s_doff[dp - dp_lo] + koff;
 #pragma unroll
       for (int it = 0; it < WIDE_KQ; ++it) {
         const int q = threadIdx.x + it * CP_THREADS;
-        if (q < nk) *reinterpret_cast<u32x4_t*>(kd + (size_t)(q >> 2) * krow + (q & 3) * 16) = kreg[it];
+        if (q < nk) *reinterpret_cast<u32x4_t*>(kd + (size_t)(q >> 2) * krow + (q & 3) * 16) = kA[it];
       }
       // value rows: 16-byte pieces of destination rows gathered from the ring
       uint8_t* vd = P.v + s_doff[dp - dp_lo] + voff;
@@ -1031,7 +1068,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
         const int dl = q / row_pieces, piece = q - dl * row_pieces;
         uint32_t wv[4] = {0u, 0u, 0u, 0u};
         for (int e = 0; e < per; ++e) {
-          const int rs = s_src[piece * per + e];
+          const int rs = s_src[t * 256 + piece * per + e];
           const uint8_t* sp = s_ring + (size_t)((rs >> lb) % ring) * vslice +
                               ((size_t)dl * b + (rs & (b - 1))) * es;
           if (es == 2) wv[e >> 1] |= (uint32_t)(*reinterpret_cast<const uint16_t*>(sp)) << (16 * (e & 1));
@@ -1039,6 +1076,11 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
         }
         *reinterpret_cast<u32x4_t*>(vd + (size_t)q * 16) = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
       }
+      __syncthreads();  // every read of this page's ring slots precedes the next page's store
+#pragma unroll
+      for (int it = 0; it < WIDE_KQ; ++it) kA[it] = kB[it];
+#pragma unroll
+      for (int it = 0; it < WIDE_VQ; ++it) vA[it] = vB[it];
     }
   }
 }
@@ -1495,7 +1537,7 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
   size_t lds;
   if (wide) {
     lds = (size_t)(span + 1) * WIDE_PART * b;
-    if (lds + sizeof(int) * (WIDE_MAX_EVICT + 256) + 16 * (2 * CHUNK_PAGES + MAX_SPAN) > 64 * 1024)
+    if (lds + sizeof(int) * (WIDE_MAX_EVICT + 2 * 256) + 16 * (2 * CHUNK_PAGES + MAX_SPAN) > 64 * 1024)
       return GP_ERR_UNSUPPORTED;
   } else {
     lds = (size_t)(W + span) * b * D * es;
@@ -1619,15 +1661,31 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
       GP_CHECK_LAUNCH();
     }
   }
-  if (!(phases & GP_PHASE_MOVE)) return GP_OK;
   const int cus = device_cus();
   const int max_items = R * H_kv * P.max_chunks * P.npart;
-  for (int l = 0; l < L; ++l) {
-    const CParams Q = layer(l);
-    if (mixed) {
+  // The snapshot only reads K/V pages (into the workspace). With one layer it joins the plan,
+  // which may run beside work that reads the same pages; with several layers the layers share
+  // the snapshot space, so each layer's snapshot directly precedes its own move.
+  auto snapshot = [&](const CParams& Q) {
+    if (mixed)
       hipLaunchKernelGGL(snapshot_mixed_kernel, dim3(std::max(1, std::min(4 * cus, max_items))),
                          dim3(CP_THREADS), 0, s, Q);
+    else
+      hipLaunchKernelGGL(snapshot_kernel, dim3(std::max(1, std::min(4 * cus, max_items))),
+                         dim3(CP_THREADS), 0, s, Q);
+  };
+  if ((phases & GP_PHASE_PLAN) && L == 1) {
+    snapshot(layer(0));
+    GP_CHECK_LAUNCH();
+  }
+  if (!(phases & GP_PHASE_MOVE)) return GP_OK;
+  for (int l = 0; l < L; ++l) {
+    const CParams Q = layer(l);
+    if (L > 1) {
+      snapshot(Q);
       GP_CHECK_LAUNCH();
+    }
+    if (mixed) {
       hipLaunchKernelGGL(compact_mixed_kernel, dim3(std::max(1, std::min(4 * cus, max_items))),
                          dim3(CP_THREADS), (size_t)(span + 1) * MX_SLOT, s, Q);
       GP_CHECK_LAUNCH();
@@ -1635,11 +1693,9 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
       GP_CHECK_LAUNCH();
       continue;
     }
-    hipLaunchKernelGGL(snapshot_kernel, dim3(std::max(1, std::min(4 * cus, max_items))),
-                       dim3(CP_THREADS), 0, s, Q);
-    GP_CHECK_LAUNCH();
-    if (wide)
-      hipLaunchKernelGGL(compact_wide_kernel, dim3(std::max(1, std::min(4 * cus, max_items))),
+    if (wide)  // a multiple of NUM_XCD workgroups (the kernel deals chunks to XCDs)
+      hipLaunchKernelGGL(compact_wide_kernel,
+                         dim3(NUM_XCD * std::max(1, std::min(4 * cus, max_items) / NUM_XCD)),
                          dim3(CP_THREADS), lds, s, Q);
     else
       hipLaunchKernelGGL(compact_kernel, dim3(std::max(1, std::min(2 * cus, max_items))),
