@@ -841,9 +841,8 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
     if (lp < dp_hi) s_doff[threadIdx.x] = (long long)pool_off(P, P.block_tables[(size_t)inf.r * P.max_pages + lp], h);
   }
   const int lqpp = P.log_qpp, qpp = 1 << lqpp;  // 16-byte pieces per page
-  const int lkq = P.log_kq, lvq = P.log_vq;
+  const int lkq = P.log_kq;
   const int krow = D * es;
-  const int per = 16 / es;                      // elements per 16-byte piece
   for (int w0 = dp_lo; w0 < dp_hi; w0 += W) {
     const int w1 = min(w0 + W, dp_hi);          // destination pages [w0, w1)
     const int nsrc = w1 - w0 + P.span;          // source pages [w0, w1 + span - 1]
@@ -901,25 +900,27 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
         reinterpret_cast<u32x4_t*>(P.k + s_doff[dp - dp_lo] + (size_t)(slot & (b - 1)) * krow)[piece] = kreg[it];
       }
     }
-    // values: 16-byte pieces of destination value rows gathered from LDS
-    const int npieces = (w1 - w0) * D << lvq;
-    for (int q = threadIdx.x; q < npieces; q += CP_THREADS) {
-      const int piece = q & ((1 << lvq) - 1);
-      const int rowi = q >> lvq;  // (page, dd)
+    // values: each lane writes two adjacent tokens of one destination value row, so the lanes of
+    // a wave read consecutive tokens of a few rows from LDS (no bank conflicts) and write whole
+    // 32- or 64-byte row segments
+    const int hb = b >> 1;  // token pairs per row
+    const int npairs = (w1 - w0) * D * hb;
+    for (int q = threadIdx.x; q < npairs; q += CP_THREADS) {
+      const int rowi = q / hb, tp = q - rowi * hb;  // (page, dd), token pair
       const int dpl = rowi / D, dd = rowi - dpl * D;
-      uint32_t wv[4] = {0u, 0u, 0u, 0u};
-      for (int e = 0; e < per; ++e) {
-        const int rs = s_src[(dpl << lb) + piece * per + e];
-        const uint8_t* src = s_v + (size_t)(rs >> lb) * pb + ((size_t)dd * b + (rs & (b - 1))) * es;
-        if (es == 2) {
-          const uint32_t x = *reinterpret_cast<const uint16_t*>(src);
-          wv[e >> 1] |= x << (16 * (e & 1));
-        } else {
-          wv[e] = *reinterpret_cast<const uint32_t*>(src);
-        }
+      const int slot = (dpl << lb) + 2 * tp;
+      const int rs0 = s_src[slot], rs1 = s_src[slot + 1];
+      const uint8_t* a0 = s_v + (size_t)(rs0 >> lb) * pb + ((size_t)dd * b + (rs0 & (b - 1))) * es;
+      const uint8_t* a1 = s_v + (size_t)(rs1 >> lb) * pb + ((size_t)dd * b + (rs1 & (b - 1))) * es;
+      uint8_t* dst = P.v + s_doff[w0 + dpl - dp_lo] + ((size_t)dd * b + 2 * tp) * es;
+      if (es == 2) {
+        const uint32_t x0 = *reinterpret_cast<const uint16_t*>(a0);
+        const uint32_t x1 = *reinterpret_cast<const uint16_t*>(a1);
+        *reinterpret_cast<uint32_t*>(dst) = x0 | (x1 << 16);
+      } else {
+        *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{*reinterpret_cast<const uint32_t*>(a0),
+                                                   *reinterpret_cast<const uint32_t*>(a1)};
       }
-      reinterpret_cast<u32x4_t*>(P.v + s_doff[w0 + dpl - dp_lo] + (size_t)dd * b * es)[piece] =
-          u32x4_t{wv[0], wv[1], wv[2], wv[3]};
     }
   }
   }

@@ -1,6 +1,6 @@
 """GPU parity for INT4 pages (PASK App. B.5): the page quantiser bit for bit against the
 oracle's quantiser, and decode attention over caches mixing released, fp8, bf16 and INT4 pages
-against the float64 oracle."""
+against the float64 oracle (two decode passes with their own stream-K widths, under grid caps)."""
 import numpy as np
 import pytest
 import torch
@@ -172,6 +172,33 @@ def test_quantize_then_decode(D, b, G):
     eo, nan_o = maxabs(f64(out), ref_o)
     el, nan_l = maxabs(lse.cpu().numpy(), ref_l)
     say(f"[quantize+decode D={D} b={b} G={G}] max|out-ref|={eo:.3e} max|lse-ref|={el:.3e}")
+    assert not nan_o and not nan_l
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+@pytest.mark.parametrize("max_wg,H_kv", [(1, 8), (3, 4), (37, 8), (100000, 8), (100000, 2)])
+def test_mixed_two_passes_capped_grid(max_wg, H_kv):
+    """A mixed cache (released / fp8 / bf16 / INT4 pages) decodes in two passes whose stream-K
+    widths differ (the INT4 pass uses four-head workgroups); under any grid cap the merged
+    result must match the oracle."""
+    from workloads.configs import attach_mixed_pools
+    lens = [0, 5, 700, 16, 3000, 1, 0, 257, 1200, 64, 4000]
+    wl = make_decode_case(len(lens), 4 * H_kv, H_kv, 128, 16, lens, seed=max_wg % 89 + H_kv).to(DEV)
+    tags = np.random.default_rng(max_wg + H_kv).choice([0, 1, 2, 3], size=wl.num_pages,
+                                                       p=[0.15, 0.25, 0.3, 0.3]).astype(np.uint8)
+    attach_mixed_pools(wl, tags, seed=H_kv)
+    say(f"[two passes cap={max_wg} H_kv={H_kv}] tags used={np.bincount(tags, minlength=4).tolist()}")
+    out, lse = gp.gp_paged_decode_attn_ex(wl.q, gp.KVCache.from_workload(wl), wl.block_tables,
+                                          wl.context_lens, wl.max_context, wl.sm_scale,
+                                          max_workgroups=max_wg)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
+                                          npy(wl.block_tables), npy(wl.context_lens), 16,
+                                          wl.sm_scale, **mixed_np(wl))
+    eo, nan_o = maxabs(f64(out), ref_o)
+    el, nan_l = maxabs(lse.cpu().numpy(), ref_l)
+    say(f"[two passes cap={max_wg} H_kv={H_kv}] max|out-ref|={eo:.3e} max|lse-ref|={el:.3e}")
     assert not nan_o and not nan_l
     assert eo <= TOL["bf16"] and el <= TOL["bf16"]
     assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
