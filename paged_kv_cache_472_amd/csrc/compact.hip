@@ -798,6 +798,16 @@ __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
   }
 }
 
+// Barrier for LDS hand-offs only: waits for this wave's LDS operations, not for its global
+// stores, so a window's writes drain while the next window's reads are in flight. Windows and
+// items of a workgroup never read bytes that another of its windows writes (see compact_kernel),
+// so the global stores need no ordering inside the kernel.
+constexpr long long NO_SRC = LLONG_MIN;  // no source page (past the request's old pages)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left at their maximum
+  __builtin_amdgcn_s_barrier();
+}
+
 // Destination slot j of a compacted head takes source slot j + #{k : ev[k] - k <= j} (ev the
 // ascending evicted candidates): the j-th kept candidate, then the recent tokens. A workgroup
 // owns a chunk of destination pages and walks it left to right in windows. Per window it
@@ -811,7 +821,7 @@ __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
 __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   const int n_items = *P.n_items;
   for (int item_k = blockIdx.x; item_k < n_items; item_k += gridDim.x) {
-  __syncthreads();  // the previous item is done with the tables and LDS
+  lds_barrier();  // the previous item is done with the tables and LDS
   const int2 item = P.items[item_k];
   const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y;
   const Info inf = P.info[i];
@@ -821,9 +831,13 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   const int dp_lo = max(dp0, c * L), dp_hi = min((c + 1) * L, inf.n_dest);
   __shared__ int s_thr[MAX_EVICT];
   __shared__ int s_src[MAX_WINDOW_SLOTS];
-  // source pages dp_lo .. dp_hi + span - 1: byte offset of (page, head) in the pool, or -1 for the
-  // snapshot, or -2 past the old pages; destination pages dp_lo .. dp_hi - 1: pool byte offset
-  __shared__ long long s_soff[CHUNK_PAGES + MAX_SPAN], s_doff[CHUNK_PAGES];
+  // source pages dp_lo .. dp_hi + span - 1: byte offset of the (page, head) key block from the
+  // key pool's base and of the value block from the value pool's base, in the pool or in the
+  // snapshot (NO_SRC past the old pages); destination pages dp_lo .. dp_hi - 1: pool byte offset.
+  // Offsets from the pool pointers keep every access in the global address space.
+  __shared__ long long s_ksrc[CHUNK_PAGES + MAX_SPAN];
+  __shared__ long long s_vsrc[CHUNK_PAGES + MAX_SPAN];
+  __shared__ long long s_doff[CHUNK_PAGES];
   extern __shared__ __align__(16) uint8_t s_v[];  // value pages of the window
   const int E = inf.E;
   const size_t pb = page_bytes(P);
@@ -833,21 +847,28 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
                              : INT_MAX;
   if (threadIdx.x < dp_hi - dp_lo + P.span) {
     const int lp = dp_lo + threadIdx.x;
-    long long so = -2;
-    if (lp < inf.P)
-      so = from_snapshot(P, lp, c, inf.n_dest) ? -1
-                                                 : (long long)pool_off(P, P.old_bt[(size_t)i * P.max_pages + lp], h);
-    s_soff[threadIdx.x] = so;
+    long long ks = NO_SRC, vs = NO_SRC;
+    if (lp < inf.P) {
+      if (from_snapshot(P, lp, c, inf.n_dest)) {
+        ks = (long long)((intptr_t)snap_ptr(P, i, h, lp, 0) - (intptr_t)P.k);
+        vs = (long long)((intptr_t)snap_ptr(P, i, h, lp, 1) - (intptr_t)P.v);
+      } else {
+        ks = vs = (long long)pool_off(P, P.old_bt[(size_t)i * P.max_pages + lp], h);
+      }
+    }
+    s_ksrc[threadIdx.x] = ks;
+    s_vsrc[threadIdx.x] = vs;
     if (lp < dp_hi) s_doff[threadIdx.x] = (long long)pool_off(P, P.block_tables[(size_t)inf.r * P.max_pages + lp], h);
   }
   const int lqpp = P.log_qpp, qpp = 1 << lqpp;  // 16-byte pieces per page
   const int lkq = P.log_kq;
   const int krow = D * es;
+  const int ld = D == 128 ? 7 : 6;
   for (int w0 = dp_lo; w0 < dp_hi; w0 += W) {
     const int w1 = min(w0 + W, dp_hi);          // destination pages [w0, w1)
     const int nsrc = w1 - w0 + P.span;          // source pages [w0, w1 + span - 1]
     const int nslots = (w1 - w0) << lb;
-    __syncthreads();  // tables are set; the previous window is done with LDS
+    lds_barrier();  // tables are set; the previous window is done with LDS
     for (int q = threadIdx.x; q < nslots; q += CP_THREADS) {
       const int j = (w0 << lb) + q;
       int cnt = 0;
@@ -855,42 +876,38 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
       for (int k = 0; k < MAX_EVICT; ++k) cnt += s_thr[k] <= j ? 1 : 0;
       s_src[q] = q + cnt;  // source slot relative to the window
     }
-    __syncthreads();
-    // issue every read of the window before using any: value pieces, then key pieces
-    auto src_page = [&](int lp, int which) -> const uint8_t* {
-      const long long so = s_soff[lp - dp_lo];
-      if (so == -1) return snap_ptr(P, i, h, lp, which);
-      return (which ? P.v : P.k) + so;
-    };
+    lds_barrier();
+    // every read of the window is issued before any is used, with no branch between them (a
+    // piece past the window or the old pages reads a valid stand-in address and is discarded)
     const int nv = nsrc << lqpp;
     u32x4_t vreg[V_PIECES];
 #pragma unroll
     for (int it = 0; it < V_PIECES; ++it) {
       const int q = threadIdx.x + it * CP_THREADS;
-      vreg[it] = u32x4_t{0u, 0u, 0u, 0u};
-      if (q < nv) {
-        const int lp = w0 + (q >> lqpp);
-        if (s_soff[lp - dp_lo] != -2)
-          vreg[it] = reinterpret_cast<const u32x4_t*>(src_page(lp, 1))[q & (qpp - 1)];
-      }
+      const long long base = s_vsrc[w0 - dp_lo + min(q >> lqpp, nsrc - 1)];
+      const long long o = (q < nv && base != NO_SRC) ? base + (long long)(q & (qpp - 1)) * 16 : 0;
+      vreg[it] = *reinterpret_cast<const u32x4_t*>(P.v + o);
     }
     const int nk = nslots << lkq;
     u32x4_t kreg[K_PIECES];
 #pragma unroll
     for (int it = 0; it < K_PIECES; ++it) {
-      const int q = threadIdx.x + it * CP_THREADS;
-      if (q < nk) {
-        const int slot = q >> lkq, piece = q & ((1 << lkq) - 1);
-        const int src = (w0 << lb) + s_src[slot];
-        kreg[it] = reinterpret_cast<const u32x4_t*>(src_page(src >> lb, 0) + (size_t)(src & (b - 1)) * krow)[piece];
-      }
+      const int q = min((int)threadIdx.x + it * CP_THREADS, nk - 1);
+      const int slot = q >> lkq, piece = q & ((1 << lkq) - 1);
+      const int src = (w0 << lb) + s_src[slot];
+      const long long base = s_ksrc[(src >> lb) - dp_lo];
+      const long long o = base != NO_SRC ? base + (long long)(src & (b - 1)) * krow + piece * 16 : 0;
+      kreg[it] = *reinterpret_cast<const u32x4_t*>(P.k + o);
     }
 #pragma unroll
     for (int it = 0; it < V_PIECES; ++it) {
       const int q = threadIdx.x + it * CP_THREADS;
-      if (q < nv) reinterpret_cast<u32x4_t*>(s_v)[q] = vreg[it];
+      if (q < nv) {
+        const bool ok = s_vsrc[w0 - dp_lo + (q >> lqpp)] != NO_SRC;
+        reinterpret_cast<u32x4_t*>(s_v)[q] = ok ? vreg[it] : u32x4_t{0u, 0u, 0u, 0u};
+      }
     }
-    __syncthreads();  // every read of this window's sources precedes any write
+    lds_barrier();  // every read of this window's sources precedes any write
 #pragma unroll
     for (int it = 0; it < K_PIECES; ++it) {
       const int q = threadIdx.x + it * CP_THREADS;
@@ -903,11 +920,11 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
     // values: each lane writes two adjacent tokens of one destination value row, so the lanes of
     // a wave read consecutive tokens of a few rows from LDS (no bank conflicts) and write whole
     // 32- or 64-byte row segments
-    const int hb = b >> 1;  // token pairs per row
-    const int npairs = (w1 - w0) * D * hb;
+    const int lhb = lb - 1, hb = 1 << lhb;  // token pairs per row
+    const int npairs = ((w1 - w0) << ld) << lhb;
     for (int q = threadIdx.x; q < npairs; q += CP_THREADS) {
-      const int rowi = q / hb, tp = q - rowi * hb;  // (page, dd), token pair
-      const int dpl = rowi / D, dd = rowi - dpl * D;
+      const int rowi = q >> lhb, tp = q & (hb - 1);  // (page, dd), token pair
+      const int dpl = rowi >> ld, dd = rowi & (D - 1);
       const int slot = (dpl << lb) + 2 * tp;
       const int rs0 = s_src[slot], rs1 = s_src[slot + 1];
       const uint8_t* a0 = s_v + (size_t)(rs0 >> lb) * pb + ((size_t)dd * b + (rs0 & (b - 1))) * es;

@@ -152,21 +152,24 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
   const bool col_ok = n16 < 2 * G;
   const int x = n16 / G, g = n16 % G;
   const int hq = h * G + g;
-  const float* qrow = P.qt + (((size_t)i * 2 + x) * P.H_q + hq) * D;
+  // columns past 2G read the first summary row (no branch around the loads) and use zeros
+  const float* qrow = col_ok ? P.qt + (((size_t)i * 2 + x) * P.H_q + hq) * D : P.qt;
 
   // summary operand: column n16 = (view x, head g)
   u32x4_t qhi[BF16 ? D / 32 : D / 16], qlo[BF16 ? D / 32 : 1];
   if constexpr (BF16) {
+    float2 qv[D / 32][4];
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qv[kk][e] = *reinterpret_cast<const float2*>(qrow + 32 * kk + 8 * g4 + 2 * e);
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float v0 = 0.f, v1 = 0.f;
-        if (col_ok) {
-          v0 = qrow[32 * kk + 8 * g4 + 2 * e];
-          v1 = qrow[32 * kk + 8 * g4 + 2 * e + 1];
-        }
+        const float v0 = col_ok ? qv[kk][e].x : 0.f, v1 = col_ok ? qv[kk][e].y : 0.f;
         const uint32_t h0 = gp::f32_to_bf16_bits(v0), h1 = gp::f32_to_bf16_bits(v1);
         hi[e] = h0 | (h1 << 16);
         lo[e] = gp::pack_bf16x2(v0 - gp::bf16_bits_to_f32(h0), v1 - gp::bf16_bits_to_f32(h1));
@@ -177,25 +180,52 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
   } else {
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-      if (col_ok) v = *reinterpret_cast<const f32x4_t*>(qrow + (D / 4) * g4 + 4 * c);
-      qhi[c] = __builtin_bit_cast(u32x4_t, v);
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(qrow + (D / 4) * g4 + 4 * c);
+      qhi[c] = col_ok ? __builtin_bit_cast(u32x4_t, v) : u32x4_t{0u, 0u, 0u, 0u};
     }
     (void)qlo;
   }
 
   float m_run = -INFINITY, l_run = 0.f;
   float* lrow = P.logits + (((size_t)i * 2 + x) * P.H_q + hq) * P.C_max;
-  for (int t = tile0 + w; t < tile1; t += LG_WAVES) {
-    const int tok0 = t << 4;
-    int pg = P.block_tables[(size_t)r * P.max_pages + tok0 / b];
-    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-    bool valid_page = pg >= 0 && pg < P.num_pages;
-    int tag = GP_TAG_BF16;
-    if (valid_page && P.page_tag) {
-      tag = P.page_tag[pg];
-      valid_page = tag != GP_TAG_RELEASE;  // released tokens take no part in the softmax
+  // this wave's tiles are tile0 + w + k LG_WAVES, k < nt (nt <= CHUNK_TILES / LG_WAVES): lane k
+  // fetches the page id and tag of tile k up front, and the key rows of plain (bf16 / fp32)
+  // tiles are loaded two tiles ahead of their use, with no branch around the loads (a tile
+  // past the wave's last, or of another format, reads the pool's first bytes and is unused)
+  constexpr int NKW = BF16 ? D / 32 : D / 16;  // 16-byte key pieces of a plain tile per lane
+  const int nt = tile1 > tile0 + w ? (tile1 - tile0 - w + LG_WAVES - 1) / LG_WAVES : 0;
+  int pg_l = -1, tag_l = GP_TAG_BF16;
+  if (lane < nt) {
+    const int tl = tile0 + w + lane * LG_WAVES;
+    const int pg = P.block_tables[(size_t)r * P.max_pages + (tl << 4) / b];
+    bool ok = pg >= 0 && pg < P.num_pages;
+    if (ok && P.page_tag) {
+      tag_l = P.page_tag[pg];
+      ok = tag_l != GP_TAG_RELEASE;  // released tokens take no part in the softmax
     }
+    pg_l = ok ? pg : -1;
+  }
+  auto load_plain = [&](int k, u32x4_t (&kw)[NKW]) {
+    const int kc = min(k, 63);
+    const int pg = __builtin_amdgcn_readlane(pg_l, kc), tag = __builtin_amdgcn_readlane(tag_l, kc);
+    const int tok0 = (tile0 + w + k * LG_WAVES) << 4;
+    const bool plain = k < nt && pg >= 0 && tag == GP_TAG_BF16;
+    const size_t base = plain ? ((size_t)pg * P.H_kv + h) * (size_t)b * D + (size_t)(tok0 % b + n16) * D : 0;
+    if constexpr (BF16) {
+      const u32x4_t* kr = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(P.k) + base + (plain ? 8 * g4 : 0));
+#pragma unroll
+      for (int kk = 0; kk < NKW; ++kk) kw[kk] = kr[plain ? 4 * kk : 0];
+    } else {
+      const u32x4_t* kr = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(P.k) + base + (plain ? (D / 4) * g4 : 0));
+#pragma unroll
+      for (int c = 0; c < NKW; ++c) kw[c] = kr[plain ? c : 0];
+    }
+  };
+  auto process = [&](int k, const u32x4_t (&kw)[NKW]) {
+    const int pg = __builtin_amdgcn_readlane(pg_l, k), tag = __builtin_amdgcn_readlane(tag_l, k);
+    const int tok0 = (tile0 + w + k * LG_WAVES) << 4;
+    const bool valid_page = pg >= 0;
+    f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
     if (valid_page && tag != GP_TAG_BF16) {
       if constexpr (BF16) {
         // fp8 / INT4 keys: the codes are exact bf16 values; the row scale multiplies the
@@ -208,9 +238,9 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
           for (int kk = 0; kk < D / 32; ++kk) {
             const u32x2_t c = *reinterpret_cast<const u32x2_t*>(kr + 32 * kk);
             const u32x2_t lo = gp::fp8x4_to_bf16x4(c.x), hi = gp::fp8x4_to_bf16x4(c.y);
-            const bf16x8_t kw = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
-            sacc = gp::mfma_bf16_16x16x32(kw, __builtin_bit_cast(bf16x8_t, qhi[kk]), sacc);
-            sacc = gp::mfma_bf16_16x16x32(kw, __builtin_bit_cast(bf16x8_t, qlo[kk]), sacc);
+            const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+            sacc = gp::mfma_bf16_16x16x32(kb, __builtin_bit_cast(bf16x8_t, qhi[kk]), sacc);
+            sacc = gp::mfma_bf16_16x16x32(kb, __builtin_bit_cast(bf16x8_t, qlo[kk]), sacc);
           }
           sc = *reinterpret_cast<const f32x4_t*>(P.k_scale + row0 + 4 * g4);
         } else {
@@ -225,9 +255,9 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
               const int c1 = (int32_t)(w4 << (24 - 8 * e)) >> 28;  // nibble 2e + 1
               e2[e] = (__float_as_uint((float)c0) >> 16) | (__float_as_uint((float)c1) & 0xffff0000u);
             }
-            const bf16x8_t kw = __builtin_bit_cast(bf16x8_t, u32x4_t{e2[0], e2[1], e2[2], e2[3]});
-            sacc = gp::mfma_bf16_16x16x32(kw, __builtin_bit_cast(bf16x8_t, qhi[kk]), sacc);
-            sacc = gp::mfma_bf16_16x16x32(kw, __builtin_bit_cast(bf16x8_t, qlo[kk]), sacc);
+            const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, u32x4_t{e2[0], e2[1], e2[2], e2[3]});
+            sacc = gp::mfma_bf16_16x16x32(kb, __builtin_bit_cast(bf16x8_t, qhi[kk]), sacc);
+            sacc = gp::mfma_bf16_16x16x32(kb, __builtin_bit_cast(bf16x8_t, qlo[kk]), sacc);
           }
           const u32x2_t hs = *reinterpret_cast<const u32x2_t*>(P.k4_scale + row0 + 4 * g4);
           sc = f32x4_t{gp::half_lo(hs.x), gp::half_hi(hs.x), gp::half_lo(hs.y), gp::half_hi(hs.y)};
@@ -236,23 +266,18 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
         for (int e = 0; e < 4; ++e) sacc[e] *= sc[e];
       }
     } else if (valid_page) {
-      const size_t base = ((size_t)pg * P.H_kv + h) * (size_t)b * D + (size_t)(tok0 % b + n16) * D;
       if constexpr (BF16) {
-        const uint16_t* kr = static_cast<const uint16_t*>(P.k) + base + 8 * g4;
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
-          const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(kr + 32 * kk);
-          sacc = gp::mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, kw), __builtin_bit_cast(bf16x8_t, qhi[kk]), sacc);
-          sacc = gp::mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, kw), __builtin_bit_cast(bf16x8_t, qlo[kk]), sacc);
+          sacc = gp::mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, kw[kk]), __builtin_bit_cast(bf16x8_t, qhi[kk]), sacc);
+          sacc = gp::mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, kw[kk]), __builtin_bit_cast(bf16x8_t, qlo[kk]), sacc);
         }
       } else {
-        const float* kr = static_cast<const float*>(P.k) + base + (D / 4) * g4;
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) {
-          const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(kr + 4 * c);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sacc = gp::mfma_f32_16x16x4(__uint_as_float(kw[e]), __uint_as_float(qhi[c][e]), sacc);
+            sacc = gp::mfma_f32_16x16x4(__uint_as_float(kw[c][e]), __uint_as_float(qhi[c][e]), sacc);
         }
       }
     }
@@ -267,6 +292,18 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
     for (int e = 0; e < 4; ++e) s += gp::safe_exp2_diff(z[e], m_new);
     l_run = l_run * gp::safe_exp2_diff(m_run, m_new) + s;
     m_run = m_new;
+  };
+  u32x4_t ring[2][NKW];
+  load_plain(0, ring[0]);
+  load_plain(1, ring[1]);
+  for (int k0 = 0; k0 < nt; k0 += 2) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (k0 + q < nt) {
+        process(k0 + q, ring[q]);
+        load_plain(k0 + q + 2, ring[q]);
+      }
+    }
   }
   // merge the 4 lanes of each column, then the waves
 #pragma unroll
@@ -464,12 +501,17 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   };
 
   const float* src = (x == 0 ? P.a_short : P.a_long) + ((size_t)i * P.H_kv + h) * P.C_max;
+  // every load is issued before any is used: indexes past the candidates read candidate 0
+  // (no branch per element) and are zeroed afterwards
   uint32_t u[WS_VPT];
 #pragma unroll
   for (int j = 0; j < WS_VPT; ++j) {
     const int t = threadIdx.x + j * WS_THREADS;
-    u[j] = t < n ? __float_as_uint(src[t]) & 0x7fffffffu : 0u;
+    u[j] = __float_as_uint(src[t < n ? t : 0]);
   }
+#pragma unroll
+  for (int j = 0; j < WS_VPT; ++j)
+    u[j] = (int)threadIdx.x + j * WS_THREADS < n ? u[j] & 0x7fffffffu : 0u;
   double p_f64 = 0.0;
   for (int k = 4; k >= 0; --k) p_f64 = p_f64 * 4294967296.0 + (double)P.p_fixed[k];
   p_f64 = ldexp(p_f64, -149);

@@ -113,3 +113,63 @@ def test_decode_lse_and_split_count_independence():
         torch.cuda.synchronize()
         e, _ = maxabs(f64(o1[0]), f64(out[r]))
         assert e <= 1e-2
+
+
+@pytest.mark.parametrize("max_wg", [1, 5, 37, 224])
+def test_decode_capped_grids_match_oracle(max_wg):
+    """Grids capped to a few workgroups (ranges long against the batch) against the oracle."""
+    wl = workload_on_gpu("3b", "small")
+    out, lse = gp.gp_paged_decode_attn_ex(wl.q, gp.KVCache.from_workload(wl), wl.block_tables,
+                                          wl.context_lens, wl.max_context, wl.sm_scale,
+                                          max_workgroups=max_wg)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
+                                          npy(wl.block_tables), npy(wl.context_lens),
+                                          wl.page_size, wl.sm_scale)
+    eo, nan_o = maxabs(f64(out), ref_o)
+    el, nan_l = maxabs(lse.cpu().numpy(), ref_l)
+    say(f"[decode capped {max_wg}] max|out-ref|={eo:.3e} max|lse-ref|={el:.3e}")
+    assert not nan_o and not nan_l
+    assert eo <= TOL[wl.dtype] and el <= TOL[wl.dtype]
+
+
+def test_decode_graph_replays():
+    """A captured decode (stream-K launch and merge) replays with the eager bits, with eager
+    calls between the replays."""
+    wl = workload_on_gpu("2", "small")
+    cache = gp.KVCache.from_workload(wl)
+    need = gp.gp_paged_decode_attn_workspace_size(wl.B, wl.H_q, wl.H_kv, wl.q.shape[2],
+                                                  wl.page_size, wl.max_context)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(wl.q)
+    lse = torch.empty((wl.B, wl.H_q), dtype=torch.float32, device=DEV)
+    o_ref, l_ref = gp.gp_paged_decode_attn(wl.q, cache, wl.block_tables, wl.context_lens,
+                                           wl.max_context, wl.sm_scale, workspace=ws)
+    o_ref, l_ref = o_ref.clone(), l_ref.clone()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm the library on the side stream before capturing
+        gp.gp_paged_decode_attn(wl.q, cache, wl.block_tables, wl.context_lens, wl.max_context,
+                                wl.sm_scale, out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gp.gp_paged_decode_attn(wl.q, cache, wl.block_tables, wl.context_lens, wl.max_context,
+                                wl.sm_scale, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"[decode graph] replay {rep}: bit-identical="
+            f"{torch.equal(out, o_ref) and torch.equal(lse, l_ref)}")
+        assert torch.equal(out, o_ref) and torch.equal(lse, l_ref)
+        # eager work between replays
+        o2, _ = gp.gp_paged_decode_attn(wl.q, cache, wl.block_tables, wl.context_lens,
+                                        wl.max_context, wl.sm_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o_ref)
