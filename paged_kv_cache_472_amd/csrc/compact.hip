@@ -183,14 +183,25 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
     }
     long long dsum = 0;  // sum over layers and KV heads of K^S - K^L
     if (ok) {
+      // eight (layer, head) pairs per step, every load issued before any is used
       bool bad_ws = false;
-      for (int l = 0; l < P.L; ++l)
-        for (int h = 0; h < P.H_kv; ++h) {
+      const int nlh = P.L * P.H_kv;
+      for (int base = 0; base < nlh; base += 8) {
+        int ks[8], kl[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int lh = min(base + u, nlh - 1), l = lh / P.H_kv, h = lh - l * P.H_kv;
           const int32_t* w = P.ws_counts + (((size_t)l * P.R + i) * P.H_kv + h) * 2;
-          const int ks = w[0], kl = w[1];
-          if (ks < 0 || kl < 0) bad_ws = true;
-          dsum += (long long)ks - kl;
+          ks[u] = w[0];
+          kl[u] = w[1];
         }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {  // no branch, so the loads stay ahead of their uses
+          const bool in = base + u < nlh;
+          bad_ws |= in && (ks[u] < 0 || kl[u] < 0);
+          dsum += in ? (long long)ks[u] - kl[u] : 0ll;
+        }
+      }
       if (n > 0 && bad_ws) ok = false;
     }
     int flags = 0, ndest = 0;
@@ -788,12 +799,29 @@ __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
       const uint8_t* vs = P.v + pool_off(P, pg, h) + (size_t)part * vb;
       uint8_t* kd = snap_ptr(P, i, h, lp, 0) + (size_t)part * kb;
       uint8_t* vd = snap_ptr(P, i, h, lp, 1) + (size_t)part * vb;
-      for (int q = threadIdx.x; q < nkq; q += CP_THREADS) {
-        const size_t o = (size_t)(q >> lkpq) * krow + (size_t)(q & ((1 << lkpq) - 1)) * 16;
-        *reinterpret_cast<u32x4_t*>(kd + o) = *reinterpret_cast<const u32x4_t*>(ks + o);
+      // four pieces per thread in flight before any is stored
+      auto key_at = [&](int q) {
+        return (size_t)(q >> lkpq) * krow + (size_t)(q & ((1 << lkpq) - 1)) * 16;
+      };
+      for (int q0 = threadIdx.x; q0 < nkq; q0 += 4 * CP_THREADS) {
+        u32x4_t x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          x[u] = *reinterpret_cast<const u32x4_t*>(ks + key_at(min(q0 + u * CP_THREADS, nkq - 1)));
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (q0 + u * CP_THREADS < nkq) *reinterpret_cast<u32x4_t*>(kd + key_at(q0 + u * CP_THREADS)) = x[u];
       }
-      for (size_t q = threadIdx.x; q < vb / 16; q += CP_THREADS)
-        reinterpret_cast<u32x4_t*>(vd)[q] = reinterpret_cast<const u32x4_t*>(vs)[q];
+      const int nvq = (int)(vb / 16);
+      for (int q0 = threadIdx.x; q0 < nvq; q0 += 4 * CP_THREADS) {
+        u32x4_t x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          x[u] = reinterpret_cast<const u32x4_t*>(vs)[min(q0 + u * CP_THREADS, nvq - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (q0 + u * CP_THREADS < nvq) reinterpret_cast<u32x4_t*>(vd)[q0 + u * CP_THREADS] = x[u];
+      }
     }
   }
 }
@@ -962,7 +990,10 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
   const int per = 16 / es;                  // elements per 16-byte piece
   __shared__ int s_thr[WIDE_MAX_EVICT];
   __shared__ int s_src[2 * 256];            // source slots of two destination pages' slots
-  __shared__ long long s_soff[CHUNK_PAGES + MAX_SPAN], s_doff[CHUNK_PAGES];
+  // source pages: byte offsets of the (page, head) blocks from the key and value pool bases (pool
+  // or snapshot; NO_SRC past the old pages); destination pages: pool byte offsets
+  __shared__ long long s_ksrc[CHUNK_PAGES + MAX_SPAN], s_vsrc[CHUNK_PAGES + MAX_SPAN];
+  __shared__ long long s_doff[CHUNK_PAGES];
   extern __shared__ __align__(16) uint8_t s_ring[];  // ring x vslice bytes
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin, and the parts of one
   // (request, head, chunk) read the two halves of the same 128-byte key lines, so all parts of a
@@ -974,7 +1005,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
     const int g = xcd + NUM_XCD * (m / P.npart);
     if (g >= n_groups) break;
     const int item_k = g * P.npart + m % P.npart;
-    __syncthreads();  // the previous item is done with the tables and the ring
+    lds_barrier();  // the previous item is done with the tables and the ring
     const int2 item = P.items[item_k];
     const int i = item.x / P.H_kv, h = item.x % P.H_kv;
     const int c = item.y / P.npart, part = item.y % P.npart;
@@ -986,39 +1017,41 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
       s_thr[k] = k < E ? P.ev[((size_t)i * P.H_kv + h) * P.max_evict + k] - k : INT_MAX;
     if (threadIdx.x < dp_hi - dp_lo + span) {
       const int lp = dp_lo + threadIdx.x;
-      long long so = -2;
-      if (lp < inf.P)
-        so = from_snapshot(P, lp, c, inf.n_dest) ? -1
-                                                   : (long long)pool_off(P, P.old_bt[(size_t)i * P.max_pages + lp], h);
-      s_soff[threadIdx.x] = so;
+      long long ks = NO_SRC, vs = NO_SRC;
+      if (lp < inf.P) {
+        if (from_snapshot(P, lp, c, inf.n_dest)) {
+          ks = (long long)((intptr_t)snap_ptr(P, i, h, lp, 0) - (intptr_t)P.k);
+          vs = (long long)((intptr_t)snap_ptr(P, i, h, lp, 1) - (intptr_t)P.v);
+        } else {
+          ks = vs = (long long)pool_off(P, P.old_bt[(size_t)i * P.max_pages + lp], h);
+        }
+      }
+      s_ksrc[threadIdx.x] = ks;
+      s_vsrc[threadIdx.x] = vs;
       if (lp < dp_hi) s_doff[threadIdx.x] = (long long)pool_off(P, P.block_tables[(size_t)inf.r * P.max_pages + lp], h);
     }
-    __syncthreads();
+    lds_barrier();
     const size_t koff = (size_t)part * WIDE_PART;  // the part's bytes inside a key row
     const size_t voff = (size_t)part * vslice;     // the part's value rows inside a page
-    auto src_page = [&](int lp, int which) -> const uint8_t* {
-      const long long so = s_soff[lp - dp_lo];
-      if (so == -1) return snap_ptr(P, i, h, lp, which);
-      return (which ? P.v : P.k) + so;
-    };
     const int nk = b * (WIDE_PART / 16);
-    // value rows of source page lp into registers (zeros past the old pages: never read)
+    // value rows of source page lp into registers, with no branch around the loads (a page past
+    // the old pages, never read, takes a stand-in address and is zeroed when stored)
     auto load_slice = [&](int lp, u32x4_t (&r)[WIDE_VQ]) {
-      const bool have = s_soff[lp - dp_lo] != -2;
-      const u32x4_t* src = have ? reinterpret_cast<const u32x4_t*>(src_page(lp, 1) + voff) : nullptr;
+      const long long vs = s_vsrc[lp - dp_lo];
+      const long long o = vs != NO_SRC ? vs + (long long)voff : 0;
 #pragma unroll
       for (int it = 0; it < WIDE_VQ; ++it) {
-        const int q = threadIdx.x + it * CP_THREADS;
-        r[it] = u32x4_t{0u, 0u, 0u, 0u};
-        if (have && q < vslice / 16) r[it] = src[q];
+        const int q = min((int)threadIdx.x + it * CP_THREADS, vslice / 16 - 1);
+        r[it] = reinterpret_cast<const u32x4_t*>(P.v + o)[q];
       }
     };
     auto store_slice = [&](int lp, const u32x4_t (&r)[WIDE_VQ]) {
       u32x4_t* dst = reinterpret_cast<u32x4_t*>(s_ring + (size_t)(lp % ring) * vslice);
+      const bool have = s_vsrc[lp - dp_lo] != NO_SRC;
 #pragma unroll
       for (int it = 0; it < WIDE_VQ; ++it) {
         const int q = threadIdx.x + it * CP_THREADS;
-        if (q < vslice / 16) dst[q] = r[it];
+        if (q < vslice / 16) dst[q] = have ? r[it] : u32x4_t{0u, 0u, 0u, 0u};
       }
     };
     // source slot of every destination slot of page dp, into table t: j + #{k : thr[k] <= j}
@@ -1038,12 +1071,11 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
     auto load_keys = [&](int t, u32x4_t (&kr)[WIDE_KQ]) {
 #pragma unroll
       for (int it = 0; it < WIDE_KQ; ++it) {
-        const int q = threadIdx.x + it * CP_THREADS;
-        if (q < nk) {
-          const int src = s_src[t * 256 + (q >> 2)];
-          kr[it] = *reinterpret_cast<const u32x4_t*>(src_page(src >> lb, 0) + (size_t)(src & (b - 1)) * krow +
-                                                     koff + (q & 3) * 16);
-        }
+        const int q = min((int)threadIdx.x + it * CP_THREADS, nk - 1);
+        const int src = s_src[t * 256 + (q >> 2)];
+        const long long ks = s_ksrc[(src >> lb) - dp_lo];
+        const long long o = ks != NO_SRC ? ks + (long long)(src & (b - 1)) * krow + (long long)koff + (q & 3) * 16 : 0;
+        kr[it] = *reinterpret_cast<const u32x4_t*>(P.k + o);
       }
     };
     // Software pipeline: while destination page dp is written, the key pieces of page dp + 1
@@ -1057,7 +1089,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
       }
     }
     make_src(dp_lo, 0);
-    __syncthreads();
+    lds_barrier();
     u32x4_t kA[WIDE_KQ], vA[WIDE_VQ];
     load_keys(0, kA);
     load_slice(dp_lo + span, vA);
@@ -1067,7 +1099,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
       store_slice(dp + span, vA);  // its ring slot held page dp - 1, which is finished
       const bool next = dp + 1 < dp_hi;
       if (next) make_src(dp + 1, t ^ 1);
-      __syncthreads();  // slice dp + span and the next source table are visible
+      lds_barrier();  // slice dp + span and the next source table are visible
       u32x4_t kB[WIDE_KQ] = {}, vB[WIDE_VQ] = {};
       if (next) {
         load_keys(t ^ 1, kB);
@@ -1081,9 +1113,10 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
       }
       // value rows: 16-byte pieces of destination rows gathered from the ring
       uint8_t* vd = P.v + s_doff[dp - dp_lo] + voff;
-      const int row_pieces = b * es / 16, nvp = vslice / 16;
+      const int lrp = lb + (es == 4 ? 2 : 1) - 4;  // log2 of the 16-byte pieces of a value row
+      const int nvp = vslice / 16;
       for (int q = threadIdx.x; q < nvp; q += CP_THREADS) {
-        const int dl = q / row_pieces, piece = q - dl * row_pieces;
+        const int dl = q >> lrp, piece = q & ((1 << lrp) - 1);
         uint32_t wv[4] = {0u, 0u, 0u, 0u};
         for (int e = 0; e < per; ++e) {
           const int rs = s_src[t * 256 + piece * per + e];
@@ -1094,7 +1127,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
         }
         *reinterpret_cast<u32x4_t*>(vd + (size_t)q * 16) = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
       }
-      __syncthreads();  // every read of this page's ring slots precedes the next page's store
+      lds_barrier();  // every read of this page's ring slots precedes the next page's store
 #pragma unroll
       for (int it = 0; it < WIDE_KQ; ++it) kA[it] = kB[it];
 #pragma unroll
@@ -1196,14 +1229,46 @@ __device__ __forceinline__ void mixed_src(const CParams& P, int tag, int pg, int
   }
 }
 
-__device__ __forceinline__ void copy_bytes(uint8_t* dst, const uint8_t* src, int n) {
-  // n is a multiple of 16 for codes and of 4 for scales
-  if ((n & 15) == 0) {
-    for (int q = threadIdx.x; q < n / 16; q += CP_THREADS)
-      reinterpret_cast<u32x4_t*>(dst)[q] = reinterpret_cast<const u32x4_t*>(src)[q];
-  } else {
-    for (int q = threadIdx.x; q < n / 4; q += CP_THREADS)
-      reinterpret_cast<uint32_t*>(dst)[q] = reinterpret_cast<const uint32_t*>(src)[q];
+// One (page, head) block of a mixed cache in registers: this thread's pieces of the key and
+// value codes (at most 2 x CP_THREADS 16-byte pieces each: a 32-token bf16 page) and of the two
+// row-scale vectors (at most CP_THREADS words). Every load is issued before any is used; a
+// thread past a part's end reads the part's last piece again (or the key codes for a page
+// without scales) and stores nothing.
+struct PageParts {
+  u32x4_t k[2], v[2];
+  uint32_t ks, vs;
+};
+__device__ __forceinline__ PageParts load_page_parts(const uint8_t* kc, const uint8_t* vc,
+                                                     const uint8_t* ks, const uint8_t* vs,
+                                                     const MixedBytes& mb) {
+  const int t = threadIdx.x, nc = mb.kc / 16, ns = mb.sc / 4;
+  const u32x4_t* k16 = reinterpret_cast<const u32x4_t*>(kc);
+  const u32x4_t* v16 = reinterpret_cast<const u32x4_t*>(vc);
+  const uint32_t* k4 = reinterpret_cast<const uint32_t*>(ns ? ks : kc);
+  const uint32_t* v4 = reinterpret_cast<const uint32_t*>(ns ? vs : vc);
+  PageParts x;
+  x.k[0] = k16[min(t, nc - 1)];
+  x.k[1] = k16[min(t + CP_THREADS, nc - 1)];
+  x.v[0] = v16[min(t, nc - 1)];
+  x.v[1] = v16[min(t + CP_THREADS, nc - 1)];
+  x.ks = k4[min(t, max(ns, 1) - 1)];
+  x.vs = v4[min(t, max(ns, 1) - 1)];
+  return x;
+}
+__device__ __forceinline__ void store_page_parts(const PageParts& x, uint8_t* kd, uint8_t* vd,
+                                                 uint8_t* ksd, uint8_t* vsd, const MixedBytes& mb) {
+  const int t = threadIdx.x, nc = mb.kc / 16, ns = mb.sc / 4;
+  if (t < nc) {
+    reinterpret_cast<u32x4_t*>(kd)[t] = x.k[0];
+    reinterpret_cast<u32x4_t*>(vd)[t] = x.v[0];
+  }
+  if (t + CP_THREADS < nc) {
+    reinterpret_cast<u32x4_t*>(kd)[t + CP_THREADS] = x.k[1];
+    reinterpret_cast<u32x4_t*>(vd)[t + CP_THREADS] = x.v[1];
+  }
+  if (t < ns) {
+    reinterpret_cast<uint32_t*>(ksd)[t] = x.ks;
+    reinterpret_cast<uint32_t*>(vsd)[t] = x.vs;
   }
 }
 
@@ -1224,12 +1289,8 @@ __global__ __launch_bounds__(CP_THREADS) void snapshot_mixed_kernel(CParams P) {
       mixed_src(P, tag, pg, h, &kc, &vc, &ks, &vs);
       uint8_t* kd = snap_ptr(P, i, h, lp, 0);
       uint8_t* vd = snap_ptr(P, i, h, lp, 1);
-      copy_bytes(kd, kc, mb.kc);
-      copy_bytes(vd, vc, mb.vc);
-      if (mb.sc) {
-        copy_bytes(kd + mb.kc, ks, mb.sc);
-        copy_bytes(vd + mb.vc, vs, mb.sc);
-      }
+      const PageParts x = load_page_parts(kc, vc, ks, vs, mb);
+      store_page_parts(x, kd, vd, kd + mb.kc, vd + mb.vc, mb);
     }
   }
 }
@@ -1242,6 +1303,8 @@ __device__ __forceinline__ int nib(uint32_t w, int n) { return (int32_t)(w << (2
 // ring, one new page per destination page); the destination page is then written in its new
 // format: the same format as every source (codes and row scales copied; INT4 value nibbles
 // regrouped into four-token blocks) or bf16 (each element's exact code * scale rounded once).
+// Barriers hand off LDS only: a destination page is never a page a later stage of the workgroup
+// reads, and every staged page is in LDS before the barrier that precedes its overwrite.
 constexpr int MX_SLOT = 2 * (2 * 32 * 128) + 2 * 4 * 32;  // bf16 K + V of a 32-token page + scales
 __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
   const int n_items = *P.n_items;
@@ -1252,10 +1315,10 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
   __shared__ int s_src[32];
   __shared__ int s_tag[MAX_SPAN + 1];
   __shared__ long long s_soff[CHUNK_PAGES + MAX_SPAN];
-  __shared__ int s_spg[CHUNK_PAGES + MAX_SPAN], s_dpg[CHUNK_PAGES];
+  __shared__ int s_spg[CHUNK_PAGES + MAX_SPAN], s_stag[CHUNK_PAGES + MAX_SPAN], s_dpg[CHUNK_PAGES];
   const int vslot = D / 16;  // INT4 value dimension slot stride: slot(j) = (j % 16) * (D/16) + j / 16
   for (int item_k = blockIdx.x; item_k < n_items; item_k += gridDim.x) {
-    __syncthreads();
+    lds_barrier();
     const int2 item = P.items[item_k];
     const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y;
     const Info inf = P.info[i];
@@ -1269,16 +1332,18 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
     if (threadIdx.x < dp_hi - dp_lo + span) {
       const int lp = dp_lo + threadIdx.x;
       long long so = -2;  // -2 past the old pages, -1 snapshot, else 0
-      int pg = -1;
+      int pg = -1, tag = -1;
       if (lp < inf.P) {
         pg = P.old_bt[(size_t)i * P.max_pages + lp];
+        tag = P.page_tag[pg];
         so = from_snapshot(P, lp, c, inf.n_dest) ? -1 : 0;
       }
       s_soff[threadIdx.x] = so;
       s_spg[threadIdx.x] = pg;
+      s_stag[threadIdx.x] = tag;
       if (lp < dp_hi) s_dpg[threadIdx.x] = P.block_tables[(size_t)inf.r * P.max_pages + lp];
     }
-    __syncthreads();
+    lds_barrier();
     // stage source page lp (its own format) into ring slot lp % ring
     auto stage = [&](int lp) {
       const int t = lp - dp_lo;
@@ -1288,7 +1353,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
         return;
       }
       const int pg = s_spg[t];
-      const int tag = P.page_tag[pg];
+      const int tag = s_stag[t];
       if (threadIdx.x == 0) s_tag[lp % ring] = tag;
       const MixedBytes mb = mixed_bytes(tag, b, D);
       const uint8_t *kc, *vc, *ks, *vs;
@@ -1301,16 +1366,12 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
         mixed_src(P, tag, pg, h, &kc, &vc, &ks, &vs);
       }
       // layout in the slot: key codes | value codes | key scales | value scales
-      copy_bytes(dst, kc, mb.kc);
-      copy_bytes(dst + mb.kc, vc, mb.vc);
-      if (mb.sc) {
-        copy_bytes(dst + mb.kc + mb.vc, ks, mb.sc);
-        copy_bytes(dst + mb.kc + mb.vc + mb.sc, vs, mb.sc);
-      }
+      const PageParts x = load_page_parts(kc, vc, ks, vs, mb);
+      store_page_parts(x, dst, dst + mb.kc, dst + mb.kc + mb.vc, dst + mb.kc + mb.vc + mb.sc, mb);
     };
     for (int lp = dp_lo; lp < dp_lo + span; ++lp) stage(lp);
     for (int dp = dp_lo; dp < dp_hi; ++dp) {
-      __syncthreads();  // the previous page is done with the ring slot and s_src
+      lds_barrier();  // the previous page is done with the ring slot and s_src
       stage(dp + span);
       if (threadIdx.x < b) {
         const int j = (dp << lb) + threadIdx.x;
@@ -1319,7 +1380,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
         for (int k = 0; k < MAX_EVICT; ++k) cnt += s_thr[k] <= j ? 1 : 0;
         s_src[threadIdx.x] = j + cnt;
       }
-      __syncthreads();  // sources staged, source table complete
+      lds_barrier();  // sources staged, source table complete
       const int td = P.new_tag[(size_t)i * P.max_pages + dp];
       const size_t ph = (size_t)s_dpg[dp - dp_lo] * P.H_kv + h;
       // element e of token q's key / value in its source format, as float (exact) or double
