@@ -203,3 +203,28 @@ def test_compact_deterministic_and_prefix_untouched():
         assert torch.equal(k1[i, :, :n], k2[i, :, :n])
     for k, v in wl.snapshot().items():   # bit patterns: the state pool holds NaN poison
         assert np.array_equal(bits(v), bits(s1[k])), k
+
+
+@pytest.mark.parametrize("page_size", [16, 32])
+def test_compact_many_items_per_workgroup(page_size):
+    """More compaction items than the grid holds (16 requests x 8 KV heads x 5-7 chunks of 16
+    pages), so workgroups walk several items and every item several windows, with the LDS-only
+    barriers between them: the whole state bit for bit against the oracle, forced compress."""
+    b = page_size
+    rng = np.random.default_rng(11 + b)
+    pages = rng.integers(96, 112, size=16) if b == 16 else rng.integers(72, 80, size=16)
+    lens = [int(p) * b - int(rng.integers(0, b)) for p in pages]
+    from workloads.configs import make_decode_case
+    wl = make_decode_case(len(lens), 32, 8, 128, b, lens, seed=5 + b,
+                          boundary=range(len(lens))).to(DEV)
+    wl.beta_s, wl.beta_l, wl.p, wl.rope_theta = 0.9, 0.999, 0.99, 10000.0
+    build_state(wl)
+    a_s, a_l, ws, nc = run_score(wl)
+    st = host_state(wl)
+    R = wl.req_idx.numel()
+    pol = [ob.POLICY_FORCE_COMPRESS] * R
+    dec, kept = run_compact(wl, a_s, a_l, ws, nc, policies=pol)
+    dec_ref, kept_ref = oracle_compact(wl, st, a_s, a_l, ws, nc, policies=pol)
+    n_items = sum(-(-int(-(-int(c) // b)) // 16) for c in npy(wl.context_lens)) * 8
+    say(f"[compact many items b={b}] requests={R} items~{n_items} decisions={sorted(set(npy(dec).tolist()))}")
+    compare_state(wl, st, dec, kept, dec_ref, kept_ref, nc)
