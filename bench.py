@@ -373,6 +373,11 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
         attach_mixed_pools(wl, tags, seed=5)
         wl.req_idx = torch.as_tensor(np.sort(rng.choice(wl.B, size=16, replace=False)),
                                      dtype=torch.int32, device=dev)
+    if name == "4":
+        # the prefix-shared batch's 8 requests that its own policy compresses (the other 8 grow)
+        keep = [k for k, pol in enumerate(wl.req_policy) if pol == 1]
+        wl.req_idx = wl.req_idx[keep].contiguous()
+        wl.req_policy = [wl.req_policy[k] for k in keep]
     path = Path(wl, gp, torch)
     path.build_state()
     es = 4 if wl.dtype == "f32" else 2
