@@ -64,11 +64,13 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's timed sample (0 disables the cpu_baseline leg)")
     ap.add_argument("--reserve-cus", type=int, default=32,
-                    help="with --overlap 1: compute units the main decode leaves free for the "
-                         "boundary pass on the second stream (its workgroup cap)")
+                    help="with --overlap 1 or 2: compute units the main decode leaves free for the "
+                         "boundary pass on the second stream (its workgroup cap; 0: no cap)")
     ap.add_argument("--overlap", type=int, default=1,
                     help="1: the boundary pass runs on a second stream beside the decode (its K/V "
-                         "movement after it); 0: everything on one stream")
+                         "movement after it); 2: the boundary requests are scored first, then the "
+                         "decode runs beside their compress-or-grow plan; 0: everything on one "
+                         "stream")
     ap.add_argument("--int4", type=int, default=1,
                     help="also time decode with every page of the batch demoted to INT4 "
                          "(PASK App. B.5) by the page quantiser (bf16 workloads)")
@@ -94,6 +96,7 @@ class Path:
         i32 = torch.int32
         self.R = wl.req_idx.numel()
         self.overlap = bool(overlap) and self.R > 0
+        self.mode = int(overlap) if self.overlap else 0
         # integer page state in one flat buffer so a step can restore it with one copy; with
         # overlap it also holds a second copy of the block tables and lengths that the decode
         # reads, so that the boundary pass may rewrite the live ones while the decode runs
@@ -236,6 +239,50 @@ class Path:
         main.wait_event(self.ev_b)
         self._compact(gp.growpage.PHASE_MOVE)
         rec(8, main)
+
+    # events of a score-first step: main stream 0 start, 1 restored, 2 summaries of the boundary
+    # requests, 3 scored, 4 decoded, 7 compaction moved (end); second stream 5 start, 6 planned
+    NEV_SCORE_FIRST = 8
+
+    def step_score_first(self, ev=None):
+        """The boundary pass's latency-bound part first, alone, then decoding beside the rest.
+        The main stream updates the boundary requests' summaries and scores them (their working
+        sets: serial reductions that slow down several-fold beside a decode that keeps HBM's
+        queues full), then decodes every request from a copy of the block tables and lengths with
+        the other requests' summary update fused in; the second stream plans the compress-or-grow
+        beside the decode (decisions, pages, kept tokens: bookkeeping on the live tables only);
+        the planned K/V movement runs on the main stream after the decode."""
+        wl, gp, torch = self.wl, self.gp, self.torch
+        main = torch.cuda.current_stream()
+        sb = self.stream_b
+        rec = (lambda k, st: ev[k].record(st)) if ev is not None else (lambda k, st: None)
+        rec(0, main)
+        self.meta.copy_(self.meta0)
+        rec(1, main)
+        gp.gp_update_query_summaries(wl.q, self.slot_b, self.fresh0, wl.qstate, wl.beta_s,
+                                     wl.beta_l)
+        rec(2, main)
+        gp.gp_score_and_working_set(wl.q, wl.qstate, wl.slot_ids, wl.req_idx, self.cache,
+                                    wl.block_tables, wl.context_lens, wl.positions,
+                                    wl.rope_theta, wl.p, wl.sm_scale, self.C_max,
+                                    a_short=self.a_s, a_long=self.a_l, ws_counts=self.wsc,
+                                    n_cand=self.ncand, workspace=self.sws)
+        rec(3, main)
+        self.ev_a.record(main)
+        gp.gp_paged_decode_attn_ex(wl.q, self.cache, self.bt_dec, self.ctx_dec, wl.max_context,
+                                   wl.sm_scale, summaries=self.upd_main,
+                                   max_workgroups=self.max_wg, out=self.out, lse=self.lse,
+                                   workspace=self.dws)
+        rec(4, main)
+        with torch.cuda.stream(sb):
+            sb.wait_event(self.ev_a)
+            rec(5, sb)
+            self._compact(gp.growpage.PHASE_PLAN)
+            rec(6, sb)
+            self.ev_b.record(sb)
+        main.wait_event(self.ev_b)
+        self._compact(gp.growpage.PHASE_MOVE)
+        rec(7, main)
 
     def _compact(self, phases):
         wl, gp = self.wl, self.gp
@@ -606,8 +653,8 @@ def main():
     torch.cuda.synchronize()
     ctx_before = wl.context_lens.cpu().numpy().copy()
 
-    step = path.step_overlap if path.overlap else path.step
-    nev = Path.NEV_OVERLAP if path.overlap else 6
+    step = {0: path.step, 1: path.step_overlap, 2: path.step_score_first}[path.mode]
+    nev = {0: 6, 1: Path.NEV_OVERLAP, 2: Path.NEV_SCORE_FIRST}[path.mode]
     print(f"[bench] warmup {args.warmup} (overlap {int(path.overlap)})", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -626,7 +673,12 @@ def main():
         return sum(events[k][a].elapsed_time(events[k][z]) for k in range(args.steps)) / args.steps
 
     # the summary update runs inside the decode call (events 1 and 2 are adjacent)
-    if path.overlap:
+    if path.mode == 2:
+        rows_ms = dict(restore=avg_ms(0, 1), boundary_summaries=avg_ms(1, 2),
+                       score_and_working_set=avg_ms(2, 3), paged_decode_attn_with_summaries=avg_ms(3, 4),
+                       compact_or_grow_plan=avg_ms(5, 6), compact_or_grow_move_incl_wait=avg_ms(4, 7))
+        event_step_ms = avg_ms(0, 7)
+    elif path.overlap:
         rows_ms = dict(restore=avg_ms(0, 1), paged_decode_attn_with_summaries=avg_ms(1, 3),
                        boundary_summaries=avg_ms(4, 5), score_and_working_set=avg_ms(5, 6),
                        compact_or_grow_plan=avg_ms(6, 7), compact_or_grow_move_incl_wait=avg_ms(3, 8))

@@ -177,7 +177,9 @@ int gp_quantize_pages_int4(const gp_kv_cache* kv, const int32_t* page_ids, int n
  *                   the call's work on the stream is.
  *   max_workgroups  0, or an upper bound on the workgroups of the streaming kernel (at least one
  *                   per group of 8 KV heads is kept), so that kernels on another stream find
- *                   free compute units while this call runs.
+ *                   free compute units while this call runs. With a cap, a bf16 or fp32 cache is
+ *                   decoded with one tile in flight per wave instead of two (shorter memory
+ *                   queues for the kernels beside it); results are the same bits either way.
  */
 typedef struct {
   const void* q_pre;       /* [B, H_q, head_dim] pre-RoPE queries, in q_dtype                 */

@@ -15,9 +15,12 @@
 // with one head per lane column), an online softmax runs on the 4 logits each lane holds, and the
 // probability tile - already in the operand layout of the next product - is multiplied with the
 // value tile (values are stored token-contiguous inside a page, so each lane reads 4 consecutive
-// tokens of one value row). Tiles are prefetched into a register ring whose slots rotate by
-// unrolling, so no register copy waits on an in-flight load; page ids are fetched 64 tiles at a
-// time, one per lane, a chunk ahead of use.
+// tokens of one value row). Each wave first lists, in its own LDS region, the tiles of up to 256
+// at a time that the pass decodes (page code and tile index, skipped pages left out), then walks
+// the list with a register ring whose slots rotate by unrolling. Every ring slot is refilled
+// unconditionally (past the end with the last entry again, never processed): with loads that
+// depend on no branch, the wait before a tile's products covers that tile's own loads and not
+// the ones issued after it, so the ring's depth is what stays in flight per wave.
 //
 // Mixed-precision caches decode in two passes over the same batch, each leaving partials that
 // the merge combines: the first takes the bf16 and fp8 tiles, the second the INT4 tiles with an
@@ -44,11 +47,20 @@ constexpr int KIND_MIXED = 2;  // a mixed cache's bf16 and fp8 tiles (and INT4 o
 constexpr int KIND_INT4 = 3;   // a mixed cache's INT4 tiles only (the second pass)
 constexpr int MAX_HEADS_PER_WG = 8;
 constexpr int MAX_THREADS = MAX_HEADS_PER_WG * GP_WAVE;
-constexpr int RING = 2;  // tiles in flight per wave
+// Tiles in flight per wave (the register ring's depth). Two keep HBM busiest when the decode has
+// the GPU to itself. A call with a workgroup cap is meant to share the GPU with latency-bound
+// kernels (a boundary pass): there the bf16 / fp32 decode keeps one, because deeper memory queues
+// slow every dependent access of the kernels beside it far more than they speed up the decode.
+constexpr int RING_FULL = 2;
+constexpr int RING_SHARED = 1;
 // The INT4 pass is bound by instruction latency, not bytes: its kernel (126 registers) runs four
 // waves per SIMD, in workgroups of four heads so that four of them fit a compute unit.
 constexpr int INT4_HEADS_PER_WG = 4;
 constexpr int MAX_BATCH = 8191;   // prefix of tile counts kept in LDS (32 KB)
+constexpr int LIST = 256;         // tiles per wave listed in LDS at a time
+
+// LDS ints of the prefix of tile counts, rounded up so that the tile lists start 16-byte aligned
+__host__ __device__ __forceinline__ int pref_ints(int B) { return (B + 1 + 3) & ~3; }
 constexpr int J_CAP_MAX = 127;    // partials one output row can have (the merge holds two per lane)
 
 struct DecodeParams {
@@ -128,7 +140,11 @@ __device__ __forceinline__ int sanitize_ctx(const DecodeParams& p, int r) {
   return ctx;
 }
 
-// Load tile `tok0` (a multiple of 16) of KV head h from the page encoded in `code`.
+// Load tile `tok0` (a multiple of 16) of KV head h from the page encoded in `code`. Loads whose
+// instruction covers whole 128-byte lines (value rows of bf16, fp32 and fp8 pages, INT4 key rows)
+// are streaming loads; key rows read 64 bytes per row per instruction (the other half comes with
+// the next instruction) and the scales keep ordinary loads: a streaming half line can leave the
+// cache before its other half is read, and then the line is fetched twice.
 template <int D, int KIND>
 __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int tok0, int h,
                                           int lane, TileRaw<D, KIND>& t) {
@@ -140,9 +156,9 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
     const size_t kv_base = ((size_t)pg * p.H_kv + h) * (size_t)b * D;
     const uint8_t* kr = p.k4 + kv_base / 2 + (size_t)(off + n16) * (D / 2) + g4 * (D / 8);
     if constexpr (D == 128)
-      t.k = *reinterpret_cast<const u32x4_t*>(kr);
+      t.k = gp::ld_stream<u32x4_t>(kr);
     else
-      *reinterpret_cast<u32x2_t*>(&t.k) = *reinterpret_cast<const u32x2_t*>(kr);
+      *reinterpret_cast<u32x2_t*>(&t.k) = gp::ld_stream<u32x2_t>(kr);
     const uint8_t* vr = p.v4 + kv_base / 2 + (size_t)((off >> 2) + g4) * (2 * D) + n16 * (D / 8);
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) t.v[i] = *reinterpret_cast<const u32x2_t*>(vr + 8 * i);
@@ -157,9 +173,9 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
       // key row (off + n16): this lane's dimensions [g4 D/4, (g4 + 1) D/4) are D/8 bytes
       const uint8_t* kr = p.k4 + kv_base / 2 + (size_t)(off + n16) * (D / 2) + g4 * (D / 8);
       if constexpr (D == 128)
-        t.k[0] = *reinterpret_cast<const u32x4_t*>(kr);
+        t.k[0] = gp::ld_stream<u32x4_t>(kr);
       else
-        *reinterpret_cast<u32x2_t*>(&t.k[0]) = *reinterpret_cast<const u32x2_t*>(kr);
+        *reinterpret_cast<u32x2_t*>(&t.k[0]) = gp::ld_stream<u32x2_t>(kr);
       // value block of tokens off + 4 g4 .. + 3: dimensions 16 i + n16 are D/8 adjacent bytes
       const uint8_t* vr = p.v4 + kv_base / 2 + (size_t)((off >> 2) + g4) * (2 * D) + n16 * (D / 8);
 #pragma unroll
@@ -179,7 +195,7 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
       const uint8_t* vr = p.v8 + kv_base + (size_t)n16 * b + off + 4 * g4;
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb)
-        t.v[nb] = u32x2_t{*reinterpret_cast<const uint32_t*>(vr + (size_t)16 * nb * b), 0u};
+        t.v[nb] = u32x2_t{gp::ld_stream<uint32_t>(vr + (size_t)16 * nb * b), 0u};
       t.ks = *reinterpret_cast<const f32x4_t*>(p.k_scale + sb);
       t.vs = *reinterpret_cast<const f32x4_t*>(p.v_scale + sb);
       return;
@@ -189,7 +205,7 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
     for (int kk = 0; kk < D / 32; ++kk) t.k[kk] = *reinterpret_cast<const u32x4_t*>(kr + 32 * kk);
     const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.v) + kv_base + (size_t)n16 * b + off + 4 * g4;
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) t.v[nb] = *reinterpret_cast<const u32x2_t*>(vr + (size_t)16 * nb * b);
+    for (int nb = 0; nb < D / 16; ++nb) t.v[nb] = gp::ld_stream<u32x2_t>(vr + (size_t)16 * nb * b);
     t.ks = f32x4_t{1.f, 1.f, 1.f, 1.f};
     t.vs = t.ks;
   } else {
@@ -200,14 +216,14 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
       for (int kk = 0; kk < D / 32; ++kk) t.k[kk] = *reinterpret_cast<const u32x4_t*>(kr + 32 * kk);
       const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.v) + kv_base + (size_t)n16 * b + off + 4 * g4;
 #pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb) t.v[nb] = *reinterpret_cast<const u32x2_t*>(vr + (size_t)16 * nb * b);
+      for (int nb = 0; nb < D / 16; ++nb) t.v[nb] = gp::ld_stream<u32x2_t>(vr + (size_t)16 * nb * b);
     } else {
       const float* kr = reinterpret_cast<const float*>(p.k) + kv_base + (size_t)(off + n16) * D + (D / 4) * g4;
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) t.k[i] = *reinterpret_cast<const u32x4_t*>(kr + 4 * i);
       const float* vr = reinterpret_cast<const float*>(p.v) + kv_base + (size_t)n16 * b + off + 4 * g4;
 #pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb) t.v[nb] = *reinterpret_cast<const u32x4_t*>(vr + (size_t)16 * nb * b);
+      for (int nb = 0; nb < D / 16; ++nb) t.v[nb] = gp::ld_stream<u32x4_t>(vr + (size_t)16 * nb * b);
     }
   }
 }
@@ -382,9 +398,9 @@ __device__ __forceinline__ int range_len(const DecodeParams& p, int U) {
   return range_len(p.num_wg, p.r_min, U);
 }
 
-template <int D, int KIND>
+template <int D, int KIND, int RING>
 __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParams p) {
-  extern __shared__ int s_pref[];  // [B + 1]
+  extern __shared__ int s_pref[];  // [B + 1] prefix, then per wave [2][LIST] tile list
   __shared__ int s_wsum[MAX_HEADS_PER_WG];
   const int wg = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -440,6 +456,10 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
     }
   }
 
+  // this wave's tile list in LDS, after the prefix: [LIST] page codes, then [LIST] tiles
+  int* lst_code = s_pref + pref_ints(p.B) + w * 2 * LIST;
+  int* lst_tile = lst_code + LIST;
+
   const int R = range_len(p, U);
   const long u0l = (long)wg * R;
   if (u0l >= U) return;
@@ -461,41 +481,7 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
     const int ctx = sanitize_ctx(p, r);
     u = seg_end;
 
-    // page codes of tiles [c0, c0 + 64) of this segment, one per lane (-1: skipped)
     const int32_t* bt = p.block_tables + (size_t)r * p.max_pages;
-    auto load_codes = [&](int c0) -> int {
-      const int t = c0 + lane;
-      int code = -1;
-      if (t < tb) {
-        const int pg = bt[(t << 4) / b];
-        code = (pg >= 0 && pg < p.num_pages) ? pg : -1;
-        if constexpr (KIND == KIND_MIXED) {
-          // with two passes the INT4 tiles belong to the second one
-          if (code >= 0) {
-            const int tag = p.page_tag[pg];
-            code = (tag == GP_TAG_FP8 || tag == GP_TAG_BF16 || (tag == GP_TAG_INT4 && p.passes == 1))
-                       ? ((pg << 2) | tag) : -1;
-          }
-        } else if constexpr (KIND == KIND_INT4) {
-          if (code >= 0) code = p.page_tag[pg] == GP_TAG_INT4 ? ((pg << 2) | GP_TAG_INT4) : -1;
-        }
-      }
-      return code;
-    };
-    int ca = ta;
-    int ids_a = load_codes(ca);
-    int ids_b = load_codes(ca + 64);
-    // code of tile x; x only grows, and the chunk window slides when x leaves it
-    auto code_of = [&](int x) -> int {
-      if (x - ca >= 64) {
-        ids_a = ids_b;
-        ca += 64;
-        ids_b = load_codes(ca + 64);
-      }
-      const int i = x - ca;
-      return i < 64 ? __builtin_amdgcn_readlane(ids_a, i) : __builtin_amdgcn_readlane(ids_b, i - 64);
-    };
-
     // query operand: head (lane % 16) of this KV head's group, zero rows past G
     const int hq0 = h * G;
     u32x4_t qf[KIND == KIND_F32 ? D / 16 : D / 32];
@@ -533,23 +519,59 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
     st.m_run = -INFINITY;
     st.l_run = 0.f;
 
-    TileRaw<D, KIND> ring[RING];
-    int codes[RING];
-#pragma unroll
-    for (int q = 0; q < RING; ++q) {
-      const int x = ta + q;
-      codes[q] = x < tb ? code_of(x) : -1;
-      if (codes[q] >= 0) load_tile<D, KIND>(p, codes[q], x << 4, h, lane, ring[q]);
-    }
-    for (int base = ta; base < tb; base += RING) {
+    for (int c0 = ta; c0 < tb; c0 += LIST) {
+      // list of the tiles of [c0, c0 + LIST) this pass decodes, in order: page code and tile
+      const int c1 = min(tb, c0 + LIST);
+      int n = 0;
+      for (int k = 0; k < LIST; k += GP_WAVE) {
+        const int t = c0 + k + lane;
+        int code = -1;
+        if (t < c1) {
+          const int pg = bt[(t << 4) / b];
+          code = (pg >= 0 && pg < p.num_pages) ? pg : -1;
+          if constexpr (KIND == KIND_MIXED) {
+            // with two passes the INT4 tiles belong to the second one
+            if (code >= 0) {
+              const int tag = p.page_tag[pg];
+              code = (tag == GP_TAG_FP8 || tag == GP_TAG_BF16 || (tag == GP_TAG_INT4 && p.passes == 1))
+                         ? ((pg << 2) | tag) : -1;
+            }
+          } else if constexpr (KIND == KIND_INT4) {
+            if (code >= 0) code = p.page_tag[pg] == GP_TAG_INT4 ? ((pg << 2) | GP_TAG_INT4) : -1;
+          }
+        }
+        const uint64_t m = __builtin_amdgcn_ballot_w64(code >= 0);
+        if (code >= 0) {
+          const int at = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          lst_code[at] = code;
+          lst_tile[at] = t;
+        }
+        n += __builtin_popcountll(m);
+      }
+      if (n == 0) continue;
+
+      // Register ring over the list. Every slot is reloaded unconditionally (past the end of the
+      // list with the last entry again, which is never processed), so each iteration issues the
+      // same loads and the wait before a tile's products covers that tile's loads only.
+      TileRaw<D, KIND> ring[RING];
+      int rc[RING], rt[RING];
 #pragma unroll
       for (int q = 0; q < RING; ++q) {
-        const int t = base + q;
-        if (t < tb) {
-          if (codes[q] >= 0) process_tile<D, KIND>(p, ring[q], codes[q], t << 4, ctx, lane, qf, qh, st);
-          const int x = t + RING;
-          codes[q] = x < tb ? code_of(x) : -1;
-          if (codes[q] >= 0) load_tile<D, KIND>(p, codes[q], x << 4, h, lane, ring[q]);
+        const int e = min(q, n - 1);
+        rc[q] = __builtin_amdgcn_readfirstlane(lst_code[e]);
+        rt[q] = __builtin_amdgcn_readfirstlane(lst_tile[e]);
+        load_tile<D, KIND>(p, rc[q], rt[q] << 4, h, lane, ring[q]);
+      }
+      for (int e0 = 0; e0 < n; e0 += RING) {
+#pragma unroll
+        for (int q = 0; q < RING; ++q) {
+          const int e = e0 + q;
+          if (e < n) process_tile<D, KIND>(p, ring[q], rc[q], rt[q] << 4, ctx, lane, qf, qh, st);
+          const int ex = min(e + RING, n - 1);
+          rc[q] = __builtin_amdgcn_readfirstlane(lst_code[ex]);
+          rt[q] = __builtin_amdgcn_readfirstlane(lst_tile[ex]);
+          load_tile<D, KIND>(p, rc[q], rt[q] << 4, h, lane, ring[q]);
         }
       }
     }
@@ -697,7 +719,7 @@ Plan plan_for(int B, int max_context) {
 
 // Workgroups of the streaming kernel that fit on the device at once (memoised per device
 // and instantiation; only host-side device properties are cached).
-template <int D, int KIND>
+template <int D, int KIND, int RING>
 int resident_workgroups(int threads, size_t lds) {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -712,7 +734,7 @@ int resident_workgroups(int threads, size_t lds) {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_streamk_kernel<D, KIND>, threads,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_streamk_kernel<D, KIND, RING>, threads,
                                                    lds) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   const int v = cus * per_cu;
@@ -721,12 +743,12 @@ int resident_workgroups(int threads, size_t lds) {
   return v;
 }
 
-template <int D, int KIND>
-int launch_decode(DecodeParams p, int max_workgroups, hipStream_t stream) {
+template <int D, int KIND, int RING>
+int launch_decode_ring(DecodeParams p, int max_workgroups, hipStream_t stream) {
   const int hg = (p.H_kv + p.heads_per_wg - 1) / p.heads_per_wg;
   const int threads = p.heads_per_wg * GP_WAVE;
-  const size_t lds = (size_t)(p.B + 1) * sizeof(int);
-  int total = resident_workgroups<D, KIND>(threads, lds);
+  const size_t lds = ((size_t)pref_ints(p.B) + (size_t)p.heads_per_wg * 2 * LIST) * sizeof(int);
+  int total = resident_workgroups<D, KIND, RING>(threads, lds);
   // a mixed cache decodes in two passes over the same ranges (the bf16 / fp8 tiles, then the
   // INT4 tiles with a deeper ring); both must cut the batch identically
   p.passes = KIND == KIND_MIXED ? 2 : 1;
@@ -737,13 +759,14 @@ int launch_decode(DecodeParams p, int max_workgroups, hipStream_t stream) {
   const int hpw1 = std::min(p.H_kv, INT4_HEADS_PER_WG);
   const int hg1 = (p.H_kv + hpw1 - 1) / hpw1;
   int total1 = 0;
+  const size_t lds1 = ((size_t)pref_ints(p.B) + (size_t)hpw1 * 2 * LIST) * sizeof(int);
   if (p.passes == 2) {
-    total1 = resident_workgroups<D, KIND_INT4>(hpw1 * GP_WAVE, lds);
+    total1 = resident_workgroups<D, KIND_INT4, RING_FULL>(hpw1 * GP_WAVE, lds1);
     if (max_workgroups > 0) total1 = std::min(total1, max_workgroups * (p.heads_per_wg / hpw1));
   }
   p.num_wg_pass[0] = p.num_wg;
   p.num_wg_pass[1] = std::max(1, total1 / hg1);
-  hipLaunchKernelGGL((decode_streamk_kernel<D, KIND>), dim3(p.num_wg, hg), dim3(threads), lds,
+  hipLaunchKernelGGL((decode_streamk_kernel<D, KIND, RING>), dim3(p.num_wg, hg), dim3(threads), lds,
                      stream, p);
   GP_CHECK_LAUNCH();
   if (p.passes == 2) {
@@ -752,7 +775,7 @@ int launch_decode(DecodeParams p, int max_workgroups, hipStream_t stream) {
     p1.q_pre = nullptr;  // the summary update ran in the first pass
     p1.heads_per_wg = hpw1;
     p1.num_wg = p.num_wg_pass[1];
-    hipLaunchKernelGGL((decode_streamk_kernel<D, KIND_INT4>), dim3(p1.num_wg, hg1),
+    hipLaunchKernelGGL((decode_streamk_kernel<D, KIND_INT4, RING_FULL>), dim3(p1.num_wg, hg1),
                        dim3(hpw1 * GP_WAVE), lds, stream, p1);
     GP_CHECK_LAUNCH();
   }
@@ -761,6 +784,16 @@ int launch_decode(DecodeParams p, int max_workgroups, hipStream_t stream) {
                      stream, p);
   GP_CHECK_LAUNCH();
   return GP_OK;
+}
+
+// Ring depth of the call: one tile in flight per wave for a capped bf16 / fp32 decode (one that
+// shares the GPU), two otherwise. Mixed caches always use two.
+template <int D, int KIND>
+int launch_decode(DecodeParams p, int max_workgroups, hipStream_t stream) {
+  if constexpr (KIND == KIND_BF16 || KIND == KIND_F32) {
+    if (max_workgroups > 0) return launch_decode_ring<D, KIND, RING_SHARED>(p, max_workgroups, stream);
+  }
+  return launch_decode_ring<D, KIND, RING_FULL>(p, max_workgroups, stream);
 }
 
 }  // namespace

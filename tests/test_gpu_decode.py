@@ -133,6 +133,34 @@ def test_decode_capped_grids_match_oracle(max_wg):
     assert eo <= TOL[wl.dtype] and el <= TOL[wl.dtype]
 
 
+@pytest.mark.parametrize("cfg", ["1", "2", "3b"])
+def test_decode_ring_depths_give_same_bits(cfg):
+    """A capped call decodes bf16 / fp32 caches with one tile in flight per wave instead of two;
+    both against the oracle. With 8 KV heads the uncapped kernel holds one workgroup per compute
+    unit, so a cap of one workgroup per compute unit keeps the same split of the batch: the same
+    tiles in the same order, hence the same bits."""
+    wl = workload_on_gpu(cfg, "small")
+    cache = gp.KVCache.from_workload(wl)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    o2, l2 = gp.gp_paged_decode_attn_ex(wl.q, cache, wl.block_tables, wl.context_lens,
+                                        wl.max_context, wl.sm_scale)
+    o1, l1 = gp.gp_paged_decode_attn_ex(wl.q, cache, wl.block_tables, wl.context_lens,
+                                        wl.max_context, wl.sm_scale, max_workgroups=cus)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
+                                          npy(wl.block_tables), npy(wl.context_lens),
+                                          wl.page_size, wl.sm_scale)
+    for o, l in ((o1, l1), (o2, l2)):
+        eo, nan_o = maxabs(f64(o), ref_o)
+        el, nan_l = maxabs(l.cpu().numpy(), ref_l)
+        assert not nan_o and not nan_l
+        assert eo <= TOL[wl.dtype] and el <= TOL[wl.dtype]
+    say(f"[ring depths {cfg}] H_kv={wl.H_kv} equal out={torch.equal(o1, o2)} lse={torch.equal(l1, l2)}")
+    if wl.H_kv == 8:
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
 def test_decode_graph_replays():
     """A captured decode (stream-K launch and merge) replays with the eager bits, with eager
     calls between the replays."""
