@@ -4,18 +4,21 @@
 // (PASK App. B.2 / B.5 pages): fp8 and INT4 keys enter as their exact code values with the row
 // scale applied to the dot product, and released tokens are left out of every softmax.
 //
-// Four launches:
+// Three launches:
 //   1. prep:      one wave per boundary request, view and query head: RMS-calibrate the summary
 //                 to q_t and rotate it to the current position (float64 arithmetic, tiny).
 //   2. logits:    matrix-core contraction of every candidate key tile with the 2G calibrated
 //                 summaries of its KV head (keys as the 16-row operand, the 2G summaries as
 //                 columns; bf16 keys meet a hi+lo bf16 split of the fp32 summaries, fp32 keys
 //                 use the fp32 MFMA); logits go to the workspace with per-chunk (max, sum).
-//   3. normalize: softmax of every row and the mean over the G heads of each view.
-//   4. working set: per (request, KV head, view) the p-coverage size, exact on the fp32 weights:
-//                 a binary search over the weight bit patterns (float32 sums per thread,
-//                 float64 across threads) finds the threshold weight, which an exact 160-bit
-//                 fixed-point sum then certifies (and corrects if rounding picked a neighbour).
+//   3. working set: per (request, KV head, view) first the weights: the softmax of each of the
+//                 G query heads' rows and their mean, written to a^S / a^L and kept in
+//                 registers; then the p-coverage size, exact on those fp32 weights: a binary
+//                 search over the weight bit patterns (float32 sums per thread, float64 across
+//                 threads) finds the threshold weight, which an exact 160-bit fixed-point sum
+//                 then certifies (and corrects if rounding picked a neighbour). Normalising in
+//                 the same kernel saves a launch and a write-then-read of the weights, which
+//                 matters most when the pass runs beside a decode that keeps HBM busy.
 #include "common.h"
 
 #include <cmath>
@@ -332,51 +335,7 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
   }
 }
 
-// ------------------------------------------------------------------------------ 3. normalize
-__global__ __launch_bounds__(256) void normalize_kernel(ScoreParams P) {
-  const int blk = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
-  int r;
-  const int n = candidates(P, i, &r);
-  if (n <= 0 || blk * 1024 >= n) return;
-  const int G = P.G;
-  __shared__ float sM[16], sInv[16];
-  const int nchunks = (n + CHUNK_TILES * 16 - 1) / (CHUNK_TILES * 16);  // <= 64
-  // one wave per (view, head) column: lane j holds chunk j's (max, sum)
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int col = w; col < 2 * G; col += 4) {
-    const int x = col / G, g = col % G;
-    const float* st = P.stats + (((size_t)i * 2 + x) * P.H_q + h * G + g) * P.nch * 2;
-    const float mj = lane < nchunks ? st[2 * lane] : -INFINITY;
-    const float lj = lane < nchunks ? st[2 * lane + 1] : 0.f;
-    const float m = gp::wave_max(mj);
-    const float l = gp::wave_sum(lj * gp::safe_exp2_diff(mj, m));
-    if (lane == 0) {
-      sM[col] = m;
-      sInv[col] = l > 0.f ? 1.f / l : 0.f;
-    }
-  }
-  __syncthreads();
-  const int t = blk * 1024 + threadIdx.x * 4;
-  if (t >= n) return;
-  const float invG = 1.0f / (float)G;
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int g = 0; g < G; ++g) {
-      const int c = x * G + g;
-      const f32x4_t z = *reinterpret_cast<const f32x4_t*>(
-          P.logits + (((size_t)i * 2 + x) * P.H_q + h * G + g) * P.C_max + t);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += gp::safe_exp2_diff(z[e], sM[c]) * sInv[c];
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] *= invG;
-    float* dst = (x == 0 ? P.a_short : P.a_long) + ((size_t)i * P.H_kv + h) * P.C_max + t;
-    *reinterpret_cast<f32x4_t*>(dst) = acc;
-  }
-}
-
-// ------------------------------------------------------------------------------ 4. working set
+// ------------------------------------------------------------------------------ 3. working set
 // 160-bit fixed point in units of 2^-149, accumulated as five 32-bit digits held in 64-bit
 // counters (carries are resolved once, after the block reduction).
 struct Acc5 {
@@ -500,18 +459,59 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     return t;
   };
 
-  const float* src = (x == 0 ? P.a_short : P.a_long) + ((size_t)i * P.H_kv + h) * P.C_max;
-  // every load is issued before any is used: indexes past the candidates read candidate 0
-  // (no branch per element) and are zeroed afterwards
-  uint32_t u[WS_VPT];
-#pragma unroll
-  for (int j = 0; j < WS_VPT; ++j) {
-    const int t = threadIdx.x + j * WS_THREADS;
-    u[j] = __float_as_uint(src[t < n ? t : 0]);
+  // ---- this row's weights (GrowPage Sec. 3.2): the softmax over C of each of the G query heads
+  // of KV head h in view x, from the logits and the per-chunk (max, sum) pairs the logits
+  // kernel left, then their mean; written to a^x and kept in registers for the search
+  const int G = P.G;
+  __shared__ float s_m[16], s_inv[16];
+  {
+    // one wave per query head: lane j holds chunk j's (max, sum)
+    const int nchunks = (n + CHUNK_TILES * 16 - 1) / (CHUNK_TILES * 16);  // <= 64
+    if (w < G) {
+      const float* st = P.stats + (((size_t)i * 2 + x) * P.H_q + h * G + w) * P.nch * 2;
+      const float mj = lane < nchunks ? st[2 * lane] : -INFINITY;
+      const float lj = lane < nchunks ? st[2 * lane + 1] : 0.f;
+      const float m = gp::wave_max(mj);
+      const float l = gp::wave_sum(lj * gp::safe_exp2_diff(mj, m));
+      if (lane == 0) {
+        s_m[w] = m;
+        s_inv[w] = l > 0.f ? 1.f / l : 0.f;
+      }
+    }
+    __syncthreads();
   }
+  float* dst = (x == 0 ? P.a_short : P.a_long) + ((size_t)i * P.H_kv + h) * P.C_max;
+  uint32_t u[WS_VPT];
+  {
+    float acc[WS_VPT];
 #pragma unroll
-  for (int j = 0; j < WS_VPT; ++j)
-    u[j] = (int)threadIdx.x + j * WS_THREADS < n ? u[j] & 0x7fffffffu : 0u;
+    for (int j = 0; j < WS_VPT; ++j) acc[j] = 0.f;
+    for (int g = 0; g < G; ++g) {
+      const float* lg = P.logits + (((size_t)i * 2 + x) * P.H_q + h * G + g) * P.C_max;
+      const float m = s_m[g], inv = s_inv[g];
+      // loads in batches of 16, each issued before any is used: indexes past the candidates
+      // read candidate 0 (no branch per element) and are dropped below
+#pragma unroll
+      for (int j0 = 0; j0 < WS_VPT; j0 += 16) {
+        float z[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int t = threadIdx.x + (j0 + j) * WS_THREADS;
+          z[j] = lg[t < n ? t : 0];
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j0 + j] += gp::safe_exp2_diff(z[j], m) * inv;
+      }
+    }
+    const float invG = 1.0f / (float)G;
+#pragma unroll
+    for (int j = 0; j < WS_VPT; ++j) {
+      const int t = threadIdx.x + j * WS_THREADS;
+      const float v = acc[j] * invG;
+      if (t < n) dst[t] = v;
+      u[j] = t < n ? __float_as_uint(v) & 0x7fffffffu : 0u;
+    }
+  }
   double p_f64 = 0.0;
   for (int k = 4; k >= 0; --k) p_f64 = p_f64 * 4294967296.0 + (double)P.p_fixed[k];
   p_f64 = ldexp(p_f64, -149);
@@ -760,8 +760,6 @@ extern "C" int gp_score_and_working_set(const void* q, int q_dtype, int B, int H
     if (D == 64) hipLaunchKernelGGL((logits_kernel<64, false>), lg, dim3(LG_THREADS), 0, s, P);
     else hipLaunchKernelGGL((logits_kernel<128, false>), lg, dim3(LG_THREADS), 0, s, P);
   }
-  GP_CHECK_LAUNCH();
-  hipLaunchKernelGGL(normalize_kernel, dim3((C_max + 1023) / 1024, H_kv, R), dim3(256), 0, s, P);
   GP_CHECK_LAUNCH();
   hipLaunchKernelGGL(working_set_kernel, dim3(2 * H_kv, R), dim3(WS_THREADS), 0, s, P);
   GP_CHECK_LAUNCH();
