@@ -26,6 +26,10 @@ events on the stream it is launched on; `cpu_baseline` is the float64 CPU oracle
 sample of the same workload. `int4_decode` (bf16 workloads, --int4 1) times decode of the same
 batch after every used page has been demoted to INT4 pages by the page quantiser (PASK App. B.5):
 the quantiser call itself, the decode time per launch and its bytes against the same peak.
+`decode_configs` (--decode-configs 1) times one decode call of the whole batch of the tiny,
+long-reasoning (both head shapes), prefix-shared and mixed-precision workloads at full size:
+median time, bytes on the same model (the prefix-shared batch also with each shared token counted
+once), GB/s and the fraction of the 8 TB/s peak.
 """
 import argparse
 import hashlib
@@ -77,6 +81,9 @@ def parse():
     ap.add_argument("--boundary-pass", type=int, default=1,
                     help="also time the boundary pass alone on the long-reasoning, prefix-shared "
                          "and tiny workloads (16- and 256-token pages)")
+    ap.add_argument("--decode-configs", type=int, default=1,
+                    help="also time one decode call of the whole batch on the tiny, long-reasoning, "
+                         "prefix-shared and mixed-precision workloads (GB/s and fraction of peak)")
     ap.add_argument("--copy-probe-gib", type=float, default=1.0,
                     help="size of the plain device copy timed beside the path (HBM reference)")
     return ap.parse_args()
@@ -522,6 +529,61 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
     return res
 
 
+DECODE_CASES = ("1", "3a", "3b", "4", "5")
+
+
+def decode_leg(name, gp, torch, np, reps, make_workload):
+    """One decode call over the whole batch of workload `name` (16-token pages, no grid cap, no
+    fused update), the median of `reps` after 3 warmups with HIP events on the launching stream.
+    Bytes on the decode's byte model: K/V of every visible token in its page's format (released
+    pages none), Q, O, lse, block-table entries, lengths. The prefix-shared batch also reports
+    its unique bytes: each shared token once, as HBM must supply it."""
+    dev = "cuda:0"
+    wl = make_workload(name, "full", device=dev)
+    cache = gp.KVCache.from_workload(wl)
+    B, H_q, d = wl.q.shape
+    out = torch.empty_like(wl.q)
+    lse = torch.empty((B, H_q), dtype=torch.float32, device=dev)
+    n = gp.gp_paged_decode_attn_workspace_size(B, H_q, wl.H_kv, d, wl.page_size, wl.max_context)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    times = []
+    for it in range(reps + 3):
+        ev[0].record()
+        gp.gp_paged_decode_attn(wl.q, cache, wl.block_tables, wl.context_lens, wl.max_context,
+                                wl.sm_scale, out=out, lse=lse, workspace=ws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        if it >= 3:
+            times.append(ev[0].elapsed_time(ev[1]))
+    ms = float(np.median(times))
+
+    class _NoBoundary:
+        R = 0
+        overlap = False
+    by = algorithmic_bytes(wl, _NoBoundary, np)
+    res = dict(workload=WORKLOAD_NAMES[name], batch=int(B),
+               mean_context=round(float(wl.context_lens.float().mean()), 1),
+               decode_ms=round(ms, 4), bytes=by["decode"], kv_bytes=by["decode_kv"],
+               gbps=round(by["decode"] / (ms * 1e-3) / 1e9, 1),
+               frac=round(by["decode"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
+    if name == "4":
+        # shared prefix pages are read by every request; count each (page, slot) token once
+        es = 2
+        ctx = wl.context_lens.cpu().numpy().astype(np.int64)
+        bt = wl.block_tables.cpu().numpy().astype(np.int64)
+        b = wl.page_size
+        toks = np.concatenate([bt[r, np.arange(c) // b] * b + np.arange(c) % b
+                               for r, c in enumerate(ctx) if c > 0])
+        uniq_kv = int(np.unique(toks).size) * wl.H_kv * d * es * 2
+        uniq = by["decode"] - by["decode_kv"] + uniq_kv
+        res.update(unique_bytes=uniq, unique_gbps=round(uniq / (ms * 1e-3) / 1e9, 1),
+                   unique_frac=round(uniq / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
+    del wl, cache, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, path, budget_s, np):
     """The float64 oracle on a bounded sample: decode of whole requests, then the boundary pass
     of boundary requests, until the time budget is used. Returns GB/s on the same byte model."""
@@ -769,6 +831,13 @@ def main():
                   flush=True)
             bpass.append(boundary_leg(name, b, gp, torch, np, 20, make_workload))
 
+    dconf = None
+    if args.decode_configs:
+        dconf = []
+        for name in DECODE_CASES:
+            print(f"[bench] decode of workload {name}", file=sys.stderr, flush=True)
+            dconf.append(decode_leg(name, gp, torch, np, 20, make_workload))
+
     cpu = None
     if args.cpu_seconds > 0:
         print(f"[bench] cpu_baseline (oracle, ~{args.cpu_seconds:.0f} s)", file=sys.stderr,
@@ -808,6 +877,7 @@ def main():
         "boundary": boundary,
         "boundary_pass": bpass,
         "int4_decode": int4,
+        "decode_configs": dconf,
         "single_stream": single,
         "rows_ms": {k: round(v, 4) for k, v in rows_ms.items()},
         "event_ms_per_step": round(event_step_ms, 4),

@@ -705,6 +705,14 @@ struct Plan {
   int r_min, j_max;
 };
 
+// KV heads per workgroup: the largest divisor of H_kv up to `cap`, so that every wave of every
+// workgroup has a head (12 KV heads: two workgroups of 6 rather than 8 + 4 and 4 idle waves).
+int heads_per_workgroup(int H_kv, int cap) {
+  for (int k = std::min(H_kv, cap); k > 1; --k)
+    if (H_kv % k == 0) return k;
+  return 1;
+}
+
 // Ranges hold at least r_min tiles, so one request is spread over at most j_max workgroups.
 Plan plan_for(int B, int max_context) {
   const int max_tiles = (max_context + 15) / 16;
@@ -756,7 +764,7 @@ int launch_decode_ring(DecodeParams p, int max_workgroups, hipStream_t stream) {
   p.num_wg = std::max(1, total / hg);
   p.pass = 0;
   // the INT4 pass has its own geometry: smaller workgroups, so that more waves hide latency
-  const int hpw1 = std::min(p.H_kv, INT4_HEADS_PER_WG);
+  const int hpw1 = heads_per_workgroup(p.H_kv, INT4_HEADS_PER_WG);
   const int hg1 = (p.H_kv + hpw1 - 1) / hpw1;
   int total1 = 0;
   const size_t lds1 = ((size_t)pref_ints(p.B) + (size_t)hpw1 * 2 * LIST) * sizeof(int);
@@ -776,7 +784,7 @@ int launch_decode_ring(DecodeParams p, int max_workgroups, hipStream_t stream) {
     p1.heads_per_wg = hpw1;
     p1.num_wg = p.num_wg_pass[1];
     hipLaunchKernelGGL((decode_streamk_kernel<D, KIND_INT4, RING_FULL>), dim3(p1.num_wg, hg1),
-                       dim3(hpw1 * GP_WAVE), lds, stream, p1);
+                       dim3(hpw1 * GP_WAVE), lds1, stream, p1);
     GP_CHECK_LAUNCH();
   }
   const long rows = (long)p.B * p.H_q;
@@ -869,7 +877,7 @@ int decode_impl(const void* q, int q_dtype, int B, int H_q, const gp_kv_cache* k
   p.num_pages = kv->num_pages;
   p.max_pages = max_pages;
   p.max_context = max_context;
-  p.heads_per_wg = std::min(H_kv, MAX_HEADS_PER_WG);
+  p.heads_per_wg = heads_per_workgroup(H_kv, MAX_HEADS_PER_WG);
   p.r_min = pl.r_min;
   p.j_max = pl.j_max;
   p.scale_log2 = sm_scale * GP_LOG2E;
