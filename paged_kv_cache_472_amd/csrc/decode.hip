@@ -16,8 +16,10 @@
 // probability tile - already in the operand layout of the next product - is multiplied with the
 // value tile (values are stored token-contiguous inside a page, so each lane reads 4 consecutive
 // tokens of one value row). Each wave first lists, in its own LDS region, the tiles of up to 256
-// at a time that the pass decodes (page code and tile index, skipped pages left out), then walks
-// the list with a register ring whose slots rotate by unrolling. Every ring slot is refilled
+// at a time that the pass decodes (page code and tile index, skipped pages left out; the first
+// pass over a mixed cache keeps its bf16 and its fp8 tiles in two lists, each walked with the
+// format fixed at compile time), then walks the list with a register ring whose slots rotate by
+// unrolling. Every ring slot is refilled
 // unconditionally (past the end with the last entry again, never processed): with loads that
 // depend on no branch, the wait before a tile's products covers that tile's own loads and not
 // the ones issued after it, so the ring's depth is what stays in flight per wave.
@@ -145,7 +147,7 @@ __device__ __forceinline__ int sanitize_ctx(const DecodeParams& p, int r) {
 // are streaming loads; key rows read 64 bytes per row per instruction (the other half comes with
 // the next instruction) and the scales keep ordinary loads: a streaming half line can leave the
 // cache before its other half is read, and then the line is fetched twice.
-template <int D, int KIND>
+template <int D, int KIND, int TAGK = -1>
 __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int tok0, int h,
                                           int lane, TileRaw<D, KIND>& t) {
   const int n16 = lane & 15, g4 = lane >> 4;
@@ -166,7 +168,8 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
     *reinterpret_cast<u32x2_t*>(&t.ks) = *reinterpret_cast<const u32x2_t*>(p.k4_scale + sc);
     *reinterpret_cast<u32x2_t*>(&t.vs) = *reinterpret_cast<const u32x2_t*>(p.v4_scale + sc);
   } else if constexpr (KIND == KIND_MIXED) {
-    const int pg = code >> 2, tag = code & 3;
+    // the page format: fixed at compile time when the caller walks a list of one format
+    const int pg = code >> 2, tag = TAGK >= 0 ? TAGK : (code & 3);
     const size_t kv_base = ((size_t)pg * p.H_kv + h) * (size_t)b * D;
     const size_t sb = ((size_t)pg * p.H_kv + h) * b + off + 4 * g4;
     if (tag == GP_TAG_INT4) {
@@ -237,7 +240,7 @@ struct WaveState {
   float m_run, l_run;
 };
 
-template <int D, int KIND>
+template <int D, int KIND, int TAGK = -1>
 __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRaw<D, KIND>& cur,
                                              int code, int tok0, int ctx, int lane,
                                              const u32x4_t* qf, const f16x8_t* qh,
@@ -250,8 +253,9 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
   float ks[4], vs[4];
   if constexpr (KIND == KIND_MIXED || KIND == KIND_INT4) {
     if constexpr (KIND == KIND_MIXED) {
-      fp8 = (code & 3) == GP_TAG_FP8;
-      int4 = (code & 3) == GP_TAG_INT4;
+      const int tag = TAGK >= 0 ? TAGK : (code & 3);
+      fp8 = tag == GP_TAG_FP8;
+      int4 = tag == GP_TAG_INT4;
     }
     if (int4) {
       const uint32_t k01 = __float_as_uint(cur.ks[0]), k23 = __float_as_uint(cur.ks[1]);
@@ -390,6 +394,43 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
 }
 
 
+// Walk n listed tiles (page codes and tile indexes in LDS) with a register ring of RING tiles.
+// Every slot is refilled unconditionally (past the end of the list with the last entry again,
+// which is never processed), so each iteration issues the same loads and the wait before a tile's
+// products covers only that tile's loads. TAGK >= 0: every listed page has that format, so no
+// load depends on a branch either.
+template <int D, int KIND, int RING, int TAGK>
+__device__ __forceinline__ void walk_tiles(const DecodeParams& p, const int* lst_code,
+                                           const int* lst_tile, int n, int h, int lane, int ctx,
+                                           const u32x4_t* qf, const f16x8_t* qh, WaveState<D>& st) {
+  if (n == 0) return;
+  TileRaw<D, KIND> ring[RING];
+  int rc[RING], rt[RING];
+#pragma unroll
+  for (int q = 0; q < RING; ++q) {
+    const int e = min(q, n - 1);
+    rc[q] = __builtin_amdgcn_readfirstlane(lst_code[e]);
+    rt[q] = __builtin_amdgcn_readfirstlane(lst_tile[e]);
+    load_tile<D, KIND, TAGK>(p, rc[q], rt[q] << 4, h, lane, ring[q]);
+  }
+  for (int e0 = 0; e0 < n; e0 += RING) {
+#pragma unroll
+    for (int q = 0; q < RING; ++q) {
+      const int e = e0 + q;
+      if (e < n) process_tile<D, KIND, TAGK>(p, ring[q], rc[q], rt[q] << 4, ctx, lane, qf, qh, st);
+      const int ex = min(e + RING, n - 1);
+      rc[q] = __builtin_amdgcn_readfirstlane(lst_code[ex]);
+      rt[q] = __builtin_amdgcn_readfirstlane(lst_tile[ex]);
+      load_tile<D, KIND, TAGK>(p, rc[q], rt[q] << 4, h, lane, ring[q]);
+    }
+  }
+}
+
+// LDS ints per wave for tile lists: page codes and tile indexes; a mixed cache's first pass keeps
+// its bf16 and fp8 tiles in two lists.
+template <int KIND>
+constexpr int list_ints() { return (KIND == KIND_MIXED ? 4 : 2) * LIST; }
+
 // Tiles per workgroup range: equal shares of the batch's U units, at least r_min.
 __device__ __forceinline__ int range_len(int num_wg, int r_min, int U) {
   return max((U + num_wg - 1) / num_wg, r_min);
@@ -456,9 +497,12 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
     }
   }
 
-  // this wave's tile list in LDS, after the prefix: [LIST] page codes, then [LIST] tiles
-  int* lst_code = s_pref + pref_ints(p.B) + w * 2 * LIST;
+  // this wave's tile lists in LDS, after the prefix: [LIST] page codes, then [LIST] tiles (a
+  // mixed cache's first pass: bf16 tiles there, fp8 tiles in a second pair)
+  int* lst_code = s_pref + pref_ints(p.B) + w * list_ints<KIND>();
   int* lst_tile = lst_code + LIST;
+  int* lst_code2 = lst_tile + LIST;  // used by KIND_MIXED only
+  int* lst_tile2 = lst_code2 + LIST;
 
   const int R = range_len(p, U);
   const long u0l = (long)wg * R;
@@ -522,7 +566,7 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
     for (int c0 = ta; c0 < tb; c0 += LIST) {
       // list of the tiles of [c0, c0 + LIST) this pass decodes, in order: page code and tile
       const int c1 = min(tb, c0 + LIST);
-      int n = 0;
+      int n = 0, n2 = 0;
       for (int k = 0; k < LIST; k += GP_WAVE) {
         const int t = c0 + k + lane;
         int code = -1;
@@ -530,49 +574,42 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
           const int pg = bt[(t << 4) / b];
           code = (pg >= 0 && pg < p.num_pages) ? pg : -1;
           if constexpr (KIND == KIND_MIXED) {
-            // with two passes the INT4 tiles belong to the second one
+            // bf16 and fp8 tiles; INT4 tiles belong to the second pass
             if (code >= 0) {
               const int tag = p.page_tag[pg];
-              code = (tag == GP_TAG_FP8 || tag == GP_TAG_BF16 || (tag == GP_TAG_INT4 && p.passes == 1))
-                         ? ((pg << 2) | tag) : -1;
+              code = (tag == GP_TAG_FP8 || tag == GP_TAG_BF16) ? ((pg << 2) | tag) : -1;
             }
           } else if constexpr (KIND == KIND_INT4) {
             if (code >= 0) code = p.page_tag[pg] == GP_TAG_INT4 ? ((pg << 2) | GP_TAG_INT4) : -1;
           }
         }
-        const uint64_t m = __builtin_amdgcn_ballot_w64(code >= 0);
-        if (code >= 0) {
+        // fp8 tiles of a mixed cache go to the second list
+        const bool second = KIND == KIND_MIXED && code >= 0 && (code & 3) == GP_TAG_FP8;
+        const bool first = code >= 0 && !second;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(first);
+        const uint64_t m2 = __builtin_amdgcn_ballot_w64(second);
+        if (first) {
           const int at = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
           lst_code[at] = code;
           lst_tile[at] = t;
         }
-        n += __builtin_popcountll(m);
-      }
-      if (n == 0) continue;
-
-      // Register ring over the list. Every slot is reloaded unconditionally (past the end of the
-      // list with the last entry again, which is never processed), so each iteration issues the
-      // same loads and the wait before a tile's products covers that tile's loads only.
-      TileRaw<D, KIND> ring[RING];
-      int rc[RING], rt[RING];
-#pragma unroll
-      for (int q = 0; q < RING; ++q) {
-        const int e = min(q, n - 1);
-        rc[q] = __builtin_amdgcn_readfirstlane(lst_code[e]);
-        rt[q] = __builtin_amdgcn_readfirstlane(lst_tile[e]);
-        load_tile<D, KIND>(p, rc[q], rt[q] << 4, h, lane, ring[q]);
-      }
-      for (int e0 = 0; e0 < n; e0 += RING) {
-#pragma unroll
-        for (int q = 0; q < RING; ++q) {
-          const int e = e0 + q;
-          if (e < n) process_tile<D, KIND>(p, ring[q], rc[q], rt[q] << 4, ctx, lane, qf, qh, st);
-          const int ex = min(e + RING, n - 1);
-          rc[q] = __builtin_amdgcn_readfirstlane(lst_code[ex]);
-          rt[q] = __builtin_amdgcn_readfirstlane(lst_tile[ex]);
-          load_tile<D, KIND>(p, rc[q], rt[q] << 4, h, lane, ring[q]);
+        if constexpr (KIND == KIND_MIXED) {
+          if (second) {
+            const int at = n2 + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m2 >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m2, 0u));
+            lst_code2[at] = code;
+            lst_tile2[at] = t;
+          }
         }
+        n += __builtin_popcountll(m);
+        n2 += __builtin_popcountll(m2);
+      }
+      if constexpr (KIND == KIND_MIXED) {
+        walk_tiles<D, KIND, RING, GP_TAG_BF16>(p, lst_code, lst_tile, n, h, lane, ctx, qf, qh, st);
+        walk_tiles<D, KIND, RING, GP_TAG_FP8>(p, lst_code2, lst_tile2, n2, h, lane, ctx, qf, qh, st);
+      } else {
+        walk_tiles<D, KIND, RING, -1>(p, lst_code, lst_tile, n, h, lane, ctx, qf, qh, st);
       }
     }
 
@@ -755,7 +792,7 @@ template <int D, int KIND, int RING>
 int launch_decode_ring(DecodeParams p, int max_workgroups, hipStream_t stream) {
   const int hg = (p.H_kv + p.heads_per_wg - 1) / p.heads_per_wg;
   const int threads = p.heads_per_wg * GP_WAVE;
-  const size_t lds = ((size_t)pref_ints(p.B) + (size_t)p.heads_per_wg * 2 * LIST) * sizeof(int);
+  const size_t lds = ((size_t)pref_ints(p.B) + (size_t)p.heads_per_wg * list_ints<KIND>()) * sizeof(int);
   int total = resident_workgroups<D, KIND, RING>(threads, lds);
   // a mixed cache decodes in two passes over the same ranges (the bf16 / fp8 tiles, then the
   // INT4 tiles with a deeper ring); both must cut the batch identically
@@ -767,7 +804,7 @@ int launch_decode_ring(DecodeParams p, int max_workgroups, hipStream_t stream) {
   const int hpw1 = heads_per_workgroup(p.H_kv, INT4_HEADS_PER_WG);
   const int hg1 = (p.H_kv + hpw1 - 1) / hpw1;
   int total1 = 0;
-  const size_t lds1 = ((size_t)pref_ints(p.B) + (size_t)hpw1 * 2 * LIST) * sizeof(int);
+  const size_t lds1 = ((size_t)pref_ints(p.B) + (size_t)hpw1 * list_ints<KIND_INT4>()) * sizeof(int);
   if (p.passes == 2) {
     total1 = resident_workgroups<D, KIND_INT4, RING_FULL>(hpw1 * GP_WAVE, lds1);
     if (max_workgroups > 0) total1 = std::min(total1, max_workgroups * (p.heads_per_wg / hpw1));
