@@ -47,6 +47,10 @@ constexpr int KIND_F32 = 0;
 constexpr int KIND_BF16 = 1;
 constexpr int KIND_MIXED = 2;  // a mixed cache's bf16 and fp8 tiles (and INT4 ones in one pass)
 constexpr int KIND_INT4 = 3;   // a mixed cache's INT4 tiles only (the second pass)
+constexpr int KIND_FP8 = 4;    // the fp8 tiles of the first pass over a mixed cache (narrow tiles)
+// Tiles in flight per wave over a list of fp8 tiles: an fp8 tile holds half the registers and
+// half the bytes of a bf16 one, so the same registers keep twice as many in flight.
+constexpr int RING_FP8 = 4;
 constexpr int MAX_HEADS_PER_WG = 8;
 constexpr int MAX_THREADS = MAX_HEADS_PER_WG * GP_WAVE;
 // Tiles in flight per wave (the register ring's depth). Two keep HBM busiest when the decode has
@@ -129,6 +133,13 @@ struct TileRaw<D, KIND_MIXED> {
 };
 
 template <int D>
+struct TileRaw<D, KIND_FP8> {
+  u32x2_t k[D / 32];   // 8 key codes of the row per 32-wide k step
+  uint32_t v[D / 16];  // 4 codes (4 tokens) of one value row per 16-row block
+  f32x4_t ks, vs;      // fp32 scales of the lane's 4 tokens
+};
+
+template <int D>
 struct TileRaw<D, KIND_INT4> {
   u32x4_t k;             // the lane's D/4 key codes (D = 64: in .xy)
   u32x2_t v[D / 64];     // 2 bytes (4 tokens) for each of D/16 value dimensions
@@ -167,6 +178,18 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
     const size_t sc = ((size_t)pg * p.H_kv + h) * b + off + 4 * g4;
     *reinterpret_cast<u32x2_t*>(&t.ks) = *reinterpret_cast<const u32x2_t*>(p.k4_scale + sc);
     *reinterpret_cast<u32x2_t*>(&t.vs) = *reinterpret_cast<const u32x2_t*>(p.v4_scale + sc);
+  } else if constexpr (KIND == KIND_FP8) {
+    const int pg = code >> 2;
+    const size_t kv_base = ((size_t)pg * p.H_kv + h) * (size_t)b * D;
+    const size_t sb = ((size_t)pg * p.H_kv + h) * b + off + 4 * g4;
+    const uint8_t* kr = p.k8 + kv_base + (size_t)(off + n16) * D + 8 * g4;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) t.k[kk] = *reinterpret_cast<const u32x2_t*>(kr + 32 * kk);
+    const uint8_t* vr = p.v8 + kv_base + (size_t)n16 * b + off + 4 * g4;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) t.v[nb] = gp::ld_stream<uint32_t>(vr + (size_t)16 * nb * b);
+    t.ks = *reinterpret_cast<const f32x4_t*>(p.k_scale + sb);
+    t.vs = *reinterpret_cast<const f32x4_t*>(p.v_scale + sb);
   } else if constexpr (KIND == KIND_MIXED) {
     // the page format: fixed at compile time when the caller walks a list of one format
     const int pg = code >> 2, tag = TAGK >= 0 ? TAGK : (code & 3);
@@ -249,9 +272,10 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
   const bool tail = tok0 + 16 > ctx;
   // ---- logits: S[token 4*g4 + i][head n16]
   f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-  bool fp8 = false, int4 = KIND == KIND_INT4;
+  constexpr bool SCALED = KIND == KIND_MIXED || KIND == KIND_INT4 || KIND == KIND_FP8;
+  bool fp8 = KIND == KIND_FP8, int4 = KIND == KIND_INT4;
   float ks[4], vs[4];
-  if constexpr (KIND == KIND_MIXED || KIND == KIND_INT4) {
+  if constexpr (SCALED) {
     if constexpr (KIND == KIND_MIXED) {
       const int tag = TAGK >= 0 ? TAGK : (code & 3);
       fp8 = tag == GP_TAG_FP8;
@@ -278,6 +302,14 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
       for (int c = 0; c < 4; ++c)
         sacc = gp::mfma_f32_16x16x4(__uint_as_float(cur.k[i][c]), __uint_as_float(qf[i][c]), sacc);
     }
+  } else if constexpr (KIND == KIND_FP8) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const u32x2_t lo = gp::fp8x4_to_bf16x4(cur.k[kk].x), hi = gp::fp8x4_to_bf16x4(cur.k[kk].y);
+      const u32x4_t kw = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+      sacc = gp::mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, kw),
+                                    __builtin_bit_cast(bf16x8_t, qf[kk]), sacc);
+    }
   } else if (int4) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
@@ -301,7 +333,7 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float z = sacc[i];
-    if constexpr (KIND == KIND_MIXED || KIND == KIND_INT4) z *= ks[i];
+    if constexpr (SCALED) z *= ks[i];
     const bool ok = tok0 + 4 * g4 + i < ctx;
     sv[i] = ok ? z * p.scale_log2 : -INFINITY;
     mx = fmaxf(mx, sv[i]);
@@ -349,20 +381,21 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       pw[i] = pv[i];
-      if constexpr (KIND == KIND_MIXED || KIND == KIND_INT4) pw[i] *= vs[i];
+      if constexpr (SCALED) pw[i] *= vs[i];
     }
-    if constexpr (KIND == KIND_MIXED || KIND == KIND_INT4) {
+    if constexpr (SCALED) {
       // scales of masked tokens may be poison; keep them out of the product
 #pragma unroll
       for (int i = 0; i < 4; ++i) if (pv[i] == 0.f) pw[i] = 0.f;
-      if (int4) {
+      if (KIND != KIND_FP8 && int4) {
         // every INT4 byte decodes to a finite code, so no value masking is needed
         const f16x2_t p02 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(pw[0], pw[2]));
         const f16x2_t p13 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(pw[1], pw[3]));
         const f16x4_t ph = f16x4_t{p02.x, p02.y, p13.x, p13.y};
 #pragma unroll
         for (int nb = 0; nb < D / 16; ++nb) {
-          const uint32_t word = cur.v[nb / 4][(nb / 2) % 2];  // dimension 16 nb + n16: 2 bytes
+          uint32_t word = 0u;  // dimension 16 nb + n16: 2 bytes
+          if constexpr (KIND != KIND_FP8) word = cur.v[nb / 4][(nb / 2) % 2];
           const uint32_t grp = (nb % 2) ? (word >> 16) : word;
           st.acc[nb] = gp::mfma_f16_16x16x16(ph, gp::int4x4_to_f16x4(grp), st.acc[nb]);
         }
@@ -380,9 +413,14 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
       }
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb) {
-        u32x2_t vw = cur.v[nb];
-        if constexpr (KIND == KIND_MIXED) {
-          if (fp8) vw = gp::fp8x4_to_bf16x4(vw.x);
+        u32x2_t vw;
+        if constexpr (KIND == KIND_FP8) {
+          vw = gp::fp8x4_to_bf16x4(cur.v[nb]);
+        } else {
+          vw = cur.v[nb];
+          if constexpr (KIND == KIND_MIXED) {
+            if (fp8) vw = gp::fp8x4_to_bf16x4(vw.x);
+          }
         }
         vw.x &= mlo;
         vw.y &= mhi;
@@ -607,7 +645,7 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
       }
       if constexpr (KIND == KIND_MIXED) {
         walk_tiles<D, KIND, RING, GP_TAG_BF16>(p, lst_code, lst_tile, n, h, lane, ctx, qf, qh, st);
-        walk_tiles<D, KIND, RING, GP_TAG_FP8>(p, lst_code2, lst_tile2, n2, h, lane, ctx, qf, qh, st);
+        walk_tiles<D, KIND_FP8, RING_FP8, -1>(p, lst_code2, lst_tile2, n2, h, lane, ctx, qf, qh, st);
       } else {
         walk_tiles<D, KIND, RING, -1>(p, lst_code, lst_tile, n, h, lane, ctx, qf, qh, st);
       }
