@@ -31,7 +31,10 @@ CASES = [
     (7, 40, 8, 128, 16, "mixed", "bf16"),     # G = 5
     (2000, 8, 8, 64, 16, "tiny", "bf16"),     # many short and empty requests per workgroup
     (1, 8, 2, 128, 32, [32768], "bf16"),      # one long request over many workgroups
-    (4, 24, 12, 128, 16, "mixed", "f32"),     # 12 KV heads: a full and a partial head group
+    (4, 24, 12, 128, 16, "mixed", "f32"),     # 12 KV heads: two workgroups of 6 heads
+    (3, 20, 10, 64, 16, "mixed", "bf16"),     # 10 KV heads: two workgroups of 5
+    (3, 14, 7, 128, 16, "mixed", "bf16"),     # 7 KV heads: one workgroup of 7
+    (2, 22, 11, 64, 16, "mixed", "f32"),      # 11 KV heads: eleven workgroups of one head
 ]
 
 
@@ -55,6 +58,26 @@ def test_decode_shapes(B, H_q, H_kv, d, b, lens, dtype):
     if empty.any():
         assert torch.all(out[torch.as_tensor(empty, device=DEV)] == 0)
         assert torch.all(torch.isneginf(lse[torch.as_tensor(empty, device=DEV)]))
+
+
+@pytest.mark.parametrize("B,H_q,H_kv,d,b,lens,dtype", [c for c in CASES if c[2] in (7, 10, 12, 16)])
+@pytest.mark.parametrize("max_wg", [3, 37])
+def test_decode_shapes_capped(B, H_q, H_kv, d, b, lens, dtype, max_wg):
+    """Capped grids (one tile in flight per wave) over head groupings that are not eight heads."""
+    rng = np.random.default_rng(B * 131 + H_q)
+    L = lens if isinstance(lens, list) else _lens(lens, B, rng)
+    wl = make_decode_case(B, H_q, H_kv, d, b, L, dtype=dtype, seed=B + H_q).to(DEV)
+    out, lse = gp.gp_paged_decode_attn_ex(wl.q, gp.KVCache.from_workload(wl), wl.block_tables,
+                                          wl.context_lens, wl.max_context, wl.sm_scale,
+                                          max_workgroups=max_wg)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
+                                          npy(wl.block_tables), npy(wl.context_lens), b, wl.sm_scale)
+    eo, nan_o = maxabs(f64(out), ref_o)
+    el, nan_l = maxabs(lse.cpu().numpy(), ref_l)
+    say(f"[shapes capped {max_wg}: {B}x{H_q}/{H_kv}x{d} {dtype}] max|out-ref|={eo:.3e} max|lse-ref|={el:.3e}")
+    assert not nan_o and not nan_l
+    assert eo <= TOL[dtype] and el <= TOL[dtype]
 
 
 def test_decode_rejects_too_many_heads_per_kv_head():
