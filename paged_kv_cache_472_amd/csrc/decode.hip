@@ -45,7 +45,7 @@ namespace {
 
 constexpr int KIND_F32 = 0;
 constexpr int KIND_BF16 = 1;
-constexpr int KIND_MIXED = 2;  // a mixed cache's bf16 and fp8 tiles (and INT4 ones in one pass)
+constexpr int KIND_MIXED = 2;  // first pass over a mixed cache: its bf16 tiles, then its fp8 tiles
 constexpr int KIND_INT4 = 3;   // a mixed cache's INT4 tiles only (the second pass)
 constexpr int KIND_FP8 = 4;    // the fp8 tiles of the first pass over a mixed cache (narrow tiles)
 // Tiles in flight per wave over a list of fp8 tiles: an fp8 tile holds half the registers and
@@ -124,15 +124,6 @@ struct TileRaw<D, KIND_BF16> {
 };
 
 template <int D>
-struct TileRaw<D, KIND_MIXED> {
-  u32x4_t k[D / 32];  // bf16: 8 elements; fp8: 8 codes in .xy; INT4: k[0] holds D/4 codes
-  u32x2_t v[D / 16];  // bf16: 4 elements; fp8: 4 codes in .x; INT4: v[0..D/64) hold 2 bytes
-                      // (4 tokens) for each of D/16 dimensions
-  f32x4_t ks, vs;     // per-token scales of the 4 tokens this lane owns (fp8: fp32 values;
-                      // INT4: their 4 half scales in .xy)
-};
-
-template <int D>
 struct TileRaw<D, KIND_FP8> {
   u32x2_t k[D / 32];   // 8 key codes of the row per 32-wide k step
   uint32_t v[D / 16];  // 4 codes (4 tokens) of one value row per 16-row block
@@ -158,7 +149,7 @@ __device__ __forceinline__ int sanitize_ctx(const DecodeParams& p, int r) {
 // are streaming loads; key rows read 64 bytes per row per instruction (the other half comes with
 // the next instruction) and the scales keep ordinary loads: a streaming half line can leave the
 // cache before its other half is read, and then the line is fetched twice.
-template <int D, int KIND, int TAGK = -1>
+template <int D, int KIND>
 __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int tok0, int h,
                                           int lane, TileRaw<D, KIND>& t) {
   const int n16 = lane & 15, g4 = lane >> 4;
@@ -179,7 +170,7 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
     *reinterpret_cast<u32x2_t*>(&t.ks) = *reinterpret_cast<const u32x2_t*>(p.k4_scale + sc);
     *reinterpret_cast<u32x2_t*>(&t.vs) = *reinterpret_cast<const u32x2_t*>(p.v4_scale + sc);
   } else if constexpr (KIND == KIND_FP8) {
-    const int pg = code >> 2;
+    const int pg = code;
     const size_t kv_base = ((size_t)pg * p.H_kv + h) * (size_t)b * D;
     const size_t sb = ((size_t)pg * p.H_kv + h) * b + off + 4 * g4;
     const uint8_t* kr = p.k8 + kv_base + (size_t)(off + n16) * D + 8 * g4;
@@ -190,50 +181,6 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
     for (int nb = 0; nb < D / 16; ++nb) t.v[nb] = gp::ld_stream<uint32_t>(vr + (size_t)16 * nb * b);
     t.ks = *reinterpret_cast<const f32x4_t*>(p.k_scale + sb);
     t.vs = *reinterpret_cast<const f32x4_t*>(p.v_scale + sb);
-  } else if constexpr (KIND == KIND_MIXED) {
-    // the page format: fixed at compile time when the caller walks a list of one format
-    const int pg = code >> 2, tag = TAGK >= 0 ? TAGK : (code & 3);
-    const size_t kv_base = ((size_t)pg * p.H_kv + h) * (size_t)b * D;
-    const size_t sb = ((size_t)pg * p.H_kv + h) * b + off + 4 * g4;
-    if (tag == GP_TAG_INT4) {
-      // key row (off + n16): this lane's dimensions [g4 D/4, (g4 + 1) D/4) are D/8 bytes
-      const uint8_t* kr = p.k4 + kv_base / 2 + (size_t)(off + n16) * (D / 2) + g4 * (D / 8);
-      if constexpr (D == 128)
-        t.k[0] = gp::ld_stream<u32x4_t>(kr);
-      else
-        *reinterpret_cast<u32x2_t*>(&t.k[0]) = gp::ld_stream<u32x2_t>(kr);
-      // value block of tokens off + 4 g4 .. + 3: dimensions 16 i + n16 are D/8 adjacent bytes
-      const uint8_t* vr = p.v4 + kv_base / 2 + (size_t)((off >> 2) + g4) * (2 * D) + n16 * (D / 8);
-#pragma unroll
-      for (int i = 0; i < D / 64; ++i) t.v[i] = *reinterpret_cast<const u32x2_t*>(vr + 8 * i);
-      // the 4 half scales of this lane's tokens (8 bytes, in .xy)
-      *reinterpret_cast<u32x2_t*>(&t.ks) = *reinterpret_cast<const u32x2_t*>(p.k4_scale + sb);
-      *reinterpret_cast<u32x2_t*>(&t.vs) = *reinterpret_cast<const u32x2_t*>(p.v4_scale + sb);
-      return;
-    }
-    if (tag == GP_TAG_FP8) {
-      const uint8_t* kr = p.k8 + kv_base + (size_t)(off + n16) * D + 8 * g4;
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) {
-        const u32x2_t c = *reinterpret_cast<const u32x2_t*>(kr + 32 * kk);
-        t.k[kk] = u32x4_t{c.x, c.y, 0u, 0u};
-      }
-      const uint8_t* vr = p.v8 + kv_base + (size_t)n16 * b + off + 4 * g4;
-#pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb)
-        t.v[nb] = u32x2_t{gp::ld_stream<uint32_t>(vr + (size_t)16 * nb * b), 0u};
-      t.ks = *reinterpret_cast<const f32x4_t*>(p.k_scale + sb);
-      t.vs = *reinterpret_cast<const f32x4_t*>(p.v_scale + sb);
-      return;
-    }
-    const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.k) + kv_base + (size_t)(off + n16) * D + 8 * g4;
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) t.k[kk] = *reinterpret_cast<const u32x4_t*>(kr + 32 * kk);
-    const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.v) + kv_base + (size_t)n16 * b + off + 4 * g4;
-#pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) t.v[nb] = gp::ld_stream<u32x2_t>(vr + (size_t)16 * nb * b);
-    t.ks = f32x4_t{1.f, 1.f, 1.f, 1.f};
-    t.vs = t.ks;
   } else {
     const size_t kv_base = ((size_t)code * p.H_kv + h) * (size_t)b * D;
     if constexpr (KIND == KIND_BF16) {
@@ -263,34 +210,27 @@ struct WaveState {
   float m_run, l_run;
 };
 
-template <int D, int KIND, int TAGK = -1>
+template <int D, int KIND>
 __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRaw<D, KIND>& cur,
-                                             int code, int tok0, int ctx, int lane,
+                                             int tok0, int ctx, int lane,
                                              const u32x4_t* qf, const f16x8_t* qh,
                                              WaveState<D>& st) {
   const int g4 = lane >> 4;
   const bool tail = tok0 + 16 > ctx;
+  // per-token scales of the lane's 4 tokens (fp8: fp32 values; INT4: halves)
+  constexpr bool SCALED = KIND == KIND_INT4 || KIND == KIND_FP8;
+  float ks[4], vs[4];
+  if constexpr (KIND == KIND_INT4) {
+    const uint32_t k01 = __float_as_uint(cur.ks[0]), k23 = __float_as_uint(cur.ks[1]);
+    const uint32_t v01 = __float_as_uint(cur.vs[0]), v23 = __float_as_uint(cur.vs[1]);
+    ks[0] = gp::half_lo(k01); ks[1] = gp::half_hi(k01); ks[2] = gp::half_lo(k23); ks[3] = gp::half_hi(k23);
+    vs[0] = gp::half_lo(v01); vs[1] = gp::half_hi(v01); vs[2] = gp::half_lo(v23); vs[3] = gp::half_hi(v23);
+  } else if constexpr (KIND == KIND_FP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { ks[i] = cur.ks[i]; vs[i] = cur.vs[i]; }
+  }
   // ---- logits: S[token 4*g4 + i][head n16]
   f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-  constexpr bool SCALED = KIND == KIND_MIXED || KIND == KIND_INT4 || KIND == KIND_FP8;
-  bool fp8 = KIND == KIND_FP8, int4 = KIND == KIND_INT4;
-  float ks[4], vs[4];
-  if constexpr (SCALED) {
-    if constexpr (KIND == KIND_MIXED) {
-      const int tag = TAGK >= 0 ? TAGK : (code & 3);
-      fp8 = tag == GP_TAG_FP8;
-      int4 = tag == GP_TAG_INT4;
-    }
-    if (int4) {
-      const uint32_t k01 = __float_as_uint(cur.ks[0]), k23 = __float_as_uint(cur.ks[1]);
-      const uint32_t v01 = __float_as_uint(cur.vs[0]), v23 = __float_as_uint(cur.vs[1]);
-      ks[0] = gp::half_lo(k01); ks[1] = gp::half_hi(k01); ks[2] = gp::half_lo(k23); ks[3] = gp::half_hi(k23);
-      vs[0] = gp::half_lo(v01); vs[1] = gp::half_hi(v01); vs[2] = gp::half_lo(v23); vs[3] = gp::half_hi(v23);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { ks[i] = cur.ks[i]; vs[i] = cur.vs[i]; }
-    }
-  }
   if constexpr (KIND == KIND_INT4) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
@@ -302,27 +242,16 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
       for (int c = 0; c < 4; ++c)
         sacc = gp::mfma_f32_16x16x4(__uint_as_float(cur.k[i][c]), __uint_as_float(qf[i][c]), sacc);
     }
-  } else if constexpr (KIND == KIND_FP8) {
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      const u32x2_t lo = gp::fp8x4_to_bf16x4(cur.k[kk].x), hi = gp::fp8x4_to_bf16x4(cur.k[kk].y);
-      const u32x4_t kw = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-      sacc = gp::mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, kw),
-                                    __builtin_bit_cast(bf16x8_t, qf[kk]), sacc);
-    }
-  } else if (int4) {
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk)
-      sacc = gp::mfma_f16_16x16x32(gp::int4x8_to_f16x8(cur.k[0][kk]), qh[kk], sacc);
   } else {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      u32x4_t kw = cur.k[kk];
-      if constexpr (KIND == KIND_MIXED) {
-        if (fp8) {
-          const u32x2_t lo = gp::fp8x4_to_bf16x4(kw.x), hi = gp::fp8x4_to_bf16x4(kw.y);
-          kw = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-        }
+      u32x4_t kw;
+      if constexpr (KIND == KIND_FP8) {
+        // fp8 codes widen exactly to bf16
+        const u32x2_t lo = gp::fp8x4_to_bf16x4(cur.k[kk].x), hi = gp::fp8x4_to_bf16x4(cur.k[kk].y);
+        kw = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+      } else {
+        kw = cur.k[kk];
       }
       sacc = gp::mfma_bf16_16x16x32(__builtin_bit_cast(bf16x8_t, kw),
                                     __builtin_bit_cast(bf16x8_t, qf[kk]), sacc);
@@ -381,28 +310,23 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       pw[i] = pv[i];
-      if constexpr (SCALED) pw[i] *= vs[i];
-    }
-    if constexpr (SCALED) {
-      // scales of masked tokens may be poison; keep them out of the product
-#pragma unroll
-      for (int i = 0; i < 4; ++i) if (pv[i] == 0.f) pw[i] = 0.f;
-      if (KIND != KIND_FP8 && int4) {
-        // every INT4 byte decodes to a finite code, so no value masking is needed
-        const f16x2_t p02 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(pw[0], pw[2]));
-        const f16x2_t p13 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(pw[1], pw[3]));
-        const f16x4_t ph = f16x4_t{p02.x, p02.y, p13.x, p13.y};
-#pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb) {
-          uint32_t word = 0u;  // dimension 16 nb + n16: 2 bytes
-          if constexpr (KIND != KIND_FP8) word = cur.v[nb / 4][(nb / 2) % 2];
-          const uint32_t grp = (nb % 2) ? (word >> 16) : word;
-          st.acc[nb] = gp::mfma_f16_16x16x16(ph, gp::int4x4_to_f16x4(grp), st.acc[nb]);
-        }
-        return;
+      if constexpr (SCALED) {
+        pw[i] *= vs[i];
+        if (pv[i] == 0.f) pw[i] = 0.f;  // scales of masked tokens may be poison
       }
     }
-    if constexpr (KIND != KIND_INT4) {
+    if constexpr (KIND == KIND_INT4) {
+      // every INT4 byte decodes to a finite code, so no value masking is needed
+      const f16x2_t p02 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(pw[0], pw[2]));
+      const f16x2_t p13 = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_pkrtz(pw[1], pw[3]));
+      const f16x4_t ph = f16x4_t{p02.x, p02.y, p13.x, p13.y};
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) {
+        const uint32_t word = cur.v[nb / 4][(nb / 2) % 2];  // dimension 16 nb + n16: 2 bytes
+        const uint32_t grp = (nb % 2) ? (word >> 16) : word;
+        st.acc[nb] = gp::mfma_f16_16x16x16(ph, gp::int4x4_to_f16x4(grp), st.acc[nb]);
+      }
+    } else {
       const u32x2_t pp = u32x2_t{gp::pack_bf16x2(pw[0], pw[1]), gp::pack_bf16x2(pw[2], pw[3])};
       // values of tokens past the context (the tail of the last page) are masked to zero bits
       uint32_t mlo = 0xffffffffu, mhi = 0xffffffffu;
@@ -414,14 +338,10 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb) {
         u32x2_t vw;
-        if constexpr (KIND == KIND_FP8) {
+        if constexpr (KIND == KIND_FP8)
           vw = gp::fp8x4_to_bf16x4(cur.v[nb]);
-        } else {
+        else
           vw = cur.v[nb];
-          if constexpr (KIND == KIND_MIXED) {
-            if (fp8) vw = gp::fp8x4_to_bf16x4(vw.x);
-          }
-        }
         vw.x &= mlo;
         vw.y &= mhi;
         st.acc[nb] = gp::mfma_bf16_16x16x16(__builtin_bit_cast(i16x4_t, pp),
@@ -435,9 +355,9 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
 // Walk n listed tiles (page codes and tile indexes in LDS) with a register ring of RING tiles.
 // Every slot is refilled unconditionally (past the end of the list with the last entry again,
 // which is never processed), so each iteration issues the same loads and the wait before a tile's
-// products covers only that tile's loads. TAGK >= 0: every listed page has that format, so no
+// products covers only that tile's loads. Every listed page has the format KIND decodes, so no
 // load depends on a branch either.
-template <int D, int KIND, int RING, int TAGK>
+template <int D, int KIND, int RING>
 __device__ __forceinline__ void walk_tiles(const DecodeParams& p, const int* lst_code,
                                            const int* lst_tile, int n, int h, int lane, int ctx,
                                            const u32x4_t* qf, const f16x8_t* qh, WaveState<D>& st) {
@@ -449,17 +369,17 @@ __device__ __forceinline__ void walk_tiles(const DecodeParams& p, const int* lst
     const int e = min(q, n - 1);
     rc[q] = __builtin_amdgcn_readfirstlane(lst_code[e]);
     rt[q] = __builtin_amdgcn_readfirstlane(lst_tile[e]);
-    load_tile<D, KIND, TAGK>(p, rc[q], rt[q] << 4, h, lane, ring[q]);
+    load_tile<D, KIND>(p, rc[q], rt[q] << 4, h, lane, ring[q]);
   }
   for (int e0 = 0; e0 < n; e0 += RING) {
 #pragma unroll
     for (int q = 0; q < RING; ++q) {
       const int e = e0 + q;
-      if (e < n) process_tile<D, KIND, TAGK>(p, ring[q], rc[q], rt[q] << 4, ctx, lane, qf, qh, st);
+      if (e < n) process_tile<D, KIND>(p, ring[q], rt[q] << 4, ctx, lane, qf, qh, st);
       const int ex = min(e + RING, n - 1);
       rc[q] = __builtin_amdgcn_readfirstlane(lst_code[ex]);
       rt[q] = __builtin_amdgcn_readfirstlane(lst_tile[ex]);
-      load_tile<D, KIND, TAGK>(p, rc[q], rt[q] << 4, h, lane, ring[q]);
+      load_tile<D, KIND>(p, rc[q], rt[q] << 4, h, lane, ring[q]);
     }
   }
 }
@@ -580,8 +500,8 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
     }
     // half copy of the query for INT4 pages: step kk of lane (n16, g4) holds dimensions
     // g4 D/4 + 8 kk + (0, 4, 1, 5, 2, 6, 3, 7), the order the lane's key codes unpack in
-    f16x8_t qh[KIND == KIND_MIXED || KIND == KIND_INT4 ? D / 32 : 1];
-    if constexpr (KIND == KIND_MIXED || KIND == KIND_INT4) {
+    f16x8_t qh[KIND == KIND_INT4 ? D / 32 : 1];
+    if constexpr (KIND == KIND_INT4) {
       const uint16_t* qr = reinterpret_cast<const uint16_t*>(p.q) + ((size_t)r * p.H_q + hq0 + n16) * D + (D / 4) * g4;
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
@@ -629,14 +549,15 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
         if (first) {
           const int at = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-          lst_code[at] = code;
+          // a mixed cache's lists hold plain page ids (each list has one format)
+          lst_code[at] = KIND == KIND_MIXED ? code >> 2 : code;
           lst_tile[at] = t;
         }
         if constexpr (KIND == KIND_MIXED) {
           if (second) {
             const int at = n2 + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m2 >> 32),
                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m2, 0u));
-            lst_code2[at] = code;
+            lst_code2[at] = code >> 2;
             lst_tile2[at] = t;
           }
         }
@@ -644,10 +565,11 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
         n2 += __builtin_popcountll(m2);
       }
       if constexpr (KIND == KIND_MIXED) {
-        walk_tiles<D, KIND, RING, GP_TAG_BF16>(p, lst_code, lst_tile, n, h, lane, ctx, qf, qh, st);
-        walk_tiles<D, KIND_FP8, RING_FP8, -1>(p, lst_code2, lst_tile2, n2, h, lane, ctx, qf, qh, st);
+        // bf16 tiles as a bf16 cache's (a scale of 1 changes no bit), then the fp8 tiles
+        walk_tiles<D, KIND_BF16, RING>(p, lst_code, lst_tile, n, h, lane, ctx, qf, qh, st);
+        walk_tiles<D, KIND_FP8, RING_FP8>(p, lst_code2, lst_tile2, n2, h, lane, ctx, qf, qh, st);
       } else {
-        walk_tiles<D, KIND, RING, -1>(p, lst_code, lst_tile, n, h, lane, ctx, qf, qh, st);
+        walk_tiles<D, KIND, RING>(p, lst_code, lst_tile, n, h, lane, ctx, qf, qh, st);
       }
     }
 
