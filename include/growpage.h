@@ -141,7 +141,7 @@ const char* gp_status_string(int status);
  * The 16-token tiles of the whole batch are divided evenly over the resident workgroups; a
  * request spread over several of them is merged from its partials with PASK App. B.5's rule.
  * Limits: B <= 8191, 1 <= H_q / H_kv <= 16, head_dim 64 or 128, page_size a multiple of 16 up to
- * 256. Any H_kv (workgroups take up to 8 KV heads each).
+ * 256. Any H_kv (a workgroup takes the largest divisor of H_kv up to 8 KV heads).
  * INT4 pages are contracted exactly in half precision: the query elements are rounded to half
  * (exact for bf16 values of magnitude 2^-14 .. 65504; larger ones overflow) and the probability
  * weights times the value scales are rounded to half toward zero before the value product.
