@@ -31,6 +31,7 @@ constexpr int CHUNK_TILES = 32;  // 512 candidate tokens per logits workgroup
 constexpr int WS_THREADS = 1024;
 constexpr int WS_VPT = 32;        // weights per thread held in registers (|C| <= 32768)
 constexpr int WS_MAX_C = WS_THREADS * WS_VPT;
+constexpr int WS_TAIL = 256;      // weights left in the search interval when one wave finishes it
 
 struct ScoreParams {
   const void* q;
@@ -419,9 +420,29 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   // Block reductions with one barrier each: wave partials alternate between two scratch
   // buffers, so a buffer is rewritten only after every thread has passed another barrier.
   __shared__ double s_d[2][WS_WAVES];
+  __shared__ double s_dc[2][WS_WAVES];
   __shared__ uint64_t s_u[2][8][WS_WAVES];
   __shared__ uint32_t s_x[2][WS_WAVES];
   int ph = 0;
+  // a float64 sum and an integer count in one barrier
+  auto sum_dc = [&](double v, uint32_t c, uint32_t* c_out) -> double {
+    v = gp::wave_sum_f64(v);
+    const double cw = gp::wave_sum_f64((double)c);
+    if (lane == 0) {
+      s_d[ph][w] = v;
+      s_dc[ph][w] = cw;
+    }
+    __syncthreads();
+    double t = 0.0, tc = 0.0;
+#pragma unroll
+    for (int k = 0; k < WS_WAVES; ++k) {
+      t += s_d[ph][k];
+      tc += s_dc[ph][k];
+    }
+    ph ^= 1;
+    *c_out = (uint32_t)tc;
+    return t;
+  };
   auto sum_d = [&](double v) -> double {
     v = gp::wave_sum_f64(v);
     if (lane == 0) s_d[ph][w] = v;
@@ -539,17 +560,78 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     }
     vmax = max_x(m);
   }
-  // bisection for the largest bit pattern T with mass(weights >= T) >= p
+  // bisection for the largest bit pattern T with mass(weights >= T) >= p. A thread's 32 weights
+  // are summed in float32 (the search only has to land on or next to the threshold; the
+  // certificate below decides exactly), threads in float64. Each block-wide step also counts the
+  // weights at or above its midpoint; once at most WS_TAIL weights lie in [lo, hi), they are
+  // listed in LDS and one wave finishes the search without barriers, the mass at or above hi
+  // entering as a constant.
   uint32_t lo = 1u, hi = vmax + 1u;  // mass(>= lo) >= p holds up to rounding; hi fails
-  while (hi - lo > 1u) {
-    const uint32_t mid = lo + (hi - lo) / 2;
-    // a thread's 32 weights are summed in float32 (the search only has to land on or next to
-    // the threshold; the certificate below decides exactly), threads in float64
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+  uint32_t c_lo = 0u, c_hi = 0u;     // weights >= lo, weights >= hi
+  double m_hi = 0.0;                 // mass of the weights >= hi
 #pragma unroll
-    for (int j = 0; j < WS_VPT; ++j) s4[j & 3] += u[j] >= mid ? __uint_as_float(u[j]) : 0.f;
-    const double s = sum_d((double)(s4[0] + s4[1]) + (double)(s4[2] + s4[3]));
-    if (s >= p_f64) lo = mid; else hi = mid;
+  for (int j = 0; j < WS_VPT; ++j) c_lo += u[j] != 0u;
+  {
+    uint32_t c;
+    (void)sum_dc(0.0, c_lo, &c);
+    c_lo = c;
+  }
+  while (hi - lo > 1u && c_lo - c_hi > (uint32_t)WS_TAIL) {
+    const uint32_t mid = lo + (hi - lo) / 2;
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    uint32_t cm = 0u;
+#pragma unroll
+    for (int j = 0; j < WS_VPT; ++j) {
+      const bool ge = u[j] >= mid;
+      s4[j & 3] += ge ? __uint_as_float(u[j]) : 0.f;
+      cm += ge;
+    }
+    uint32_t c_mid;
+    const double sm = sum_dc((double)(s4[0] + s4[1]) + (double)(s4[2] + s4[3]), cm, &c_mid);
+    if (sm >= p_f64) {
+      lo = mid;
+      c_lo = c_mid;
+    } else {
+      hi = mid;
+      c_hi = c_mid;
+      m_hi = sm;
+    }
+  }
+  if (hi - lo > 1u) {
+    // at most WS_TAIL weights in [lo, hi): list them, then one wave bisects over the list
+    __shared__ float s_tail[WS_TAIL];
+    __shared__ uint32_t s_ntail, s_lo;
+    if (threadIdx.x == 0) s_ntail = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < WS_VPT; ++j) {
+      if (u[j] >= lo && u[j] < hi) {
+        const uint32_t k = atomicAdd(&s_ntail, 1u);
+        if (k < (uint32_t)WS_TAIL) s_tail[k] = __uint_as_float(u[j]);
+      }
+    }
+    __syncthreads();
+    if (w == 0) {
+      const uint32_t nt = min(s_ntail, (uint32_t)WS_TAIL);  // == c_lo - c_hi <= WS_TAIL
+      uint32_t x[WS_TAIL / GP_WAVE];
+#pragma unroll
+      for (int k = 0; k < WS_TAIL / GP_WAVE; ++k) {
+        const uint32_t idx = lane + GP_WAVE * k;
+        x[k] = idx < nt ? __float_as_uint(s_tail[idx]) : 0u;
+      }
+      uint32_t l2 = lo, h2 = hi;
+      while (h2 - l2 > 1u) {
+        const uint32_t mid = l2 + (h2 - l2) / 2;
+        float sl = 0.f;
+#pragma unroll
+        for (int k = 0; k < WS_TAIL / GP_WAVE; ++k) sl += x[k] >= mid ? __uint_as_float(x[k]) : 0.f;
+        const double sm = m_hi + gp::wave_sum_f64((double)sl);
+        if (sm >= p_f64) l2 = mid; else h2 = mid;
+      }
+      if (lane == 0) s_lo = l2;
+    }
+    __syncthreads();
+    lo = s_lo;
   }
   // snap T to the largest present weight <= lo
   uint32_t T;
