@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void prep_kernel(ScoreParams P) {
 }
 
 // ------------------------------------------------------------------------------ 2. logits
-template <int D, bool BF16>
+template <int D, bool BF16, bool MIXED>
 __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
   // heads vary fastest over the grid, so the KV heads of a page (adjacent in HBM) are read by
   // neighbouring workgroups at the same time
@@ -230,8 +230,10 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
     const int tok0 = (tile0 + w + k * LG_WAVES) << 4;
     const bool valid_page = pg >= 0;
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-    if (valid_page && tag != GP_TAG_BF16) {
-      if constexpr (BF16) {
+    // fp8 / INT4 pages exist only in a mixed cache (its own instantiation: a plain cache's kernel
+    // has no load behind this branch, so its waits cover each tile's own loads only)
+    if (MIXED && valid_page && tag != GP_TAG_BF16) {
+      if constexpr (BF16 && MIXED) {
         // fp8 / INT4 keys: the codes are exact bf16 values; the row scale multiplies the
         // finished dot products (rows 4 g4 + e of the tile)
         const size_t row0 = ((size_t)pg * P.H_kv + h) * (size_t)b + tok0 % b;
@@ -303,10 +305,8 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
   for (int k0 = 0; k0 < nt; k0 += 2) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      if (k0 + q < nt) {
-        process(k0 + q, ring[q]);
-        load_plain(k0 + q + 2, ring[q]);
-      }
+      if (k0 + q < nt) process(k0 + q, ring[q]);
+      load_plain(k0 + q + 2, ring[q]);  // past the wave's last tile: the pool's first bytes, unused
     }
   }
   // merge the 4 lanes of each column, then the waves
@@ -835,12 +835,15 @@ extern "C" int gp_score_and_working_set(const void* q, int q_dtype, int B, int H
   hipLaunchKernelGGL(prep_kernel, dim3(R, (2 * H_q + 3) / 4), dim3(256), 0, s, P);
   GP_CHECK_LAUNCH();
   dim3 lg(H_kv, P.nch, R);
-  if (q_dtype == GP_BF16) {
-    if (D == 64) hipLaunchKernelGGL((logits_kernel<64, true>), lg, dim3(LG_THREADS), 0, s, P);
-    else hipLaunchKernelGGL((logits_kernel<128, true>), lg, dim3(LG_THREADS), 0, s, P);
+  if (kv->page_tag) {  // mixed caches are bf16 (checked above)
+    if (D == 64) hipLaunchKernelGGL((logits_kernel<64, true, true>), lg, dim3(LG_THREADS), 0, s, P);
+    else hipLaunchKernelGGL((logits_kernel<128, true, true>), lg, dim3(LG_THREADS), 0, s, P);
+  } else if (q_dtype == GP_BF16) {
+    if (D == 64) hipLaunchKernelGGL((logits_kernel<64, true, false>), lg, dim3(LG_THREADS), 0, s, P);
+    else hipLaunchKernelGGL((logits_kernel<128, true, false>), lg, dim3(LG_THREADS), 0, s, P);
   } else {
-    if (D == 64) hipLaunchKernelGGL((logits_kernel<64, false>), lg, dim3(LG_THREADS), 0, s, P);
-    else hipLaunchKernelGGL((logits_kernel<128, false>), lg, dim3(LG_THREADS), 0, s, P);
+    if (D == 64) hipLaunchKernelGGL((logits_kernel<64, false, false>), lg, dim3(LG_THREADS), 0, s, P);
+    else hipLaunchKernelGGL((logits_kernel<128, false, false>), lg, dim3(LG_THREADS), 0, s, P);
   }
   GP_CHECK_LAUNCH();
   hipLaunchKernelGGL(working_set_kernel, dim3(2 * H_kv, R), dim3(WS_THREADS), 0, s, P);
