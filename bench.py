@@ -776,6 +776,10 @@ def main():
     value = step_bytes / (ms_step * 1e-3) / 1e9
     if single is not None:
         single["value"] = round(step_bytes / (single["ms_per_step"] * 1e-3) / 1e9, 2)
+        # the same decode call with the GPU to itself (no grid cap, two tiles in flight per wave)
+        dec_gbps = (by["decode_main"] + by["summaries"]) / (single["decode_ms"] * 1e-3) / 1e9
+        single["decode_gbps"] = round(dec_gbps, 1)
+        single["decode_frac"] = round(dec_gbps / HBM_PEAK_GBPS, 4)
 
     dec_ms = rows_ms["paged_decode_attn_with_summaries"]
     achieved = (by["decode_main"] + by["summaries_main"]) / (dec_ms * 1e-3) / 1e9
