@@ -140,3 +140,48 @@ def test_compact_or_grow_phases_equal_one_call(cfg):
         assert np.array_equal(k1[i, :, :max(n, 0)], k2[i, :, :max(n, 0)])
     for name in s1:
         assert np.array_equal(s1[name], s2[name]), name
+
+
+def test_fused_capped_full_size_as_benchmarked():
+    """The decode call the benchmark times, at full size: the Qwen3-8B-shaped batch (64 requests,
+    contexts 4096..16384), the summary update of every request but the boundary ones fused in, and
+    the grid capped at the compute units less 32 (one tile in flight per wave). Sampled requests'
+    outputs and the updated summary rows against the float64 oracle."""
+    from gpu_common import gather_pages_to_host, sample_requests
+    wl = workload_on_gpu("2", "full")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    slots = npy(wl.slot_ids).astype(np.int64).copy()
+    slots[npy(wl.req_idx).astype(np.int64)] = -1      # boundary requests update on their own
+    # summary slots start poisoned: initialise them from the first past query, as the bench does
+    gp.gp_update_query_summaries(wl.q_hist[0].contiguous(), wl.slot_ids,
+                                 torch.ones(wl.B, dtype=torch.uint8, device=DEV), wl.qstate,
+                                 wl.beta_s, wl.beta_l)
+    torch.cuda.synchronize()
+    state0 = wl.qstate.clone()
+    out, lse = gp.gp_paged_decode_attn_ex(
+        wl.q, gp.KVCache.from_workload(wl), wl.block_tables, wl.context_lens, wl.max_context,
+        wl.sm_scale,
+        summaries=dict(q_pre=wl.q, slot_ids=torch.as_tensor(slots, dtype=torch.int32, device=DEV),
+                       fresh=torch.zeros(wl.B, dtype=torch.uint8, device=DEV), qstate=wl.qstate,
+                       beta_s=wl.beta_s, beta_l=wl.beta_l),
+        max_workgroups=cus - 32)
+    torch.cuda.synchronize()
+    reqs = sample_requests(wl, 3, seed=11)
+    sub, bt = gather_pages_to_host(wl, reqs)
+    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q[reqs]), f64(sub["k_pool"]), f64(sub["v_pool"]),
+                                          bt, npy(wl.context_lens[reqs]), wl.page_size, wl.sm_scale)
+    eo, nan_o = maxabs(f64(out[reqs]), ref_o)
+    el, nan_l = maxabs(lse[reqs].cpu().numpy(), ref_l)
+    # summary rows of the sampled requests that were updated, and a boundary request's untouched row
+    st_ref = f64(state0)
+    upd = [r for r in reqs if slots[r] >= 0]
+    update_query_summaries(f64(wl.q)[upd], slots[upd], np.zeros(len(upd), dtype=np.uint8), st_ref,
+                           wl.beta_s, wl.beta_l)
+    es, nan_s = maxabs(wl.qstate.cpu().numpy()[slots[upd]], st_ref[slots[upd]])
+    b0 = int(npy(wl.req_idx)[0])
+    s0 = int(npy(wl.slot_ids)[b0])
+    say(f"[fused full as benchmarked, cap {cus - 32}] requests={reqs} max|out-ref|={eo:.3e} "
+        f"max|lse-ref|={el:.3e} max|state-ref|={es:.3e}")
+    assert not (nan_o or nan_l or nan_s)
+    assert eo <= TOL["bf16"] and el <= TOL["bf16"] and es <= TOL["f32"]
+    assert torch.equal(wl.qstate[s0].view(torch.int32), state0[s0].view(torch.int32))
