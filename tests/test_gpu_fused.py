@@ -185,3 +185,60 @@ def test_fused_capped_full_size_as_benchmarked():
     assert not (nan_o or nan_l or nan_s)
     assert eo <= TOL["bf16"] and el <= TOL["bf16"] and es <= TOL["f32"]
     assert torch.equal(wl.qstate[s0].view(torch.int32), state0[s0].view(torch.int32))
+
+
+def test_compact_phases_full_size_qwen3_shaped():
+    """The boundary pass of the benchmarked step at full size: the Qwen3-8B-shaped batch's boundary
+    requests, every one forced to compress, through PLAN then MOVE (gp_compact_or_grow_phase);
+    two of them replayed by the oracle on a copy of their own pages (no page is shared, none is
+    popped): decisions, kept indices, lengths and the K/V bytes of their pages."""
+    from test_gpu_boundary import bits, build_state, c_max_of, run_score
+    from oracle import boundary as ob
+    wl = workload_on_gpu("2", "full")
+    build_state(wl)
+    C_max = c_max_of(wl)
+    a_s, a_l, ws, nc = run_score(wl, C_max=C_max)
+    req = npy(wl.req_idx).tolist()
+    pick = sorted(np.random.default_rng(9).choice(len(req), size=2, replace=False).tolist())
+    sub_req = [req[i] for i in pick]
+    bt_all = npy(wl.block_tables).astype(np.int64)
+    pages = np.unique(bt_all[sub_req][bt_all[sub_req] >= 0])
+    idx = torch.as_tensor(pages, dtype=torch.long, device=DEV)
+    k_before = wl.k_pool.index_select(0, idx).cpu()
+    v_before = wl.v_pool.index_select(0, idx).cpu()
+    ctx_before = npy(wl.context_lens).astype(np.int64)[sub_req].copy()
+    R = len(req)
+    pol = torch.full((R,), ob.POLICY_FORCE_COMPRESS, dtype=torch.int32, device=DEV)
+    cache = gp.KVCache.from_workload(wl)
+    args = (wl.req_idx, a_s, a_l, ws, nc, wl.tau, wl.k_loc, 0, cache, wl.block_tables,
+            wl.n_pages, wl.context_lens, wl.refcount, wl.free_stack, wl.free_top)
+    need = gp.gp_compact_or_grow_workspace_size(R, wl.H_kv, wl.block_tables.shape[1],
+                                                wl.page_size, C_max)
+    wsp = torch.empty(need, dtype=torch.uint8, device=DEV)
+    dec, kept = gp.gp_compact_or_grow(*args, policies=pol, workspace=wsp, phases=1)
+    gp.gp_compact_or_grow(*args, policies=pol, decision=dec, kept_idx=kept, workspace=wsp, phases=2)
+    torch.cuda.synchronize()
+    say(f"[phases full 2] R={R} C_max={C_max} decisions={npy(dec).tolist()}")
+    assert (npy(dec) == ob.COMPRESS).all()
+    remap = {int(p): j for j, p in enumerate(pages)}
+    bt_sub = np.full((len(sub_req), bt_all.shape[1]), -1, dtype=np.int64)
+    for j, r in enumerate(sub_req):
+        bt_sub[j] = [remap[int(p)] if p >= 0 else -1 for p in bt_all[r]]
+    st = dict(k_pool=bits(k_before), v_pool=bits(v_before), block_tables=bt_sub,
+              n_pages=npy(wl.n_pages).astype(np.int64)[sub_req].copy(), context_lens=ctx_before,
+              refcount=np.ones(len(pages), dtype=np.int64),
+              free_stack=np.full(len(pages), -1, dtype=np.int64), free_top=np.zeros(1, np.int64))
+    n_sub = npy(nc).astype(np.int64)[pick]
+    dec_ref, kept_ref = ob.compact_or_grow(
+        list(range(len(sub_req))), npy(a_s)[pick].astype(np.float64),
+        npy(a_l)[pick].astype(np.float64), npy(ws)[pick].astype(np.int64), n_sub, wl.tau, wl.k_loc,
+        ob.POLICY_FORCE_COMPRESS, st["k_pool"], st["v_pool"], st["block_tables"], st["n_pages"],
+        st["context_lens"], st["refcount"], st["free_stack"], st["free_top"], wl.page_size)
+    assert list(dec_ref) == [ob.COMPRESS] * len(sub_req)
+    kp = npy(kept)
+    for j, i in enumerate(pick):
+        n = int(n_sub[j])
+        assert np.array_equal(kp[i, :, :n].astype(np.int64), kept_ref[j, :, :n]), f"kept row {i}"
+        assert int(wl.context_lens[sub_req[j]]) == int(st["context_lens"][j])
+    assert np.array_equal(bits(wl.k_pool.index_select(0, idx)), st["k_pool"])
+    assert np.array_equal(bits(wl.v_pool.index_select(0, idx)), st["v_pool"])
