@@ -138,7 +138,7 @@ class Workload:
 
 
 # --------------------------------------------------------------------------------------------
-# per-config recipes (shapes from the workload descriptions; readings documented in the design doc)
+# per-workload recipes: shapes, dtypes, length mixes and pools of the synthetic workloads
 # --------------------------------------------------------------------------------------------
 
 def _spec(name: str, scale: str) -> dict:
