@@ -50,12 +50,12 @@ PMC_FILE = os.path.join(ROOT, "profiles", "decode_qwen3_8b_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_472_amd", "csrc", "decode.hip")
 
 WORKLOAD_NAMES = {
-    "1": "tiny decode step (B=2, ctx 200/333, Hq=8, Hkv=2, d=64, fp32)",
-    "2": "Qwen3-8B-shaped decode layer (B=64, ctx U[4096,16384], Hq=32, Hkv=8, d=128, b=16, bf16)",
-    "3a": "long-reasoning mix, 8/2 heads d=64 (B=256, lognormal ctx, bf16)",
-    "3b": "long-reasoning mix, 32/8 heads d=128 (B=256, lognormal ctx, bf16)",
-    "4": "prefix-shared batch (B=128, shared 2048 + U[1024,8192], Hq=40, Hkv=8, d=128, bf16)",
-    "5": "mixed-precision pages (B=128, ctx U[8192,24576], 30/40/30 release/fp8/bf16)",
+    "tiny": "tiny decode step (B=2, ctx 200/333, Hq=8, Hkv=2, d=64, fp32)",
+    "qwen3_8b": "Qwen3-8B-shaped decode layer (B=64, ctx U[4096,16384], Hq=32, Hkv=8, d=128, b=16, bf16)",
+    "long_reasoning_d64": "long-reasoning mix, 8/2 heads d=64 (B=256, lognormal ctx, bf16)",
+    "long_reasoning_d128": "long-reasoning mix, 32/8 heads d=128 (B=256, lognormal ctx, bf16)",
+    "prefix_shared": "prefix-shared batch (B=128, shared 2048 + U[1024,8192], Hq=40, Hkv=8, d=128, bf16)",
+    "mixed_precision": "mixed-precision pages (B=128, ctx U[8192,24576], 30/40/30 release/fp8/bf16)",
 }
 
 
@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--workload", default="qwen3_8b", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's timed sample (0 disables the cpu_baseline leg)")
     ap.add_argument("--reserve-cus", type=int, default=32,
@@ -402,7 +402,7 @@ def int4_leg(wl, gp, torch, np, steps):
                 frac=round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
 
 
-BOUNDARY_CASES = (("3b", 16), ("3b", 256), ("3a", 256), ("4", 16), ("1", 16), ("5", 16))
+BOUNDARY_CASES = (("long_reasoning_d128", 16), ("long_reasoning_d128", 256), ("long_reasoning_d64", 256), ("prefix_shared", 16), ("tiny", 16), ("mixed_precision", 16))
 MIXED_BOUNDARY = ("mixed-precision pages, 40/30/30 fp8/bf16/INT4 with none released (B=128, ctx "
                   "U[8192,24576], Hq=32, Hkv=8, d=128, b=16), 16 seeded requests forced to compress")
 MIXED_NAMES = ("k8", "v8", "k_scale", "v_scale", "k4", "v4", "k4_scale", "v4_scale")
@@ -427,7 +427,7 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
         attach_mixed_pools(wl, tags, seed=5)
         wl.req_idx = torch.as_tensor(np.sort(rng.choice(wl.B, size=16, replace=False)),
                                      dtype=torch.int32, device=dev)
-    if name == "4":
+    if name == "prefix_shared":
         # the prefix-shared batch's 8 requests that its own policy compresses (the other 8 grow)
         keep = [k for k, pol in enumerate(wl.req_policy) if pol == 1]
         wl.req_idx = wl.req_idx[keep].contiguous()
@@ -529,7 +529,7 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
     return res
 
 
-DECODE_CASES = ("1", "3a", "3b", "4", "5")
+DECODE_CASES = ("tiny", "long_reasoning_d64", "long_reasoning_d128", "prefix_shared", "mixed_precision")
 
 
 def decode_leg(name, gp, torch, np, reps, make_workload):
@@ -567,7 +567,7 @@ def decode_leg(name, gp, torch, np, reps, make_workload):
                decode_ms=round(ms, 4), bytes=by["decode"], kv_bytes=by["decode_kv"],
                gbps=round(by["decode"] / (ms * 1e-3) / 1e9, 1),
                frac=round(by["decode"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
-    if name == "4":
+    if name == "prefix_shared":
         # shared prefix pages are read by every request; count each (page, slot) token once
         es = 2
         ctx = wl.context_lens.cpu().numpy().astype(np.int64)
@@ -708,8 +708,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = "cuda:0"
-    print(f"[bench] building workload {args.config} on {dev}", file=sys.stderr, flush=True)
-    wl = make_workload(args.config, "full", device=dev)
+    print(f"[bench] building workload {args.workload} on {dev}", file=sys.stderr, flush=True)
+    wl = make_workload(args.workload, "full", device=dev)
     path = Path(wl, gp, torch, overlap=args.overlap, reserve_cus=args.reserve_cus)
     path.build_state()
     torch.cuda.synchronize()
@@ -803,7 +803,7 @@ def main():
     if os.path.exists(PMC_FILE):
         with open(PMC_FILE) as fh:
             pmc = json.load(fh)
-        if (pmc.get("decode_src_sha") == file_sha(DECODE_SRC) and pmc.get("config") == args.config
+        if (pmc.get("decode_src_sha") == file_sha(DECODE_SRC) and pmc.get("workload") == args.workload
                 and pmc.get("overlap", 0) == int(path.overlap)
                 and pmc.get("reserve_cus", 0) == (args.reserve_cus if path.overlap else 0)
                 and pmc.get("decode_call") == "every request, fused summary update"):
@@ -861,7 +861,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if wl.dtype == "f32" else "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[args.config], "batch": wl.B,
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "batch": wl.B,
                    "mean_context": round(float(wl.context_lens.float().mean()), 1),
                    "boundary_requests": path.R, "page_size": wl.page_size},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,

@@ -21,7 +21,7 @@ MIXED_POOLS = ("k8", "v8", "k_scale", "v_scale", "page_tag", "k4", "v4", "k4_sca
 def workload_on_gpu(cfg, scale, page_size=16, int4_frac=0.0):
     """Small workloads are drawn on the CPU and copied (identical values on both sides);
     full-size ones are drawn directly on the GPU."""
-    say(f"[workload] config={cfg} scale={scale} page_size={page_size} int4_frac={int4_frac}")
+    say(f"[workload] {cfg} scale={scale} page_size={page_size} int4_frac={int4_frac}")
     if scale == "small":
         return make_workload(cfg, "small", device="cpu", page_size=page_size,
                              int4_frac=int4_frac).to(DEV)

@@ -1,7 +1,7 @@
 """GPU parity for the page-boundary pass: gp_score_and_working_set and gp_compact_or_grow (HIP,
 through the C ABI) against the float64 / exact-integer oracle.
 
-Protocol: floating-point scores within the config tolerance of the oracle's float64 scores
+Protocol: floating-point scores within the dtype tolerance of the oracle's float64 scores
 (computed from the same query state); working-set counts, decisions, kept indices, block tables,
 page pool and the moved K/V bits compared bit-exactly, with the oracle's integer stages run on
 the GPU's own float32 scores (identical scores, ties to the lower token index).
@@ -124,8 +124,8 @@ def compare_state(wl, st, dec, kept, dec_ref, kept_ref, nc):
         assert np.array_equal(after[name], st[name]), name
 
 
-@pytest.mark.parametrize("cfg,page_size", [("1", 16), ("2", 16), ("3a", 16), ("3b", 16), ("4", 16),
-                                            ("1", 32), ("3a", 32), ("4", 32)])
+@pytest.mark.parametrize("cfg,page_size", [("tiny", 16), ("qwen3_8b", 16), ("long_reasoning_d64", 16), ("long_reasoning_d128", 16), ("prefix_shared", 16),
+                                            ("tiny", 32), ("long_reasoning_d64", 32), ("prefix_shared", 32)])
 def test_score_small(cfg, page_size):
     wl = workload_on_gpu(cfg, "small", page_size)
     build_state(wl)
@@ -133,7 +133,7 @@ def test_score_small(cfg, page_size):
     check_score(wl, a_s, a_l, ws, nc, label=f"small {cfg} b={page_size}")
 
 
-@pytest.mark.parametrize("cfg", ["2", "3a", "3b", "4"])
+@pytest.mark.parametrize("cfg", ["qwen3_8b", "long_reasoning_d64", "long_reasoning_d128", "prefix_shared"])
 def test_score_full_size(cfg):
     wl = workload_on_gpu(cfg, "full")
     build_state(wl)
@@ -143,9 +143,9 @@ def test_score_full_size(cfg):
 
 
 @pytest.mark.parametrize("cfg,policy_mode,page_size", [
-    ("1", "auto", 16), ("2", "auto", 16), ("3a", "auto", 16), ("3b", "auto", 16),
-    ("4", "config", 16), ("4", "auto", 16), ("1", "inverse", 16), ("3a", "compress", 16),
-    ("1", "compress", 32), ("3a", "compress", 32), ("3b", "compress", 32), ("4", "config", 32)])
+    ("tiny", "auto", 16), ("qwen3_8b", "auto", 16), ("long_reasoning_d64", "auto", 16), ("long_reasoning_d128", "auto", 16),
+    ("prefix_shared", "config", 16), ("prefix_shared", "auto", 16), ("tiny", "inverse", 16), ("long_reasoning_d64", "compress", 16),
+    ("tiny", "compress", 32), ("long_reasoning_d64", "compress", 32), ("long_reasoning_d128", "compress", 32), ("prefix_shared", "config", 32)])
 def test_compact_or_grow_small(cfg, policy_mode, page_size):
     wl = workload_on_gpu(cfg, "small", page_size)
     build_state(wl)
@@ -162,7 +162,7 @@ def test_compact_or_grow_small(cfg, policy_mode, page_size):
 
 @pytest.mark.parametrize("tau", [0.001, -0.001, 0.25])
 def test_compact_tau(tau):
-    wl = workload_on_gpu("3b", "small")
+    wl = workload_on_gpu("long_reasoning_d128", "small")
     build_state(wl)
     a_s, a_l, ws, nc = run_score(wl)
     st = host_state(wl)
@@ -171,7 +171,7 @@ def test_compact_tau(tau):
     compare_state(wl, st, dec, kept, dec_ref, kept_ref, nc)
 
 
-@pytest.mark.parametrize("cfg,expect", [("1", ob.GROW_FALLBACK_COMPRESS), ("4", ob.NO_PAGES)])
+@pytest.mark.parametrize("cfg,expect", [("tiny", ob.GROW_FALLBACK_COMPRESS), ("prefix_shared", ob.NO_PAGES)])
 def test_empty_free_pool(cfg, expect):
     wl = workload_on_gpu(cfg, "small")
     build_state(wl)
@@ -186,7 +186,7 @@ def test_empty_free_pool(cfg, expect):
 
 
 def test_compact_deterministic_and_prefix_untouched():
-    wl = workload_on_gpu("4", "small")
+    wl = workload_on_gpu("prefix_shared", "small")
     build_state(wl)
     a_s, a_l, ws, nc = run_score(wl)
     snap = wl.snapshot()

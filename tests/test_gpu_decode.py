@@ -22,9 +22,9 @@ def _run_gpu(wl, q=None, bt=None, ctx=None, max_context=None):
     return out, lse
 
 
-@pytest.mark.parametrize("cfg,page_size", [("1", 16), ("2", 16), ("3a", 16), ("3b", 16), ("4", 16),
-                                            ("5", 16), ("1", 32), ("3a", 32), ("4", 32), ("5", 32),
-                                            ("2", 64)])
+@pytest.mark.parametrize("cfg,page_size", [("tiny", 16), ("qwen3_8b", 16), ("long_reasoning_d64", 16), ("long_reasoning_d128", 16), ("prefix_shared", 16),
+                                            ("mixed_precision", 16), ("tiny", 32), ("long_reasoning_d64", 32), ("prefix_shared", 32), ("mixed_precision", 32),
+                                            ("qwen3_8b", 64)])
 def test_decode_small_elementwise(cfg, page_size):
     wl = workload_on_gpu(cfg, "small", page_size)
     out, lse = _run_gpu(wl)
@@ -39,7 +39,7 @@ def test_decode_small_elementwise(cfg, page_size):
     assert eo <= TOL[wl.dtype] and el <= TOL[wl.dtype]
 
 
-@pytest.mark.parametrize("cfg", ["2", "3a", "3b", "4", "5"])
+@pytest.mark.parametrize("cfg", ["qwen3_8b", "long_reasoning_d64", "long_reasoning_d128", "prefix_shared", "mixed_precision"])
 def test_decode_full_size_sampled(cfg):
     wl = workload_on_gpu(cfg, "full")
     out, lse = _run_gpu(wl)
@@ -59,7 +59,7 @@ def test_decode_full_size_sampled(cfg):
 
 
 def test_decode_deterministic_and_grow_bit_identical():
-    wl = workload_on_gpu("2", "small")
+    wl = workload_on_gpu("qwen3_8b", "small")
     o1, l1 = _run_gpu(wl)
     o2, l2 = _run_gpu(wl)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
@@ -73,7 +73,7 @@ def test_decode_deterministic_and_grow_bit_identical():
 
 
 def test_decode_edge_cases():
-    wl = workload_on_gpu("2", "small")
+    wl = workload_on_gpu("qwen3_8b", "small")
     ctx = wl.context_lens.clone()
     # empty, one token, exactly one page, a page plus one token; plus a huge max_context bound
     ctx[0], ctx[1], ctx[2] = 0, 1, 16
@@ -103,7 +103,7 @@ def test_decode_edge_cases():
 
 def test_decode_lse_and_split_count_independence():
     """The same request decoded with a different split plan (other batch size) agrees."""
-    wl = workload_on_gpu("3b", "small")
+    wl = workload_on_gpu("long_reasoning_d128", "small")
     out, lse = _run_gpu(wl)
     for r in range(wl.B):
         o1, l1 = gp.gp_paged_decode_attn(wl.q[r:r + 1].contiguous(), gp.KVCache.from_workload(wl),
@@ -118,7 +118,7 @@ def test_decode_lse_and_split_count_independence():
 @pytest.mark.parametrize("max_wg", [1, 5, 37, 224])
 def test_decode_capped_grids_match_oracle(max_wg):
     """Grids capped to a few workgroups (ranges long against the batch) against the oracle."""
-    wl = workload_on_gpu("3b", "small")
+    wl = workload_on_gpu("long_reasoning_d128", "small")
     out, lse = gp.gp_paged_decode_attn_ex(wl.q, gp.KVCache.from_workload(wl), wl.block_tables,
                                           wl.context_lens, wl.max_context, wl.sm_scale,
                                           max_workgroups=max_wg)
@@ -133,7 +133,7 @@ def test_decode_capped_grids_match_oracle(max_wg):
     assert eo <= TOL[wl.dtype] and el <= TOL[wl.dtype]
 
 
-@pytest.mark.parametrize("cfg", ["1", "2", "3b"])
+@pytest.mark.parametrize("cfg", ["tiny", "qwen3_8b", "long_reasoning_d128"])
 def test_decode_ring_depths_give_same_bits(cfg):
     """A capped call decodes bf16 / fp32 caches with one tile in flight per wave instead of two;
     both against the oracle. With 8 KV heads the uncapped kernel holds one workgroup per compute
@@ -164,7 +164,7 @@ def test_decode_ring_depths_give_same_bits(cfg):
 def test_decode_graph_replays():
     """A captured decode (stream-K launch and merge) replays with the eager bits, with eager
     calls between the replays."""
-    wl = workload_on_gpu("2", "small")
+    wl = workload_on_gpu("qwen3_8b", "small")
     cache = gp.KVCache.from_workload(wl)
     need = gp.gp_paged_decode_attn_workspace_size(wl.B, wl.H_q, wl.H_kv, wl.q.shape[2],
                                                   wl.page_size, wl.max_context)

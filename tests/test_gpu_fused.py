@@ -36,9 +36,9 @@ def _prime(wl):
                                  wl.beta_s, wl.beta_l)
 
 
-@pytest.mark.parametrize("cfg", ["1", "2", "4", "5"])
+@pytest.mark.parametrize("cfg", ["tiny", "qwen3_8b", "prefix_shared", "mixed_precision"])
 def test_fused_equals_separate_bitwise(cfg):
-    wl = workload_on_gpu(cfg, "small", int4_frac=0.5 if cfg == "5" else 0.0)
+    wl = workload_on_gpu(cfg, "small", int4_frac=0.5 if cfg == "mixed_precision" else 0.0)
     _prime(wl)
     slots, fresh = _slots_and_fresh(wl, 3)
     slot_t = torch.as_tensor(slots, dtype=torch.int32, device=DEV)
@@ -100,7 +100,7 @@ def test_fused_capped_grid_matches_oracle(max_wg):
     assert lens[0] == 0 and bound[0]
 
 
-@pytest.mark.parametrize("cfg", ["1", "3b", "4"])
+@pytest.mark.parametrize("cfg", ["tiny", "long_reasoning_d128", "prefix_shared"])
 def test_compact_or_grow_phases_equal_one_call(cfg):
     """PLAN then MOVE (gp_compact_or_grow_phase) leaves exactly the state of one
     gp_compact_or_grow call: pools, block tables, page pool, decisions and kept indices."""
@@ -148,7 +148,7 @@ def test_fused_capped_full_size_as_benchmarked():
     the grid capped at the compute units less 32 (one tile in flight per wave). Sampled requests'
     outputs and the updated summary rows against the float64 oracle."""
     from gpu_common import gather_pages_to_host, sample_requests
-    wl = workload_on_gpu("2", "full")
+    wl = workload_on_gpu("qwen3_8b", "full")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     slots = npy(wl.slot_ids).astype(np.int64).copy()
     slots[npy(wl.req_idx).astype(np.int64)] = -1      # boundary requests update on their own
@@ -194,7 +194,7 @@ def test_compact_phases_full_size_qwen3_shaped():
     popped): decisions, kept indices, lengths and the K/V bytes of their pages."""
     from test_gpu_boundary import bits, build_state, c_max_of, run_score
     from oracle import boundary as ob
-    wl = workload_on_gpu("2", "full")
+    wl = workload_on_gpu("qwen3_8b", "full")
     build_state(wl)
     C_max = c_max_of(wl)
     a_s, a_l, ws, nc = run_score(wl, C_max=C_max)

@@ -103,7 +103,7 @@ def _run_decode(wl, cache=None):
 
 @pytest.mark.parametrize("page_size,int4_frac", [(16, 0.5), (32, 0.5), (16, 1.0)])
 def test_decode_int4_small_elementwise(page_size, int4_frac):
-    wl = workload_on_gpu("5", "small", page_size, int4_frac=int4_frac)
+    wl = workload_on_gpu("mixed_precision", "small", page_size, int4_frac=int4_frac)
     tags = npy(wl.page_tag)
     used = np.unique(npy(wl.block_tables)[npy(wl.block_tables) >= 0])
     assert set(np.unique(tags[used])) >= {TAG_INT4, TAG_BF16 if int4_frac < 1 else TAG_INT4}
@@ -120,7 +120,7 @@ def test_decode_int4_small_elementwise(page_size, int4_frac):
 
 
 def test_decode_int4_full_size_sampled():
-    wl = workload_on_gpu("5", "full", int4_frac=0.5)
+    wl = workload_on_gpu("mixed_precision", "full", int4_frac=0.5)
     out, lse = _run_decode(wl)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
     reqs = sample_requests(wl, 3)

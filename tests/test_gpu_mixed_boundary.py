@@ -96,10 +96,10 @@ def test_score_mixed_matches_oracle(b, d, pattern):
     assert emax <= TOL["bf16"]
 
 
-def test_score_mixed_full_size_config5():
+def test_score_mixed_full_size():
     """Mixed-precision batch (released / fp8 / bf16 / INT4 pages, contexts 8K-24K): scores of
     eight requests, two of them checked against the oracle."""
-    wl = workload_on_gpu("5", "full", int4_frac=0.5)
+    wl = workload_on_gpu("mixed_precision", "full", int4_frac=0.5)
     wl.req_idx = torch.as_tensor([3, 17, 40, 41, 77, 90, 101, 127], dtype=torch.int32, device=DEV)
     build_state(wl)
     a_s, a_l, ws, nc = run_score(wl)
@@ -121,7 +121,7 @@ def test_score_mixed_full_size_config5():
             e, nan = maxabs(npy(a)[i, :, :n], r[j, :, :n])
             assert not nan
             emax = max(emax, e)
-    say(f"[score mixed full config 5] requests={reqs} max|a-ref|={emax:.3e}")
+    say(f"[score mixed-precision full] requests={reqs} max|a-ref|={emax:.3e}")
     assert emax <= TOL["bf16"]
 
 

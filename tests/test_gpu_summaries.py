@@ -11,8 +11,8 @@ from util import f64, npy
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cfg,scale", [("1", "small"), ("2", "small"), ("3b", "small"),
-                                       ("4", "small"), ("2", "full")])
+@pytest.mark.parametrize("cfg,scale", [("tiny", "small"), ("qwen3_8b", "small"), ("long_reasoning_d128", "small"),
+                                       ("prefix_shared", "small"), ("qwen3_8b", "full")])
 def test_summaries_match_oracle(cfg, scale):
     wl = workload_on_gpu(cfg, scale)
     st_ref = np.full((wl.qstate.shape[0], 2, wl.H_q, wl.d), np.nan)
@@ -36,7 +36,7 @@ def test_summaries_match_oracle(cfg, scale):
 
 
 def test_fresh_slot_overwrites_and_beta_zero():
-    wl = workload_on_gpu("2", "small")
+    wl = workload_on_gpu("qwen3_8b", "small")
     wl.qstate.fill_(123.0)
     fresh = torch.ones(wl.B, dtype=torch.uint8, device=wl.q.device)
     gp.gp_update_query_summaries(wl.q, wl.slot_ids, fresh, wl.qstate, 0.0, 0.999)

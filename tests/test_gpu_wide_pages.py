@@ -19,9 +19,9 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("cfg,policy_mode,page_size", [
-    ("1", "compress", 64), ("1", "auto", 128), ("1", "compress", 256),
-    ("3a", "auto", 256), ("3a", "compress", 256), ("3a", "compress", 64),
-    ("3b", "compress", 256), ("3b", "auto", 128), ("4", "config", 64), ("4", "compress", 128)])
+    ("tiny", "compress", 64), ("tiny", "auto", 128), ("tiny", "compress", 256),
+    ("long_reasoning_d64", "auto", 256), ("long_reasoning_d64", "compress", 256), ("long_reasoning_d64", "compress", 64),
+    ("long_reasoning_d128", "compress", 256), ("long_reasoning_d128", "auto", 128), ("prefix_shared", "config", 64), ("prefix_shared", "compress", 128)])
 def test_compact_wide_small(cfg, policy_mode, page_size):
     wl = workload_on_gpu(cfg, "small", page_size)
     build_state(wl)
@@ -94,7 +94,7 @@ def test_compact_wide_full_size_sampled():
     """Long-reasoning batch (32/8 heads, d = 128, lengths up to 32768) with 256-token pages:
     every boundary request compressed on the GPU; three of them replayed by the oracle on a copy
     of their own pages."""
-    wl = workload_on_gpu("3b", "full", 256)
+    wl = workload_on_gpu("long_reasoning_d128", "full", 256)
     build_state(wl)
     C_max = c_max_of(wl)
     a_s, a_l, ws, nc = run_score(wl, C_max=C_max)

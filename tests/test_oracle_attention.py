@@ -74,7 +74,7 @@ def _contiguous_copy(wl):
     return np.stack(k2), np.stack(v2), bt2
 
 
-@pytest.mark.parametrize("cfg", ["1", "2", "4"])
+@pytest.mark.parametrize("cfg", ["tiny", "qwen3_8b", "prefix_shared"])
 def test_permutation_invariance(cfg):
     wl = make_workload(cfg, "small")
     q = f64(wl.q)
@@ -87,7 +87,7 @@ def test_permutation_invariance(cfg):
     assert np.isfinite(o1).all()
 
 
-@pytest.mark.parametrize("cfg", ["1", "3b"])
+@pytest.mark.parametrize("cfg", ["tiny", "long_reasoning_d128"])
 def test_matches_torch_sdpa_float64(cfg):
     wl = make_workload(cfg, "small")
     q = f64(wl.q)
@@ -134,7 +134,7 @@ def _nibble(byte_array, high):
 
 @pytest.mark.parametrize("int4_frac", [0.0, 0.5])
 def test_released_page_equals_deleting_its_tokens(int4_frac):
-    wl = make_workload("5", "small", int4_frac=int4_frac)
+    wl = make_workload("mixed_precision", "small", int4_frac=int4_frac)
     args = (f64(wl.k_pool), f64(wl.v_pool), npy(wl.block_tables), npy(wl.context_lens),
             wl.page_size)
     mixed = _mixed(wl)
@@ -176,7 +176,7 @@ def test_released_page_equals_deleting_its_tokens(int4_frac):
 def test_int4_page_equals_float_page_of_its_values():
     """Dequantised through the oracle's own unpacking, an INT4 page must give the same output
     as a float page holding code * scale; the values come from arithmetic shifts here."""
-    wl = make_workload("5", "small", int4_frac=1.0)
+    wl = make_workload("mixed_precision", "small", int4_frac=1.0)
     tags = npy(wl.page_tag)
     assert (tags == 3).any()
     kp, vp = f64(wl.k_pool), f64(wl.v_pool)
@@ -202,7 +202,7 @@ def test_int4_page_equals_float_page_of_its_values():
 
 
 def test_all_pages_released_gives_zero():
-    wl = make_workload("5", "small")
+    wl = make_workload("mixed_precision", "small")
     tags = np.zeros_like(npy(wl.page_tag))
     out, lse = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
                                       npy(wl.block_tables), npy(wl.context_lens), wl.page_size,

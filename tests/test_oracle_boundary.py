@@ -124,7 +124,7 @@ def test_theorem_3_1_tight_construction():
 
 # ------------------------------------------------------------------ scores
 def test_scores_are_distributions_and_views_agree_when_equal():
-    wl = make_workload("1", "small")
+    wl = make_workload("tiny", "small")
     st = np.zeros((512, 2, wl.H_q, wl.d))
     q = f64(wl.q)
     update_query_summaries(q, npy(wl.slot_ids), [1] * wl.B, st, 0.9, 0.999)  # both = q_t
@@ -265,11 +265,11 @@ def _check_pool_invariants(wl, st, check_free=True):
         assert st["refcount"][pg] == held.get(pg, 0)                 # refcounts = references
 
 
-@pytest.mark.parametrize("cfg,page_size", [("1", 16), ("3a", 16), ("4", 16), ("3a", 256),
-                                            ("4", 64), ("1", 128)])
+@pytest.mark.parametrize("cfg,page_size", [("tiny", 16), ("long_reasoning_d64", 16), ("prefix_shared", 16), ("long_reasoning_d64", 256),
+                                            ("prefix_shared", 64), ("tiny", 128)])
 def test_compaction_invariants(cfg, page_size):
     wl = make_workload(cfg, "small", page_size=page_size)
-    pol = wl.req_policy if cfg == "4" else None
+    pol = wl.req_policy if cfg == "prefix_shared" else None
     before, st, dec, kept, req, (a_s, a_l, ws, nc) = _run_boundary(wl, policies=pol)
     _check_pool_invariants(wl, before)
     _check_pool_invariants(wl, st)
@@ -304,7 +304,7 @@ def test_compaction_invariants(cfg, page_size):
                 dp, do = st["block_tables"][r, dst // b], dst % b
                 assert np.array_equal(st["k_pool"][dp, h, do], before["k_pool"][sp, h, so])
                 assert np.array_equal(st["v_pool"][dp, h, :, do], before["v_pool"][sp, h, :, so])
-    if cfg == "4":
+    if cfg == "prefix_shared":
         shared = before["block_tables"][0, :wl.shared_pages]
         assert np.array_equal(st["k_pool"][shared], before["k_pool"][shared])
         assert np.array_equal(st["v_pool"][shared], before["v_pool"][shared])
@@ -314,7 +314,7 @@ def test_compaction_invariants(cfg, page_size):
 
 
 def test_grow_leaves_attention_bit_identical():
-    wl = make_workload("4", "small")
+    wl = make_workload("prefix_shared", "small")
     before, st, dec, kept, req, _ = _run_boundary(wl, policies=[ob.POLICY_FORCE_GROW] * 2)
     assert list(dec) == [ob.GROW, ob.GROW]
     args = dict(page_size=wl.page_size, sm_scale=wl.sm_scale)
@@ -326,7 +326,7 @@ def test_grow_leaves_attention_bit_identical():
 
 
 def test_empty_pool_fallback_and_no_pages():
-    wl = make_workload("4", "small")
+    wl = make_workload("prefix_shared", "small")
     # no free page: forced grow falls back to compress, which needs replacement pages for the
     # shared prefix -> NO_PAGES and the request is untouched
     before, st, dec, kept, req, _ = _run_boundary(wl, policies=[ob.POLICY_FORCE_GROW] * 2,
@@ -335,7 +335,7 @@ def test_empty_pool_fallback_and_no_pages():
     for k in ("block_tables", "n_pages", "context_lens", "refcount", "free_top"):
         assert np.array_equal(st[k], before[k])
     assert np.array_equal(st["k_pool"], before["k_pool"], equal_nan=True)
-    wl1 = make_workload("1", "small")
+    wl1 = make_workload("tiny", "small")
     before, st, dec, kept, req, _ = _run_boundary(wl1, policies=[ob.POLICY_FORCE_GROW] * 2,
                                                   free_top=0)
     assert list(dec) == [ob.GROW_FALLBACK_COMPRESS] * 2

@@ -6,7 +6,7 @@ Storage layout produced here (the layout the library consumes):
 * ``v_pool``  ``[num_pages, H_kv, d, b]``   values are stored transposed inside a page
   (``d`` rows of ``b`` tokens), so that the token index is the contiguous axis.
 * mixed-precision pages (GrowPage's companion page on packed KV, PASK B.5, and the fp8 tag of
-  the mixed config): ``k8 [num_pages, H_kv, b, d]`` and ``v8 [num_pages, H_kv, d, b]`` hold
+  the mixed-precision workload): ``k8 [num_pages, H_kv, b, d]`` and ``v8 [num_pages, H_kv, d, b]`` hold
   OCP E4M3FN codes, ``k_scale / v_scale [num_pages, H_kv, b]`` one fp32 scale per token row
   and KV head, and ``page_tag [num_pages]`` (0 released, 1 fp8, 2 bf16, 3 int4).
 * INT4 pages (PASK B.5, present in every mixed workload): ``k4 [num_pages, H_kv, b, d/2]``
@@ -20,7 +20,8 @@ Storage layout produced here (the layout the library consumes):
 * page pool: ``refcount [num_pages]`` and a LIFO ``free_stack [num_pages]`` with ``free_top [1]``.
 * query-state pool ``[M, 2, H_q, d]`` fp32 (GrowPage App. E.1, Eq. 11, one layer).
 
-Draw order (fixed): metadata from ``numpy.random.Generator(PCG64(1000 + c))``; bulk tensors
+Draw order (fixed), with c = ``WORKLOAD_SEED[name]``: metadata from
+``numpy.random.Generator(PCG64(1000 + c))``; bulk tensors
 from ``torch.Generator(device).manual_seed(1000 + c)`` in the order q, q_hist, K, V, K8, V8 and,
 with ``int4_frac > 0``, K4, V4, K4 scales, V4 scales; the INT4 page choice comes from its own
 ``numpy.random.Generator(PCG64(1000 + c + 7919))`` so that the other draws do not move.
@@ -41,7 +42,12 @@ DTYPE_BF16 = "bf16"
 
 TAG_RELEASE, TAG_FP8, TAG_BF16, TAG_INT4 = 0, 1, 2, 3
 
-CONFIG_NAMES = ("1", "2", "3a", "3b", "4", "5")
+WORKLOAD_NAMES = ("tiny", "qwen3_8b", "long_reasoning_d64", "long_reasoning_d128", "prefix_shared",
+                  "mixed_precision")
+# seed number c of each workload (its draws come from SEED_BASE + c; the two long-reasoning head
+# shapes share one)
+WORKLOAD_SEED = {"tiny": 1, "qwen3_8b": 2, "long_reasoning_d64": 3, "long_reasoning_d128": 3,
+                 "prefix_shared": 4, "mixed_precision": 5}
 SEED_BASE = 1000
 NUM_SLOTS = 512          # max_num_seqs of the query-state pool (GrowPage App. E.1)
 PAST_QUERIES = 32
@@ -87,7 +93,7 @@ class Workload:
     v4: Optional[torch.Tensor] = None
     k4_scale: Optional[torch.Tensor] = None
     v4_scale: Optional[torch.Tensor] = None
-    # method parameters for this config
+    # method parameters for this workload
     beta_s: float = 0.9
     beta_l: float = 0.999
     p: float = 0.99
@@ -143,29 +149,29 @@ class Workload:
 
 def _spec(name: str, scale: str) -> dict:
     small = scale == "small"
-    if name == "1":
+    if name == "tiny":
         return dict(B=2, H_q=8, H_kv=2, d=64, dtype=DTYPE_F32, lens=("fixed", [200, 333]),
                     pool=("fixed", 64), beta_s=0.5, beta_l=0.99, p=0.9, boundary=("all",))
-    if name == "2":
+    if name == "qwen3_8b":
         return dict(B=3 if small else 64, H_q=32, H_kv=8, d=128, dtype=DTYPE_BF16,
                     lens=("uniform", 300, 1200) if small else ("uniform", 4096, 16384),
                     pool=("ratio", 1.25), sinks=0.01, boundary=("frac", 1 / 16, 1))
-    if name in ("3a", "3b"):
-        heads = dict(H_q=8, H_kv=2, d=64) if name == "3a" else dict(H_q=32, H_kv=8, d=128)
+    if name in ("long_reasoning_d64", "long_reasoning_d128"):
+        heads = dict(H_q=8, H_kv=2, d=64) if name == "long_reasoning_d64" else dict(H_q=32, H_kv=8, d=128)
         return dict(B=4 if small else 256, dtype=DTYPE_BF16, **heads,
                     lens=("lognormal", 1024, 0.5, 200, 2048) if small
                     else ("lognormal", 8192, 1.0, 512, 32768),
                     pool=("ratio", 1.25), capacity=(0.25, 1.0), boundary=("frac", 1 / 16, 2))
-    if name == "4":
+    if name == "prefix_shared":
         return dict(B=4 if small else 128, H_q=40, H_kv=8, d=128, dtype=DTYPE_BF16,
                     shared=64 if small else 2048,
                     lens=("uniform", 100, 400) if small else ("uniform", 1024, 8192),
                     pool=("ratio", 1.25), boundary=("prefix", 1 if small else 8))
-    if name == "5":
+    if name == "mixed_precision":
         return dict(B=3 if small else 128, H_q=32, H_kv=8, d=128, dtype=DTYPE_BF16, mixed=True,
                     lens=("uniform", 300, 1200) if small else ("uniform", 8192, 24576),
                     pool=("ratio", 1.25), boundary=("none",))
-    raise ValueError(f"unknown config {name!r}")
+    raise ValueError(f"unknown workload {name!r}")
 
 
 def _randn(gen: torch.Generator, shape, device) -> torch.Tensor:
@@ -180,15 +186,14 @@ def _nan_fill_pages(pool: torch.Tensor, pages: np.ndarray) -> None:
 
 def make_workload(name: str, scale: str = "full", device="cpu", seed_offset: int = 0,
                   page_size: int = 16, int4_frac: float = 0.0) -> Workload:
-    """Build config ``name`` ("1", "2", "3a", "3b", "4", "5") at ``scale`` ("full"/"small").
+    """Build workload ``name`` (one of WORKLOAD_NAMES) at ``scale`` ("full"/"small").
 
-    ``int4_frac`` (mixed configs only): share of the bf16 pages turned into INT4 pages.
+    ``int4_frac`` (mixed-precision workload only): share of the bf16 pages turned into INT4 pages.
     """
-    if name not in CONFIG_NAMES:
-        raise ValueError(f"unknown config {name!r}")
+    if name not in WORKLOAD_NAMES:
+        raise ValueError(f"unknown workload {name!r}")
     sp = _spec(name, scale)
-    cfg_num = int(name[0])
-    seed = SEED_BASE + cfg_num + seed_offset
+    seed = SEED_BASE + WORKLOAD_SEED[name] + seed_offset
     rng = np.random.Generator(np.random.PCG64(seed))
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
