@@ -417,6 +417,9 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     return;
   }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // weights per thread that can be candidates: the rest of a thread's 32 slots hold zeros, which
+  // no sum, count or maximum below depends on, so the loops skip them (a uniform bound)
+  const int nv = (n + WS_THREADS - 1) / WS_THREADS;
   // Block reductions with one barrier each: wave partials alternate between two scratch
   // buffers, so a buffer is rewritten only after every thread has passed another barrier.
   __shared__ double s_d[2][WS_WAVES];
@@ -518,10 +521,11 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int t = threadIdx.x + (j0 + j) * WS_THREADS;
-          z[j] = lg[t < n ? t : 0];
+          z[j] = j0 + j < nv ? lg[t < n ? t : 0] : 0.f;
         }
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[j0 + j] += gp::safe_exp2_diff(z[j], m) * inv;
+        for (int j = 0; j < 16; ++j)
+          if (j0 + j < nv) acc[j0 + j] += gp::safe_exp2_diff(z[j], m) * inv;
       }
     }
     const float invG = 1.0f / (float)G;
@@ -544,8 +548,10 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     uint32_t m = 0u;
 #pragma unroll
     for (int j = 0; j < WS_VPT; ++j) {
-      acc_add(a, u[j]);
-      m = max(m, u[j]);
+      if (j < nv) {
+        acc_add(a, u[j]);
+        m = max(m, u[j]);
+      }
     }
     uint64_t t[8] = {a.d[0], a.d[1], a.d[2], a.d[3], a.d[4], a.d[5], 0ull, 0ull};
     sum_u8(t);
@@ -570,7 +576,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   uint32_t c_lo = 0u, c_hi = 0u;     // weights >= lo, weights >= hi
   double m_hi = 0.0;                 // mass of the weights >= hi
 #pragma unroll
-  for (int j = 0; j < WS_VPT; ++j) c_lo += u[j] != 0u;
+  for (int j = 0; j < WS_VPT; ++j) c_lo += j < nv && u[j] != 0u;
   {
     uint32_t c;
     (void)sum_dc(0.0, c_lo, &c);
@@ -582,9 +588,11 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     uint32_t cm = 0u;
 #pragma unroll
     for (int j = 0; j < WS_VPT; ++j) {
-      const bool ge = u[j] >= mid;
-      s4[j & 3] += ge ? __uint_as_float(u[j]) : 0.f;
-      cm += ge;
+      if (j < nv) {
+        const bool ge = u[j] >= mid;
+        s4[j & 3] += ge ? __uint_as_float(u[j]) : 0.f;
+        cm += ge;
+      }
     }
     uint32_t c_mid;
     const double sm = sum_dc((double)(s4[0] + s4[1]) + (double)(s4[2] + s4[3]), cm, &c_mid);
@@ -605,7 +613,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < WS_VPT; ++j) {
-      if (u[j] >= lo && u[j] < hi) {
+      if (j < nv && u[j] >= lo && u[j] < hi) {
         const uint32_t k = atomicAdd(&s_ntail, 1u);
         if (k < (uint32_t)WS_TAIL) s_tail[k] = __uint_as_float(u[j]);
       }
@@ -638,7 +646,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   {
     uint32_t best = 0u;
 #pragma unroll
-    for (int j = 0; j < WS_VPT; ++j) if (u[j] <= lo) best = max(best, u[j]);
+    for (int j = 0; j < WS_VPT; ++j) if (j < nv && u[j] <= lo) best = max(best, u[j]);
     T = max_x(best);
   }
   // exact certificate: mass(> T) < p <= mass(>= T); move T to a neighbour value until it holds
@@ -647,6 +655,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     uint32_t cgt = 0, ceq = 0;
 #pragma unroll 4
     for (int j = 0; j < WS_VPT; ++j) {
+      if (j >= nv) continue;
       if (u[j] > T) {
         acc_add(gt, u[j]);
         ++cgt;
@@ -670,7 +679,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
       // too high: next smaller present value
       uint32_t best = 0u;
 #pragma unroll
-      for (int j = 0; j < WS_VPT; ++j) if (u[j] < T) best = max(best, u[j]);
+      for (int j = 0; j < WS_VPT; ++j) if (j < nv && u[j] < T) best = max(best, u[j]);
       T = max_x(best);
       continue;
     }
@@ -678,7 +687,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
       // too low: next larger present value
       uint32_t best = 0u;
 #pragma unroll
-      for (int j = 0; j < WS_VPT; ++j) if (u[j] > T) best = max(best, ~u[j]);
+      for (int j = 0; j < WS_VPT; ++j) if (j < nv && u[j] > T) best = max(best, ~u[j]);
       T = ~max_x(best);
       continue;
     }
