@@ -179,7 +179,7 @@ class Path:
 
     def step(self, ev=None):
         wl, gp = self.wl, self.gp
-        rec = (lambda k: ev[k].record()) if ev is not None else (lambda k: None)
+        rec = (lambda k: ev[k] is not None and ev[k].record()) if ev is not None else (lambda k: None)
         rec(0)
         self.meta.copy_(self.meta0)
         rec(1)
@@ -218,7 +218,7 @@ class Path:
         wl, gp, torch = self.wl, self.gp, self.torch
         main = torch.cuda.current_stream()
         sb = self.stream_b
-        rec = (lambda k, st: ev[k].record(st)) if ev is not None else (lambda k, st: None)
+        rec = (lambda k, st: ev[k] is not None and ev[k].record(st)) if ev is not None else (lambda k, st: None)
         rec(0, main)
         self.meta.copy_(self.meta0)
         rec(1, main)
@@ -262,7 +262,7 @@ class Path:
         wl, gp, torch = self.wl, self.gp, self.torch
         main = torch.cuda.current_stream()
         sb = self.stream_b
-        rec = (lambda k, st: ev[k].record(st)) if ev is not None else (lambda k, st: None)
+        rec = (lambda k, st: ev[k] is not None and ev[k].record(st)) if ev is not None else (lambda k, st: None)
         rec(0, main)
         self.meta.copy_(self.meta0)
         rec(1, main)
@@ -721,15 +721,30 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    # The timed steps record only the two events around the main decode call (the roofline's):
+    # every other event adds a marker between the step's launches (about 11 us per step in all).
+    # The per-row breakdown comes from a second run of the same steps with every event.
+    dec_a, dec_z = {0: (2, 3), 1: (1, 3), 2: (3, 4)}[path.mode]
+    timed = [[torch.cuda.Event(enable_timing=True) if j in (dec_a, dec_z) else None
+              for j in range(nev)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(events[k])
+        step(timed[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = sum(timed[k][dec_a].elapsed_time(timed[k][dec_z]) for k in range(args.steps)) / args.steps
+    # K/V the last timed step's compaction moved (pages keep what earlier steps wrote, so the
+    # amount drifts a little from step to step)
+    moved = moved_bytes(wl, path, ctx_before, np)
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    print(f"[bench] per-row breakdown, {args.steps} instrumented steps", file=sys.stderr, flush=True)
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
 
     def avg_ms(a, z):
         return sum(events[k][a].elapsed_time(events[k][z]) for k in range(args.steps)) / args.steps
@@ -756,22 +771,29 @@ def main():
     if path.overlap:
         # the same rows one after another on one stream, for reference
         print(f"[bench] single-stream reference, {args.steps} steps", file=sys.stderr, flush=True)
-        ev1 = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+        # (timed with the decode bracket only, like the main steps; rows from a second run)
+        tm1 = [[torch.cuda.Event(enable_timing=True) if j in (2, 3) else None for j in range(6)]
+               for _ in range(args.steps)]
         for _ in range(2):
             path.step()
         torch.cuda.synchronize()
         s0 = time.perf_counter()
         for k in range(args.steps):
-            path.step(ev1[k])
+            path.step(tm1[k])
         torch.cuda.synchronize()
         ms1 = (time.perf_counter() - s0) * 1e3 / args.steps
+        dec1 = sum(tm1[k][2].elapsed_time(tm1[k][3]) for k in range(args.steps)) / args.steps
+        ev1 = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+        for k in range(args.steps):
+            path.step(ev1[k])
+        torch.cuda.synchronize()
         a1 = lambda i, j: sum(ev1[k][i].elapsed_time(ev1[k][j]) for k in range(args.steps)) / args.steps  # noqa: E731
-        single = dict(ms_per_step=round(ms1, 4), decode_ms=round(a1(2, 3), 4),
+        single = dict(ms_per_step=round(ms1, 4), decode_ms=round(dec1, 4),
                       score_us=round(a1(3, 4) * 1e3, 1), compact_us=round(a1(4, 5) * 1e3, 1),
                       boundary_us_per_request=round((a1(3, 5)) * 1e3 / path.R, 1))
 
     by = algorithmic_bytes(wl, path, np)
-    by["compact"] = moved_bytes(wl, path, ctx_before, np)
+    by["compact"] = moved
     step_bytes = by["decode"] + by["summaries"] + by["score"] + by["compact"]
     value = step_bytes / (ms_step * 1e-3) / 1e9
     if single is not None:
@@ -781,7 +803,6 @@ def main():
         single["decode_gbps"] = round(dec_gbps, 1)
         single["decode_frac"] = round(dec_gbps / HBM_PEAK_GBPS, 4)
 
-    dec_ms = rows_ms["paged_decode_attn_with_summaries"]
     achieved = (by["decode_main"] + by["summaries_main"]) / (dec_ms * 1e-3) / 1e9
 
     # plain device copy of known size: the practical HBM ceiling on this machine
