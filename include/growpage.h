@@ -35,7 +35,10 @@
  *       block_tables [B, max_pages] int32, context_lens [B] int32 (cached tokens of a request;
  *       token slot j lives at page block_tables[r][j / page_size], offset j % page_size).
  *     The query head g uses KV head g / (H_q / H_kv).
- *   - Re-entrant; the library keeps no mutable global state.
+ *   - Re-entrant. Calls share no device memory and no host state that affects results. The only
+ *     host-side mutable state is two memo tables of device properties (the compute-unit count
+ *     and the resident workgroups of each decode kernel per device), each entry one atomic word,
+ *     so concurrent calls at worst query the device twice; results never depend on them.
  */
 #ifndef GROWPAGE_H
 #define GROWPAGE_H
@@ -102,6 +105,8 @@ enum {
  *                        row and KV head.
  *             A byte value in an INT4 pool always decodes to finite codes (-8 .. 7), so only
  *             the scales of live tokens need to be meaningful.
+ *             A uniformly fp8 cache is a mixed cache whose pages are all tagged GP_TAG_FP8 (the
+ *             bf16 and INT4 pools are then never read, but must still be given).
  *   page_size a multiple of 16 (16 .. 256); head_dim 64 or 128.
  */
 typedef struct {
@@ -111,7 +116,7 @@ typedef struct {
   void* v8;
   float* k_scale;
   float* v_scale;
-  uint8_t* page_tag; /* written only by gp_quantize_pages_int4 */
+  uint8_t* page_tag; /* written by gp_quantize_pages_int4 and by mixed-cache compaction */
   int32_t num_pages;
   int32_t page_size;
   int32_t num_kv_heads;

@@ -320,9 +320,9 @@ def _move_mixed(kp, vp, mx, old_bt, new_bt, srcs, first_repl, ctx_new, b, P):
     old_tag = np.asarray(tags)[old_bt[:P]].copy()
     new_tag = {}
     for dp in range(dpm, n_dest):
-        lo = min(int(src[dp * b]) for src in srcs) // b
-        hi = max(int(src[dp * b + b - 1]) for src in srcs) // b
-        ts = set(old_tag[lo:hi + 1].tolist())
+        # the old pages that supply at least one token of this page, in any head
+        supply = {int(sl) // b for src in srcs for sl in src[dp * b:(dp + 1) * b]}
+        ts = {int(old_tag[pg]) for pg in supply}
         new_tag[dp] = ts.pop() if len(ts) == 1 else TAG_BF16
     kb, vb = kp.view(np.uint16), vp.view(np.uint16)
     old = {name: np.asarray(mx[name]).copy() for name in

@@ -1169,20 +1169,25 @@ __global__ __launch_bounds__(256) void mixed_plan_kernel(CParams P) {
   const int dpm = s_dpm;
   for (int h = threadIdx.x; h < H; h += blockDim.x) P.dp0[(size_t)i * H + h] = dpm;
   for (int dp = dpm + (int)threadIdx.x; dp < inf.n_dest; dp += blockDim.x) {
-    int lo = INT_MAX, hi = 0;
+    // bit s set: old page dp + s supplies a token of this page in some head. The source slot of
+    // destination slot j is j + #{k : ev[k] - k <= j} >= j, and it exceeds j by at most the E <= 2b
+    // evictions, so s <= 2; a page lying between two suppliers that lost all its tokens in every
+    // head supplies none.
+    uint32_t supply = 0;
     for (int h = 0; h < H; ++h) {
       const int32_t* ev = P.ev + ((size_t)i * H + h) * P.max_evict;
-      auto src = [&](int j) {  // j + #{k : ev[k] - k <= j}
-        int c = 0;
-        for (int k = 0; k < inf.E; ++k) c += (ev[k] - k <= j) ? 1 : 0;
-        return j + c;
-      };
-      lo = min(lo, src(dp * b) / b);
-      hi = max(hi, src(dp * b + b - 1) / b);
+      int c = 0;  // evictions k with ev[k] - k <= j (ev ascending, so ev[k] - k never decreases)
+      for (int j = dp * b; j < dp * b + b; ++j) {
+        while (c < inf.E && ev[c] - c <= j) ++c;
+        supply |= 1u << min(31, (j + c) / b - dp);
+      }
     }
-    int tag = P.page_tag[P.old_bt[(size_t)i * P.max_pages + lo]];
-    for (int lp = lo + 1; lp <= hi; ++lp)
-      if (P.page_tag[P.old_bt[(size_t)i * P.max_pages + lp]] != tag) tag = GP_TAG_BF16;
+    int tag = -1;
+    for (int s = 0; s < 32; ++s) {
+      if (!(supply >> s & 1u)) continue;
+      const int t = P.page_tag[P.old_bt[(size_t)i * P.max_pages + dp + s]];
+      tag = (tag < 0 || tag == t) ? t : GP_TAG_BF16;
+    }
     P.new_tag[(size_t)i * P.max_pages + dp] = tag;
   }
 }
@@ -1509,11 +1514,13 @@ int device_cus() {
   static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  const int v = cache[dev & 63].load();
-  if (v > 0) return v;
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  cache[dev & 63].store(cus);
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 

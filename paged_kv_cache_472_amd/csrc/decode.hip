@@ -725,19 +725,19 @@ Plan plan_for(int B, int max_context) {
   return pl;
 }
 
-// Workgroups of the streaming kernel that fit on the device at once (memoised per device
-// and instantiation; only host-side device properties are cached).
+// Workgroups of the streaming kernel that fit on the device at once. Memoised per device and
+// instantiation: each entry is one 64-bit atomic holding the query (block size and LDS bytes)
+// in its high half and the answer in its low half, so a reader never pairs one query with
+// another's answer. Only host-side device properties are cached.
 template <int D, int KIND, int RING>
 int resident_workgroups(int threads, size_t lds) {
-  static std::atomic<int> cache[64];
+  static std::atomic<uint64_t> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  const int slot = dev & 63;
-  const int key = threads * 65536 + (int)std::min<size_t>(lds, 65535);
-  static std::atomic<int> cache_key[64];
-  if (cache_key[slot].load() == key) {
-    const int v = cache[slot].load();
-    if (v > 0) return v;
+  const uint32_t key = (uint32_t)threads << 16 | (uint32_t)std::min<size_t>(lds, 65535);
+  if (dev < 64) {
+    const uint64_t e = cache[dev].load(std::memory_order_relaxed);
+    if ((uint32_t)(e >> 32) == key && (uint32_t)e > 0) return (int)(uint32_t)e;
   }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
@@ -746,8 +746,7 @@ int resident_workgroups(int threads, size_t lds) {
                                                    lds) != hipSuccess || per_cu <= 0)
     per_cu = 1;
   const int v = cus * per_cu;
-  cache[slot].store(v);
-  cache_key[slot].store(key);
+  if (dev < 64) cache[dev].store((uint64_t)key << 32 | (uint32_t)v, std::memory_order_relaxed);
   return v;
 }
 

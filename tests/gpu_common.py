@@ -9,6 +9,25 @@ from workloads import make_workload
 TOL = {"f32": 2e-4, "bf16": 2e-2}
 DEV = "cuda:0"
 
+# fp32 outputs (lse, scores, summaries) are checked at the fp32 bound whatever the cache dtype.
+# lse: the logits of bf16 / fp8 / INT4 keys against bf16 (or exactly half-rounded) queries are
+# exact products summed in fp32; the running sum of exponentials adds at most one fp32 rounding
+# per 16-token tile, so its relative error stays below 2048 * 2^-24 = 1.2e-4 even for 32K tokens,
+# and lse inherits it as an absolute error.
+LSE_TOL = 2e-4
+# bf16 outputs: the probabilities are rounded to bf16 (fp8 pages: times the row scale) before
+# the value product, and the output once more at the end: each is a relative error of at most
+# 2^-9, so |out - ref| <= 2^-9 |ref| + 2^-9 sum_j w_j |v_j| (+ fp32 accumulation). The bound
+# below doubles both terms; A = sum_j w_j |v_j| is the oracle's attention over |V|.
+OUT_REL_BF16 = 2.0 ** -8
+OUT_ABS_BF16 = 1e-5
+# scores: the summaries meet bf16 keys as a hi + lo bf16 pair (16 significant bits), so a logit
+# is off by at most about 2^-16 sum_i |q_i k_i| / sqrt(d) (~1e-4 for RMS-1 queries and N(0,1)
+# keys); that moves every weight by the same relative amount. Bound: 1e-3 relative, plus a
+# floor of 1e-6 of the row's largest weight for weights the GPU flushes to zero.
+SCORE_REL = 1e-3
+SCORE_FLOOR = 1e-6
+
 
 def say(*a):
     print(*a, flush=True)
@@ -65,3 +84,63 @@ def gather_pages_to_host(wl, requests):
         row = bt_full[r]
         bt_sub[i] = np.where(row >= 0, remap[np.maximum(row, 0)], -1)
     return sub, bt_sub
+
+
+def decode_reference(q, k_pool, v_pool, block_tables, context_lens, page_size, sm_scale,
+                     mixed=None):
+    """The oracle's decode (out, lse) of every request, plus its attention over |V| (the
+    probability-weighted mean of |v| that scales the bf16 rounding bound)."""
+    from oracle import attention as oatt
+    q = np.asarray(q, dtype=np.float64)
+    B, H_q, d = q.shape
+    H_kv = np.asarray(k_pool).shape[1]
+    G = H_q // H_kv
+    out = np.zeros((B, H_q, d))
+    lse = np.zeros((B, H_q))
+    wabs = np.zeros((B, H_q, d))
+    mx = mixed or {}
+    for r in range(B):
+        k, v, _ = oatt.gather_request_kv(r, k_pool, v_pool, block_tables, context_lens,
+                                         page_size, **mx)
+        for h in range(H_kv):
+            rows = slice(h * G, (h + 1) * G)
+            out[r, rows], lse[r, rows] = oatt.attend(q[r, rows], k[h], v[h], sm_scale)
+            wabs[r, rows], _ = oatt.attend(q[r, rows], k[h], np.abs(v[h]), sm_scale)
+    return out, lse, wabs
+
+
+def check_decode(out, lse, ref, dtype, label):
+    """Element-wise check of a decode against decode_reference(): lse at the fp32 bound, out at
+    2e-4 (fp32) or the bf16 rounding bound; prints the observed errors."""
+    ref_o, ref_l, ref_a = ref
+    o = out.detach().to("cpu", torch.float64).numpy() if isinstance(out, torch.Tensor) else out
+    l_ = lse.detach().cpu().numpy() if isinstance(lse, torch.Tensor) else lse
+    eo, nan_o = maxabs(o, ref_o)
+    el, nan_l = maxabs(l_, ref_l)
+    if dtype == "f32":
+        bound = np.full(ref_o.shape, TOL["f32"])
+    else:
+        bound = OUT_REL_BF16 * (np.abs(ref_o) + ref_a) + OUT_ABS_BF16
+    ratio = float(np.max(np.abs(o - ref_o) / bound)) if ref_o.size else 0.0
+    say(f"[{label}] max|out-ref|={eo:.3e} (max error / bound {ratio:.3f}) "
+        f"max|lse-ref|={el:.3e} (bound {LSE_TOL:.0e})")
+    assert not nan_o and not nan_l, "NaN in output or lse"
+    assert el <= LSE_TOL, f"lse error {el:.3e}"
+    assert ratio <= 1.0, f"out error {eo:.3e}, {ratio:.3f} of the bound"
+    return eo, el
+
+
+def check_scores(a, ref, n, label=""):
+    """Scores of one request (rows [H_kv, >= n]) against the oracle's: relative bound plus a
+    floor of the row maximum; returns the largest relative error."""
+    a = np.asarray(a, dtype=np.float64)[:, :n]
+    ref = np.asarray(ref, dtype=np.float64)[:, :n]
+    assert not np.isnan(a).any(), f"NaN in scores {label}"
+    if n == 0:
+        return 0.0
+    floor = SCORE_FLOOR * ref.max(axis=1, keepdims=True)
+    err = np.abs(a - ref)
+    assert (err <= SCORE_REL * np.abs(ref) + floor).all(), \
+        f"scores {label}: max|a-ref| {err.max():.3e}, max rel {np.max(err / np.maximum(ref, 1e-300)):.3e}"
+    big = ref > floor
+    return float(np.max(err[big] / ref[big])) if big.any() else 0.0

@@ -11,7 +11,7 @@ import torch
 import paged_kv_cache_472_amd as gp
 from oracle import attention as oatt
 from oracle.summaries import update_query_summaries
-from gpu_common import DEV, TOL, maxabs, mixed_np, say, workload_on_gpu
+from gpu_common import DEV, TOL, check_decode, decode_reference, maxabs, mixed_np, say, workload_on_gpu
 from util import f64, npy
 from workloads.configs import make_decode_case
 
@@ -85,17 +85,14 @@ def test_fused_capped_grid_matches_oracle(max_wg):
                                     beta_s=0.9, beta_l=0.999),
         max_workgroups=max_wg)
     torch.cuda.synchronize()
-    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
-                                          npy(wl.block_tables), npy(wl.context_lens), 16,
-                                          wl.sm_scale)
+    ref = decode_reference(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool), npy(wl.block_tables),
+                           npy(wl.context_lens), 16, wl.sm_scale)
     bound = slots >= 0
     update_query_summaries(f64(q_pre)[bound], slots[bound], fresh[bound], state_ref, 0.9, 0.999)
-    eo, nan_o = maxabs(f64(out), ref_o)
-    el, nan_l = maxabs(lse.cpu().numpy(), ref_l)
+    check_decode(out, lse, ref, "bf16", f"fused cap={max_wg}")
     es, nan_s = maxabs(qstate.cpu().numpy(), state_ref)
-    say(f"[fused cap={max_wg}] max|out-ref|={eo:.3e} max|lse-ref|={el:.3e} max|state-ref|={es:.3e}")
-    assert not (nan_o or nan_l or nan_s)
-    assert eo <= TOL["bf16"] and el <= TOL["bf16"] and es <= TOL["f32"]
+    say(f"[fused cap={max_wg}] max|state-ref|={es:.3e}")
+    assert not nan_s and es <= TOL["f32"]
     # the empty requests still had their summaries updated (request 0 is bound and empty)
     assert lens[0] == 0 and bound[0]
 
@@ -168,10 +165,9 @@ def test_fused_capped_full_size_as_benchmarked():
     torch.cuda.synchronize()
     reqs = sample_requests(wl, 3, seed=11)
     sub, bt = gather_pages_to_host(wl, reqs)
-    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q[reqs]), f64(sub["k_pool"]), f64(sub["v_pool"]),
-                                          bt, npy(wl.context_lens[reqs]), wl.page_size, wl.sm_scale)
-    eo, nan_o = maxabs(f64(out[reqs]), ref_o)
-    el, nan_l = maxabs(lse[reqs].cpu().numpy(), ref_l)
+    ref = decode_reference(f64(wl.q[reqs]), f64(sub["k_pool"]), f64(sub["v_pool"]), bt,
+                           npy(wl.context_lens[reqs]), wl.page_size, wl.sm_scale)
+    check_decode(out[reqs], lse[reqs], ref, "bf16", f"fused full as benchmarked, cap {cus - 32}")
     # summary rows of the sampled requests that were updated, and a boundary request's untouched row
     st_ref = f64(state0)
     upd = [r for r in reqs if slots[r] >= 0]
@@ -180,10 +176,8 @@ def test_fused_capped_full_size_as_benchmarked():
     es, nan_s = maxabs(wl.qstate.cpu().numpy()[slots[upd]], st_ref[slots[upd]])
     b0 = int(npy(wl.req_idx)[0])
     s0 = int(npy(wl.slot_ids)[b0])
-    say(f"[fused full as benchmarked, cap {cus - 32}] requests={reqs} max|out-ref|={eo:.3e} "
-        f"max|lse-ref|={el:.3e} max|state-ref|={es:.3e}")
-    assert not (nan_o or nan_l or nan_s)
-    assert eo <= TOL["bf16"] and el <= TOL["bf16"] and es <= TOL["f32"]
+    say(f"[fused full as benchmarked, cap {cus - 32}] requests={reqs} max|state-ref|={es:.3e}")
+    assert not nan_s and es <= TOL["f32"]
     assert torch.equal(wl.qstate[s0].view(torch.int32), state0[s0].view(torch.int32))
 
 

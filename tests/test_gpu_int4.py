@@ -8,8 +8,8 @@ import torch
 import paged_kv_cache_472_amd as gp
 from oracle import attention as oatt
 from oracle import int4 as oi4
-from gpu_common import (DEV, TOL, gather_pages_to_host, maxabs, mixed_np, sample_requests, say,
-                        workload_on_gpu)
+from gpu_common import (DEV, check_decode, decode_reference, gather_pages_to_host, mixed_np,
+                        sample_requests, say, workload_on_gpu)
 from util import f64, npy
 from workloads.configs import make_decode_case
 
@@ -108,15 +108,9 @@ def test_decode_int4_small_elementwise(page_size, int4_frac):
     used = np.unique(npy(wl.block_tables)[npy(wl.block_tables) >= 0])
     assert set(np.unique(tags[used])) >= {TAG_INT4, TAG_BF16 if int4_frac < 1 else TAG_INT4}
     out, lse = _run_decode(wl)
-    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
-                                          npy(wl.block_tables), npy(wl.context_lens),
-                                          wl.page_size, wl.sm_scale, **mixed_np(wl))
-    eo, nan_o = maxabs(f64(out), ref_o)
-    el, nan_l = maxabs(lse.cpu().numpy(), ref_l)
-    say(f"[decode int4 small b={page_size} frac={int4_frac}] max|out-ref|={eo:.3e} "
-        f"max|lse-ref|={el:.3e}")
-    assert not nan_o and not nan_l
-    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    ref = decode_reference(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool), npy(wl.block_tables),
+                           npy(wl.context_lens), wl.page_size, wl.sm_scale, mixed_np(wl))
+    check_decode(out, lse, ref, "bf16", f"decode int4 small b={page_size} frac={int4_frac}")
 
 
 def test_decode_int4_full_size_sampled():
@@ -125,14 +119,9 @@ def test_decode_int4_full_size_sampled():
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
     reqs = sample_requests(wl, 3)
     sub, bt = gather_pages_to_host(wl, reqs)
-    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q[reqs]), f64(sub["k_pool"]), f64(sub["v_pool"]),
-                                          bt, npy(wl.context_lens[reqs]), wl.page_size,
-                                          wl.sm_scale, **mixed_np(sub))
-    eo, nan_o = maxabs(f64(out[reqs]), ref_o)
-    el, nan_l = maxabs(lse[reqs].cpu().numpy(), ref_l)
-    say(f"[decode int4 full] requests={reqs} max|out-ref|={eo:.3e} max|lse-ref|={el:.3e}")
-    assert not nan_o and not nan_l
-    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    ref = decode_reference(f64(wl.q[reqs]), f64(sub["k_pool"]), f64(sub["v_pool"]), bt,
+                           npy(wl.context_lens[reqs]), wl.page_size, wl.sm_scale, mixed_np(sub))
+    check_decode(out[reqs], lse[reqs], ref, "bf16", f"decode int4 full requests={reqs}")
 
 
 @pytest.mark.parametrize("D,b,G", [(64, 16, 4), (128, 32, 1), (64, 64, 16)])
@@ -165,15 +154,11 @@ def test_quantize_then_decode(D, b, G):
     otags = tags.copy()
     otags[demote] = TAG_INT4
     z8 = np.zeros(1, dtype=np.uint8)
-    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q), kp, vp, bt, npy(wl.context_lens), b,
-                                          wl.sm_scale, page_tag=otags, k8=z8, v8=z8, k_scale=z8,
-                                          v_scale=z8, k4=k4, v4=v4, k4_scale=ks, v4_scale=vs)
+    ref = decode_reference(f64(wl.q), kp, vp, bt, npy(wl.context_lens), b, wl.sm_scale,
+                           dict(page_tag=otags, k8=z8, v8=z8, k_scale=z8, v_scale=z8, k4=k4, v4=v4,
+                                k4_scale=ks, v4_scale=vs))
     assert np.array_equal(cache.page_tag.cpu().numpy(), otags)
-    eo, nan_o = maxabs(f64(out), ref_o)
-    el, nan_l = maxabs(lse.cpu().numpy(), ref_l)
-    say(f"[quantize+decode D={D} b={b} G={G}] max|out-ref|={eo:.3e} max|lse-ref|={el:.3e}")
-    assert not nan_o and not nan_l
-    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    check_decode(out, lse, ref, "bf16", f"quantize+decode D={D} b={b} G={G}")
     assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
 
 
@@ -193,12 +178,7 @@ def test_mixed_two_passes_capped_grid(max_wg, H_kv):
                                           wl.context_lens, wl.max_context, wl.sm_scale,
                                           max_workgroups=max_wg)
     torch.cuda.synchronize()
-    ref_o, ref_l = oatt.paged_decode_attn(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool),
-                                          npy(wl.block_tables), npy(wl.context_lens), 16,
-                                          wl.sm_scale, **mixed_np(wl))
-    eo, nan_o = maxabs(f64(out), ref_o)
-    el, nan_l = maxabs(lse.cpu().numpy(), ref_l)
-    say(f"[two passes cap={max_wg} H_kv={H_kv}] max|out-ref|={eo:.3e} max|lse-ref|={el:.3e}")
-    assert not nan_o and not nan_l
-    assert eo <= TOL["bf16"] and el <= TOL["bf16"]
+    ref = decode_reference(f64(wl.q), f64(wl.k_pool), f64(wl.v_pool), npy(wl.block_tables),
+                           npy(wl.context_lens), 16, wl.sm_scale, mixed_np(wl))
+    check_decode(out, lse, ref, "bf16", f"two passes cap={max_wg} H_kv={H_kv}")
     assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))

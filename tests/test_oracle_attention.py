@@ -42,6 +42,21 @@ def test_decode_golden_two_tokens():
     assert abs(lse[0] - rows["lse"][0]) < 1e-12
 
 
+def test_decode_gqa_golden():
+    """Hand-worked GQA decode (tests/golden/decode_gqa.txt): query head g reads KV head g // G."""
+    rows = {r[0]: np.array([float(x) for x in r[1:]]) for r in golden_lines("decode_gqa.txt")}
+    b, d = 16, 2
+    q = rows["q"].reshape(1, 4, d)
+    k_pool = np.full((1, 2, b, d), np.nan)
+    v_pool = np.full((1, 2, d, b), np.nan)
+    for h in range(2):
+        k_pool[0, h, :2] = rows[f"k_h{h}"].reshape(2, d)
+        v_pool[0, h, :, :2] = rows[f"v_h{h}"].reshape(2, d).T
+    out, lse = oatt.paged_decode_attn(q, k_pool, v_pool, np.array([[0]]), np.array([2]), b, 1.0)
+    assert np.allclose(out[0], rows["o"].reshape(4, d), rtol=0, atol=1e-12)
+    assert np.allclose(lse[0], rows["lse"], rtol=0, atol=1e-12)
+
+
 def test_softmax_rows_sum_to_one():
     rng = np.random.default_rng(0)
     q = rng.standard_normal((4, 32))

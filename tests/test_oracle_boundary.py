@@ -159,6 +159,33 @@ def test_score_matches_single_head_softmax_by_hand():
 
 
 # ------------------------------------------------------------------ decision
+def test_score_gqa_golden():
+    """Hand-worked scores with G = 2 (tests/golden/score_gqa.txt): each KV head's weights are the
+    mean of its own query heads' softmax distributions."""
+    from fractions import Fraction
+    rows = {r[0]: r[1:] for r in golden_lines("score_gqa.txt")}
+    b, d, H_q = 16, 2, 4
+    ln4, ln9 = math.log(4.0), math.log(9.0)
+    q = np.array([[[0.0, 0.0], [ln4, 0.0], [0.0, ln9], [0.0, 0.0]]])
+    qstate = np.zeros((1, 2, H_q, d))
+    qstate[0, 0] = q[0]
+    qstate[0, 1] = 3.0 * q[0]
+    qstate[0, :, 0] = qstate[0, :, 3] = (1.0, 1.0)    # q_t = 0 there: the calibrated summary is 0
+    k_pool = np.zeros((2, 2, b, d))
+    k_pool[0, 0, 0], k_pool[0, 0, 1], k_pool[0, 0, 2:] = (1, 0), (0, 1), (0, -1)
+    k_pool[0, 1, 0], k_pool[0, 1, 1], k_pool[0, 1, 2:] = (0, 1), (0, 0), (1, 0)
+    a_s, a_l, ws, nc = ob.score_and_working_set(q, qstate, [0], [0], k_pool, np.array([[0, 1]]),
+                                                [20], [19], b, 0.0, 0.2, 1.0)
+    assert nc.tolist() == [16]
+    for h in range(2):
+        fr = [float(Fraction(x)) for x in rows[f"a_h{h}"]]
+        expect = np.array(fr[:2] + [fr[2]] * 14)
+        assert np.allclose(a_s[0, h, :16], expect, rtol=1e-12, atol=0)
+        assert np.allclose(a_l[0, h, :16], expect, rtol=1e-12, atol=0)
+    assert ws[0, :, 0].tolist() == [int(x) for x in rows["ws"]]
+    assert ws[0, :, 1].tolist() == [int(x) for x in rows["ws"]]
+
+
 def test_decision_golden():
     for row in golden_lines("decision_cases.txt"):
         ks0, kl0, ks1, kl1, n, tau, pol, dec = row

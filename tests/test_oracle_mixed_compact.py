@@ -217,3 +217,37 @@ def test_mixed_scores_equal_dequantised_pages_and_released_deleted():
         mask[vis_c] = False
         assert (a[0][:, :nc[0]][:, mask] == 0).all()
     assert np.array_equal(ws, rws)
+
+
+def test_destination_tag_from_supplying_pages_not_their_range():
+    """A Shrink evicts 2b tokens: here all of page 1 (bf16) and half of pages 0 and 2 (fp8), the
+    same in every head, with no per-page quota (k_loc = 0). Destination page 0 then receives
+    slots 0..7 of page 0 and slots 32..39 of page 2: both fp8, so it stays an fp8 page and its
+    tokens keep their codes and scales, although the bf16 page 1 lies between its suppliers."""
+    tags = [F8, BF] + [F8] * 63 + [BF]                # 66 pages, the last one the recent page
+    wl, mx, kb, vb = _mixed_case(tags, seed=13)
+    st = _state(wl)
+    bt = st["block_tables"].copy()
+    k8_0, ks_0 = mx["k8"].copy(), mx["k_scale"].copy()
+    n = 65 * 16
+    evict = list(range(8, 32)) + list(range(40, 48))
+    s = np.ones((1, wl.H_kv, n))
+    s[:, :, evict] = 0.5
+    ws = np.zeros((1, wl.H_kv, 2), dtype=np.int64)
+    ws[..., 1] = n                                    # Delta = -1 < -0.005: shrink
+    dec, kept = ob.compact_or_grow([0], s, s, ws, np.array([n]), 0.0, 0, ob.POLICY_SHRINK, kb,
+                                   vb, st["block_tables"], st["n_pages"], st["context_lens"],
+                                   st["refcount"], st["free_stack"], st["free_top"], 16, mixed=mx)
+    assert list(dec) == [ob.SHRINK]
+    assert st["context_lens"][0] == 64 * 16
+    kept_slots = [t for t in range(n) if t not in set(evict)]
+    assert np.array_equal(kept[0, 0, :n - 32], kept_slots)
+    assert int(mx["page_tag"][bt[0, 0]]) == F8        # the range rule would make it bf16
+    src = kept_slots[:16]
+    assert src == list(range(8)) + list(range(32, 40))
+    for j, t in enumerate(src):
+        assert np.array_equal(mx["k8"][bt[0, 0], :, j], k8_0[bt[0, t // 16], :, t % 16])
+        assert np.array_equal(mx["k_scale"][bt[0, 0], :, j], ks_0[bt[0, t // 16], :, t % 16])
+    # destination page 1 reads page 3 only; the last kept page is the old recent (bf16) page
+    assert int(mx["page_tag"][bt[0, 1]]) == F8
+    assert int(mx["page_tag"][bt[0, 63]]) == BF
