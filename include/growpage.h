@@ -35,10 +35,11 @@
  *       block_tables [B, max_pages] int32, context_lens [B] int32 (cached tokens of a request;
  *       token slot j lives at page block_tables[r][j / page_size], offset j % page_size).
  *     The query head g uses KV head g / (H_q / H_kv).
- *   - Re-entrant. Calls share no device memory and no host state that affects results. The only
- *     host-side mutable state is two memo tables of device properties (the compute-unit count
- *     and the resident workgroups of each decode kernel per device), each entry one atomic word,
- *     so concurrent calls at worst query the device twice; results never depend on them.
+ *   - Re-entrant. Calls share no device memory (except gp_paged_decode_attn_noalloc, whose
+ *     calls share one static buffer per device) and no host state that affects results. The
+ *     only host-side mutable state is three memo tables per device (the compute-unit count, the
+ *     resident workgroups of each decode kernel, the device address of the static buffer), each
+ *     entry one atomic word, so concurrent calls at worst query the device twice.
  */
 #ifndef GROWPAGE_H
 #define GROWPAGE_H
@@ -57,7 +58,8 @@ typedef enum {
   GP_ERR_INVALID = -1,      /* a pointer, size or parameter is out of range            */
   GP_ERR_UNSUPPORTED = -2,  /* a valid combination this build does not implement       */
   GP_ERR_WORKSPACE = -3,    /* workspace missing or smaller than *_workspace_size()     */
-  GP_ERR_HIP = -4           /* a HIP launch failed                                      */
+  GP_ERR_HIP = -4,          /* a HIP launch failed                                      */
+  GP_ERR_SCRATCH = -5       /* the call needs more than GP_NOALLOC_SCRATCH_BYTES        */
 } gp_status;
 
 typedef enum { GP_F32 = 0, GP_BF16 = 1 } gp_dtype;
@@ -201,6 +203,28 @@ int gp_paged_decode_attn_ex(const void* q, int q_dtype, int B, int H_q, const gp
                             void* out, float* lse, const gp_summary_update* summaries,
                             int max_workgroups, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * gp_paged_decode_attn_ex without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * split partials live in a static device buffer of GP_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every device it runs on until the process ends. Arguments, results and bits as
+ * gp_paged_decode_attn_ex. The call allocates nothing (no hipMalloc, no library allocation).
+ *   Limit: the call needs the prefix of tile counts plus B * H_q * passes * j_max * (head_dim + 2)
+ *   floats of partials (passes = 2 for a mixed cache, else 1; j_max grows with max_context and
+ *   shrinks with B, as gp_paged_decode_attn_workspace_size counts them); a call needing more
+ *   than GP_NOALLOC_SCRATCH_BYTES returns GP_ERR_SCRATCH and launches nothing.
+ *   Every call on one device shares that device's buffer: calls that may overlap on one device
+ *   (other streams, other threads) race and must be ordered by the caller. Nothing in the
+ *   buffer needs clearing between calls (each call writes what it reads).
+ */
+#define GP_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int gp_paged_decode_attn_noalloc(const void* q, int q_dtype, int B, int H_q,
+                                 const gp_kv_cache* kv, const int32_t* block_tables,
+                                 int max_pages, const int32_t* context_lens, int max_context,
+                                 float sm_scale, void* out, float* lse,
+                                 const gp_summary_update* summaries, int max_workgroups,
+                                 void* stream);
 
 /*
  * Dual-timescale EMA of the pre-RoPE queries (GrowPage Eq. 6, App. E.1).

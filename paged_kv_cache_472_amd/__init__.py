@@ -11,6 +11,7 @@ from .growpage import (  # noqa: F401
     gp_compact_or_grow_workspace_size,
     gp_paged_decode_attn,
     gp_paged_decode_attn_ex,
+    gp_paged_decode_attn_noalloc,
     gp_paged_decode_attn_workspace_size,
     gp_quantize_pages_int4,
     gp_score_and_working_set,

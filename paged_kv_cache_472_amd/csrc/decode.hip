@@ -803,6 +803,36 @@ int launch_decode(DecodeParams p, int max_workgroups, hipStream_t stream) {
   return launch_decode_ring<D, KIND, RING_FULL>(p, max_workgroups, stream);
 }
 
+// Bytes of the decode workspace when `passes` passes leave partials (a mixed cache decodes its
+// INT4 tiles in a pass of their own): the prefix of tile counts, 256-byte aligned, then every
+// output row's partial outputs and partial (max, sum) pairs.
+size_t decode_ws_bytes(int B, int H_q, int head_dim, int max_context, int passes) {
+  const Plan pl = plan_for(B, max_context);
+  const size_t partials = (size_t)B * H_q * passes * pl.j_max * (head_dim + 2) * sizeof(float);
+  const size_t pref = ((size_t)(B + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
+  return pref + partials;
+}
+
+// Scratch of gp_paged_decode_attn_noalloc: a static device array, one copy on every device the
+// library runs on, held until the process ends. Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): it takes the device address that
+// hipGetSymbolAddress returns for the current device, looked up on the first call on that device.
+static __device__ __align__(256) unsigned char scratch[GP_NOALLOC_SCRATCH_BYTES];
+
+int scratch_on_current_device(void** out) {
+  static std::atomic<void*> ptrs[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GP_ERR_HIP;
+  if (dev >= 64) return GP_ERR_UNSUPPORTED;
+  void* ptr = ptrs[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GP_ERR_HIP;
+    ptrs[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return GP_OK;
+}
+
 }  // namespace
 
 extern "C" size_t gp_paged_decode_attn_workspace_size(int B, int H_q, int H_kv, int head_dim,
@@ -810,20 +840,18 @@ extern "C" size_t gp_paged_decode_attn_workspace_size(int B, int H_q, int H_kv, 
   (void)page_size;
   (void)H_kv;
   if (B <= 0 || H_q <= 0 || head_dim <= 0 || max_context < 0) return 0;
-  const Plan pl = plan_for(B, max_context);
-  // two passes' partials (a mixed cache decodes its INT4 tiles in a pass of their own)
-  const size_t partials = (size_t)B * H_q * 2 * pl.j_max * (head_dim + 2) * sizeof(float);
-  const size_t pref = ((size_t)(B + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
-  return pref + partials;
+  return decode_ws_bytes(B, H_q, head_dim, max_context, 2);
 }
 
 namespace {
 
+// static_scratch: take the workspace from the library's static scratch on the current device
+// (workspace / workspace_bytes are ignored), laid out for the passes this call needs.
 int decode_impl(const void* q, int q_dtype, int B, int H_q, const gp_kv_cache* kv,
                 const int32_t* block_tables, int max_pages, const int32_t* context_lens,
                 int max_context, float sm_scale, void* out, float* lse,
                 const gp_summary_update* upd, int max_workgroups, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, bool static_scratch = false) {
   if (B < 0 || H_q <= 0 || !kv || max_pages <= 0 || max_context < 0) return GP_ERR_INVALID;
   if (max_workgroups < 0) return GP_ERR_INVALID;
   if (upd && (!upd->q_pre || !upd->slot_ids || !upd->fresh || !upd->qstate || upd->num_slots <= 0))
@@ -847,8 +875,16 @@ int decode_impl(const void* q, int q_dtype, int B, int H_q, const gp_kv_cache* k
   if ((long)kv->num_pages * 4 > (long)INT32_MAX) return GP_ERR_UNSUPPORTED;  // tag packing
   if ((long)B * ((max_context + 15) / 16) > (long)INT32_MAX / 2) return GP_ERR_UNSUPPORTED;
 
-  const size_t need = gp_paged_decode_attn_workspace_size(B, H_q, H_kv, D, b, max_context);
-  if (!workspace || workspace_bytes < need) return GP_ERR_WORKSPACE;
+  const int passes = mixed ? 2 : 1;
+  if (static_scratch) {
+    if (decode_ws_bytes(B, H_q, D, max_context, passes) > GP_NOALLOC_SCRATCH_BYTES)
+      return GP_ERR_SCRATCH;
+    const int st = scratch_on_current_device(&workspace);
+    if (st != GP_OK) return st;
+  } else {
+    const size_t need = gp_paged_decode_attn_workspace_size(B, H_q, H_kv, D, b, max_context);
+    if (!workspace || workspace_bytes < need) return GP_ERR_WORKSPACE;
+  }
   const Plan pl = plan_for(B, max_context);
 
   DecodeParams p{};
@@ -883,7 +919,7 @@ int decode_impl(const void* q, int q_dtype, int B, int H_q, const gp_kv_cache* k
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   p.ws_pref = reinterpret_cast<int32_t*>(ws);
   p.ws_o = reinterpret_cast<float*>(ws + (((size_t)(B + 1) * sizeof(int32_t) + 255) & ~(size_t)255));
-  p.ws_ml = p.ws_o + (size_t)B * H_q * 2 * pl.j_max * D;
+  p.ws_ml = p.ws_o + (size_t)B * H_q * passes * pl.j_max * D;
   if (upd) {
     p.q_pre = upd->q_pre;
     p.slot_ids = upd->slot_ids;
@@ -920,4 +956,14 @@ extern "C" int gp_paged_decode_attn_ex(const void* q, int q_dtype, int B, int H_
   return decode_impl(q, q_dtype, B, H_q, kv, block_tables, max_pages, context_lens, max_context,
                      sm_scale, out, lse, summaries, max_workgroups, workspace, workspace_bytes,
                      stream);
+}
+
+extern "C" int gp_paged_decode_attn_noalloc(const void* q, int q_dtype, int B, int H_q,
+                                            const gp_kv_cache* kv, const int32_t* block_tables,
+                                            int max_pages, const int32_t* context_lens,
+                                            int max_context, float sm_scale, void* out, float* lse,
+                                            const gp_summary_update* summaries, int max_workgroups,
+                                            void* stream) {
+  return decode_impl(q, q_dtype, B, H_q, kv, block_tables, max_pages, context_lens, max_context,
+                     sm_scale, out, lse, summaries, max_workgroups, nullptr, 0, stream, true);
 }

@@ -54,6 +54,7 @@ extern "C" const char* gp_status_string(int status) {
     case GP_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case GP_ERR_WORKSPACE: return "workspace missing or too small";
     case GP_ERR_HIP: return "HIP launch failed";
+    case GP_ERR_SCRATCH: return "call needs more scratch than the static buffer holds";
     default: return "unknown status";
   }
 }

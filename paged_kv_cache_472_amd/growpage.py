@@ -21,6 +21,7 @@ PHASE_PLAN, PHASE_MOVE = 1, 2
 EXPORTED = (
     "gp_version", "gp_status_string",
     "gp_paged_decode_attn_workspace_size", "gp_paged_decode_attn", "gp_paged_decode_attn_ex",
+    "gp_paged_decode_attn_noalloc",
     "gp_update_query_summaries",
     "gp_score_and_working_set_workspace_size", "gp_score_and_working_set",
     "gp_compact_or_grow_workspace_size", "gp_compact_or_grow", "gp_compact_or_grow_phase",
@@ -75,6 +76,10 @@ def lib():
         L.gp_paged_decode_attn_ex.argtypes = [_VP, _I, _I, _I, ctypes.POINTER(GpKvCache), _VP, _I,
                                               _VP, _I, _F, _VP, _VP,
                                               ctypes.POINTER(GpSummaryUpdate), _I, _VP, _SZ, _VP]
+        L.gp_paged_decode_attn_noalloc.restype = _I
+        L.gp_paged_decode_attn_noalloc.argtypes = [_VP, _I, _I, _I, ctypes.POINTER(GpKvCache), _VP,
+                                                   _I, _VP, _I, _F, _VP, _VP,
+                                                   ctypes.POINTER(GpSummaryUpdate), _I, _VP]
         L.gp_update_query_summaries.restype = _I
         L.gp_update_query_summaries.argtypes = [_VP, _I, _I, _I, _I, _VP, _VP, _VP, _I, _F, _F, _VP]
         L.gp_score_and_working_set_workspace_size.restype = _SZ
@@ -207,6 +212,34 @@ def gp_paged_decode_attn_ex(q, cache, block_tables, context_lens, max_context, s
         _ptr(lse), None if upd is None else ctypes.byref(upd), int(max_workgroups),
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream())
     _check(st, "gp_paged_decode_attn_ex")
+    return out, lse
+
+
+def _summary_struct(summaries):
+    if summaries is None:
+        return None
+    u = summaries
+    return GpSummaryUpdate(_ptr(u["q_pre"]), _ptr(u["slot_ids"]), _ptr(u["fresh"]),
+                           _ptr(u["qstate"]), u["qstate"].shape[0], float(u["beta_s"]),
+                           float(u["beta_l"]))
+
+
+def gp_paged_decode_attn_noalloc(q, cache, block_tables, context_lens, max_context, sm_scale,
+                                 summaries=None, max_workgroups=0, out=None, lse=None):
+    """gp_paged_decode_attn_ex with its split partials in the library's static device buffer
+    (no workspace); out / lse are allocated here unless given. Returns (out, lse)."""
+    B, H_q, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=q.device)
+    upd = _summary_struct(summaries)
+    kv = cache.struct()
+    st = lib().gp_paged_decode_attn_noalloc(
+        _ptr(q), _dtype_code(q), B, H_q, ctypes.byref(kv), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), int(max_context), float(sm_scale), _ptr(out),
+        _ptr(lse), None if upd is None else ctypes.byref(upd), int(max_workgroups), _stream())
+    _check(st, "gp_paged_decode_attn_noalloc")
     return out, lse
 
 

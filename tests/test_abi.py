@@ -50,7 +50,7 @@ def test_version_and_status_strings(lib):
     m = re.search(r"#define\s+GP_VERSION\s+(\d+)", open(HEADER).read())
     assert lib.gp_version() == int(m.group(1))
     assert lib.gp_status_string(0) == b"ok"
-    for code in (-1, -2, -3, -4):
+    for code in (-1, -2, -3, -4, -5):
         assert lib.gp_status_string(code) not in (b"ok", b"unknown status")
     assert lib.gp_status_string(7) == b"unknown status"
 
@@ -97,6 +97,12 @@ def test_invalid_arguments_rejected_on_host(lib):
                                     0.1, fake, None, None, 0, None) == -3
     assert lib.gp_paged_decode_attn(fake, 1, 9000, 32, ctypes.byref(kv), fake, 1024, fake, 16384,
                                     0.1, fake, None, fake, 1 << 40, None) == -2
+    # the allocation-free decode: a call whose partials exceed the static buffer is refused on
+    # the host (4096 requests of up to 16384 tokens need about 1.2 GB of partials)
+    assert lib.gp_paged_decode_attn_noalloc(fake, 1, 4096, 32, ctypes.byref(kv), fake, 1024, fake,
+                                            16384, 0.1, fake, None, None, 0, None) == -5
+    assert lib.gp_paged_decode_attn_noalloc(None, 1, 4, 32, ctypes.byref(kv), fake, 8, fake, 128,
+                                            0.1, fake, None, None, 0, None) == -1
     # max_context beyond the block table's reach
     assert lib.gp_paged_decode_attn(fake, 1, 4, 32, ctypes.byref(kv), fake, 8, fake, 1000, 0.1,
                                     fake, None, None, 0, None) == -1
