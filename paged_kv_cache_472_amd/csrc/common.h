@@ -222,6 +222,33 @@ __device__ __forceinline__ double wave_sum_f64(double x) {
   return __builtin_bit_cast(double, readlane63_u64(__builtin_bit_cast(uint64_t, x)));
 }
 
+// Sums and maxima over the 16 lanes of each DPP row (quad swaps, half-row and row mirrors): every
+// lane of a row ends with its row's result. A block reduction hands its (at most 16) wave
+// partials to the lanes of a row this way: one LDS read per lane instead of 16.
+__device__ __forceinline__ double row16_sum_f64(double x) {
+  x += __builtin_bit_cast(double, dpp_u64<0xb1>(__builtin_bit_cast(uint64_t, x)));
+  x += __builtin_bit_cast(double, dpp_u64<0x4e>(__builtin_bit_cast(uint64_t, x)));
+  x += __builtin_bit_cast(double, dpp_u64<0x141>(__builtin_bit_cast(uint64_t, x)));
+  x += __builtin_bit_cast(double, dpp_u64<0x140>(__builtin_bit_cast(uint64_t, x)));
+  return x;
+}
+
+__device__ __forceinline__ uint64_t row16_sum_u64(uint64_t v) {
+  v += dpp_u64<0xb1>(v);
+  v += dpp_u64<0x4e>(v);
+  v += dpp_u64<0x141>(v);
+  v += dpp_u64<0x140>(v);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xb1>(v));
+  v = max(v, dpp_u32<0x4e>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  return v;
+}
+
 // maximum of unsigned values (lanes outside a broadcast's row mask see 0, the identity)
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp_u32<0xb1>(v));

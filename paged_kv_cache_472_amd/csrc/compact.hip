@@ -53,6 +53,11 @@ constexpr int WIDE_PART = 64;             // bytes of each key row one wide comp
 constexpr int NUM_XCD = 8;                // accelerator dies of the chip, each with its own L2
 constexpr int WIDE_MAX_PARTS = 128 * 4 / WIDE_PART;
 constexpr int KEY_BITS = 46;              // 31 score bits above a 15-bit complemented index
+// Candidate sets of at most this many selection chunks (SEL_T pages each) are selected by one
+// workgroup per (request, KV head), chunk after chunk; longer ones by a workgroup per chunk and a
+// merge (measured, 16 requests of up to 18K candidates: one workgroup per head 79 us, per chunk
+// 36 us; one request of 2K candidates: 20 us against 26 us).
+constexpr int FUSED_MAX_CHUNKS = 2;
 
 struct Info {
   int r, mode, P, ctx_old, n, K_t, R_n, E, ctx_new, n_dest, first_repl, pad;
@@ -103,6 +108,8 @@ struct CParams {
   int npart;          // parts of the head dimension compacted apart (1 below WIDE_MIN_PAGE)
   int log_b, log_kq, log_vq, log_qpp;  // log2 of page size, 16-byte pieces per key row / value row / page
   int log_kpq;        // log2 of the 16-byte pieces of a key row one part owns
+  int fuse_items;     // the selection appends the compaction items itself (one layer, uniform
+                      // cache); the allocator zeroes the item count before it
   double tau;
 };
 
@@ -161,13 +168,42 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
   __shared__ int s_w[DA_THREADS / GP_WAVE];
   __shared__ int s_any_repl, s_top_end, s_nrel;
 
+  // the stack top before the call, fetched while the requests are examined
+  __shared__ int s_top0;
+  if (tid == 0) {
+    const int t0 = *P.free_top;
+    s_top0 = (t0 < 0 || t0 > P.num_pages) ? 0 : t0;
+    if (P.fuse_items) *P.n_items = 0;  // the selection appends the compaction items
+  }
+
   // ---- A: per request (one thread each): validity, primary decision, compaction geometry
   for (int i = tid; i < R; i += DA_THREADS) {
     Info inf = {};
     inf.mode = MODE_NONE;
     const int nc = P.n_cand[i];
-    inf.n = (nc > 0 && nc <= P.C_max) ? nc : 0;
     const int r = P.req_idx[i];
+    // the working-set counts depend on the request's position only: their loads go out with
+    // the first ones, eight (layer, head) pairs per step, every load before any use
+    long long dsum = 0;  // sum over layers and KV heads of K^S - K^L
+    bool bad_ws = false;
+    const int nlh = P.L * P.H_kv;
+    for (int base = 0; base < nlh; base += 8) {
+      int ks[8], kl[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int lh = min(base + u, nlh - 1), l = lh / P.H_kv, h = lh - l * P.H_kv;
+        const int32_t* w = P.ws_counts + (((size_t)l * P.R + i) * P.H_kv + h) * 2;
+        ks[u] = w[0];
+        kl[u] = w[1];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {  // no branch, so the loads stay ahead of their uses
+        const bool in = base + u < nlh;
+        bad_ws |= in && (ks[u] < 0 || kl[u] < 0);
+        dsum += in ? (long long)ks[u] - kl[u] : 0ll;
+      }
+    }
+    inf.n = (nc > 0 && nc <= P.C_max) ? nc : 0;
     inf.r = r;
     bool ok = r >= 0 && r < P.B && nc >= 0 && nc <= P.C_max;
     int Pn = 0, ctx = 0;
@@ -181,29 +217,7 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
       n = ctx == 0 ? 0 : ((ctx + b - 1) / b - 1) * b;
       ok = n == nc;
     }
-    long long dsum = 0;  // sum over layers and KV heads of K^S - K^L
-    if (ok) {
-      // eight (layer, head) pairs per step, every load issued before any is used
-      bool bad_ws = false;
-      const int nlh = P.L * P.H_kv;
-      for (int base = 0; base < nlh; base += 8) {
-        int ks[8], kl[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int lh = min(base + u, nlh - 1), l = lh / P.H_kv, h = lh - l * P.H_kv;
-          const int32_t* w = P.ws_counts + (((size_t)l * P.R + i) * P.H_kv + h) * 2;
-          ks[u] = w[0];
-          kl[u] = w[1];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {  // no branch, so the loads stay ahead of their uses
-          const bool in = base + u < nlh;
-          bad_ws |= in && (ks[u] < 0 || kl[u] < 0);
-          dsum += in ? (long long)ks[u] - kl[u] : 0ll;
-        }
-      }
-      if (n > 0 && bad_ws) ok = false;
-    }
+    if (ok && n > 0 && bad_ws) ok = false;
     int flags = 0, ndest = 0;
     if (ok) {
       flags |= F_VALID;
@@ -281,8 +295,7 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
 
   // ---- C: allocation order (registers only): outcome, stack top before the pops, release base
   if (tid == 0) {
-    int top = *P.free_top;
-    if (top < 0 || top > P.num_pages) top = 0;
+    int top = s_top0;
     int nrel = 0, any = 0;
     for (int i = 0; i < R; ++i) {
       const int fl = s_flags[i];
@@ -467,6 +480,19 @@ __device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v)
   return gp::readlane63_u64(v);
 }
 
+// Compaction items of one compacting head, appended to the work list: the chunks from the one
+// holding its first changed page dp0 to the one holding its last destination page, each with every
+// part of the head dimension. The order of the list does not matter (items never share bytes, and
+// the pages a chunk reads from the next one are saved before any item runs).
+__device__ __forceinline__ void append_items(const CParams& P, int i, int h, int dp0, int n_dest) {
+  const int L = P.chunk_pages;
+  if (dp0 >= n_dest) return;
+  const int c0 = dp0 / L * P.npart;
+  const int cnt = ((n_dest + L - 1) / L - dp0 / L) * P.npart;
+  const int off = atomicAdd(P.n_items, cnt);
+  for (int k = 0; k < cnt; ++k) P.items[off + k] = make_int2(i * P.H_kv + h, c0 + k);
+}
+
 // Selection (Eq. 9-10) in three short launches over chunks of SEL_T pages (one page per
 // thread, so the k_loc quota of a page is ranked in registers).
 //   select_local: per chunk, the E smallest eviction keys (s, ~index) of the chunk: each wave
@@ -588,7 +614,11 @@ __global__ __launch_bounds__(GP_WAVE) void select_merge_kernel(CParams P) {
   if (lane < E) s_sorted[rank] = tok;
   __syncthreads();
   if (lane < E) P.ev[((size_t)i * P.H_kv + h) * P.max_evict + lane] = s_sorted[lane];
-  if (lane == 0) P.dp0[(size_t)i * P.H_kv + h] = min(s_sorted[0] / b, inf.first_repl);
+  if (lane == 0) {
+    const int dp0 = min(s_sorted[0] / b, inf.first_repl);
+    P.dp0[(size_t)i * P.H_kv + h] = dp0;
+    if (P.fuse_items) append_items(P, i, h, dp0, inf.n_dest);
+  }
 }
 
 template <int PB>
@@ -621,6 +651,127 @@ __global__ __launch_bounds__(SEL_T) void select_write_kernel(CParams P) {
       ++before;
     } else {
       out[t - before] = t;
+    }
+  }
+}
+
+// The three selection steps in one workgroup per (request, KV head), for calls with few requests:
+// the chunks of SEL_T pages are taken one after another, each leaving its E smallest eviction keys
+// merged into a running set of E in LDS; then the evicted list, the first changed page, kept_idx
+// and (with fuse_items) the compaction items of the head.
+template <int PB>
+__global__ __launch_bounds__(SEL_T) void select_fused_kernel(CParams P) {
+  constexpr int b = PB;
+  constexpr int NW = SEL_T / GP_WAVE;
+  const int h = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const Info inf = P.info[i];
+  const int n = inf.n;
+  int32_t* out = P.kept_idx + ((size_t)i * P.H_kv + h) * P.C_max;
+  if (inf.mode != MODE_COMPACT) {
+    for (int t = tid; t < n; t += SEL_T) out[t] = inf.mode == MODE_IDENTITY ? t : -1;
+    return;
+  }
+  const int K_t = inf.K_t, E = inf.E;
+  const int kloc = min(P.k_loc, b);
+  const bool pool_all = (long)(n / b) * kloc >= K_t;  // |S_loc| >= K_t: the K_t best of all of C
+  const float* as = P.a_short + ((size_t)i * P.H_kv + h) * P.C_max;
+  const float* al = P.a_long + ((size_t)i * P.H_kv + h) * P.C_max;
+  const int nch = (n + SEL_T * b - 1) / (SEL_T * b);
+  __shared__ unsigned long long s_cand[NW * MAX_EVICT];
+  __shared__ unsigned long long s_best[MAX_EVICT];
+  __shared__ int s_ev[MAX_EVICT];
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = (c * SEL_T + tid) * b;  // first candidate of this thread's page
+    uint32_t sv[b];
+#pragma unroll
+    for (int j = 0; j < b; j += 4) {
+      f32x4_t x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+      if (t0 < n) {  // pages are whole: t0 < n covers all b candidates
+        x = *reinterpret_cast<const f32x4_t*>(as + t0 + j);
+        y = *reinterpret_cast<const f32x4_t*>(al + t0 + j);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sv[j + e] = max(__float_as_uint(x[e]) & 0x7fffffffu, __float_as_uint(y[e]) & 0x7fffffffu);
+    }
+    unsigned long long key[b];
+#pragma unroll
+    for (int j = 0; j < b; ++j) {
+      bool cand = t0 < n;
+      if (cand && !pool_all) {
+        // rank of candidate j inside its page under (s desc, index asc): the k_loc best stay
+        int rank = 0;
+#pragma unroll
+        for (int u = 0; u < b; ++u) rank += (sv[u] > sv[j] || (sv[u] == sv[j] && u < j)) ? 1 : 0;
+        cand = rank >= kloc;
+      }
+      key[j] = cand ? (((unsigned long long)sv[j] << 32) | (0xffffffffu - (uint32_t)(t0 + j))) : ~0ull;
+    }
+    // each wave's E smallest
+    unsigned long long prev = 0;
+    for (int e = 0; e < E; ++e) {
+      unsigned long long m = ~0ull;
+#pragma unroll
+      for (int j = 0; j < b; ++j)
+        if ((e == 0 || key[j] > prev) && key[j] < m) m = key[j];
+      m = wave_min_u64(m);
+      prev = m;
+      if (lane == 0) s_cand[wv * MAX_EVICT + e] = m;
+    }
+    __syncthreads();
+    if (wv == 0) {
+      // the E smallest of the waves' survivors and the running set
+      constexpr int TOT = (NW + 1) * MAX_EVICT;
+      constexpr int PER = (TOT + GP_WAVE - 1) / GP_WAVE;
+      unsigned long long cv[PER];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int idx = lane + GP_WAVE * k;
+        unsigned long long v = ~0ull;
+        if (idx < NW * MAX_EVICT) v = (idx % MAX_EVICT) < E ? s_cand[idx] : ~0ull;
+        else if (idx < TOT && c > 0 && idx - NW * MAX_EVICT < E) v = s_best[idx - NW * MAX_EVICT];
+        cv[k] = v;
+      }
+      unsigned long long pv = 0;
+      for (int e = 0; e < E; ++e) {
+        unsigned long long m = ~0ull;
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+          if ((e == 0 || cv[k] > pv) && cv[k] < m) m = cv[k];
+        m = wave_min_u64(m);
+        pv = m;
+        if (lane == 0) s_best[e] = m;
+      }
+    }
+    __syncthreads();
+  }
+  // the evicted tokens sorted by index: lane e ranks the e-th smallest key's token among the E
+  if (wv == 0) {
+    const int tok = lane < E ? (int)(0xffffffffu - (uint32_t)(s_best[lane] & 0xffffffffu)) : INT_MAX;
+    int rank = 0;
+    for (int e = 0; e < E; ++e) rank += __shfl(tok, e, GP_WAVE) < tok ? 1 : 0;
+    if (lane < E) s_ev[rank] = tok;
+  }
+  __syncthreads();
+  if (tid < E) P.ev[((size_t)i * P.H_kv + h) * P.max_evict + tid] = s_ev[tid];
+  if (tid < E) out[K_t + tid] = -1;
+  const int dp0 = min(s_ev[0] / b, inf.first_repl);
+  if (tid == 0) {
+    P.dp0[(size_t)i * P.H_kv + h] = dp0;
+    if (P.fuse_items) append_items(P, i, h, dp0, inf.n_dest);
+  }
+  // kept_idx: kept token t goes to position t - #(evicted < t)
+  for (int c = 0; c < nch; ++c) {
+    const int t0 = (c * SEL_T + tid) * b;
+    if (t0 >= n) break;
+    int before = 0;  // evicted tokens below t0
+#pragma unroll
+    for (int e = 0; e < MAX_EVICT; ++e) before += (e < E && s_ev[e] < t0) ? 1 : 0;
+    for (int j = 0; j < b; ++j) {
+      const int t = t0 + j;
+      if (before < E && s_ev[before] == t) ++before;
+      else out[t - before] = t;
     }
   }
 }
@@ -718,7 +869,11 @@ __global__ __launch_bounds__(WIDE_T) void select_wide_kernel(CParams P) {
     int k = ex;
     for (int j = 0; j < WIDE_VPT; ++j)
       if ((evm >> j) & 1u) ev[k++] = t0 + j;
-    if (ex == 0) P.dp0[(size_t)i * P.H_kv + h] = min((t0 + __ffs(evm) - 1) / b, inf.first_repl);
+    if (ex == 0) {
+      const int dp0 = min((t0 + __ffs(evm) - 1) / b, inf.first_repl);
+      P.dp0[(size_t)i * P.H_kv + h] = dp0;
+      if (P.fuse_items) append_items(P, i, h, dp0, inf.n_dest);
+    }
   }
   if (live) {
     int before = ex;  // evicted tokens below t0 + j
@@ -1675,6 +1830,8 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
   P.max_evict = wide ? 2 * b : MAX_EVICT;
   P.npart = wide ? D * es / WIDE_PART : 1;
   P.log_kpq = ilog2(D * es / P.npart / 16);
+  // one layer of a uniform cache: the selection lists the compaction items itself
+  P.fuse_items = (L == 1 && !mixed) ? 1 : 0;
   P.log_b = ilog2(b);
   P.log_kq = ilog2(D * es / 16);
   P.log_vq = ilog2(b * es / 16);
@@ -1719,32 +1876,36 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
     // one decision and allocation per request for all layers (Eq. 8 over layers and KV heads)
     hipLaunchKernelGGL(decide_alloc_kernel, dim3(1), dim3(DA_THREADS), 0, s, layer(0));
     GP_CHECK_LAUNCH();
-    const int nch = (C_max + SEL_T * b - 1) / (SEL_T * b);
-    const dim3 g(nch, H_kv, R);
+    const dim3 gw(H_kv, R);
+    const int nch = (C_max + SEL_T * b - 1) / (SEL_T * b);  // chunks of the longest candidate set
     for (int l = 0; l < L; ++l) {  // selection per layer and KV head (Eq. 9-10)
       const CParams Q = layer(l);
       if (wide) {
-        const dim3 gw(H_kv, R);
         if (b == 64) hipLaunchKernelGGL(select_wide_kernel<2>, gw, dim3(WIDE_T), 0, s, Q);
         else if (b == 128) hipLaunchKernelGGL(select_wide_kernel<4>, gw, dim3(WIDE_T), 0, s, Q);
         else hipLaunchKernelGGL(select_wide_kernel<8>, gw, dim3(WIDE_T), 0, s, Q);
-        GP_CHECK_LAUNCH();
-      } else {
+      } else if (nch <= FUSED_MAX_CHUNKS) {
+        if (b == 16) hipLaunchKernelGGL(select_fused_kernel<16>, gw, dim3(SEL_T), 0, s, Q);
+        else hipLaunchKernelGGL(select_fused_kernel<32>, gw, dim3(SEL_T), 0, s, Q);
+      } else {  // longer candidate sets: the chunks of a head in parallel
+        const dim3 g(nch, H_kv, R);
         if (b == 16) hipLaunchKernelGGL(select_local_kernel<16>, g, dim3(SEL_T), 0, s, Q);
         else hipLaunchKernelGGL(select_local_kernel<32>, g, dim3(SEL_T), 0, s, Q);
         GP_CHECK_LAUNCH();
-        hipLaunchKernelGGL(select_merge_kernel, dim3(H_kv, R), dim3(GP_WAVE), 0, s, Q);
+        hipLaunchKernelGGL(select_merge_kernel, gw, dim3(GP_WAVE), 0, s, Q);
         GP_CHECK_LAUNCH();
         if (b == 16) hipLaunchKernelGGL(select_write_kernel<16>, g, dim3(SEL_T), 0, s, Q);
         else hipLaunchKernelGGL(select_write_kernel<32>, g, dim3(SEL_T), 0, s, Q);
-        GP_CHECK_LAUNCH();
       }
+      GP_CHECK_LAUNCH();
       if (mixed) {  // destination tags; every head rewrites from the first changed page
         hipLaunchKernelGGL(mixed_plan_kernel, dim3(R), dim3(256), 0, s, Q);
         GP_CHECK_LAUNCH();
       }
-      hipLaunchKernelGGL(chunk_list_kernel, dim3(1), dim3(DA_THREADS), 0, s, Q);
-      GP_CHECK_LAUNCH();
+      if (!P.fuse_items) {
+        hipLaunchKernelGGL(chunk_list_kernel, dim3(1), dim3(DA_THREADS), 0, s, Q);
+        GP_CHECK_LAUNCH();
+      }
     }
   }
   const int cus = device_cus();

@@ -4,14 +4,14 @@
 // (PASK App. B.2 / B.5 pages): fp8 and INT4 keys enter as their exact code values with the row
 // scale applied to the dot product, and released tokens are left out of every softmax.
 //
-// Three launches:
-//   1. prep:      one wave per boundary request, view and query head: RMS-calibrate the summary
-//                 to q_t and rotate it to the current position (float64 arithmetic, tiny).
-//   2. logits:    matrix-core contraction of every candidate key tile with the 2G calibrated
-//                 summaries of its KV head (keys as the 16-row operand, the 2G summaries as
-//                 columns; bf16 keys meet a hi+lo bf16 split of the fp32 summaries, fp32 keys
-//                 use the fp32 MFMA); logits go to the workspace with per-chunk (max, sum).
-//   3. working set: per (request, KV head, view) first the weights: the softmax of each of the
+// Two launches:
+//   1. logits:    each workgroup first RMS-calibrates the 2G summaries of its KV head to q_t and
+//                 rotates them to the current position (float64 arithmetic, into LDS), then
+//                 contracts its chunk of candidate key tiles with them on the matrix cores
+//                 (keys as the 16-row operand, the 2G summaries as columns; bf16 keys meet a
+//                 hi+lo bf16 split of the fp32 summaries, fp32 keys use the fp32 MFMA); logits
+//                 go to the workspace with per-chunk (max, sum).
+//   2. working set: per (request, KV head, view) first the weights: the softmax of each of the
 //                 G query heads' rows and their mean, written to a^S / a^L and kept in
 //                 registers; then the p-coverage size, exact on those fp32 weights: a binary
 //                 search over the weight bit patterns (float32 sums per thread, float64 across
@@ -21,6 +21,7 @@
 //                 matters most when the pass runs beside a decode that keeps HBM busy.
 #include "common.h"
 
+#include <algorithm>
 #include <cmath>
 
 namespace {
@@ -51,7 +52,6 @@ struct ScoreParams {
   float* a_long;
   int32_t* ws_counts;
   int32_t* n_cand;
-  float* qt;      // [R, 2, H_q, D]
   float* logits;  // [R, 2, H_q, C_max]  (log2 domain)
   float* stats;   // [R, 2, H_q, NCH, 2]
   int B, R, H_q, H_kv, G, D, page_size, num_pages, max_pages, num_slots, C_max, nch;
@@ -77,35 +77,32 @@ __device__ __forceinline__ int candidates(const ScoreParams& P, int i, int* r_ou
   return n > P.C_max ? -1 : n;
 }
 
-// ------------------------------------------------------------------------------ 1. prep
-// one wave per (boundary request, view, query head) row
-__global__ __launch_bounds__(256) void prep_kernel(ScoreParams P) {
-  const int i = blockIdx.x;
-  int r;
-  const int n = candidates(P, i, &r);
-  if (blockIdx.y == 0 && threadIdx.x == 0) P.n_cand[i] = n;
-  if (n < 0) return;
+// ------------------------------------------------------------------------------ 1. calibration
+// The 2G summary rows of KV head h of boundary request i (row c = view c / G, query head
+// h G + c % G), RMS-calibrated to q_t (Eq. 12) and rotated to the current position, in float64,
+// into s_qt[c][0 .. D). One wave per row (a wave takes rows w, w + 4, ...).
+__device__ __forceinline__ void calibrated_rows(const ScoreParams& P, int i, int r, int h,
+                                                float (*s_qt)[128]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int D = P.D, half = D / 2;
+  const int D = P.D, half = D / 2, G = P.G;
   const int slot = P.slot_ids[r];
   const double pos = (double)P.positions[r];
-  const int row = blockIdx.y * 4 + w;
-  if (row < 2 * P.H_q) {
-    const int x = row / P.H_q, g = row % P.H_q;
+  for (int c = w; c < 2 * G; c += LG_WAVES) {
+    const int x = c / G, g = h * G + c % G;
     double qv[2], sv[2];
     double sq = 0.0, ss = 0.0;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int d = lane + 64 * c;
-      qv[c] = sv[c] = 0.0;
+    for (int e = 0; e < 2; ++e) {
+      const int d = lane + 64 * e;
+      qv[e] = sv[e] = 0.0;
       if (d < D) {
         const size_t qi = ((size_t)r * P.H_q + g) * D + d;
-        qv[c] = P.q_bf16 ? (double)gp::bf16_bits_to_f32(static_cast<const uint16_t*>(P.q)[qi])
+        qv[e] = P.q_bf16 ? (double)gp::bf16_bits_to_f32(static_cast<const uint16_t*>(P.q)[qi])
                          : (double)static_cast<const float*>(P.q)[qi];
-        sv[c] = (double)P.qstate[(((size_t)slot * 2 + x) * P.H_q + g) * D + d];
+        sv[e] = (double)P.qstate[(((size_t)slot * 2 + x) * P.H_q + g) * D + d];
       }
-      sq += qv[c] * qv[c];
-      ss += sv[c] * sv[c];
+      sq += qv[e] * qv[e];
+      ss += sv[e] * sv[e];
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -113,28 +110,23 @@ __global__ __launch_bounds__(256) void prep_kernel(ScoreParams P) {
       ss += __shfl_xor(ss, o, GP_WAVE);
     }
     const double gamma = ss > 0.0 ? sqrt(sq / ss) : 0.0;  // RMS ratio (the 1/D cancels)
-    // calibrated vector into LDS-free registers, then rotate pairs (d, d + D/2)
-    double cv[2] = {gamma * sv[0], gamma * sv[1]};
+    const double cv[2] = {gamma * sv[0], gamma * sv[1]};
+    // the partner of element d is d +/- D/2: lane-local when D == 128, a shuffle when 64
     double part[2];
-    // the partner of element d is d +/- D/2: lane-local when D == 128 (c swaps), a shuffle when 64
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      if (D == 128) part[c] = cv[1 - c];
-      else part[c] = __shfl_xor(cv[0], 32, GP_WAVE);
-    }
+    for (int e = 0; e < 2; ++e) part[e] = D == 128 ? cv[1 - e] : __shfl_xor(cv[0], 32, GP_WAVE);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int d = lane + 64 * c;
+    for (int e = 0; e < 2; ++e) {
+      const int d = lane + 64 * e;
       if (d >= D) continue;
-      const int j = d % half;
-      double out = cv[c];
+      double out = cv[e];
       if (P.rope_theta > 0.0) {
-        const double ang = pos * P.inv_freq[j];
+        const double ang = pos * P.inv_freq[d % half];
         double sn, cs;
         sincos(ang, &sn, &cs);
-        out = (d < half) ? cv[c] * cs - part[c] * sn : part[c] * sn + cv[c] * cs;
+        out = (d < half) ? cv[e] * cs - part[e] * sn : part[e] * sn + cv[e] * cs;
       }
-      P.qt[(((size_t)i * 2 + x) * P.H_q + g) * D + d] = (float)out;
+      s_qt[c][d] = (float)out;
     }
   }
 }
@@ -147,6 +139,7 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
   const int h = blockIdx.x, chunk = blockIdx.y, i = blockIdx.z;
   int r;
   const int n = candidates(P, i, &r);
+  if (h == 0 && chunk == 0 && threadIdx.x == 0) P.n_cand[i] = n;
   const int tile0 = chunk * CHUNK_TILES;
   if (n <= 0 || tile0 * 16 >= n) return;
   const int tile1 = min(n >> 4, tile0 + CHUNK_TILES);
@@ -156,8 +149,52 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
   const bool col_ok = n16 < 2 * G;
   const int x = n16 / G, g = n16 % G;
   const int hq = h * G + g;
+  // this wave's tiles are tile0 + w + k LG_WAVES, k < nt (nt <= CHUNK_TILES / LG_WAVES): lane k
+  // fetches the page id and tag of tile k up front, and the key rows of plain (bf16 / fp32)
+  // tiles are loaded two tiles ahead of their use, with no branch around the loads (a tile
+  // past the wave's last, or of another format, reads the pool's first bytes and is unused)
+  constexpr int NKW = BF16 ? D / 32 : D / 16;  // 16-byte key pieces of a plain tile per lane
+  const int nt = tile1 > tile0 + w ? (tile1 - tile0 - w + LG_WAVES - 1) / LG_WAVES : 0;
+  int pg_l = -1, tag_l = GP_TAG_BF16;
+  if (lane < nt) {
+    const int tl = tile0 + w + lane * LG_WAVES;
+    const int pg = P.block_tables[(size_t)r * P.max_pages + (tl << 4) / b];
+    bool ok = pg >= 0 && pg < P.num_pages;
+    if (ok && P.page_tag) {
+      tag_l = P.page_tag[pg];
+      ok = tag_l != GP_TAG_RELEASE;  // released tokens take no part in the softmax
+    }
+    pg_l = ok ? pg : -1;
+  }
+  auto load_plain = [&](int k, u32x4_t (&kw)[NKW]) {
+    const int kc = min(k, 63);
+    const int pg = __builtin_amdgcn_readlane(pg_l, kc), tag = __builtin_amdgcn_readlane(tag_l, kc);
+    const int tok0 = (tile0 + w + k * LG_WAVES) << 4;
+    const bool plain = k < nt && pg >= 0 && tag == GP_TAG_BF16;
+    const size_t base = plain ? ((size_t)pg * P.H_kv + h) * (size_t)b * D + (size_t)(tok0 % b + n16) * D : 0;
+    if constexpr (BF16) {
+      const u32x4_t* kr = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(P.k) + base + (plain ? 8 * g4 : 0));
+#pragma unroll
+      for (int kk = 0; kk < NKW; ++kk) kw[kk] = kr[plain ? 4 * kk : 0];
+    } else {
+      const u32x4_t* kr = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(P.k) + base + (plain ? (D / 4) * g4 : 0));
+#pragma unroll
+      for (int c = 0; c < NKW; ++c) kw[c] = kr[plain ? c : 0];
+    }
+  };
+  // the first two tiles' keys are in flight while the summaries are calibrated
+  u32x4_t ring[2][NKW];
+  load_plain(0, ring[0]);
+  load_plain(1, ring[1]);
+
+  // the calibrated, rotated summaries of this KV head (each workgroup of the head computes them:
+  // a few hundred float64 operations, cheaper than a launch of their own,
+  // and hidden behind the first key loads)
+  __shared__ float s_qt[16][128];
+  calibrated_rows(P, i, r, h, s_qt);
+  __syncthreads();
   // columns past 2G read the first summary row (no branch around the loads) and use zeros
-  const float* qrow = col_ok ? P.qt + (((size_t)i * 2 + x) * P.H_q + hq) * D : P.qt;
+  const float* qrow = s_qt[col_ok ? n16 : 0];
 
   // summary operand: column n16 = (view x, head g)
   u32x4_t qhi[BF16 ? D / 32 : D / 16], qlo[BF16 ? D / 32 : 1];
@@ -192,39 +229,6 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
 
   float m_run = -INFINITY, l_run = 0.f;
   float* lrow = P.logits + (((size_t)i * 2 + x) * P.H_q + hq) * P.C_max;
-  // this wave's tiles are tile0 + w + k LG_WAVES, k < nt (nt <= CHUNK_TILES / LG_WAVES): lane k
-  // fetches the page id and tag of tile k up front, and the key rows of plain (bf16 / fp32)
-  // tiles are loaded two tiles ahead of their use, with no branch around the loads (a tile
-  // past the wave's last, or of another format, reads the pool's first bytes and is unused)
-  constexpr int NKW = BF16 ? D / 32 : D / 16;  // 16-byte key pieces of a plain tile per lane
-  const int nt = tile1 > tile0 + w ? (tile1 - tile0 - w + LG_WAVES - 1) / LG_WAVES : 0;
-  int pg_l = -1, tag_l = GP_TAG_BF16;
-  if (lane < nt) {
-    const int tl = tile0 + w + lane * LG_WAVES;
-    const int pg = P.block_tables[(size_t)r * P.max_pages + (tl << 4) / b];
-    bool ok = pg >= 0 && pg < P.num_pages;
-    if (ok && P.page_tag) {
-      tag_l = P.page_tag[pg];
-      ok = tag_l != GP_TAG_RELEASE;  // released tokens take no part in the softmax
-    }
-    pg_l = ok ? pg : -1;
-  }
-  auto load_plain = [&](int k, u32x4_t (&kw)[NKW]) {
-    const int kc = min(k, 63);
-    const int pg = __builtin_amdgcn_readlane(pg_l, kc), tag = __builtin_amdgcn_readlane(tag_l, kc);
-    const int tok0 = (tile0 + w + k * LG_WAVES) << 4;
-    const bool plain = k < nt && pg >= 0 && tag == GP_TAG_BF16;
-    const size_t base = plain ? ((size_t)pg * P.H_kv + h) * (size_t)b * D + (size_t)(tok0 % b + n16) * D : 0;
-    if constexpr (BF16) {
-      const u32x4_t* kr = reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(P.k) + base + (plain ? 8 * g4 : 0));
-#pragma unroll
-      for (int kk = 0; kk < NKW; ++kk) kw[kk] = kr[plain ? 4 * kk : 0];
-    } else {
-      const u32x4_t* kr = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(P.k) + base + (plain ? (D / 4) * g4 : 0));
-#pragma unroll
-      for (int c = 0; c < NKW; ++c) kw[c] = kr[plain ? c : 0];
-    }
-  };
   auto process = [&](int k, const u32x4_t (&kw)[NKW]) {
     const int pg = __builtin_amdgcn_readlane(pg_l, k), tag = __builtin_amdgcn_readlane(tag_l, k);
     const int tok0 = (tile0 + w + k * LG_WAVES) << 4;
@@ -299,9 +303,6 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
     l_run = l_run * gp::safe_exp2_diff(m_run, m_new) + s;
     m_run = m_new;
   };
-  u32x4_t ring[2][NKW];
-  load_plain(0, ring[0]);
-  load_plain(1, ring[1]);
   for (int k0 = 0; k0 < nt; k0 += 2) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -405,6 +406,7 @@ __device__ __forceinline__ int cmp_p(const uint32_t a[6], const uint32_t p[5]) {
 }
 
 constexpr int WS_WAVES = WS_THREADS / GP_WAVE;
+static_assert(WS_WAVES <= 16, "block reductions hand one partial per wave to the 16 lanes of a DPP row");
 
 __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) {
   const int row = blockIdx.x, i = blockIdx.y;
@@ -417,9 +419,10 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     return;
   }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int NT = WS_THREADS;
   // weights per thread that can be candidates: the rest of a thread's 32 slots hold zeros, which
   // no sum, count or maximum below depends on, so the loops skip them (a uniform bound)
-  const int nv = (n + WS_THREADS - 1) / WS_THREADS;
+  const int nv = (n + NT - 1) / NT;
   // Block reductions with one barrier each: wave partials alternate between two scratch
   // buffers, so a buffer is rewritten only after every thread has passed another barrier.
   __shared__ double s_d[2][WS_WAVES];
@@ -436,12 +439,10 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
       s_dc[ph][w] = cw;
     }
     __syncthreads();
-    double t = 0.0, tc = 0.0;
-#pragma unroll
-    for (int k = 0; k < WS_WAVES; ++k) {
-      t += s_d[ph][k];
-      tc += s_dc[ph][k];
-    }
+    // lane k of every row takes wave k's partial; the row reduction leaves the total everywhere
+    const int k = lane & 15;
+    const double t = gp::row16_sum_f64(k < WS_WAVES ? s_d[ph][k] : 0.0);
+    const double tc = gp::row16_sum_f64(k < WS_WAVES ? s_dc[ph][k] : 0.0);
     ph ^= 1;
     *c_out = (uint32_t)tc;
     return t;
@@ -450,9 +451,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     v = gp::wave_sum_f64(v);
     if (lane == 0) s_d[ph][w] = v;
     __syncthreads();
-    double t = 0.0;
-#pragma unroll
-    for (int k = 0; k < WS_WAVES; ++k) t += s_d[ph][k];
+    const double t = gp::row16_sum_f64((lane & 15) < WS_WAVES ? s_d[ph][lane & 15] : 0.0);
     ph ^= 1;
     return t;
   };
@@ -464,21 +463,14 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     }
     __syncthreads();
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint64_t t = 0;
-#pragma unroll
-      for (int k = 0; k < WS_WAVES; ++k) t += s_u[ph][c][k];
-      v[c] = t;
-    }
+    for (int c = 0; c < 8; ++c) v[c] = gp::row16_sum_u64((lane & 15) < WS_WAVES ? s_u[ph][c][lane & 15] : 0ull);
     ph ^= 1;
   };
   auto max_x = [&](uint32_t v) -> uint32_t {
     v = gp::wave_max_u32(v);
     if (lane == 0) s_x[ph][w] = v;
     __syncthreads();
-    uint32_t t = 0;
-#pragma unroll
-    for (int k = 0; k < WS_WAVES; ++k) t = max(t, s_x[ph][k]);
+    const uint32_t t = gp::row16_max_u32((lane & 15) < WS_WAVES ? s_x[ph][lane & 15] : 0u);
     ph ^= 1;
     return t;
   };
@@ -491,15 +483,15 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   {
     // one wave per query head: lane j holds chunk j's (max, sum)
     const int nchunks = (n + CHUNK_TILES * 16 - 1) / (CHUNK_TILES * 16);  // <= 64
-    if (w < G) {
-      const float* st = P.stats + (((size_t)i * 2 + x) * P.H_q + h * G + w) * P.nch * 2;
+    for (int g = w; g < G; g += WS_WAVES) {
+      const float* st = P.stats + (((size_t)i * 2 + x) * P.H_q + h * G + g) * P.nch * 2;
       const float mj = lane < nchunks ? st[2 * lane] : -INFINITY;
       const float lj = lane < nchunks ? st[2 * lane + 1] : 0.f;
       const float m = gp::wave_max(mj);
       const float l = gp::wave_sum(lj * gp::safe_exp2_diff(mj, m));
       if (lane == 0) {
-        s_m[w] = m;
-        s_inv[w] = l > 0.f ? 1.f / l : 0.f;
+        s_m[g] = m;
+        s_inv[g] = l > 0.f ? 1.f / l : 0.f;
       }
     }
     __syncthreads();
@@ -510,31 +502,35 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     float acc[WS_VPT];
 #pragma unroll
     for (int j = 0; j < WS_VPT; ++j) acc[j] = 0.f;
-    for (int g = 0; g < G; ++g) {
-      const float* lg = P.logits + (((size_t)i * 2 + x) * P.H_q + h * G + g) * P.C_max;
-      const float m = s_m[g], inv = s_inv[g];
-      // loads in batches of 16, each issued before any is used: indexes past the candidates
-      // read candidate 0 (no branch per element) and are dropped below
+    // four weights of every query head per batch, all loads of a batch issued before any is
+    // used; indexes past the candidates read candidate 0 (no branch per element) and are
+    // dropped below
+    const float* lg0 = P.logits + (((size_t)i * 2 + x) * P.H_q + h * G) * P.C_max;
 #pragma unroll
-      for (int j0 = 0; j0 < WS_VPT; j0 += 16) {
-        float z[16];
+    for (int j0 = 0; j0 < WS_VPT; j0 += 4) {
+      if (j0 >= nv) continue;  // uniform: skips the batch without breaking the unrolling
+      float z[8][4];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int t = threadIdx.x + (j0 + j) * WS_THREADS;
-          z[j] = j0 + j < nv ? lg[t < n ? t : 0] : 0.f;
+      for (int g = 0; g < 8; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = threadIdx.x + (j0 + j) * NT;
+          z[g][j] = (g < G && j0 + j < nv) ? lg0[(size_t)g * P.C_max + (t < n ? t : 0)] : 0.f;
         }
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (j0 + j < nv) acc[j0 + j] += gp::safe_exp2_diff(z[j], m) * inv;
-      }
+      for (int g = 0; g < 8; ++g)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (g < G && j0 + j < nv) acc[j0 + j] += gp::safe_exp2_diff(z[g][j], s_m[g]) * s_inv[g];
     }
     const float invG = 1.0f / (float)G;
 #pragma unroll
     for (int j = 0; j < WS_VPT; ++j) {
-      const int t = threadIdx.x + j * WS_THREADS;
+      const int t = threadIdx.x + j * NT;
       const float v = acc[j] * invG;
-      if (t < n) dst[t] = v;
-      u[j] = t < n ? __float_as_uint(v) & 0x7fffffffu : 0u;
+      const bool mine = j < nv && t < n;
+      if (mine) dst[t] = v;
+      u[j] = mine ? __float_as_uint(v) & 0x7fffffffu : 0u;
     }
   }
   double p_f64 = 0.0;
@@ -613,14 +609,20 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < WS_VPT; ++j) {
-      if (j < nv && u[j] >= lo && u[j] < hi) {
-        const uint32_t k = atomicAdd(&s_ntail, 1u);
-        if (k < (uint32_t)WS_TAIL) s_tail[k] = __uint_as_float(u[j]);
-      }
+      const bool in = j < nv && u[j] >= lo && u[j] < hi;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(in);
+      if (m == 0) continue;
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&s_ntail, (uint32_t)__builtin_popcountll(m));
+      base = __shfl(base, 0, GP_WAVE);
+      const uint32_t k = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (in && k < (uint32_t)WS_TAIL) s_tail[k] = __uint_as_float(u[j]);
     }
     __syncthreads();
     if (w == 0) {
       const uint32_t nt = min(s_ntail, (uint32_t)WS_TAIL);  // == c_lo - c_hi <= WS_TAIL
+      const uint32_t kn = (nt + GP_WAVE - 1) / GP_WAVE;       // weights per lane, uniform
       uint32_t x[WS_TAIL / GP_WAVE];
 #pragma unroll
       for (int k = 0; k < WS_TAIL / GP_WAVE; ++k) {
@@ -630,10 +632,11 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
       uint32_t l2 = lo, h2 = hi;
       while (h2 - l2 > 1u) {
         const uint32_t mid = l2 + (h2 - l2) / 2;
-        float sl = 0.f;
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < WS_TAIL / GP_WAVE; ++k) sl += x[k] >= mid ? __uint_as_float(x[k]) : 0.f;
-        const double sm = m_hi + gp::wave_sum_f64((double)sl);
+        for (int k = 0; k < WS_TAIL / GP_WAVE; ++k)
+          if ((uint32_t)k < kn) s4[k & 3] += x[k] >= mid ? __uint_as_float(x[k]) : 0.f;
+        const double sm = m_hi + gp::wave_sum_f64((double)(s4[0] + s4[1]) + (double)(s4[2] + s4[3]));
         if (sm >= p_f64) l2 = mid; else h2 = mid;
       }
       if (lane == 0) s_lo = l2;
@@ -764,8 +767,7 @@ extern "C" size_t gp_score_and_working_set_workspace_size(int R, int H_q, int H_
   if (R <= 0 || H_q <= 0 || head_dim <= 0 || C_max <= 0) return 0;
   const size_t nch = (C_max + CHUNK_TILES * 16 - 1) / (CHUNK_TILES * 16);
   const size_t c_pad = (size_t)((C_max + 3) / 4) * 4;
-  return ((size_t)R * 2 * H_q * head_dim + (size_t)R * 2 * H_q * c_pad + (size_t)R * 2 * H_q * nch * 2) *
-         sizeof(float);
+  return ((size_t)R * 2 * H_q * c_pad + (size_t)R * 2 * H_q * nch * 2) * sizeof(float);
 }
 
 extern "C" int gp_score_and_working_set(const void* q, int q_dtype, int B, int H_q, const float* qstate,
@@ -836,13 +838,10 @@ extern "C" int gp_score_and_working_set(const void* q, int q_dtype, int B, int H
     P.inv_freq[j] = (rope_theta > 0.f && j < D / 2) ? std::pow((double)rope_theta, -2.0 * j / D) : 0.0;
   p_to_fixed(p, P.p_fixed);
   float* ws = static_cast<float*>(workspace);
-  P.qt = ws;
-  P.logits = P.qt + (size_t)R * 2 * H_q * D;
+  P.logits = ws;
   P.stats = P.logits + (size_t)R * 2 * H_q * (size_t)((C_max + 3) / 4) * 4;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(prep_kernel, dim3(R, (2 * H_q + 3) / 4), dim3(256), 0, s, P);
-  GP_CHECK_LAUNCH();
   dim3 lg(H_kv, P.nch, R);
   if (kv->page_tag) {  // mixed caches are bf16 (checked above)
     if (D == 64) hipLaunchKernelGGL((logits_kernel<64, true, true>), lg, dim3(LG_THREADS), 0, s, P);
