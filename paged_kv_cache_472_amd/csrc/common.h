@@ -222,6 +222,17 @@ __device__ __forceinline__ double wave_sum_f64(double x) {
   return __builtin_bit_cast(double, readlane63_u64(__builtin_bit_cast(uint64_t, x)));
 }
 
+// Maximum with the lane 16 (or 32) positions away: gfx950's lane-swap instructions exchange the
+// odd and even rows of a wave (or its two halves) in the VALU, without the LDS permute path.
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Sums and maxima over the 16 lanes of each DPP row (quad swaps, half-row and row mirrors): every
 // lane of a row ends with its row's result. A block reduction hands its (at most 16) wave
 // partials to the lanes of a row this way: one LDS read per lane instead of 16.

@@ -213,13 +213,17 @@ struct WaveState {
   float m_run, l_run;
 };
 
-template <int D, int KIND>
+// TAIL: the tile holds the request's last token (tok0 + 16 > ctx), so some of its tokens lie past
+// the context and are masked. Only such a tile needs the masks and the guards against -inf logits
+// (every token of another tile is live, so its logits and the running maximum are finite); the
+// walk branches between the two forms once per tile.
+template <int D, int KIND, bool TAIL>
 __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRaw<D, KIND>& cur,
                                              int tok0, int ctx, int lane,
                                              const u32x4_t* qf, const f16x8_t* qh,
                                              WaveState<D>& st) {
   const int g4 = lane >> 4;
-  const bool tail = tok0 + 16 > ctx;
+  constexpr bool tail = TAIL;
   // per-token scales of the lane's 4 tokens (fp8: fp32 values; INT4: halves)
   constexpr bool SCALED = KIND == KIND_INT4 || KIND == KIND_FP8;
   float ks[4], vs[4];
@@ -261,17 +265,17 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
     }
   }
   float sv[4];
-  float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float z = sacc[i];
     if constexpr (SCALED) z *= ks[i];
-    const bool ok = tok0 + 4 * g4 + i < ctx;
-    sv[i] = ok ? z * p.scale_log2 : -INFINITY;
-    mx = fmaxf(mx, sv[i]);
+    sv[i] = z * p.scale_log2;
+    if constexpr (TAIL)
+      if (tok0 + 4 * g4 + i >= ctx) sv[i] = -INFINITY;
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, GP_WAVE));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, GP_WAVE));
+  float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  mx = gp::xor16_max(mx);
+  mx = gp::xor32_max(mx);
   // lazy rescaling: the running maximum moves only when a logit exceeds it by more than 2^8
   // (log2 domain 8), so the weights stay below 256 and most tiles skip the rescale of the rows
   const bool move = mx > st.m_run + 8.0f;
@@ -281,7 +285,8 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
   float psum = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    pv[i] = gp::safe_exp2_diff(sv[i], m_new);
+    // outside a tail tile the logits and m_new are finite (m_new >= this tile's maximum)
+    pv[i] = TAIL ? gp::safe_exp2_diff(sv[i], m_new) : __builtin_amdgcn_exp2f(sv[i] - m_new);
     psum += pv[i];
   }
   st.l_run = st.l_run * alpha + psum;
@@ -315,7 +320,8 @@ __device__ __forceinline__ void process_tile(const DecodeParams& p, const TileRa
       pw[i] = pv[i];
       if constexpr (SCALED) {
         pw[i] *= vs[i];
-        if (pv[i] == 0.f) pw[i] = 0.f;  // scales of masked tokens may be poison
+        if constexpr (TAIL)
+          if (pv[i] == 0.f) pw[i] = 0.f;  // scales of masked tokens may be poison
       }
     }
     if constexpr (KIND == KIND_INT4) {
@@ -374,16 +380,30 @@ __device__ __forceinline__ void walk_tiles(const DecodeParams& p, const int* lst
     rt[q] = __builtin_amdgcn_readfirstlane(lst_tile[e]);
     load_tile<D, KIND>(p, rc[q], rt[q] << 4, h, lane, ring[q]);
   }
+  // only the list's last tile can hold the request's last token: the loop decodes every other
+  // tile without masks, and that one, if it is a tail tile, after the loop (its ring slot then
+  // holds it again: slots past the end reload the last entry)
+  // (fp32 caches, used for small checks only, keep one tile form: their registers are tight)
+  constexpr bool SPLIT = KIND != KIND_F32;
+  const int last_tok0 = __builtin_amdgcn_readfirstlane(lst_tile[n - 1]) << 4;
+  const bool has_tail = SPLIT && last_tok0 + 16 > ctx;
+  const int n_main = has_tail ? n - 1 : n;
   for (int e0 = 0; e0 < n; e0 += RING) {
 #pragma unroll
     for (int q = 0; q < RING; ++q) {
       const int e = e0 + q;
-      if (e < n) process_tile<D, KIND>(p, ring[q], rt[q] << 4, ctx, lane, qf, qh, st);
+      if (e < n_main) process_tile<D, KIND, !SPLIT>(p, ring[q], rt[q] << 4, ctx, lane, qf, qh, st);
       const int ex = min(e + RING, n - 1);
       rc[q] = __builtin_amdgcn_readfirstlane(lst_code[ex]);
       rt[q] = __builtin_amdgcn_readfirstlane(lst_tile[ex]);
       load_tile<D, KIND>(p, rc[q], rt[q] << 4, h, lane, ring[q]);
     }
+  }
+  if (SPLIT && has_tail) {
+    const int slot = (n - 1) % RING;
+#pragma unroll
+    for (int q = 0; q < RING; ++q)
+      if (q == slot) process_tile<D, KIND, true>(p, ring[q], last_tok0, ctx, lane, qf, qh, st);
   }
 }
 
