@@ -415,9 +415,8 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
     boundary request forced to compress, so each one moves its tokens) on workload `name` with
     `b`-token pages. The integer page state and the boundary requests' K/V pages are restored
     before every repetition, outside the timed region; the median of `reps` after 3 warmups.
-    Also the same pass for the first boundary request alone (R = 1). Bytes per request: keys
-    of C read, both score planes written and read back, and the K/V of the tokens that shift,
-    read and written."""
+    Also the same pass for the first boundary request alone (R = 1). Bytes per request: keys of C read, both score planes written and read
+    back, and the K/V of the tokens that shift, read and written."""
     dev = "cuda:0"
     wl = make_workload(name, "full", device=dev, page_size=b)
     if wl.mixed:
@@ -447,36 +446,51 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
     saved = {n: getattr(wl, n).index_select(0, pidx) for n in pools}
     tag0 = wl.page_tag.clone() if wl.mixed else None
     out = {}
+
+    def restore():
+        for n in names:
+            getattr(wl, n).copy_(ints[n])
+        for n in pools:
+            getattr(wl, n).index_copy_(0, pidx, saved[n])
+        if tag0 is not None:
+            wl.page_tag.copy_(tag0)
+
     for label, req in (("all", req_all), ("one", req_all[:1].clone())):
         R = req.numel()
         pol = torch.full((R,), 1, dtype=torch.int32, device=dev)   # forced compress
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        t_s, t_c = [], []
-        for it in range(reps + 3):
-            for n in names:
-                getattr(wl, n).copy_(ints[n])
-            for n in pools:
-                getattr(wl, n).index_copy_(0, pidx, saved[n])
-            if tag0 is not None:
-                wl.page_tag.copy_(tag0)
-            ev[0].record()
+
+        def score():
             gp.gp_score_and_working_set(wl.q, wl.qstate, wl.slot_ids, req, path.cache,
                                         wl.block_tables, wl.context_lens, wl.positions,
                                         wl.rope_theta, wl.p, wl.sm_scale, path.C_max,
                                         a_short=path.a_s[:R], a_long=path.a_l[:R],
                                         ws_counts=path.wsc[:R], n_cand=path.ncand[:R],
                                         workspace=path.sws)
-            ev[1].record()
+
+        def compact():
             gp.gp_compact_or_grow(req, path.a_s[:R], path.a_l[:R], path.wsc[:R], path.ncand[:R],
                                   wl.tau, wl.k_loc, 0, path.cache, wl.block_tables, wl.n_pages,
                                   wl.context_lens, wl.refcount, wl.free_stack, wl.free_top,
                                   policies=pol, decision=path.dec[:R], kept_idx=path.kept[:R],
                                   workspace=path.cws)
-            ev[2].record()
-            torch.cuda.synchronize()
-            if it >= 3:
-                t_s.append(ev[0].elapsed_time(ev[1]))
-                t_c.append(ev[1].elapsed_time(ev[2]))
+
+        def timed(run_score, run_compact):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            t_s, t_c = [], []
+            for it in range(reps + 3):
+                restore()
+                ev[0].record()
+                run_score()
+                ev[1].record()
+                run_compact()
+                ev[2].record()
+                torch.cuda.synchronize()
+                if it >= 3:
+                    t_s.append(ev[0].elapsed_time(ev[1]))
+                    t_c.append(ev[1].elapsed_time(ev[2]))
+            return float(np.median(t_s)), float(np.median(t_c))
+
+        ms_s, ms_c = timed(score, compact)
         dec = path.dec[:R].cpu().numpy()
         nc = path.ncand[:R].cpu().numpy().astype(np.int64)
         kept = path.kept[:R].cpu().numpy()
@@ -517,7 +531,6 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
                 score_bytes += int(sum(row_bytes.get(int(t), 0) for t in tg)) * wl.H_kv
             score_bytes += 4 * wl.H_kv * c * 4          # both score planes written and read
         byts = score_bytes + moved
-        ms_s, ms_c = float(np.median(t_s)), float(np.median(t_c))
         ms = ms_s + ms_c
         out[label] = dict(requests=int(R), us_per_request=round(ms * 1e3 / R, 1),
                           score_us=round(ms_s * 1e3, 1), compact_us=round(ms_c * 1e3, 1),

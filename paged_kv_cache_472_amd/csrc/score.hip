@@ -33,6 +33,10 @@ constexpr int WS_THREADS = 1024;
 constexpr int WS_VPT = 32;        // weights per thread held in registers (|C| <= 32768)
 constexpr int WS_MAX_C = WS_THREADS * WS_VPT;
 constexpr int WS_TAIL = 256;      // weights left in the search interval when one wave finishes it
+// Relative rounding bound of a block's float64 sum of nonnegative weights: a thread adds its (at
+// most 32) weights in sequence, a wave reduces in 6 levels, the 16 wave partials in 4: at most 42
+// roundings on any path, each a relative 2^-53; the bound takes 64.
+constexpr double SUM_ERR = 64.0 * 0x1p-53;
 
 struct ScoreParams {
   const void* q;
@@ -537,30 +541,42 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   for (int k = 4; k >= 0; --k) p_f64 = p_f64 * 4294967296.0 + (double)P.p_fixed[k];
   p_f64 = ldexp(p_f64, -149);
 
-  // exact total mass: if it never reaches p, K = |C|; also the largest weight
+  // Total mass: if it never reaches p, K = |C|; also the largest weight. The float64 sum of the
+  // nonnegative weights is within SUM_ERR of the exact one (relative), so it decides unless p lies
+  // inside that bound; then the exact 160-bit sum does.
   uint32_t vmax;
   {
-    Acc5 a = {};
+    double ts = 0.0;
     uint32_t m = 0u;
 #pragma unroll
     for (int j = 0; j < WS_VPT; ++j) {
       if (j < nv) {
-        acc_add(a, u[j]);
+        ts += (double)__uint_as_float(u[j]);
         m = max(m, u[j]);
       }
     }
-    uint64_t t[8] = {a.d[0], a.d[1], a.d[2], a.d[3], a.d[4], a.d[5], 0ull, 0ull};
-    sum_u8(t);
-    Acc5 tt;
+    const double tot_f = sum_d(ts);
+    vmax = max_x(m);
+    const double err = SUM_ERR * tot_f;
+    bool below = tot_f + err < p_f64;
+    if (!below && tot_f - err < p_f64) {  // undecided: exact
+      Acc5 a = {};
 #pragma unroll
-    for (int k = 0; k < 6; ++k) tt.d[k] = t[k];
-    uint32_t tot[6];
-    acc_norm(tt, tot);
-    if (cmp_p(tot, P.p_fixed) < 0) {
+      for (int j = 0; j < WS_VPT; ++j)
+        if (j < nv) acc_add(a, u[j]);
+      uint64_t t[8] = {a.d[0], a.d[1], a.d[2], a.d[3], a.d[4], a.d[5], 0ull, 0ull};
+      sum_u8(t);
+      Acc5 tt;
+#pragma unroll
+      for (int k = 0; k < 6; ++k) tt.d[k] = t[k];
+      uint32_t tot[6];
+      acc_norm(tt, tot);
+      below = cmp_p(tot, P.p_fixed) < 0;
+    }
+    if (below) {
       if (threadIdx.x == 0) *out = n;
       return;
     }
-    vmax = max_x(m);
   }
   // bisection for the largest bit pattern T with mass(weights >= T) >= p. A thread's 32 weights
   // are summed in float32 (the search only has to land on or next to the threshold; the
@@ -652,8 +668,63 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     for (int j = 0; j < WS_VPT; ++j) if (j < nv && u[j] <= lo) best = max(best, u[j]);
     T = max_x(best);
   }
-  // exact certificate: mass(> T) < p <= mass(>= T); move T to a neighbour value until it holds
+  // next smaller / next larger weight value present in the row
+  auto below_T = [&](uint32_t T0) {
+    uint32_t best = 0u;
+#pragma unroll
+    for (int j = 0; j < WS_VPT; ++j) if (j < nv && u[j] < T0) best = max(best, u[j]);
+    return max_x(best);
+  };
+  auto above_T = [&](uint32_t T0) {
+    uint32_t best = 0u;
+#pragma unroll
+    for (int j = 0; j < WS_VPT; ++j) if (j < nv && u[j] > T0) best = max(best, ~u[j]);
+    return ~max_x(best);
+  };
+  // certificate: mass(> T) < p <= mass(>= T); move T to a neighbour value until it holds. The
+  // float64 sums, with their rounding bound, decide it and K = #(> T) + ceil((p - mass(> T)) / T)
+  // whenever the bound leaves no doubt; otherwise the exact 160-bit sums below do.
   for (int iter = 0; iter < 64; ++iter) {
+    {
+      double gs = 0.0;
+      uint32_t cc = 0;  // #(> T) << 16 | #(== T): each at most 32768 over the block
+#pragma unroll 4
+      for (int j = 0; j < WS_VPT; ++j) {
+        if (j >= nv) continue;
+        if (u[j] > T) {
+          gs += (double)__uint_as_float(u[j]);
+          cc += 1u << 16;
+        } else if (u[j] == T) {
+          cc += 1u;
+        }
+      }
+      uint32_t cnt;
+      const double mgt_f = sum_dc(gs, cc, &cnt);
+      const uint32_t n_gt = cnt >> 16, n_eq = cnt & 0xffffu;
+      const double Tf = (double)__uint_as_float(T);
+      const double e_gt = SUM_ERR * mgt_f;
+      const double mge_f = mgt_f + (double)n_eq * Tf;  // the product is exact: one rounding
+      const double e_ge = e_gt + 0x1p-52 * mge_f;
+      if (T != 0u && mge_f + e_ge < p_f64) {  // mass(>= T) < p: too high
+        T = below_T(T);
+        continue;
+      }
+      if (mgt_f - e_gt >= p_f64) {             // mass(> T) >= p: too low
+        T = above_T(T);
+        continue;
+      }
+      if (T != 0u && mge_f - e_ge >= p_f64 && mgt_f + e_gt < p_f64) {
+        // X = (p - mass(> T)) / T in (0, #(== T)]: its ceiling is certain when no integer lies
+        // within the bound of X
+        const double X = (p_f64 - mgt_f) / Tf;
+        const double eX = 2.0 * ((e_gt + 0x1p-53 * (p_f64 - mgt_f)) / Tf + 0x1p-52 * X);
+        const double k1 = ceil(X - eX), k2 = ceil(X + eX);
+        if (k1 == k2) {
+          if (threadIdx.x == 0) *out = (int32_t)(n_gt + (uint32_t)max(1.0, k1));
+          return;
+        }
+      }
+    }
     Acc5 gt = {};
     uint32_t cgt = 0, ceq = 0;
 #pragma unroll 4
@@ -678,20 +749,12 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     Acc5 sge = sgt;  // mass(>= T) = mass(> T) + #(== T) * T
     acc_add_mul(sge, T, ceq);
     acc_norm(sge, mge);
-    if (T != 0u && cmp_p(mge, P.p_fixed) < 0) {
-      // too high: next smaller present value
-      uint32_t best = 0u;
-#pragma unroll
-      for (int j = 0; j < WS_VPT; ++j) if (j < nv && u[j] < T) best = max(best, u[j]);
-      T = max_x(best);
+    if (T != 0u && cmp_p(mge, P.p_fixed) < 0) {  // too high: next smaller present value
+      T = below_T(T);
       continue;
     }
-    if (cmp_p(mgt, P.p_fixed) >= 0) {
-      // too low: next larger present value
-      uint32_t best = 0u;
-#pragma unroll
-      for (int j = 0; j < WS_VPT; ++j) if (j < nv && u[j] > T) best = max(best, ~u[j]);
-      T = ~max_x(best);
+    if (cmp_p(mgt, P.p_fixed) >= 0) {  // too low: next larger present value
+      T = above_T(T);
       continue;
     }
     // K = #(> T) + ceil((p - mass(> T)) / T), all exact

@@ -228,3 +228,97 @@ def test_compact_many_items_per_workgroup(page_size):
     n_items = sum(-(-int(-(-int(c) // b)) // 16) for c in npy(wl.context_lens)) * 8
     say(f"[compact many items b={b}] requests={R} items~{n_items} decisions={sorted(set(npy(dec).tolist()))}")
     compare_state(wl, st, dec, kept, dec_ref, kept_ref, nc)
+
+
+@pytest.mark.parametrize("n_hist,p", [(1024, 0.5), (1024, 0.75), (1008, 0.5), (2048, 0.999)])
+def test_working_set_uniform_weights_at_the_threshold(n_hist, p):
+    """Zero keys give every candidate the same weight (exactly 2^-10 for 1024 candidates), so the
+    working set is ceil(p |C|) (GrowPage Eq. 7 under uniform scores). With p |C| an integer the
+    running mass reaches p exactly at the threshold weight, which a float64 sum cannot settle:
+    the exact sums decide. Counts against the oracle on the GPU's weights and the closed form."""
+    from workloads.configs import make_decode_case
+    wl = make_decode_case(1, 8, 2, 64, 16, [n_hist + 5], seed=3, boundary=[0]).to(DEV)
+    wl.beta_s, wl.beta_l, wl.p, wl.rope_theta = 0.9, 0.999, p, 10000.0
+    wl.k_pool.zero_()
+    build_state(wl)
+    a_s, a_l, ws, nc = run_score(wl)
+    check_score(wl, a_s, a_l, ws, nc, label=f"uniform n={n_hist} p={p}")
+    assert int(nc[0]) == n_hist
+    if n_hist & (n_hist - 1) == 0:      # weights exactly 1 / n_hist
+        assert (a_s[0, :, :n_hist] == 1.0 / n_hist).all()
+        k = int(np.ceil(p * n_hist))
+        assert npy(ws).reshape(-1).tolist() == [k] * (2 * wl.H_kv)
+
+
+@pytest.mark.parametrize("cfg", ["long_reasoning_d128", "prefix_shared"])
+def test_boundary_pass_graph_replays(cfg):
+    """The boundary pass (score + working set, compress-or-grow) captured as two HIP graphs and
+    replayed three times, the state restored and eager work in between: every replay leaves the
+    eager call's bits (scores, counts, decisions, kept indices, page state, K/V)."""
+    wl = workload_on_gpu(cfg, "small")
+    build_state(wl)
+    C_max = c_max_of(wl)
+    R = wl.req_idx.numel()
+    cache = gp.KVCache.from_workload(wl)
+    H = wl.H_kv
+    a_s = torch.zeros((R, H, C_max), dtype=torch.float32, device=DEV)
+    a_l, wsc = torch.zeros_like(a_s), torch.zeros((R, H, 2), dtype=torch.int32, device=DEV)
+    nc = torch.zeros(R, dtype=torch.int32, device=DEV)
+    dec = torch.zeros(R, dtype=torch.int32, device=DEV)
+    kept = torch.zeros((R, H, C_max), dtype=torch.int32, device=DEV)
+    sws = torch.empty(gp.gp_score_and_working_set_workspace_size(R, wl.H_q, H, wl.d, wl.page_size,
+                                                                 C_max), dtype=torch.uint8, device=DEV)
+    cws = torch.empty(gp.gp_compact_or_grow_workspace_size(R, H, wl.block_tables.shape[1],
+                                                           wl.page_size, C_max),
+                      dtype=torch.uint8, device=DEV)
+    pol = torch.full((R,), ob.POLICY_FORCE_COMPRESS, dtype=torch.int32, device=DEV)
+    snap = {k: v.clone() for k, v in wl.snapshot().items()}
+    pools0 = (wl.k_pool.clone(), wl.v_pool.clone())
+
+    def restore():
+        wl.restore(snap)
+        wl.k_pool.copy_(pools0[0])
+        wl.v_pool.copy_(pools0[1])
+
+    def score():
+        gp.gp_score_and_working_set(wl.q, wl.qstate, wl.slot_ids, wl.req_idx, cache,
+                                    wl.block_tables, wl.context_lens, wl.positions, wl.rope_theta,
+                                    wl.p, wl.sm_scale, C_max, a_short=a_s, a_long=a_l,
+                                    ws_counts=wsc, n_cand=nc, workspace=sws)
+
+    def compact():
+        gp.gp_compact_or_grow(wl.req_idx, a_s, a_l, wsc, nc, wl.tau, wl.k_loc, 0, cache,
+                              wl.block_tables, wl.n_pages, wl.context_lens, wl.refcount,
+                              wl.free_stack, wl.free_top, policies=pol, decision=dec,
+                              kept_idx=kept, workspace=cws)
+
+    def state():
+        return [t.clone() for t in (a_s, a_l, wsc, nc, dec, kept)] + \
+               [v.clone() for v in wl.snapshot().values()] + [wl.k_pool.clone(), wl.v_pool.clone()]
+
+    score()
+    compact()
+    torch.cuda.synchronize()
+    ref = state()
+    restore()
+    torch.cuda.synchronize()
+    g_s, g_c = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_s):
+        score()
+    with torch.cuda.graph(g_c):
+        compact()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        restore()
+        a_s.zero_()
+        kept.zero_()
+        torch.cuda.synchronize()
+        g_s.replay()
+        g_c.replay()
+        torch.cuda.synchronize()
+        got = state()
+        same = all(np.array_equal(bits(x), bits(y)) for x, y in zip(got, ref))
+        say(f"[boundary graph {cfg}] replay {rep}: bit-identical={same}")
+        assert same
+        score()   # eager work between the replays
+        torch.cuda.synchronize()
