@@ -91,6 +91,10 @@ __device__ __forceinline__ void calibrated_rows(const ScoreParams& P, int i, int
   const int D = P.D, half = D / 2, G = P.G;
   const int slot = P.slot_ids[r];
   const double pos = (double)P.positions[r];
+  // the rotation angle depends on the pair index only: lane l holds elements l and l + 64, and
+  // both belong to pair l % (D/2), so one sine and cosine per lane serve every row
+  double sn = 0.0, cs = 1.0;
+  if (P.rope_theta > 0.0) sincos(pos * P.inv_freq[lane % half], &sn, &cs);
   for (int c = w; c < 2 * G; c += LG_WAVES) {
     const int x = c / G, g = h * G + c % G;
     double qv[2], sv[2];
@@ -124,12 +128,8 @@ __device__ __forceinline__ void calibrated_rows(const ScoreParams& P, int i, int
       const int d = lane + 64 * e;
       if (d >= D) continue;
       double out = cv[e];
-      if (P.rope_theta > 0.0) {
-        const double ang = pos * P.inv_freq[d % half];
-        double sn, cs;
-        sincos(ang, &sn, &cs);
+      if (P.rope_theta > 0.0)  // d % half == lane % half
         out = (d < half) ? cv[e] * cs - part[e] * sn : part[e] * sn + cv[e] * cs;
-      }
       s_qt[c][d] = (float)out;
     }
   }
