@@ -118,7 +118,8 @@ def test_decode_capped_grids_match_oracle(max_wg):
 
 @pytest.mark.parametrize("cfg", ["tiny", "qwen3_8b", "long_reasoning_d128"])
 def test_decode_ring_depths_give_same_bits(cfg):
-    """A capped call decodes bf16 / fp32 caches with one tile in flight per wave instead of two;
+    """A capped call decodes bf16 / fp32 caches with one tile in flight per wave (an uncapped one
+    with two, except over eight-head workgroups of 128-dimensional heads, which also keep one);
     both against the oracle. With 8 KV heads the uncapped kernel holds one workgroup per compute
     unit, so a cap of one workgroup per compute unit keeps the same split of the batch: the same
     tiles in the same order, hence the same bits."""
