@@ -415,8 +415,10 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
     boundary request forced to compress, so each one moves its tokens) on workload `name` with
     `b`-token pages. The integer page state and the boundary requests' K/V pages are restored
     before every repetition, outside the timed region; the median of `reps` after 3 warmups.
-    Also the same pass for the first boundary request alone (R = 1). Bytes per request: keys of C read, both score planes written and read
-    back, and the K/V of the tokens that shift, read and written."""
+    Also the same pass for the first boundary request alone (R = 1). Each call passes the
+    candidate bound of its own requests (C_max from their lengths, which the caller knows), as the
+    step does. Bytes per request: keys of C read, both score planes written and read back, and the
+    K/V of the tokens that shift, read and written."""
     dev = "cuda:0"
     wl = make_workload(name, "full", device=dev, page_size=b)
     if wl.mixed:
@@ -455,23 +457,30 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
         if tag0 is not None:
             wl.page_tag.copy_(tag0)
 
+    ctx_h = ints["context_lens"].cpu().tolist()
     for label, req in (("all", req_all), ("one", req_all[:1].clone())):
         R = req.numel()
         pol = torch.full((R,), 1, dtype=torch.int32, device=dev)   # forced compress
+        # the candidate bound of this call, from the lengths the caller knows (as in the step)
+        cm = max(max(0, (math.ceil(ctx_h[r] / b) - 1) * b) for r in req.cpu().tolist())
+        C = max(16, -(-cm // 16) * 16)
+        a_s = torch.empty((R, wl.H_kv, C), dtype=torch.float32, device=dev)
+        a_l = torch.empty_like(a_s)
+        kept_t = torch.empty((R, wl.H_kv, C), dtype=torch.int32, device=dev)
 
         def score():
             gp.gp_score_and_working_set(wl.q, wl.qstate, wl.slot_ids, req, path.cache,
                                         wl.block_tables, wl.context_lens, wl.positions,
-                                        wl.rope_theta, wl.p, wl.sm_scale, path.C_max,
-                                        a_short=path.a_s[:R], a_long=path.a_l[:R],
+                                        wl.rope_theta, wl.p, wl.sm_scale, C,
+                                        a_short=a_s, a_long=a_l,
                                         ws_counts=path.wsc[:R], n_cand=path.ncand[:R],
                                         workspace=path.sws)
 
         def compact():
-            gp.gp_compact_or_grow(req, path.a_s[:R], path.a_l[:R], path.wsc[:R], path.ncand[:R],
+            gp.gp_compact_or_grow(req, a_s, a_l, path.wsc[:R], path.ncand[:R],
                                   wl.tau, wl.k_loc, 0, path.cache, wl.block_tables, wl.n_pages,
                                   wl.context_lens, wl.refcount, wl.free_stack, wl.free_top,
-                                  policies=pol, decision=path.dec[:R], kept_idx=path.kept[:R],
+                                  policies=pol, decision=path.dec[:R], kept_idx=kept_t,
                                   workspace=path.cws)
 
         def timed(run_score, run_compact):
@@ -493,7 +502,7 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
         ms_s, ms_c = timed(score, compact)
         dec = path.dec[:R].cpu().numpy()
         nc = path.ncand[:R].cpu().numpy().astype(np.int64)
-        kept = path.kept[:R].cpu().numpy()
+        kept = kept_t.cpu().numpy()
         ctx0 = ints["context_lens"].cpu().numpy()
         ctx1 = wl.context_lens.cpu().numpy()
         moved = 0
@@ -535,7 +544,7 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
         out[label] = dict(requests=int(R), us_per_request=round(ms * 1e3 / R, 1),
                           score_us=round(ms_s * 1e3, 1), compact_us=round(ms_c * 1e3, 1),
                           bytes=byts, gbps=round(byts / (ms * 1e-3) / 1e9, 1),
-                          mean_candidates=round(float(nc.mean()), 1),
+                          mean_candidates=round(float(nc.mean()), 1), c_max=C,
                           decisions=sorted(set(int(x) for x in dec)))
     res = dict(workload=MIXED_BOUNDARY if wl.mixed else WORKLOAD_NAMES[name], page_size=b,
                k_loc=int(wl.k_loc), **out["all"], single_request=out["one"])

@@ -233,6 +233,44 @@ __device__ __forceinline__ float xor32_max(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Larger and smaller of this lane's value and lane (lane ^ J)'s: quad permutations fetch the
+// partner for 1 and 2; for 4 and 8 a quad reversal (lane ^ 3) or half-row mirror (lane ^ 7 in an
+// 8-lane half) followed by the half-row (7 - i) or row (15 - i) mirror; for 16 and 32 the
+// lane-swap instructions leave the two values of each pair in the two results.
+template <int J>
+__device__ __forceinline__ void lane_pair_minmax(uint32_t v, uint32_t& hi, uint32_t& lo) {
+  static_assert(J == 1 || J == 2 || J == 4 || J == 8 || J == 16 || J == 32, "lane_pair_minmax: J");
+  uint32_t a = v, b;
+  if constexpr (J == 1) b = dpp_u32<0xb1>(v);
+  if constexpr (J == 2) b = dpp_u32<0x4e>(v);
+  if constexpr (J == 4) b = dpp_u32<0x141>(dpp_u32<0x1b>(v));
+  if constexpr (J == 8) b = dpp_u32<0x140>(dpp_u32<0x141>(v));
+  if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  }
+  if constexpr (J == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    a = r[0];
+    b = r[1];
+  }
+  hi = max(a, b);
+  lo = min(a, b);
+}
+
+// Inclusive prefix sum over the 64 lanes (lane order): shifts by 1, 2, 4 and 8 inside each row of
+// 16, then the row broadcasts of lanes 15 and 31 carry the rows below.
+__device__ __forceinline__ double wave_scan_f64(double x) {
+  x += __builtin_bit_cast(double, dpp_u64<0x111>(__builtin_bit_cast(uint64_t, x)));
+  x += __builtin_bit_cast(double, dpp_u64<0x112>(__builtin_bit_cast(uint64_t, x)));
+  x += __builtin_bit_cast(double, dpp_u64<0x114>(__builtin_bit_cast(uint64_t, x)));
+  x += __builtin_bit_cast(double, dpp_u64<0x118>(__builtin_bit_cast(uint64_t, x)));
+  x += __builtin_bit_cast(double, dpp_u64<0x142, 0xa>(__builtin_bit_cast(uint64_t, x)));
+  x += __builtin_bit_cast(double, dpp_u64<0x143, 0xc>(__builtin_bit_cast(uint64_t, x)));
+  return x;
+}
+
 // Sums and maxima over the 16 lanes of each DPP row (quad swaps, half-row and row mirrors): every
 // lane of a row ends with its row's result. A block reduction hands its (at most 16) wave
 // partials to the lanes of a row this way: one LDS read per lane instead of 16.

@@ -32,7 +32,7 @@ constexpr int CHUNK_TILES = 32;  // 512 candidate tokens per logits workgroup
 constexpr int WS_THREADS = 1024;
 constexpr int WS_VPT = 32;        // weights per thread held in registers (|C| <= 32768)
 constexpr int WS_MAX_C = WS_THREADS * WS_VPT;
-constexpr int WS_TAIL = 256;      // weights left in the search interval when one wave finishes it
+constexpr int WS_TAIL = 256;      // weights left in the search interval when one wave sorts them
 // Relative rounding bound of a block's float64 sum of nonnegative weights: a thread adds its (at
 // most 32) weights in sequence, a wave reduces in 6 levels, the 16 wave partials in 4: at most 42
 // roundings on any path, each a relative 2^-53; the bound takes 64.
@@ -409,6 +409,39 @@ __device__ __forceinline__ int cmp_p(const uint32_t a[6], const uint32_t p[5]) {
   return 0;
 }
 
+// Bitonic sort, descending, of 256 keys held four per lane by one wave (key k * 64 + lane in
+// x[k]): partners 64 or 128 keys apart sit in this lane's own registers, nearer ones in other
+// lanes of the same register.
+template <int SIZE, int J>
+__device__ __forceinline__ void bitonic_step(uint32_t (&x)[4], int lane) {
+  if constexpr (J >= GP_WAVE) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k & (J / GP_WAVE)) continue;
+      const int k2 = k | (J / GP_WAVE);
+      const bool desc = ((k * GP_WAVE + lane) & SIZE) == 0;  // the same for k2 (J < SIZE)
+      const uint32_t a = x[k], b = x[k2];
+      x[k] = desc ? max(a, b) : min(a, b);
+      x[k2] = desc ? min(a, b) : max(a, b);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t hi, lo;
+      gp::lane_pair_minmax<J>(x[k], hi, lo);
+      const bool lower = (lane & J) == 0;
+      const bool desc = ((k * GP_WAVE + lane) & SIZE) == 0;
+      x[k] = lower == desc ? hi : lo;
+    }
+  }
+  if constexpr (J > 1) bitonic_step<SIZE, J / 2>(x, lane);
+}
+template <int SIZE>
+__device__ __forceinline__ void bitonic_sort_desc(uint32_t (&x)[4], int lane) {
+  if constexpr (SIZE > 2) bitonic_sort_desc<SIZE / 2>(x, lane);
+  bitonic_step<SIZE, SIZE / 2>(x, lane);
+}
+
 constexpr int WS_WAVES = WS_THREADS / GP_WAVE;
 static_assert(WS_WAVES <= 16, "block reductions hand one partial per wave to the 16 lanes of a DPP row");
 
@@ -582,8 +615,8 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   // are summed in float32 (the search only has to land on or next to the threshold; the
   // certificate below decides exactly), threads in float64. Each block-wide step also counts the
   // weights at or above its midpoint; once at most WS_TAIL weights lie in [lo, hi), they are
-  // listed in LDS and one wave finishes the search without barriers, the mass at or above hi
-  // entering as a constant.
+  // listed in LDS and one wave finishes the search without barriers: it sorts them and walks a
+  // running sum down from the mass at or above hi.
   uint32_t lo = 1u, hi = vmax + 1u;  // mass(>= lo) >= p holds up to rounding; hi fails
   uint32_t c_lo = 0u, c_hi = 0u;     // weights >= lo, weights >= hi
   double m_hi = 0.0;                 // mass of the weights >= hi
@@ -618,8 +651,10 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     }
   }
   if (hi - lo > 1u) {
-    // at most WS_TAIL weights in [lo, hi): list them, then one wave bisects over the list
-    __shared__ float s_tail[WS_TAIL];
+    // at most WS_TAIL weights in [lo, hi): list them; one wave sorts the list (descending) and
+    // takes the first weight at which the running mass, from the mass at or above hi, reaches p
+    static_assert(WS_TAIL == 4 * GP_WAVE, "the tail sort holds four keys per lane");
+    __shared__ uint32_t s_tail[WS_TAIL];
     __shared__ uint32_t s_ntail, s_lo;
     if (threadIdx.x == 0) s_ntail = 0u;
     __syncthreads();
@@ -633,29 +668,33 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
       base = __shfl(base, 0, GP_WAVE);
       const uint32_t k = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      if (in && k < (uint32_t)WS_TAIL) s_tail[k] = __uint_as_float(u[j]);
+      if (in && k < (uint32_t)WS_TAIL) s_tail[k] = u[j];
     }
     __syncthreads();
     if (w == 0) {
       const uint32_t nt = min(s_ntail, (uint32_t)WS_TAIL);  // == c_lo - c_hi <= WS_TAIL
-      const uint32_t kn = (nt + GP_WAVE - 1) / GP_WAVE;       // weights per lane, uniform
-      uint32_t x[WS_TAIL / GP_WAVE];
+      uint32_t xs[4];
 #pragma unroll
-      for (int k = 0; k < WS_TAIL / GP_WAVE; ++k) {
+      for (int k = 0; k < 4; ++k) {
         const uint32_t idx = lane + GP_WAVE * k;
-        x[k] = idx < nt ? __float_as_uint(s_tail[idx]) : 0u;
+        xs[k] = idx < nt ? s_tail[idx] : 0u;  // empty places sort last
       }
-      uint32_t l2 = lo, h2 = hi;
-      while (h2 - l2 > 1u) {
-        const uint32_t mid = l2 + (h2 - l2) / 2;
-        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+      bitonic_sort_desc<WS_TAIL>(xs, lane);
+      // inclusive running mass in sorted order; no crossing (rounding) keeps lo
+      double run = m_hi;
+      uint32_t found = lo;
+      bool hit_any = false;
 #pragma unroll
-        for (int k = 0; k < WS_TAIL / GP_WAVE; ++k)
-          if ((uint32_t)k < kn) s4[k & 3] += x[k] >= mid ? __uint_as_float(x[k]) : 0.f;
-        const double sm = m_hi + gp::wave_sum_f64((double)(s4[0] + s4[1]) + (double)(s4[2] + s4[3]));
-        if (sm >= p_f64) l2 = mid; else h2 = mid;
+      for (int k = 0; k < 4; ++k) {
+        const double c = run + gp::wave_scan_f64((double)__uint_as_float(xs[k]));
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(xs[k] != 0u && c >= p_f64);
+        if (!hit_any && hit != 0ull) {
+          found = (uint32_t)__builtin_amdgcn_readlane((int)xs[k], (int)__builtin_ctzll(hit));
+          hit_any = true;
+        }
+        run = __builtin_bit_cast(double, gp::readlane63_u64(__builtin_bit_cast(uint64_t, c)));
       }
-      if (lane == 0) s_lo = l2;
+      if (lane == 0) s_lo = found;
     }
     __syncthreads();
     lo = s_lo;
