@@ -233,6 +233,21 @@ __device__ __forceinline__ float xor32_max(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Wave-uniform copies of values that every lane holds alike (a reduction result, a broadcast from
+// LDS, a field of a record all lanes loaded): kept in scalar registers, so that the branches and
+// loops they control are scalar, not masked per lane.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t uni(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+__device__ __forceinline__ uint64_t uni(uint64_t v) {
+  const uint32_t lo = uni((uint32_t)v), hi = uni((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ double uni(double v) {
+  return __builtin_bit_cast(double, uni(__builtin_bit_cast(uint64_t, v)));
+}
+
 // Larger and smaller of this lane's value and lane (lane ^ J)'s: quad permutations fetch the
 // partner for 1 and 2; for 4 and 8 a quad reversal (lane ^ 3) or half-row mirror (lane ^ 7 in an
 // 8-lane half) followed by the half-row (7 - i) or row (15 - i) mirror; for 16 and 32 the
@@ -288,6 +303,25 @@ __device__ __forceinline__ uint64_t row16_sum_u64(uint64_t v) {
   v += dpp_u64<0x141>(v);
   v += dpp_u64<0x140>(v);
   return v;
+}
+
+__device__ __forceinline__ uint32_t row16_sum_u32(uint32_t v) {
+  v += dpp_u32<0xb1>(v);
+  v += dpp_u32<0x4e>(v);
+  v += dpp_u32<0x141>(v);
+  v += dpp_u32<0x140>(v);
+  return v;
+}
+
+// sum of unsigned values (lanes outside a broadcast's row mask add 0)
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v += dpp_u32<0xb1>(v);
+  v += dpp_u32<0x4e>(v);
+  v += dpp_u32<0x141>(v);
+  v += dpp_u32<0x140>(v);
+  v += dpp_u32<0x142, 0xa>(v);
+  v += dpp_u32<0x143, 0xc>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {

@@ -113,6 +113,30 @@ struct CParams {
   double tau;
 };
 
+// A request's record and a work item, loaded by every lane of a workgroup alike and kept in
+// scalar registers (the loops and branches they control are then scalar, not masked per lane).
+__device__ __forceinline__ Info info_of(const CParams& P, int i) {
+  const Info v = P.info[i];
+  Info u;
+  u.r = gp::uni(v.r);
+  u.mode = gp::uni(v.mode);
+  u.P = gp::uni(v.P);
+  u.ctx_old = gp::uni(v.ctx_old);
+  u.n = gp::uni(v.n);
+  u.K_t = gp::uni(v.K_t);
+  u.R_n = gp::uni(v.R_n);
+  u.E = gp::uni(v.E);
+  u.ctx_new = gp::uni(v.ctx_new);
+  u.n_dest = gp::uni(v.n_dest);
+  u.first_repl = gp::uni(v.first_repl);
+  u.pad = 0;
+  return u;
+}
+__device__ __forceinline__ int2 item_of(const CParams& P, int k) {
+  const int2 v = P.items[k];
+  return make_int2(gp::uni(v.x), gp::uni(v.y));
+}
+
 // grow iff D / (H n) > tau, decided exactly (D integer, tau a double)
 __device__ bool trend_exceeds(long long Dsum, long long HN, double tau) {
   if (tau == 0.0) return Dsum > 0;
@@ -506,7 +530,7 @@ template <int PB>
 __global__ __launch_bounds__(SEL_T) void select_local_kernel(CParams P) {
   constexpr int b = PB;
   const int c = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
-  const Info inf = P.info[i];
+  const Info inf = info_of(P, i);
   const int n = inf.n;
   if (inf.mode != MODE_COMPACT || c * SEL_T * b >= n) return;
   const int K_t = inf.K_t, E = inf.E;
@@ -581,7 +605,7 @@ __global__ __launch_bounds__(SEL_T) void select_local_kernel(CParams P) {
 
 __global__ __launch_bounds__(GP_WAVE) void select_merge_kernel(CParams P) {
   const int h = blockIdx.x, i = blockIdx.y;
-  const Info inf = P.info[i];
+  const Info inf = info_of(P, i);
   if (inf.mode != MODE_COMPACT) return;
   const int b = P.page_size, E = inf.E, lane = threadIdx.x;
   const int nch = (inf.n + SEL_T * b - 1) / (SEL_T * b);
@@ -625,7 +649,7 @@ template <int PB>
 __global__ __launch_bounds__(SEL_T) void select_write_kernel(CParams P) {
   constexpr int b = PB;
   const int c = blockIdx.x, h = blockIdx.y, i = blockIdx.z;
-  const Info inf = P.info[i];
+  const Info inf = info_of(P, i);
   const int n = inf.n;
   if (c * SEL_T * b >= n) return;
   int32_t* out = P.kept_idx + ((size_t)i * P.H_kv + h) * P.C_max;
@@ -665,7 +689,7 @@ __global__ __launch_bounds__(SEL_T) void select_fused_kernel(CParams P) {
   constexpr int NW = SEL_T / GP_WAVE;
   const int h = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const Info inf = P.info[i];
+  const Info inf = info_of(P, i);
   const int n = inf.n;
   int32_t* out = P.kept_idx + ((size_t)i * P.H_kv + h) * P.C_max;
   if (inf.mode != MODE_COMPACT) {
@@ -787,7 +811,7 @@ __global__ __launch_bounds__(SEL_T) void select_fused_kernel(CParams P) {
 template <int LPP>  // lanes per page: page_size / WIDE_VPT
 __global__ __launch_bounds__(WIDE_T) void select_wide_kernel(CParams P) {
   const int h = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
-  const Info inf = P.info[i];
+  const Info inf = info_of(P, i);
   const int n = inf.n;
   int32_t* out = P.kept_idx + ((size_t)i * P.H_kv + h) * P.C_max;
   if (inf.mode != MODE_COMPACT) {
@@ -937,15 +961,15 @@ __global__ __launch_bounds__(DA_THREADS) void chunk_list_kernel(CParams P) {
 // chunk's to rewrite, and this chunk's last source pages): the bytes of the item's part, i.e.
 // its slice of every key row and its value rows. Workgroups stride over the work list.
 __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
-  const int n_items = *P.n_items;
+  const int n_items = gp::uni(*P.n_items);
   const int krow = P.D * P.es, kb = krow / P.npart;   // key row bytes, of them the part's
   const size_t vb = page_bytes(P) / P.npart;           // value bytes of the part (contiguous rows)
   const int lkpq = P.log_kpq, nkq = P.page_size << lkpq;
   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-    const int2 item = P.items[it];
+    const int2 item = item_of(P, it);
     const int i = item.x / P.H_kv, h = item.x % P.H_kv;
     const int c = item.y / P.npart, part = item.y % P.npart;
-    const Info inf = P.info[i];
+    const Info inf = info_of(P, i);
     for (int s = 0; s < P.span; ++s) {
       const int lp = (c + 1) * P.chunk_pages + s;
       if (!from_snapshot(P, lp, c, inf.n_dest)) continue;  // uniform over the workgroup
@@ -1002,15 +1026,15 @@ __device__ __forceinline__ void lds_barrier() {
 // rewritten when read, and the first `span` pages of the next chunk, which another workgroup
 // rewrites, come from the snapshot.
 __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
-  const int n_items = *P.n_items;
+  const int n_items = gp::uni(*P.n_items);
   for (int item_k = blockIdx.x; item_k < n_items; item_k += gridDim.x) {
   lds_barrier();  // the previous item is done with the tables and LDS
-  const int2 item = P.items[item_k];
+  const int2 item = item_of(P, item_k);
   const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y;
-  const Info inf = P.info[i];
+  const Info inf = info_of(P, i);
   const int L = P.chunk_pages, W = P.window_pages, D = P.D, es = P.es;
   const int lb = P.log_b, b = 1 << lb;
-  const int dp0 = P.dp0[item.x];
+  const int dp0 = gp::uni(P.dp0[item.x]);
   const int dp_lo = max(dp0, c * L), dp_hi = min((c + 1) * L, inf.n_dest);
   __shared__ int s_thr[MAX_EVICT];
   __shared__ int s_src[MAX_WINDOW_SLOTS];
@@ -1137,7 +1161,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
 constexpr int WIDE_KQ = 4;  // key pieces per thread and page: 256 slots x 4 pieces / CP_THREADS
 constexpr int WIDE_VQ = 4;  // value pieces per thread and page slice
 __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
-  const int n_items = *P.n_items;
+  const int n_items = gp::uni(*P.n_items);
   const int L = P.chunk_pages, span = P.span, ring = span + 1, es = P.es;
   const int lb = P.log_b, b = 1 << lb;
   const int krow = P.D * es;
@@ -1161,12 +1185,12 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
     if (g >= n_groups) break;
     const int item_k = g * P.npart + m % P.npart;
     lds_barrier();  // the previous item is done with the tables and the ring
-    const int2 item = P.items[item_k];
+    const int2 item = item_of(P, item_k);
     const int i = item.x / P.H_kv, h = item.x % P.H_kv;
     const int c = item.y / P.npart, part = item.y % P.npart;
-    const Info inf = P.info[i];
+    const Info inf = info_of(P, i);
     const int E = inf.E;
-    const int dp0 = P.dp0[item.x];
+    const int dp0 = gp::uni(P.dp0[item.x]);
     const int dp_lo = max(dp0, c * L), dp_hi = min((c + 1) * L, inf.n_dest);
     for (int k = threadIdx.x; k < WIDE_MAX_EVICT; k += CP_THREADS)
       s_thr[k] = k < E ? P.ev[((size_t)i * P.H_kv + h) * P.max_evict + k] - k : INT_MAX;
@@ -1311,7 +1335,7 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
 // becomes a bf16 page.
 __global__ __launch_bounds__(256) void mixed_plan_kernel(CParams P) {
   const int i = blockIdx.x;
-  const Info inf = P.info[i];
+  const Info inf = info_of(P, i);
   if (inf.mode != MODE_COMPACT) return;
   const int b = P.page_size, H = P.H_kv;
   __shared__ int s_dpm;
@@ -1350,7 +1374,7 @@ __global__ __launch_bounds__(256) void mixed_plan_kernel(CParams P) {
 // The destination tags, written once every page of the call has moved.
 __global__ __launch_bounds__(256) void mixed_tags_kernel(CParams P) {
   const int i = blockIdx.x;
-  const Info inf = P.info[i];
+  const Info inf = info_of(P, i);
   if (inf.mode != MODE_COMPACT) return;
   const int dpm = P.dp0[(size_t)i * P.H_kv];
   for (int dp = dpm + (int)threadIdx.x; dp < inf.n_dest; dp += blockDim.x)
@@ -1434,11 +1458,11 @@ __device__ __forceinline__ void store_page_parts(const PageParts& x, uint8_t* kd
 
 // The snapshot of a mixed cache holds the saved page in its own format.
 __global__ __launch_bounds__(CP_THREADS) void snapshot_mixed_kernel(CParams P) {
-  const int n_items = *P.n_items;
+  const int n_items = gp::uni(*P.n_items);
   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-    const int2 item = P.items[it];
+    const int2 item = item_of(P, it);
     const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y;
-    const Info inf = P.info[i];
+    const Info inf = info_of(P, i);
     for (int s = 0; s < P.span; ++s) {
       const int lp = (c + 1) * P.chunk_pages + s;
       if (!from_snapshot(P, lp, c, inf.n_dest)) continue;
@@ -1467,7 +1491,7 @@ __device__ __forceinline__ int nib(uint32_t w, int n) { return (int32_t)(w << (2
 // reads, and every staged page is in LDS before the barrier that precedes its overwrite.
 constexpr int MX_SLOT = 2 * (2 * 32 * 128) + 2 * 4 * 32;  // bf16 K + V of a 32-token page + scales
 __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
-  const int n_items = *P.n_items;
+  const int n_items = gp::uni(*P.n_items);
   const int L = P.chunk_pages, span = P.span, ring = span + 1;
   const int lb = P.log_b, b = 1 << lb, D = P.D;
   extern __shared__ __align__(16) uint8_t s_mx[];  // ring x MX_SLOT bytes
@@ -1479,11 +1503,11 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
   const int vslot = D / 16;  // INT4 value dimension slot stride: slot(j) = (j % 16) * (D/16) + j / 16
   for (int item_k = blockIdx.x; item_k < n_items; item_k += gridDim.x) {
     lds_barrier();
-    const int2 item = P.items[item_k];
+    const int2 item = item_of(P, item_k);
     const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y;
-    const Info inf = P.info[i];
+    const Info inf = info_of(P, i);
     const int E = inf.E;
-    const int dp0 = P.dp0[item.x];
+    const int dp0 = gp::uni(P.dp0[item.x]);
     const int dp_lo = max(dp0, c * L), dp_hi = min((c + 1) * L, inf.n_dest);
     if (threadIdx.x < MAX_EVICT)
       s_thr[threadIdx.x] = (int)threadIdx.x < E

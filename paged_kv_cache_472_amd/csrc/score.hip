@@ -142,7 +142,8 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
   // neighbouring workgroups at the same time
   const int h = blockIdx.x, chunk = blockIdx.y, i = blockIdx.z;
   int r;
-  const int n = candidates(P, i, &r);
+  const int n = gp::uni(candidates(P, i, &r));
+  r = gp::uni(r);
   if (h == 0 && chunk == 0 && threadIdx.x == 0) P.n_cand[i] = n;
   const int tile0 = chunk * CHUNK_TILES;
   if (n <= 0 || tile0 * 16 >= n) return;
@@ -449,7 +450,8 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   const int row = blockIdx.x, i = blockIdx.y;
   const int h = row >> 1, x = row & 1;
   int r;
-  const int n = candidates(P, i, &r);
+  const int n = gp::uni(candidates(P, i, &r));
+  r = gp::uni(r);
   int32_t* out = P.ws_counts + ((size_t)i * P.H_kv + h) * 2 + x;
   if (n <= 0) {
     if (threadIdx.x == 0) *out = n < 0 ? -1 : 0;
@@ -463,14 +465,14 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   // Block reductions with one barrier each: wave partials alternate between two scratch
   // buffers, so a buffer is rewritten only after every thread has passed another barrier.
   __shared__ double s_d[2][WS_WAVES];
-  __shared__ double s_dc[2][WS_WAVES];
+  __shared__ uint32_t s_dc[2][WS_WAVES];
   __shared__ uint64_t s_u[2][8][WS_WAVES];
   __shared__ uint32_t s_x[2][WS_WAVES];
   int ph = 0;
   // a float64 sum and an integer count in one barrier
   auto sum_dc = [&](double v, uint32_t c, uint32_t* c_out) -> double {
     v = gp::wave_sum_f64(v);
-    const double cw = gp::wave_sum_f64((double)c);
+    const uint32_t cw = gp::wave_sum_u32(c);
     if (lane == 0) {
       s_d[ph][w] = v;
       s_dc[ph][w] = cw;
@@ -479,18 +481,10 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     // lane k of every row takes wave k's partial; the row reduction leaves the total everywhere
     const int k = lane & 15;
     const double t = gp::row16_sum_f64(k < WS_WAVES ? s_d[ph][k] : 0.0);
-    const double tc = gp::row16_sum_f64(k < WS_WAVES ? s_dc[ph][k] : 0.0);
+    const uint32_t tc = gp::row16_sum_u32(k < WS_WAVES ? s_dc[ph][k] : 0u);
     ph ^= 1;
-    *c_out = (uint32_t)tc;
-    return t;
-  };
-  auto sum_d = [&](double v) -> double {
-    v = gp::wave_sum_f64(v);
-    if (lane == 0) s_d[ph][w] = v;
-    __syncthreads();
-    const double t = gp::row16_sum_f64((lane & 15) < WS_WAVES ? s_d[ph][lane & 15] : 0.0);
-    ph ^= 1;
-    return t;
+    *c_out = gp::uni(tc);
+    return gp::uni(t);
   };
   auto sum_u8 = [&](uint64_t (&v)[8]) {
 #pragma unroll
@@ -500,8 +494,28 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     }
     __syncthreads();
 #pragma unroll
-    for (int c = 0; c < 8; ++c) v[c] = gp::row16_sum_u64((lane & 15) < WS_WAVES ? s_u[ph][c][lane & 15] : 0ull);
+    for (int c = 0; c < 8; ++c) v[c] = gp::uni(gp::row16_sum_u64((lane & 15) < WS_WAVES ? s_u[ph][c][lane & 15] : 0ull));
     ph ^= 1;
+  };
+  // the sum, the count and the maximum in one barrier
+  auto sum_cnt_max = [&](double v, uint32_t c, uint32_t m, uint32_t* c_out, uint32_t* m_out) -> double {
+    v = gp::wave_sum_f64(v);
+    c = gp::wave_sum_u32(c);
+    m = gp::wave_max_u32(m);
+    if (lane == 0) {
+      s_d[ph][w] = v;
+      s_dc[ph][w] = c;
+      s_x[ph][w] = m;
+    }
+    __syncthreads();
+    const int k = lane & 15;
+    const double t = gp::row16_sum_f64(k < WS_WAVES ? s_d[ph][k] : 0.0);
+    const uint32_t tc = gp::row16_sum_u32(k < WS_WAVES ? s_dc[ph][k] : 0u);
+    const uint32_t tm = gp::row16_max_u32(k < WS_WAVES ? s_x[ph][k] : 0u);
+    ph ^= 1;
+    *c_out = gp::uni(tc);
+    *m_out = gp::uni(tm);
+    return gp::uni(t);
   };
   auto max_x = [&](uint32_t v) -> uint32_t {
     v = gp::wave_max_u32(v);
@@ -509,7 +523,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     __syncthreads();
     const uint32_t t = gp::row16_max_u32((lane & 15) < WS_WAVES ? s_x[ph][lane & 15] : 0u);
     ph ^= 1;
-    return t;
+    return gp::uni(t);
   };
 
   // ---- this row's weights (GrowPage Sec. 3.2): the softmax over C of each of the G query heads
@@ -570,26 +584,34 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
       u[j] = mine ? __float_as_uint(v) & 0x7fffffffu : 0u;
     }
   }
+  // the loops below take a thread's weights u[0 .. nv) in groups of four, with one uniform test
+  // per group: the slots past nv hold 0, which no loop counts, sums or takes as a maximum
+  auto each = [&](auto&& f) {
+#pragma unroll
+    for (int j0 = 0; j0 < WS_VPT; j0 += 4) {
+      if (j0 < nv) {
+#pragma unroll
+        for (int j = j0; j < j0 + 4; ++j) f(j);
+      }
+    }
+  };
   double p_f64 = 0.0;
   for (int k = 4; k >= 0; --k) p_f64 = p_f64 * 4294967296.0 + (double)P.p_fixed[k];
   p_f64 = ldexp(p_f64, -149);
 
-  // Total mass: if it never reaches p, K = |C|; also the largest weight. The float64 sum of the
-  // nonnegative weights is within SUM_ERR of the exact one (relative), so it decides unless p lies
-  // inside that bound; then the exact 160-bit sum does.
-  uint32_t vmax;
+  // Total mass: if it never reaches p, K = |C|; also the largest weight and the count of nonzero
+  // weights. The float64 sum of the nonnegative weights is within SUM_ERR of the exact one
+  // (relative), so it decides unless p lies inside that bound; then the exact 160-bit sum does.
+  uint32_t vmax, n_nz;
   {
     double ts = 0.0;
-    uint32_t m = 0u;
-#pragma unroll
-    for (int j = 0; j < WS_VPT; ++j) {
-      if (j < nv) {
-        ts += (double)__uint_as_float(u[j]);
-        m = max(m, u[j]);
-      }
-    }
-    const double tot_f = sum_d(ts);
-    vmax = max_x(m);
+    uint32_t m = 0u, c = 0u;
+    each([&](int j) {
+      ts += (double)__uint_as_float(u[j]);
+      m = max(m, u[j]);
+      c += u[j] != 0u;
+    });
+    const double tot_f = sum_cnt_max(ts, c, m, &n_nz, &vmax);
     const double err = SUM_ERR * tot_f;
     bool below = tot_f + err < p_f64;
     if (!below && tot_f - err < p_f64) {  // undecided: exact
@@ -618,27 +640,17 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   // listed in LDS and one wave finishes the search without barriers: it sorts them and walks a
   // running sum down from the mass at or above hi.
   uint32_t lo = 1u, hi = vmax + 1u;  // mass(>= lo) >= p holds up to rounding; hi fails
-  uint32_t c_lo = 0u, c_hi = 0u;     // weights >= lo, weights >= hi
+  uint32_t c_lo = n_nz, c_hi = 0u;  // weights >= lo, weights >= hi
   double m_hi = 0.0;                 // mass of the weights >= hi
-#pragma unroll
-  for (int j = 0; j < WS_VPT; ++j) c_lo += j < nv && u[j] != 0u;
-  {
-    uint32_t c;
-    (void)sum_dc(0.0, c_lo, &c);
-    c_lo = c;
-  }
   while (hi - lo > 1u && c_lo - c_hi > (uint32_t)WS_TAIL) {
     const uint32_t mid = lo + (hi - lo) / 2;
     float s4[4] = {0.f, 0.f, 0.f, 0.f};
     uint32_t cm = 0u;
-#pragma unroll
-    for (int j = 0; j < WS_VPT; ++j) {
-      if (j < nv) {
-        const bool ge = u[j] >= mid;
-        s4[j & 3] += ge ? __uint_as_float(u[j]) : 0.f;
-        cm += ge;
-      }
-    }
+    each([&](int j) {
+      const bool ge = u[j] >= mid;
+      s4[j & 3] += ge ? __uint_as_float(u[j]) : 0.f;
+      cm += ge;
+    });
     uint32_t c_mid;
     const double sm = sum_dc((double)(s4[0] + s4[1]) + (double)(s4[2] + s4[3]), cm, &c_mid);
     if (sm >= p_f64) {
@@ -658,18 +670,17 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     __shared__ uint32_t s_ntail, s_lo;
     if (threadIdx.x == 0) s_ntail = 0u;
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < WS_VPT; ++j) {
-      const bool in = j < nv && u[j] >= lo && u[j] < hi;
+    each([&](int j) {
+      const bool in = u[j] >= lo && u[j] < hi;
       const uint64_t m = __builtin_amdgcn_ballot_w64(in);
-      if (m == 0) continue;
+      if (m == 0) return;
       uint32_t base = 0;
       if (lane == 0) base = atomicAdd(&s_ntail, (uint32_t)__builtin_popcountll(m));
       base = __shfl(base, 0, GP_WAVE);
       const uint32_t k = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
       if (in && k < (uint32_t)WS_TAIL) s_tail[k] = u[j];
-    }
+    });
     __syncthreads();
     if (w == 0) {
       const uint32_t nt = min(s_ntail, (uint32_t)WS_TAIL);  // == c_lo - c_hi <= WS_TAIL
@@ -697,27 +708,24 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
       if (lane == 0) s_lo = found;
     }
     __syncthreads();
-    lo = s_lo;
+    lo = gp::uni(s_lo);
   }
   // snap T to the largest present weight <= lo
   uint32_t T;
   {
     uint32_t best = 0u;
-#pragma unroll
-    for (int j = 0; j < WS_VPT; ++j) if (j < nv && u[j] <= lo) best = max(best, u[j]);
+    each([&](int j) { if (u[j] <= lo) best = max(best, u[j]); });
     T = max_x(best);
   }
   // next smaller / next larger weight value present in the row
   auto below_T = [&](uint32_t T0) {
     uint32_t best = 0u;
-#pragma unroll
-    for (int j = 0; j < WS_VPT; ++j) if (j < nv && u[j] < T0) best = max(best, u[j]);
+    each([&](int j) { if (u[j] < T0) best = max(best, u[j]); });
     return max_x(best);
   };
   auto above_T = [&](uint32_t T0) {
     uint32_t best = 0u;
-#pragma unroll
-    for (int j = 0; j < WS_VPT; ++j) if (j < nv && u[j] > T0) best = max(best, ~u[j]);
+    each([&](int j) { if (u[j] > T0) best = max(best, ~u[j]); });
     return ~max_x(best);
   };
   // certificate: mass(> T) < p <= mass(>= T); move T to a neighbour value until it holds. The
@@ -726,17 +734,17 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   for (int iter = 0; iter < 64; ++iter) {
     {
       double gs = 0.0;
-      uint32_t cc = 0;  // #(> T) << 16 | #(== T): each at most 32768 over the block
-#pragma unroll 4
-      for (int j = 0; j < WS_VPT; ++j) {
-        if (j >= nv) continue;
+      // #(> T) << 16 | #(== T): each at most 32768 over the block (with T = 0 the empty slots
+      // count as equal, which nothing below uses: the mass at T is then 0)
+      uint32_t cc = 0;
+      each([&](int j) {
         if (u[j] > T) {
           gs += (double)__uint_as_float(u[j]);
           cc += 1u << 16;
         } else if (u[j] == T) {
           cc += 1u;
         }
-      }
+      });
       uint32_t cnt;
       const double mgt_f = sum_dc(gs, cc, &cnt);
       const uint32_t n_gt = cnt >> 16, n_eq = cnt & 0xffffu;
