@@ -158,6 +158,7 @@ __device__ bool trend_exceeds(long long Dsum, long long HN, double tau) {
 // requests at once; only a short register scan over the requests runs serially.
 constexpr int DA_THREADS = 1024;
 constexpr int DA_MAX_R = 1024;
+constexpr int DA_PAIRS = 4;  // (request, page) pairs per allocator thread whose loads fly together
 enum : int {
   F_VALID = 1, F_GROW = 2, F_SLOT = 4, F_EMPTY = 8, F_CHECK = 16, F_BAD = 32, F_SHRINK = 64
 };
@@ -189,6 +190,8 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
   __shared__ int s_flags[DA_MAX_R], s_cnt[DA_MAX_R], s_pn[DA_MAX_R], s_ndest[DA_MAX_R];
   __shared__ unsigned char s_shr[DA_MAX_R];
   __shared__ int s_r[DA_MAX_R], s_top[DA_MAX_R], s_relbase[DA_MAX_R], s_pref[DA_MAX_R + 1];
+  __shared__ int s_before[DA_MAX_R];  // shared pages of the compacting requests before request i
+  __shared__ int s_first[DA_MAX_R];   // first replaced page of request i (INT_MAX: none)
   __shared__ int s_w[DA_THREADS / GP_WAVE];
   __shared__ int s_any_repl, s_top_end, s_nrel;
 
@@ -299,33 +302,58 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
     s_pref[R] = acc;
   }
   __syncthreads();
-  const int npairs = s_pref[R];
-  for (int f = tid; f < npairs; f += DA_THREADS) {
-    int lo = 0, hi = R;  // last i with s_pref[i] <= f
+  const int npairs = gp::uni(s_pref[R]);
+  // (request, page) pair f: the last i with s_pref[i] <= f, and the page's index in the request
+  auto pair_of = [&](int f, int* j) {
+    int lo = 0, hi = R;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (s_pref[mid] <= f) lo = mid; else hi = mid;
     }
-    const int i = lo, j = f - s_pref[i];
-    const int pg = P.block_tables[(size_t)s_r[i] * P.max_pages + j];
-    P.old_bt[(size_t)i * P.max_pages + j] = pg;
-    if (pg < 0 || pg >= P.num_pages) atomicOr(&s_flags[i], F_BAD);
-    // mixed caches: a request that must move tokens keeps its pages when one is released
-    // (one tag per page cannot keep a released token masked among live ones)
-    else if (P.page_tag && P.page_tag[pg] == GP_TAG_RELEASE) atomicOr(&s_flags[i], F_BAD);
-    else if (j < s_ndest[i] && P.refcount[pg] > 1) atomicAdd(&s_cnt[i], 1);
+    *j = f - s_pref[lo];
+    return lo;
+  };
+  // DA_PAIRS pairs per thread at a time, every block-table load of the batch issued before the
+  // dependent refcount and tag loads, and those before any use (past npairs: the last pair again,
+  // unused; an invalid page id reads page 0, unused)
+  for (int f0 = 0; f0 < npairs; f0 += DA_PAIRS * DA_THREADS) {
+    int iv[DA_PAIRS], jv[DA_PAIRS], pgv[DA_PAIRS], rcv[DA_PAIRS], tgv[DA_PAIRS];
+#pragma unroll
+    for (int u = 0; u < DA_PAIRS; ++u) {
+      iv[u] = pair_of(min(f0 + u * DA_THREADS + tid, npairs - 1), &jv[u]);
+      pgv[u] = P.block_tables[(size_t)s_r[iv[u]] * P.max_pages + jv[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < DA_PAIRS; ++u) {
+      const int pc = (pgv[u] >= 0 && pgv[u] < P.num_pages) ? pgv[u] : 0;
+      rcv[u] = P.refcount[pc];
+      tgv[u] = P.page_tag ? (int)P.page_tag[pc] : GP_TAG_BF16;
+    }
+#pragma unroll
+    for (int u = 0; u < DA_PAIRS; ++u) {
+      if (f0 + u * DA_THREADS + tid >= npairs) continue;
+      const int i = iv[u], j = jv[u], pg = pgv[u];
+      P.old_bt[(size_t)i * P.max_pages + j] = pg;
+      if (pg < 0 || pg >= P.num_pages) atomicOr(&s_flags[i], F_BAD);
+      // mixed caches: a request that must move tokens keeps its pages when one is released
+      // (one tag per page cannot keep a released token masked among live ones)
+      else if (tgv[u] == GP_TAG_RELEASE) atomicOr(&s_flags[i], F_BAD);
+      else if (j < s_ndest[i] && rcv[u] > 1) atomicAdd(&s_cnt[i], 1);
+    }
   }
   __syncthreads();
 
   // ---- C: allocation order (registers only): outcome, stack top before the pops, release base
   if (tid == 0) {
     int top = s_top0;
-    int nrel = 0, any = 0;
+    int nrel = 0, any = 0, nsh = 0;
     for (int i = 0; i < R; ++i) {
       const int fl = s_flags[i];
       int out = O_NONE, dec = GP_DECISION_NO_PAGES;
       s_top[i] = top;
       s_relbase[i] = nrel;
+      s_before[i] = nsh;
+      s_first[i] = INT_MAX;
       bool shr = false;
       if (fl & F_VALID) {
         bool compress = true;
@@ -359,6 +387,7 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
           } else {
             out = O_COMPACT;
             dec = code;
+            nsh += s_cnt[i];
             top -= s_cnt[i];
             nrel += s_cnt[i] + (shr ? 1 : 0);  // the Shrink's last page follows its replacements
             any |= s_cnt[i] > 0;
@@ -412,41 +441,47 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
   if (s_any_repl) {
     __syncthreads();
     int carry = 0;
-    for (int f0 = 0; f0 < npairs; f0 += DA_THREADS) {
-      const int f = f0 + tid;
-      int i = 0, j = 0, pg = -1;
-      bool sh = false;
-      if (f < npairs) {
-        int lo = 0, hi = R;
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (s_pref[mid] <= f) lo = mid; else hi = mid;
-        }
-        i = lo;
-        j = f - s_pref[i];
-        if ((s_flags[i] >> 4) == O_COMPACT && j < s_ndest[i]) {
-          pg = P.old_bt[(size_t)i * P.max_pages + j];
-          sh = P.refcount[pg] > 1;
-        }
+    for (int f0 = 0; f0 < npairs; f0 += DA_PAIRS * DA_THREADS) {
+      // thread tid takes the consecutive pairs f0 + DA_PAIRS tid + u, so one block scan of the
+      // per-thread counts ranks the shared pairs in pair order; the loads of a batch fly together
+      int iv[DA_PAIRS], jv[DA_PAIRS], pgv[DA_PAIRS];
+      bool cv[DA_PAIRS], shv[DA_PAIRS];
+#pragma unroll
+      for (int u = 0; u < DA_PAIRS; ++u) {
+        const int f = f0 + DA_PAIRS * tid + u;
+        iv[u] = pair_of(min(f, npairs - 1), &jv[u]);
+        cv[u] = f < npairs && (s_flags[iv[u]] >> 4) == O_COMPACT && jv[u] < s_ndest[iv[u]];
+        pgv[u] = P.old_bt[(size_t)iv[u] * P.max_pages + jv[u]];
+      }
+      int nsh = 0;
+#pragma unroll
+      for (int u = 0; u < DA_PAIRS; ++u) {
+        const int pc = (pgv[u] >= 0 && pgv[u] < P.num_pages) ? pgv[u] : 0;
+        shv[u] = cv[u] && P.refcount[pc] > 1;
+        nsh += shv[u] ? 1 : 0;
       }
       int total;
-      const int ex = carry + block_excl_scan(sh ? 1 : 0, s_w, &total);
-      if (sh) {
+      int ex = carry + block_excl_scan(nsh, s_w, &total);
+#pragma unroll
+      for (int u = 0; u < DA_PAIRS; ++u) {
+        if (!shv[u]) continue;
+        const int i = iv[u], j = jv[u], pg = pgv[u];
         // shared pairs of earlier requests precede request i's in the scan
-        int before = 0;
-        for (int k = 0; k < i; ++k)
-          if ((s_flags[k] >> 4) == O_COMPACT) before += s_cnt[k];
-        const int rank = ex - before;
+        const int rank = ex++ - s_before[i];
         const int top = s_top[i];
         const int np = P.free_stack[top - 1 - rank];
         P.free_stack[top - 1 - rank] = -1;
         P.rel[s_relbase[i] + rank] = pg;
         P.block_tables[(size_t)s_r[i] * P.max_pages + j] = np;
         if (np >= 0 && np < P.num_pages) P.refcount[np] = 1;
-        atomicMin(&P.info[i].first_repl, j);
+        atomicMin(&s_first[i], j);
       }
       carry += total;
     }
+    __syncthreads();
+    // a compacting request rewrites from its first replaced page at the latest
+    for (int i = tid; i < R; i += DA_THREADS)
+      if (s_first[i] != INT_MAX) P.info[i].first_repl = min(s_ndest[i], s_first[i]);
   }
   __threadfence();
   __syncthreads();
@@ -504,6 +539,107 @@ __device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v)
   return gp::readlane63_u64(v);
 }
 
+// Larger and smaller of this lane's 64-bit key and lane (lane ^ J)'s (see gp::lane_pair_minmax:
+// the two halves move alike, so a lane-swap pair holds the two keys whole)
+template <int J>
+__device__ __forceinline__ void lane_pair_minmax_u64(unsigned long long v, unsigned long long& hi,
+                                                     unsigned long long& lo) {
+  const uint32_t vl = (uint32_t)v, vh = (uint32_t)(v >> 32);
+  unsigned long long a = v, b;
+  if constexpr (J == 16 || J == 32) {
+    const auto rl = J == 16 ? __builtin_amdgcn_permlane16_swap(vl, vl, false, false)
+                            : __builtin_amdgcn_permlane32_swap(vl, vl, false, false);
+    const auto rh = J == 16 ? __builtin_amdgcn_permlane16_swap(vh, vh, false, false)
+                            : __builtin_amdgcn_permlane32_swap(vh, vh, false, false);
+    a = ((unsigned long long)rh[0] << 32) | rl[0];
+    b = ((unsigned long long)rh[1] << 32) | rl[1];
+  } else {
+    uint32_t bl, bh;
+    if constexpr (J == 1) { bl = gp::dpp_u32<0xb1>(vl); bh = gp::dpp_u32<0xb1>(vh); }
+    if constexpr (J == 2) { bl = gp::dpp_u32<0x4e>(vl); bh = gp::dpp_u32<0x4e>(vh); }
+    if constexpr (J == 4) {
+      bl = gp::dpp_u32<0x141>(gp::dpp_u32<0x1b>(vl));
+      bh = gp::dpp_u32<0x141>(gp::dpp_u32<0x1b>(vh));
+    }
+    if constexpr (J == 8) {
+      bl = gp::dpp_u32<0x140>(gp::dpp_u32<0x141>(vl));
+      bh = gp::dpp_u32<0x140>(gp::dpp_u32<0x141>(vh));
+    }
+    b = ((unsigned long long)bh << 32) | bl;
+  }
+  hi = a > b ? a : b;
+  lo = a > b ? b : a;
+}
+
+// One key per lane, sorted ascending over the 64 lanes (bitonic network).
+template <int SIZE, int J>
+__device__ __forceinline__ void sort64_step(unsigned long long& x, int lane) {
+  unsigned long long hi, lo;
+  lane_pair_minmax_u64<J>(x, hi, lo);
+  const bool lower = (lane & J) == 0, asc = (lane & SIZE) == 0;
+  x = lower == asc ? lo : hi;
+  if constexpr (J > 1) sort64_step<SIZE, J / 2>(x, lane);
+}
+template <int SIZE = 64>
+__device__ __forceinline__ unsigned long long sort64_asc(unsigned long long x, int lane) {
+  if constexpr (SIZE > 2) x = sort64_asc<SIZE / 2>(x, lane);
+  sort64_step<SIZE, SIZE / 2>(x, lane);
+  return x;
+}
+
+// The E smallest of the K keys of every lane of a wave (E <= MAX_EVICT; all keys distinct;
+// ~0 marks no key), ascending into out[0 .. E) (~0 past the wave's keys). The E-th smallest lane
+// minimum bounds the E-th smallest key from above (E lanes hold a key at or below it), so when at
+// most 64 keys lie at or below it they are listed in the wave's 64-key LDS scratch and sorted
+// across the lanes; otherwise E rounds of wave minima.
+template <int K>
+__device__ __forceinline__ void wave_smallest(const unsigned long long (&key)[K], int E, int lane,
+                                              unsigned long long* s_tmp, unsigned long long* out) {
+  unsigned long long lm = ~0ull;
+#pragma unroll
+  for (int j = 0; j < K; ++j) lm = key[j] < lm ? key[j] : lm;
+  const unsigned long long srt = sort64_asc(lm, lane);
+  const unsigned long long T = gp::uni((uint64_t)(
+      ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(srt >> 32), E - 1) << 32) |
+      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)srt, E - 1)));
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < K; ++j) cnt += (key[j] <= T && key[j] != ~0ull) ? 1u : 0u;
+  const uint32_t C = gp::uni(gp::wave_sum_u32(cnt));
+  if (C <= GP_WAVE) {
+    uint32_t base = 0;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const bool c = key[j] <= T && key[j] != ~0ull;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(c);
+      const uint32_t at = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (c) s_tmp[at] = key[j];
+      base += (uint32_t)__builtin_popcountll(m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    unsigned long long v = (uint32_t)lane < C ? s_tmp[lane] : ~0ull;
+    v = sort64_asc(v, lane);
+    if (lane < E) out[lane] = v;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the scratch may be reused by this wave next
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    unsigned long long prev = 0;
+    for (int e = 0; e < E; ++e) {
+      unsigned long long m = ~0ull;
+#pragma unroll
+      for (int j = 0; j < K; ++j)
+        if ((e == 0 || key[j] > prev) && key[j] < m) m = key[j];
+      m = wave_min_u64(m);
+      prev = m;
+      if (lane == 0) out[e] = m;
+    }
+  }
+}
+
 // Compaction items of one compacting head, appended to the work list: the chunks from the one
 // holding its first changed page dp0 to the one holding its last destination page, each with every
 // part of the head dimension. The order of the list does not matter (items never share bytes, and
@@ -515,6 +651,27 @@ __device__ __forceinline__ void append_items(const CParams& P, int i, int h, int
   const int cnt = ((n_dest + L - 1) / L - dp0 / L) * P.npart;
   const int off = atomicAdd(P.n_items, cnt);
   for (int k = 0; k < cnt; ++k) P.items[off + k] = make_int2(i * P.H_kv + h, c0 + k);
+}
+
+// kept_idx over the output positions [p0, p1), written by consecutive threads: position p holds
+// the p-th kept candidate, p + #{k : ev[k] - k <= p} (ev the E evicted candidates, ascending, so
+// ev[k] - k never decreases); the thresholds ev[k] - k are wave-uniform
+__device__ __forceinline__ void write_kept(int32_t* out, int p0, int p1, const int* s_ev, int E,
+                                           int tid, int nthreads) {
+  int thr[MAX_EVICT];
+#pragma unroll
+  for (int k = 0; k < MAX_EVICT; ++k) thr[k] = gp::uni(k < E ? s_ev[k] - k : INT_MAX);
+  for (int p = p0 + tid; p < p1; p += nthreads) {
+    int c = 0;
+#pragma unroll
+    for (int k0 = 0; k0 < MAX_EVICT; k0 += 8) {
+      if (k0 < E) {
+#pragma unroll
+        for (int k = k0; k < k0 + 8; ++k) c += thr[k] <= p ? 1 : 0;
+      }
+    }
+    out[p] = p + c;
+  }
 }
 
 // Selection (Eq. 9-10) in three short launches over chunks of SEL_T pages (one page per
@@ -569,17 +726,9 @@ __global__ __launch_bounds__(SEL_T) void select_local_kernel(CParams P) {
   }
   constexpr int NW = SEL_T / GP_WAVE;
   __shared__ unsigned long long s_cand[NW * MAX_EVICT];
+  __shared__ unsigned long long s_tmp[NW * GP_WAVE];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  unsigned long long prev = 0;
-  for (int e = 0; e < E; ++e) {
-    unsigned long long m = ~0ull;
-#pragma unroll
-    for (int j = 0; j < b; ++j)
-      if ((e == 0 || key[j] > prev) && key[j] < m) m = key[j];
-    m = wave_min_u64(m);
-    prev = m;
-    if (lane == 0) s_cand[wv * MAX_EVICT + e] = m;
-  }
+  wave_smallest<b>(key, E, lane, s_tmp + wv * GP_WAVE, s_cand + wv * MAX_EVICT);
   __syncthreads();
   if (wv == 0) {
     constexpr int PER = NW * MAX_EVICT / GP_WAVE;
@@ -590,16 +739,7 @@ __global__ __launch_bounds__(SEL_T) void select_local_kernel(CParams P) {
       cv[k] = (idx % MAX_EVICT) < E ? s_cand[idx] : ~0ull;
     }
     unsigned long long* dst = P.cand + (((size_t)i * P.H_kv + h) * SEL_MAX_CHUNKS + c) * MAX_EVICT;
-    unsigned long long pv = 0;
-    for (int e = 0; e < E; ++e) {
-      unsigned long long m = ~0ull;
-#pragma unroll
-      for (int k = 0; k < PER; ++k)
-        if ((e == 0 || cv[k] > pv) && cv[k] < m) m = cv[k];
-      m = wave_min_u64(m);
-      pv = m;
-      if (lane == 0) dst[e] = m;
-    }
+    wave_smallest<PER>(cv, E, lane, s_tmp, dst);
   }
 }
 
@@ -617,17 +757,13 @@ __global__ __launch_bounds__(GP_WAVE) void select_merge_kernel(CParams P) {
     const int idx = lane + GP_WAVE * k;  // chunk idx / MAX_EVICT, rank idx % MAX_EVICT
     cv[k] = (idx / MAX_EVICT < nch && (idx % MAX_EVICT) < E) ? src[idx] : ~0ull;
   }
-  int tok = INT_MAX;  // lane e < E: the e-th evicted token (by key)
-  unsigned long long pv = 0;
-  for (int e = 0; e < E; ++e) {
-    unsigned long long m = ~0ull;
-#pragma unroll
-    for (int k = 0; k < PER; ++k)
-      if ((e == 0 || cv[k] > pv) && cv[k] < m) m = cv[k];
-    m = wave_min_u64(m);
-    pv = m;
-    if (lane == e) tok = (int)(0xffffffffu - (uint32_t)(m & 0xffffffffu));
-  }
+  __shared__ unsigned long long s_tmp[GP_WAVE], s_best[MAX_EVICT];
+  wave_smallest<PER>(cv, E, lane, s_tmp, s_best);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // lane e < E: the e-th evicted token (by key)
+  const int tok = lane < E ? (int)(0xffffffffu - (uint32_t)(s_best[lane] & 0xffffffffu)) : INT_MAX;
   // sort the evicted tokens by index: rank of lane e's token among the E
   int rank = 0;
   for (int e = 0; e < E; ++e) {
@@ -665,18 +801,16 @@ __global__ __launch_bounds__(SEL_T) void select_write_kernel(CParams P) {
     s_ev[threadIdx.x] = threadIdx.x < E ? P.ev[((size_t)i * P.H_kv + h) * P.max_evict + threadIdx.x] : INT_MAX;
   __syncthreads();
   if (c == 0 && threadIdx.x < E) out[inf.K_t + threadIdx.x] = -1;
-  if (t0 >= n) return;
-  int before = 0;  // evicted tokens below t0
+  // this chunk's kept candidates: the output positions between those of its first candidate and
+  // of the next chunk's
+  const int ta = c * SEL_T * b, tb = min(n, ta + SEL_T * b);
+  int ea = 0, eb = 0;
 #pragma unroll
-  for (int e = 0; e < MAX_EVICT; ++e) before += s_ev[e] < t0 ? 1 : 0;
-  for (int j = 0; j < b; ++j) {
-    const int t = t0 + j;
-    if (before < E && s_ev[before] == t) {
-      ++before;
-    } else {
-      out[t - before] = t;
-    }
+  for (int e = 0; e < MAX_EVICT; ++e) {
+    ea += s_ev[e] < ta ? 1 : 0;
+    eb += s_ev[e] < tb ? 1 : 0;
   }
+  write_kept(out, ta - ea, tb - eb, s_ev, E, threadIdx.x, SEL_T);
 }
 
 // The three selection steps in one workgroup per (request, KV head), for calls with few requests:
@@ -704,6 +838,7 @@ __global__ __launch_bounds__(SEL_T) void select_fused_kernel(CParams P) {
   const int nch = (n + SEL_T * b - 1) / (SEL_T * b);
   __shared__ unsigned long long s_cand[NW * MAX_EVICT];
   __shared__ unsigned long long s_best[MAX_EVICT];
+  __shared__ unsigned long long s_tmp[NW * GP_WAVE];
   __shared__ int s_ev[MAX_EVICT];
   for (int c = 0; c < nch; ++c) {
     const int t0 = (c * SEL_T + tid) * b;  // first candidate of this thread's page
@@ -733,16 +868,7 @@ __global__ __launch_bounds__(SEL_T) void select_fused_kernel(CParams P) {
       key[j] = cand ? (((unsigned long long)sv[j] << 32) | (0xffffffffu - (uint32_t)(t0 + j))) : ~0ull;
     }
     // each wave's E smallest
-    unsigned long long prev = 0;
-    for (int e = 0; e < E; ++e) {
-      unsigned long long m = ~0ull;
-#pragma unroll
-      for (int j = 0; j < b; ++j)
-        if ((e == 0 || key[j] > prev) && key[j] < m) m = key[j];
-      m = wave_min_u64(m);
-      prev = m;
-      if (lane == 0) s_cand[wv * MAX_EVICT + e] = m;
-    }
+    wave_smallest<b>(key, E, lane, s_tmp + wv * GP_WAVE, s_cand + wv * MAX_EVICT);
     __syncthreads();
     if (wv == 0) {
       // the E smallest of the waves' survivors and the running set
@@ -757,16 +883,7 @@ __global__ __launch_bounds__(SEL_T) void select_fused_kernel(CParams P) {
         else if (idx < TOT && c > 0 && idx - NW * MAX_EVICT < E) v = s_best[idx - NW * MAX_EVICT];
         cv[k] = v;
       }
-      unsigned long long pv = 0;
-      for (int e = 0; e < E; ++e) {
-        unsigned long long m = ~0ull;
-#pragma unroll
-        for (int k = 0; k < PER; ++k)
-          if ((e == 0 || cv[k] > pv) && cv[k] < m) m = cv[k];
-        m = wave_min_u64(m);
-        pv = m;
-        if (lane == 0) s_best[e] = m;
-      }
+      wave_smallest<PER>(cv, E, lane, s_tmp, s_best);
     }
     __syncthreads();
   }
@@ -785,19 +902,8 @@ __global__ __launch_bounds__(SEL_T) void select_fused_kernel(CParams P) {
     P.dp0[(size_t)i * P.H_kv + h] = dp0;
     if (P.fuse_items) append_items(P, i, h, dp0, inf.n_dest);
   }
-  // kept_idx: kept token t goes to position t - #(evicted < t)
-  for (int c = 0; c < nch; ++c) {
-    const int t0 = (c * SEL_T + tid) * b;
-    if (t0 >= n) break;
-    int before = 0;  // evicted tokens below t0
-#pragma unroll
-    for (int e = 0; e < MAX_EVICT; ++e) before += (e < E && s_ev[e] < t0) ? 1 : 0;
-    for (int j = 0; j < b; ++j) {
-      const int t = t0 + j;
-      if (before < E && s_ev[before] == t) ++before;
-      else out[t - before] = t;
-    }
-  }
+  // kept_idx: the K_t kept candidates in order
+  write_kept(out, 0, K_t, s_ev, E, tid, SEL_T);
 }
 
 // Selection for pages of 64..256 tokens (up to 2 page_size evictions): one workgroup per
