@@ -294,6 +294,9 @@ int gp_score_and_working_set(const void* q, int q_dtype, int B, int H_q, const f
  *   a_short / a_long / ws_counts / n_cand as produced by gp_score_and_working_set.
  *   kv, block_tables, n_pages, context_lens, refcount, free_stack, free_top are updated in place.
  *   Requests of one call must be distinct.
+ *   workspace: at least gp_compact_or_grow_workspace_size(R, H_kv, max_pages, page_size, C_max)
+ *   bytes for this call's R and C_max (the size, like the length of the compaction's work items,
+ *   depends on them), otherwise GP_ERR_WORKSPACE.
  *   Mixed-precision caches (page_tag given; GP_BF16 with every fp8 and INT4 pool; pages of 16
  *   or 32 tokens; one layer): a request that must move tokens while one of its pages is
  *   released is answered NO_PAGES and left untouched (one tag per page cannot keep a released

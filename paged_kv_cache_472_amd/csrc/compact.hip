@@ -39,6 +39,10 @@ constexpr int MAX_EVICT = 32;
 constexpr int MAX_SPAN = 2;               // pages a compaction shifts by at most (Shrink: 2)
 constexpr int SHRINK_MIN_CAPACITY = 1024; // tokens a Shrink must leave (GrowPage App. H.1)
 constexpr int CHUNK_PAGES = 16;           // destination pages per compaction item (pages <= 32 tokens)
+// calls whose 16-page items would number at most this many use 8-page items instead: the shift of
+// a few requests then spreads over more workgroups (measured: one request of the long-reasoning
+// 32/8-head batch 53 -> 47 us for its compress-or-grow; with 16 requests 16-page items are faster)
+constexpr long SMALL_CALL_ITEMS = 512;
 constexpr int WIDE_CHUNK_PAGES = 8;       // the same for larger pages: more, shorter items
 constexpr int MAX_WINDOW_SLOTS = 8 * 32;  // LDS window pages (<= 8) x page size (<= 32)
 constexpr int CP_THREADS = 256;
@@ -1176,7 +1180,6 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   const int lqpp = P.log_qpp, qpp = 1 << lqpp;  // 16-byte pieces per page
   const int lkq = P.log_kq;
   const int krow = D * es;
-  const int ld = D == 128 ? 7 : 6;
   for (int w0 = dp_lo; w0 < dp_hi; w0 += W) {
     const int w1 = min(w0 + W, dp_hi);          // destination pages [w0, w1)
     const int nsrc = w1 - w0 + P.span;          // source pages [w0, w1 + span - 1]
@@ -1230,26 +1233,31 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
         reinterpret_cast<u32x4_t*>(P.k + s_doff[dp - dp_lo] + (size_t)(slot & (b - 1)) * krow)[piece] = kreg[it];
       }
     }
-    // values: each lane writes two adjacent tokens of one destination value row, so the lanes of
-    // a wave read consecutive tokens of a few rows from LDS (no bank conflicts) and write whole
-    // 32- or 64-byte row segments
-    const int lhb = lb - 1, hb = 1 << lhb;  // token pairs per row
-    const int npairs = ((w1 - w0) << ld) << lhb;
-    for (int q = threadIdx.x; q < npairs; q += CP_THREADS) {
-      const int rowi = q >> lhb, tp = q & (hb - 1);  // (page, dd), token pair
-      const int dpl = rowi >> ld, dd = rowi & (D - 1);
+    // values: each lane writes two adjacent tokens of destination value rows, so the lanes of a
+    // wave read consecutive tokens of a few rows from LDS (no bank conflicts) and write whole
+    // 32- or 64-byte row segments. A lane keeps its token pair for the whole window: the pair's
+    // two source slots are read once per destination page and serve all of its rows.
+    const int lhb = lb - 1;                  // token pairs per row: 1 << lhb
+    const int tp = threadIdx.x & ((1 << lhb) - 1), r0 = threadIdx.x >> lhb;
+    const int rpi = CP_THREADS >> lhb;       // rows per pass of the block (32 or 16; D is a multiple)
+    const size_t rb = (size_t)b * es;        // bytes of one value row
+    for (int dpl = 0; dpl < w1 - w0; ++dpl) {
       const int slot = (dpl << lb) + 2 * tp;
       const int rs0 = s_src[slot], rs1 = s_src[slot + 1];
-      const uint8_t* a0 = s_v + (size_t)(rs0 >> lb) * pb + ((size_t)dd * b + (rs0 & (b - 1))) * es;
-      const uint8_t* a1 = s_v + (size_t)(rs1 >> lb) * pb + ((size_t)dd * b + (rs1 & (b - 1))) * es;
-      uint8_t* dst = P.v + s_doff[w0 + dpl - dp_lo] + ((size_t)dd * b + 2 * tp) * es;
-      if (es == 2) {
-        const uint32_t x0 = *reinterpret_cast<const uint16_t*>(a0);
-        const uint32_t x1 = *reinterpret_cast<const uint16_t*>(a1);
-        *reinterpret_cast<uint32_t*>(dst) = x0 | (x1 << 16);
-      } else {
-        *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{*reinterpret_cast<const uint32_t*>(a0),
-                                                   *reinterpret_cast<const uint32_t*>(a1)};
+      const uint8_t* a0 = s_v + (size_t)(rs0 >> lb) * pb + (size_t)(rs0 & (b - 1)) * es;
+      const uint8_t* a1 = s_v + (size_t)(rs1 >> lb) * pb + (size_t)(rs1 & (b - 1)) * es;
+      uint8_t* dst = P.v + s_doff[w0 + dpl - dp_lo] + (size_t)(2 * tp) * es;
+#pragma unroll 4
+      for (int dd = r0; dd < D; dd += rpi) {
+        if (es == 2) {
+          const uint32_t x0 = *reinterpret_cast<const uint16_t*>(a0 + dd * rb);
+          const uint32_t x1 = *reinterpret_cast<const uint16_t*>(a1 + dd * rb);
+          *reinterpret_cast<uint32_t*>(dst + dd * rb) = x0 | (x1 << 16);
+        } else {
+          *reinterpret_cast<u32x2_t*>(dst + dd * rb) =
+              u32x2_t{*reinterpret_cast<const uint32_t*>(a0 + dd * rb),
+                      *reinterpret_cast<const uint32_t*>(a1 + dd * rb)};
+        }
       }
     }
   }
@@ -1827,13 +1835,21 @@ struct WsLayout {
   size_t info, old_bt, rel, new_tag, layer0, layer_bytes, ev, dp0, items, n_items, cand, snap, total;
 };
 
-WsLayout ws_layout(int L, int R, int H_kv, int max_pages, int page_size) {
+// destination pages per compaction item: the call's shape decides, so that the workspace size
+// and the call agree
+int chunk_pages_for(int R, int H_kv, int page_size, int C_max) {
+  if (page_size >= WIDE_MIN_PAGE) return WIDE_CHUNK_PAGES;
+  const long chunks16 = ((long)C_max / page_size + 1 + CHUNK_PAGES - 1) / CHUNK_PAGES;
+  return (long)R * H_kv * chunks16 <= SMALL_CALL_ITEMS ? CHUNK_PAGES / 2 : CHUNK_PAGES;
+}
+
+WsLayout ws_layout(int L, int R, int H_kv, int max_pages, int page_size, int C_max) {
   // snapshots sized for the widest supported element (fp32) and head_dim 128
   const int es = 4, D = 128;
   const bool wide = page_size >= WIDE_MIN_PAGE;
   const size_t max_evict = wide ? 2 * (size_t)page_size : MAX_EVICT;
   const size_t parts = wide ? WIDE_MAX_PARTS : 1;
-  const size_t cp = wide ? WIDE_CHUNK_PAGES : CHUNK_PAGES;
+  const size_t cp = (size_t)chunk_pages_for(R, H_kv, page_size, C_max);
   const size_t max_chunks = (size_t)(max_pages + cp - 1) / cp;
   WsLayout w{};
   size_t off = 0;
@@ -1925,7 +1941,7 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
         !kv->k4_scale || !kv->v4_scale)
       return GP_ERR_INVALID;
   }
-  const WsLayout wl = ws_layout(L, R, H_kv, max_pages, b);
+  const WsLayout wl = ws_layout(L, R, H_kv, max_pages, b, C_max);
   if (!workspace || workspace_bytes < wl.total) return GP_ERR_WORKSPACE;
 
   CParams P{};
@@ -1954,7 +1970,7 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
   P.policy = policy;
   P.es = es;
   P.tau = tau;
-  P.chunk_pages = wide ? WIDE_CHUNK_PAGES : CHUNK_PAGES;
+  P.chunk_pages = chunk_pages_for(R, H_kv, b, C_max);
   P.max_chunks = (max_pages + P.chunk_pages - 1) / P.chunk_pages;
   P.window_pages = W;
   P.max_evict = wide ? 2 * b : MAX_EVICT;
@@ -2087,9 +2103,8 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
 extern "C" size_t gp_compact_or_grow_layers_workspace_size(int num_layers, int R, int H_kv,
                                                           int max_pages, int page_size,
                                                           int C_max) {
-  (void)C_max;
   if (num_layers <= 0 || R <= 0 || H_kv <= 0 || max_pages <= 0 || page_size <= 0) return 0;
-  return ws_layout(num_layers, R, H_kv, max_pages, page_size).total;
+  return ws_layout(num_layers, R, H_kv, max_pages, page_size, C_max).total;
 }
 
 extern "C" size_t gp_compact_or_grow_workspace_size(int R, int H_kv, int max_pages, int page_size,
