@@ -26,8 +26,14 @@
 
 namespace {
 
-constexpr int LG_WAVES = 4;
-constexpr int LG_THREADS = LG_WAVES * GP_WAVE;
+// Waves per logits workgroup: eight when the call has few workgroups (a wave's tiles and
+// calibration rows are then fewer, so each workgroup finishes sooner), four otherwise (less
+// per-workgroup setup for the same bytes). The kernel reads its count from blockDim.
+constexpr int LG_MAX_WAVES = 8;
+constexpr int LG_MIN_WAVES = 4;
+constexpr long LG_FEW_WORKGROUPS = 1024;
+constexpr int CAL_ROWS = (16 + LG_MIN_WAVES - 1) / LG_MIN_WAVES;  // calibrated rows per wave (2G <= 16)
+constexpr int LG_MAX_THREADS = LG_MAX_WAVES * GP_WAVE;
 constexpr int CHUNK_TILES = 32;  // 512 candidate tokens per logits workgroup
 constexpr int WS_THREADS = 1024;
 constexpr int WS_VPT = 32;        // weights per thread held in registers (|C| <= 32768)
@@ -84,41 +90,50 @@ __device__ __forceinline__ int candidates(const ScoreParams& P, int i, int* r_ou
 // ------------------------------------------------------------------------------ 1. calibration
 // The 2G summary rows of KV head h of boundary request i (row c = view c / G, query head
 // h G + c % G), RMS-calibrated to q_t (Eq. 12) and rotated to the current position, in float64,
-// into s_qt[c][0 .. D). One wave per row (a wave takes rows w, w + 4, ...).
+// into s_qt[c][0 .. D). One wave per row (a wave takes rows w, w + waves, ...).
 __device__ __forceinline__ void calibrated_rows(const ScoreParams& P, int i, int r, int h,
                                                 float (*s_qt)[128]) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nwv = blockDim.x >> 6;
   const int D = P.D, half = D / 2, G = P.G;
   const int slot = P.slot_ids[r];
   const double pos = (double)P.positions[r];
+  // this wave's rows (at most CAL_ROWS of the 2G <= 16): every query and summary element they
+  // need is loaded before any is used
+  double qv[CAL_ROWS][2], sv[CAL_ROWS][2];
+#pragma unroll
+  for (int k = 0; k < CAL_ROWS; ++k) {
+    const int c = w + k * nwv;
+    const int cc = c < 2 * G ? c : 0;  // rows past 2G read row 0, unused
+    const int x = cc / G, g = h * G + cc % G;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int d = min(lane + 64 * e, D - 1);
+      const size_t qi = ((size_t)r * P.H_q + g) * D + d;
+      qv[k][e] = P.q_bf16 ? (double)gp::bf16_bits_to_f32(static_cast<const uint16_t*>(P.q)[qi])
+                          : (double)static_cast<const float*>(P.q)[qi];
+      sv[k][e] = (double)P.qstate[(((size_t)slot * 2 + x) * P.H_q + g) * D + d];
+    }
+  }
   // the rotation angle depends on the pair index only: lane l holds elements l and l + 64, and
   // both belong to pair l % (D/2), so one sine and cosine per lane serve every row
   double sn = 0.0, cs = 1.0;
   if (P.rope_theta > 0.0) sincos(pos * P.inv_freq[lane % half], &sn, &cs);
-  for (int c = w; c < 2 * G; c += LG_WAVES) {
-    const int x = c / G, g = h * G + c % G;
-    double qv[2], sv[2];
+#pragma unroll
+  for (int k = 0; k < CAL_ROWS; ++k) {
+    const int c = w + k * nwv;
+    if (c >= 2 * G) continue;  // uniform over the wave
     double sq = 0.0, ss = 0.0;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int d = lane + 64 * e;
-      qv[e] = sv[e] = 0.0;
-      if (d < D) {
-        const size_t qi = ((size_t)r * P.H_q + g) * D + d;
-        qv[e] = P.q_bf16 ? (double)gp::bf16_bits_to_f32(static_cast<const uint16_t*>(P.q)[qi])
-                         : (double)static_cast<const float*>(P.q)[qi];
-        sv[e] = (double)P.qstate[(((size_t)slot * 2 + x) * P.H_q + g) * D + d];
+      if (lane + 64 * e < D) {
+        sq += qv[k][e] * qv[k][e];
+        ss += sv[k][e] * sv[k][e];
       }
-      sq += qv[e] * qv[e];
-      ss += sv[e] * sv[e];
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      sq += __shfl_xor(sq, o, GP_WAVE);
-      ss += __shfl_xor(ss, o, GP_WAVE);
-    }
+    sq = gp::wave_sum_f64(sq);
+    ss = gp::wave_sum_f64(ss);
     const double gamma = ss > 0.0 ? sqrt(sq / ss) : 0.0;  // RMS ratio (the 1/D cancels)
-    const double cv[2] = {gamma * sv[0], gamma * sv[1]};
+    const double cv[2] = {gamma * sv[k][0], gamma * sv[k][1]};
     // the partner of element d is d +/- D/2: lane-local when D == 128, a shuffle when 64
     double part[2];
 #pragma unroll
@@ -137,7 +152,7 @@ __device__ __forceinline__ void calibrated_rows(const ScoreParams& P, int i, int
 
 // ------------------------------------------------------------------------------ 2. logits
 template <int D, bool BF16, bool MIXED>
-__global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
+__global__ __launch_bounds__(LG_MAX_THREADS) void logits_kernel(ScoreParams P) {
   // heads vary fastest over the grid, so the KV heads of a page (adjacent in HBM) are read by
   // neighbouring workgroups at the same time
   const int h = blockIdx.x, chunk = blockIdx.y, i = blockIdx.z;
@@ -148,21 +163,21 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
   const int tile0 = chunk * CHUNK_TILES;
   if (n <= 0 || tile0 * 16 >= n) return;
   const int tile1 = min(n >> 4, tile0 + CHUNK_TILES);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nwv = blockDim.x >> 6;
   const int n16 = lane & 15, g4 = lane >> 4;
   const int G = P.G, b = P.page_size;
   const bool col_ok = n16 < 2 * G;
   const int x = n16 / G, g = n16 % G;
   const int hq = h * G + g;
-  // this wave's tiles are tile0 + w + k LG_WAVES, k < nt (nt <= CHUNK_TILES / LG_WAVES): lane k
+  // this wave's tiles are tile0 + w + k nwv, k < nt (nt <= CHUNK_TILES / nwv): lane k
   // fetches the page id and tag of tile k up front, and the key rows of plain (bf16 / fp32)
   // tiles are loaded two tiles ahead of their use, with no branch around the loads (a tile
   // past the wave's last, or of another format, reads the pool's first bytes and is unused)
   constexpr int NKW = BF16 ? D / 32 : D / 16;  // 16-byte key pieces of a plain tile per lane
-  const int nt = tile1 > tile0 + w ? (tile1 - tile0 - w + LG_WAVES - 1) / LG_WAVES : 0;
+  const int nt = tile1 > tile0 + w ? (tile1 - tile0 - w + nwv - 1) / nwv : 0;
   int pg_l = -1, tag_l = GP_TAG_BF16;
   if (lane < nt) {
-    const int tl = tile0 + w + lane * LG_WAVES;
+    const int tl = tile0 + w + lane * nwv;
     const int pg = P.block_tables[(size_t)r * P.max_pages + (tl << 4) / b];
     bool ok = pg >= 0 && pg < P.num_pages;
     if (ok && P.page_tag) {
@@ -174,7 +189,7 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
   auto load_plain = [&](int k, u32x4_t (&kw)[NKW]) {
     const int kc = min(k, 63);
     const int pg = __builtin_amdgcn_readlane(pg_l, kc), tag = __builtin_amdgcn_readlane(tag_l, kc);
-    const int tok0 = (tile0 + w + k * LG_WAVES) << 4;
+    const int tok0 = (tile0 + w + k * nwv) << 4;
     const bool plain = k < nt && pg >= 0 && tag == GP_TAG_BF16;
     const size_t base = plain ? ((size_t)pg * P.H_kv + h) * (size_t)b * D + (size_t)(tok0 % b + n16) * D : 0;
     if constexpr (BF16) {
@@ -236,7 +251,7 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
   float* lrow = P.logits + (((size_t)i * 2 + x) * P.H_q + hq) * P.C_max;
   auto process = [&](int k, const u32x4_t (&kw)[NKW]) {
     const int pg = __builtin_amdgcn_readlane(pg_l, k), tag = __builtin_amdgcn_readlane(tag_l, k);
-    const int tok0 = (tile0 + w + k * LG_WAVES) << 4;
+    const int tok0 = (tile0 + w + k * nwv) << 4;
     const bool valid_page = pg >= 0;
     f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
     // fp8 / INT4 pages exist only in a mixed cache (its own instantiation: a plain cache's kernel
@@ -323,7 +338,7 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
     l_run = l_run * gp::safe_exp2_diff(m_run, mm) + lo_ * gp::safe_exp2_diff(mo, mm);
     m_run = mm;
   }
-  __shared__ float sm[LG_WAVES][16], sl[LG_WAVES][16];
+  __shared__ float sm[LG_MAX_WAVES][16], sl[LG_MAX_WAVES][16];
   if (lane < 16) {
     sm[w][lane] = m_run;
     sl[w][lane] = l_run;
@@ -332,9 +347,9 @@ __global__ __launch_bounds__(LG_THREADS) void logits_kernel(ScoreParams P) {
   if (threadIdx.x < 2 * G) {
     const int c = threadIdx.x;
     float m = -INFINITY;
-    for (int ww = 0; ww < LG_WAVES; ++ww) m = fmaxf(m, sm[ww][c]);
+    for (int ww = 0; ww < nwv; ++ww) m = fmaxf(m, sm[ww][c]);
     float l = 0.f;
-    for (int ww = 0; ww < LG_WAVES; ++ww) l += sl[ww][c] * gp::safe_exp2_diff(sm[ww][c], m);
+    for (int ww = 0; ww < nwv; ++ww) l += sl[ww][c] * gp::safe_exp2_diff(sm[ww][c], m);
     const int xx = c / G, gg = c % G;
     float* st = P.stats + ((((size_t)i * 2 + xx) * P.H_q + h * G + gg) * P.nch + chunk) * 2;
     st[0] = m;
@@ -953,15 +968,16 @@ extern "C" int gp_score_and_working_set(const void* q, int q_dtype, int B, int H
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   dim3 lg(H_kv, P.nch, R);
+  const dim3 lt(((long)H_kv * P.nch * R <= LG_FEW_WORKGROUPS ? LG_MAX_WAVES : LG_MIN_WAVES) * GP_WAVE);
   if (kv->page_tag) {  // mixed caches are bf16 (checked above)
-    if (D == 64) hipLaunchKernelGGL((logits_kernel<64, true, true>), lg, dim3(LG_THREADS), 0, s, P);
-    else hipLaunchKernelGGL((logits_kernel<128, true, true>), lg, dim3(LG_THREADS), 0, s, P);
+    if (D == 64) hipLaunchKernelGGL((logits_kernel<64, true, true>), lg, lt, 0, s, P);
+    else hipLaunchKernelGGL((logits_kernel<128, true, true>), lg, lt, 0, s, P);
   } else if (q_dtype == GP_BF16) {
-    if (D == 64) hipLaunchKernelGGL((logits_kernel<64, true, false>), lg, dim3(LG_THREADS), 0, s, P);
-    else hipLaunchKernelGGL((logits_kernel<128, true, false>), lg, dim3(LG_THREADS), 0, s, P);
+    if (D == 64) hipLaunchKernelGGL((logits_kernel<64, true, false>), lg, lt, 0, s, P);
+    else hipLaunchKernelGGL((logits_kernel<128, true, false>), lg, lt, 0, s, P);
   } else {
-    if (D == 64) hipLaunchKernelGGL((logits_kernel<64, false, false>), lg, dim3(LG_THREADS), 0, s, P);
-    else hipLaunchKernelGGL((logits_kernel<128, false, false>), lg, dim3(LG_THREADS), 0, s, P);
+    if (D == 64) hipLaunchKernelGGL((logits_kernel<64, false, false>), lg, lt, 0, s, P);
+    else hipLaunchKernelGGL((logits_kernel<128, false, false>), lg, lt, 0, s, P);
   }
   GP_CHECK_LAUNCH();
   hipLaunchKernelGGL(working_set_kernel, dim3(2 * H_kv, R), dim3(WS_THREADS), 0, s, P);
