@@ -162,7 +162,7 @@ __device__ bool trend_exceeds(long long Dsum, long long HN, double tau) {
 // requests at once; only a short register scan over the requests runs serially.
 constexpr int DA_THREADS = 1024;
 constexpr int DA_MAX_R = 1024;
-constexpr int DA_PAIRS = 4;  // (request, page) pairs per allocator thread whose loads fly together
+constexpr int DA_PAIRS = 8;  // (request, page) pairs per allocator thread whose loads fly together
 enum : int {
   F_VALID = 1, F_GROW = 2, F_SLOT = 4, F_EMPTY = 8, F_CHECK = 16, F_BAD = 32, F_SHRINK = 64
 };
@@ -487,7 +487,9 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
     for (int i = tid; i < R; i += DA_THREADS)
       if (s_first[i] != INT_MAX) P.info[i].first_repl = min(s_ndest[i], s_first[i]);
   }
-  __threadfence();
+  // the release list written above is read back below by other threads: with no release the
+  // fence (a wait for every store of the kernel) is skipped
+  if (s_nrel > 0) __threadfence();
   __syncthreads();
 
   // ---- E: release the replaced references after every pop, in release order, in chunks of
@@ -1088,28 +1090,23 @@ __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
       const uint8_t* vs = P.v + pool_off(P, pg, h) + (size_t)part * vb;
       uint8_t* kd = snap_ptr(P, i, h, lp, 0) + (size_t)part * kb;
       uint8_t* vd = snap_ptr(P, i, h, lp, 1) + (size_t)part * vb;
-      // four pieces per thread in flight before any is stored
+      // four key and four value pieces per thread in flight before any is stored
       auto key_at = [&](int q) {
         return (size_t)(q >> lkpq) * krow + (size_t)(q & ((1 << lkpq) - 1)) * 16;
       };
-      for (int q0 = threadIdx.x; q0 < nkq; q0 += 4 * CP_THREADS) {
-        u32x4_t x[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          x[u] = *reinterpret_cast<const u32x4_t*>(ks + key_at(min(q0 + u * CP_THREADS, nkq - 1)));
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (q0 + u * CP_THREADS < nkq) *reinterpret_cast<u32x4_t*>(kd + key_at(q0 + u * CP_THREADS)) = x[u];
-      }
       const int nvq = (int)(vb / 16);
-      for (int q0 = threadIdx.x; q0 < nvq; q0 += 4 * CP_THREADS) {
-        u32x4_t x[4];
+      for (int q0 = threadIdx.x; q0 < max(nkq, nvq); q0 += 4 * CP_THREADS) {
+        u32x4_t xk[4], xv[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          x[u] = reinterpret_cast<const u32x4_t*>(vs)[min(q0 + u * CP_THREADS, nvq - 1)];
+        for (int u = 0; u < 4; ++u) {
+          xk[u] = *reinterpret_cast<const u32x4_t*>(ks + key_at(min(q0 + u * CP_THREADS, nkq - 1)));
+          xv[u] = reinterpret_cast<const u32x4_t*>(vs)[min(q0 + u * CP_THREADS, nvq - 1)];
+        }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (q0 + u * CP_THREADS < nvq) reinterpret_cast<u32x4_t*>(vd)[q0 + u * CP_THREADS] = x[u];
+        for (int u = 0; u < 4; ++u) {
+          if (q0 + u * CP_THREADS < nkq) *reinterpret_cast<u32x4_t*>(kd + key_at(q0 + u * CP_THREADS)) = xk[u];
+          if (q0 + u * CP_THREADS < nvq) reinterpret_cast<u32x4_t*>(vd)[q0 + u * CP_THREADS] = xv[u];
+        }
       }
     }
   }
