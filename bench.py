@@ -414,8 +414,10 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
     """Boundary-pass latency per request (score + working set, then compress-or-grow with every
     boundary request forced to compress, so each one moves its tokens) on workload `name` with
     `b`-token pages. The integer page state and the boundary requests' K/V pages are restored
-    before every repetition, outside the timed region; the median of `reps` after 3 warmups.
-    Also the same pass for the first boundary request alone (R = 1). Each call passes the
+    before every repetition, outside the timed region; the median of `reps` after 3 warmups, with
+    two events around the whole pass (the score / compress-or-grow split comes from a second
+    series with a marker between the two calls). Also the same pass for the first boundary request
+    alone (R = 1). Each call passes the
     candidate bound of its own requests (C_max from their lengths, which the caller knows), as the
     step does. Bytes per request: keys of C read, both score planes written and read back, and the
     K/V of the tokens that shift, read and written."""
@@ -483,23 +485,30 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
                                   policies=pol, decision=path.dec[:R], kept_idx=kept_t,
                                   workspace=path.cws)
 
-        def timed(run_score, run_compact):
+        def timed(run_score, run_compact, split):
+            # split: a marker between the two calls gives the score / compress-or-grow split,
+            # at the cost of the marker's own gap; the whole pass is timed without it
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             t_s, t_c = [], []
             for it in range(reps + 3):
                 restore()
                 ev[0].record()
                 run_score()
-                ev[1].record()
+                if split:
+                    ev[1].record()
                 run_compact()
                 ev[2].record()
                 torch.cuda.synchronize()
                 if it >= 3:
-                    t_s.append(ev[0].elapsed_time(ev[1]))
-                    t_c.append(ev[1].elapsed_time(ev[2]))
-            return float(np.median(t_s)), float(np.median(t_c))
+                    if split:
+                        t_s.append(ev[0].elapsed_time(ev[1]))
+                        t_c.append(ev[1].elapsed_time(ev[2]))
+                    else:
+                        t_s.append(ev[0].elapsed_time(ev[2]))
+            return float(np.median(t_s)), float(np.median(t_c)) if t_c else 0.0
 
-        ms_s, ms_c = timed(score, compact)
+        ms_s, ms_c = timed(score, compact, True)
+        ms_pass, _ = timed(score, compact, False)
         dec = path.dec[:R].cpu().numpy()
         nc = path.ncand[:R].cpu().numpy().astype(np.int64)
         kept = kept_t.cpu().numpy()
@@ -540,7 +549,7 @@ def boundary_leg(name, b, gp, torch, np, reps, make_workload):
                 score_bytes += int(sum(row_bytes.get(int(t), 0) for t in tg)) * wl.H_kv
             score_bytes += 4 * wl.H_kv * c * 4          # both score planes written and read
         byts = score_bytes + moved
-        ms = ms_s + ms_c
+        ms = ms_pass
         out[label] = dict(requests=int(R), us_per_request=round(ms * 1e3 / R, 1),
                           score_us=round(ms_s * 1e3, 1), compact_us=round(ms_c * 1e3, 1),
                           bytes=byts, gbps=round(byts / (ms * 1e-3) / 1e9, 1),

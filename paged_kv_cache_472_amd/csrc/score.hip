@@ -545,6 +545,21 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   // of KV head h in view x, from the logits and the per-chunk (max, sum) pairs the logits
   // kernel left, then their mean; written to a^x and kept in registers for the search
   const int G = P.G;
+  // the logits of the first batch of four weights per thread (every query head) are loaded before
+  // the per-chunk statistics are merged, so the two loads overlap; indexes past the candidates
+  // read candidate 0 (no branch per element) and are dropped below
+  const float* lg0 = P.logits + (((size_t)i * 2 + x) * P.H_q + h * G) * P.C_max;
+  auto load_batch = [&](int j0, float (&z)[8][4]) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = threadIdx.x + (j0 + j) * NT;
+        z[g][j] = (g < G && j0 + j < nv) ? lg0[(size_t)g * P.C_max + (t < n ? t : 0)] : 0.f;
+      }
+  };
+  float z0[8][4];
+  load_batch(0, z0);
   __shared__ float s_m[16], s_inv[16];
   {
     // one wave per query head: lane j holds chunk j's (max, sum)
@@ -568,21 +583,19 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     float acc[WS_VPT];
 #pragma unroll
     for (int j = 0; j < WS_VPT; ++j) acc[j] = 0.f;
-    // four weights of every query head per batch, all loads of a batch issued before any is
-    // used; indexes past the candidates read candidate 0 (no branch per element) and are
-    // dropped below
-    const float* lg0 = P.logits + (((size_t)i * 2 + x) * P.H_q + h * G) * P.C_max;
+    // four weights of every query head per batch, all loads of a batch issued before any is used
 #pragma unroll
     for (int j0 = 0; j0 < WS_VPT; j0 += 4) {
       if (j0 >= nv) continue;  // uniform: skips the batch without breaking the unrolling
       float z[8][4];
+      if (j0 == 0) {
 #pragma unroll
-      for (int g = 0; g < 8; ++g)
+        for (int g = 0; g < 8; ++g)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = threadIdx.x + (j0 + j) * NT;
-          z[g][j] = (g < G && j0 + j < nv) ? lg0[(size_t)g * P.C_max + (t < n ? t : 0)] : 0.f;
-        }
+          for (int j = 0; j < 4; ++j) z[g][j] = z0[g][j];
+      } else {
+        load_batch(j0, z);
+      }
 #pragma unroll
       for (int g = 0; g < 8; ++g)
 #pragma unroll
