@@ -119,6 +119,31 @@ def test_matches_torch_sdpa_float64(cfg):
             assert np.allclose(o[r, h * wl.G:(h + 1) * wl.G], ref, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("cfg", ["tiny", "long_reasoning_d128", "prefix_shared"])
+def test_gqa_mapping_matches_repeated_kv_sdpa(cfg):
+    """GQA pinned apart from the oracle's head slicing: K/V gathered here straight from the pools
+    (K [page, head, slot, d], V [page, head, d, slot]), repeated G times along the head axis with
+    torch.repeat_interleave (query head g sees KV head g // G), and attended by torch SDPA for all
+    query heads at once in float64."""
+    wl = make_workload(cfg, "small")
+    q, kp, vp = f64(wl.q), f64(wl.k_pool), f64(wl.v_pool)
+    bt, ctx, b = npy(wl.block_tables), npy(wl.context_lens), wl.page_size
+    o, _ = oatt.paged_decode_attn(q, kp, vp, bt, ctx, b, wl.sm_scale)
+    for r in range(wl.B):
+        n = int(ctx[r])
+        if n == 0:
+            continue
+        t = np.arange(n)
+        pg, sl = bt[r, t // b], t % b
+        k = kp[pg, :, sl, :].transpose(1, 0, 2)        # [H_kv, n, d]
+        v = vp[pg, :, :, sl].transpose(1, 0, 2)        # [H_kv, n, d]
+        kr = torch.from_numpy(np.ascontiguousarray(k)).repeat_interleave(wl.G, dim=0)
+        vr = torch.from_numpy(np.ascontiguousarray(v)).repeat_interleave(wl.G, dim=0)
+        qs = torch.from_numpy(q[r])[:, None, :]        # [H_q, 1, d]
+        ref = torch.nn.functional.scaled_dot_product_attention(qs, kr, vr, scale=wl.sm_scale)
+        assert np.allclose(o[r], ref[:, 0].numpy(), rtol=0, atol=1e-12)
+
+
 def test_split_merge_equals_single_pass():
     rng = np.random.default_rng(1)
     q = rng.standard_normal((5, 16))
