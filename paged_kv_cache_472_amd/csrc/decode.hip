@@ -26,7 +26,7 @@
 //
 // Mixed-precision caches decode in two passes over the same batch, each leaving partials that
 // the merge combines: the first takes the bf16 and fp8 tiles, the second the INT4 tiles with an
-// INT4-only kernel (16 registers per tile, four waves per SIMD, its own stream-K width). Released
+// INT4-only kernel (16 registers per tile, three tiles in flight per wave, its own stream-K width). Released
 // pages are skipped, fp8 codes are widened exactly to bf16 and their row scales applied to the
 // logits and the probability weights, and INT4 pages (PASK App. B.5) are contracted in half
 // precision: their nibbles become exact half values through the mantissa of 1024.0. An INT4
@@ -62,8 +62,9 @@ constexpr int MAX_THREADS = MAX_HEADS_PER_WG * GP_WAVE;
 // slow every dependent access of the kernels beside it far more than they speed up the decode.
 constexpr int RING_FULL = 2;
 constexpr int RING_SHARED = 1;
-// The INT4 pass is bound by instruction latency, not bytes: its kernel (126 registers) runs four
-// waves per SIMD, in workgroups of four heads so that four of them fit a compute unit.
+// The INT4 pass is bound by instruction issue, not bytes (about twice the VALU instructions of a
+// bf16 tile for a quarter of the bytes): its kernel (168 registers) runs three waves per SIMD, in
+// workgroups of four heads, so that more of them share a compute unit than eight-head ones would.
 constexpr int INT4_HEADS_PER_WG = 4;
 constexpr int MAX_BATCH = 8191;   // prefix of tile counts kept in LDS (32 KB)
 constexpr int LIST = 256;         // tiles per wave listed in LDS at a time
