@@ -286,6 +286,17 @@ __device__ __forceinline__ double wave_scan_f64(double x) {
   return x;
 }
 
+// Inclusive prefix sum of 64-bit integers over the 64 lanes (lane order), as wave_scan_f64.
+__device__ __forceinline__ uint64_t wave_scan_u64(uint64_t x) {
+  x += dpp_u64<0x111>(x);
+  x += dpp_u64<0x112>(x);
+  x += dpp_u64<0x114>(x);
+  x += dpp_u64<0x118>(x);
+  x += dpp_u64<0x142, 0xa>(x);
+  x += dpp_u64<0x143, 0xc>(x);
+  return x;
+}
+
 // Sums and maxima over the 16 lanes of each DPP row (quad swaps, half-row and row mirrors): every
 // lane of a row ends with its row's result. A block reduction hands its (at most 16) wave
 // partials to the lanes of a row this way: one LDS read per lane instead of 16.

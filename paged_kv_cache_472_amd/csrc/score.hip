@@ -39,6 +39,12 @@ constexpr int WS_THREADS = 1024;
 constexpr int WS_VPT = 32;        // weights per thread held in registers (|C| <= 32768)
 constexpr int WS_MAX_C = WS_THREADS * WS_VPT;
 constexpr int WS_TAIL = 256;      // weights left in the search interval when one wave sorts them
+// First level of the threshold search: 1024 bins of a weight's bit pattern >> 20 (sign, exponent
+// and three mantissa bits: a weight <= 1 has a pattern below 2^30), each holding the bin's count
+// (bits 48..63) and mass in units of 2^-47 (bits 0..47: a distribution's total stays below 2).
+constexpr int WS_BIN_SHIFT = 20;
+constexpr int WS_BINS = 1024;
+constexpr int WS_MASS_BITS = 47;
 // Relative rounding bound of a block's float64 sum of nonnegative weights: a thread adds its (at
 // most 32) weights in sequence, a wave reduces in 6 levels, the 16 wave partials in 4: at most 42
 // roundings on any path, each a relative 2^-53; the bound takes 64.
@@ -484,6 +490,13 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   __shared__ uint64_t s_u[2][8][WS_WAVES];
   __shared__ uint32_t s_x[2][WS_WAVES];
   int ph = 0;
+  static_assert(WS_BINS == WS_THREADS, "one histogram bin per thread");
+  __shared__ unsigned long long s_hist[WS_BINS];
+  __shared__ int s_bin;
+  __shared__ unsigned long long s_bin_incl, s_bin_excl;
+  __shared__ unsigned long long s_wtot[WS_WAVES];
+  s_hist[threadIdx.x] = 0ull;
+  if (threadIdx.x == 0) s_bin = -1;
   // a float64 sum and an integer count in one barrier
   auto sum_dc = [&](double v, uint32_t c, uint32_t* c_out) -> double {
     v = gp::wave_sum_f64(v);
@@ -638,6 +651,14 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
       ts += (double)__uint_as_float(u[j]);
       m = max(m, u[j]);
       c += u[j] != 0u;
+      // the weight's bin: one count and its mass in units of 2^-47 (truncated)
+      if (u[j] != 0u) {
+        const uint32_t E = u[j] >> 23;
+        const uint64_t M = E ? ((u[j] & 0x7fffffu) | 0x800000u) : (u[j] & 0x7fffffu);
+        const int sh = (E ? (int)E : 1) - 150 + WS_MASS_BITS;  // value = M * 2^(sh - 47)
+        const uint64_t fx = sh >= 0 ? (M << sh) : (-sh < 64 ? (M >> -sh) : 0ull);
+        atomicAdd(&s_hist[min(u[j] >> WS_BIN_SHIFT, (uint32_t)WS_BINS - 1u)], (1ull << 48) | fx);
+      }
     });
     const double tot_f = sum_cnt_max(ts, c, m, &n_nz, &vmax);
     const double err = SUM_ERR * tot_f;
@@ -661,15 +682,46 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
       return;
     }
   }
-  // bisection for the largest bit pattern T with mass(weights >= T) >= p. A thread's 32 weights
-  // are summed in float32 (the search only has to land on or next to the threshold; the
-  // certificate below decides exactly), threads in float64. Each block-wide step also counts the
-  // weights at or above its midpoint; once at most WS_TAIL weights lie in [lo, hi), they are
-  // listed in LDS and one wave finishes the search without barriers: it sorts them and walks a
-  // running sum down from the mass at or above hi.
+  // search for the largest bit pattern T with mass(weights >= T) >= p: first the histogram bin
+  // that holds it (counts and fixed-point masses gathered while the total was summed), then
+  // bisection inside the bin. A thread's 32 weights are summed in float32 (the search only has to
+  // land on or next to the threshold; the certificate below decides exactly), threads in float64.
+  // Each block-wide step also counts the weights at or above its midpoint; once at most WS_TAIL
+  // weights lie in [lo, hi), they are listed in LDS and one wave finishes the search without
+  // barriers: it sorts them and walks a running sum down from the mass at or above hi.
   uint32_t lo = 1u, hi = vmax + 1u;  // mass(>= lo) >= p holds up to rounding; hi fails
   uint32_t c_lo = n_nz, c_hi = 0u;  // weights >= lo, weights >= hi
   double m_hi = 0.0;                 // mass of the weights >= hi
+  {
+    // first level: the bin where the mass counted from the top reaches p (a prefix sum over the
+    // bins from the largest down; thread t holds bin 1023 - t). Rounding may leave p just past
+    // the total, and then the bisection starts from the whole range.
+    const uint64_t MASK = (1ull << 48) - 1ull;
+    const uint64_t p_fx = (uint64_t)ldexp(p_f64, WS_MASS_BITS);
+    const int bin = WS_BINS - 1 - (int)threadIdx.x;
+    const uint64_t v = s_hist[bin];
+    const uint64_t sc = gp::wave_scan_u64(v);
+    if (lane == 63) s_wtot[w] = sc;
+    __syncthreads();
+    uint64_t pre = 0ull;
+    for (int k = 0; k < w; ++k) pre += s_wtot[k];
+    const uint64_t incl = pre + sc, excl = incl - v;
+    if ((excl & MASK) < p_fx && (incl & MASK) >= p_fx) {
+      s_bin = bin;
+      s_bin_incl = incl;
+      s_bin_excl = excl;
+    }
+    __syncthreads();
+    const int b0 = gp::uni(s_bin);
+    if (b0 >= 0) {
+      const uint64_t bi = gp::uni((uint64_t)s_bin_incl), be = gp::uni((uint64_t)s_bin_excl);
+      lo = max(1u, (uint32_t)b0 << WS_BIN_SHIFT);
+      hi = min(vmax + 1u, ((uint32_t)b0 + 1u) << WS_BIN_SHIFT);
+      c_hi = (uint32_t)(be >> 48);
+      c_lo = (uint32_t)(bi >> 48);
+      m_hi = ldexp((double)(be & MASK), -WS_MASS_BITS);
+    }
+  }
   while (hi - lo > 1u && c_lo - c_hi > (uint32_t)WS_TAIL) {
     const uint32_t mid = lo + (hi - lo) / 2;
     float s4[4] = {0.f, 0.f, 0.f, 0.f};
