@@ -494,7 +494,9 @@ def attach_mixed_pools(wl: Workload, page_tag, seed: int = 0) -> Workload:
     get random E4M3 codes of magnitude below 8 and fp32 row scales in [0.01, 0.5), INT4
     pages random code bytes (no nibble 8) and half row scales in [0.01, 0.5); the pools of the
     formats a page does not use, and every pool of a released page, hold poison (NaN bf16,
-    NaN fp8 codes, NaN scales, nibble 8)."""
+    NaN fp8 codes, NaN scales, nibble 8). Re-tagging a workload that is already mixed: a page
+    that becomes bf16 without having been bf16 holds poison in the bf16 pools, so its K and V
+    get fresh standard-normal values (drawn last, so first-time tagging is unchanged)."""
     dev = wl.k_pool.device
     P, H, b, d = wl.k_pool.shape
     gen = torch.Generator(device=dev)
@@ -532,6 +534,15 @@ def attach_mixed_pools(wl: Workload, page_tag, seed: int = 0) -> Workload:
             for pool, val in pools_vals:
                 pool.index_fill_(0, idx, val)
 
+    old = getattr(wl, "page_tag", None) if getattr(wl, "mixed", False) else None
+    if old is not None:
+        fresh = np.nonzero((tags == TAG_BF16) & (old.cpu().numpy() != TAG_BF16))[0]
+        if len(fresh):
+            idx = torch.as_tensor(fresh, dtype=torch.long, device=dev)
+            nk = (len(fresh),) + tuple(wl.k_pool.shape[1:])
+            nv = (len(fresh),) + tuple(wl.v_pool.shape[1:])
+            wl.k_pool.index_copy_(0, idx, _randn(gen, nk, dev).to(wl.k_pool.dtype))
+            wl.v_pool.index_copy_(0, idx, _randn(gen, nv, dev).to(wl.v_pool.dtype))
     poison(np.nonzero(tags != TAG_BF16)[0], (wl.k_pool, float("nan")), (wl.v_pool, float("nan")))
     poison(np.nonzero(tags != TAG_FP8)[0], (k8, 0x7F), (v8, 0x7F), (k_scale, float("nan")),
            (v_scale, float("nan")))
