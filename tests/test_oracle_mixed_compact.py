@@ -251,3 +251,27 @@ def test_destination_tag_from_supplying_pages_not_their_range():
     # destination page 1 reads page 3 only; the last kept page is the old recent (bf16) page
     assert int(mx["page_tag"][bt[0, 1]]) == F8
     assert int(mx["page_tag"][bt[0, 63]]) == BF
+
+
+def test_retagging_a_mixed_workload_leaves_no_poison_in_context():
+    """Re-tagging a workload that is already mixed (as the boundary-pass benchmark does): every
+    in-context token of a page tagged bf16 must hold finite K and V, and every in-context page of
+    another format keeps poison in the bf16 pools."""
+    from workloads import make_workload
+    from workloads.configs import attach_mixed_pools, TAG_BF16
+    wl = make_workload("mixed_precision", "small", device="cpu")
+    rng = np.random.Generator(np.random.PCG64(2024))
+    tags = rng.choice([1, 2, 3], size=wl.num_pages, p=[0.4, 0.3, 0.3]).astype(np.uint8)
+    attach_mixed_pools(wl, tags, seed=5)
+    bt, ctx, b = wl.block_tables.numpy(), wl.context_lens.numpy(), wl.page_size
+    k, v = wl.k_pool.float(), wl.v_pool.float()
+    n_bf16 = 0
+    for r in range(wl.B):
+        for t in range(0, int(ctx[r]), b):
+            pg, m = int(bt[r, t // b]), min(b, int(ctx[r]) - t)
+            if tags[pg] == TAG_BF16:
+                n_bf16 += 1
+                assert torch.isfinite(k[pg, :, :m]).all() and torch.isfinite(v[pg, :, :, :m]).all()
+            else:
+                assert torch.isnan(k[pg]).all()
+    assert n_bf16 > 0
