@@ -1443,35 +1443,71 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
 // Destination tags of a compacting request (one workgroup per request): every head rewrites
 // from the first destination page that changes for any head; a destination page keeps the
 // precision of the pages that supply its tokens (any head) when they share one tag, else it
-// becomes a bf16 page.
+// becomes a bf16 page. Destination slot j takes source slot j + cnt(j), cnt(j) = #{k : ev[k] - k
+// <= j}, an increasing map onto the kept tokens; so the sources of page dp in one head are the
+// kept tokens between the sources of its first and last slots. The pages holding those two are
+// suppliers; a page strictly between them (a shift of at most two pages leaves at most one)
+// supplies iff not all of its b tokens are evicted. One thread per destination page; the heads'
+// thresholds ev[k] - k sit in LDS, up to PLAN_HEADS heads at a time.
+constexpr int PLAN_HEADS = 64;
 __global__ __launch_bounds__(256) void mixed_plan_kernel(CParams P) {
   const int i = blockIdx.x;
   const Info inf = info_of(P, i);
   if (inf.mode != MODE_COMPACT) return;
-  const int b = P.page_size, H = P.H_kv;
+  const int lb = P.log_b, b = 1 << lb, H = P.H_kv, E = inf.E;
   __shared__ int s_dpm;
+  __shared__ __align__(16) int s_thr[PLAN_HEADS][MAX_EVICT];
   if (threadIdx.x == 0) {
     int m = INT_MAX;
     for (int h = 0; h < H; ++h) m = min(m, P.dp0[(size_t)i * H + h]);
     s_dpm = m;
   }
   __syncthreads();
-  const int dpm = s_dpm;
+  const int dpm = gp::uni(s_dpm);
   for (int h = threadIdx.x; h < H; h += blockDim.x) P.dp0[(size_t)i * H + h] = dpm;
-  for (int dp = dpm + (int)threadIdx.x; dp < inf.n_dest; dp += blockDim.x) {
-    // bit s set: old page dp + s supplies a token of this page in some head. The source slot of
-    // destination slot j is j + #{k : ev[k] - k <= j} >= j, and it exceeds j by at most the E <= 2b
-    // evictions, so s <= 2; a page lying between two suppliers that lost all its tokens in every
-    // head supplies none.
+  for (int base = dpm; base < inf.n_dest; base += blockDim.x) {
+    const int dp = base + (int)threadIdx.x;
+    const int j0 = dp << lb, j1 = j0 + b - 1;
     uint32_t supply = 0;
-    for (int h = 0; h < H; ++h) {
-      const int32_t* ev = P.ev + ((size_t)i * H + h) * P.max_evict;
-      int c = 0;  // evictions k with ev[k] - k <= j (ev ascending, so ev[k] - k never decreases)
-      for (int j = dp * b; j < dp * b + b; ++j) {
-        while (c < inf.E && ev[c] - c <= j) ++c;
-        supply |= 1u << min(31, (j + c) / b - dp);
+    for (int h0 = 0; h0 < H; h0 += PLAN_HEADS) {
+      const int nh = min(PLAN_HEADS, H - h0);
+      __syncthreads();  // the previous heads' thresholds are no longer read
+      for (int e = threadIdx.x; e < nh * MAX_EVICT; e += blockDim.x) {
+        const int hh = e / MAX_EVICT, k = e % MAX_EVICT;
+        s_thr[hh][k] = k < E ? P.ev[((size_t)i * H + h0 + hh) * P.max_evict + k] - k : INT_MAX;
+      }
+      __syncthreads();
+      if (dp >= inf.n_dest) continue;
+      for (int hh = 0; hh < nh; ++hh) {
+        const int4* th = reinterpret_cast<const int4*>(s_thr[hh]);
+        int c0 = 0, c1 = 0;
+#pragma unroll
+        for (int k = 0; k < MAX_EVICT / 4; ++k) {
+          const int4 t = th[k];
+          c0 += (t.x <= j0) + (t.y <= j0) + (t.z <= j0) + (t.w <= j0);
+          c1 += (t.x <= j1) + (t.y <= j1) + (t.z <= j1) + (t.w <= j1);
+        }
+        const int s_lo = ((j0 + c0) >> lb) - dp, s_hi = ((j1 + c1) >> lb) - dp;
+        supply |= 1u << s_lo;
+        supply |= 1u << s_hi;
+        for (int s = s_lo + 1; s < s_hi; ++s) {
+          // evictions inside old page dp + s: ev[k] = thr[k] + k in [lo, lo + b)
+          const int lo = (dp + s) << lb;
+          int ne = 0;
+#pragma unroll
+          for (int k = 0; k < MAX_EVICT / 4; ++k) {
+            const int4 t = th[k];
+            const int e0 = 4 * k;
+            ne += (t.x != INT_MAX && t.x + e0 >= lo && t.x + e0 < lo + b);
+            ne += (t.y != INT_MAX && t.y + e0 + 1 >= lo && t.y + e0 + 1 < lo + b);
+            ne += (t.z != INT_MAX && t.z + e0 + 2 >= lo && t.z + e0 + 2 < lo + b);
+            ne += (t.w != INT_MAX && t.w + e0 + 3 >= lo && t.w + e0 + 3 < lo + b);
+          }
+          if (ne < b) supply |= 1u << s;
+        }
       }
     }
+    if (dp >= inf.n_dest) continue;
     int tag = -1;
     for (int s = 0; s < 32; ++s) {
       if (!(supply >> s & 1u)) continue;
@@ -1593,27 +1629,61 @@ __global__ __launch_bounds__(CP_THREADS) void snapshot_mixed_kernel(CParams P) {
 // signed nibble n (0..7 from the low end) of a 32-bit word
 __device__ __forceinline__ int nib(uint32_t w, int n) { return (int32_t)(w << (28 - 4 * n)) >> 28; }
 
-// Compaction of a mixed-precision cache (pages of 16 or 32 tokens). Per item, destination pages
-// one at a time: the source pages dp .. dp + span are staged in LDS in their own formats (an LDS
-// ring, one new page per destination page); the destination page is then written in its new
-// format: the same format as every source (codes and row scales copied; INT4 value nibbles
-// regrouped into four-token blocks) or bf16 (each element's exact code * scale rounded once).
-// Barriers hand off LDS only: a destination page is never a page a later stage of the workgroup
-// reads, and every staged page is in LDS before the barrier that precedes its overwrite.
-constexpr int MX_SLOT = 2 * (2 * 32 * 128) + 2 * 4 * 32;  // bf16 K + V of a 32-token page + scales
+// Compaction of a mixed-precision cache (pages of 16 or 32 tokens), in windows of W destination
+// pages like the uniform path. Per window the source slot of every destination slot is tabulated;
+// the value parts (codes, then row scales) of the W + span source pages are staged in LDS in
+// their own formats, since a value row gathers one element per token; every key piece of the
+// window is read into registers straight from its source row. The destination page is written in
+// its new format: the same format as every source (codes and row scales copied; INT4 value
+// nibbles regrouped into four-token blocks) or bf16 (each element's exact code * scale rounded
+// once). All loads of a window are issued before any is used, at valid stand-in addresses where a
+// piece has no source. Every source and destination block is a byte offset from the bf16 key
+// pool's base, which keeps the accesses in the global address space. The ordering argument of
+// compact_kernel holds unchanged: a window reads only pages at or above its own destination
+// pages (the next chunk's first pages from the snapshot), and every staged byte is read before
+// the barrier that precedes the next window's staging.
+constexpr int MXK_PIECES = 4;   // key pieces per thread and window (16-byte pieces of bf16 rows)
+constexpr int MXV_PIECES = 12;  // staged value pieces per thread and window
+__device__ __forceinline__ int mx_row_bytes(int tag, int D) {
+  return tag == GP_TAG_FP8 ? D : (tag == GP_TAG_INT4 ? D / 2 : 2 * D);
+}
+__device__ __forceinline__ int mx_scale_bytes(int tag) {
+  return tag == GP_TAG_FP8 ? 4 : (tag == GP_TAG_INT4 ? 2 : 0);
+}
+// word w (0..3) of a 16-byte piece
+__device__ __forceinline__ uint32_t word_of(const u32x4_t& x, int w) {
+  return w == 0 ? x[0] : (w == 1 ? x[1] : (w == 2 ? x[2] : x[3]));
+}
+// bf16 bits of the element with fp8 code c (low byte) times an fp32 row scale: one rounding
+__device__ __forceinline__ uint32_t fp8_times(uint32_t c, float sc) {
+  return f64_to_bf16_bits((double)__builtin_amdgcn_cvt_pk_f32_fp8(c, false)[0] * (double)sc);
+}
+// bf16 bits of INT4 code q times a half row scale: the product is exact in float
+__device__ __forceinline__ uint32_t int4_times(int q, float sc) {
+  return gp::f32_to_bf16_bits((float)q * sc);
+}
+__device__ __forceinline__ float half_bits_to_f32(uint32_t hs) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)hs);
+}
 __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
   const int n_items = gp::uni(*P.n_items);
-  const int L = P.chunk_pages, span = P.span, ring = span + 1;
+  const int L = P.chunk_pages, W = P.window_pages, span = P.span;
   const int lb = P.log_b, b = 1 << lb, D = P.D;
-  extern __shared__ __align__(16) uint8_t s_mx[];  // ring x MX_SLOT bytes
+  const int VS = 2 * b * D;                 // LDS slot of one source value part (bf16 codes is the largest)
+  const int lnpv = lb + __builtin_ctz(D) - 3;   // log2 of the 16-byte pieces of a slot
+  const int lnpr = __builtin_ctz(D) - 3;        // log2 of the 16-byte pieces of a bf16 key row
+  const int vslot = D / 16;                 // INT4 value dimension slot: (e % 16) * (D/16) + e / 16
+  extern __shared__ __align__(16) uint8_t s_v[];  // (W + span) slots of VS bytes
   __shared__ int s_thr[MAX_EVICT];
-  __shared__ int s_src[32];
-  __shared__ int s_tag[MAX_SPAN + 1];
-  __shared__ long long s_soff[CHUNK_PAGES + MAX_SPAN];
-  __shared__ int s_spg[CHUNK_PAGES + MAX_SPAN], s_stag[CHUNK_PAGES + MAX_SPAN], s_dpg[CHUNK_PAGES];
-  const int vslot = D / 16;  // INT4 value dimension slot stride: slot(j) = (j % 16) * (D/16) + j / 16
+  __shared__ int s_src[MAX_WINDOW_SLOTS];
+  __shared__ int s_stag[CHUNK_PAGES + MAX_SPAN], s_dtag[CHUNK_PAGES];
+  __shared__ long long s_kc[CHUNK_PAGES + MAX_SPAN], s_ks[CHUNK_PAGES + MAX_SPAN];
+  __shared__ long long s_vc[CHUNK_PAGES + MAX_SPAN], s_vs[CHUNK_PAGES + MAX_SPAN];
+  __shared__ long long s_dk[CHUNK_PAGES], s_dks[CHUNK_PAGES], s_dv[CHUNK_PAGES], s_dvs[CHUNK_PAGES];
+  uint8_t* const base = P.k;
+  auto off = [&](const void* p) { return (long long)((intptr_t)p - (intptr_t)base); };
   for (int item_k = blockIdx.x; item_k < n_items; item_k += gridDim.x) {
-    lds_barrier();
+    lds_barrier();  // the previous item is done with the tables and LDS
     const int2 item = item_of(P, item_k);
     const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y;
     const Info inf = info_of(P, i);
@@ -1625,166 +1695,231 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
                                ? P.ev[((size_t)i * P.H_kv + h) * P.max_evict + threadIdx.x] - (int)threadIdx.x
                                : INT_MAX;
     if (threadIdx.x < dp_hi - dp_lo + span) {
-      const int lp = dp_lo + threadIdx.x;
-      long long so = -2;  // -2 past the old pages, -1 snapshot, else 0
-      int pg = -1, tag = -1;
+      const int t = threadIdx.x, lp = dp_lo + t;
+      int tag = GP_TAG_BF16;
+      long long kc = NO_SRC, ks = NO_SRC, vc = NO_SRC, vs = NO_SRC;
       if (lp < inf.P) {
-        pg = P.old_bt[(size_t)i * P.max_pages + lp];
+        const int pg = P.old_bt[(size_t)i * P.max_pages + lp];
         tag = P.page_tag[pg];
-        so = from_snapshot(P, lp, c, inf.n_dest) ? -1 : 0;
+        const MixedBytes mb = mixed_bytes(tag, b, D);
+        const uint8_t *pk, *pv, *pks, *pvs;
+        if (from_snapshot(P, lp, c, inf.n_dest)) {
+          pk = snap_ptr(P, i, h, lp, 0);
+          pv = snap_ptr(P, i, h, lp, 1);
+          pks = pk + mb.kc;
+          pvs = pv + mb.vc;
+        } else {
+          mixed_src(P, tag, pg, h, &pk, &pv, &pks, &pvs);
+        }
+        kc = off(pk);
+        vc = off(pv);
+        ks = pks ? off(pks) : 0;
+        vs = pvs ? off(pvs) : 0;
       }
-      s_soff[threadIdx.x] = so;
-      s_spg[threadIdx.x] = pg;
-      s_stag[threadIdx.x] = tag;
-      if (lp < dp_hi) s_dpg[threadIdx.x] = P.block_tables[(size_t)inf.r * P.max_pages + lp];
+      s_stag[t] = tag;
+      s_kc[t] = kc;
+      s_ks[t] = ks;
+      s_vc[t] = vc;
+      s_vs[t] = vs;
+      if (lp < dp_hi) {
+        const int td = P.new_tag[(size_t)i * P.max_pages + lp];
+        const uint8_t *pk, *pv, *pks, *pvs;
+        mixed_src(P, td, P.block_tables[(size_t)inf.r * P.max_pages + lp], h, &pk, &pv, &pks, &pvs);
+        s_dtag[t] = td;
+        s_dk[t] = off(pk);
+        s_dv[t] = off(pv);
+        s_dks[t] = pks ? off(pks) : 0;
+        s_dvs[t] = pvs ? off(pvs) : 0;
+      }
     }
-    lds_barrier();
-    // stage source page lp (its own format) into ring slot lp % ring
-    auto stage = [&](int lp) {
-      const int t = lp - dp_lo;
-      uint8_t* dst = s_mx + (size_t)(lp % ring) * MX_SLOT;
-      if (s_soff[t] == -2) {
-        if (threadIdx.x == 0) s_tag[lp % ring] = -1;
-        return;
-      }
-      const int pg = s_spg[t];
-      const int tag = s_stag[t];
-      if (threadIdx.x == 0) s_tag[lp % ring] = tag;
-      const MixedBytes mb = mixed_bytes(tag, b, D);
-      const uint8_t *kc, *vc, *ks, *vs;
-      if (s_soff[t] == -1) {
-        kc = snap_ptr(P, i, h, lp, 0);
-        vc = snap_ptr(P, i, h, lp, 1);
-        ks = kc + mb.kc;
-        vs = vc + mb.vc;
-      } else {
-        mixed_src(P, tag, pg, h, &kc, &vc, &ks, &vs);
-      }
-      // layout in the slot: key codes | value codes | key scales | value scales
-      const PageParts x = load_page_parts(kc, vc, ks, vs, mb);
-      store_page_parts(x, dst, dst + mb.kc, dst + mb.kc + mb.vc, dst + mb.kc + mb.vc + mb.sc, mb);
-    };
-    for (int lp = dp_lo; lp < dp_lo + span; ++lp) stage(lp);
-    for (int dp = dp_lo; dp < dp_hi; ++dp) {
-      lds_barrier();  // the previous page is done with the ring slot and s_src
-      stage(dp + span);
-      if (threadIdx.x < b) {
-        const int j = (dp << lb) + threadIdx.x;
+    for (int w0 = dp_lo; w0 < dp_hi; w0 += W) {
+      const int w1 = min(w0 + W, dp_hi);  // destination pages [w0, w1)
+      const int nsrc = w1 - w0 + span;    // source pages [w0, w1 + span - 1]
+      const int nslots = (w1 - w0) << lb;
+      const int t0 = w0 - dp_lo;          // table index of page w0
+      lds_barrier();  // tables are set; the previous window is done with LDS
+      for (int q = threadIdx.x; q < nslots; q += CP_THREADS) {
+        const int j = (w0 << lb) + q;
         int cnt = 0;
 #pragma unroll
         for (int k = 0; k < MAX_EVICT; ++k) cnt += s_thr[k] <= j ? 1 : 0;
-        s_src[threadIdx.x] = j + cnt;
+        s_src[q] = q + cnt;  // source slot relative to the window
       }
-      lds_barrier();  // sources staged, source table complete
-      const int td = P.new_tag[(size_t)i * P.max_pages + dp];
-      const size_t ph = (size_t)s_dpg[dp - dp_lo] * P.H_kv + h;
-      // element e of token q's key / value in its source format, as float (exact) or double
-      auto src_of = [&](int q, int* slot, int* tag, int* so) {
-        const int sl = s_src[q];
-        *slot = (sl >> lb) % ring;
-        *tag = s_tag[*slot];
-        *so = sl & (b - 1);
-      };
-      if (td == GP_TAG_BF16) {
-        uint16_t* kd = reinterpret_cast<uint16_t*>(P.k) + ph * b * D;
-        uint16_t* vd = reinterpret_cast<uint16_t*>(P.v) + ph * b * D;
-        for (int q2 = threadIdx.x; q2 < b * D; q2 += CP_THREADS) {
-          // key element (token q, dim e) and value element (dim e2, token q3)
-          const int q = q2 / D, e = q2 % D;
-          int sl, tg, so;
-          src_of(q, &sl, &tg, &so);
-          const uint8_t* base = s_mx + (size_t)sl * MX_SLOT;
-          const MixedBytes mb = mixed_bytes(tg, b, D);
-          uint32_t kbits;
-          if (tg == GP_TAG_BF16) {
-            kbits = reinterpret_cast<const uint16_t*>(base)[so * D + e];
-          } else if (tg == GP_TAG_FP8) {
-            const uint32_t code = base[so * D + e];
-            const float f = __builtin_amdgcn_cvt_pk_f32_fp8(code, false)[0];
-            const float sc = reinterpret_cast<const float*>(base + mb.kc + mb.vc)[so];
-            kbits = f64_to_bf16_bits((double)f * (double)sc);
-          } else {
-            const uint32_t byte = base[so * (D / 2) + e / 2];
-            const int cde = nib(byte, e & 1);
-            const uint16_t hs = reinterpret_cast<const uint16_t*>(base + mb.kc + mb.vc)[so];
-            kbits = gp::f32_to_bf16_bits((float)cde * (float)__builtin_bit_cast(_Float16, hs));
-          }
-          kd[q * D + e] = (uint16_t)kbits;
-          // value element: dim e2, token q3 of the destination page ([D][b] layout)
-          const int e2 = q2 / b, q3 = q2 % b;
-          src_of(q3, &sl, &tg, &so);
-          const uint8_t* vb = s_mx + (size_t)sl * MX_SLOT;
-          const MixedBytes mv = mixed_bytes(tg, b, D);
-          uint32_t vbits;
-          if (tg == GP_TAG_BF16) {
-            vbits = reinterpret_cast<const uint16_t*>(vb + mv.kc)[e2 * b + so];
-          } else if (tg == GP_TAG_FP8) {
-            const uint32_t code = vb[mv.kc + e2 * b + so];
-            const float f = __builtin_amdgcn_cvt_pk_f32_fp8(code, false)[0];
-            const float sc = reinterpret_cast<const float*>(vb + mv.kc + mv.vc + mv.sc)[so];
-            vbits = f64_to_bf16_bits((double)f * (double)sc);
-          } else {
-            // four-token block so / 4, dimension slot of e2, byte (so % 4) / 2, nibble so % 2
-            const int slot = (e2 % 16) * vslot + e2 / 16;
-            const uint32_t byte = vb[mv.kc + ((so >> 2) * D + slot) * 2 + ((so & 3) >> 1)];
-            const int cde = nib(byte, so & 1);
-            const uint16_t hs = reinterpret_cast<const uint16_t*>(vb + mv.kc + mv.vc + mv.sc)[so];
-            vbits = gp::f32_to_bf16_bits((float)cde * (float)__builtin_bit_cast(_Float16, hs));
-          }
-          vd[e2 * b + q3] = (uint16_t)vbits;
-        }
-      } else if (td == GP_TAG_FP8) {
-        // every source is fp8: codes and row scales move as they are
-        uint8_t* kd = P.k8 + ph * b * D;
-        uint8_t* vd = P.v8 + ph * b * D;
-        for (int q2 = threadIdx.x; q2 < b * D; q2 += CP_THREADS) {
-          const int q = q2 / D, e = q2 % D;
-          int sl, tg, so;
-          src_of(q, &sl, &tg, &so);
-          kd[q * D + e] = s_mx[(size_t)sl * MX_SLOT + so * D + e];
-          const int e2 = q2 / b, q3 = q2 % b;
-          src_of(q3, &sl, &tg, &so);
-          vd[e2 * b + q3] = s_mx[(size_t)sl * MX_SLOT + b * D + e2 * b + so];
-        }
-        if (threadIdx.x < b) {
-          const int q = threadIdx.x;
-          int sl, tg, so;
-          src_of(q, &sl, &tg, &so);
-          const float* sc = reinterpret_cast<const float*>(s_mx + (size_t)sl * MX_SLOT + 2 * b * D);
-          P.k_scale[ph * b + q] = sc[so];
-          P.v_scale[ph * b + q] = sc[b + so];
-        }
-      } else {
-        // every source is INT4: key rows and scales copied, value nibbles regrouped
-        uint8_t* kd = P.k4 + ph * b * D / 2;
-        uint8_t* vd = P.v4 + ph * b * D / 2;
-        for (int q2 = threadIdx.x; q2 < b * D / 2; q2 += CP_THREADS) {
-          const int q = q2 / (D / 2), e = q2 % (D / 2);
-          int sl, tg, so;
-          src_of(q, &sl, &tg, &so);
-          kd[q * (D / 2) + e] = s_mx[(size_t)sl * MX_SLOT + so * (D / 2) + e];
-          // destination value byte q2: block Q, dimension slot ds, byte k (tokens 4Q+2k, 4Q+2k+1)
-          const int k = q2 & 1, ds = (q2 >> 1) % D, Q = (q2 >> 1) / D;
-          uint32_t out = 0;
+      lds_barrier();
+      // value parts of the source pages: piece k of slot t is codes piece k, then scale pieces
+      u32x4_t vreg[MXV_PIECES];
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            src_of(4 * Q + 2 * k + t, &sl, &tg, &so);
-            const uint32_t byte = s_mx[(size_t)sl * MX_SLOT + b * D / 2 + ((so >> 2) * D + ds) * 2 + ((so & 3) >> 1)];
-            out |= ((byte >> (4 * (so & 1))) & 0xFu) << (4 * t);
+      for (int it = 0; it < MXV_PIECES; ++it) {
+        const int q = threadIdx.x + it * CP_THREADS;
+        const int t = min(q >> lnpv, nsrc - 1), k = q & ((1 << lnpv) - 1);
+        const int tag = s_stag[t0 + t];
+        const MixedBytes mb = mixed_bytes(tag, b, D);
+        const long long vc = s_vc[t0 + t];
+        long long o = 0;
+        if (q >> lnpv < nsrc && vc != NO_SRC && 16 * k < mb.vc + mb.sc)
+          o = 16 * k < mb.vc ? vc + 16 * k : s_vs[t0 + t] + (16 * k - mb.vc);
+        vreg[it] = *reinterpret_cast<const u32x4_t*>(base + o);
+      }
+      // key pieces on the bf16 row grid: piece p of destination row `slot`, from the source row in
+      // its own format (a converted piece reads 8 fp8 codes or 8 INT4 nibbles and the row scale)
+      const int nk = nslots << lnpr;
+      u32x4_t kreg[MXK_PIECES];
+      uint32_t kscale[MXK_PIECES];
+#pragma unroll
+      for (int it = 0; it < MXK_PIECES; ++it) {
+        const int q = min((int)threadIdx.x + it * CP_THREADS, nk - 1);
+        const int slot = q >> lnpr, p = q & ((1 << lnpr) - 1);
+        const int td = s_dtag[t0 + (slot >> lb)];
+        const int src = s_src[slot];
+        const int ts = s_stag[t0 + (src >> lb)], so = src & (b - 1);
+        const long long kc = s_kc[t0 + (src >> lb)];
+        const int sub = ts == td ? 16 * p : (ts == GP_TAG_FP8 ? 8 * p : 4 * p);
+        const bool ok = 16 * p < mx_row_bytes(td, D) && kc != NO_SRC;
+        const long long o = ok ? kc + (long long)so * mx_row_bytes(ts, D) + (sub & ~15) : 0;
+        kreg[it] = *reinterpret_cast<const u32x4_t*>(base + o);
+        const long long so_s = (ok && ts != td) ? s_ks[t0 + (src >> lb)] + (long long)so * mx_scale_bytes(ts) : 0;
+        kscale[it] = *reinterpret_cast<const uint32_t*>(base + (so_s & ~3ll));
+        kscale[it] = (so_s & 2) ? kscale[it] >> 16 : kscale[it];
+      }
+      // key row scale of destination row threadIdx.x (fp8 / INT4 destinations; nslots <= threads)
+      uint32_t ksrow;
+      {
+        const int q = min((int)threadIdx.x, nslots - 1);
+        const int td = s_dtag[t0 + (q >> lb)], src = s_src[q];
+        const long long ks = s_ks[t0 + (src >> lb)];
+        const long long so_s =
+            (td != GP_TAG_BF16 && ks != NO_SRC) ? ks + (long long)(src & (b - 1)) * mx_scale_bytes(td) : 0;
+        ksrow = *reinterpret_cast<const uint32_t*>(base + (so_s & ~3ll));
+        ksrow = (so_s & 2) ? ksrow >> 16 : ksrow;
+      }
+#pragma unroll
+      for (int it = 0; it < MXV_PIECES; ++it) {
+        const int q = threadIdx.x + it * CP_THREADS;
+        if (q >> lnpv < nsrc) reinterpret_cast<u32x4_t*>(s_v)[q] = vreg[it];
+      }
+      lds_barrier();  // every read of this window's sources precedes any write
+#pragma unroll
+      for (int it = 0; it < MXK_PIECES; ++it) {
+        const int q = threadIdx.x + it * CP_THREADS;
+        if (q >= nk) continue;
+        const int slot = q >> lnpr, p = q & ((1 << lnpr) - 1);
+        const int dpl = slot >> lb, td = s_dtag[t0 + dpl];
+        if (16 * p >= mx_row_bytes(td, D)) continue;
+        const int src = s_src[slot];
+        const int ts = s_stag[t0 + (src >> lb)];
+        u32x4_t out = kreg[it];
+        if (ts != td) {  // td is bf16: 8 elements 8p .. 8p + 7
+          uint32_t e[8];
+          if (ts == GP_TAG_FP8) {
+            const int w = ((8 * p) & 15) >> 2;  // 0 or 2
+            const uint32_t lo = word_of(kreg[it], w), hi = word_of(kreg[it], w + 1);
+            const float sc = __uint_as_float(kscale[it]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              e[m] = fp8_times(lo >> (8 * m), sc);
+              e[4 + m] = fp8_times(hi >> (8 * m), sc);
+            }
+          } else {
+            const uint32_t wd = word_of(kreg[it], ((4 * p) & 15) >> 2);
+            const float sc = half_bits_to_f32(kscale[it] & 0xffffu);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) e[m] = int4_times(nib(wd, m), sc);
           }
-          vd[q2] = (uint8_t)out;
+          out = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
         }
-        if (threadIdx.x < b) {
-          const int q = threadIdx.x;
-          int sl, tg, so;
-          src_of(q, &sl, &tg, &so);
-          const uint16_t* sc = reinterpret_cast<const uint16_t*>(s_mx + (size_t)sl * MX_SLOT + b * D);
-          P.k4_scale[ph * b + q] = sc[so];
-          P.v4_scale[ph * b + q] = sc[b + so];
+        *reinterpret_cast<u32x4_t*>(base + s_dk[t0 + dpl] + (long long)(slot & (b - 1)) * mx_row_bytes(td, D) + 16 * p) = out;
+      }
+      // row scales of fp8 / INT4 destination rows (every source of such a page has its format):
+      // the key scale read above, the value scale from the staged slot
+      if ((int)threadIdx.x < nslots) {
+        const int q = threadIdx.x, dpl = q >> lb, td = s_dtag[t0 + dpl];
+        if (td != GP_TAG_BF16) {
+          const int src = s_src[q], so = src & (b - 1), row = q & (b - 1);
+          const uint8_t* vsc = s_v + (size_t)(src >> lb) * VS + mixed_bytes(td, b, D).vc;
+          if (td == GP_TAG_FP8) {
+            reinterpret_cast<uint32_t*>(base + s_dks[t0 + dpl])[row] = ksrow;
+            reinterpret_cast<uint32_t*>(base + s_dvs[t0 + dpl])[row] = reinterpret_cast<const uint32_t*>(vsc)[so];
+          } else {
+            reinterpret_cast<uint16_t*>(base + s_dks[t0 + dpl])[row] = (uint16_t)ksrow;
+            reinterpret_cast<uint16_t*>(base + s_dvs[t0 + dpl])[row] = reinterpret_cast<const uint16_t*>(vsc)[so];
+          }
+        }
+      }
+      // values, gathered from the staged slots. bf16 and fp8 destinations ([D][b] rows): a lane
+      // takes two adjacent tokens, whose sources it looks up once per page, and writes them in
+      // every row it owns; INT4 destinations ([b/4][D][2]): a lane writes the two bytes of one
+      // dimension slot of a four-token block.
+      const int lhb = lb - 1;
+      const int tp = threadIdx.x & ((1 << lhb) - 1), r0 = threadIdx.x >> lhb;
+      const int rpi = CP_THREADS >> lhb;
+      for (int dpl = 0; dpl < w1 - w0; ++dpl) {
+        const int td = s_dtag[t0 + dpl];
+        uint8_t* dv = base + s_dv[t0 + dpl];
+        if (td == GP_TAG_INT4) {
+          for (int u = threadIdx.x; u < (b >> 2) * D; u += CP_THREADS) {
+            const int ds = u % D, Q = u / D;
+            uint32_t out = 0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const int src = s_src[(dpl << lb) + 4 * Q + m], so = src & (b - 1);
+              const uint8_t* a = s_v + (size_t)(src >> lb) * VS;
+              const uint32_t byte = a[((so >> 2) * D + ds) * 2 + ((so & 3) >> 1)];
+              out |= ((byte >> (4 * (so & 1))) & 0xFu) << (4 * m);
+            }
+            reinterpret_cast<uint16_t*>(dv)[Q * D + ds] = (uint16_t)out;
+          }
+          continue;
+        }
+        int so[2], tg[2];
+        const uint8_t* a[2];
+        float sc[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int src = s_src[(dpl << lb) + 2 * tp + m];
+          so[m] = src & (b - 1);
+          tg[m] = s_stag[t0 + (src >> lb)];
+          a[m] = s_v + (size_t)(src >> lb) * VS;
+          const MixedBytes mb = mixed_bytes(tg[m], b, D);
+          sc[m] = tg[m] == GP_TAG_FP8 ? reinterpret_cast<const float*>(a[m] + mb.vc)[so[m]]
+                  : tg[m] == GP_TAG_INT4 ? half_bits_to_f32(reinterpret_cast<const uint16_t*>(a[m] + mb.vc)[so[m]])
+                                         : 0.f;
+        }
+        if (td == GP_TAG_FP8) {
+          for (int dd = r0; dd < D; dd += rpi) {
+            const uint32_t x0 = a[0][dd * b + so[0]], x1 = a[1][dd * b + so[1]];
+            reinterpret_cast<uint16_t*>(dv + dd * b)[tp] = (uint16_t)(x0 | (x1 << 8));
+          }
+          continue;
+        }
+        for (int dd = r0; dd < D; dd += rpi) {
+          uint32_t x[2];
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            if (tg[m] == GP_TAG_BF16) {
+              x[m] = reinterpret_cast<const uint16_t*>(a[m])[dd * b + so[m]];
+            } else if (tg[m] == GP_TAG_FP8) {
+              x[m] = fp8_times(a[m][dd * b + so[m]], sc[m]);
+            } else {
+              const int sl = (dd % 16) * vslot + dd / 16;
+              const uint32_t byte = a[m][((so[m] >> 2) * D + sl) * 2 + ((so[m] & 3) >> 1)];
+              x[m] = int4_times(nib(byte, so[m] & 1), sc[m]);
+            }
+          }
+          reinterpret_cast<uint32_t*>(dv + dd * 2 * b)[tp] = x[0] | (x[1] << 16);
         }
       }
     }
   }
+}
+
+// Window of a mixed-precision compaction: the W * b destination key rows (bf16-sized) must fit
+// MXK_PIECES pieces per thread and the W + span staged value parts MXV_PIECES.
+int mixed_window_pages(int page_size, int D, int span) {
+  int W = 8;
+  while (W > 1 && ((long)W * page_size * (D / 8) > (long)MXK_PIECES * CP_THREADS ||
+                   (long)(W + span) * page_size * (D / 8) > (long)MXV_PIECES * CP_THREADS))
+    --W;
+  return W;
 }
 
 // Window of W destination pages: LDS holds the W + span source value pages, and the W * b key
@@ -2076,8 +2211,10 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
       GP_CHECK_LAUNCH();
     }
     if (mixed) {
+      CParams M = Q;
+      M.window_pages = mixed_window_pages(b, D, span);
       hipLaunchKernelGGL(compact_mixed_kernel, dim3(std::max(1, std::min(4 * cus, max_items))),
-                         dim3(CP_THREADS), (size_t)(span + 1) * MX_SLOT, s, Q);
+                         dim3(CP_THREADS), (size_t)(M.window_pages + span) * 2 * b * D, s, M);
       GP_CHECK_LAUNCH();
       hipLaunchKernelGGL(mixed_tags_kernel, dim3(R), dim3(256), 0, s, Q);
       GP_CHECK_LAUNCH();
