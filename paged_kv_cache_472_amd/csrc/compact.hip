@@ -1643,7 +1643,7 @@ __device__ __forceinline__ int nib(uint32_t w, int n) { return (int32_t)(w << (2
 // pages (the next chunk's first pages from the snapshot), and every staged byte is read before
 // the barrier that precedes the next window's staging.
 constexpr int MXK_PIECES = 4;   // key pieces per thread and window (16-byte pieces of bf16 rows)
-constexpr int MXV_PIECES = 12;  // staged value pieces per thread and window
+constexpr int MXV_PIECES = 8;   // staged value pieces per thread and window
 __device__ __forceinline__ int mx_row_bytes(int tag, int D) {
   return tag == GP_TAG_FP8 ? D : (tag == GP_TAG_INT4 ? D / 2 : 2 * D);
 }
@@ -1654,9 +1654,24 @@ __device__ __forceinline__ int mx_scale_bytes(int tag) {
 __device__ __forceinline__ uint32_t word_of(const u32x4_t& x, int w) {
   return w == 0 ? x[0] : (w == 1 ? x[1] : (w == 2 ? x[2] : x[3]));
 }
+// bf16 bits of a * b rounded once, to nearest with ties to even. The float product can only go
+// wrong when it lands exactly on a bf16 midpoint while the exact product does not: its residual
+// (an fma, exact for a normal product of normal factors) then says which way to round. Zero
+// products are exact; nonzero ones below 2^-96, or a subnormal b, take the float64 route.
+__device__ __forceinline__ uint32_t mul_to_bf16_bits(float a, float b) {
+  const float p = a * b;
+  if ((fabsf(p) < 0x1p-96f && p != 0.f) || fabsf(b) < 0x1p-126f)
+    return f64_to_bf16_bits((double)a * (double)b);
+  const uint32_t u = __float_as_uint(p);
+  if ((u & 0xffffu) == 0x8000u) {
+    const float e = __builtin_fmaf(a, b, -p);
+    if (e != 0.f) return (u >> 16) + (((__float_as_uint(e) ^ u) >> 31) ^ 1u);
+  }
+  return gp::f32_to_bf16_bits(p);
+}
 // bf16 bits of the element with fp8 code c (low byte) times an fp32 row scale: one rounding
 __device__ __forceinline__ uint32_t fp8_times(uint32_t c, float sc) {
-  return f64_to_bf16_bits((double)__builtin_amdgcn_cvt_pk_f32_fp8(c, false)[0] * (double)sc);
+  return mul_to_bf16_bits(__builtin_amdgcn_cvt_pk_f32_fp8(c, false)[0], sc);
 }
 // bf16 bits of INT4 code q times a half row scale: the product is exact in float
 __device__ __forceinline__ uint32_t int4_times(int q, float sc) {
@@ -1682,6 +1697,9 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
   __shared__ long long s_dk[CHUNK_PAGES], s_dks[CHUNK_PAGES], s_dv[CHUNK_PAGES], s_dvs[CHUNK_PAGES];
   uint8_t* const base = P.k;
   auto off = [&](const void* p) { return (long long)((intptr_t)p - (intptr_t)base); };
+  // stand-in pieces: 16 * (q & sm) stays inside the bf16 key pool (at most its first 16 KB)
+  const long long pool_pieces = (long long)P.num_pages * P.H_kv * b * D * 2 / 16;
+  const int sm = (int)(1ll << (63 - __builtin_clzll((unsigned long long)min(pool_pieces, 1024ll)))) - 1;
   for (int item_k = blockIdx.x; item_k < n_items; item_k += gridDim.x) {
     lds_barrier();  // the previous item is done with the tables and LDS
     const int2 item = item_of(P, item_k);
@@ -1737,8 +1755,12 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
       const int nsrc = w1 - w0 + span;    // source pages [w0, w1 + span - 1]
       const int nslots = (w1 - w0) << lb;
       const int t0 = w0 - dp_lo;          // table index of page w0
+      // the thread index, opaque to the compiler inside the window: otherwise it hoists every
+      // per-piece index out of the loops and holds them in registers for the whole kernel
+      int tx = threadIdx.x;
+      asm volatile("" : "+v"(tx));
       lds_barrier();  // tables are set; the previous window is done with LDS
-      for (int q = threadIdx.x; q < nslots; q += CP_THREADS) {
+      for (int q = tx; q < nslots; q += CP_THREADS) {
         const int j = (w0 << lb) + q;
         int cnt = 0;
 #pragma unroll
@@ -1750,14 +1772,18 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
       u32x4_t vreg[MXV_PIECES];
 #pragma unroll
       for (int it = 0; it < MXV_PIECES; ++it) {
-        const int q = threadIdx.x + it * CP_THREADS;
+        const int q = tx + it * CP_THREADS;
         const int t = min(q >> lnpv, nsrc - 1), k = q & ((1 << lnpv) - 1);
         const int tag = s_stag[t0 + t];
         const MixedBytes mb = mixed_bytes(tag, b, D);
         const long long vc = s_vc[t0 + t];
-        long long o = 0;
-        if (q >> lnpv < nsrc && vc != NO_SRC && 16 * k < mb.vc + mb.sc)
-          o = 16 * k < mb.vc ? vc + 16 * k : s_vs[t0 + t] + (16 * k - mb.vc);
+        // a piece with nothing to stage reads a codes piece of the same page (fetched by another
+        // lane anyway), or one of the pool's first lines: stand-ins spread over many cache lines
+        // rather than all landing on one
+        long long o = 16 * (q & sm);
+        if (q >> lnpv < nsrc && vc != NO_SRC)
+          o = 16 * k < mb.vc ? vc + 16 * k
+              : (16 * k < mb.vc + mb.sc ? s_vs[t0 + t] + (16 * k - mb.vc) : vc + ((16 * k) & (mb.vc - 1)));
         vreg[it] = *reinterpret_cast<const u32x4_t*>(base + o);
       }
       // key pieces on the bf16 row grid: piece p of destination row `slot`, from the source row in
@@ -1767,7 +1793,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
       uint32_t kscale[MXK_PIECES];
 #pragma unroll
       for (int it = 0; it < MXK_PIECES; ++it) {
-        const int q = min((int)threadIdx.x + it * CP_THREADS, nk - 1);
+        const int q = min(tx + it * CP_THREADS, nk - 1);
         const int slot = q >> lnpr, p = q & ((1 << lnpr) - 1);
         const int td = s_dtag[t0 + (slot >> lb)];
         const int src = s_src[slot];
@@ -1775,64 +1801,69 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
         const long long kc = s_kc[t0 + (src >> lb)];
         const int sub = ts == td ? 16 * p : (ts == GP_TAG_FP8 ? 8 * p : 4 * p);
         const bool ok = 16 * p < mx_row_bytes(td, D) && kc != NO_SRC;
-        const long long o = ok ? kc + (long long)so * mx_row_bytes(ts, D) + (sub & ~15) : 0;
+        const long long row = kc != NO_SRC ? kc + (long long)so * mx_row_bytes(ts, D) : 16 * (q & sm);
+        const long long o = ok ? row + (sub & ~15) : row;  // a piece past the row: the row's first
         kreg[it] = *reinterpret_cast<const u32x4_t*>(base + o);
-        const long long so_s = (ok && ts != td) ? s_ks[t0 + (src >> lb)] + (long long)so * mx_scale_bytes(ts) : 0;
+        const long long so_s = (ok && ts != td) ? s_ks[t0 + (src >> lb)] + (long long)so * mx_scale_bytes(ts) : o;
         kscale[it] = *reinterpret_cast<const uint32_t*>(base + (so_s & ~3ll));
         kscale[it] = (so_s & 2) ? kscale[it] >> 16 : kscale[it];
       }
-      // key row scale of destination row threadIdx.x (fp8 / INT4 destinations; nslots <= threads)
+      // key row scale of destination row tx (fp8 / INT4 destinations; nslots <= threads)
       uint32_t ksrow;
       {
-        const int q = min((int)threadIdx.x, nslots - 1);
+        const int q = min(tx, nslots - 1);
         const int td = s_dtag[t0 + (q >> lb)], src = s_src[q];
-        const long long ks = s_ks[t0 + (src >> lb)];
-        const long long so_s =
-            (td != GP_TAG_BF16 && ks != NO_SRC) ? ks + (long long)(src & (b - 1)) * mx_scale_bytes(td) : 0;
+        const long long ks = s_ks[t0 + (src >> lb)], kc = s_kc[t0 + (src >> lb)];
+        const long long so_s = (td != GP_TAG_BF16 && ks != NO_SRC)
+                                   ? ks + (long long)(src & (b - 1)) * mx_scale_bytes(td)
+                                   : (kc != NO_SRC ? kc : 16 * (q & sm));
         ksrow = *reinterpret_cast<const uint32_t*>(base + (so_s & ~3ll));
         ksrow = (so_s & 2) ? ksrow >> 16 : ksrow;
       }
 #pragma unroll
       for (int it = 0; it < MXV_PIECES; ++it) {
-        const int q = threadIdx.x + it * CP_THREADS;
+        const int q = tx + it * CP_THREADS;
         if (q >> lnpv < nsrc) reinterpret_cast<u32x4_t*>(s_v)[q] = vreg[it];
       }
       lds_barrier();  // every read of this window's sources precedes any write
 #pragma unroll
       for (int it = 0; it < MXK_PIECES; ++it) {
-        const int q = threadIdx.x + it * CP_THREADS;
+        const int q = tx + it * CP_THREADS;
         if (q >= nk) continue;
         const int slot = q >> lnpr, p = q & ((1 << lnpr) - 1);
         const int dpl = slot >> lb, td = s_dtag[t0 + dpl];
         if (16 * p >= mx_row_bytes(td, D)) continue;
         const int src = s_src[slot];
         const int ts = s_stag[t0 + (src >> lb)];
-        u32x4_t out = kreg[it];
+        const u32x4_t kr = kreg[it];
+        const uint32_t ksc = kscale[it];
+        u32x4_t out = kr;
         if (ts != td) {  // td is bf16: 8 elements 8p .. 8p + 7
           uint32_t e[8];
           if (ts == GP_TAG_FP8) {
             const int w = ((8 * p) & 15) >> 2;  // 0 or 2
-            const uint32_t lo = word_of(kreg[it], w), hi = word_of(kreg[it], w + 1);
-            const float sc = __uint_as_float(kscale[it]);
+            const uint32_t lo = word_of(kr, w), hi = word_of(kr, w + 1);
+            const float sc = __uint_as_float(ksc);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
               e[m] = fp8_times(lo >> (8 * m), sc);
               e[4 + m] = fp8_times(hi >> (8 * m), sc);
             }
           } else {
-            const uint32_t wd = word_of(kreg[it], ((4 * p) & 15) >> 2);
-            const float sc = half_bits_to_f32(kscale[it] & 0xffffu);
+            const uint32_t wd = word_of(kr, ((4 * p) & 15) >> 2);
+            const float sc = half_bits_to_f32(ksc & 0xffffu);
 #pragma unroll
             for (int m = 0; m < 8; ++m) e[m] = int4_times(nib(wd, m), sc);
           }
           out = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
         }
         *reinterpret_cast<u32x4_t*>(base + s_dk[t0 + dpl] + (long long)(slot & (b - 1)) * mx_row_bytes(td, D) + 16 * p) = out;
+        __builtin_amdgcn_sched_barrier(0);  // one piece's conversion at a time: fewer live registers
       }
       // row scales of fp8 / INT4 destination rows (every source of such a page has its format):
       // the key scale read above, the value scale from the staged slot
-      if ((int)threadIdx.x < nslots) {
-        const int q = threadIdx.x, dpl = q >> lb, td = s_dtag[t0 + dpl];
+      if (tx < nslots) {
+        const int q = tx, dpl = q >> lb, td = s_dtag[t0 + dpl];
         if (td != GP_TAG_BF16) {
           const int src = s_src[q], so = src & (b - 1), row = q & (b - 1);
           const uint8_t* vsc = s_v + (size_t)(src >> lb) * VS + mixed_bytes(td, b, D).vc;
@@ -1850,13 +1881,13 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
       // every row it owns; INT4 destinations ([b/4][D][2]): a lane writes the two bytes of one
       // dimension slot of a four-token block.
       const int lhb = lb - 1;
-      const int tp = threadIdx.x & ((1 << lhb) - 1), r0 = threadIdx.x >> lhb;
+      const int tp = tx & ((1 << lhb) - 1), r0 = tx >> lhb;
       const int rpi = CP_THREADS >> lhb;
       for (int dpl = 0; dpl < w1 - w0; ++dpl) {
         const int td = s_dtag[t0 + dpl];
         uint8_t* dv = base + s_dv[t0 + dpl];
         if (td == GP_TAG_INT4) {
-          for (int u = threadIdx.x; u < (b >> 2) * D; u += CP_THREADS) {
+          for (int u = tx; u < (b >> 2) * D; u += CP_THREADS) {
             const int ds = u % D, Q = u / D;
             uint32_t out = 0;
 #pragma unroll
