@@ -1677,6 +1677,33 @@ __device__ __forceinline__ uint32_t fp8_times(uint32_t c, float sc) {
 __device__ __forceinline__ uint32_t int4_times(int q, float sc) {
   return gp::f32_to_bf16_bits((float)q * sc);
 }
+typedef __bf16 mx_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float mx_f32x2 __attribute__((ext_vector_type(2)));
+// two floats to a bf16 pair (low half p0), to nearest even, in one instruction on gfx950
+__device__ __forceinline__ uint32_t pk_bf16(float p0, float p1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((mx_f32x2){p0, p1}, mx_bf16x2));
+}
+// The products x0 * s0 and x1 * s1 rounded once to a bf16 pair, where each x is exact in float
+// and each product either exact in float (INT4 codes times a half scale) or an fp8 value times a
+// float scale of magnitude in [2^-87, 2^100) (a normal product whose float rounding is off by at
+// most half a float ulp). The hardware rounding of the float product is then right unless that
+// product sits exactly on a bf16 midpoint while the exact one does not: the product's fma residual
+// (exact for a normal product) gives the side. `inexact` marks the products that may have rounded.
+__device__ __forceinline__ uint32_t pair_to_bf16(float x0, float s0, bool inexact0, float x1, float s1,
+                                                 bool inexact1) {
+  const float p0 = x0 * s0, p1 = x1 * s1;
+  uint32_t r = pk_bf16(p0, p1);
+  const uint32_t u0 = __float_as_uint(p0), u1 = __float_as_uint(p1);
+  const bool m0 = inexact0 && (u0 & 0xffffu) == 0x8000u, m1 = inexact1 && (u1 & 0xffffu) == 0x8000u;
+  if (__builtin_expect(m0 || m1, 0)) {
+    const float e0 = __builtin_fmaf(x0, s0, -p0), e1 = __builtin_fmaf(x1, s1, -p1);
+    if (m0 && e0 != 0.f) r = (r & 0xffff0000u) | ((u0 >> 16) + (((__float_as_uint(e0) ^ u0) >> 31) ^ 1u));
+    if (m1 && e1 != 0.f) r = (r & 0xffffu) | (((u1 >> 16) + (((__float_as_uint(e1) ^ u1) >> 31) ^ 1u)) << 16);
+  }
+  return r;
+}
+// a float scale that keeps every nonzero fp8 product normal (fp8 values are at least 2^-9)
+__device__ __forceinline__ bool fp8_scale_fast(float sc) { return fabsf(sc) >= 0x1p-87f && fabsf(sc) < 0x1p100f; }
 __device__ __forceinline__ float half_bits_to_f32(uint32_t hs) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)hs);
 }
@@ -1768,24 +1795,6 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
         s_src[q] = q + cnt;  // source slot relative to the window
       }
       lds_barrier();
-      // value parts of the source pages: piece k of slot t is codes piece k, then scale pieces
-      u32x4_t vreg[MXV_PIECES];
-#pragma unroll
-      for (int it = 0; it < MXV_PIECES; ++it) {
-        const int q = tx + it * CP_THREADS;
-        const int t = min(q >> lnpv, nsrc - 1), k = q & ((1 << lnpv) - 1);
-        const int tag = s_stag[t0 + t];
-        const MixedBytes mb = mixed_bytes(tag, b, D);
-        const long long vc = s_vc[t0 + t];
-        // a piece with nothing to stage reads a codes piece of the same page (fetched by another
-        // lane anyway), or one of the pool's first lines: stand-ins spread over many cache lines
-        // rather than all landing on one
-        long long o = 16 * (q & sm);
-        if (q >> lnpv < nsrc && vc != NO_SRC)
-          o = 16 * k < mb.vc ? vc + 16 * k
-              : (16 * k < mb.vc + mb.sc ? s_vs[t0 + t] + (16 * k - mb.vc) : vc + ((16 * k) & (mb.vc - 1)));
-        vreg[it] = *reinterpret_cast<const u32x4_t*>(base + o);
-      }
       // key pieces on the bf16 row grid: piece p of destination row `slot`, from the source row in
       // its own format (a converted piece reads 8 fp8 codes or 8 INT4 nibbles and the row scale)
       const int nk = nslots << lnpr;
@@ -1820,12 +1829,25 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
         ksrow = *reinterpret_cast<const uint32_t*>(base + (so_s & ~3ll));
         ksrow = (so_s & 2) ? ksrow >> 16 : ksrow;
       }
+      // value parts of the source pages, straight into LDS (one 16-byte piece per lane, a wave's
+      // pieces contiguous): piece k of slot t is codes piece k, then the scale pieces; lanes with
+      // no piece to stage issue no load
 #pragma unroll
       for (int it = 0; it < MXV_PIECES; ++it) {
         const int q = tx + it * CP_THREADS;
-        if (q >> lnpv < nsrc) reinterpret_cast<u32x4_t*>(s_v)[q] = vreg[it];
+        const int t = min(q >> lnpv, nsrc - 1), k = q & ((1 << lnpv) - 1);
+        const MixedBytes mb = mixed_bytes(s_stag[t0 + t], b, D);
+        const long long vc = s_vc[t0 + t];
+        if (q >> lnpv < nsrc && vc != NO_SRC && 16 * k < mb.vc + mb.sc) {
+          const long long o = 16 * k < mb.vc ? vc + 16 * k : s_vs[t0 + t] + (16 * k - mb.vc);
+          __builtin_amdgcn_global_load_lds(
+              static_cast<const void*>(base + o),
+              (__attribute__((address_space(3))) void*)(s_v + 16 * ((tx & ~(GP_WAVE - 1)) + it * CP_THREADS)), 16, 0, 0);
+        }
       }
-      lds_barrier();  // every read of this window's sources precedes any write
+      // every load of the window has landed (the staged pieces in LDS too) before any write
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
 #pragma unroll
       for (int it = 0; it < MXK_PIECES; ++it) {
         const int q = tx + it * CP_THREADS;
@@ -1839,23 +1861,30 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
         const uint32_t ksc = kscale[it];
         u32x4_t out = kr;
         if (ts != td) {  // td is bf16: 8 elements 8p .. 8p + 7
-          uint32_t e[8];
+          uint32_t e[4];
           if (ts == GP_TAG_FP8) {
             const int w = ((8 * p) & 15) >> 2;  // 0 or 2
-            const uint32_t lo = word_of(kr, w), hi = word_of(kr, w + 1);
+            const uint32_t wd[2] = {word_of(kr, w), word_of(kr, w + 1)};
             const float sc = __uint_as_float(ksc);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              e[m] = fp8_times(lo >> (8 * m), sc);
-              e[4 + m] = fp8_times(hi >> (8 * m), sc);
+            if (__builtin_expect(!fp8_scale_fast(sc), 0)) {
+              // a scale outside the fast range: element by element, the exact route
+              uint16_t* kd16 = reinterpret_cast<uint16_t*>(
+                  base + s_dk[t0 + dpl] + (long long)(slot & (b - 1)) * mx_row_bytes(td, D) + 16 * p);
+#pragma unroll 1
+              for (int m = 0; m < 8; ++m) kd16[m] = (uint16_t)fp8_times(wd[m >> 2] >> (8 * (m & 3)), sc);
+              continue;
             }
+            const mx_f32x2 f[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(wd[0], false), __builtin_amdgcn_cvt_pk_f32_fp8(wd[0], true),
+                                   __builtin_amdgcn_cvt_pk_f32_fp8(wd[1], false), __builtin_amdgcn_cvt_pk_f32_fp8(wd[1], true)};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) e[m] = pair_to_bf16(f[m][0], sc, true, f[m][1], sc, true);
           } else {
             const uint32_t wd = word_of(kr, ((4 * p) & 15) >> 2);
             const float sc = half_bits_to_f32(ksc & 0xffffu);
 #pragma unroll
-            for (int m = 0; m < 8; ++m) e[m] = int4_times(nib(wd, m), sc);
+            for (int m = 0; m < 4; ++m) e[m] = pk_bf16((float)nib(wd, 2 * m) * sc, (float)nib(wd, 2 * m + 1) * sc);
           }
-          out = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+          out = u32x4_t{e[0], e[1], e[2], e[3]};
         }
         *reinterpret_cast<u32x4_t*>(base + s_dk[t0 + dpl] + (long long)(slot & (b - 1)) * mx_row_bytes(td, D) + 16 * p) = out;
         __builtin_amdgcn_sched_barrier(0);  // one piece's conversion at a time: fewer live registers
@@ -1913,7 +1942,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
           const MixedBytes mb = mixed_bytes(tg[m], b, D);
           sc[m] = tg[m] == GP_TAG_FP8 ? reinterpret_cast<const float*>(a[m] + mb.vc)[so[m]]
                   : tg[m] == GP_TAG_INT4 ? half_bits_to_f32(reinterpret_cast<const uint16_t*>(a[m] + mb.vc)[so[m]])
-                                         : 0.f;
+                                         : 1.f;
         }
         if (td == GP_TAG_FP8) {
           for (int dd = r0; dd < D; dd += rpi) {
@@ -1922,21 +1951,46 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
           }
           continue;
         }
-        for (int dd = r0; dd < D; dd += rpi) {
-          uint32_t x[2];
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
+        // bf16 destination. fp8 tokens with a scale outside the fast range go element by
+        // element the exact way; otherwise each row reads the 32-bit LDS word holding each
+        // token's element (a bf16 half, an fp8 byte or an INT4 nibble's byte), takes the
+        // element as a float times its scale (bf16 bits are kept as they are) and rounds the two
+        // tokens with one packed conversion
+        const bool slow = (tg[0] == GP_TAG_FP8 && !fp8_scale_fast(sc[0])) ||
+                          (tg[1] == GP_TAG_FP8 && !fp8_scale_fast(sc[1]));
+        if (__builtin_expect(slow, 0)) {
+#pragma unroll 1
+          for (int e = 0; e < 2 * (D / rpi); ++e) {
+            const int m = e & 1, dd = r0 + (e >> 1) * rpi;
+            uint32_t x;
             if (tg[m] == GP_TAG_BF16) {
-              x[m] = reinterpret_cast<const uint16_t*>(a[m])[dd * b + so[m]];
+              x = reinterpret_cast<const uint16_t*>(a[m])[dd * b + so[m]];
             } else if (tg[m] == GP_TAG_FP8) {
-              x[m] = fp8_times(a[m][dd * b + so[m]], sc[m]);
+              x = fp8_times(a[m][dd * b + so[m]], sc[m]);
             } else {
               const int sl = (dd % 16) * vslot + dd / 16;
-              const uint32_t byte = a[m][((so[m] >> 2) * D + sl) * 2 + ((so[m] & 3) >> 1)];
-              x[m] = int4_times(nib(byte, so[m] & 1), sc[m]);
+              x = int4_times(nib(a[m][((so[m] >> 2) * D + sl) * 2 + ((so[m] & 3) >> 1)], so[m] & 1), sc[m]);
             }
+            reinterpret_cast<uint16_t*>(dv + dd * 2 * b)[2 * tp + m] = (uint16_t)x;
           }
-          reinterpret_cast<uint32_t*>(dv + dd * 2 * b)[tp] = x[0] | (x[1] << 16);
+          continue;
+        }
+        for (int dd = r0; dd < D; dd += rpi) {
+          const int sl = (dd % 16) * vslot + dd / 16;
+          uint32_t y[2];
+          float f[2];
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const int ad = tg[m] == GP_TAG_BF16 ? (dd * b + so[m]) * 2
+                           : (tg[m] == GP_TAG_FP8 ? dd * b + so[m] : ((so[m] >> 2) * D + sl) * 2 + ((so[m] & 3) >> 1));
+            y[m] = *reinterpret_cast<const uint32_t*>(a[m] + (ad & ~3)) >> ((ad & 3) * 8);
+            f[m] = tg[m] == GP_TAG_FP8 ? __builtin_amdgcn_cvt_pk_f32_fp8(y[m], false)[0]
+                                       : (float)nib(y[m], so[m] & 1);
+          }
+          const uint32_t cv = pair_to_bf16(f[0], sc[0], tg[0] == GP_TAG_FP8, f[1], sc[1], tg[1] == GP_TAG_FP8);
+          const uint32_t lo = tg[0] == GP_TAG_BF16 ? (y[0] & 0xffffu) : (cv & 0xffffu);
+          const uint32_t hi = tg[1] == GP_TAG_BF16 ? (y[1] << 16) : (cv & 0xffff0000u);
+          reinterpret_cast<uint32_t*>(dv + dd * 2 * b)[tp] = lo | hi;
         }
       }
     }
