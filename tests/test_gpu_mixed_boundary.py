@@ -158,6 +158,58 @@ def test_compact_mixed_matches_oracle(b, d, pattern, policy):
     check_decode(out, lse, ref, "bf16", f"decode after mixed compaction b={b} d={d} {pattern}")
 
 
+def _midpoint_scales(n_min=16, seed=5):
+    """fp32 scales s in [1, 2) whose float product 1.5 * s lands exactly on a bf16 midpoint
+    (low 16 bits 0x8000) while the exact product (28 significant bits, exact in float64) does
+    not: the products that a float-then-bf16 rounding gets wrong without the residual."""
+    rng = np.random.default_rng(seed)
+    cand = rng.uniform(1.0, 2.0, 4_000_000).astype(np.float32)
+    x = 1.5 * cand.astype(np.float64)
+    p = x.astype(np.float32)
+    hit = ((p.view(np.uint32) & 0xFFFF) == 0x8000) & (p.astype(np.float64) != x)
+    mids = cand[hit]
+    assert len(mids) >= n_min
+    return mids
+
+
+def test_compact_mixed_bf16_rounding_edges():
+    """Promotion to bf16 (GrowPage Sec. 3.3 over PASK App. B.2 fp8 pages): fp8 codes of +-1.5
+    times row scales whose float product sits on a bf16 midpoint that the exact product misses,
+    and rows with tiny (2^-100, 2^-88), huge (2^110) and subnormal scales. Every moved element
+    must equal the exact product rounded once, bit for bit against the oracle."""
+    b, d = 16, 128
+    wl = _case(b, d, "random", [5 * b, 9 * b, 4 * b + 5, 12 * b], seed=77)
+    rng = np.random.default_rng(11)
+    mids = _midpoint_scales()
+    specials = np.array([2.0 ** -100, 2.0 ** -88, 2.0 ** 110, 1e-40], dtype=np.float32)
+    fp8 = np.nonzero(npy(wl.page_tag) == F8)[0]
+    idx = torch.as_tensor(fp8, dtype=torch.long, device=DEV)
+    shape_k, shape_v = (len(fp8),) + tuple(wl.k8.shape[1:]), (len(fp8),) + tuple(wl.v8.shape[1:])
+    sign_k = rng.integers(0, 2, size=shape_k).astype(np.uint8) << 7
+    sign_v = rng.integers(0, 2, size=shape_v).astype(np.uint8) << 7
+    wl.k8.index_copy_(0, idx, torch.as_tensor(0x3C | sign_k, device=DEV))   # +-1.5 in E4M3
+    wl.v8.index_copy_(0, idx, torch.as_tensor(0x3C | sign_v, device=DEV))
+
+    def scales(shape):
+        s = rng.choice(mids, size=shape) * np.exp2(rng.integers(-6, 7, size=shape)).astype(np.float32)
+        special = rng.random(shape) < 0.1
+        s[special] = rng.choice(specials, size=int(special.sum()))
+        return torch.as_tensor(s.astype(np.float32), device=DEV)
+
+    wl.k_scale.index_copy_(0, idx, scales((len(fp8),) + tuple(wl.k_scale.shape[1:])))
+    wl.v_scale.index_copy_(0, idx, scales((len(fp8),) + tuple(wl.v_scale.shape[1:])))
+    build_state(wl)
+    a_s, a_l, ws, nc = run_score(wl)
+    st, mx = host_state(wl), host_mixed(wl)
+    dec, kept = run_compact(wl, a_s, a_l, ws, nc, policy=ob.POLICY_FORCE_COMPRESS)
+    dec_ref, kept_ref = _oracle_mixed(wl, st, mx, a_s, a_l, ws, nc, ob.POLICY_FORCE_COMPRESS)
+    promoted = int(((npy(wl.page_tag) == BF) & (mx["page_tag"] == BF)).sum())
+    say(f"[compact mixed rounding edges] midpoint scales={len(mids)} decisions={npy(dec).tolist()} "
+        f"bf16 pages after={promoted}")
+    compare_state(wl, st, dec, kept, dec_ref, kept_ref, nc)
+    compare_mixed(wl, mx)
+
+
 def test_shrink_mixed_matches_oracle():
     b = 16
     wl = _case(b, 64, "random", [70 * b, 66 * b, 64 * b + 3], seed=21)
