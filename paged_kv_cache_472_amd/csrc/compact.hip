@@ -113,6 +113,8 @@ struct CParams {
   int log_b, log_kq, log_vq, log_qpp;  // log2 of page size, 16-byte pieces per key row / value row / page
   int log_kpq;        // log2 of the 16-byte pieces of a key row one part owns
   int fuse_items;     // the selection appends the compaction items itself (one layer, uniform
+  int split_check;    // the page checks of the requests ran in page_check_kernel (chk holds them)
+  int32_t* chk;       // [R][2]: a page of the request is invalid or released; shared pages it writes
                       // cache); the allocator zeroes the item count before it
   double tau;
 };
@@ -188,6 +190,149 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_w, int* total) {
   return off + x - v;
 }
 
+// Request i of the call: validity, primary decision (Eq. 8 over layers and KV heads) and
+// compaction geometry. Its flags carry F_* bits and the eviction count E in bits 8 and up.
+struct ReqPlan {
+  Info inf;
+  int flags, ndest, Pn, r;
+};
+__device__ ReqPlan plan_request(const CParams& P, int i) {
+  const int b = P.page_size;
+  Info inf = {};
+  inf.mode = MODE_NONE;
+  const int nc = P.n_cand[i];
+  const int r = P.req_idx[i];
+  // the working-set counts depend on the request's position only: their loads go out with
+  // the first ones, eight (layer, head) pairs per step, every load before any use
+  long long dsum = 0;  // sum over layers and KV heads of K^S - K^L
+  bool bad_ws = false;
+  const int nlh = P.L * P.H_kv;
+  for (int base = 0; base < nlh; base += 8) {
+    int ks[8], kl[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int lh = min(base + u, nlh - 1), l = lh / P.H_kv, h = lh - l * P.H_kv;
+      const int32_t* w = P.ws_counts + (((size_t)l * P.R + i) * P.H_kv + h) * 2;
+      ks[u] = w[0];
+      kl[u] = w[1];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // no branch, so the loads stay ahead of their uses
+      const bool in = base + u < nlh;
+      bad_ws |= in && (ks[u] < 0 || kl[u] < 0);
+      dsum += in ? (long long)ks[u] - kl[u] : 0ll;
+    }
+  }
+  inf.n = (nc > 0 && nc <= P.C_max) ? nc : 0;
+  inf.r = r;
+  bool ok = r >= 0 && r < P.B && nc >= 0 && nc <= P.C_max;
+  int Pn = 0, ctx = 0;
+  if (ok) {
+    Pn = P.n_pages[r];
+    ctx = P.context_lens[r];
+    ok = Pn >= 1 && Pn <= P.max_pages && ctx >= 0 && (long)ctx <= (long)Pn * b;
+  }
+  int n = 0;
+  if (ok) {
+    n = ctx == 0 ? 0 : ((ctx + b - 1) / b - 1) * b;
+    ok = n == nc;
+  }
+  if (ok && n > 0 && bad_ws) ok = false;
+  int flags = 0, ndest = 0;
+  if (ok) {
+    flags |= F_VALID;
+    const int pol = P.policies ? P.policies[i] : P.policy;
+    const long long HN = (long long)P.L * P.H_kv * n;  // Delta = dsum / HN
+    bool want_grow, want_shrink = false;
+    if (pol == GP_POLICY_FORCE_COMPRESS) want_grow = false;
+    else if (pol == GP_POLICY_FORCE_GROW || n == 0) want_grow = true;
+    else {
+      const bool g = trend_exceeds(dsum, HN, P.tau);
+      want_grow = (pol == GP_POLICY_INVERSE) ? !g : g;
+      // GrowPage-Shrink (Eq. 13): Delta < -0.005 = -1/200, decided exactly
+      if (!want_grow && pol == GP_POLICY_SHRINK) want_shrink = dsum * 200 < -HN;
+    }
+    // a Shrink must leave a capacity of at least SHRINK_MIN_CAPACITY tokens
+    const bool shrink = want_shrink && Pn >= 2 && (long)(Pn - 1) * b >= SHRINK_MIN_CAPACITY;
+    if (want_grow) flags |= F_GROW;
+    if (shrink) flags |= F_SHRINK;
+    if (Pn < P.max_pages) flags |= F_SLOT;
+    if (n == 0) flags |= F_EMPTY;
+    const int R_n = ctx - n;
+    const int keep = shrink ? Pn - 2 : Pn - 1;  // pages of history plus recent tokens kept
+    const int K_t = min(n, max(0, keep * b - R_n));
+    const int E = n - K_t;
+    inf.P = Pn;
+    inf.ctx_old = ctx;
+    inf.K_t = K_t;
+    inf.R_n = R_n;
+    inf.E = E;
+    inf.ctx_new = K_t + R_n;
+    ndest = (inf.ctx_new + b - 1) / b;
+    inf.n_dest = ndest;
+    if (E > 0 && E <= P.max_evict) flags |= F_CHECK;  // may compact: check its pages
+    flags |= min(E, 65535) << 8;
+  }
+  ReqPlan out;
+  out.inf = inf;
+  out.flags = flags;
+  out.ndest = ndest;
+  out.Pn = Pn;
+  out.r = r;
+  return out;
+}
+
+// The page checks of phase B below for calls with many (request, page) pairs, one workgroup per
+// request: the random refcount and tag loads of all pairs would otherwise queue on the one
+// compute unit of the allocator. Writes the request's old block-table row, whether a page id is
+// invalid or a page released, and how many pages it writes are shared.
+constexpr int PC_THREADS = 256;
+__global__ __launch_bounds__(PC_THREADS) void page_check_kernel(CParams P) {
+  const int i = blockIdx.x, tid = threadIdx.x;
+  __shared__ int s_pl[3];
+  __shared__ int s_bad, s_cnt;
+  if (tid == 0) {
+    const ReqPlan pl = plan_request(P, i);
+    s_pl[0] = (pl.flags & F_CHECK) ? pl.Pn : 0;
+    s_pl[1] = pl.ndest;
+    s_pl[2] = pl.r;
+    s_bad = 0;
+    s_cnt = 0;
+  }
+  __syncthreads();
+  const int Pn = s_pl[0], ndest = s_pl[1], r = s_pl[2];
+  int bad = 0, cnt = 0;
+  for (int j0 = 0; j0 < Pn; j0 += 4 * PC_THREADS) {
+    int pg[4], rc[4], tg[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = min(j0 + u * PC_THREADS + tid, Pn - 1);
+      pg[u] = P.block_tables[(size_t)r * P.max_pages + j];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pc = (pg[u] >= 0 && pg[u] < P.num_pages) ? pg[u] : 0;
+      rc[u] = P.refcount[pc];
+      tg[u] = P.page_tag ? (int)P.page_tag[pc] : GP_TAG_BF16;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * PC_THREADS + tid;
+      if (j >= Pn) continue;
+      P.old_bt[(size_t)i * P.max_pages + j] = pg[u];
+      if (pg[u] < 0 || pg[u] >= P.num_pages || tg[u] == GP_TAG_RELEASE) bad = 1;
+      else if (j < ndest && rc[u] > 1) ++cnt;
+    }
+  }
+  if (bad) atomicOr(&s_bad, 1);
+  if (cnt) atomicAdd(&s_cnt, cnt);
+  __syncthreads();
+  if (tid == 0) {
+    P.chk[2 * i] = s_bad;
+    P.chk[2 * i + 1] = s_cnt;
+  }
+}
+
 __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
   const int tid = threadIdx.x;
   const int b = P.page_size, R = P.R;
@@ -209,81 +354,9 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
 
   // ---- A: per request (one thread each): validity, primary decision, compaction geometry
   for (int i = tid; i < R; i += DA_THREADS) {
-    Info inf = {};
-    inf.mode = MODE_NONE;
-    const int nc = P.n_cand[i];
-    const int r = P.req_idx[i];
-    // the working-set counts depend on the request's position only: their loads go out with
-    // the first ones, eight (layer, head) pairs per step, every load before any use
-    long long dsum = 0;  // sum over layers and KV heads of K^S - K^L
-    bool bad_ws = false;
-    const int nlh = P.L * P.H_kv;
-    for (int base = 0; base < nlh; base += 8) {
-      int ks[8], kl[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int lh = min(base + u, nlh - 1), l = lh / P.H_kv, h = lh - l * P.H_kv;
-        const int32_t* w = P.ws_counts + (((size_t)l * P.R + i) * P.H_kv + h) * 2;
-        ks[u] = w[0];
-        kl[u] = w[1];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {  // no branch, so the loads stay ahead of their uses
-        const bool in = base + u < nlh;
-        bad_ws |= in && (ks[u] < 0 || kl[u] < 0);
-        dsum += in ? (long long)ks[u] - kl[u] : 0ll;
-      }
-    }
-    inf.n = (nc > 0 && nc <= P.C_max) ? nc : 0;
-    inf.r = r;
-    bool ok = r >= 0 && r < P.B && nc >= 0 && nc <= P.C_max;
-    int Pn = 0, ctx = 0;
-    if (ok) {
-      Pn = P.n_pages[r];
-      ctx = P.context_lens[r];
-      ok = Pn >= 1 && Pn <= P.max_pages && ctx >= 0 && (long)ctx <= (long)Pn * b;
-    }
-    int n = 0;
-    if (ok) {
-      n = ctx == 0 ? 0 : ((ctx + b - 1) / b - 1) * b;
-      ok = n == nc;
-    }
-    if (ok && n > 0 && bad_ws) ok = false;
-    int flags = 0, ndest = 0;
-    if (ok) {
-      flags |= F_VALID;
-      const int pol = P.policies ? P.policies[i] : P.policy;
-      const long long HN = (long long)P.L * P.H_kv * n;  // Delta = dsum / HN
-      bool want_grow, want_shrink = false;
-      if (pol == GP_POLICY_FORCE_COMPRESS) want_grow = false;
-      else if (pol == GP_POLICY_FORCE_GROW || n == 0) want_grow = true;
-      else {
-        const bool g = trend_exceeds(dsum, HN, P.tau);
-        want_grow = (pol == GP_POLICY_INVERSE) ? !g : g;
-        // GrowPage-Shrink (Eq. 13): Delta < -0.005 = -1/200, decided exactly
-        if (!want_grow && pol == GP_POLICY_SHRINK) want_shrink = dsum * 200 < -HN;
-      }
-      // a Shrink must leave a capacity of at least SHRINK_MIN_CAPACITY tokens
-      const bool shrink = want_shrink && Pn >= 2 && (long)(Pn - 1) * b >= SHRINK_MIN_CAPACITY;
-      if (want_grow) flags |= F_GROW;
-      if (shrink) flags |= F_SHRINK;
-      if (Pn < P.max_pages) flags |= F_SLOT;
-      if (n == 0) flags |= F_EMPTY;
-      const int R_n = ctx - n;
-      const int keep = shrink ? Pn - 2 : Pn - 1;  // pages of history plus recent tokens kept
-      const int K_t = min(n, max(0, keep * b - R_n));
-      const int E = n - K_t;
-      inf.P = Pn;
-      inf.ctx_old = ctx;
-      inf.K_t = K_t;
-      inf.R_n = R_n;
-      inf.E = E;
-      inf.ctx_new = K_t + R_n;
-      ndest = (inf.ctx_new + b - 1) / b;
-      inf.n_dest = ndest;
-      if (E > 0 && E <= P.max_evict) flags |= F_CHECK;  // may compact: check its pages
-      flags |= min(E, 65535) << 8;
-    }
+    const ReqPlan pl = plan_request(P, i);
+    const int flags = pl.flags, ndest = pl.ndest, Pn = pl.Pn, r = pl.r;
+    const Info inf = pl.inf;
     if (i < DA_MAX_R) {
       s_flags[i] = flags;
       s_cnt[i] = 0;
@@ -297,6 +370,15 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
 
   // ---- B: every (request, page) pair of a request that may compact: all page ids valid,
   // count the shared ones among the pages it writes, keep a copy of the old block table row
+  // (done by page_check_kernel for calls with many pairs)
+  if (P.split_check) {
+    for (int i = tid; i < R; i += DA_THREADS) {
+      if (s_pn[i] > 0) {
+        if (P.chk[2 * i]) s_flags[i] |= F_BAD;
+        s_cnt[i] = P.chk[2 * i + 1];
+      }
+    }
+  }
   if (tid == 0) {
     int acc = 0;
     for (int i = 0; i < R; ++i) {
@@ -307,6 +389,7 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
   }
   __syncthreads();
   const int npairs = gp::uni(s_pref[R]);
+  const int npairs_b = P.split_check ? 0 : npairs;  // pairs phase B checks here
   // (request, page) pair f: the last i with s_pref[i] <= f, and the page's index in the request
   auto pair_of = [&](int f, int* j) {
     int lo = 0, hi = R;
@@ -320,11 +403,11 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
   // DA_PAIRS pairs per thread at a time, every block-table load of the batch issued before the
   // dependent refcount and tag loads, and those before any use (past npairs: the last pair again,
   // unused; an invalid page id reads page 0, unused)
-  for (int f0 = 0; f0 < npairs; f0 += DA_PAIRS * DA_THREADS) {
+  for (int f0 = 0; f0 < npairs_b; f0 += DA_PAIRS * DA_THREADS) {
     int iv[DA_PAIRS], jv[DA_PAIRS], pgv[DA_PAIRS], rcv[DA_PAIRS], tgv[DA_PAIRS];
 #pragma unroll
     for (int u = 0; u < DA_PAIRS; ++u) {
-      iv[u] = pair_of(min(f0 + u * DA_THREADS + tid, npairs - 1), &jv[u]);
+      iv[u] = pair_of(min(f0 + u * DA_THREADS + tid, npairs_b - 1), &jv[u]);
       pgv[u] = P.block_tables[(size_t)s_r[iv[u]] * P.max_pages + jv[u]];
     }
 #pragma unroll
@@ -335,7 +418,7 @@ __global__ __launch_bounds__(DA_THREADS) void decide_alloc_kernel(CParams P) {
     }
 #pragma unroll
     for (int u = 0; u < DA_PAIRS; ++u) {
-      if (f0 + u * DA_THREADS + tid >= npairs) continue;
+      if (f0 + u * DA_THREADS + tid >= npairs_b) continue;
       const int i = iv[u], j = jv[u], pg = pgv[u];
       P.old_bt[(size_t)i * P.max_pages + j] = pg;
       if (pg < 0 || pg >= P.num_pages) atomicOr(&s_flags[i], F_BAD);
@@ -2049,7 +2132,7 @@ namespace {
 // evicted lists, first changed pages and chunk work list; shared by the layers (used one layer
 // at a time, in stream order) the selection survivors and the chunk snapshots.
 struct WsLayout {
-  size_t info, old_bt, rel, new_tag, layer0, layer_bytes, ev, dp0, items, n_items, cand, snap, total;
+  size_t info, old_bt, rel, new_tag, chk, layer0, layer_bytes, ev, dp0, items, n_items, cand, snap, total;
 };
 
 // destination pages per compaction item: the call's shape decides, so that the workspace size
@@ -2078,6 +2161,8 @@ WsLayout ws_layout(int L, int R, int H_kv, int max_pages, int page_size, int C_m
   off += (size_t)R * max_pages * 4;
   w.new_tag = off;
   off += (size_t)R * max_pages * 4;
+  w.chk = off;
+  off += (size_t)R * 2 * 4;
   off = (off + 255) & ~(size_t)255;
   w.layer0 = off;
   w.ev = 0;
@@ -2204,6 +2289,9 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
   P.old_bt = reinterpret_cast<int32_t*>(ws + wl.old_bt);
   P.rel = reinterpret_cast<int32_t*>(ws + wl.rel);
   P.new_tag = reinterpret_cast<int32_t*>(ws + wl.new_tag);
+  P.chk = reinterpret_cast<int32_t*>(ws + wl.chk);
+  // many (request, page) pairs: their checks spread over one workgroup per request
+  P.split_check = (R >= 2 && (long)R * (C_max / b + 2) > 2 * DA_THREADS) ? 1 : 0;
   if (mixed) {
     P.page_tag = kv->page_tag;
     P.k8 = static_cast<uint8_t*>(kv->k8);
@@ -2237,6 +2325,10 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (phases & GP_PHASE_PLAN) {
     // one decision and allocation per request for all layers (Eq. 8 over layers and KV heads)
+    if (P.split_check) {
+      hipLaunchKernelGGL(page_check_kernel, dim3(R), dim3(PC_THREADS), 0, s, layer(0));
+      GP_CHECK_LAUNCH();
+    }
     hipLaunchKernelGGL(decide_alloc_kernel, dim3(1), dim3(DA_THREADS), 0, s, layer(0));
     GP_CHECK_LAUNCH();
     const dim3 gw(H_kv, R);
