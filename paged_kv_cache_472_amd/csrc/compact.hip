@@ -1533,8 +1533,9 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
 // supplies iff not all of its b tokens are evicted. One thread per destination page; the heads'
 // thresholds ev[k] - k sit in LDS, up to PLAN_HEADS heads at a time.
 constexpr int PLAN_HEADS = 64;
-__global__ __launch_bounds__(256) void mixed_plan_kernel(CParams P) {
-  const int i = blockIdx.x;
+constexpr int PLAN_THREADS = 256;  // destination pages per workgroup (grid: page blocks x requests)
+__global__ __launch_bounds__(PLAN_THREADS) void mixed_plan_kernel(CParams P) {
+  const int i = blockIdx.y;
   const Info inf = info_of(P, i);
   if (inf.mode != MODE_COMPACT) return;
   const int lb = P.log_b, b = 1 << lb, H = P.H_kv, E = inf.E;
@@ -1546,59 +1547,71 @@ __global__ __launch_bounds__(256) void mixed_plan_kernel(CParams P) {
     s_dpm = m;
   }
   __syncthreads();
+  // (a workgroup of another block may already have lowered some heads' dp0 to this minimum:
+  // the minimum is the same)
   const int dpm = gp::uni(s_dpm);
-  for (int h = threadIdx.x; h < H; h += blockDim.x) P.dp0[(size_t)i * H + h] = dpm;
-  for (int base = dpm; base < inf.n_dest; base += blockDim.x) {
-    const int dp = base + (int)threadIdx.x;
-    const int j0 = dp << lb, j1 = j0 + b - 1;
-    uint32_t supply = 0;
-    for (int h0 = 0; h0 < H; h0 += PLAN_HEADS) {
-      const int nh = min(PLAN_HEADS, H - h0);
-      __syncthreads();  // the previous heads' thresholds are no longer read
-      for (int e = threadIdx.x; e < nh * MAX_EVICT; e += blockDim.x) {
-        const int hh = e / MAX_EVICT, k = e % MAX_EVICT;
-        s_thr[hh][k] = k < E ? P.ev[((size_t)i * H + h0 + hh) * P.max_evict + k] - k : INT_MAX;
+  if (blockIdx.x == 0)
+    for (int h = threadIdx.x; h < H; h += blockDim.x) P.dp0[(size_t)i * H + h] = dpm;
+  const int base = dpm + (int)blockIdx.x * PLAN_THREADS;
+  if (base >= inf.n_dest) return;
+  const int dp = base + (int)threadIdx.x;
+  const bool mine = dp < inf.n_dest;
+  // the tags of the three old pages that can supply page dp, fetched first
+  int tag3[3];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const int lp = min(dp + s, inf.P - 1);
+    tag3[s] = mine ? P.page_tag[P.old_bt[(size_t)i * P.max_pages + lp]] : GP_TAG_BF16;
+  }
+  const int j0 = dp << lb, j1 = j0 + b - 1;
+  uint32_t supply = 0;
+  for (int h0 = 0; h0 < H; h0 += PLAN_HEADS) {
+    const int nh = min(PLAN_HEADS, H - h0);
+    __syncthreads();  // the previous heads' thresholds are no longer read
+    for (int e = threadIdx.x; e < nh * MAX_EVICT; e += blockDim.x) {
+      const int hh = e / MAX_EVICT, k = e % MAX_EVICT;
+      s_thr[hh][k] = k < E ? P.ev[((size_t)i * H + h0 + hh) * P.max_evict + k] - k : INT_MAX;
+    }
+    __syncthreads();
+    if (!mine) continue;
+    for (int hh = 0; hh < nh; ++hh) {
+      const int4* th = reinterpret_cast<const int4*>(s_thr[hh]);
+      int c0 = 0, c1 = 0;
+#pragma unroll
+      for (int k = 0; k < MAX_EVICT / 4; ++k) {
+        const int4 t = th[k];
+        c0 += (t.x <= j0) + (t.y <= j0) + (t.z <= j0) + (t.w <= j0);
+        c1 += (t.x <= j1) + (t.y <= j1) + (t.z <= j1) + (t.w <= j1);
       }
-      __syncthreads();
-      if (dp >= inf.n_dest) continue;
-      for (int hh = 0; hh < nh; ++hh) {
-        const int4* th = reinterpret_cast<const int4*>(s_thr[hh]);
-        int c0 = 0, c1 = 0;
+      const int s_lo = ((j0 + c0) >> lb) - dp, s_hi = ((j1 + c1) >> lb) - dp;
+      supply |= 1u << s_lo;
+      supply |= 1u << s_hi;
+      for (int s = s_lo + 1; s < s_hi; ++s) {
+        // evictions inside old page dp + s: ev[k] = thr[k] + k in [lo, lo + b)
+        const int lo = (dp + s) << lb;
+        int ne = 0;
 #pragma unroll
         for (int k = 0; k < MAX_EVICT / 4; ++k) {
           const int4 t = th[k];
-          c0 += (t.x <= j0) + (t.y <= j0) + (t.z <= j0) + (t.w <= j0);
-          c1 += (t.x <= j1) + (t.y <= j1) + (t.z <= j1) + (t.w <= j1);
+          const int e0 = 4 * k;
+          ne += (t.x != INT_MAX && t.x + e0 >= lo && t.x + e0 < lo + b);
+          ne += (t.y != INT_MAX && t.y + e0 + 1 >= lo && t.y + e0 + 1 < lo + b);
+          ne += (t.z != INT_MAX && t.z + e0 + 2 >= lo && t.z + e0 + 2 < lo + b);
+          ne += (t.w != INT_MAX && t.w + e0 + 3 >= lo && t.w + e0 + 3 < lo + b);
         }
-        const int s_lo = ((j0 + c0) >> lb) - dp, s_hi = ((j1 + c1) >> lb) - dp;
-        supply |= 1u << s_lo;
-        supply |= 1u << s_hi;
-        for (int s = s_lo + 1; s < s_hi; ++s) {
-          // evictions inside old page dp + s: ev[k] = thr[k] + k in [lo, lo + b)
-          const int lo = (dp + s) << lb;
-          int ne = 0;
-#pragma unroll
-          for (int k = 0; k < MAX_EVICT / 4; ++k) {
-            const int4 t = th[k];
-            const int e0 = 4 * k;
-            ne += (t.x != INT_MAX && t.x + e0 >= lo && t.x + e0 < lo + b);
-            ne += (t.y != INT_MAX && t.y + e0 + 1 >= lo && t.y + e0 + 1 < lo + b);
-            ne += (t.z != INT_MAX && t.z + e0 + 2 >= lo && t.z + e0 + 2 < lo + b);
-            ne += (t.w != INT_MAX && t.w + e0 + 3 >= lo && t.w + e0 + 3 < lo + b);
-          }
-          if (ne < b) supply |= 1u << s;
-        }
+        if (ne < b) supply |= 1u << s;
       }
     }
-    if (dp >= inf.n_dest) continue;
-    int tag = -1;
-    for (int s = 0; s < 32; ++s) {
-      if (!(supply >> s & 1u)) continue;
-      const int t = P.page_tag[P.old_bt[(size_t)i * P.max_pages + dp + s]];
-      tag = (tag < 0 || tag == t) ? t : GP_TAG_BF16;
-    }
-    P.new_tag[(size_t)i * P.max_pages + dp] = tag;
   }
+  if (!mine) return;
+  // at most MAX_EVICT <= 2b evictions: a destination slot's source is at most two pages on
+  int tag = -1;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    if (!(supply >> s & 1u)) continue;
+    tag = (tag < 0 || tag == tag3[s]) ? tag3[s] : GP_TAG_BF16;
+  }
+  P.new_tag[(size_t)i * P.max_pages + dp] = tag;
 }
 
 // The destination tags, written once every page of the call has moved.
@@ -2354,7 +2367,8 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
       }
       GP_CHECK_LAUNCH();
       if (mixed) {  // destination tags; every head rewrites from the first changed page
-        hipLaunchKernelGGL(mixed_plan_kernel, dim3(R), dim3(256), 0, s, Q);
+        hipLaunchKernelGGL(mixed_plan_kernel, dim3((max_pages + PLAN_THREADS - 1) / PLAN_THREADS, R),
+                           dim3(PLAN_THREADS), 0, s, Q);
         GP_CHECK_LAUNCH();
       }
       if (!P.fuse_items) {
