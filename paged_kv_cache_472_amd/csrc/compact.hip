@@ -2041,6 +2041,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
                                          : 1.f;
         }
         if (td == GP_TAG_FP8) {
+          #pragma unroll 4
           for (int dd = r0; dd < D; dd += rpi) {
             const uint32_t x0 = a[0][dd * b + so[0]], x1 = a[1][dd * b + so[1]];
             reinterpret_cast<uint16_t*>(dv + dd * b)[tp] = (uint16_t)(x0 | (x1 << 8));
@@ -2071,22 +2072,49 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
           }
           continue;
         }
-        for (int dd = r0; dd < D; dd += rpi) {
-          const int sl = (dd % 16) * vslot + dd / 16;
-          uint32_t y[2];
-          float f[2];
+        // a token's element of row r0 + k rpi sits at va + k vk bytes of its slot (rpi is a
+        // multiple of 16, so the INT4 dimension slot steps by rpi / 16 as well); the address,
+        // the conversion and the result are picked by arithmetic selects, so the rows of a page
+        // carry no branch and their LDS reads go out together
+        int va[2], vk[2];
+        bool f8[2], bf[2];
 #pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            const int ad = tg[m] == GP_TAG_BF16 ? (dd * b + so[m]) * 2
-                           : (tg[m] == GP_TAG_FP8 ? dd * b + so[m] : ((so[m] >> 2) * D + sl) * 2 + ((so[m] & 3) >> 1));
-            y[m] = *reinterpret_cast<const uint32_t*>(a[m] + (ad & ~3)) >> ((ad & 3) * 8);
-            f[m] = tg[m] == GP_TAG_FP8 ? __builtin_amdgcn_cvt_pk_f32_fp8(y[m], false)[0]
-                                       : (float)nib(y[m], so[m] & 1);
+        for (int m = 0; m < 2; ++m) {
+          f8[m] = tg[m] == GP_TAG_FP8;
+          bf[m] = tg[m] == GP_TAG_BF16;
+          const int a_bf = (so[m] + b * r0) * 2, a_f8 = so[m] + b * r0;
+          const int a_i4 = ((so[m] >> 2) * D + (r0 % 16) * vslot + r0 / 16) * 2 + ((so[m] & 3) >> 1);
+          va[m] = bf[m] ? a_bf : (f8[m] ? a_f8 : a_i4);
+          vk[m] = bf[m] ? 2 * b * rpi : (f8[m] ? b * rpi : 2 * (rpi / 16));
+        }
+        const int nrow = D / rpi;  // 2, 4 or 8
+        for (int k0 = 0; k0 < nrow; k0 += 4) {
+          uint32_t y[4][2];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              const int ad = va[m] + min(k0 + k, nrow - 1) * vk[m];
+              y[k][m] = *reinterpret_cast<const uint32_t*>(a[m] + (ad & ~3)) >> ((ad & 3) * 8);
+            }
           }
-          const uint32_t cv = pair_to_bf16(f[0], sc[0], tg[0] == GP_TAG_FP8, f[1], sc[1], tg[1] == GP_TAG_FP8);
-          const uint32_t lo = tg[0] == GP_TAG_BF16 ? (y[0] & 0xffffu) : (cv & 0xffffu);
-          const uint32_t hi = tg[1] == GP_TAG_BF16 ? (y[1] << 16) : (cv & 0xffff0000u);
-          reinterpret_cast<uint32_t*>(dv + dd * 2 * b)[tp] = lo | hi;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if (k0 + k >= nrow) continue;
+            float f[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              const uint32_t u8 = __float_as_uint(__builtin_amdgcn_cvt_pk_f32_fp8(y[k][m], false)[0]);
+              const uint32_t u4 = __float_as_uint((float)nib(y[k][m], so[m] & 1));
+              const uint32_t msk = 0u - (uint32_t)f8[m];
+              f[m] = __uint_as_float((u8 & msk) | (u4 & ~msk));
+            }
+            const uint32_t cv = pair_to_bf16(f[0], sc[0], f8[0], f[1], sc[1], f8[1]);
+            const uint32_t m0 = 0u - (uint32_t)bf[0], m1 = 0u - (uint32_t)bf[1];
+            const uint32_t lo = ((y[k][0] & 0xffffu) & m0) | (cv & 0xffffu & ~m0);
+            const uint32_t hi = ((y[k][1] << 16) & m1) | (cv & 0xffff0000u & ~m1);
+            reinterpret_cast<uint32_t*>(dv + (r0 + (k0 + k) * rpi) * 2 * b)[tp] = lo | hi;
+          }
         }
       }
     }
