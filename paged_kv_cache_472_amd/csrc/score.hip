@@ -98,14 +98,17 @@ __device__ __forceinline__ int candidates(const ScoreParams& P, int i, int* r_ou
 // h G + c % G), RMS-calibrated to q_t (Eq. 12) and rotated to the current position, in float64,
 // into s_qt[c][0 .. D). One wave per row (a wave takes rows w, w + waves, ...).
 __device__ __forceinline__ void calibrated_rows(const ScoreParams& P, int i, int r, int h,
-                                                float (*s_qt)[128]) {
+                                                int slot, double pos, double inv_freq, float (*s_qt)[128]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nwv = blockDim.x >> 6;
   const int D = P.D, half = D / 2, G = P.G;
-  const int slot = P.slot_ids[r];
-  const double pos = (double)P.positions[r];
   // this wave's rows (at most CAL_ROWS of the 2G <= 16): every query and summary element they
   // need is loaded before any is used
+  // (one load form for both query dtypes, the 32-bit word holding the element: a dtype select
+  // per element made the compiler branch per load and wait for each load before the next)
   double qv[CAL_ROWS][2], sv[CAL_ROWS][2];
+  const bool qb = P.q_bf16 != 0;
+  const int qsh = qb ? 1 : 2;  // log2 of the query element size
+  const uint8_t* q8 = static_cast<const uint8_t*>(P.q);
 #pragma unroll
   for (int k = 0; k < CAL_ROWS; ++k) {
     const int c = w + k * nwv;
@@ -114,16 +117,16 @@ __device__ __forceinline__ void calibrated_rows(const ScoreParams& P, int i, int
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int d = min(lane + 64 * e, D - 1);
-      const size_t qi = ((size_t)r * P.H_q + g) * D + d;
-      qv[k][e] = P.q_bf16 ? (double)gp::bf16_bits_to_f32(static_cast<const uint16_t*>(P.q)[qi])
-                          : (double)static_cast<const float*>(P.q)[qi];
+      const size_t qbyte = (((size_t)r * P.H_q + g) * D + d) << qsh;
+      const uint32_t wq = *reinterpret_cast<const uint32_t*>(q8 + (qbyte & ~(size_t)3)) >> (8 * (qbyte & 3));
+      qv[k][e] = (double)(qb ? gp::bf16_bits_to_f32(wq & 0xffffu) : __uint_as_float(wq));
       sv[k][e] = (double)P.qstate[(((size_t)slot * 2 + x) * P.H_q + g) * D + d];
     }
   }
   // the rotation angle depends on the pair index only: lane l holds elements l and l + 64, and
   // both belong to pair l % (D/2), so one sine and cosine per lane serve every row
   double sn = 0.0, cs = 1.0;
-  if (P.rope_theta > 0.0) sincos(pos * P.inv_freq[lane % half], &sn, &cs);
+  if (P.rope_theta > 0.0) sincos(pos * inv_freq, &sn, &cs);
 #pragma unroll
   for (int k = 0; k < CAL_ROWS; ++k) {
     const int c = w + k * nwv;
@@ -208,7 +211,12 @@ __global__ __launch_bounds__(LG_MAX_THREADS) void logits_kernel(ScoreParams P) {
       for (int c = 0; c < NKW; ++c) kw[c] = kr[plain ? c : 0];
     }
   };
-  // the first two tiles' keys are in flight while the summaries are calibrated
+  // the request's state slot, position and this lane's rotation frequency first (the summary
+  // loads and the rotation wait for them, not for the key loads behind them), then the first
+  // two tiles' keys, in flight while the summaries are calibrated
+  const int slot = P.slot_ids[r];
+  const double pos = (double)P.positions[r];
+  const double inv_freq = P.inv_freq[lane % (D / 2)];
   u32x4_t ring[2][NKW];
   load_plain(0, ring[0]);
   load_plain(1, ring[1]);
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(LG_MAX_THREADS) void logits_kernel(ScoreParams P) {
   // a few hundred float64 operations, cheaper than a launch of their own,
   // and hidden behind the first key loads)
   __shared__ float s_qt[16][128];
-  calibrated_rows(P, i, r, h, s_qt);
+  calibrated_rows(P, i, r, h, slot, pos, inv_freq, s_qt);
   __syncthreads();
   // columns past 2G read the first summary row (no branch around the loads) and use zeros
   const float* qrow = s_qt[col_ok ? n16 : 0];
