@@ -1115,13 +1115,17 @@ __device__ __forceinline__ uint8_t* snap_ptr(const CParams& P, int i, int h, int
   return P.snap + (((((size_t)i * P.H_kv + h) * P.max_chunks + c) * MAX_SPAN + s) * 2 + which) *
                       page_bytes(P);
 }
-// does chunk c read logical page lp from the snapshot? Only the first `span` pages of the next
-// chunk, and only those that chunk rewrites (pages below n_dest): the workgroup of chunk c + 1
-// may have rewritten them by the time chunk c reads them. Pages of chunk c itself are read before
-// the same workgroup writes them.
-__device__ __forceinline__ bool from_snapshot(const CParams& P, int lp, int c, int n_dest) {
+// does chunk c read logical page lp from the snapshot? Only the first pages of the next chunk
+// that its sources reach, and only those that chunk rewrites (pages below n_dest): the workgroup
+// of chunk c + 1 may have rewritten them by the time chunk c reads them. Pages of chunk c itself
+// are read before the same workgroup writes them. A request evicting E tokens shifts a slot by at
+// most E, so its sources reach ceil(E / b) pages past a destination page (one for a Compress, two
+// for a Shrink; the call's span is the most any request may need): a page past those is never
+// used, whatever it holds when read.
+__device__ __forceinline__ bool from_snapshot(const CParams& P, int lp, int c, const Info& inf) {
   const int first = (c + 1) * P.chunk_pages;
-  return lp >= first && lp < first + P.span && lp < n_dest;
+  const int reach = min(P.span, (inf.E + (1 << P.log_b) - 1) >> P.log_b);
+  return lp >= first && lp < first + reach && lp < inf.n_dest;
 }
 
 // List of the (request, head, chunk, part) items that compaction rewrites: for a compacting head
@@ -1167,7 +1171,7 @@ __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
     const Info inf = info_of(P, i);
     for (int s = 0; s < P.span; ++s) {
       const int lp = (c + 1) * P.chunk_pages + s;
-      if (!from_snapshot(P, lp, c, inf.n_dest)) continue;  // uniform over the workgroup
+      if (!from_snapshot(P, lp, c, inf)) continue;  // uniform over the workgroup
       const int pg = P.old_bt[(size_t)i * P.max_pages + lp];
       const uint8_t* ks = P.k + pool_off(P, pg, h) + (size_t)part * kb;
       const uint8_t* vs = P.v + pool_off(P, pg, h) + (size_t)part * vb;
@@ -1246,7 +1250,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
     const int lp = dp_lo + threadIdx.x;
     long long ks = NO_SRC, vs = NO_SRC;
     if (lp < inf.P) {
-      if (from_snapshot(P, lp, c, inf.n_dest)) {
+      if (from_snapshot(P, lp, c, inf)) {
         ks = (long long)((intptr_t)snap_ptr(P, i, h, lp, 0) - (intptr_t)P.k);
         vs = (long long)((intptr_t)snap_ptr(P, i, h, lp, 1) - (intptr_t)P.v);
       } else {
@@ -1392,7 +1396,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
       const int lp = dp_lo + threadIdx.x;
       long long ks = NO_SRC, vs = NO_SRC;
       if (lp < inf.P) {
-        if (from_snapshot(P, lp, c, inf.n_dest)) {
+        if (from_snapshot(P, lp, c, inf)) {
           ks = (long long)((intptr_t)snap_ptr(P, i, h, lp, 0) - (intptr_t)P.k);
           vs = (long long)((intptr_t)snap_ptr(P, i, h, lp, 1) - (intptr_t)P.v);
         } else {
@@ -1708,7 +1712,7 @@ __global__ __launch_bounds__(CP_THREADS) void snapshot_mixed_kernel(CParams P) {
     const Info inf = info_of(P, i);
     for (int s = 0; s < P.span; ++s) {
       const int lp = (c + 1) * P.chunk_pages + s;
-      if (!from_snapshot(P, lp, c, inf.n_dest)) continue;
+      if (!from_snapshot(P, lp, c, inf)) continue;
       const int pg = P.old_bt[(size_t)i * P.max_pages + lp];
       const int tag = P.page_tag[pg];
       const MixedBytes mb = mixed_bytes(tag, P.page_size, P.D);
@@ -1844,7 +1848,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
         tag = P.page_tag[pg];
         const MixedBytes mb = mixed_bytes(tag, b, D);
         const uint8_t *pk, *pv, *pks, *pvs;
-        if (from_snapshot(P, lp, c, inf.n_dest)) {
+        if (from_snapshot(P, lp, c, inf)) {
           pk = snap_ptr(P, i, h, lp, 0);
           pv = snap_ptr(P, i, h, lp, 1);
           pks = pk + mb.kc;
