@@ -763,14 +763,15 @@ __device__ __forceinline__ void write_kept(int32_t* out, int p0, int p1, const i
   }
 }
 
-// Selection (Eq. 9-10) in three short launches over chunks of SEL_T pages (one page per
+// Selection (Eq. 9-10) in two short launches over chunks of SEL_T pages (one page per
 // thread, so the k_loc quota of a page is ranked in registers).
 //   select_local: per chunk, the E smallest eviction keys (s, ~index) of the chunk: each wave
 //                 finds its own E smallest with shuffles, then one wave picks the E smallest of
 //                 the 4 * E survivors.
-//   select_merge: per (request, KV head), the E smallest of all chunk survivors: the evicted
-//                 tokens, sorted by token index, and the first destination page that changes.
-//   select_write: per chunk, kept_idx: kept token t goes to position t - #(evicted < t).
+//   select_write: per chunk, first the E smallest of all of its head's chunk survivors (the
+//                 evicted tokens, sorted by token index; chunk 0 also records them and the first
+//                 destination page that changes), then kept_idx: kept token t goes to position
+//                 t - #(evicted < t).
 // Keys are unique, so the result is exactly the (s desc, index asc) order whatever the split.
 template <int PB>
 __global__ __launch_bounds__(SEL_T) void select_local_kernel(CParams P) {
@@ -832,12 +833,13 @@ __global__ __launch_bounds__(SEL_T) void select_local_kernel(CParams P) {
   }
 }
 
-__global__ __launch_bounds__(GP_WAVE) void select_merge_kernel(CParams P) {
-  const int h = blockIdx.x, i = blockIdx.y;
-  const Info inf = info_of(P, i);
-  if (inf.mode != MODE_COMPACT) return;
-  const int b = P.page_size, E = inf.E, lane = threadIdx.x;
-  const int nch = (inf.n + SEL_T * b - 1) / (SEL_T * b);
+// The E smallest eviction keys of a head over the survivors of its chunks (one wave), as the
+// evicted tokens sorted by index into s_ev[0 .. E) (INT_MAX past E)
+__device__ __forceinline__ void merge_evicted(const CParams& P, int i, int h, int n, int E, int lane,
+                                              unsigned long long* s_tmp, unsigned long long* s_best,
+                                              int* s_ev) {
+  const int b = P.page_size;
+  const int nch = (n + SEL_T * b - 1) / (SEL_T * b);
   const unsigned long long* src = P.cand + ((size_t)i * P.H_kv + h) * SEL_MAX_CHUNKS * MAX_EVICT;
   constexpr int PER = SEL_MAX_CHUNKS * MAX_EVICT / GP_WAVE;
   unsigned long long cv[PER];
@@ -846,28 +848,19 @@ __global__ __launch_bounds__(GP_WAVE) void select_merge_kernel(CParams P) {
     const int idx = lane + GP_WAVE * k;  // chunk idx / MAX_EVICT, rank idx % MAX_EVICT
     cv[k] = (idx / MAX_EVICT < nch && (idx % MAX_EVICT) < E) ? src[idx] : ~0ull;
   }
-  __shared__ unsigned long long s_tmp[GP_WAVE], s_best[MAX_EVICT];
   wave_smallest<PER>(cv, E, lane, s_tmp, s_best);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // lane e < E: the e-th evicted token (by key)
+  // lane e < E: the e-th evicted token (by key); its rank by index places it
   const int tok = lane < E ? (int)(0xffffffffu - (uint32_t)(s_best[lane] & 0xffffffffu)) : INT_MAX;
-  // sort the evicted tokens by index: rank of lane e's token among the E
   int rank = 0;
   for (int e = 0; e < E; ++e) {
     const int o = __shfl(tok, e, GP_WAVE);
     rank += o < tok ? 1 : 0;
   }
-  __shared__ int s_sorted[MAX_EVICT];
-  if (lane < E) s_sorted[rank] = tok;
-  __syncthreads();
-  if (lane < E) P.ev[((size_t)i * P.H_kv + h) * P.max_evict + lane] = s_sorted[lane];
-  if (lane == 0) {
-    const int dp0 = min(s_sorted[0] / b, inf.first_repl);
-    P.dp0[(size_t)i * P.H_kv + h] = dp0;
-    if (P.fuse_items) append_items(P, i, h, dp0, inf.n_dest);
-  }
+  if (lane < E) s_ev[rank] = tok;
+  else if (lane < MAX_EVICT) s_ev[lane] = INT_MAX;
 }
 
 template <int PB>
@@ -885,11 +878,24 @@ __global__ __launch_bounds__(SEL_T) void select_write_kernel(CParams P) {
     return;
   }
   const int E = inf.E;
+  // every chunk's workgroup merges the head's chunk survivors itself (a few hundred keys in one
+  // wave), which saves a launch between the local selection and this one; chunk 0's writes the
+  // evicted list, the first changed page and the compaction items
   __shared__ int s_ev[MAX_EVICT];
-  if (threadIdx.x < MAX_EVICT)
-    s_ev[threadIdx.x] = threadIdx.x < E ? P.ev[((size_t)i * P.H_kv + h) * P.max_evict + threadIdx.x] : INT_MAX;
+  __shared__ unsigned long long s_tmp[GP_WAVE], s_best[MAX_EVICT];
+  if (threadIdx.x < GP_WAVE) merge_evicted(P, i, h, n, E, threadIdx.x, s_tmp, s_best, s_ev);
   __syncthreads();
-  if (c == 0 && threadIdx.x < E) out[inf.K_t + threadIdx.x] = -1;
+  if (c == 0) {
+    if (threadIdx.x < E) {
+      P.ev[((size_t)i * P.H_kv + h) * P.max_evict + threadIdx.x] = s_ev[threadIdx.x];
+      out[inf.K_t + threadIdx.x] = -1;
+    }
+    if (threadIdx.x == 0) {
+      const int dp0 = min(s_ev[0] / b, inf.first_repl);
+      P.dp0[(size_t)i * P.H_kv + h] = dp0;
+      if (P.fuse_items) append_items(P, i, h, dp0, inf.n_dest);
+    }
+  }
   // this chunk's kept candidates: the output positions between those of its first candidate and
   // of the next chunk's
   const int ta = c * SEL_T * b, tb = min(n, ta + SEL_T * b);
@@ -2391,8 +2397,6 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
         const dim3 g(nch, H_kv, R);
         if (b == 16) hipLaunchKernelGGL(select_local_kernel<16>, g, dim3(SEL_T), 0, s, Q);
         else hipLaunchKernelGGL(select_local_kernel<32>, g, dim3(SEL_T), 0, s, Q);
-        GP_CHECK_LAUNCH();
-        hipLaunchKernelGGL(select_merge_kernel, gw, dim3(GP_WAVE), 0, s, Q);
         GP_CHECK_LAUNCH();
         if (b == 16) hipLaunchKernelGGL(select_write_kernel<16>, g, dim3(SEL_T), 0, s, Q);
         else hipLaunchKernelGGL(select_write_kernel<32>, g, dim3(SEL_T), 0, s, Q);
