@@ -78,6 +78,18 @@ struct ScoreParams {
   uint32_t p_fixed[5];  // p in units of 2^-149, little-endian 32-bit digits (rounded up)
 };
 
+// |C| of request r from its state slot and length (or -1 for an invalid request / slot, or
+// |C| > C_max)
+__device__ __forceinline__ int candidates_of(const ScoreParams& P, int r, int slot, int ctx) {
+  if (r < 0 || r >= P.B) return -1;
+  if (slot < 0 || slot >= P.num_slots) return -1;
+  if (ctx < 0 || (long)ctx > (long)P.max_pages * P.page_size) return -1;
+  if (ctx == 0) return 0;
+  const int used = (ctx + P.page_size - 1) / P.page_size;
+  const int n = (used - 1) * P.page_size;
+  return n > P.C_max ? -1 : n;
+}
+
 // |C| of request index i (or -1 for an invalid request / slot, or |C| > C_max)
 __device__ __forceinline__ int candidates(const ScoreParams& P, int i, int* r_out) {
   const int r = P.req_idx[i];
@@ -165,14 +177,28 @@ __global__ __launch_bounds__(LG_MAX_THREADS) void logits_kernel(ScoreParams P) {
   // heads vary fastest over the grid, so the KV heads of a page (adjacent in HBM) are read by
   // neighbouring workgroups at the same time
   const int h = blockIdx.x, chunk = blockIdx.y, i = blockIdx.z;
-  int r;
-  const int n = gp::uni(candidates(P, i, &r));
-  r = gp::uni(r);
-  if (h == 0 && chunk == 0 && threadIdx.x == 0) P.n_cand[i] = n;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nwv = blockDim.x >> 6;
   const int tile0 = chunk * CHUNK_TILES;
+  // Once the request index is known, every load that depends only on it goes out together: the
+  // state slot and length (which decide |C|), the position, this lane's rotation frequency and
+  // the page id of this lane's tile of the chunk (read before |C| is known, at an index kept
+  // inside the request's block-table row, and dropped below when past |C|)
+  const int r = gp::uni(P.req_idx[i]);
+  if (P.B <= 0) {  // no request is valid (and no row may be read)
+    if (h == 0 && chunk == 0 && threadIdx.x == 0) P.n_cand[i] = -1;
+    return;
+  }
+  const int rc = min(max(r, 0), P.B - 1);
+  const int slot = P.slot_ids[rc];
+  const int ctx = P.context_lens[rc];
+  const double pos = (double)P.positions[rc];
+  const double inv_freq = P.inv_freq[lane % (D / 2)];
+  const int pg_raw = P.block_tables[(size_t)rc * P.max_pages +
+                                    min(((tile0 + w + lane * nwv) << 4) / P.page_size, P.max_pages - 1)];
+  const int n = gp::uni(candidates_of(P, r, slot, ctx));
+  if (h == 0 && chunk == 0 && threadIdx.x == 0) P.n_cand[i] = n;
   if (n <= 0 || tile0 * 16 >= n) return;
   const int tile1 = min(n >> 4, tile0 + CHUNK_TILES);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nwv = blockDim.x >> 6;
   const int n16 = lane & 15, g4 = lane >> 4;
   const int G = P.G, b = P.page_size;
   const bool col_ok = n16 < 2 * G;
@@ -186,8 +212,7 @@ __global__ __launch_bounds__(LG_MAX_THREADS) void logits_kernel(ScoreParams P) {
   const int nt = tile1 > tile0 + w ? (tile1 - tile0 - w + nwv - 1) / nwv : 0;
   int pg_l = -1, tag_l = GP_TAG_BF16;
   if (lane < nt) {
-    const int tl = tile0 + w + lane * nwv;
-    const int pg = P.block_tables[(size_t)r * P.max_pages + (tl << 4) / b];
+    const int pg = pg_raw;
     bool ok = pg >= 0 && pg < P.num_pages;
     if (ok && P.page_tag) {
       tag_l = P.page_tag[pg];
@@ -211,12 +236,7 @@ __global__ __launch_bounds__(LG_MAX_THREADS) void logits_kernel(ScoreParams P) {
       for (int c = 0; c < NKW; ++c) kw[c] = kr[plain ? c : 0];
     }
   };
-  // the request's state slot, position and this lane's rotation frequency first (the summary
-  // loads and the rotation wait for them, not for the key loads behind them), then the first
-  // two tiles' keys, in flight while the summaries are calibrated
-  const int slot = P.slot_ids[r];
-  const double pos = (double)P.positions[r];
-  const double inv_freq = P.inv_freq[lane % (D / 2)];
+  // the first two tiles' keys are in flight while the summaries are calibrated
   u32x4_t ring[2][NKW];
   load_plain(0, ring[0]);
   load_plain(1, ring[1]);
