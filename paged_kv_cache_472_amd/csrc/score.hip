@@ -38,12 +38,13 @@ constexpr int CHUNK_TILES = 32;  // 512 candidate tokens per logits workgroup
 constexpr int WS_THREADS = 1024;
 constexpr int WS_VPT = 32;        // weights per thread held in registers (|C| <= 32768)
 constexpr int WS_MAX_C = WS_THREADS * WS_VPT;
-constexpr int WS_TAIL = 256;      // weights left in the search interval when one wave sorts them
-// First level of the threshold search: 1024 bins of a weight's bit pattern >> 20 (sign, exponent
-// and three mantissa bits: a weight <= 1 has a pattern below 2^30), each holding the bin's count
+constexpr int WS_TAIL = 64;       // weights left in the search interval when one wave sorts them
+constexpr int WS_TK = WS_TAIL / 64;  // tail keys per lane
+// First level of the threshold search: 4096 bins of a weight's bit pattern >> 18 (sign, exponent
+// and five mantissa bits: a weight <= 1 has a pattern below 2^30), each holding the bin's count
 // (bits 48..63) and mass in units of 2^-47 (bits 0..47: a distribution's total stays below 2).
-constexpr int WS_BIN_SHIFT = 20;
-constexpr int WS_BINS = 1024;
+constexpr int WS_BIN_SHIFT = 18;
+constexpr int WS_BINS = 4096;
 constexpr int WS_MASS_BITS = 47;
 // Relative rounding bound of a block's float64 sum of nonnegative weights: a thread adds its (at
 // most 32) weights in sequence, a wave reduces in 6 levels, the 16 wave partials in 4: at most 42
@@ -459,14 +460,14 @@ __device__ __forceinline__ int cmp_p(const uint32_t a[6], const uint32_t p[5]) {
   return 0;
 }
 
-// Bitonic sort, descending, of 256 keys held four per lane by one wave (key k * 64 + lane in
-// x[k]): partners 64 or 128 keys apart sit in this lane's own registers, nearer ones in other
+// Bitonic sort, descending, of 64 TK keys held TK per lane by one wave (key k * 64 + lane in
+// x[k]): partners 64 or more keys apart sit in this lane's own registers, nearer ones in other
 // lanes of the same register.
-template <int SIZE, int J>
-__device__ __forceinline__ void bitonic_step(uint32_t (&x)[4], int lane) {
+template <int SIZE, int J, int TK>
+__device__ __forceinline__ void bitonic_step(uint32_t (&x)[TK], int lane) {
   if constexpr (J >= GP_WAVE) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < TK; ++k) {
       if (k & (J / GP_WAVE)) continue;
       const int k2 = k | (J / GP_WAVE);
       const bool desc = ((k * GP_WAVE + lane) & SIZE) == 0;  // the same for k2 (J < SIZE)
@@ -476,7 +477,7 @@ __device__ __forceinline__ void bitonic_step(uint32_t (&x)[4], int lane) {
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < TK; ++k) {
       uint32_t hi, lo;
       gp::lane_pair_minmax<J>(x[k], hi, lo);
       const bool lower = (lane & J) == 0;
@@ -484,14 +485,13 @@ __device__ __forceinline__ void bitonic_step(uint32_t (&x)[4], int lane) {
       x[k] = lower == desc ? hi : lo;
     }
   }
-  if constexpr (J > 1) bitonic_step<SIZE, J / 2>(x, lane);
+  if constexpr (J > 1) bitonic_step<SIZE, J / 2, TK>(x, lane);
 }
-template <int SIZE>
-__device__ __forceinline__ void bitonic_sort_desc(uint32_t (&x)[4], int lane) {
-  if constexpr (SIZE > 2) bitonic_sort_desc<SIZE / 2>(x, lane);
-  bitonic_step<SIZE, SIZE / 2>(x, lane);
+template <int SIZE, int TK>
+__device__ __forceinline__ void bitonic_sort_desc(uint32_t (&x)[TK], int lane) {
+  if constexpr (SIZE > 2) bitonic_sort_desc<SIZE / 2, TK>(x, lane);
+  bitonic_step<SIZE, SIZE / 2, TK>(x, lane);
 }
-
 constexpr int WS_WAVES = WS_THREADS / GP_WAVE;
 static_assert(WS_WAVES <= 16, "block reductions hand one partial per wave to the 16 lanes of a DPP row");
 
@@ -518,12 +518,14 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   __shared__ uint64_t s_u[2][8][WS_WAVES];
   __shared__ uint32_t s_x[2][WS_WAVES];
   int ph = 0;
-  static_assert(WS_BINS == WS_THREADS, "one histogram bin per thread");
+  constexpr int BPT = WS_BINS / WS_THREADS;  // histogram bins per thread
+  static_assert(BPT * WS_THREADS == WS_BINS, "whole bins per thread");
   __shared__ unsigned long long s_hist[WS_BINS];
   __shared__ int s_bin;
   __shared__ unsigned long long s_bin_incl, s_bin_excl;
   __shared__ unsigned long long s_wtot[WS_WAVES];
-  s_hist[threadIdx.x] = 0ull;
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) s_hist[k * WS_THREADS + threadIdx.x] = 0ull;
   if (threadIdx.x == 0) s_bin = -1;
   // a float64 sum and an integer count in one barrier
   auto sum_dc = [&](double v, uint32_t c, uint32_t* c_out) -> double {
@@ -722,22 +724,33 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   double m_hi = 0.0;                 // mass of the weights >= hi
   {
     // first level: the bin where the mass counted from the top reaches p (a prefix sum over the
-    // bins from the largest down; thread t holds bin 1023 - t). Rounding may leave p just past
-    // the total, and then the bisection starts from the whole range.
+    // bins from the largest down; thread t holds bins 4095 - 4t - k, k < 4, in that order).
+    // Rounding may leave p just past the total, and then the bisection starts from the whole range.
     const uint64_t MASK = (1ull << 48) - 1ull;
     const uint64_t p_fx = (uint64_t)ldexp(p_f64, WS_MASS_BITS);
-    const int bin = WS_BINS - 1 - (int)threadIdx.x;
-    const uint64_t v = s_hist[bin];
-    const uint64_t sc = gp::wave_scan_u64(v);
+    const int bin0 = WS_BINS - 1 - BPT * (int)threadIdx.x;
+    uint64_t v[BPT], cum[BPT];
+    uint64_t tsum = 0ull;
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      v[k] = s_hist[bin0 - k];
+      tsum += v[k];
+      cum[k] = tsum;  // inclusive, inside the thread
+    }
+    const uint64_t sc = gp::wave_scan_u64(tsum);
     if (lane == 63) s_wtot[w] = sc;
     __syncthreads();
     uint64_t pre = 0ull;
     for (int k = 0; k < w; ++k) pre += s_wtot[k];
-    const uint64_t incl = pre + sc, excl = incl - v;
-    if ((excl & MASK) < p_fx && (incl & MASK) >= p_fx) {
-      s_bin = bin;
-      s_bin_incl = incl;
-      s_bin_excl = excl;
+    pre += sc - tsum;  // before this thread's first bin
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const uint64_t incl = pre + cum[k], excl = incl - v[k];
+      if ((excl & MASK) < p_fx && (incl & MASK) >= p_fx) {
+        s_bin = bin0 - k;
+        s_bin_incl = incl;
+        s_bin_excl = excl;
+      }
     }
     __syncthreads();
     const int b0 = gp::uni(s_bin);
@@ -773,7 +786,7 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   if (hi - lo > 1u) {
     // at most WS_TAIL weights in [lo, hi): list them; one wave sorts the list (descending) and
     // takes the first weight at which the running mass, from the mass at or above hi, reaches p
-    static_assert(WS_TAIL == 4 * GP_WAVE, "the tail sort holds four keys per lane");
+    static_assert(WS_TAIL == WS_TK * GP_WAVE, "the tail sort holds WS_TK keys per lane");
     __shared__ uint32_t s_tail[WS_TAIL];
     __shared__ uint32_t s_ntail, s_lo;
     if (threadIdx.x == 0) s_ntail = 0u;
@@ -792,19 +805,19 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
     __syncthreads();
     if (w == 0) {
       const uint32_t nt = min(s_ntail, (uint32_t)WS_TAIL);  // == c_lo - c_hi <= WS_TAIL
-      uint32_t xs[4];
+      uint32_t xs[WS_TK];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < WS_TK; ++k) {
         const uint32_t idx = lane + GP_WAVE * k;
         xs[k] = idx < nt ? s_tail[idx] : 0u;  // empty places sort last
       }
-      bitonic_sort_desc<WS_TAIL>(xs, lane);
+      bitonic_sort_desc<WS_TAIL, WS_TK>(xs, lane);
       // inclusive running mass in sorted order; no crossing (rounding) keeps lo
       double run = m_hi;
       uint32_t found = lo;
       bool hit_any = false;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < WS_TK; ++k) {
         const double c = run + gp::wave_scan_f64((double)__uint_as_float(xs[k]));
         const uint64_t hit = __builtin_amdgcn_ballot_w64(xs[k] != 0u && c >= p_f64);
         if (!hit_any && hit != 0ull) {
