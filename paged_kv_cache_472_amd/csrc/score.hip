@@ -91,20 +91,6 @@ __device__ __forceinline__ int candidates_of(const ScoreParams& P, int r, int sl
   return n > P.C_max ? -1 : n;
 }
 
-// |C| of request index i (or -1 for an invalid request / slot, or |C| > C_max)
-__device__ __forceinline__ int candidates(const ScoreParams& P, int i, int* r_out) {
-  const int r = P.req_idx[i];
-  *r_out = r;
-  if (r < 0 || r >= P.B) return -1;
-  const int slot = P.slot_ids[r];
-  if (slot < 0 || slot >= P.num_slots) return -1;
-  const int ctx = P.context_lens[r];
-  if (ctx < 0 || (long)ctx > (long)P.max_pages * P.page_size) return -1;
-  if (ctx == 0) return 0;
-  const int used = (ctx + P.page_size - 1) / P.page_size;
-  const int n = (used - 1) * P.page_size;
-  return n > P.C_max ? -1 : n;
-}
 
 // ------------------------------------------------------------------------------ 1. calibration
 // The 2G summary rows of KV head h of boundary request i (row c = view c / G, query head
@@ -498,15 +484,41 @@ static_assert(WS_WAVES <= 16, "block reductions hand one partial per wave to the
 __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) {
   const int row = blockIdx.x, i = blockIdx.y;
   const int h = row >> 1, x = row & 1;
-  int r;
-  const int n = gp::uni(candidates(P, i, &r));
-  r = gp::uni(r);
   int32_t* out = P.ws_counts + ((size_t)i * P.H_kv + h) * 2 + x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int G = P.G;
+  // Once the request index is known, the loads that depend only on it go out together: the
+  // state slot and length (which decide |C|), the first batch of logits (four per thread and
+  // query head, at indices kept inside the row) and each query head's per-chunk (max, sum)
+  // pairs (every chunk slot of the row); what lies past |C| is dropped once |C| is known.
+  const int r = gp::uni(P.req_idx[i]);
+  if (P.B <= 0) {  // no request is valid (and no row may be read)
+    if (threadIdx.x == 0) *out = -1;
+    return;
+  }
+  const int rc = min(max(r, 0), P.B - 1);
+  const int slot = P.slot_ids[rc];
+  const int ctx = P.context_lens[rc];
+  const float* lg0 = P.logits + (((size_t)i * 2 + x) * P.H_q + h * G) * P.C_max;
+  float z0[8][4];
+#pragma unroll
+  for (int g = 0; g < 8; ++g)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = min((int)threadIdx.x + j * WS_THREADS, P.C_max - 1);
+      z0[g][j] = g < G ? lg0[(size_t)g * P.C_max + t] : 0.f;
+    }
+  float mj_raw = -INFINITY, lj_raw = 0.f;
+  if (w < G && lane < P.nch) {
+    const float* st = P.stats + (((size_t)i * 2 + x) * P.H_q + h * G + w) * P.nch * 2;
+    mj_raw = st[2 * lane];
+    lj_raw = st[2 * lane + 1];
+  }
+  const int n = gp::uni(candidates_of(P, r, slot, ctx));
   if (n <= 0) {
     if (threadIdx.x == 0) *out = n < 0 ? -1 : 0;
     return;
   }
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   constexpr int NT = WS_THREADS;
   // weights per thread that can be candidates: the rest of a thread's 32 slots hold zeros, which
   // no sum, count or maximum below depends on, so the loops skip them (a uniform bound)
@@ -587,11 +599,8 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
   // ---- this row's weights (GrowPage Sec. 3.2): the softmax over C of each of the G query heads
   // of KV head h in view x, from the logits and the per-chunk (max, sum) pairs the logits
   // kernel left, then their mean; written to a^x and kept in registers for the search
-  const int G = P.G;
-  // the logits of the first batch of four weights per thread (every query head) are loaded before
-  // the per-chunk statistics are merged, so the two loads overlap; indexes past the candidates
-  // read candidate 0 (no branch per element) and are dropped below
-  const float* lg0 = P.logits + (((size_t)i * 2 + x) * P.H_q + h * G) * P.C_max;
+  // later batches: indexes past the candidates read candidate 0 (no branch per element) and are
+  // dropped below
   auto load_batch = [&](int j0, float (&z)[8][4]) {
 #pragma unroll
     for (int g = 0; g < 8; ++g)
@@ -601,16 +610,15 @@ __global__ __launch_bounds__(WS_THREADS) void working_set_kernel(ScoreParams P) 
         z[g][j] = (g < G && j0 + j < nv) ? lg0[(size_t)g * P.C_max + (t < n ? t : 0)] : 0.f;
       }
   };
-  float z0[8][4];
-  load_batch(0, z0);
   __shared__ float s_m[16], s_inv[16];
   {
     // one wave per query head: lane j holds chunk j's (max, sum)
     const int nchunks = (n + CHUNK_TILES * 16 - 1) / (CHUNK_TILES * 16);  // <= 64
-    for (int g = w; g < G; g += WS_WAVES) {
-      const float* st = P.stats + (((size_t)i * 2 + x) * P.H_q + h * G + g) * P.nch * 2;
-      const float mj = lane < nchunks ? st[2 * lane] : -INFINITY;
-      const float lj = lane < nchunks ? st[2 * lane + 1] : 0.f;
+    static_assert(WS_WAVES >= 8, "one wave per query head (G <= 8)");
+    if (w < G) {
+      const int g = w;
+      const float mj = lane < nchunks ? mj_raw : -INFINITY;
+      const float lj = lane < nchunks ? lj_raw : 0.f;
       const float m = gp::wave_max(mj);
       const float l = gp::wave_sum(lj * gp::safe_exp2_diff(mj, m));
       if (lane == 0) {
