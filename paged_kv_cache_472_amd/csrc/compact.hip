@@ -918,6 +918,17 @@ __global__ __launch_bounds__(SEL_T) void select_fused_kernel(CParams P) {
   constexpr int NW = SEL_T / GP_WAVE;
   const int h = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
+  const float* as = P.a_short + ((size_t)i * P.H_kv + h) * P.C_max;
+  const float* al = P.a_long + ((size_t)i * P.H_kv + h) * P.C_max;
+  // the first chunk's scores go out with the request's plan (their addresses do not depend on
+  // it; indexes are kept inside the row and pages past |C| are dropped below)
+  f32x4_t x0[b / 4], y0[b / 4];
+#pragma unroll
+  for (int j = 0; j < b; j += 4) {
+    const int t = min(tid * b + j, P.C_max - 4);
+    x0[j / 4] = *reinterpret_cast<const f32x4_t*>(as + t);
+    y0[j / 4] = *reinterpret_cast<const f32x4_t*>(al + t);
+  }
   const Info inf = info_of(P, i);
   const int n = inf.n;
   int32_t* out = P.kept_idx + ((size_t)i * P.H_kv + h) * P.C_max;
@@ -928,8 +939,6 @@ __global__ __launch_bounds__(SEL_T) void select_fused_kernel(CParams P) {
   const int K_t = inf.K_t, E = inf.E;
   const int kloc = min(P.k_loc, b);
   const bool pool_all = (long)(n / b) * kloc >= K_t;  // |S_loc| >= K_t: the K_t best of all of C
-  const float* as = P.a_short + ((size_t)i * P.H_kv + h) * P.C_max;
-  const float* al = P.a_long + ((size_t)i * P.H_kv + h) * P.C_max;
   const int nch = (n + SEL_T * b - 1) / (SEL_T * b);
   __shared__ unsigned long long s_cand[NW * MAX_EVICT];
   __shared__ unsigned long long s_best[MAX_EVICT];
@@ -942,8 +951,13 @@ __global__ __launch_bounds__(SEL_T) void select_fused_kernel(CParams P) {
     for (int j = 0; j < b; j += 4) {
       f32x4_t x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
       if (t0 < n) {  // pages are whole: t0 < n covers all b candidates
-        x = *reinterpret_cast<const f32x4_t*>(as + t0 + j);
-        y = *reinterpret_cast<const f32x4_t*>(al + t0 + j);
+        if (c == 0) {
+          x = x0[j / 4];
+          y = y0[j / 4];
+        } else {
+          x = *reinterpret_cast<const f32x4_t*>(as + t0 + j);
+          y = *reinterpret_cast<const f32x4_t*>(al + t0 + j);
+        }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
