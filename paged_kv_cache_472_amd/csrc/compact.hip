@@ -101,7 +101,8 @@ struct CParams {
   int32_t* ev;        // [R, H_kv, max_evict]
   int32_t* dp0;       // [R, H_kv]
   unsigned long long* cand;  // [R, H_kv, SEL_MAX_CHUNKS, MAX_EVICT] chunk survivors
-  int2* items;               // [R * H_kv * max_chunks * npart] (request * H_kv + head, chunk * npart + part)
+  int4* items;               // [R * H_kv * max_chunks * npart] (request * H_kv + head, chunk * npart + part,
+                             //  request row r, the head's first changed page dp0)
   int32_t* n_items;          // [1]
   uint8_t* snap;      // [R, H_kv, max_chunks, MAX_SPAN, 2, page bytes]
   int R, B, H_kv, D, page_size, num_pages, max_pages, C_max, k_loc, policy, es;
@@ -138,9 +139,9 @@ __device__ __forceinline__ Info info_of(const CParams& P, int i) {
   u.pad = 0;
   return u;
 }
-__device__ __forceinline__ int2 item_of(const CParams& P, int k) {
-  const int2 v = P.items[k];
-  return make_int2(gp::uni(v.x), gp::uni(v.y));
+__device__ __forceinline__ int4 item_of(const CParams& P, int k) {
+  const int4 v = P.items[k];
+  return make_int4(gp::uni(v.x), gp::uni(v.y), gp::uni(v.z), gp::uni(v.w));
 }
 
 // grow iff D / (H n) > tau, decided exactly (D integer, tau a double)
@@ -733,13 +734,13 @@ __device__ __forceinline__ void wave_smallest(const unsigned long long (&key)[K]
 // holding its first changed page dp0 to the one holding its last destination page, each with every
 // part of the head dimension. The order of the list does not matter (items never share bytes, and
 // the pages a chunk reads from the next one are saved before any item runs).
-__device__ __forceinline__ void append_items(const CParams& P, int i, int h, int dp0, int n_dest) {
+__device__ __forceinline__ void append_items(const CParams& P, int i, int h, int r, int dp0, int n_dest) {
   const int L = P.chunk_pages;
   if (dp0 >= n_dest) return;
   const int c0 = dp0 / L * P.npart;
   const int cnt = ((n_dest + L - 1) / L - dp0 / L) * P.npart;
   const int off = atomicAdd(P.n_items, cnt);
-  for (int k = 0; k < cnt; ++k) P.items[off + k] = make_int2(i * P.H_kv + h, c0 + k);
+  for (int k = 0; k < cnt; ++k) P.items[off + k] = make_int4(i * P.H_kv + h, c0 + k, r, dp0);
 }
 
 // kept_idx over the output positions [p0, p1), written by consecutive threads: position p holds
@@ -893,7 +894,7 @@ __global__ __launch_bounds__(SEL_T) void select_write_kernel(CParams P) {
     if (threadIdx.x == 0) {
       const int dp0 = min(s_ev[0] / b, inf.first_repl);
       P.dp0[(size_t)i * P.H_kv + h] = dp0;
-      if (P.fuse_items) append_items(P, i, h, dp0, inf.n_dest);
+      if (P.fuse_items) append_items(P, i, h, inf.r, dp0, inf.n_dest);
     }
   }
   // this chunk's kept candidates: the output positions between those of its first candidate and
@@ -1009,7 +1010,7 @@ __global__ __launch_bounds__(SEL_T) void select_fused_kernel(CParams P) {
   const int dp0 = min(s_ev[0] / b, inf.first_repl);
   if (tid == 0) {
     P.dp0[(size_t)i * P.H_kv + h] = dp0;
-    if (P.fuse_items) append_items(P, i, h, dp0, inf.n_dest);
+    if (P.fuse_items) append_items(P, i, h, inf.r, dp0, inf.n_dest);
   }
   // kept_idx: the K_t kept candidates in order
   write_kept(out, 0, K_t, s_ev, E, tid, SEL_T);
@@ -1111,7 +1112,7 @@ __global__ __launch_bounds__(WIDE_T) void select_wide_kernel(CParams P) {
     if (ex == 0) {
       const int dp0 = min((t0 + __ffs(evm) - 1) / b, inf.first_repl);
       P.dp0[(size_t)i * P.H_kv + h] = dp0;
-      if (P.fuse_items) append_items(P, i, h, dp0, inf.n_dest);
+      if (P.fuse_items) append_items(P, i, h, inf.r, dp0, inf.n_dest);
     }
   }
   if (live) {
@@ -1157,11 +1158,12 @@ __global__ __launch_bounds__(DA_THREADS) void chunk_list_kernel(CParams P) {
   int carry = 0;
   for (int base = 0; base < n; base += DA_THREADS) {
     const int ih = base + threadIdx.x;
-    int c0 = 0, cnt = 0;
+    int c0 = 0, cnt = 0, r = 0, dp0 = 0;
     if (ih < n) {
       const Info inf = P.info[ih / P.H_kv];
       if (inf.mode == MODE_COMPACT) {
-        const int dp0 = P.dp0[ih];
+        r = inf.r;
+        dp0 = P.dp0[ih];
         if (dp0 < inf.n_dest) {
           c0 = dp0 / L * P.npart;
           cnt = ((inf.n_dest + L - 1) / L - dp0 / L) * P.npart;
@@ -1170,7 +1172,7 @@ __global__ __launch_bounds__(DA_THREADS) void chunk_list_kernel(CParams P) {
     }
     int total;
     const int off = carry + block_excl_scan(cnt, s_w, &total);
-    for (int k = 0; k < cnt; ++k) P.items[off + k] = make_int2(ih, c0 + k);  // chunk * npart + part
+    for (int k = 0; k < cnt; ++k) P.items[off + k] = make_int4(ih, c0 + k, r, dp0);  // chunk * npart + part
     carry += total;
   }
   if (threadIdx.x == 0) *P.n_items = carry;
@@ -1185,14 +1187,20 @@ __global__ __launch_bounds__(CP_THREADS) void snapshot_kernel(CParams P) {
   const size_t vb = page_bytes(P) / P.npart;           // value bytes of the part (contiguous rows)
   const int lkpq = P.log_kpq, nkq = P.page_size << lkpq;
   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-    const int2 item = item_of(P, it);
+    const int4 item = item_of(P, it);
     const int i = item.x / P.H_kv, h = item.x % P.H_kv;
     const int c = item.y / P.npart, part = item.y % P.npart;
+    // the old block-table entries of the next chunk's first pages load with the request's record
+    // (indexes kept inside the row; pages the snapshot skips are dropped)
+    int pgs[MAX_SPAN];
+#pragma unroll
+    for (int s = 0; s < MAX_SPAN; ++s)
+      pgs[s] = P.old_bt[(size_t)i * P.max_pages + min((c + 1) * P.chunk_pages + s, P.max_pages - 1)];
     const Info inf = info_of(P, i);
     for (int s = 0; s < P.span; ++s) {
       const int lp = (c + 1) * P.chunk_pages + s;
       if (!from_snapshot(P, lp, c, inf)) continue;  // uniform over the workgroup
-      const int pg = P.old_bt[(size_t)i * P.max_pages + lp];
+      const int pg = gp::uni(s == 0 ? pgs[0] : pgs[MAX_SPAN - 1]);
       const uint8_t* ks = P.k + pool_off(P, pg, h) + (size_t)part * kb;
       const uint8_t* vs = P.v + pool_off(P, pg, h) + (size_t)part * vb;
       uint8_t* kd = snap_ptr(P, i, h, lp, 0) + (size_t)part * kb;
@@ -1243,13 +1251,22 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   const int n_items = gp::uni(*P.n_items);
   for (int item_k = blockIdx.x; item_k < n_items; item_k += gridDim.x) {
   lds_barrier();  // the previous item is done with the tables and LDS
-  const int2 item = item_of(P, item_k);
-  const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y;
-  const Info inf = info_of(P, i);
+  const int4 item = item_of(P, item_k);
+  const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y, r = item.z;
   const int L = P.chunk_pages, W = P.window_pages, D = P.D, es = P.es;
   const int lb = P.log_b, b = 1 << lb;
-  const int dp0 = gp::uni(P.dp0[item.x]);
-  const int dp_lo = max(dp0, c * L), dp_hi = min((c + 1) * L, inf.n_dest);
+  const int dp_lo = max(item.w, c * L);
+  // the item's own loads go out together (the item carries the request row and dp0): the
+  // request's record, the head's evicted list and the old and new block-table entries of pages
+  // dp_lo .. (indexes kept inside the rows; what lies past the chunk or the old pages is
+  // dropped once the record is in)
+  const Info inf = info_of(P, i);
+  const int t = threadIdx.x;
+  const int ev_t = P.ev[((size_t)i * P.H_kv + h) * P.max_evict + min(t, P.max_evict - 1)];
+  const int lpc = min(dp_lo + t, P.max_pages - 1);
+  const int old_pg = P.old_bt[(size_t)i * P.max_pages + lpc];
+  const int new_pg = P.block_tables[(size_t)r * P.max_pages + lpc];
+  const int dp_hi = min((c + 1) * L, inf.n_dest);
   __shared__ int s_thr[MAX_EVICT];
   __shared__ int s_src[MAX_WINDOW_SLOTS];
   // source pages dp_lo .. dp_hi + span - 1: byte offset of the (page, head) key block from the
@@ -1262,24 +1279,21 @@ __global__ __launch_bounds__(CP_THREADS) void compact_kernel(CParams P) {
   extern __shared__ __align__(16) uint8_t s_v[];  // value pages of the window
   const int E = inf.E;
   const size_t pb = page_bytes(P);
-  if (threadIdx.x < MAX_EVICT)
-    s_thr[threadIdx.x] = threadIdx.x < E
-                             ? P.ev[((size_t)i * P.H_kv + h) * P.max_evict + threadIdx.x] - (int)threadIdx.x
-                             : INT_MAX;
-  if (threadIdx.x < dp_hi - dp_lo + P.span) {
-    const int lp = dp_lo + threadIdx.x;
+  if (t < MAX_EVICT) s_thr[t] = t < E ? ev_t - t : INT_MAX;
+  if (t < dp_hi - dp_lo + P.span) {
+    const int lp = dp_lo + t;
     long long ks = NO_SRC, vs = NO_SRC;
     if (lp < inf.P) {
       if (from_snapshot(P, lp, c, inf)) {
         ks = (long long)((intptr_t)snap_ptr(P, i, h, lp, 0) - (intptr_t)P.k);
         vs = (long long)((intptr_t)snap_ptr(P, i, h, lp, 1) - (intptr_t)P.v);
       } else {
-        ks = vs = (long long)pool_off(P, P.old_bt[(size_t)i * P.max_pages + lp], h);
+        ks = vs = (long long)pool_off(P, old_pg, h);
       }
     }
-    s_ksrc[threadIdx.x] = ks;
-    s_vsrc[threadIdx.x] = vs;
-    if (lp < dp_hi) s_doff[threadIdx.x] = (long long)pool_off(P, P.block_tables[(size_t)inf.r * P.max_pages + lp], h);
+    s_ksrc[t] = ks;
+    s_vsrc[t] = vs;
+    if (lp < dp_hi) s_doff[t] = (long long)pool_off(P, new_pg, h);
   }
   const int lqpp = P.log_qpp, qpp = 1 << lqpp;  // 16-byte pieces per page
   const int lkq = P.log_kq;
@@ -1403,7 +1417,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_wide_kernel(CParams P) {
     if (g >= n_groups) break;
     const int item_k = g * P.npart + m % P.npart;
     lds_barrier();  // the previous item is done with the tables and the ring
-    const int2 item = item_of(P, item_k);
+    const int4 item = item_of(P, item_k);
     const int i = item.x / P.H_kv, h = item.x % P.H_kv;
     const int c = item.y / P.npart, part = item.y % P.npart;
     const Info inf = info_of(P, i);
@@ -1727,7 +1741,7 @@ __device__ __forceinline__ void store_page_parts(const PageParts& x, uint8_t* kd
 __global__ __launch_bounds__(CP_THREADS) void snapshot_mixed_kernel(CParams P) {
   const int n_items = gp::uni(*P.n_items);
   for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-    const int2 item = item_of(P, it);
+    const int4 item = item_of(P, it);
     const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y;
     const Info inf = info_of(P, i);
     for (int s = 0; s < P.span; ++s) {
@@ -1849,7 +1863,7 @@ __global__ __launch_bounds__(CP_THREADS) void compact_mixed_kernel(CParams P) {
   const int sm = (int)(1ll << (63 - __builtin_clzll((unsigned long long)min(pool_pieces, 1024ll)))) - 1;
   for (int item_k = blockIdx.x; item_k < n_items; item_k += gridDim.x) {
     lds_barrier();  // the previous item is done with the tables and LDS
-    const int2 item = item_of(P, item_k);
+    const int4 item = item_of(P, item_k);
     const int i = item.x / P.H_kv, h = item.x % P.H_kv, c = item.y;
     const Info inf = info_of(P, i);
     const int E = inf.E;
@@ -2236,7 +2250,7 @@ WsLayout ws_layout(int L, int R, int H_kv, int max_pages, int page_size, int C_m
   lo += (size_t)R * H_kv * 4;
   lo = (lo + 15) & ~(size_t)15;
   w.items = lo;
-  lo += (size_t)R * H_kv * max_chunks * parts * sizeof(int2);
+  lo += (size_t)R * H_kv * max_chunks * parts * sizeof(int4);
   w.n_items = lo;
   lo += 256;
   w.layer_bytes = (lo + 255) & ~(size_t)255;
@@ -2382,7 +2396,7 @@ int compact_impl(const int32_t* req_idx, int R, int B, int L, const float* a_sho
     uint8_t* lw = ws + wl.layer0 + (size_t)l * wl.layer_bytes;
     Q.ev = reinterpret_cast<int32_t*>(lw + wl.ev);
     Q.dp0 = reinterpret_cast<int32_t*>(lw + wl.dp0);
-    Q.items = reinterpret_cast<int2*>(lw + wl.items);
+    Q.items = reinterpret_cast<int4*>(lw + wl.items);
     Q.n_items = reinterpret_cast<int32_t*>(lw + wl.n_items);
     return Q;
   };
