@@ -83,11 +83,33 @@ __device__ __forceinline__ f16x4_t int4x4_to_f16x4(uint32_t w) {
   return f16x4_t{a.x, a.y, b.x, b.y};
 }
 
+// One word of two 4-code groups (dimension A in bits 0..15, dimension B in 16..31; nibble j of a
+// group = token j) -> the halves of both dimensions, each in the token order (0, 2, 1, 3). One
+// byte permute first interleaves the groups' bytes (A.b0, B.b0, A.b1, B.b1), so that each mask
+// picks two tokens of one dimension and a single shift serves dimension B.
+__device__ __forceinline__ void int4_word_to_f16x4x2(uint32_t w, f16x4_t& a, f16x4_t& b) {
+  const uint32_t x = __builtin_amdgcn_perm(w, w, 0x03010200u);
+  const f16x2_t a02 = int4_lo_pair(x), a13 = int4_hi_pair(x);
+  const f16x2_t b02 = int4_lo_pair(x >> 8), b13 = int4_hi_pair(x >> 8);
+  a = f16x4_t{a02.x, a02.y, a13.x, a13.y};
+  b = f16x4_t{b02.x, b02.y, b13.x, b13.y};
+}
+
 __device__ __forceinline__ float half_lo(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
 }
 __device__ __forceinline__ float half_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// x times the half in the low / high 16 bits of w, rounded once to float: written as an fma with
+// a +0 addend of the widened half so that it becomes one mixed-precision fma instruction instead of
+// a conversion and a product (same value; only a -0 product turns into +0).
+__device__ __forceinline__ float mul_half_lo(float x, uint32_t w) {
+  return __builtin_fmaf(x, (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)), 0.0f);
+}
+__device__ __forceinline__ float mul_half_hi(float x, uint32_t w) {
+  return __builtin_fmaf(x, (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)), 0.0f);
 }
 
 // Dual-timescale EMA step (GrowPage Sec. 3.2 Eq. 6) on four consecutive elements of one slot's

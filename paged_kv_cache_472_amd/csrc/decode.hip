@@ -148,6 +148,56 @@ __device__ __forceinline__ int sanitize_ctx(const DecodeParams& p, int r) {
   return ctx;
 }
 
+// The key and value halves of one INT4 tile (the walk over INT4 tiles refills them separately).
+template <int D>
+struct KRing4 {
+  u32x4_t k;   // the lane's D/4 key codes (D = 64: in .xy)
+  u32x2_t ks;  // the 4 half scales of the lane's tokens
+};
+template <int D>
+struct VRing4 {
+  u32x2_t v[D / 64];  // 2 bytes (4 tokens) for each of D/16 value dimensions
+  u32x2_t vs;         // the 4 half scales of the lane's tokens
+};
+
+// Row index (page, KV head, first token of the tile) of an INT4 tile: wave-uniform, so the
+// loads below take a scalar base plus a 32-bit lane offset. The lane offsets are made opaque per
+// load; otherwise the compiler hoists pool + lane offset out of the tile loop as a 64-bit vector
+// pointer and adds the page part to it with vector instructions on every tile.
+__device__ __forceinline__ size_t int4_row0(const DecodeParams& p, int code, int tok0, int h) {
+  return ((size_t)(code >> 2) * p.H_kv + h) * (size_t)p.page_size + tok0 % p.page_size;
+}
+
+template <int D>
+__device__ __forceinline__ void load_k4(const DecodeParams& p, int code, int tok0, int h,
+                                        int lane, KRing4<D>& t) {
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const size_t row0 = int4_row0(p, code, tok0, h);
+  uint32_t k_lane = (uint32_t)(n16 * (D / 2) + g4 * (D / 8));
+  uint32_t s_lane = (uint32_t)(8 * g4);  // bytes: 4 half scales per lane
+  asm volatile("" : "+v"(k_lane), "+v"(s_lane));
+  const uint8_t* kb = p.k4 + row0 * (D / 2);
+  if constexpr (D == 128)
+    t.k = gp::ld_stream<u32x4_t>(kb + k_lane);
+  else
+    *reinterpret_cast<u32x2_t*>(&t.k) = gp::ld_stream<u32x2_t>(kb + k_lane);
+  t.ks = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint8_t*>(p.k4_scale + row0) + s_lane);
+}
+
+template <int D>
+__device__ __forceinline__ void load_v4(const DecodeParams& p, int code, int tok0, int h,
+                                        int lane, VRing4<D>& t) {
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const size_t row0 = int4_row0(p, code, tok0, h);
+  uint32_t v_lane = (uint32_t)(g4 * (2 * D) + n16 * (D / 8));
+  uint32_t s_lane = (uint32_t)(8 * g4);
+  asm volatile("" : "+v"(v_lane), "+v"(s_lane));
+  const uint8_t* vb = p.v4 + (row0 >> 2) * (2 * D);  // 4-token blocks of 2 D bytes
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) t.v[i] = *reinterpret_cast<const u32x2_t*>(vb + v_lane + 8 * i);
+  t.vs = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const uint8_t*>(p.v4_scale + row0) + s_lane);
+}
+
 // Load tile `tok0` (a multiple of 16) of KV head h from the page encoded in `code`. Loads whose
 // instruction covers whole 128-byte lines (value rows of bf16, fp32 and fp8 pages, INT4 key rows)
 // are streaming loads; key rows read 64 bytes per row per instruction (the other half comes with
@@ -160,19 +210,15 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int code, int t
   const int b = p.page_size;
   const int off = tok0 % b;
   if constexpr (KIND == KIND_INT4) {
-    const int pg = code >> 2;
-    const size_t kv_base = ((size_t)pg * p.H_kv + h) * (size_t)b * D;
-    const uint8_t* kr = p.k4 + kv_base / 2 + (size_t)(off + n16) * (D / 2) + g4 * (D / 8);
-    if constexpr (D == 128)
-      t.k = gp::ld_stream<u32x4_t>(kr);
-    else
-      *reinterpret_cast<u32x2_t*>(&t.k) = gp::ld_stream<u32x2_t>(kr);
-    const uint8_t* vr = p.v4 + kv_base / 2 + (size_t)((off >> 2) + g4) * (2 * D) + n16 * (D / 8);
+    KRing4<D> kh;
+    VRing4<D> vh;
+    load_k4<D>(p, code, tok0, h, lane, kh);
+    load_v4<D>(p, code, tok0, h, lane, vh);
+    t.k = kh.k;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) t.v[i] = *reinterpret_cast<const u32x2_t*>(vr + 8 * i);
-    const size_t sc = ((size_t)pg * p.H_kv + h) * b + off + 4 * g4;
-    *reinterpret_cast<u32x2_t*>(&t.ks) = *reinterpret_cast<const u32x2_t*>(p.k4_scale + sc);
-    *reinterpret_cast<u32x2_t*>(&t.vs) = *reinterpret_cast<const u32x2_t*>(p.v4_scale + sc);
+    for (int i = 0; i < D / 64; ++i) t.v[i] = vh.v[i];
+    *reinterpret_cast<u32x2_t*>(&t.ks) = kh.ks;
+    *reinterpret_cast<u32x2_t*>(&t.vs) = vh.vs;
   } else if constexpr (KIND == KIND_FP8) {
     const int pg = code;
     const size_t kv_base = ((size_t)pg * p.H_kv + h) * (size_t)b * D;
@@ -408,6 +454,118 @@ __device__ __forceinline__ void walk_tiles(const DecodeParams& p, const int* lst
   }
 }
 
+// Walk n listed INT4 tiles in turns of RING_INT4 tiles, with the softmax bookkeeping once per
+// turn: the logits of the turn's tiles, one cross-lane maximum and one (rare) rescale of the
+// output rows for all of them, then their weighted values. A key slot is refilled right after its
+// logits and a value slot right after its products, so each wait covers one half tile. Slots past
+// the list's main part (its end, or a tail tile, which is decoded after the loop with its masks)
+// go through the same instructions as no-ops: their logits stay out of the maximum and their
+// weights are zero (INT4 codes are always finite, so zero weights leave the rows unchanged).
+// Why per turn: the per-tile rescale branch made the compiler copy all 32 output registers on
+// every tile's common path; here the bookkeeping and any such copies come once per turn.
+template <int D>
+__device__ __forceinline__ void walk_tiles_int4(const DecodeParams& p, const int* lst_code,
+                                                const int* lst_tile, int n, int h, int lane,
+                                                int ctx, const f16x8_t* qh, WaveState<D>& st) {
+  constexpr int RING = RING_INT4;
+  if (n == 0) return;
+  const int g4 = lane >> 4;
+  KRing4<D> kr[RING];
+  VRing4<D> vr[RING];
+#pragma unroll
+  for (int q = 0; q < RING; ++q) {
+    const int e = min(q, n - 1);
+    const int c = __builtin_amdgcn_readfirstlane(lst_code[e]);
+    const int t = __builtin_amdgcn_readfirstlane(lst_tile[e]) << 4;
+    load_k4<D>(p, c, t, h, lane, kr[q]);
+    load_v4<D>(p, c, t, h, lane, vr[q]);
+  }
+  const int last_tok0 = __builtin_amdgcn_readfirstlane(lst_tile[n - 1]) << 4;
+  const bool has_tail = last_tok0 + 16 > ctx;
+  const int n_main = has_tail ? n - 1 : n;
+  for (int e0 = 0; e0 < n; e0 += RING) {
+    // ---- logits of the turn's tiles: S[token 4*g4 + i][head n16], log2 domain
+    float sv[RING][4];
+    float tmax = -INFINITY;
+    int nc[RING], nt[RING];  // the entry each slot is refilled with (keys now, values below)
+#pragma unroll
+    for (int q = 0; q < RING; ++q) {
+      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk)
+        sacc = gp::mfma_f16_16x16x32(gp::int4x8_to_f16x8(kr[q].k[kk]), qh[kk], sacc);
+      sv[q][0] = gp::mul_half_lo(sacc[0], kr[q].ks.x) * p.scale_log2;
+      sv[q][1] = gp::mul_half_hi(sacc[1], kr[q].ks.x) * p.scale_log2;
+      sv[q][2] = gp::mul_half_lo(sacc[2], kr[q].ks.y) * p.scale_log2;
+      sv[q][3] = gp::mul_half_hi(sacc[3], kr[q].ks.y) * p.scale_log2;
+      const float m4 = fmaxf(fmaxf(sv[q][0], sv[q][1]), fmaxf(sv[q][2], sv[q][3]));
+      tmax = e0 + q < n_main ? fmaxf(tmax, m4) : tmax;
+      const int ex = min(e0 + q + RING, n - 1);
+      nc[q] = __builtin_amdgcn_readfirstlane(lst_code[ex]);
+      nt[q] = __builtin_amdgcn_readfirstlane(lst_tile[ex]) << 4;
+      load_k4<D>(p, nc[q], nt[q], h, lane, kr[q]);
+    }
+    // ---- one running-maximum step for the turn (lazy: moves only by more than 2^8)
+    float mx = gp::xor16_max(tmax);
+    mx = gp::xor32_max(mx);
+    const bool move = mx > st.m_run + 8.0f;
+    const float m_new = move ? mx : st.m_run;
+    const float alpha = move ? gp::safe_exp2_diff(st.m_run, m_new) : 1.0f;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(move) != 0, 0)) {
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g4 + i, GP_WAVE);
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.acc[nb][i] *= al[i];
+    }
+    // ---- weighted values of the turn's tiles
+    float psum = 0.f;
+#pragma unroll
+    for (int q = 0; q < RING; ++q) {
+      const bool live = e0 + q < n_main;
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(sv[q][i] - m_new);
+      const float ps = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+      const float pw[4] = {gp::mul_half_lo(pv[0], vr[q].vs.x), gp::mul_half_hi(pv[1], vr[q].vs.x),
+                           gp::mul_half_lo(pv[2], vr[q].vs.y), gp::mul_half_hi(pv[3], vr[q].vs.y)};
+      psum += live ? ps : 0.f;
+      // a no-op slot's weights may be NaN (its scales can be poison): the select clears them
+      const uint32_t p02 = live ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[0], pw[2])) : 0u;
+      const uint32_t p13 = live ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pw[1], pw[3])) : 0u;
+      const f16x4_t ph = __builtin_bit_cast(f16x4_t, u32x2_t{p02, p13});
+#pragma unroll
+      for (int wd = 0; wd < D / 32; ++wd) {
+        // dimensions 16 (2 wd) + n16 and 16 (2 wd + 1) + n16: 2 bytes each
+        f16x4_t va, vb;
+        gp::int4_word_to_f16x4x2(vr[q].v[wd / 2][wd % 2], va, vb);
+        st.acc[2 * wd] = gp::mfma_f16_16x16x16(ph, va, st.acc[2 * wd]);
+        st.acc[2 * wd + 1] = gp::mfma_f16_16x16x16(ph, vb, st.acc[2 * wd + 1]);
+      }
+      load_v4<D>(p, nc[q], nt[q], h, lane, vr[q]);
+    }
+    st.l_run = st.l_run * alpha + psum;
+    st.m_run = m_new;
+  }
+  if (has_tail) {
+    // slots past the end hold the last entry again
+    const int slot = (n - 1) % RING;
+#pragma unroll
+    for (int q = 0; q < RING; ++q)
+      if (q == slot) {
+        TileRaw<D, KIND_INT4> t;
+        t.k = kr[q].k;
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) t.v[i] = vr[q].v[i];
+        *reinterpret_cast<u32x2_t*>(&t.ks) = kr[q].ks;
+        *reinterpret_cast<u32x2_t*>(&t.vs) = vr[q].vs;
+        process_tile<D, KIND_INT4, true>(p, t, last_tok0, ctx, lane, nullptr, qh, st);
+      }
+  }
+}
+
 // LDS ints per wave for tile lists: page codes and tile indexes; a mixed cache's first pass keeps
 // its bf16 and fp8 tiles in two lists.
 template <int KIND>
@@ -592,6 +750,8 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
         // bf16 tiles as a bf16 cache's (a scale of 1 changes no bit), then the fp8 tiles
         walk_tiles<D, KIND_BF16, RING>(p, lst_code, lst_tile, n, h, lane, ctx, qf, qh, st);
         walk_tiles<D, KIND_FP8, RING_FP8>(p, lst_code2, lst_tile2, n2, h, lane, ctx, qf, qh, st);
+      } else if constexpr (KIND == KIND_INT4) {
+        walk_tiles_int4<D>(p, lst_code, lst_tile, n, h, lane, ctx, qh, st);
       } else {
         walk_tiles<D, KIND, RING>(p, lst_code, lst_tile, n, h, lane, ctx, qf, qh, st);
       }
