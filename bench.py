@@ -384,20 +384,30 @@ def int4_leg(wl, gp, torch, np, steps):
     def run():
         gp.gp_paged_decode_attn(wl.q, cache, wl.block_tables, wl.context_lens, wl.max_context,
                                 wl.sm_scale, out=out, lse=lse, workspace=ws)
-    for _ in range(3):
-        run()
-    e[2].record()
-    for _ in range(steps):
-        run()
-    e[3].record()
-    torch.cuda.synchronize()
-    ms = e[2].elapsed_time(e[3]) / steps
+
+    def timed():
+        for _ in range(3):
+            run()
+        e[2].record()
+        for _ in range(steps):
+            run()
+        e[3].record()
+        torch.cuda.synchronize()
+        return e[2].elapsed_time(e[3]) / steps
+    # every page the tables reach is INT4 and the cache says so: the bf16 / fp8 pass, which would
+    # find no page, is not launched (gp_kv_cache.tags_present); the same call with the tags
+    # undeclared runs both passes
+    cache.tags_present = (gp.growpage.TAG_INT4,)
+    ms = timed()
+    cache.tags_present = ()
+    ms_both = timed()
     ctx = wl.context_lens.cpu().numpy().astype(np.int64)
     pages = np.array([math.ceil(c / b) for c in ctx], dtype=np.int64)
     kv = int(ctx.sum()) * H * (d + 2 * 2)
     total = kv + int((2 * wl.H_q * d * 2 + wl.H_q * 4 + pages * 4 + 4).sum())
     return dict(pages=int(used.numel()), quantize_ms=round(e[0].elapsed_time(e[1]), 4),
-                decode_ms=round(ms, 4), bytes_per_launch=total,
+                decode_ms=round(ms, 4), tags_declared=True, decode_ms_tags_undeclared=round(ms_both, 4),
+                bytes_per_launch=total,
                 achieved_gbps=round(total / (ms * 1e-3) / 1e9, 1),
                 frac=round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4))
 
@@ -574,6 +584,11 @@ def decode_leg(name, gp, torch, np, reps, make_workload):
     dev = "cuda:0"
     wl = make_workload(name, "full", device=dev)
     cache = gp.KVCache.from_workload(wl)
+    if wl.mixed:
+        # the tags the batch's pages carry, as a caller that manages its tiers knows them: a
+        # decode pass with none of its tags is not launched (gp_kv_cache.tags_present)
+        bt = wl.block_tables.cpu().numpy()
+        cache.tags_present = tuple(int(t) for t in np.unique(wl.page_tag.cpu().numpy()[np.unique(bt[bt >= 0])]))
     B, H_q, d = wl.q.shape
     out = torch.empty_like(wl.q)
     lse = torch.empty((B, H_q), dtype=torch.float32, device=dev)

@@ -110,6 +110,15 @@ enum {
  *             A uniformly fp8 cache is a mixed cache whose pages are all tagged GP_TAG_FP8 (the
  *             bf16 and INT4 pools are then never read, but must still be given).
  *   page_size a multiple of 16 (16 .. 256); head_dim 64 or 128.
+ *   tags_present  mixed caches only, read by the decode calls: 0 (unknown: every pass runs), or
+ *             the set of page tags (bit 1 << GP_TAG_*) that the pages the block tables reach may
+ *             carry. A mixed decode runs one pass over the bf16 and fp8 pages and one over the
+ *             INT4 pages; a pass whose tags are all absent from the set is not launched (with no
+ *             bf16, fp8 or INT4 bit at all, the first pass still runs). A launched pass decodes
+ *             every page of its tags, declared or not; the pages of a pass that is not launched
+ *             are skipped exactly like released pages. The set is a promise of the caller:
+ *             breaking it loses those pages' tokens, nothing more (no read outside the pools).
+ *             The score and compaction calls read every page's tag and ignore this field.
  */
 typedef struct {
   void* k;
@@ -128,6 +137,7 @@ typedef struct {
   void* v4;
   uint16_t* k4_scale;
   uint16_t* v4_scale;
+  uint32_t tags_present;
 } gp_kv_cache;
 
 int gp_version(void);

@@ -948,14 +948,21 @@ int device_cus() {
 }
 
 template <int D, int KIND, int RING>
-int launch_decode_ring(DecodeParams p, int max_workgroups, hipStream_t stream) {
+int launch_decode_ring(DecodeParams p, int max_workgroups, hipStream_t stream, uint32_t tags) {
   const int hg = (p.H_kv + p.heads_per_wg - 1) / p.heads_per_wg;
   const int threads = p.heads_per_wg * GP_WAVE;
   const size_t lds = ((size_t)pref_ints(p.B) + (size_t)p.heads_per_wg * list_ints<KIND>()) * sizeof(int);
-  int total = resident_workgroups<D, KIND, RING>(threads, lds);
   // a mixed cache decodes in two passes over the same ranges (the bf16 / fp8 tiles, then the
-  // INT4 tiles with a deeper ring); both must cut the batch identically
-  p.passes = KIND == KIND_MIXED ? 2 : 1;
+  // INT4 tiles with a deeper ring); both must cut the batch identically. A pass whose page tags
+  // the caller declares absent is not launched (tags == 0: unknown, both run); with no INT4 pass
+  // left the first runs alone, and with no first pass the INT4 pass runs alone as pass 0.
+  bool run_first = true, run_int4 = KIND == KIND_MIXED;
+  if (KIND == KIND_MIXED && tags != 0) {
+    run_int4 = (tags & (1u << GP_TAG_INT4)) != 0;
+    run_first = (tags & ((1u << GP_TAG_BF16) | (1u << GP_TAG_FP8))) != 0 || !run_int4;
+  }
+  p.passes = (run_first ? 1 : 0) + (run_int4 ? 1 : 0);
+  int total = resident_workgroups<D, KIND, RING>(threads, lds);
   if (max_workgroups > 0) total = std::min(total, max_workgroups);
   p.num_wg = std::max(1, total / hg);
   p.pass = 0;
@@ -964,21 +971,24 @@ int launch_decode_ring(DecodeParams p, int max_workgroups, hipStream_t stream) {
   const int hg1 = (p.H_kv + hpw1 - 1) / hpw1;
   int total1 = 0;
   const size_t lds1 = ((size_t)pref_ints(p.B) + (size_t)hpw1 * list_ints<KIND_INT4>()) * sizeof(int);
-  if (p.passes == 2) {
+  if (run_int4) {
     total1 = resident_workgroups<D, KIND_INT4, RING_INT4>(hpw1 * GP_WAVE, lds1);
     if (max_workgroups > 0) total1 = std::min(total1, max_workgroups * (p.heads_per_wg / hpw1));
   }
-  p.num_wg_pass[0] = p.num_wg;
-  p.num_wg_pass[1] = std::max(1, total1 / hg1);
-  hipLaunchKernelGGL((decode_streamk_kernel<D, KIND, RING>), dim3(p.num_wg, hg), dim3(threads), lds,
-                     stream, p);
-  GP_CHECK_LAUNCH();
-  if (p.passes == 2) {
+  const int width1 = std::max(1, total1 / hg1);
+  p.num_wg_pass[0] = run_first ? p.num_wg : width1;
+  p.num_wg_pass[1] = run_first && run_int4 ? width1 : 1;
+  if (run_first) {
+    hipLaunchKernelGGL((decode_streamk_kernel<D, KIND, RING>), dim3(p.num_wg, hg), dim3(threads), lds,
+                       stream, p);
+    GP_CHECK_LAUNCH();
+  }
+  if (run_int4) {
     DecodeParams p1 = p;
-    p1.pass = 1;
-    p1.q_pre = nullptr;  // the summary update ran in the first pass
+    p1.pass = run_first ? 1 : 0;
+    if (run_first) p1.q_pre = nullptr;  // the summary update ran in the first pass
     p1.heads_per_wg = hpw1;
-    p1.num_wg = p.num_wg_pass[1];
+    p1.num_wg = width1;
     hipLaunchKernelGGL((decode_streamk_kernel<D, KIND_INT4, RING_INT4>), dim3(p1.num_wg, hg1),
                        dim3(hpw1 * GP_WAVE), lds1, stream, p1);
     GP_CHECK_LAUNCH();
@@ -997,15 +1007,15 @@ int launch_decode_ring(DecodeParams p, int max_workgroups, hipStream_t stream) {
 // wave with the same grid (Qwen3-8B-shaped batch 0.422 -> 0.413 ms) or than two workgroups per
 // compute unit (0.432 ms). Smaller tiles need the deeper ring to keep enough bytes in flight.
 template <int D, int KIND>
-int launch_decode(DecodeParams p, int max_workgroups, hipStream_t stream) {
+int launch_decode(DecodeParams p, int max_workgroups, hipStream_t stream, uint32_t tags) {
   if constexpr (KIND == KIND_BF16 || KIND == KIND_F32) {
-    if (max_workgroups > 0) return launch_decode_ring<D, KIND, RING_SHARED>(p, max_workgroups, stream);
+    if (max_workgroups > 0) return launch_decode_ring<D, KIND, RING_SHARED>(p, max_workgroups, stream, 0);
     if (D == 128 && p.heads_per_wg == MAX_HEADS_PER_WG) {
       const int hg = (p.H_kv + p.heads_per_wg - 1) / p.heads_per_wg;
-      return launch_decode_ring<D, KIND, RING_SHARED>(p, device_cus() * hg, stream);
+      return launch_decode_ring<D, KIND, RING_SHARED>(p, device_cus() * hg, stream, 0);
     }
   }
-  return launch_decode_ring<D, KIND, RING_FULL>(p, max_workgroups, stream);
+  return launch_decode_ring<D, KIND, RING_FULL>(p, max_workgroups, stream, tags);
 }
 
 // Bytes of the decode workspace when `passes` passes leave partials (a mixed cache decodes its
@@ -1136,9 +1146,10 @@ int decode_impl(const void* q, int q_dtype, int B, int H_q, const gp_kv_cache* k
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int mw = max_workgroups;
-  if (mixed) return D == 64 ? launch_decode<64, KIND_MIXED>(p, mw, s) : launch_decode<128, KIND_MIXED>(p, mw, s);
-  if (q_dtype == GP_BF16) return D == 64 ? launch_decode<64, KIND_BF16>(p, mw, s) : launch_decode<128, KIND_BF16>(p, mw, s);
-  return D == 64 ? launch_decode<64, KIND_F32>(p, mw, s) : launch_decode<128, KIND_F32>(p, mw, s);
+  const uint32_t tags = mixed ? kv->tags_present : 0u;
+  if (mixed) return D == 64 ? launch_decode<64, KIND_MIXED>(p, mw, s, tags) : launch_decode<128, KIND_MIXED>(p, mw, s, tags);
+  if (q_dtype == GP_BF16) return D == 64 ? launch_decode<64, KIND_BF16>(p, mw, s, 0) : launch_decode<128, KIND_BF16>(p, mw, s, 0);
+  return D == 64 ? launch_decode<64, KIND_F32>(p, mw, s, 0) : launch_decode<128, KIND_F32>(p, mw, s, 0);
 }
 
 }  // namespace

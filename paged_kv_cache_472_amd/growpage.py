@@ -41,6 +41,7 @@ class GpKvCache(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("k4", ctypes.c_void_p), ("v4", ctypes.c_void_p),
         ("k4_scale", ctypes.c_void_p), ("v4_scale", ctypes.c_void_p),
+        ("tags_present", ctypes.c_uint32),
     ]
 
 
@@ -134,10 +135,12 @@ class KVCache:
     """Device tensors of one layer's paged cache (layouts in include/growpage.h)."""
 
     def __init__(self, k, v, page_size, k8=None, v8=None, k_scale=None, v_scale=None, page_tag=None,
-                 k4=None, v4=None, k4_scale=None, v4_scale=None):
+                 k4=None, v4=None, k4_scale=None, v4_scale=None, tags_present=()):
         self.k, self.v, self.page_size = k, v, int(page_size)
         self.k8, self.v8, self.k_scale, self.v_scale, self.page_tag = k8, v8, k_scale, v_scale, page_tag
         self.k4, self.v4, self.k4_scale, self.v4_scale = k4, v4, k4_scale, v4_scale
+        # page tags (TAG_*) the decode may meet; empty: unknown (include/growpage.h, tags_present)
+        self.tags_present = tuple(int(t) for t in tags_present)
 
     @classmethod
     def from_workload(cls, wl):
@@ -157,7 +160,7 @@ class KVCache:
             _ptr(self.k), _ptr(self.v), _ptr(self.k8), _ptr(self.v8), _ptr(self.k_scale),
             _ptr(self.v_scale), _ptr(self.page_tag), self.k.shape[0], self.page_size,
             self.k.shape[1], self.k.shape[3], _dtype_code(self.k), _ptr(self.k4), _ptr(self.v4),
-            _ptr(self.k4_scale), _ptr(self.v4_scale))
+            _ptr(self.k4_scale), _ptr(self.v4_scale), sum(1 << t for t in set(self.tags_present)))
 
 
 def gp_paged_decode_attn_workspace_size(B, H_q, H_kv, head_dim, page_size, max_context):
