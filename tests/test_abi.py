@@ -219,3 +219,35 @@ def test_mixed_boundary_arguments_rejected_on_host(lib):
     assert lib.gp_compact_or_grow_layers(*largs(two)) == -2
     two[1] = ctypes.pointer(u1)
     assert lib.gp_compact_or_grow_layers(*largs(two)) == -1
+
+
+def test_binding_structs_match_the_header_layout(tmp_path):
+    """The ctypes mirrors of the header's argument structs (gp_kv_cache, gp_summary_update) have the
+    header's fields in its order, at the offsets and total size a C compiler gives them: a field
+    added on one side only (as tags_present once was) fails here instead of shifting every later
+    argument of a call."""
+    from paged_kv_cache_472_amd.growpage import GpKvCache, GpSummaryUpdate
+    structs = {"gp_kv_cache": GpKvCache, "gp_summary_update": GpSummaryUpdate}
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "growpage.h"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append(f'  printf("{name} size %zu\\n", sizeof({name}));')
+        for field, _ in cls._fields_:
+            lines.append(f'  printf("{name} {field} %zu\\n", offsetof({name}, {field}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True, capture_output=True)
+    got = {}
+    for ln in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        struct, key, val = ln.split()
+        got[(struct, key)] = int(val)
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name, cls in structs.items():
+        body = re.search(r"typedef struct \{([^{}]*)\}\s*" + name + r"\s*;", text).group(1)
+        header_fields = re.findall(r"(\w+)\s*(?:,|;)", body)
+        assert header_fields == [f for f, _ in cls._fields_], name
+        assert ctypes.sizeof(cls) == got[(name, "size")], name
+        for field, _ in cls._fields_:
+            assert getattr(cls, field).offset == got[(name, field)], (name, field)
