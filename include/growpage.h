@@ -51,7 +51,8 @@
 extern "C" {
 #endif
 
-#define GP_VERSION 1
+/* Raised whenever an argument struct or a call's signature changes (2: gp_kv_cache.tags_present). */
+#define GP_VERSION 2
 
 typedef enum {
   GP_OK = 0,
