@@ -124,7 +124,7 @@ def test_decode_int4_full_size_sampled():
     check_decode(out[reqs], lse[reqs], ref, "bf16", f"decode int4 full requests={reqs}")
 
 
-@pytest.mark.parametrize("D,b,G", [(64, 16, 4), (128, 32, 1), (64, 64, 16)])
+@pytest.mark.parametrize("D,b,G", [(64, 16, 4), (128, 32, 1), (64, 64, 16), (128, 256, 4)])
 def test_quantize_then_decode(D, b, G):
     """Demote every other used page on the GPU, decode there; the oracle demotes the same pages
     with its own quantiser and decodes."""
