@@ -807,7 +807,8 @@ __global__ __launch_bounds__(MAX_THREADS) void decode_streamk_kernel(DecodeParam
 template <int D, int KIND>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // one output row per wave: its index is wave-uniform (scalar tests on the partial counts)
+  const long row = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= (long)p.B * p.H_q) return;
   const int r = (int)(row / p.H_q);
   const int U = p.ws_pref[p.B];
@@ -826,6 +827,20 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   const int SL = p.passes * p.j_max;  // slots per row
   auto slot = [&](int k) { return k < J0 ? k : p.j_max + (k - J0); };  // k < NP
   const float* ml = p.ws_ml + row * SL * 2;
+  const float* wo = p.ws_o + row * SL * D;
+  constexpr int PER = D / 64;
+  constexpr int BATCH = 8;  // partial rows fetched before any is used
+  float x[BATCH][PER];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u)
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        x[u][e] = k0 + u < NP ? wo[(size_t)slot(k0 + u) * D + lane + 64 * e] : 0.f;
+  };
+  // the first batch of partial rows goes out with the (max, sum) loads: they depend only on the
+  // partial count, so a row with at most BATCH partials waits for one round trip, not two
+  fetch(0);
   float mk[4], lk[4];
   float mloc = -INFINITY;
 #pragma unroll
@@ -844,19 +859,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
   }
   const float den = gp::wave_sum(dsum);
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  const float* wo = p.ws_o + row * SL * D;
-  constexpr int PER = D / 64;
-  constexpr int BATCH = 8;  // partial rows fetched before any is used
   float num[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) num[e] = 0.f;
   for (int k0 = 0; k0 < NP; k0 += BATCH) {
-    float x[BATCH][PER];
-#pragma unroll
-    for (int u = 0; u < BATCH; ++u)
-#pragma unroll
-      for (int e = 0; e < PER; ++e)
-        x[u][e] = k0 + u < NP ? wo[(size_t)slot(k0 + u) * D + lane + 64 * e] : 0.f;
+    if (k0 > 0) fetch(k0);
 #pragma unroll
     for (int u = 0; u < BATCH; ++u) {
       const int k = k0 + u;
